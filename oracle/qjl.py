@@ -1,0 +1,102 @@
+"""QJL key sketch and inner-product estimators, plain float64.
+
+Test infrastructure (see the package docstring).
+
+eliza quantization README, QJL, "Algorithm in one paragraph": for each key k the norm ||k|| is kept,
+k is multiplied by a Gaussian Johnson-Lindenstrauss matrix and only the signs
+of the m sketch coordinates are kept, eight per byte.  At attention time the
+query is projected through the same matrix and the score is rebuilt from the
+stored signs:
+        <q, k>  ~  ||k|| . sqrt(pi/2) / m . < S q, sign(S k) >,
+which is unbiased with variance ((pi/2) ||q||^2 ||k||^2 - <q,k>^2) / m
+(turbopress 0.4.2 README, "Findings" item 1, gives the matching noise scale
+sqrt(pi/2) ||r|| ||x|| / sqrt(k)).
+
+Readings where the pages leave a step open: S is the m x d matrix applied as S k (the
+pages store it as head_dim x proj_dim and multiply k on the left of it, the
+same numbers transposed); the key norm is stored as fp16; sign(0) = -1 (bit 0);
+a query head h reads KV head h // (Hq / Hkv).
+
+The two-stage estimator combines the codec and the residual sketch:
+        <q, x>  ~  <q, xhat> + rnorm16 . sqrt(pi/2) / m . < S q, sign(S r) >
+with xhat the dequantized block and S = G . R the residual projection.
+"""
+
+import math
+
+import numpy as np
+
+from .numerics import round_fp16, pack_bits_lsb, unpack_bits_lsb
+from . import codec
+
+SQRT_HALF_PI = math.sqrt(math.pi / 2.0)
+
+
+def sketch(k, G):
+    """keys (n, d) float64, G (m, d) -> dict(norm, norm16, p = G k, bits (n, m/8))."""
+    k = np.asarray(k, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    norm = np.sqrt(np.sum(k * k, axis=1))
+    p = k @ G.T
+    return {"norm": norm, "norm16": round_fp16(norm), "p": p, "bits": pack_bits_lsb(p > 0)}
+
+
+def estimate(bits, norm16, Sq, m):
+    """Estimator from packed bits (n, m/8), fp16 norms (n,), projected queries Sq (nq, m).
+
+    Returns (nq, n): norm16[t] * sqrt(pi/2)/m * sum_i (2 bit_ti - 1) Sq_i.
+    """
+    s = np.where(unpack_bits_lsb(bits, m), 1.0, -1.0)          # (n, m)
+    return (np.asarray(Sq, dtype=np.float64) @ s.T) * (np.asarray(norm16, dtype=np.float64)[None, :] * SQRT_HALF_PI / m)
+
+
+def estimate_scale(norm16, Sq, m):
+    """L1 scale of the summed terms, norm16 * sqrt(pi/2)/m * sum_i |Sq_i|  (nq, n)."""
+    a = np.sum(np.abs(np.asarray(Sq, dtype=np.float64)), axis=1)
+    return a[:, None] * (np.asarray(norm16, dtype=np.float64)[None, :] * SQRT_HALF_PI / m)
+
+
+def score_gqa(bits, norm16, q, G):
+    """GQA scores.  bits (B, Hkv, T, m/8), norm16 (B, Hkv, T), q (B, Hq, d), G (m, d).
+
+    Returns scores (B, Hq, T) and their L1 scales (B, Hq, T).
+    """
+    B, Hkv, T, mb = bits.shape
+    m = mb * 8
+    Hq = q.shape[1]
+    group = Hq // Hkv
+    G = np.asarray(G, dtype=np.float64)
+    out = np.zeros((B, Hq, T))
+    scale = np.zeros((B, Hq, T))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            Sq = np.asarray(q[b, h], dtype=np.float64)[None, :] @ G.T
+            out[b, h] = estimate(bits[b, g], norm16[b, g], Sq, m)[0]
+            scale[b, h] = estimate_scale(norm16[b, g], Sq, m)[0]
+    return out, scale
+
+
+def two_stage(codes, n16, qbits, rnorm16, q, bits, D, G):
+    """Two-stage estimate of <q, x> for every (query, block).
+
+    codes (n, d), n16 (n,), qbits (n, m/8), rnorm16 (n,), q (nq, d).
+    Returns (est (nq, n), scale (nq, n)) where scale is the L1 size of the summed
+    terms, sum_j |q_j xhat_j| + rnorm16 sqrt(pi/2)/m sum_i |(S q)_i|.
+    """
+    codes = np.asarray(codes)
+    d = codes.shape[1]
+    m = np.asarray(qbits).shape[1] * 8
+    q = np.asarray(q, dtype=np.float64)
+    xhat = codec.dequantize(codes, n16, bits, D)
+    S = codec.residual_projection(d, D, G)
+    Sq = q @ S.T
+    first = q @ xhat.T
+    second = estimate(qbits, rnorm16, Sq, m)
+    scale = np.abs(q) @ np.abs(xhat).T + estimate_scale(rnorm16, Sq, m)
+    return first + second, scale
+
+
+def storage_ratio(head_dim, m, norm_bytes=2, elem_bytes=2):
+    """Bytes of a bf16 key over bytes of its sketch: head_dim*2 / (m/8 + 2)."""
+    return head_dim * elem_bytes / (m / 8 + norm_bytes)

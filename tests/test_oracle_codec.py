@@ -1,0 +1,170 @@
+"""Pins for the oracle's block codec (CPU only).
+
+The checks do not re-type the oracle's formulas: reconstructions are rebuilt
+here from the Kronecker form of H, codes are checked by brute force over every
+code vector on d = 4 / 8 blocks, and the statistics are compared with the
+Lloyd-Max distortion.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import codec, lloyd_max, hadamard
+from oracle.numerics import round_fp16
+
+
+def _kron_H(d):
+    H = np.array([[1.0]])
+    while H.shape[0] < d:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def _recon(codes, n, D, bits):
+    """x_hat = n R^T c / sqrt(d) with R = H diag(D)/sqrt(d), built independently."""
+    d = codes.shape[-1]
+    c, _, _ = lloyd_max.codebook(bits)
+    R = _kron_H(d) * D[None, :] / math.sqrt(d)
+    return n * (c[codes] @ R) / math.sqrt(d)
+
+
+@pytest.mark.parametrize("d,bits", [(4, 1), (4, 2), (4, 3), (8, 1), (8, 2)])
+def test_brute_force_nearest_reconstruction(d, bits):
+    rng = np.random.default_rng(100 + d * 10 + bits)
+    L = 1 << bits
+    all_codes = np.array(list(itertools.product(range(L), repeat=d)), dtype=np.int64)
+    for trial in range(12):
+        D = rng.choice([-1.0, 1.0], size=d)
+        x = rng.standard_normal(d)
+        x /= np.linalg.norm(x)            # norm 1: exactly representable in fp16, n16 = n
+        q = codec.quantize(x[None, :], bits, D)
+        assert q["n16"][0] == 1.0
+        recons = _recon(all_codes, 1.0, D, bits)
+        err = np.sum((recons - x[None, :]) ** 2, axis=1)
+        best = all_codes[np.argmin(err)]
+        assert np.array_equal(q["codes"][0].astype(np.int64), best)
+        # dequantize agrees with the independent reconstruction
+        assert np.allclose(codec.dequantize(q["codes"], q["n16"], bits, D)[0],
+                           _recon(q["codes"][0].astype(np.int64), 1.0, D, bits), atol=1e-14)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 8])
+def test_codes_are_per_coordinate_nearest_centroid(bits):
+    d = 64
+    rng = np.random.default_rng(bits)
+    D = rng.choice([-1.0, 1.0], size=d)
+    x = rng.standard_normal((200, d)) * 0.02
+    q = codec.quantize(x, bits, D)
+    c, _, _ = lloyd_max.codebook(bits)
+    dist = np.abs(q["y"][..., None] - c[None, None, :])
+    nearest = np.argmin(dist, axis=-1)
+    near_b, _ = codec.boundary_distance(q["y"], bits)
+    ok = near_b > 1e-9     # a decision within fp32 rounding of a boundary may go either way
+    assert np.array_equal(q["codes"][ok], nearest[ok])
+    # y is sqrt(d) R x / ||x||
+    R = _kron_H(d) * D[None, :] / math.sqrt(d)
+    y_ref = math.sqrt(d) * (x @ R.T) / np.linalg.norm(x, axis=1, keepdims=True)
+    assert np.allclose(q["y"], y_ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits,d", [(2, 128), (3, 128), (4, 128), (5, 128), (4, 64), (3, 256)])
+def test_round_trip_distortion_matches_lloyd_max(bits, d):
+    rng = np.random.default_rng(bits * 1000 + d)
+    D = rng.choice([-1.0, 1.0], size=d)
+    x = rng.standard_normal((3000, d))
+    q = codec.quantize(x, bits, D)
+    rel = codec.mse_per_coordinate(x, q["codes"], q["n16"], bits, D)
+    _, _, mse = lloyd_max.codebook(bits)
+    assert abs(np.mean(rel) - mse) < 0.04 * mse
+
+
+def test_norms_are_fp16_of_l2_norm():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((100, 128)) * 10.0 ** rng.integers(-3, 3, (100, 1))
+    D = np.ones(128)
+    q = codec.quantize(x, 4, D)
+    assert np.array_equal(q["n16"], np.linalg.norm(x, axis=1).astype(np.float16).astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 5])
+def test_zero_block(bits):
+    d = 128
+    D = np.random.default_rng(0).choice([-1.0, 1.0], size=d)
+    G = np.random.default_rng(1).standard_normal((64, d))
+    x = np.zeros((1, d))
+    q = codec.quantize(x, bits, D)
+    assert q["n16"][0] == 0.0
+    assert np.all(q["codes"] == (1 << (bits - 1)) - 1)
+    assert np.all(codec.dequantize(q["codes"], q["n16"], bits, D) == 0.0)
+    r = codec.qjl_residual(x, q["codes"], q["n16"], bits, D, G)
+    assert r["rnorm16"][0] == 0.0 and np.all(r["bits"] == 0)
+
+
+def test_one_hot_block_maps_to_unit_coordinates():
+    d, bits = 128, 4
+    rng = np.random.default_rng(9)
+    D = rng.choice([-1.0, 1.0], size=d)
+    j = 17
+    x = np.zeros((1, d))
+    x[0, j] = -3.0
+    q = codec.quantize(x, bits, D)
+    # y_i = H_ij D_j sign(x_j): every coordinate is +-1
+    expect_y = _kron_H(d)[:, j] * D[j] * -1.0
+    assert np.allclose(q["y"][0], expect_y, atol=1e-14)
+    _, beta, _ = lloyd_max.codebook(bits)
+    code_pos, code_neg = int(np.sum(1.0 > beta)), int(np.sum(-1.0 > beta))
+    assert np.array_equal(q["codes"][0], np.where(expect_y > 0, code_pos, code_neg).astype(np.uint8))
+
+
+def test_power_of_two_scaling_keeps_codes():
+    rng = np.random.default_rng(12)
+    d, bits = 128, 5
+    D = rng.choice([-1.0, 1.0], size=d)
+    x = rng.standard_normal((50, d))
+    a = codec.quantize(x, bits, D)
+    b = codec.quantize(x * 8.0, bits, D)
+    assert np.array_equal(a["codes"], b["codes"])
+    assert np.array_equal(a["n16"] * 8.0, b["n16"])
+
+
+def test_idempotent_away_from_boundaries():
+    rng = np.random.default_rng(13)
+    d, bits = 128, 4
+    D = rng.choice([-1.0, 1.0], size=d)
+    x = rng.standard_normal((200, d))
+    a = codec.quantize(x, bits, D)
+    xhat = codec.dequantize(a["codes"], a["n16"], bits, D)
+    b = codec.quantize(xhat, bits, D)
+    dist, _ = codec.boundary_distance(b["y"], bits)
+    ok = dist > 1e-6
+    assert ok.mean() > 0.999
+    assert np.array_equal(a["codes"][ok], b["codes"][ok])
+
+
+def test_residual_projection_identities():
+    rng = np.random.default_rng(14)
+    d, bits, m = 128, 3, 64
+    D = rng.choice([-1.0, 1.0], size=d)
+    G = rng.standard_normal((m, d))
+    x = rng.standard_normal((20, d))
+    q = codec.quantize(x, bits, D)
+    out = codec.qjl_residual(x, q["codes"], q["n16"], bits, D, G)
+    # r is x minus the independent reconstruction
+    r_ref = x - _recon(q["codes"].astype(np.int64), q["n16"][:, None], D, bits)
+    assert np.allclose(out["r"], r_ref, atol=1e-13)
+    assert np.allclose(out["rnorm"], np.linalg.norm(r_ref, axis=1), rtol=1e-13)
+    assert np.array_equal(out["rnorm16"], round_fp16(out["rnorm"]))
+    # S r equals G applied to the rotated residual R r
+    R = _kron_H(d) * D[None, :] / math.sqrt(d)
+    assert np.allclose(out["p"], (r_ref @ R.T) @ G.T, atol=1e-12)
+    bits_unpacked = (out["bits"][:, :, None] >> np.arange(8)) & 1
+    assert np.array_equal(bits_unpacked.reshape(20, m).astype(bool), out["p"] > 0)
+
+
+def test_storage_accounting():
+    # codes-only payload: 1 byte per coordinate + fp16 norm per block
+    assert codec.storage_bytes_per_block(128) == 130
+    assert codec.storage_bytes_per_block(128, m=64) == 130 + 8 + 2
