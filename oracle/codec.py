@@ -8,7 +8,7 @@ of d = 2^k values:
   2. the block is normalised to the unit sphere, u = x / n;
   3. it is rotated by the randomized Walsh-Hadamard transform and scaled by
      sqrt(d), so each coordinate is close to N(0, 1):
-        y = sqrt(d) . R u = H (D * u),       R = H . diag(D) / sqrt(d);
+        y = sqrt(d) . R u = H (D * u) = H (D * x) / n,   R = H . diag(D) / sqrt(d);
   4. each coordinate takes the index of its nearest Lloyd-Max N(0,1) centroid,
      stored as a byte: code_i = #{ j : y_i > beta_j } (beta ascending);
   5. (optional) a 1-bit QJL sketch of the residual is appended.
@@ -65,9 +65,12 @@ def quantize(x, bits, D):
     norm = np.sqrt(np.sum(x * x, axis=1))
     n16 = round_fp16(norm)
     safe = np.where(norm > 0, norm, 1.0)
-    u = np.where(norm[:, None] > 0, x / safe[:, None], 0.0)
     H = sylvester(d)
-    y = (u * np.asarray(D, dtype=np.float64)[None, :]) @ H.T
+    # the rotation is linear, so H (D * x) / n equals H (D * u); rotating the exact
+    # input first keeps coordinates that are exactly zero (ties at the middle
+    # boundary of a structured block) exactly zero instead of +-1e-17
+    z = (x * np.asarray(D, dtype=np.float64)[None, :]) @ H.T
+    y = np.where(norm[:, None] > 0, z / safe[:, None], 0.0)
     y32 = round_fp32(y)
     beta32 = round_fp32(beta)
     codes = np.zeros(y.shape, dtype=np.int64)
@@ -81,9 +84,13 @@ def boundary_distance(y, bits):
     and the code on the far side of that boundary."""
     _, beta, _ = lloyd_max.codebook(bits)
     y = np.asarray(y, dtype=np.float64)
-    diff = np.abs(y[..., None] - beta)
-    j = np.argmin(diff, axis=-1)
-    dist = np.take_along_axis(diff, j[..., None], axis=-1)[..., 0]
+    # nearest boundary: one of the two neighbours of y's position in the sorted list
+    pos = np.searchsorted(beta, y)
+    lo = np.clip(pos - 1, 0, len(beta) - 1)
+    hi = np.clip(pos, 0, len(beta) - 1)
+    d_lo, d_hi = np.abs(y - beta[lo]), np.abs(y - beta[hi])
+    j = np.where(d_lo <= d_hi, lo, hi)
+    dist = np.minimum(d_lo, d_hi)
     below = y <= beta[j]                  # code j on the lower side, j+1 above
     other = np.where(below, j + 1, j)
     return dist, other.astype(np.uint8)
