@@ -1,0 +1,170 @@
+/*
+ * pq.h - C ABI of the MI355X (gfx950) block codec and QJL sketch library.
+ *
+ * The library implements one data-parallel path:
+ *
+ *   * the rotate-then-quantize block codec: per block of d = 2^k values the
+ *     L2 norm is stored as fp16, the block is normalised, rotated by the
+ *     randomized Walsh-Hadamard transform R = H.D/sqrt(d), scaled by sqrt(d)
+ *     and every coordinate is replaced by the index of its nearest Lloyd-Max
+ *     centroid for N(0,1) (eliza quantization README, PolarQuant, "Algorithm
+ *     in one paragraph"; glq 0.7.2 README, "How it works" item 2);
+ *   * its inverse, centroid lookup -> /sqrt(d) -> R^T -> *norm (same section);
+ *   * the optional QJL residual stage: packed signs of a Gaussian projection
+ *     of the quantization residual r plus fp16(||r||) (same section, the 1-bit
+ *     QJL residual correction; turbopress 0.4.2 README, "Package layout",
+ *     qjl.py);
+ *   * the QJL key sketch, fp16(||k||) and packed sign(S k) (eliza quantization
+ *     README, QJL, "Algorithm in one paragraph");
+ *   * the QJL asymmetric estimator of <q, k> from the packed key bits and the
+ *     two-stage estimator of <q, x> from codes + residual bits (same section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Status      0 (PQ_OK) on success, a PQ_E* code otherwise.  Arguments are
+ *               validated synchronously before any HIP call; an invalid call
+ *               launches nothing and writes nothing.  PQ_EHIP means a HIP API
+ *               call failed; its hipError_t is kept per thread and returned by
+ *               pq_last_hip_error().
+ *   Execution   device entry points enqueue kernels on `stream` (a hipStream_t;
+ *               NULL = the legacy default stream) and return without waiting.
+ *               Faults inside a kernel surface at the caller's next
+ *               synchronisation.  Calls on one stream run in order.
+ *   Memory      every pointer argument of a device entry point is device
+ *               memory allocated and owned by the caller; the library allocates
+ *               nothing, keeps no pointer after return and holds no mutable
+ *               global state, so concurrent calls from several threads are
+ *               safe.  Host helpers take host memory.
+ *   Alignment   tensors must be aligned to 16 bytes, except `norms`,
+ *               `rnorms` (2 bytes) and the sign mask (1 byte).
+ *   Empty input n_blocks == 0 (or n_keys == 0, n_q == 0, batch == 0) returns
+ *               PQ_OK once the size parameters are valid; pointers are then not
+ *               examined (they may be NULL) and nothing is launched.
+ *   Dtypes      bf16 and fp16 values are passed as their uint16 bit patterns.
+ *               PQ_F32 = IEEE fp32, PQ_BF16 = bfloat16.
+ *   Signs D     `signs` is a d/8-byte mask, bit j (least significant bit
+ *               first) set means D_j = -1.
+ *   Projection  `proj` is the Gaussian JL matrix G, m x d row-major bf16.
+ *   Bits        QJL sign bits are packed 8 per byte, least significant bit
+ *               first; bit value 1 means sign +1, a projection of exactly 0
+ *               gives bit 0 (qjl_apply.py, `_qjl_decode_keys`).
+ *   Limits      d in {64, 128, 256, 512}; bits in 1..8; m a multiple of 8 in
+ *               [8, 1024] (QJL residual stage and key sketch), a multiple of
+ *               64 in [64, 1024] for the score entry points; block norms must
+ *               be finite (a norm >= 65520 is stored as fp16 +inf).
+ */
+#ifndef PQ_H
+#define PQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQ_ABI_VERSION 1
+
+#define PQ_OK 0
+#define PQ_EINVAL 1        /* bad pointer, size, alignment, dtype or parameter */
+#define PQ_EUNSUPPORTED 2  /* valid request outside what the kernels implement */
+#define PQ_EHIP 3          /* a HIP runtime call failed, see pq_last_hip_error() */
+
+#define PQ_F32 0
+#define PQ_BF16 1
+
+/* ---------------------------------------------------------------- host side */
+
+int pq_abi_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* pq_strerror(int status);
+
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int pq_last_hip_error(void);
+
+/*
+ * Lloyd-Max quantizer for N(0,1) at `bits` bits, as used by the kernels
+ * (eliza quantization README, PolarQuant, "Algorithm in one paragraph":
+ * iterative conditional-expectation centroids; turbopress 0.4.2 README,
+ * "Package layout", codebooks.py: float64 fixed point).
+ *   centroids   out, 2^bits ascending values (may be NULL)
+ *   boundaries  out, 2^bits - 1 midpoints of adjacent centroids (may be NULL)
+ *   mse         out, distortion E[(X - Q(X))^2] of the fixed point (may be NULL)
+ * Returns PQ_EINVAL for bits outside 1..8.  Thread safe; the first call for a
+ * bit width runs the fixed-point iteration (up to ~0.1 s at 8 bits).
+ */
+int pq_codebook(int bits, double* centroids, double* boundaries, double* mse);
+
+/* ---------------------------------------------------------------- device side */
+
+/*
+ * Quantize n_blocks consecutive blocks of d values (eliza quantization
+ * README, PolarQuant, "Algorithm in one paragraph").
+ *   in_dtype   PQ_F32 or PQ_BF16; x holds n_blocks*d values, block b at x + b*d
+ *   signs      d/8-byte rotation sign mask (device)
+ *   codes      out, n_blocks*d bytes: code[b*d + i] = #{j : y_i > beta_j} for the
+ *              rotated, normalised, sqrt(d)-scaled coordinate y_i (Sylvester
+ *              order), decided in fp32
+ *   norms      out, n_blocks fp16: fp16(||x_b||) round-to-nearest-even
+ *   m          0 = no QJL stage (proj, qjl_bits, rnorms must then be NULL);
+ *              otherwise the number of residual projections
+ *   proj       G, m x d bf16 (device)
+ *   qjl_bits   out, n_blocks * m/8 bytes: sign bits of S r with S = G.R (the
+ *              Gaussian matrix applied to the rotated residual; G.R is itself
+ *              an i.i.d. Gaussian matrix) and r = x - dequantize(code, norm)
+ *   rnorms     out, n_blocks fp16: fp16(||r||)
+ */
+int pq_quantize(int d, int bits, int in_dtype, const void* x, int64_t n_blocks,
+                const uint8_t* signs, int m, const uint16_t* proj,
+                uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits, uint16_t* rnorms,
+                void* stream);
+
+/*
+ * Dequantize: xhat_b = norm_b/d * D * (H c[code_b]) (eliza quantization README,
+ * PolarQuant, "Algorithm in one paragraph": lookup -> /sqrt(d) -> inverse
+ * rotation -> *norm).  QJL bits are not used.
+ *   codes      n_blocks*d bytes, each < 2^bits
+ *   norms      n_blocks fp16
+ *   out_dtype  PQ_F32 or PQ_BF16 (round to nearest even); out holds n_blocks*d
+ */
+int pq_dequantize(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                  const uint8_t* signs, int out_dtype, void* out, void* stream);
+
+/*
+ * QJL key sketch (eliza quantization README, QJL, "Algorithm in one paragraph").
+ *   keys       n_keys*d bf16, key t at keys + t*d
+ *   proj       G, m x d bf16
+ *   bits       out, n_keys * m/8 bytes: sign(G k) packed LSB-first
+ *   norms      out, n_keys fp16: fp16(||k||)
+ */
+int qjl_sketch(int d, int m, const uint16_t* keys, int64_t n_keys, const uint16_t* proj,
+               uint8_t* bits, uint16_t* norms, void* stream);
+
+/*
+ * Project queries through the JL matrix: sq[i] = G q_i in fp32 (the query side
+ * of the QJL estimator, same section).
+ *   q          n_q*d bf16;  sq  out, n_q*m fp32
+ */
+int qjl_project(int d, int m, const uint16_t* q, int64_t n_q, const uint16_t* proj, float* sq,
+                void* stream);
+
+/*
+ * QJL asymmetric estimator for grouped-query attention (eliza quantization
+ * README, QJL, "Algorithm in one paragraph"; GQA score kernel named there):
+ *   scores[b][h][t] = norm[b][g][t] * sqrt(pi/2)/m * sum_i (2 bit_i - 1) sq[b][h][i]
+ * with g = h / (q_heads / kv_heads).
+ *   sq         batch*q_heads*m fp32 from qjl_project
+ *   bits       batch*kv_heads*n_keys * m/8 bytes (layout [b][g][t][m/8])
+ *   norms      batch*kv_heads*n_keys fp16
+ *   scores     out, batch*q_heads*n_keys fp32
+ * q_heads must be a multiple of kv_heads with q_heads/kv_heads <= 4.
+ */
+int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
+              const uint8_t* bits, const uint16_t* norms, float* scores, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ_H */

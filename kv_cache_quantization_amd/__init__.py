@@ -1,0 +1,181 @@
+"""MI355X (gfx950) rotate-then-quantize block codec and QJL sketch.
+
+Python binding of the C ABI in ``include/pq.h`` (library ``libpqhip.so`` built
+in this directory by ``python -m kv_cache_quantization_amd.build``).  The
+binding only marshals arguments: every step of the path runs in the library's
+HIP kernels.  torch supplies device memory and the current HIP stream.
+
+Importing works without a GPU (the library loads, compute calls then fail with
+PQ_EHIP); importing fails loudly when the library has not been built.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpqhip.so")
+
+PQ_OK, PQ_EINVAL, PQ_EUNSUPPORTED, PQ_EHIP = 0, 1, 2, 3
+PQ_F32, PQ_BF16 = 0, 1
+
+
+class PQError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.pq_strerror(status).decode()
+        if status == PQ_EHIP:
+            msg += " (hipError_t %d)" % _lib.pq_last_hip_error()
+        super().__init__("%s: %s" % (where, msg))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("kv_cache_quantization_amd: %s is not built "
+                          "(run python -m kv_cache_quantization_amd.build)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
+    sig = {
+        "pq_abi_version": ([], I),
+        "pq_strerror": ([I], ctypes.c_char_p),
+        "pq_last_hip_error": ([], I),
+        "pq_codebook": ([I, D, D, D], I),
+        "pq_quantize": ([I, I, I, P, L, P, I, P, P, P, P, P, P], I),
+        "pq_dequantize": ([I, I, P, P, L, P, I, P, P], I),
+        "qjl_sketch": ([I, I, P, L, P, P, P, P], I),
+        "qjl_project": ([I, I, P, L, P, P, P], I),
+        "qjl_score": ([I, I, I, I, L, P, P, P, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_quantize",
+           "pq_dequantize", "qjl_sketch", "qjl_project", "qjl_score")
+
+
+def lib():
+    """The loaded ctypes library (for tests of the raw C ABI)."""
+    return _lib
+
+
+def _check(status, where):
+    if status != PQ_OK:
+        raise PQError(status, where)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtypes):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def codebook(bits):
+    """(centroids, boundaries, mse) of the library's Lloyd-Max N(0,1) quantizer (host)."""
+    L = 1 << bits
+    c = (ctypes.c_double * L)()
+    b = (ctypes.c_double * max(L - 1, 1))()
+    mse = ctypes.c_double()
+    _check(_lib.pq_codebook(bits, c, b, ctypes.byref(mse)), "pq_codebook")
+    return list(c), list(b)[:L - 1], mse.value
+
+
+def quantize(x, d, bits, signs, proj=None, out=None):
+    """Quantize the contiguous d-element blocks of ``x`` (fp32 or bf16).
+
+    Returns (codes uint8 [n, d], norms fp16 [n], qjl_bits uint8 [n, m/8] or None,
+    rnorms fp16 [n] or None).  ``proj`` (bf16 [m, d]) turns on the QJL residual stage.
+    ``out`` may hold preallocated (codes, norms, qjl_bits, rnorms).
+    """
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(signs, "signs", (torch.uint8,))
+    if x.numel() % d:
+        raise ValueError("x.numel() must be a multiple of d")
+    n = x.numel() // d
+    m = 0
+    if proj is not None:
+        _dev(proj, "proj", (torch.bfloat16,))
+        m = proj.shape[0]
+    if out is None:
+        codes = torch.empty((n, d), dtype=torch.uint8, device=x.device)
+        norms = torch.empty((n,), dtype=torch.float16, device=x.device)
+        qb = torch.empty((n, m // 8), dtype=torch.uint8, device=x.device) if m else None
+        rn = torch.empty((n,), dtype=torch.float16, device=x.device) if m else None
+    else:
+        codes, norms, qb, rn = out
+    dt = PQ_BF16 if x.dtype == torch.bfloat16 else PQ_F32
+    _check(_lib.pq_quantize(d, bits, dt, _ptr(x), n, _ptr(signs), m, _ptr(proj), _ptr(codes), _ptr(norms),
+                            _ptr(qb), _ptr(rn), _stream()), "pq_quantize")
+    return codes, norms, qb, rn
+
+
+def dequantize(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None):
+    """Reconstruct blocks from codes (uint8 [n, d]) and fp16 norms; returns [n, d]."""
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(norms, "norms", (torch.float16,))
+    _dev(signs, "signs", (torch.uint8,))
+    n = codes.numel() // d
+    if out is None:
+        out = torch.empty((n, d), dtype=out_dtype, device=codes.device)
+    _dev(out, "out", (torch.float32, torch.bfloat16))
+    dt = PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32
+    _check(_lib.pq_dequantize(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs), dt, _ptr(out), _stream()),
+           "pq_dequantize")
+    return out
+
+
+def qjl_sketch(keys, proj, out=None):
+    """keys bf16 [..., d]; returns (bits uint8 [n, m/8], norms fp16 [n])."""
+    _dev(keys, "keys", (torch.bfloat16,))
+    _dev(proj, "proj", (torch.bfloat16,))
+    m, d = proj.shape
+    n = keys.numel() // d
+    if out is None:
+        bits = torch.empty((n, m // 8), dtype=torch.uint8, device=keys.device)
+        norms = torch.empty((n,), dtype=torch.float16, device=keys.device)
+    else:
+        bits, norms = out
+    _check(_lib.qjl_sketch(d, m, _ptr(keys), n, _ptr(proj), _ptr(bits), _ptr(norms), _stream()), "qjl_sketch")
+    return bits, norms
+
+
+def qjl_project(q, proj, out=None):
+    """Project queries q (bf16 [..., d]) through G: fp32 [n_q, m]."""
+    _dev(q, "q", (torch.bfloat16,))
+    _dev(proj, "proj", (torch.bfloat16,))
+    m, d = proj.shape
+    nq = q.numel() // d
+    if out is None:
+        out = torch.empty((nq, m), dtype=torch.float32, device=q.device)
+    _check(_lib.qjl_project(d, m, _ptr(q), nq, _ptr(proj), _ptr(out), _stream()), "qjl_project")
+    return out
+
+
+def qjl_score(sq, bits, norms, batch, kv_heads, q_heads, n_keys, out=None):
+    """QJL scores [batch, q_heads, n_keys] fp32 from projected queries and packed key bits."""
+    _dev(sq, "sq", (torch.float32,))
+    _dev(bits, "bits", (torch.uint8,))
+    _dev(norms, "norms", (torch.float16,))
+    m = sq.shape[-1]
+    if out is None:
+        out = torch.empty((batch, q_heads, n_keys), dtype=torch.float32, device=sq.device)
+    _check(_lib.qjl_score(m, batch, kv_heads, q_heads, n_keys, _ptr(sq), _ptr(bits), _ptr(norms), _ptr(out),
+                          _stream()), "qjl_score")
+    return out

@@ -1,0 +1,277 @@
+// C ABI of the codec library: argument validation, the Lloyd-Max codebook,
+// the search-grid geometry and kernel launches.  See include/pq.h for the
+// contract of every entry point.
+#include "../../include/pq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "pq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return PQ_OK;
+  g_last_hip_error = (int)e;
+  return PQ_EHIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_d(int d) {
+  if (!is_pow2(d)) return PQ_EINVAL;
+  if (d < 64 || d > 512) return PQ_EUNSUPPORTED;
+  return PQ_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Lloyd-Max quantizer for N(0,1) (eliza quantization README, PolarQuant, "Algorithm in one
+// paragraph"): centroids are the conditional means of their cells, boundaries the
+// midpoints of adjacent centroids; iterated in double to a fixed point.  The start is the
+// high-resolution optimum (point density proportional to pdf^(1/3), i.e. centroids at the
+// quantiles of N(0, 3)), which is close to the fixed point for every bit width.
+// ------------------------------------------------------------------------------------------
+struct Codebook {
+  std::vector<double> c, beta;
+  double mse = 0.0;
+};
+
+double gauss_pdf(double x) { return std::exp(-0.5 * x * x) * 0.3989422804014327; }
+
+// P(lo < X <= hi) for X ~ N(0,1), accurate in both tails
+double gauss_mass(double lo, double hi) {
+  const double k = 0.7071067811865476;
+  if (lo >= 0.0) return 0.5 * (std::erfc(lo * k) - std::erfc(hi * k));
+  if (hi <= 0.0) return 0.5 * (std::erfc(-hi * k) - std::erfc(-lo * k));
+  return 1.0 - 0.5 * std::erfc(-lo * k) - 0.5 * std::erfc(hi * k);
+}
+
+double gauss_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 200; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (gauss_mass(-INFINITY, mid) < p) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+Codebook solve_codebook(int bits) {
+  const int L = 1 << bits;
+  Codebook cb;
+  cb.c.resize(L);
+  for (int k = 0; k < L; ++k) cb.c[k] = std::sqrt(3.0) * gauss_quantile((k + 0.5) / L);
+  std::vector<double> beta(L - 1), cn(L), mass(L);
+  for (int it = 0; it < 4000000; ++it) {
+    for (int k = 0; k + 1 < L; ++k) beta[k] = 0.5 * (cb.c[k] + cb.c[k + 1]);
+    double step = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const double lo = k == 0 ? -INFINITY : beta[k - 1];
+      const double hi = k == L - 1 ? INFINITY : beta[k];
+      mass[k] = gauss_mass(lo, hi);
+      const double num = (k == 0 ? 0.0 : gauss_pdf(lo)) - (k == L - 1 ? 0.0 : gauss_pdf(hi));
+      cn[k] = num / mass[k];
+      step = std::max(step, std::fabs(cn[k] - cb.c[k]));
+    }
+    cb.c.swap(cn);
+    if (step < 1e-13) break;
+  }
+  for (int k = 0; k < L / 2; ++k) {            // exact symmetry of the N(0,1) fixed point
+    const double v = 0.5 * (cb.c[L - 1 - k] - cb.c[k]);
+    cb.c[k] = -v;
+    cb.c[L - 1 - k] = v;
+  }
+  cb.beta.resize(L - 1);
+  for (int k = 0; k + 1 < L; ++k) cb.beta[k] = 0.5 * (cb.c[k] + cb.c[k + 1]);
+  double acc = 0.0;
+  for (int k = 0; k < L; ++k) {
+    const double lo = k == 0 ? -INFINITY : cb.beta[k - 1];
+    const double hi = k == L - 1 ? INFINITY : cb.beta[k];
+    acc += gauss_mass(lo, hi) * cb.c[k] * cb.c[k];
+  }
+  cb.mse = 1.0 - acc;
+  return cb;
+}
+
+std::once_flag g_cb_once[pqi::kMaxBits + 1];
+Codebook g_cb[pqi::kMaxBits + 1];
+
+const Codebook& codebook(int bits) {
+  std::call_once(g_cb_once[bits], [bits] { g_cb[bits] = solve_codebook(bits); });
+  return g_cb[bits];
+}
+
+// fp32 tables and search-grid geometry for the kernels
+pqi::CodecTables make_tables(int bits) {
+  const Codebook& cb = codebook(bits);
+  pqi::CodecTables t;
+  std::memset(&t, 0, sizeof(t));
+  const int L = 1 << bits;
+  for (int k = 0; k < L; ++k) t.cent[k] = (float)cb.c[k];
+  for (int k = 0; k + 1 < L; ++k) t.beta[k] = (float)cb.beta[k];
+  t.nbound = L - 1;
+  double w, Y;
+  if (L == 2) {
+    w = 0.5;
+    Y = 2.0;
+  } else {
+    double gap = INFINITY;
+    for (int k = 0; k + 2 < L; ++k) gap = std::min(gap, (double)t.beta[k + 1] - (double)t.beta[k]);
+    w = gap / 4.0;
+    Y = (double)t.beta[L - 2] + 4.0 * w;
+  }
+  int ncell = (int)std::ceil(2.0 * Y / w);
+  ncell += ncell & 1;                 // keep the following LDS arrays 16-byte aligned
+  t.ncell = ncell;
+  t.cell_lo = (float)(-Y);
+  t.cell_w = (float)w;
+  t.cell_inv_w = (float)(1.0 / w);
+  t.cell_off = (float)(Y / w);
+  return t;
+}
+
+int launch_cfg(pqi::LaunchCfg* c) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  e = hipDeviceGetAttribute(&c->cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_status(e);
+  e = hipDeviceGetAttribute(&c->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return hip_status(e);
+  return PQ_OK;
+}
+
+constexpr int64_t kMaxElems = INT64_MAX / 8;
+
+}  // namespace
+
+extern "C" {
+
+int pq_abi_version(void) { return PQ_ABI_VERSION; }
+
+const char* pq_strerror(int status) {
+  switch (status) {
+    case PQ_OK: return "ok";
+    case PQ_EINVAL: return "invalid argument (pointer, size, alignment, dtype or parameter)";
+    case PQ_EUNSUPPORTED: return "unsupported parameter combination";
+    case PQ_EHIP: return "HIP runtime error (see pq_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+int pq_last_hip_error(void) { return g_last_hip_error; }
+
+int pq_codebook(int bits, double* centroids, double* boundaries, double* mse) {
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  const Codebook& cb = codebook(bits);
+  if (centroids) std::copy(cb.c.begin(), cb.c.end(), centroids);
+  if (boundaries) std::copy(cb.beta.begin(), cb.beta.end(), boundaries);
+  if (mse) *mse = cb.mse;
+  return PQ_OK;
+}
+
+int pq_quantize(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
+                int m, const uint16_t* proj, uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits,
+                uint16_t* rnorms, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (in_dtype != PQ_F32 && in_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (m < 0 || (m % 8) != 0) return PQ_EINVAL;
+  if (m > 1024) return PQ_EUNSUPPORTED;
+  if (m == 0 && (proj || qjl_bits || rnorms)) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!x || !signs || !codes || !norms) return PQ_EINVAL;
+  if (m > 0 && (!proj || !qjl_bits || !rnorms)) return PQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(norms, 2)) return PQ_EINVAL;
+  if (m > 0 && (!aligned(proj, 16) || !aligned(rnorms, 2))) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::QuantArgs a;
+  a.x = x; a.n_blocks = n_blocks; a.signs = signs; a.proj = proj; a.codes = codes; a.norms = norms;
+  a.qbits = qjl_bits; a.rnorms = rnorms; a.m = m; a.t = make_tables(bits);
+  return hip_status(pqi::launch_quantize(d, in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+int pq_dequantize(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                  const uint8_t* signs, int out_dtype, void* out, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (out_dtype != PQ_F32 && out_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!codes || !norms || !signs || !out) return PQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::DequantArgs a;
+  a.codes = codes; a.norms = norms; a.n_blocks = n_blocks; a.signs = signs; a.out = out;
+  a.t = make_tables(bits);
+  return hip_status(pqi::launch_dequantize(d, out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+int qjl_sketch(int d, int m, const uint16_t* keys, int64_t n_keys, const uint16_t* proj, uint8_t* bits,
+               uint16_t* norms, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (m <= 0 || (m % 8) != 0) return PQ_EINVAL;
+  if (m > 1024) return PQ_EUNSUPPORTED;
+  if (n_keys < 0 || n_keys > kMaxElems / d) return PQ_EINVAL;
+  if (n_keys == 0) return PQ_OK;
+  if (!keys || !proj || !bits || !norms) return PQ_EINVAL;
+  if (!aligned(keys, 16) || !aligned(proj, 16) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::SketchArgs a;
+  a.keys = keys; a.n_keys = n_keys; a.proj = proj; a.bits = bits; a.norms = norms; a.m = m;
+  return hip_status(pqi::launch_sketch(d, a, cfg, (hipStream_t)stream));
+}
+
+int qjl_project(int d, int m, const uint16_t* q, int64_t n_q, const uint16_t* proj, float* sq,
+                void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (m <= 0 || (m % 8) != 0) return PQ_EINVAL;
+  if (m > 1024) return PQ_EUNSUPPORTED;
+  if (n_q < 0 || n_q > (int64_t)INT32_MAX / m) return PQ_EINVAL;
+  if (n_q == 0) return PQ_OK;
+  if (!q || !proj || !sq) return PQ_EINVAL;
+  if (!aligned(q, 2) || !aligned(proj, 2) || !aligned(sq, 4)) return PQ_EINVAL;
+  pqi::ProjectArgs a;
+  a.q = q; a.n_q = n_q; a.proj = proj; a.sq = sq; a.d = d; a.m = m;
+  return hip_status(pqi::launch_project(a, (hipStream_t)stream));
+}
+
+int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
+              const uint8_t* bits, const uint16_t* norms, float* scores, void* stream) {
+  if (m <= 0 || (m % 8) != 0) return PQ_EINVAL;
+  if ((m % 64) != 0 || m > 1024) return PQ_EUNSUPPORTED;
+  if (batch < 0 || kv_heads <= 0 || q_heads <= 0 || n_keys < 0) return PQ_EINVAL;
+  if (q_heads % kv_heads != 0) return PQ_EINVAL;
+  if (q_heads / kv_heads > 4) return PQ_EUNSUPPORTED;
+  if ((int64_t)batch * kv_heads > INT32_MAX / 1024) return PQ_EINVAL;
+  if (n_keys > kMaxElems / ((int64_t)batch * q_heads + 1)) return PQ_EINVAL;
+  if (batch == 0 || n_keys == 0) return PQ_OK;
+  if (!sq || !bits || !norms || !scores) return PQ_EINVAL;
+  if (!aligned(sq, 4) || !aligned(scores, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  int st2 = launch_cfg(&cfg);
+  if (st2) return st2;
+  pqi::ScoreArgs a;
+  a.sq = sq; a.bits = bits; a.norms = norms; a.scores = scores; a.n_keys = n_keys; a.m = m;
+  a.batch = batch; a.kv_heads = kv_heads; a.q_heads = q_heads;
+  return hip_status(pqi::launch_score(a, cfg, (hipStream_t)stream));
+}
+
+}  // extern "C"

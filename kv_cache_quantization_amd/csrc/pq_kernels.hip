@@ -1,0 +1,656 @@
+// gfx950 kernels of the block codec and the QJL sketch.
+//
+// Every kernel is persistent: each wave walks over tiles of 16 blocks (keys)
+// with a grid stride, so the per-workgroup set-up (codebook, search grid and
+// projection matrix staged in LDS) is paid once per workgroup.
+#include "pq_device.h"
+#include "pq_internal.h"
+
+using namespace pqd;
+using pqi::CodecTables;
+
+namespace {
+
+constexpr int kThreads = 256;             // 4 waves per workgroup
+constexpr int kWaves = kThreads / 64;
+
+// ------------------------------------------------------------------------------------------
+// LDS set-up shared by quantize and dequantize
+// ------------------------------------------------------------------------------------------
+__device__ void build_search_grid(const CodecTables& t, uint2* tab) {
+  for (int k = threadIdx.x; k < t.ncell; k += blockDim.x) {
+    const float c = t.cell_lo + ((float)k + 0.5f) * t.cell_w;
+    int best = 0;
+    float bd = fabsf(t.beta[0] - c);
+    for (int j = 1; j < t.nbound; ++j) {
+      const float dd = fabsf(t.beta[j] - c);
+      if (dd < bd) { bd = dd; best = j; }
+    }
+    tab[k] = make_uint2(__float_as_uint(t.beta[best]), (uint32_t)best);
+  }
+}
+
+__device__ void copy_centroids(const CodecTables& t, float* cent) {
+  for (int k = threadIdx.x; k <= t.nbound; k += blockDim.x) cent[k] = t.cent[k];
+}
+
+// Projection matrix G (m x D bf16) staged in LDS, rows >= m zero.  16-byte chunk c
+// of row n is stored at chunk position c ^ (n & SW) so that the 16 rows read by
+// one 16-lane group hit 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int g_swizzle(int n, int c) {
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int SW = CPR < 16 ? CPR - 1 : 15;
+  return n * CPR + (c ^ (n & SW));
+}
+
+template <int D>
+__device__ void stage_projection(const uint16_t* proj, int m, int m_pad, uint4* gl) {
+  constexpr int CPR = D / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(proj);
+  for (int i = threadIdx.x; i < m_pad * CPR; i += blockDim.x) {
+    const int n = i / CPR, c = i % CPR;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < m) w = src[i];
+    gl[g_swizzle<D>(n, c)] = w;
+  }
+}
+
+// fp16 copy of G scaled by 2^10 (exact for |G| >= 2^-24; the bf16 mantissa fits in fp16)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w) {
+  const _Float16 lo = (_Float16)(bf16_lo(w) * 1024.0f);
+  const _Float16 hi = (_Float16)(bf16_hi(w) * 1024.0f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+template <int D>
+__device__ void stage_projection_f16(const uint16_t* proj, int m, int m_pad, uint4* gl) {
+  constexpr int CPR = D / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(proj);
+  for (int i = threadIdx.x; i < m_pad * CPR; i += blockDim.x) {
+    const int n = i / CPR, c = i % CPR;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < m) {
+      const uint4 b = src[i];
+      w = make_uint4(bf16x2_to_f16x2_scaled(b.x), bf16x2_to_f16x2_scaled(b.y),
+                     bf16x2_to_f16x2_scaled(b.z), bf16x2_to_f16x2_scaled(b.w));
+    }
+    gl[g_swizzle<D>(n, c)] = w;
+  }
+}
+
+template <int D, bool G_LDS>
+__device__ __forceinline__ f16x8 load_gfrag_f16(const uint4* gl, const uint16_t* proj, int m, int row, int col8) {
+  uint4 w;
+  if constexpr (G_LDS) {
+    w = gl[g_swizzle<D>(row, col8)];
+  } else {
+    w = make_uint4(0, 0, 0, 0);
+    if (row < m) {
+      const uint4 b = reinterpret_cast<const uint4*>(proj)[row * (D / 8) + col8];
+      w = make_uint4(bf16x2_to_f16x2_scaled(b.x), bf16x2_to_f16x2_scaled(b.y),
+                     bf16x2_to_f16x2_scaled(b.z), bf16x2_to_f16x2_scaled(b.w));
+    }
+  }
+  return __builtin_bit_cast(f16x8, w);
+}
+
+template <int D, bool G_LDS>
+__device__ __forceinline__ bf16x8 load_gfrag(const uint4* gl, const uint16_t* proj, int m, int row, int col8) {
+  uint4 w;
+  if constexpr (G_LDS) {
+    w = gl[g_swizzle<D>(row, col8)];
+  } else {
+    w = make_uint4(0, 0, 0, 0);
+    if (row < m) w = reinterpret_cast<const uint4*>(proj)[row * (D / 8) + col8];
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Write the sign bits of one 16-column N tile for the 16 block rows of a wave.
+// acc[i] of lane l is P[4 (l>>4) + i][16 nt + (l & 15)]; a ballot per i gives,
+// in bits 16 g .. 16 g + 15, the 16 signs of block row 4 g + i, which are the
+// little-endian 16-bit value at byte 2 nt of that row (bit j <-> column j, LSB first).
+__device__ __forceinline__ void store_sign_tile(const f32x4& acc, int lane, int64_t row0, int64_t nrows,
+                                                uint8_t* bits, int mb, int nt) {
+  const uint64_t b0 = __ballot(acc[0] > 0.0f);
+  const uint64_t b1 = __ballot(acc[1] > 0.0f);
+  const uint64_t b2 = __ballot(acc[2] > 0.0f);
+  const uint64_t b3 = __ballot(acc[3] > 0.0f);
+  if (lane < 16) {
+    const int i = lane & 3, gg = lane >> 2;
+    const uint64_t b = i == 0 ? b0 : i == 1 ? b1 : i == 2 ? b2 : b3;
+    const uint32_t chunk = (uint32_t)(b >> (16 * gg)) & 0xffffu;
+    const int64_t row = row0 + lane;
+    if (row < nrows) {
+      uint8_t* dst = bits + row * (int64_t)mb + 2 * nt;
+      dst[0] = (uint8_t)chunk;
+      if (2 * nt + 1 < mb) dst[1] = (uint8_t)(chunk >> 8);
+    }
+  }
+}
+
+template <int D>
+__host__ __device__ constexpr int cperm_inv(int o) {
+  for (int j = 0; j < D / 4; ++j)
+    if (cperm<D>(j) == o) return j;
+  return -1;
+}
+
+// ------------------------------------------------------------------------------------------
+// Quantize (+ optional QJL residual stage)
+// ------------------------------------------------------------------------------------------
+template <int D, bool IN_BF16, bool QJL, bool G_LDS>
+__global__ __launch_bounds__(kThreads) void pq_quantize_kernel(const pqi::QuantArgs a) {
+  constexpr int E = D / 4;
+  constexpr int KS = D / 32;                         // MFMA K steps per block
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint2* tab = reinterpret_cast<uint2*>(smem);
+  float* cent = reinterpret_cast<float*>(smem + a.t.ncell * 8);
+  uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * 8 + 1024);
+
+  const int m = a.m;
+  const int m_pad = (m + 15) & ~15;
+  build_search_grid(a.t, tab);
+  copy_centroids(a.t, cent);
+  if constexpr (QJL && G_LDS) stage_projection_f16<D>(a.proj, m, m_pad, gl);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+
+  // rotation signs of this lane's elements in the load layout, as xor masks
+  uint32_t smask[E / 2];
+#pragma unroll
+  for (int p = 0; p < E / 2; ++p) {
+    const int e = load_e(g, 2 * p);
+    const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
+    const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
+    smask[p] = (s0 << 15) | (s1 << 31);
+  }
+
+  const float inv_w = a.t.cell_inv_w, off = a.t.cell_off;
+  const float top = (float)(a.t.ncell - 1);
+  const int64_t n_blocks = a.n_blocks;
+  const int64_t n_tiles = (n_blocks + 15) >> 4;
+  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+  const int mb = m >> 3;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+
+  for (int64_t T = wave_id; T < n_tiles; T += n_waves) {
+    const int64_t blk = T * 16 + r;
+    const bool valid = blk < n_blocks;
+    float v[E];
+    float ss;
+    if constexpr (IN_BF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + blk * D);
+#pragma unroll
+      for (int s = 0; s < E / 8; ++s) {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (valid) w = src[4 * s + g];
+        w.x ^= smask[4 * s + 0]; w.y ^= smask[4 * s + 1];
+        w.z ^= smask[4 * s + 2]; w.w ^= smask[4 * s + 3];
+        v[8 * s + 0] = bf16_lo(w.x); v[8 * s + 1] = bf16_hi(w.x);
+        v[8 * s + 2] = bf16_lo(w.y); v[8 * s + 3] = bf16_hi(w.y);
+        v[8 * s + 4] = bf16_lo(w.z); v[8 * s + 5] = bf16_hi(w.z);
+        v[8 * s + 6] = bf16_lo(w.w); v[8 * s + 7] = bf16_hi(w.w);
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + blk * D);
+#pragma unroll
+      for (int s = 0; s < E / 8; ++s) {
+        float4 w0 = make_float4(0, 0, 0, 0), w1 = w0;
+        if (valid) { w0 = src[8 * s + 2 * g]; w1 = src[8 * s + 2 * g + 1]; }
+        const float f[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t sm = (t & 1) ? (smask[4 * s + t / 2] & 0x80000000u) : (smask[4 * s + t / 2] << 16);
+          v[8 * s + t] = __uint_as_float(__float_as_uint(f[t]) ^ sm);
+        }
+      }
+    }
+    ss = tree_sumsq<E>(v);
+
+    wht_forward<D>(v);                     // v = z = H (D x), unnormalised
+
+    ss = sum4(ss);
+    const float n = sqrtf(ss);
+    const uint16_t n16 = f32_to_f16(n);
+    const float inv_n = n > 0.0f ? 1.0f / n : 0.0f;
+    // residual rho = z - n16 c[code] (= H D r) formed with one rounding and rescaled by a
+    // power of two so that it sits near 1 for the fp16 split
+    float rscale = 1.0f, nsc = 0.0f;
+    if constexpr (QJL) {
+      if (n > 0.0f) {
+        rscale = ldexpf(1.0f, -ilogbf(n));
+        nsc = f16_to_f32(n16) * rscale;
+      }
+    }
+
+    uint32_t cw[E / 4];
+#pragma unroll
+    for (int w = 0; w < E / 4; ++w) cw[w] = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float y = v[j] * inv_n;
+      const float tc = fminf(fmaxf(fmaf(y, inv_w, off), 0.0f), top);
+      const uint2 te = tab[(int)tc];
+      const uint32_t code = te.y + (y > __uint_as_float(te.x) ? 1u : 0u);
+      const int o = cperm<D>(j);
+      cw[o >> 2] |= code << (8 * (o & 3));
+      if constexpr (QJL) v[j] = fmaf(-nsc, cent[code], v[j] * rscale);
+    }
+    if (valid) {
+      uint4* dst = reinterpret_cast<uint4*>(a.codes + blk * D + E * qpos<D>(g));
+#pragma unroll
+      for (int w = 0; w < E / 16; ++w)
+        dst[w] = make_uint4(cw[4 * w + 0], cw[4 * w + 1], cw[4 * w + 2], cw[4 * w + 3]);
+      if (g == 0) a.norms[blk] = n16;
+    }
+
+    if constexpr (QJL) {
+      const float rss = sum4(tree_sumsq<E>(v));
+      const float rn = sqrtf(rss) / rscale * inv_sqrt_d;    // ||r|| = ||H D r|| / sqrt(d)
+      if (valid && g == 0) a.rnorms[blk] = f32_to_f16(rn);
+      // residual split into fp16 high and low parts (22 significant bits), MFMA A fragments
+      f16x8 ahi[KS], alo[KS];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x = v[cperm_inv<D>(8 * k + t)];
+          const _Float16 h = (_Float16)x;
+          ahi[k][t] = h;
+          alo[k][t] = (_Float16)(x - (float)h);
+        }
+      }
+      const int colbase = E * qpos<D>(g);   // element offset of this quarter's run
+      for (int nt = 0; nt < (m_pad >> 4); ++nt) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const int row = 16 * nt + r;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const f16x8 b = load_gfrag_f16<D, G_LDS>(gl, a.proj, m, row, (colbase >> 3) + k);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[k], b, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[k], b, acc, 0, 0, 0);
+        }
+        store_sign_tile(acc, lane, T * 16, n_blocks, a.qbits, mb, nt);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Dequantize
+// ------------------------------------------------------------------------------------------
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
+  constexpr int E = D / 4;
+  __shared__ float cent[1 << pqi::kMaxBits];
+  copy_centroids(a.t, cent);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+
+  // output sign masks: register chunk s holds elements 8 g + dq_out_chunk(s) + 0..7
+  uint32_t smask[E / 2];
+#pragma unroll
+  for (int p = 0; p < E / 2; ++p) {
+    const int e = 8 * g + dq_out_chunk<D>(p >> 2) + 2 * (p & 3);
+    const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
+    const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
+    smask[p] = OUT_BF16 ? ((s0 << 15) | (s1 << 31)) : (s0 | (s1 << 1));
+  }
+
+  const int64_t n_blocks = a.n_blocks;
+  const int64_t n_tiles = (n_blocks + 15) >> 4;
+  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+
+  for (int64_t T = wave_id; T < n_tiles; T += n_waves) {
+    const int64_t blk = T * 16 + r;
+    const bool valid = blk < n_blocks;
+    float v[E];
+    float scale = 0.0f;
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(a.codes + blk * D + E * g);
+#pragma unroll
+      for (int w = 0; w < E / 16; ++w) {
+        uint4 q = make_uint4(0, 0, 0, 0);
+        if (valid) q = src[w];
+        const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) v[16 * w + 4 * u + b] = cent[(qq[u] >> (8 * b)) & 0xffu];
+      }
+      if (valid) scale = f16_to_f32(a.norms[blk]) * (1.0f / (float)D);
+    }
+
+    wht_dequant<D>(v);
+
+    if (valid) {
+      if constexpr (OUT_BF16) {
+        uint16_t* out = static_cast<uint16_t*>(a.out) + blk * D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < E / 8; ++s) {
+          uint4 w;
+          w.x = pack_bf16x2(v[8 * s + 0] * scale, v[8 * s + 1] * scale) ^ smask[4 * s + 0];
+          w.y = pack_bf16x2(v[8 * s + 2] * scale, v[8 * s + 3] * scale) ^ smask[4 * s + 1];
+          w.z = pack_bf16x2(v[8 * s + 4] * scale, v[8 * s + 5] * scale) ^ smask[4 * s + 2];
+          w.w = pack_bf16x2(v[8 * s + 6] * scale, v[8 * s + 7] * scale) ^ smask[4 * s + 3];
+          *reinterpret_cast<uint4*>(out + dq_out_chunk<D>(s)) = w;
+        }
+      } else {
+        float* out = static_cast<float*>(a.out) + blk * D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < E / 8; ++s) {
+          float f[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t sb = (smask[4 * s + t / 2] >> (t & 1)) & 1u;
+            f[t] = __uint_as_float(__float_as_uint(v[8 * s + t] * scale) ^ (sb << 31));
+          }
+          float4* o4 = reinterpret_cast<float4*>(out + dq_out_chunk<D>(s));
+          o4[0] = make_float4(f[0], f[1], f[2], f[3]);
+          o4[1] = make_float4(f[4], f[5], f[6], f[7]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// QJL key sketch: norm + sign(G k), keys feed the MFMA directly (bf16 products are exact)
+// ------------------------------------------------------------------------------------------
+template <int D, bool G_LDS>
+__global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchArgs a) {
+  constexpr int KS = D / 32;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint4* gl = reinterpret_cast<uint4*>(smem);
+  const int m = a.m, m_pad = (m + 15) & ~15, mb = m >> 3;
+  if constexpr (G_LDS) {
+    stage_projection<D>(a.proj, m, m_pad, gl);
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n_keys = a.n_keys;
+  const int64_t n_tiles = (n_keys + 15) >> 4;
+  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+
+  for (int64_t T = wave_id; T < n_tiles; T += n_waves) {
+    const int64_t key = T * 16 + r;
+    const bool valid = key < n_keys;
+    bf16x8 kf[KS];
+    float ss = 0.0f;
+    const uint4* src = reinterpret_cast<const uint4*>(a.keys + key * D);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (valid) w = src[4 * s + g];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float lo = bf16_lo(ww[u]), hi = bf16_hi(ww[u]);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+      kf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+    ss = sum4(ss);
+    if (valid && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
+    for (int nt = 0; nt < (m_pad >> 4); ++nt) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int row = 16 * nt + r;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 b = load_gfrag<D, G_LDS>(gl, a.proj, m, row, 4 * s + g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], b, acc, 0, 0, 0);
+      }
+      store_sign_tile(acc, lane, T * 16, n_keys, a.bits, mb, nt);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Query projection sq = G q (fp32), one thread per output value
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void qjl_project_kernel(const pqi::ProjectArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.n_q * a.m) return;
+  const int64_t qi = idx / a.m;
+  const int n = (int)(idx % a.m);
+  const uint16_t* q = a.q + qi * a.d;
+  const uint16_t* gr = a.proj + (int64_t)n * a.d;
+  float acc = 0.0f;
+  for (int e = 0; e < a.d; ++e) acc = fmaf(bf16_to_f32(gr[e]), bf16_to_f32(q[e]), acc);
+  a.sq[idx] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// QJL score for grouped-query attention on the int8 matrix cores.
+//
+// sum_i (2 b_i - 1) sq_i = 2 sum_i b_i sq_i - sum_i sq_i.  Each projected query
+// is quantized to integers Q_i = rint(sq_i / s), s = max|sq| / 2080768, and
+// split into three int8 limbs Q = 16384 h2 + 128 h1 + h0; the bit vectors,
+// expanded to bytes {0, 1}, meet the limbs in v_mfma_i32_16x16x64_i8 with exact
+// int32 accumulation.  A rows: 4 query heads x 4 slots (h2, h1, h0, 0); B columns:
+// 16 keys.  Lane group gq holds bits [m/4 gq, m/4 (gq+1)) of its key.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t spread_nibble(uint32_t nib) {
+  // 4 bits -> 4 bytes of value 0/1 (bit j -> byte j)
+  return (nib * 0x204081u) & 0x01010101u;
+}
+
+template <int KS>
+__global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArgs a, int chunks_per_group) {
+  constexpr int m = 64 * KS, mb = m >> 3;
+  const int group = a.q_heads / a.kv_heads;
+  const int grp = blockIdx.x / chunks_per_group;          // (batch, kv head) pair
+  const int chunk = blockIdx.x % chunks_per_group;
+  const int b = grp / a.kv_heads, gk = grp % a.kv_heads;
+
+  __shared__ float sqs[4][1024];
+  __shared__ float scl[4];
+  __shared__ double sumq[4];
+  for (int i = threadIdx.x; i < 4 * m; i += blockDim.x) {
+    const int hh = i / m, n = i % m;
+    sqs[hh][n] = hh < group ? a.sq[((int64_t)b * a.q_heads + gk * group + hh) * m + n] : 0.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    const int hh = threadIdx.x;
+    float amax = 0.0f;
+    for (int n = 0; n < m; ++n) amax = fmaxf(amax, fabsf(sqs[hh][n]));
+    const float s = amax / 2080768.0f;
+    double sq_int = 0.0;                                  // exact: integers, |sum| < 2^31
+    for (int n = 0; n < m; ++n) sq_int += s > 0.0f ? (double)rintf(sqs[hh][n] / s) : 0.0;
+    scl[threadIdx.x] = s;
+    sumq[threadIdx.x] = sq_int;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, gq = lane >> 4;
+  // A fragments in registers: row r = 4 hh + limb
+  const int hh = r >> 2, limb = r & 3;
+  const float s_h = scl[hh];
+  i32x4 af[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    uint32_t wd[4];
+    for (int u = 0; u < 4; ++u) {
+      uint32_t word = 0;
+      for (int bb = 0; bb < 4; ++bb) {
+        const int i = (m >> 2) * gq + 16 * k + 4 * u + bb;
+        int q = s_h > 0.0f ? (int)rintf(sqs[hh][i] / s_h) : 0;
+        const int h2 = (int)rintf((float)q / 16384.0f);
+        const int rem = q - 16384 * h2;
+        const int h1 = (int)rintf((float)rem / 128.0f);
+        const int h0 = rem - 128 * h1;
+        const int lv = limb == 0 ? h2 : limb == 1 ? h1 : limb == 2 ? h0 : 0;
+        word |= ((uint32_t)(lv & 0xff)) << (8 * bb);
+      }
+      wd[u] = word;
+    }
+    af[k] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+  }
+
+  const int64_t T = a.n_keys;
+  const int64_t n_tiles = (T + 15) >> 4;
+  const uint8_t* bits = a.bits + (int64_t)grp * T * mb;
+  const uint16_t* norms = a.norms + (int64_t)grp * T;
+  const float c0 = 1.2533141373155003f / (float)m;       // sqrt(pi/2) / m
+  const int lane_bytes = mb >> 2;                          // bytes of one lane group (m/32)
+  const int h_out = gk * group + gq;
+  float* out = a.scores + ((int64_t)b * a.q_heads + h_out) * T;
+  const float s_out = scl[gq & 3];
+  const double sumq_out = sumq[gq & 3];
+
+  for (int64_t tile = (int64_t)chunk * kWaves + (threadIdx.x >> 6); tile < n_tiles;
+       tile += (int64_t)chunks_per_group * kWaves) {
+    const int64_t key = tile * 16 + r;
+    const bool valid = key < T;
+    i32x4 acc = {0, 0, 0, 0};
+    const uint8_t* kb = bits + key * mb + lane_bytes * gq;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint32_t w16 = 0;
+      if (valid) w16 = (uint32_t)kb[2 * k] | ((uint32_t)kb[2 * k + 1] << 8);
+      const i32x4 bf = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
+                        (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[k], bf, acc, 0, 0, 0);
+    }
+    // lane (gq, key r): acc[i] = sum_i bit * limb_i of head gq
+    if (valid && gq < group) {
+      const double S = 16384.0 * (double)acc[0] + 128.0 * (double)acc[1] + (double)acc[2];
+      const double nu = (double)f16_to_f32(norms[key]);
+      out[key] = (float)(nu * (double)c0 * (double)s_out * (2.0 * S - sumq_out));
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// launch helpers
+// ------------------------------------------------------------------------------------------
+int grid_for(int64_t n_tiles, const pqi::LaunchCfg& c, int per_cu) {
+  int64_t want = (n_tiles + kWaves - 1) / kWaves;
+  int64_t cap = (int64_t)c.cu_count * per_cu;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+template <int D>
+hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int m_pad = (a.m + 15) & ~15;
+  const size_t base = (size_t)a.t.ncell * 8 + 1024;
+  const size_t glb = (size_t)m_pad * D * 2;
+  const bool qjl = a.m > 0;
+  const bool g_lds = qjl && base + glb <= (size_t)c.max_lds && base + glb <= 65536;
+  const size_t lds = base + (g_lds ? glb : 0);
+  const int grid = grid_for(n_tiles, c, 8);
+  if (!qjl) {
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, false, false>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, false, false>), grid, kThreads, lds, s, a);
+  } else if (g_lds) {
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true>), grid, kThreads, lds, s, a);
+  } else {
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false>), grid, kThreads, lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dequantize_d(bool out_bf16, const pqi::DequantArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int grid = grid_for(n_tiles, c, 8);
+  if (out_bf16) hipLaunchKernelGGL((pq_dequantize_kernel<D, true>), grid, kThreads, 0, s, a);
+  else hipLaunchKernelGGL((pq_dequantize_kernel<D, false>), grid, kThreads, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
+  const int64_t n_tiles = (a.n_keys + 15) >> 4;
+  const int m_pad = (a.m + 15) & ~15;
+  const size_t glb = (size_t)m_pad * D * 2;
+  const bool g_lds = glb <= (size_t)c.max_lds && glb <= 65536;
+  const int grid = grid_for(n_tiles, c, 8);
+  if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true>), grid, kThreads, glb, s, a);
+  else hipLaunchKernelGGL((qjl_sketch_kernel<D, false>), grid, kThreads, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace pqi {
+
+hipError_t launch_quantize(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_quantize_d<64>(in_bf16, a, c, s);
+    case 128: return launch_quantize_d<128>(in_bf16, a, c, s);
+    case 256: return launch_quantize_d<256>(in_bf16, a, c, s);
+    case 512: return launch_quantize_d<512>(in_bf16, a, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequantize(int d, bool out_bf16, const DequantArgs& a, const LaunchCfg& c, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_dequantize_d<64>(out_bf16, a, c, s);
+    case 128: return launch_dequantize_d<128>(out_bf16, a, c, s);
+    case 256: return launch_dequantize_d<256>(out_bf16, a, c, s);
+    case 512: return launch_dequantize_d<512>(out_bf16, a, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_sketch(int d, const SketchArgs& a, const LaunchCfg& c, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_sketch_d<64>(a, c, s);
+    case 128: return launch_sketch_d<128>(a, c, s);
+    case 256: return launch_sketch_d<256>(a, c, s);
+    case 512: return launch_sketch_d<512>(a, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
+  const int64_t total = a.n_q * a.m;
+  const int grid = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(qjl_project_kernel, grid, 256, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s) {
+  const int groups = a.batch * a.kv_heads;
+  const int64_t n_tiles = (a.n_keys + 15) >> 4;
+  // enough workgroups to fill the chip, at most one wave per tile
+  int64_t per_group = ((int64_t)c.cu_count * 8 + groups - 1) / groups;
+  const int64_t max_per_group = (n_tiles + kWaves - 1) / kWaves;
+  if (per_group > max_per_group) per_group = max_per_group;
+  if (per_group < 1) per_group = 1;
+  const int grid = (int)(per_group * groups);
+  const int cpg = (int)per_group;
+  switch (a.m >> 6) {
+#define PQ_SCORE_CASE(K) \
+    case K: hipLaunchKernelGGL(qjl_score_kernel<K>, grid, kThreads, 0, s, a, cpg); break;
+    PQ_SCORE_CASE(1) PQ_SCORE_CASE(2) PQ_SCORE_CASE(3) PQ_SCORE_CASE(4)
+    PQ_SCORE_CASE(5) PQ_SCORE_CASE(6) PQ_SCORE_CASE(7) PQ_SCORE_CASE(8)
+    PQ_SCORE_CASE(9) PQ_SCORE_CASE(10) PQ_SCORE_CASE(11) PQ_SCORE_CASE(12)
+    PQ_SCORE_CASE(13) PQ_SCORE_CASE(14) PQ_SCORE_CASE(15) PQ_SCORE_CASE(16)
+#undef PQ_SCORE_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pqi

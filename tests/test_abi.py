@@ -1,0 +1,120 @@
+"""The C ABI: library loads, exports every declared symbol, validates arguments on
+the host and reports HIP failures (CPU only: no kernel is launched)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_quantization_amd as pq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", f)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", txt, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pq.lib()
+    declared = _declared()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(pq.EXPORTS) == set(declared)
+
+
+def test_abi_version_and_strerror():
+    lib = pq.lib()
+    assert lib.pq_abi_version() == 1
+    for st in range(5):
+        assert isinstance(lib.pq_strerror(st), bytes) and lib.pq_strerror(st)
+    assert lib.pq_strerror(0) == b"ok"
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6])
+def test_library_codebook_matches_oracle(bits):
+    c, b, mse = pq.codebook(bits)
+    oc, ob, om = oracle.lloyd_max.codebook(bits)
+    assert np.allclose(c, oc, atol=1e-9, rtol=0)
+    assert np.allclose(b, ob, atol=1e-9, rtol=0)
+    assert abs(mse - om) < 1e-9
+    # the fp32 tables the kernels use agree with the oracle's fp32 decision thresholds
+    assert np.array_equal(np.float32(b), np.float32(ob))
+
+
+def test_codebook_rejects_bad_bits():
+    lib = pq.lib()
+    D = ctypes.POINTER(ctypes.c_double)
+    assert lib.pq_codebook(0, D(), D(), D()) == pq.PQ_EINVAL
+    assert lib.pq_codebook(9, D(), D(), D()) == pq.PQ_EINVAL
+
+
+# Fake device pointers: never dereferenced, because validation fails before any HIP call.
+P16 = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x10002)
+NUL = ctypes.c_void_p(0)
+
+
+def _q(**kw):
+    a = dict(d=128, bits=4, dt=pq.PQ_BF16, x=P16, n=16, signs=P16, m=0, proj=NUL, codes=P16, norms=P16,
+             qb=NUL, rn=NUL)
+    a.update(kw)
+    return pq.lib().pq_quantize(a["d"], a["bits"], a["dt"], a["x"], a["n"], a["signs"], a["m"], a["proj"],
+                                a["codes"], a["norms"], a["qb"], a["rn"], NUL)
+
+
+@pytest.mark.parametrize("kw,st", [
+    (dict(d=96), pq.PQ_EINVAL), (dict(d=32), pq.PQ_EUNSUPPORTED), (dict(d=1024), pq.PQ_EUNSUPPORTED),
+    (dict(bits=0), pq.PQ_EINVAL), (dict(bits=9), pq.PQ_EINVAL), (dict(dt=7), pq.PQ_EINVAL),
+    (dict(n=-1), pq.PQ_EINVAL), (dict(x=NUL), pq.PQ_EINVAL), (dict(codes=NUL), pq.PQ_EINVAL),
+    (dict(norms=NUL), pq.PQ_EINVAL), (dict(signs=NUL), pq.PQ_EINVAL),
+    (dict(x=P2), pq.PQ_EINVAL), (dict(codes=ctypes.c_void_p(0x10008)), pq.PQ_EINVAL),
+    (dict(norms=ctypes.c_void_p(0x10001)), pq.PQ_EINVAL),
+    (dict(m=12, proj=P16, qb=P16, rn=P16), pq.PQ_EINVAL), (dict(m=2048, proj=P16, qb=P16, rn=P16), pq.PQ_EUNSUPPORTED),
+    (dict(m=64), pq.PQ_EINVAL), (dict(m=64, proj=P16, qb=P16), pq.PQ_EINVAL),
+    (dict(m=0, proj=P16), pq.PQ_EINVAL), (dict(m=-8), pq.PQ_EINVAL),
+    (dict(n=2 ** 62), pq.PQ_EINVAL),
+])
+def test_quantize_validation(kw, st):
+    assert _q(**kw) == st
+
+
+def test_empty_input_is_a_no_op():
+    assert _q(n=0) == pq.PQ_OK
+    lib = pq.lib()
+    assert lib.pq_dequantize(128, 4, P16, P16, 0, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_OK
+    assert lib.qjl_sketch(128, 256, P16, 0, P16, P16, P16, NUL) == pq.PQ_OK
+    assert lib.qjl_score(256, 4, 8, 32, 0, P16, P16, P16, P16, NUL) == pq.PQ_OK
+
+
+def test_other_entry_points_validate():
+    lib = pq.lib()
+    assert lib.pq_dequantize(100, 4, P16, P16, 4, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.pq_dequantize(128, 4, P16, P16, 4, P16, 3, P16, NUL) == pq.PQ_EINVAL
+    assert lib.pq_dequantize(128, 4, P16, P16, 4, P16, pq.PQ_F32, P2, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_sketch(128, 12, P16, 4, P16, P16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_sketch(128, 256, P16, 4, NUL, P16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_project(128, 0, P16, 4, P16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_score(256, 4, 8, 30, 64, P16, P16, P16, P16, NUL) == pq.PQ_EINVAL      # 30 % 8
+    assert lib.qjl_score(256, 4, 8, 64, 64, P16, P16, P16, P16, NUL) == pq.PQ_EUNSUPPORTED  # 8 q per kv
+    assert lib.qjl_score(96, 4, 8, 32, 64, P16, P16, P16, P16, NUL) == pq.PQ_EUNSUPPORTED   # m % 64
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a machine without a GPU")
+def test_valid_call_without_gpu_reports_hip_error():
+    # arguments pass validation, so the library reaches the HIP runtime, which has no device
+    assert _q() == pq.PQ_EHIP
+    assert pq.lib().pq_last_hip_error() != 0
+    with pytest.raises(pq.PQError):
+        raise pq.PQError(pq.PQ_EHIP, "pq_quantize")
