@@ -124,18 +124,19 @@ pqi::CodecTables make_tables(int bits) {
     w = 0.5;
     Y = 2.0;
   } else {
+    // a cell narrower than the smallest boundary gap holds at most one boundary, and the
+    // boundary nearest to its centre decides every y that rounds into it
     double gap = INFINITY;
     for (int k = 0; k + 2 < L; ++k) gap = std::min(gap, (double)t.beta[k + 1] - (double)t.beta[k]);
-    w = gap / 4.0;
-    Y = (double)t.beta[L - 2] + 4.0 * w;
+    w = 0.9 * gap;
+    Y = (double)t.beta[L - 2] + w;
   }
-  int ncell = (int)std::ceil(2.0 * Y / w);
-  ncell += ncell & 1;                 // keep the following LDS arrays 16-byte aligned
-  t.ncell = ncell;
-  t.cell_lo = (float)(-Y);
+  t.half = (int)std::ceil(Y / w);
+  t.ncell = 2 * t.half + 1;
+  // one copy of the grid per lane of a 16-lane LDS access group when it fits in 64 KiB
+  t.nrep = (size_t)t.ncell * 16 * 16 <= 65536 ? 16 : 1;
   t.cell_w = (float)w;
   t.cell_inv_w = (float)(1.0 / w);
-  t.cell_off = (float)(Y / w);
   return t;
 }
 

@@ -36,8 +36,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 b = (__bf16)f;
   return __builtin_bit_cast(uint16_t, b);
 }
+// two fp32 -> packed bf16 pair in one v_cvt_pk_bf16_f32 (round to nearest even)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const b2 b = __builtin_convertvector((f2){lo, hi}, b2);
+  return __builtin_bit_cast(uint32_t, b);
 }
 // fp32 -> fp16 bits, round to nearest even, overflow to +-inf (v_cvt_f16_f32)
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {

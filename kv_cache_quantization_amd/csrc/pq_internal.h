@@ -11,18 +11,20 @@ constexpr int kMaxBits = 8;
 constexpr int kMaxCells = 4096;
 
 // fp32 codebook and the geometry of the uniform search grid the kernels build
-// in LDS: cell k covers [cell_lo + k w, cell_lo + (k+1) w) and stores the
-// boundary nearest to its centre, so code = base + (y > boundary) is exact for
-// every y in the cell (w is a quarter of the smallest boundary gap).
+// in LDS: cell k (0 <= k < ncell) is centred on (k - half) w and stores the
+// boundary nearest to its centre together with the codes and centroids on
+// both sides, so code = base + (y > boundary) is exact for every y that rounds
+// to the cell (w is 0.9 of the smallest boundary gap).  Each cell is stored
+// nrep times so that the 16 lanes of one LDS access group read distinct banks.
 struct CodecTables {
   float cent[1 << kMaxBits];
   float beta[(1 << kMaxBits) - 1];
   int nbound;
-  int ncell;
-  float cell_lo;
+  int ncell;        // 2 * half + 1
+  int half;
+  int nrep;         // copies of each cell (16: one per lane of a 16-lane group, else 1)
   float cell_w;
   float cell_inv_w;
-  float cell_off;   // -cell_lo * cell_inv_w
 };
 
 struct QuantArgs {

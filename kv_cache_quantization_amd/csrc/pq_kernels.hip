@@ -14,20 +14,51 @@ namespace {
 constexpr int kThreads = 256;             // 4 waves per workgroup
 constexpr int kWaves = kThreads / 64;
 
+// Persistent grids: workgroups per CU for each kernel (a wave then walks over
+// n_tiles / (4 * grid) tiles, prefetching the next one).
+#ifndef PQ_QUANT_WG_PER_CU
+#define PQ_QUANT_WG_PER_CU 4
+#endif
+#ifndef PQ_DEQUANT_WG_PER_CU
+#define PQ_DEQUANT_WG_PER_CU 4
+#endif
+#ifndef PQ_QUANT_WAVES_PER_EU
+#define PQ_QUANT_WAVES_PER_EU 1
+#endif
+#ifndef PQ_SKETCH_WG_PER_CU
+#define PQ_SKETCH_WG_PER_CU 4
+#endif
+
 // ------------------------------------------------------------------------------------------
 // LDS set-up shared by quantize and dequantize
 // ------------------------------------------------------------------------------------------
-__device__ void build_search_grid(const CodecTables& t, uint2* tab) {
+__device__ void build_search_grid(const CodecTables& t, uint4* tab) {
   for (int k = threadIdx.x; k < t.ncell; k += blockDim.x) {
-    const float c = t.cell_lo + ((float)k + 0.5f) * t.cell_w;
+    const float c = (float)(k - t.half) * t.cell_w;
     int best = 0;
     float bd = fabsf(t.beta[0] - c);
     for (int j = 1; j < t.nbound; ++j) {
       const float dd = fabsf(t.beta[j] - c);
       if (dd < bd) { bd = dd; best = j; }
     }
-    tab[k] = make_uint2(__float_as_uint(t.beta[best]), (uint32_t)best);
+    const uint4 e = make_uint4(__float_as_uint(t.beta[best]), (uint32_t)best, __float_as_uint(t.cent[best]),
+                               __float_as_uint(t.cent[best + 1]));
+    for (int rep = 0; rep < t.nrep; ++rep) tab[k * t.nrep + rep] = e;
   }
+}
+
+// Adding 2^23 to a float in [0, 2^23) rounds it to an integer held in the low
+// mantissa bits: the search-grid cell of y is the bit pattern of
+// med3(fma(y, 1/w, half + 2^23), 2^23, 2^23 + ncell - 1) minus that of 2^23.
+constexpr float kMagic = 8388608.0f;
+constexpr uint32_t kMagicBits = 0x4B000000u;
+
+// Byte offset, from the start of the grid, of this lane's copy of the cell holding y.
+// rep_shift = log2(16 nrep); lane_off = 16 (lane % nrep) - (kMagicBits << rep_shift) (mod 2^32).
+__device__ __forceinline__ uint32_t cell_addr(float y, float inv_w, float offM, float topM, uint32_t rep_shift,
+                                              uint32_t lane_off) {
+  const float u = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
+  return (__float_as_uint(u) << rep_shift) + lane_off;
 }
 
 __device__ void copy_centroids(const CodecTables& t, float* cent) {
@@ -130,6 +161,38 @@ __device__ __forceinline__ void store_sign_tile(const f32x4& acc, int lane, int6
   }
 }
 
+// Sign bits of one 16-column N tile: b_i is the ballot of acc[i] > 0, whose bits
+// 16 g .. 16 g + 15 hold the signs of block row 4 g + i, i.e. the little-endian
+// 16-bit value at byte 2 nt of that row (column j <-> bit j, least significant first).
+// Returns that chunk for block row rr = 4 gg + i.
+__device__ __forceinline__ uint32_t sign_chunk(uint64_t b0, uint64_t b1, uint64_t b2, uint64_t b3, int i,
+                                               int gg) {
+  const bool hi = (gg & 2) != 0;
+  const uint32_t w0 = hi ? (uint32_t)(b0 >> 32) : (uint32_t)b0;
+  const uint32_t w1 = hi ? (uint32_t)(b1 >> 32) : (uint32_t)b1;
+  const uint32_t w2 = hi ? (uint32_t)(b2 >> 32) : (uint32_t)b2;
+  const uint32_t w3 = hi ? (uint32_t)(b3 >> 32) : (uint32_t)b3;
+  const uint32_t w = (i & 2) ? ((i & 1) ? w3 : w2) : ((i & 1) ? w1 : w0);
+  return __builtin_amdgcn_ubfe(w, 16 * (gg & 1), 16);
+}
+
+// Lane (q, rr) of the wave stores the chunk of N tile nt0 + q of block row rr.
+__device__ __forceinline__ void store_sign_chunk(uint32_t chunk, int lane, int64_t row0, int64_t nrows,
+                                                 uint8_t* bits, int mb, int nt0) {
+  const int q = lane >> 4, rr = lane & 15;
+  const int64_t row = row0 + rr;
+  const int byte = 2 * (nt0 + q);
+  if (row < nrows && byte < mb) {
+    uint8_t* dst = bits + row * (int64_t)mb + byte;
+    if ((mb & 1) == 0) {
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)chunk;
+    } else {
+      dst[0] = (uint8_t)chunk;
+      if (byte + 1 < mb) dst[1] = (uint8_t)(chunk >> 8);
+    }
+  }
+}
+
 template <int D>
 __host__ __device__ constexpr int cperm_inv(int o) {
   for (int j = 0; j < D / 4; ++j)
@@ -140,77 +203,115 @@ __host__ __device__ constexpr int cperm_inv(int o) {
 // ------------------------------------------------------------------------------------------
 // Quantize (+ optional QJL residual stage)
 // ------------------------------------------------------------------------------------------
-template <int D, bool IN_BF16, bool QJL, bool G_LDS>
-__global__ __launch_bounds__(kThreads) void pq_quantize_kernel(const pqi::QuantArgs a) {
-  constexpr int E = D / 4;
-  constexpr int KS = D / 32;                         // MFMA K steps per block
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint2* tab = reinterpret_cast<uint2*>(smem);
-  float* cent = reinterpret_cast<float*>(smem + a.t.ncell * 8);
-  uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * 8 + 1024);
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-  const int m = a.m;
-  const int m_pad = (m + 15) & ~15;
-  build_search_grid(a.t, tab);
-  copy_centroids(a.t, cent);
-  if constexpr (QJL && G_LDS) stage_projection_f16<D>(a.proj, m, m_pad, gl);
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, g = lane >> 4;
-
-  // rotation signs of this lane's elements in the load layout, as xor masks
-  uint32_t smask[E / 2];
+template <int D, bool IN_BF16>
+__device__ __forceinline__ void load_tile(uint4 (&raw)[IN_BF16 ? D / 32 : D / 16], const void* x, int64_t T,
+                                          int64_t n_blocks, int64_t full_tiles, int r, int g) {
+  constexpr int NR = IN_BF16 ? D / 32 : D / 16;
+  const int64_t blk = T * 16 + r;
+  const uint4* src = IN_BF16 ? reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + blk * D)
+                             : reinterpret_cast<const uint4*>(static_cast<const float*>(x) + blk * D);
+  // lane-quarter g reads elements 32 s + 8 g .. +8 (16 bytes of bf16, 32 of fp32)
+  auto idx = [&](int i) { return IN_BF16 ? 4 * i + g : 8 * (i >> 1) + 2 * g + (i & 1); };
+  // streamed once: non-temporal loads keep the caches for the tables
+  auto ld = [&](int i) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + idx(i));
+    return make_uint4(w.x, w.y, w.z, w.w);
+  };
+  if (T < full_tiles) {                       // uniform: every row of the tile exists
 #pragma unroll
-  for (int p = 0; p < E / 2; ++p) {
-    const int e = load_e(g, 2 * p);
-    const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
-    const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
-    smask[p] = (s0 << 15) | (s1 << 31);
+    for (int i = 0; i < NR; ++i) raw[i] = ld(i);
+  } else {
+    const bool valid = blk < n_blocks;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) raw[i] = valid ? ld(i) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+
+// Two fp32 values -> packed fp16 high parts (round to nearest even).
+__device__ __forceinline__ uint32_t split_hi_f16x2(float x0, float x1) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 h = {(_Float16)x0, (_Float16)x1};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// Low parts fp16(x - hi): v_fma_mix computes x - hi exactly from the fp16 hi and
+// the fp32 x and rounds once to fp16, writing the low or the high half.
+__device__ __forceinline__ uint32_t split_lo_f16x2(uint32_t hp, float x0, float x1) {
+  uint32_t lo;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hp), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(hp), "v"(x1));
+  return lo;
+}
+
+template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP>
+struct Quantizer {
+  static constexpr int E = D / 4;
+  static constexpr int KS = D / 32;                         // MFMA K steps per block
+  static constexpr int NR = IN_BF16 ? D / 32 : D / 16;      // 16-byte loads per lane per tile
+  static constexpr uint32_t kRepShift = REP ? 8u : 4u;      // log2(bytes per cell)
+
+  const pqi::QuantArgs& a;
+  const unsigned char* smem;
+  const uint4* gl;
+  uint32_t smask[E / 2];
+  int lane, r, g, m, m_pad, mb;
+  float inv_w, offM, topM, inv_sqrt_d;
+  uint32_t lane_off;
+
+  __device__ Quantizer(const pqi::QuantArgs& args, const unsigned char* sm, const uint4* g_lds)
+      : a(args), smem(sm), gl(g_lds) {
+    lane = threadIdx.x & 63;
+    r = lane & 15;
+    g = lane >> 4;
+    m = a.m;
+    m_pad = (m + 15) & ~15;
+    mb = m >> 3;
+#pragma unroll
+    for (int p = 0; p < E / 2; ++p) {
+      const int e = load_e(g, 2 * p);
+      const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
+      const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
+      smask[p] = (s0 << 15) | (s1 << 31);
+    }
+    inv_w = a.t.cell_inv_w;
+    offM = (float)a.t.half + kMagic;
+    topM = kMagic + (float)(a.t.ncell - 1);
+    inv_sqrt_d = 1.0f / sqrtf((float)D);
+    lane_off = (REP ? 16u * (uint32_t)(lane & 15) : 0u) - (kMagicBits << kRepShift);
   }
 
-  const float inv_w = a.t.cell_inv_w, off = a.t.cell_off;
-  const float top = (float)(a.t.ncell - 1);
-  const int64_t n_blocks = a.n_blocks;
-  const int64_t n_tiles = (n_blocks + 15) >> 4;
-  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
-  const int mb = m >> 3;
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-
-  for (int64_t T = wave_id; T < n_tiles; T += n_waves) {
+  __device__ __forceinline__ void tile(const uint4 (&raw)[NR], int64_t T) {
+    const int64_t n_blocks = a.n_blocks;
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
     float v[E];
-    float ss;
     if constexpr (IN_BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + blk * D);
 #pragma unroll
-      for (int s = 0; s < E / 8; ++s) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (valid) w = src[4 * s + g];
-        w.x ^= smask[4 * s + 0]; w.y ^= smask[4 * s + 1];
-        w.z ^= smask[4 * s + 2]; w.w ^= smask[4 * s + 3];
-        v[8 * s + 0] = bf16_lo(w.x); v[8 * s + 1] = bf16_hi(w.x);
-        v[8 * s + 2] = bf16_lo(w.y); v[8 * s + 3] = bf16_hi(w.y);
-        v[8 * s + 4] = bf16_lo(w.z); v[8 * s + 5] = bf16_hi(w.z);
-        v[8 * s + 6] = bf16_lo(w.w); v[8 * s + 7] = bf16_hi(w.w);
+      for (int s = 0; s < NR; ++s) {
+        const uint32_t w[4] = {raw[s].x ^ smask[4 * s + 0], raw[s].y ^ smask[4 * s + 1],
+                               raw[s].z ^ smask[4 * s + 2], raw[s].w ^ smask[4 * s + 3]};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[8 * s + 2 * u] = bf16_lo(w[u]);
+          v[8 * s + 2 * u + 1] = bf16_hi(w[u]);
+        }
       }
     } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + blk * D);
 #pragma unroll
-      for (int s = 0; s < E / 8; ++s) {
-        float4 w0 = make_float4(0, 0, 0, 0), w1 = w0;
-        if (valid) { w0 = src[8 * s + 2 * g]; w1 = src[8 * s + 2 * g + 1]; }
-        const float f[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      for (int s = 0; s < NR / 2; ++s) {
+        const uint32_t f[8] = {raw[2 * s].x, raw[2 * s].y, raw[2 * s].z, raw[2 * s].w,
+                               raw[2 * s + 1].x, raw[2 * s + 1].y, raw[2 * s + 1].z, raw[2 * s + 1].w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const uint32_t sm = (t & 1) ? (smask[4 * s + t / 2] & 0x80000000u) : (smask[4 * s + t / 2] << 16);
-          v[8 * s + t] = __uint_as_float(__float_as_uint(f[t]) ^ sm);
+          v[8 * s + t] = __uint_as_float(f[t] ^ sm);
         }
       }
     }
-    ss = tree_sumsq<E>(v);
+    float ss = tree_sumsq<E>(v);
 
     wht_forward<D>(v);                     // v = z = H (D x), unnormalised
 
@@ -234,13 +335,31 @@ __global__ __launch_bounds__(kThreads) void pq_quantize_kernel(const pqi::QuantA
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const float y = v[j] * inv_n;
-      const float tc = fminf(fmaxf(fmaf(y, inv_w, off), 0.0f), top);
-      const uint2 te = tab[(int)tc];
-      const uint32_t code = te.y + (y > __uint_as_float(te.x) ? 1u : 0u);
+      const float u = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
+      const uint32_t addr = (__float_as_uint(u) << kRepShift) + lane_off;
+      uint32_t code;
+      if constexpr (QJL) {
+        u32x4 te = *static_cast<const u32x4*>(__builtin_assume_aligned(smem + addr, 16));
+        asm("" : "+v"(te));                // keep the cell as one 16-byte LDS read
+        const bool gt = y > __uint_as_float(te.x);
+        code = te.y + (gt ? 1u : 0u);
+        const float c = __uint_as_float(gt ? te.w : te.z);
+        v[j] = fmaf(-nsc, c, v[j] * rscale);
+        asm volatile("" : "+v"(v[j]));     // keep the residual next to its lookup
+      } else {
+        u32x2 te = *static_cast<const u32x2*>(__builtin_assume_aligned(smem + addr, 8));
+        asm("" : "+v"(te));
+        code = te.y + (y > __uint_as_float(te.x) ? 1u : 0u);
+      }
       const int o = cperm<D>(j);
       cw[o >> 2] |= code << (8 * (o & 3));
-      if constexpr (QJL) v[j] = fmaf(-nsc, cent[code], v[j] * rscale);
+      // at most 8 grid lookups in flight: bounds the registers the scheduler may tie up
+      if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
+    // materialise the packed codes here: otherwise the whole decision chain sinks into
+    // the store branch below and keeps every lookup result live until then
+#pragma unroll
+    for (int w = 0; w < E / 4; ++w) asm volatile("" : "+v"(cw[w]));
     if (valid) {
       uint4* dst = reinterpret_cast<uint4*>(a.codes + blk * D + E * qpos<D>(g));
 #pragma unroll
@@ -254,30 +373,64 @@ __global__ __launch_bounds__(kThreads) void pq_quantize_kernel(const pqi::QuantA
       const float rn = sqrtf(rss) / rscale * inv_sqrt_d;    // ||r|| = ||H D r|| / sqrt(d)
       if (valid && g == 0) a.rnorms[blk] = f32_to_f16(rn);
       // residual split into fp16 high and low parts (22 significant bits), MFMA A fragments
-      f16x8 ahi[KS], alo[KS];
+      u32x4 ahi[KS], alo[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float x = v[cperm_inv<D>(8 * k + t)];
-          const _Float16 h = (_Float16)x;
-          ahi[k][t] = h;
-          alo[k][t] = (_Float16)(x - (float)h);
+        for (int t = 0; t < 4; ++t) {
+          const float x0 = v[cperm_inv<D>(8 * k + 2 * t)], x1 = v[cperm_inv<D>(8 * k + 2 * t + 1)];
+          const uint32_t hp = split_hi_f16x2(x0, x1);
+          ahi[k][t] = hp;
+          alo[k][t] = split_lo_f16x2(hp, x0, x1);
         }
       }
       const int colbase = E * qpos<D>(g);   // element offset of this quarter's run
-      for (int nt = 0; nt < (m_pad >> 4); ++nt) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        const int row = 16 * nt + r;
+      const int ntiles = m_pad >> 4;
+      const int myq = lane >> 4, ri = r & 3, rg = r >> 2;
+      for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
+        uint32_t mychunk = 0;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const f16x8 b = load_gfrag_f16<D, G_LDS>(gl, a.proj, m, row, (colbase >> 3) + k);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[k], b, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[k], b, acc, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (nt0 + q < ntiles) {
+            const int row = 16 * (nt0 + q) + r;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+              const f16x8 b = load_gfrag_f16<D, G_LDS>(gl, a.proj, m, row, (colbase >> 3) + k);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ahi[k]), b, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, alo[k]), b, acc, 0, 0, 0);
+            }
+          }
+          const uint32_t c = sign_chunk(__ballot(acc[0] > 0.0f), __ballot(acc[1] > 0.0f),
+                                        __ballot(acc[2] > 0.0f), __ballot(acc[3] > 0.0f), ri, rg);
+          mychunk = myq == q ? c : mychunk;
         }
-        store_sign_tile(acc, lane, T * 16, n_blocks, a.qbits, mb, nt);
+        store_sign_chunk(mychunk, lane, T * 16, n_blocks, a.qbits, mb, nt0);
       }
     }
+  }
+};
+
+template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUANT_WAVES_PER_EU))) void pq_quantize_kernel(const pqi::QuantArgs a) {
+  using Q = Quantizer<D, IN_BF16, QJL, G_LDS, REP>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint4* tab = reinterpret_cast<uint4*>(smem);
+  uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
+  build_search_grid(a.t, tab);
+  if constexpr (QJL && G_LDS) stage_projection_f16<D>(a.proj, a.m, (a.m + 15) & ~15, gl);
+  __syncthreads();
+
+  Q q(a, smem, gl);
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t full_tiles = a.n_blocks >> 4;
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+  int64_t T = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  // several waves per SIMD overlap one wave's loads with another's arithmetic
+  uint4 raw[Q::NR];
+  for (; T < n_tiles; T += n_waves) {
+    load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
+    q.tile(raw, T);
   }
 }
 
@@ -287,6 +440,7 @@ __global__ __launch_bounds__(kThreads) void pq_quantize_kernel(const pqi::QuantA
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
   constexpr int E = D / 4;
+  constexpr int NR = E / 16;                          // 16-byte code loads per lane per tile
   __shared__ float cent[1 << pqi::kMaxBits];
   copy_centroids(a.t, cent);
   __syncthreads();
@@ -306,28 +460,39 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 
   const int64_t n_blocks = a.n_blocks;
   const int64_t n_tiles = (n_blocks + 15) >> 4;
-  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)gridDim.x * kWaves;
 
-  for (int64_t T = wave_id; T < n_tiles; T += n_waves) {
+  auto load = [&](uint4 (&q)[NR], uint16_t& nb, int64_t T) {
+    const int64_t blk = T * 16 + r;
+    const bool valid = blk < n_blocks;
+    const uint4* src = reinterpret_cast<const uint4*>(a.codes + blk * D + E * g);
+#pragma unroll
+    for (int w = 0; w < NR; ++w) q[w] = valid ? src[w] : make_uint4(0, 0, 0, 0);
+    nb = valid ? a.norms[blk] : (uint16_t)0;
+  };
+
+  int64_t T = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  uint4 q[NR];
+  uint16_t nb;
+  load(q, nb, T);
+
+  for (; T < n_tiles; T += n_waves) {
+    uint4 qn[NR];
+    uint16_t nbn;
+    load(qn, nbn, T + n_waves);
+
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
     float v[E];
-    float scale = 0.0f;
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(a.codes + blk * D + E * g);
 #pragma unroll
-      for (int w = 0; w < E / 16; ++w) {
-        uint4 q = make_uint4(0, 0, 0, 0);
-        if (valid) q = src[w];
-        const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+    for (int w = 0; w < NR; ++w) {
+      const uint32_t qq[4] = {q[w].x, q[w].y, q[w].z, q[w].w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) v[16 * w + 4 * u + b] = cent[(qq[u] >> (8 * b)) & 0xffu];
-      }
-      if (valid) scale = f16_to_f32(a.norms[blk]) * (1.0f / (float)D);
+        for (int b = 0; b < 4; ++b) v[16 * w + 4 * u + b] = cent[(qq[u] >> (8 * b)) & 0xffu];
     }
+    const float scale = f16_to_f32(nb) * (1.0f / (float)D);
 
     wht_dequant<D>(v);
 
@@ -359,6 +524,9 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
         }
       }
     }
+#pragma unroll
+    for (int w = 0; w < NR; ++w) q[w] = qn[w];
+    nb = nbn;
   }
 }
 
@@ -545,33 +713,40 @@ int grid_for(int64_t n_tiles, const pqi::LaunchCfg& c, int per_cu) {
   return (int)want;
 }
 
-template <int D>
-hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
-  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
-  const int m_pad = (a.m + 15) & ~15;
-  const size_t base = (size_t)a.t.ncell * 8 + 1024;
-  const size_t glb = (size_t)m_pad * D * 2;
-  const bool qjl = a.m > 0;
-  const bool g_lds = qjl && base + glb <= (size_t)c.max_lds && base + glb <= 65536;
-  const size_t lds = base + (g_lds ? glb : 0);
-  const int grid = grid_for(n_tiles, c, 8);
+template <int D, bool REP>
+hipError_t launch_quantize_r(bool in_bf16, bool qjl, bool g_lds, int grid, size_t lds, const pqi::QuantArgs& a,
+                             hipStream_t s) {
   if (!qjl) {
-    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, false, false>), grid, kThreads, lds, s, a);
-    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, false, false>), grid, kThreads, lds, s, a);
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, false, false, REP>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, false, false, REP>), grid, kThreads, lds, s, a);
   } else if (g_lds) {
-    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true>), grid, kThreads, lds, s, a);
-    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true>), grid, kThreads, lds, s, a);
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true, REP>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true, REP>), grid, kThreads, lds, s, a);
   } else {
-    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false>), grid, kThreads, lds, s, a);
-    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false>), grid, kThreads, lds, s, a);
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, REP>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, REP>), grid, kThreads, lds, s, a);
   }
   return hipGetLastError();
 }
 
 template <int D>
+hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int m_pad = (a.m + 15) & ~15;
+  const size_t base = (size_t)a.t.ncell * a.t.nrep * 16;
+  const size_t glb = (size_t)m_pad * D * 2;
+  const bool qjl = a.m > 0;
+  const bool g_lds = qjl && base + glb <= (size_t)c.max_lds && base + glb <= 65536;
+  const size_t lds = base + (g_lds ? glb : 0);
+  const int grid = grid_for(n_tiles, c, PQ_QUANT_WG_PER_CU);
+  if (a.t.nrep == 16) return launch_quantize_r<D, true>(in_bf16, qjl, g_lds, grid, lds, a, s);
+  return launch_quantize_r<D, false>(in_bf16, qjl, g_lds, grid, lds, a, s);
+}
+
+template <int D>
 hipError_t launch_dequantize_d(bool out_bf16, const pqi::DequantArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
-  const int grid = grid_for(n_tiles, c, 8);
+  const int grid = grid_for(n_tiles, c, PQ_DEQUANT_WG_PER_CU);
   if (out_bf16) hipLaunchKernelGGL((pq_dequantize_kernel<D, true>), grid, kThreads, 0, s, a);
   else hipLaunchKernelGGL((pq_dequantize_kernel<D, false>), grid, kThreads, 0, s, a);
   return hipGetLastError();
@@ -583,7 +758,7 @@ hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hi
   const int m_pad = (a.m + 15) & ~15;
   const size_t glb = (size_t)m_pad * D * 2;
   const bool g_lds = glb <= (size_t)c.max_lds && glb <= 65536;
-  const int grid = grid_for(n_tiles, c, 8);
+  const int grid = grid_for(n_tiles, c, PQ_SKETCH_WG_PER_CU);
   if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true>), grid, kThreads, glb, s, a);
   else hipLaunchKernelGGL((qjl_sketch_kernel<D, false>), grid, kThreads, 0, s, a);
   return hipGetLastError();
