@@ -23,12 +23,10 @@ Readings where the pages leave a step open:
   * the code decision is taken in fp32 (the precision of the kernel):
     fp32(y_i) is compared with fp32(beta_j).  ``boundary_distance`` gives the
     float64 distance to the nearest boundary for the parity rule;
-  * QJL residual: r = x - xhat in the original coordinates, rnorm16 =
-    fp16(||r||), bits = [S r > 0] packed LSB-first, where the seeded Gaussian
-    projection applied to r is S = G . R with G the seeded m x d bf16 Gaussian
-    matrix.  G R has i.i.d. N(0,1) entries whenever G does (R is orthogonal),
-    so S is itself a seeded Gaussian JL matrix; it also equals the projection
-    G applied to the rotated residual R r.
+  * QJL residual: r = x - xhat in the block's own coordinates, rnorm16 =
+    fp16(||r||), bits = [S r > 0] packed LSB-first, where S is the seeded
+    m x d Gaussian matrix itself (stored as bf16 values), applied to r without
+    any rotation.
 """
 
 import math
@@ -36,7 +34,7 @@ import math
 import numpy as np
 
 from . import lloyd_max
-from .hadamard import sylvester, rotation
+from .hadamard import sylvester
 from .numerics import round_fp16, round_fp32, pack_bits_lsb
 
 BAND = 1e-4   # coordinates this close to a boundary may take either side (parity rule)
@@ -107,8 +105,12 @@ def dequantize(codes, n16, bits, D):
 
 
 def residual_projection(d, D, G):
-    """S = G . R, the m x d Gaussian projection the QJL stage applies to r."""
-    return np.asarray(G, dtype=np.float64) @ rotation(d, D)
+    """S, the m x d Gaussian projection the QJL stage applies to r: the seeded
+    matrix G as given (d and D are accepted for symmetry with the codec calls
+    and do not enter S)."""
+    G = np.asarray(G, dtype=np.float64)
+    assert G.shape[1] == d
+    return G
 
 
 def qjl_residual(x, codes, n16, bits, D, G):

@@ -157,9 +157,13 @@ def test_residual_projection_identities():
     assert np.allclose(out["r"], r_ref, atol=1e-13)
     assert np.allclose(out["rnorm"], np.linalg.norm(r_ref, axis=1), rtol=1e-13)
     assert np.array_equal(out["rnorm16"], round_fp16(out["rnorm"]))
-    # S r equals G applied to the rotated residual R r
+    # p is G applied to r itself, one dot product per row of G
+    for i in (0, 7, m - 1):
+        for b in (0, 19):
+            assert abs(out["p"][b, i] - sum(G[i, e] * r_ref[b, e] for e in range(d))) < 1e-12
+    # and it is not G applied to the rotated residual R r
     R = _kron_H(d) * D[None, :] / math.sqrt(d)
-    assert np.allclose(out["p"], (r_ref @ R.T) @ G.T, atol=1e-12)
+    assert not np.allclose(out["p"], (r_ref @ R.T) @ G.T, atol=1e-3)
     bits_unpacked = (out["bits"][:, :, None] >> np.arange(8)) & 1
     assert np.array_equal(bits_unpacked.reshape(20, m).astype(bool), out["p"] > 0)
 
