@@ -110,9 +110,9 @@ int pq_codebook(int bits, double* centroids, double* boundaries, double* mse);
  *   m          0 = no QJL stage (proj, qjl_bits, rnorms must then be NULL);
  *              otherwise the number of residual projections
  *   proj       G, m x d bf16 (device)
- *   qjl_bits   out, n_blocks * m/8 bytes: sign bits of S r with S = G.R (the
- *              Gaussian matrix applied to the rotated residual; G.R is itself
- *              an i.i.d. Gaussian matrix) and r = x - dequantize(code, norm)
+ *   qjl_bits   out, n_blocks * m/8 bytes: sign bits of G r, the seeded
+ *              Gaussian matrix applied to the residual r = x - dequantize(code,
+ *              norm) in the block's own coordinates
  *   rnorms     out, n_blocks fp16: fp16(||r||)
  */
 int pq_quantize(int d, int bits, int in_dtype, const void* x, int64_t n_blocks,

@@ -193,4 +193,14 @@ __host__ __device__ constexpr int dq_out_chunk(int s) {
                   : (((s & 1) << 7) | (((s >> 1) & 1) << 8) | (((s >> 2) & 1) << 5) | (((s >> 3) & 1) << 6));
 }
 
+// The quantize kernel takes the rotated residual rho (contiguous layout, registers
+// renamed to offset order) back through the dequantize butterflies: register chunk k
+// (registers 8k .. 8k+7) of quarter g then holds elements 8 res_col8(k) + 0..7 of
+// H rho = d D r.  For d = 64 the contiguous layout keeps element bits 4 and 5 in lane
+// bits 5 and 4, which swaps those two bits of the dequantize output map.
+template <int D>
+__host__ __device__ constexpr int res_col8(int g, int k) {
+  return D == 64 ? ((g & 1) | (k << 1) | ((g >> 1) << 2)) : g + dq_out_chunk<D>(k) / 8;
+}
+
 }  // namespace pqd

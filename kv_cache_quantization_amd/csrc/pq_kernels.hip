@@ -87,41 +87,46 @@ __device__ void stage_projection(const uint16_t* proj, int m, int m_pad, uint4* 
   }
 }
 
-// fp16 copy of G scaled by 2^10 (exact for |G| >= 2^-24; the bf16 mantissa fits in fp16)
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w) {
+// fp16 copy of a bf16 pair of G scaled by 2^10 (exact for |G| >= 2^-24; the bf16
+// mantissa fits in fp16), with the sign of element 2t (2t+1) flipped when bit 2t
+// (2t+1) of the sign byte sb is set.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_signed(uint32_t w, uint32_t sb, int t) {
+  w ^= (((sb >> (2 * t)) & 1u) << 15) | (((sb >> (2 * t + 1)) & 1u) << 31);
   const _Float16 lo = (_Float16)(bf16_lo(w) * 1024.0f);
   const _Float16 hi = (_Float16)(bf16_hi(w) * 1024.0f);
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+// Columns 8 c .. 8 c + 7 of row n of G D (the rotation signs applied to the columns
+// of G; byte c of the sign mask covers exactly these 8 columns), fp16, scaled by 2^10.
+__device__ __forceinline__ uint4 gd_chunk_f16(const uint4* src, const uint8_t* signs, int cpr, int n, int c) {
+  const uint4 b = src[n * cpr + c];
+  const uint32_t sb = signs[c];
+  return make_uint4(bf16x2_to_f16x2_signed(b.x, sb, 0), bf16x2_to_f16x2_signed(b.y, sb, 1),
+                    bf16x2_to_f16x2_signed(b.z, sb, 2), bf16x2_to_f16x2_signed(b.w, sb, 3));
+}
+
 template <int D>
-__device__ void stage_projection_f16(const uint16_t* proj, int m, int m_pad, uint4* gl) {
+__device__ void stage_projection_f16(const uint16_t* proj, const uint8_t* signs, int m, int m_pad, uint4* gl) {
   constexpr int CPR = D / 8;
   const uint4* src = reinterpret_cast<const uint4*>(proj);
   for (int i = threadIdx.x; i < m_pad * CPR; i += blockDim.x) {
     const int n = i / CPR, c = i % CPR;
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (n < m) {
-      const uint4 b = src[i];
-      w = make_uint4(bf16x2_to_f16x2_scaled(b.x), bf16x2_to_f16x2_scaled(b.y),
-                     bf16x2_to_f16x2_scaled(b.z), bf16x2_to_f16x2_scaled(b.w));
-    }
+    if (n < m) w = gd_chunk_f16(src, signs, CPR, n, c);
     gl[g_swizzle<D>(n, c)] = w;
   }
 }
 
 template <int D, bool G_LDS>
-__device__ __forceinline__ f16x8 load_gfrag_f16(const uint4* gl, const uint16_t* proj, int m, int row, int col8) {
+__device__ __forceinline__ f16x8 load_gfrag_f16(const uint4* gl, const uint16_t* proj, const uint8_t* signs, int m,
+                                                int row, int col8) {
   uint4 w;
   if constexpr (G_LDS) {
     w = gl[g_swizzle<D>(row, col8)];
   } else {
     w = make_uint4(0, 0, 0, 0);
-    if (row < m) {
-      const uint4 b = reinterpret_cast<const uint4*>(proj)[row * (D / 8) + col8];
-      w = make_uint4(bf16x2_to_f16x2_scaled(b.x), bf16x2_to_f16x2_scaled(b.y),
-                     bf16x2_to_f16x2_scaled(b.z), bf16x2_to_f16x2_scaled(b.w));
-    }
+    if (row < m) w = gd_chunk_f16(reinterpret_cast<const uint4*>(proj), signs, D / 8, row, col8);
   }
   return __builtin_bit_cast(f16x8, w);
 }
@@ -372,19 +377,25 @@ struct Quantizer {
       const float rss = sum4(tree_sumsq<E>(v));
       const float rn = sqrtf(rss) / rscale * inv_sqrt_d;    // ||r|| = ||H D r|| / sqrt(d)
       if (valid && g == 0) a.rnorms[blk] = f32_to_f16(rn);
-      // residual split into fp16 high and low parts (22 significant bits), MFMA A fragments
+      // back to the block's coordinates: w = H rho = d D r (times rscale).  The signs D
+      // are folded into the staged G, so the products below give d rscale 2^10 (G r).
+      float w[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) w[i] = v[cperm_inv<D>(i)];
+      wht_dequant<D>(w);
+      // split into fp16 high and low parts (22 significant bits), MFMA A fragments;
+      // register chunk k of quarter g holds columns 8 res_col8(g, k) + 0..7
       u32x4 ahi[KS], alo[KS];
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float x0 = v[cperm_inv<D>(8 * k + 2 * t)], x1 = v[cperm_inv<D>(8 * k + 2 * t + 1)];
+          const float x0 = w[8 * k + 2 * t], x1 = w[8 * k + 2 * t + 1];
           const uint32_t hp = split_hi_f16x2(x0, x1);
           ahi[k][t] = hp;
           alo[k][t] = split_lo_f16x2(hp, x0, x1);
         }
       }
-      const int colbase = E * qpos<D>(g);   // element offset of this quarter's run
       const int ntiles = m_pad >> 4;
       const int myq = lane >> 4, ri = r & 3, rg = r >> 2;
       for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
@@ -396,7 +407,7 @@ struct Quantizer {
             const int row = 16 * (nt0 + q) + r;
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-              const f16x8 b = load_gfrag_f16<D, G_LDS>(gl, a.proj, m, row, (colbase >> 3) + k);
+              const f16x8 b = load_gfrag_f16<D, G_LDS>(gl, a.proj, a.signs, m, row, res_col8<D>(g, k));
               acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ahi[k]), b, acc, 0, 0, 0);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, alo[k]), b, acc, 0, 0, 0);
             }
@@ -418,7 +429,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUA
   uint4* tab = reinterpret_cast<uint4*>(smem);
   uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
   build_search_grid(a.t, tab);
-  if constexpr (QJL && G_LDS) stage_projection_f16<D>(a.proj, a.m, (a.m + 15) & ~15, gl);
+  if constexpr (QJL && G_LDS) stage_projection_f16<D>(a.proj, a.signs, a.m, (a.m + 15) & ~15, gl);
   __syncthreads();
 
   Q q(a, smem, gl);
