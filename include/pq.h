@@ -163,6 +163,44 @@ int qjl_project(int d, int m, const uint16_t* q, int64_t n_q, const uint16_t* pr
 int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
               const uint8_t* bits, const uint16_t* norms, float* scores, void* stream);
 
+/*
+ * Two-stage estimator of <q, x> from the stored codes and QJL residual bits,
+ * without reconstructing x (eliza quantization README, TurboQuant, "Algorithm in
+ * one paragraph"; scores straight from the packed indices: same README, "Fused
+ * TurboQuant"):
+ *   score = n16/d * <H(D q), c[code]> + rnorm16 * sqrt(pi/2)/m * <G q, 2 b - 1>
+ * where <H(D q), c[code]> n16/d = <q, dequantize(code, n16)> since H is symmetric.
+ *
+ * pq_query_prep_bytes: bytes of the prepared-query buffer for n_heads heads
+ * (-1 for invalid d or m).  Per head, at stride pq_query_prep_bytes(d, m, 1):
+ *   float qrot[16][d]   H (D q) of query row r, rows >= n_q zero
+ *   float sq[16][m]     G q
+ *   float scale[2][16], int32 isum[2][16], then int8 limb tiles (internal)
+ *
+ * pq_query_prep: fill that buffer.
+ *   q          n_heads * n_q * d bf16, layout [head][query][d], 1 <= n_q <= 16
+ *   signs      the rotation sign mask of the codes to be scored
+ *   proj       G, m x d bf16 (NULL when m == 0)
+ *   prep       out, pq_query_prep_bytes(d, m, n_heads) bytes, 16-byte aligned
+ *
+ * pq_score: scores[h][i][t] for every head h, query i < n_q and token t.
+ *   codes      n_heads * n_tok * d bytes, layout [head][token][d] (pq_quantize output)
+ *   norms      n_heads * n_tok fp16
+ *   qjl_bits   n_heads * n_tok * m/8 bytes, rnorms n_heads * n_tok fp16 (both
+ *              NULL when m == 0: the score is then the first term alone)
+ *   scores     out, n_heads * n_q * n_tok fp32, layout [head][query][token]
+ * Limits: bits in 1..4 (PQ_EUNSUPPORTED above), m a multiple of 64 with
+ * d + m <= 1344, n_q <= 16 (call again for more queries).  The query terms are
+ * carried as integers of 21 bits relative to their largest entry; the sums
+ * over d and m are exact.
+ */
+int64_t pq_query_prep_bytes(int d, int m, int n_heads);
+int pq_query_prep(int d, int m, int n_heads, int n_q, const uint16_t* q, const uint8_t* signs,
+                  const uint16_t* proj, void* prep, void* stream);
+int pq_score(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+             const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits, const uint16_t* rnorms,
+             float* scores, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

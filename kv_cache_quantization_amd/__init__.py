@@ -46,6 +46,9 @@ def _load():
         "qjl_sketch": ([I, I, P, L, P, P, P, P], I),
         "qjl_project": ([I, I, P, L, P, P, P], I),
         "qjl_score": ([I, I, I, I, L, P, P, P, P, P], I),
+        "pq_query_prep_bytes": ([I, I, I], L),
+        "pq_query_prep": ([I, I, I, I, P, P, P, P, P], I),
+        "pq_score": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -56,7 +59,8 @@ def _load():
 
 _lib = _load()
 EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_quantize",
-           "pq_dequantize", "qjl_sketch", "qjl_project", "qjl_score")
+           "pq_dequantize", "qjl_sketch", "qjl_project", "qjl_score", "pq_query_prep_bytes",
+           "pq_query_prep", "pq_score")
 
 
 def lib():
@@ -178,4 +182,58 @@ def qjl_score(sq, bits, norms, batch, kv_heads, q_heads, n_keys, out=None):
         out = torch.empty((batch, q_heads, n_keys), dtype=torch.float32, device=sq.device)
     _check(_lib.qjl_score(m, batch, kv_heads, q_heads, n_keys, _ptr(sq), _ptr(bits), _ptr(norms), _ptr(out),
                           _stream()), "qjl_score")
+    return out
+
+
+def query_prep_bytes(d, m, n_heads):
+    """Bytes of the prepared-query buffer of the two-stage score."""
+    nb = _lib.pq_query_prep_bytes(d, m, n_heads)
+    if nb < 0:
+        raise PQError(PQ_EINVAL, "pq_query_prep_bytes")
+    return nb
+
+
+def query_prep(q, signs, proj=None, out=None):
+    """Prepare queries q (bf16 [n_heads, n_q, d], n_q <= 16) for ``score``.
+
+    Returns a uint8 device buffer; per head it starts with H(D q) as fp32 [16, d]
+    and G q as fp32 [16, m] (see ``prep_views``).
+    """
+    _dev(q, "q", (torch.bfloat16,))
+    _dev(signs, "signs", (torch.uint8,))
+    n_heads, n_q, d = q.shape
+    m = 0
+    if proj is not None:
+        _dev(proj, "proj", (torch.bfloat16,))
+        m = proj.shape[0]
+    if out is None:
+        out = torch.empty((query_prep_bytes(d, m, n_heads),), dtype=torch.uint8, device=q.device)
+    _check(_lib.pq_query_prep(d, m, n_heads, n_q, _ptr(q), _ptr(signs), _ptr(proj), _ptr(out), _stream()),
+           "pq_query_prep")
+    return out
+
+
+def prep_views(prep, d, m, n_heads):
+    """(qrot fp32 [n_heads, 16, d], sq fp32 [n_heads, 16, m]) views of a prepared-query buffer."""
+    per = query_prep_bytes(d, m, 1)
+    heads = prep.view(n_heads, per)
+    qrot = heads[:, :16 * d * 4].contiguous().view(torch.float32).view(n_heads, 16, d)
+    sq = heads[:, 16 * d * 4:16 * (d + m) * 4].contiguous().view(torch.float32).view(n_heads, 16, m)
+    return qrot, sq
+
+
+def score(prep, codes, norms, d, bits, n_heads, n_q, n_tok, qjl_bits=None, rnorms=None, m=0, out=None):
+    """Two-stage scores fp32 [n_heads, n_q, n_tok] from codes [n_heads, n_tok, d], norms,
+    and (with m > 0) the QJL residual bits and residual norms."""
+    _dev(prep, "prep", (torch.uint8,))
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(norms, "norms", (torch.float16,))
+    if m:
+        _dev(qjl_bits, "qjl_bits", (torch.uint8,))
+        _dev(rnorms, "rnorms", (torch.float16,))
+    if out is None:
+        out = torch.empty((n_heads, n_q, n_tok), dtype=torch.float32, device=codes.device)
+    _dev(out, "out", (torch.float32,))
+    _check(_lib.pq_score(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(codes), _ptr(norms), _ptr(qjl_bits),
+                         _ptr(rnorms), _ptr(out), _stream()), "pq_score")
     return out

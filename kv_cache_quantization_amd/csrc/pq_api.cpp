@@ -275,4 +275,65 @@ int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const
   return hip_status(pqi::launch_score(a, cfg, (hipStream_t)stream));
 }
 
+int64_t pq_query_prep_bytes(int d, int m, int n_heads) {
+  if (check_d(d) || m < 0 || (m % 64) != 0 || m > 1024 || n_heads < 0) return -1;
+  return (int64_t)n_heads * pqi::prep_head_bytes(d, m);
+}
+
+int pq_query_prep(int d, int m, int n_heads, int n_q, const uint16_t* q, const uint8_t* signs,
+                  const uint16_t* proj, void* prep, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (m < 0 || (m % 8) != 0) return PQ_EINVAL;
+  if ((m % 64) != 0 || m > 1024) return PQ_EUNSUPPORTED;
+  if (n_heads < 0 || n_q < 0 || n_q > pqi::kScoreRows) return PQ_EINVAL;
+  if (n_heads > INT32_MAX / pqi::kScoreRows) return PQ_EINVAL;
+  if (m == 0 && proj) return PQ_EINVAL;
+  if (n_heads == 0) return PQ_OK;
+  if (!signs || !prep || (n_q > 0 && !q) || (m > 0 && !proj)) return PQ_EINVAL;
+  if (!aligned(prep, 16) || (q && !aligned(q, 2)) || (proj && !aligned(proj, 2))) return PQ_EINVAL;
+  pqi::QueryPrepArgs a;
+  a.q = q; a.signs = signs; a.proj = proj; a.prep = static_cast<unsigned char*>(prep);
+  a.n_heads = n_heads; a.n_q = n_q; a.d = d; a.m = m;
+  return hip_status(pqi::launch_query_prep(a, (hipStream_t)stream));
+}
+
+int pq_score(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+             const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits, const uint16_t* rnorms,
+             float* scores, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (bits > pqi::kMaxScoreBits) return PQ_EUNSUPPORTED;
+  if (m < 0 || (m % 8) != 0) return PQ_EINVAL;
+  if ((m % 64) != 0 || m > 1024) return PQ_EUNSUPPORTED;
+  if (pqi::prep_head_bytes(d, m) - pqi::prep_off_meta(d, m) > 65536) return PQ_EUNSUPPORTED;
+  if (n_heads < 0 || n_q < 0 || n_q > pqi::kScoreRows || n_tok < 0) return PQ_EINVAL;
+  if (n_tok > kMaxElems / ((int64_t)d * (n_heads + 1))) return PQ_EINVAL;
+  if (m == 0 && (qjl_bits || rnorms)) return PQ_EINVAL;
+  if (n_heads == 0 || n_q == 0 || n_tok == 0) return PQ_OK;
+  if (!prep || !codes || !norms || !scores) return PQ_EINVAL;
+  if (m > 0 && (!qjl_bits || !rnorms)) return PQ_EINVAL;
+  if (!aligned(prep, 16) || !aligned(codes, 16) || !aligned(norms, 2) || !aligned(scores, 4)) return PQ_EINVAL;
+  if (m > 0 && (!aligned(qjl_bits, 2) || !aligned(rnorms, 2))) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::TwoStageArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.prep = static_cast<const unsigned char*>(prep);
+  a.codes = codes; a.norms = norms; a.qbits = qjl_bits; a.rnorms = rnorms; a.scores = scores;
+  a.n_tok = n_tok; a.n_heads = n_heads; a.n_q = n_q; a.m = m;
+  // Walsh coefficients of the codebook over the odd subsets of the code bits:
+  // alpha_p = 2^-b sum_k c_k s_p(k); the even subsets vanish by antisymmetry
+  const Codebook& cb = codebook(bits);
+  const int L = 1 << bits;
+  for (int p = 0; p < (L >> 1); ++p) {
+    const uint32_t mask = pqi::plane_mask(bits, p);
+    double acc = 0.0;
+    for (int k = 0; k < L; ++k) acc += (__builtin_popcount((uint32_t)k & mask) & 1) ? cb.c[k] : -cb.c[k];
+    a.alpha[p] = acc / (double)L;
+  }
+  return hip_status(pqi::launch_two_stage(d, bits, a, cfg, (hipStream_t)stream));
+}
+
 }  // extern "C"

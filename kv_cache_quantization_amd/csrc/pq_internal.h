@@ -79,6 +79,59 @@ struct ScoreArgs {
   int q_heads;
 };
 
+// Prepared queries of the two-stage score, per KV head (byte offsets from the head's
+// start; stride prep_head_bytes(d, m)):
+//   qrot   float[16][d]   H (D q) of query row r (rows >= n_q are zero)
+//   sq     float[16][m]   G q
+//   meta   float scale[2][16] (code term, QJL term), int32 isum[2][16]
+//   frag_c int8 limbs of rint(qrot / scale) in MFMA A-fragment order, 3 x (d/64) x 1 KiB
+//   frag_q the same for sq, 3 x (m/64) x 1 KiB
+constexpr int kScoreRows = 16;
+constexpr int kMaxScoreBits = 4;
+constexpr int kMaxPlanes = 1 << (kMaxScoreBits - 1);
+constexpr float kLimbRange = 2080768.0f;       // 127 * 16384 + 127 * 128 + 127
+
+__host__ __device__ constexpr int64_t prep_off_sq(int d) { return (int64_t)kScoreRows * d * 4; }
+__host__ __device__ constexpr int64_t prep_off_meta(int d, int m) { return prep_off_sq(d) + (int64_t)kScoreRows * m * 4; }
+__host__ __device__ constexpr int64_t prep_off_frag_c(int d, int m) { return prep_off_meta(d, m) + 256; }
+__host__ __device__ constexpr int64_t prep_off_frag_q(int d, int m) { return prep_off_frag_c(d, m) + 3 * (d / 64) * 1024; }
+__host__ __device__ constexpr int64_t prep_head_bytes(int d, int m) { return prep_off_frag_q(d, m) + 3 * (m / 64) * 1024; }
+
+// p-th subset (in increasing order of its bit mask) of the code bits {0 .. bits-1} with
+// an odd number of elements.
+__host__ __device__ constexpr uint32_t plane_mask(int bits, int p) {
+  int seen = 0;
+  for (uint32_t mask = 1; mask < (1u << bits); ++mask) {
+    if (__builtin_popcount(mask) & 1) {
+      if (seen == p) return mask;
+      ++seen;
+    }
+  }
+  return 0;
+}
+
+struct QueryPrepArgs {
+  const uint16_t* q;       // [n_heads][n_q][d] bf16
+  const uint8_t* signs;
+  const uint16_t* proj;    // G, m x d bf16 (NULL when m == 0)
+  unsigned char* prep;     // n_heads * prep_head_bytes(d, m)
+  int n_heads, n_q, d, m;
+};
+
+struct TwoStageArgs {
+  const unsigned char* prep;
+  const uint8_t* codes;    // [n_heads][n_tok][d]
+  const uint16_t* norms;   // [n_heads][n_tok]
+  const uint8_t* qbits;    // [n_heads][n_tok][m/8]
+  const uint16_t* rnorms;  // [n_heads][n_tok]
+  float* scores;           // [n_heads][n_q][n_tok]
+  int64_t n_tok;
+  int n_heads, n_q, m;
+  // c[code] = sum_p alpha[p] s_p(code), s_p = +1 when popcount(code & plane_mask[p]) is odd,
+  // else -1 (the odd-subset Walsh expansion of an antisymmetric codebook)
+  double alpha[kMaxPlanes];
+};
+
 struct LaunchCfg {
   int cu_count;
   int max_lds;       // bytes of LDS one workgroup may use
@@ -89,5 +142,7 @@ hipError_t launch_dequantize(int d, bool out_bf16, const DequantArgs& a, const L
 hipError_t launch_sketch(int d, const SketchArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s);
+hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const LaunchCfg& c, hipStream_t s);
 
 }  // namespace pqi

@@ -53,13 +53,6 @@ __device__ void build_search_grid(const CodecTables& t, uint4* tab) {
 constexpr float kMagic = 8388608.0f;
 constexpr uint32_t kMagicBits = 0x4B000000u;
 
-// Byte offset, from the start of the grid, of this lane's copy of the cell holding y.
-// rep_shift = log2(16 nrep); lane_off = 16 (lane % nrep) - (kMagicBits << rep_shift) (mod 2^32).
-__device__ __forceinline__ uint32_t cell_addr(float y, float inv_w, float offM, float topM, uint32_t rep_shift,
-                                              uint32_t lane_off) {
-  const float u = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
-  return (__float_as_uint(u) << rep_shift) + lane_off;
-}
 
 __device__ void copy_centroids(const CodecTables& t, float* cent) {
   for (int k = threadIdx.x; k <= t.nbound; k += blockDim.x) cent[k] = t.cent[k];
@@ -714,6 +707,251 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
 }
 
 // ------------------------------------------------------------------------------------------
+// Two-stage score: query preparation
+//
+// For every query row r of a KV head: qrot = H (D q) and sq = G q in fp32, then both are
+// quantized to integers Q = rint(v / s), s = max|v| / kLimbRange, split into three int8
+// limbs Q = 16384 h2 + 128 h1 + h0, and written in the A-fragment order of
+// v_mfma_i32_16x16x64_i8: limb l, K step k is a 1 KiB block whose 16 bytes at 16 L
+// (lane L = 16 gq + r) are elements 64 k + 16 gq + 0..15 (code term) or
+// (m/4) gq + 16 k + 0..15 (QJL term) of row r.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pq_query_rotate_kernel(const pqi::QueryPrepArgs a) {
+  const int h = blockIdx.x / pqi::kScoreRows, r = blockIdx.x % pqi::kScoreRows;
+  const int d = a.d, m = a.m;
+  unsigned char* base = a.prep + (int64_t)h * pqi::prep_head_bytes(d, m);
+  float* qrot = reinterpret_cast<float*>(base) + (int64_t)r * d;
+  float* sq = reinterpret_cast<float*>(base + pqi::prep_off_sq(d)) + (int64_t)r * m;
+  __shared__ float v[512];
+  __shared__ float qv[512];
+  const bool live = r < a.n_q;
+  const uint16_t* q = a.q + ((int64_t)h * a.n_q + r) * d;
+  for (int e = threadIdx.x; e < d; e += blockDim.x) {
+    float x = live ? bf16_to_f32(q[e]) : 0.0f;
+    qv[e] = x;
+    if ((a.signs[e >> 3] >> (e & 7)) & 1) x = -x;
+    v[e] = x;
+  }
+  __syncthreads();
+  // in-place Walsh-Hadamard butterflies in Sylvester order
+  for (int half = 1; half < d; half <<= 1) {
+    for (int t = threadIdx.x; t < d / 2; t += blockDim.x) {
+      const int i = (t / half) * 2 * half + (t % half);
+      const float x0 = v[i], x1 = v[i + half];
+      v[i] = x0 + x1;
+      v[i + half] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < d; e += blockDim.x) qrot[e] = v[e];
+  for (int n = threadIdx.x; n < m; n += blockDim.x) {
+    const uint16_t* gr = a.proj + (int64_t)n * d;
+    float acc = 0.0f;
+    if (live)
+      for (int e = 0; e < d; ++e) acc = fmaf(bf16_to_f32(gr[e]), qv[e], acc);
+    sq[n] = acc;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ int quant_int(float x, float s) { return s > 0.0f ? (int)rintf(x / s) : 0; }
+
+__device__ __forceinline__ int limb_of(int Q, int l) {
+  const int h2 = (int)rintf((float)Q * (1.0f / 16384.0f));
+  const int rem = Q - 16384 * h2;
+  const int h1 = (int)rintf((float)rem * (1.0f / 128.0f));
+  const int h0 = rem - 128 * h1;
+  return l == 0 ? h2 : l == 1 ? h1 : h0;
+}
+
+__global__ __launch_bounds__(256) void pq_query_quant_kernel(const pqi::QueryPrepArgs a) {
+  const int h = blockIdx.x;
+  const int d = a.d, m = a.m;
+  unsigned char* base = a.prep + (int64_t)h * pqi::prep_head_bytes(d, m);
+  const float* qrot = reinterpret_cast<const float*>(base);
+  const float* sq = reinterpret_cast<const float*>(base + pqi::prep_off_sq(d));
+  float* scale = reinterpret_cast<float*>(base + pqi::prep_off_meta(d, m));    // [2][16]
+  int* isum = reinterpret_cast<int*>(base + pqi::prep_off_meta(d, m) + 128);    // [2][16]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int job = wv; job < 2 * pqi::kScoreRows; job += 4) {
+    const int term = job / pqi::kScoreRows, r = job % pqi::kScoreRows;
+    const int len = term == 0 ? d : m;
+    const float* src = term == 0 ? qrot + (int64_t)r * d : sq + (int64_t)r * m;
+    float amax = 0.0f;
+    for (int e = lane; e < len; e += 64) amax = fmaxf(amax, fabsf(src[e]));
+    amax = wave_max(amax);
+    const float s = amax / pqi::kLimbRange;
+    int acc = 0;
+    for (int e = lane; e < len; e += 64) acc += quant_int(src[e], s);
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      scale[job] = s;
+      isum[job] = acc;
+    }
+  }
+  __syncthreads();
+  // fragment bytes, one 32-bit word (4 consecutive K elements) per thread step
+  const int kc = d / 64, kq = m / 64;
+  uint32_t* fc = reinterpret_cast<uint32_t*>(base + pqi::prep_off_frag_c(d, m));
+  uint32_t* fq = reinterpret_cast<uint32_t*>(base + pqi::prep_off_frag_q(d, m));
+  const int words_c = 3 * kc * 256, words_q = 3 * kq * 256;
+  for (int wi = threadIdx.x; wi < words_c + words_q; wi += blockDim.x) {
+    const bool qjl = wi >= words_c;
+    const int w = qjl ? wi - words_c : wi;
+    const int blk = w >> 8, inblk = w & 255;          // 1 KiB block = 256 words
+    const int nk = qjl ? kq : kc;
+    const int l = blk / nk, k = blk % nk;
+    const int L = inblk >> 2, byte0 = 4 * (inblk & 3);
+    const int r = L & 15, gq = L >> 4;
+    const float* src = qjl ? sq + (int64_t)r * m : qrot + (int64_t)r * d;
+    const float s = scale[(qjl ? pqi::kScoreRows : 0) + r];
+    uint32_t word = 0;
+    for (int b = 0; b < 4; ++b) {
+      const int i = byte0 + b;
+      const int e = qjl ? (m / 4) * gq + 16 * k + i : 64 * k + 16 * gq + i;
+      word |= (uint32_t)(limb_of(quant_int(src[e], s), l) & 0xff) << (8 * b);
+    }
+    (qjl ? fq : fc)[w] = word;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Two-stage score on the int8 matrix cores.
+//
+// score = n16/d <qrot, c[code]> + rnorm16 sqrt(pi/2)/m <sq, 2 b - 1>.  The codebook is
+// antisymmetric and code 2^b-1-k is the bitwise complement of k, so c[code] is a sum of
+// odd Walsh functions of the code bits: c[code] = sum_p alpha_p s_p(code) with
+// s_p = 2 u_p - 1, u_p = parity(code & mask_p).  Each <qrot, s_p> is then an exact
+// integer product of the query limbs with 0/1 bytes, like the QJL term.  A rows: the 16
+// query rows; B columns: 16 tokens; lane (token r, group gq) holds code bytes
+// 64 k + 16 gq + 0..15 of its token.
+// ------------------------------------------------------------------------------------------
+// Bytes {0, 1}: parity of (code & mask) for the four codes of w (mask folds to a constant
+// once the plane loop is unrolled).
+__device__ __forceinline__ int plane_bytes(uint32_t w, uint32_t mask) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (mask & (1u << i)) x ^= w >> i;
+  return (int)(x & 0x01010101u);
+}
+
+__device__ __forceinline__ i32x4 plane_frag(const uint4& w, uint32_t mask) {
+  return i32x4{plane_bytes(w.x, mask), plane_bytes(w.y, mask), plane_bytes(w.z, mask), plane_bytes(w.w, mask)};
+}
+
+template <int D, int BITS, bool QJL>
+__global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageArgs a, int chunks_per_group) {
+  constexpr int KC = D / 64;
+  constexpr int NP = 1 << (BITS - 1);
+  const int m = QJL ? a.m : 0;
+  const int KQ = m >> 6, mb = m >> 3;
+  const int grp = blockIdx.x / chunks_per_group, chunk = blockIdx.x % chunks_per_group;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const unsigned char* src = a.prep + (int64_t)grp * pqi::prep_head_bytes(D, m);
+  {
+    const int64_t off = pqi::prep_off_meta(D, m);
+    const int nbytes = (int)(pqi::prep_head_bytes(D, m) - off);
+    const uint4* s4 = reinterpret_cast<const uint4*>(src + off);
+    uint4* d4 = reinterpret_cast<uint4*>(smem);
+    for (int i = threadIdx.x; i < nbytes / 16; i += blockDim.x) d4[i] = s4[i];
+  }
+  __syncthreads();
+  const float* scale = reinterpret_cast<const float*>(smem);
+  const int* isum = reinterpret_cast<const int*>(smem + 128);
+  const i32x4* fc = reinterpret_cast<const i32x4*>(smem + 256);
+  const i32x4* fq = fc + 3 * KC * 64;
+
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, gq = lane >> 4;
+  const int64_t T = a.n_tok;
+  const int64_t n_tiles = (T + 15) >> 4;
+  const uint8_t* codes = a.codes + (int64_t)grp * T * D;
+  const uint16_t* norms = a.norms + (int64_t)grp * T;
+  const uint8_t* qbits = QJL ? a.qbits + (int64_t)grp * T * mb : nullptr;
+  const uint16_t* rnorms = QJL ? a.rnorms + (int64_t)grp * T : nullptr;
+  float* out = a.scores + (int64_t)grp * a.n_q * T;
+  const double cq = QJL ? 1.2533141373155003 / (double)m : 0.0;     // sqrt(pi/2) / m
+
+  for (int64_t tile = (int64_t)chunk * kWaves + (threadIdx.x >> 6); tile < n_tiles;
+       tile += (int64_t)chunks_per_group * kWaves) {
+    const int64_t tok = tile * 16 + r;
+    const bool valid = tok < T;
+    uint4 cw[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      cw[k] = make_uint4(0, 0, 0, 0);
+      if (valid) {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + tok * D + 64 * k + 16 * gq));
+        cw[k] = make_uint4(w.x, w.y, w.z, w.w);
+      }
+    }
+    i32x4 acc[NP][3];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int l = 0; l < 3; ++l) acc[p][l] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const i32x4 a0 = fc[(0 * KC + k) * 64 + lane];
+      const i32x4 a1 = fc[(1 * KC + k) * 64 + lane];
+      const i32x4 a2 = fc[(2 * KC + k) * 64 + lane];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const i32x4 b = plane_frag(cw[k], pqi::plane_mask(BITS, p));
+        acc[p][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc[p][0], 0, 0, 0);
+        acc[p][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc[p][1], 0, 0, 0);
+        acc[p][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b, acc[p][2], 0, 0, 0);
+      }
+    }
+    i32x4 accq[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+    if constexpr (QJL) {
+      const uint8_t* kb = qbits + tok * mb + (mb >> 2) * gq;
+      for (int k = 0; k < KQ; ++k) {
+        uint32_t w16 = 0;
+        if (valid) w16 = *reinterpret_cast<const uint16_t*>(kb + 2 * k);
+        const i32x4 b = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
+                         (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
+        accq[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(0 * KQ + k) * 64 + lane], b, accq[0], 0, 0, 0);
+        accq[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(1 * KQ + k) * 64 + lane], b, accq[1], 0, 0, 0);
+        accq[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(2 * KQ + k) * 64 + lane], b, accq[2], 0, 0, 0);
+      }
+    }
+    if (valid) {
+      const double n16 = (double)f16_to_f32(norms[tok]) / (double)D;
+      const double rn = QJL ? (double)f16_to_f32(rnorms[tok]) * cq : 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = 4 * gq + i;
+        if (qi < a.n_q) {
+          double first = 0.0;
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const double S = 16384.0 * (double)acc[p][0][i] + 128.0 * (double)acc[p][1][i] + (double)acc[p][2][i];
+            first += a.alpha[p] * (2.0 * S - (double)isum[qi]);
+          }
+          double val = n16 * (double)scale[qi] * first;
+          if constexpr (QJL) {
+            const double S = 16384.0 * (double)accq[0][i] + 128.0 * (double)accq[1][i] + (double)accq[2][i];
+            val += rn * (double)scale[16 + qi] * (2.0 * S - (double)isum[16 + qi]);
+          }
+          out[(int64_t)qi * T + tok] = (float)val;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // launch helpers
 // ------------------------------------------------------------------------------------------
 int grid_for(int64_t n_tiles, const pqi::LaunchCfg& c, int per_cu) {
@@ -775,9 +1013,53 @@ hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hi
   return hipGetLastError();
 }
 
+template <int D, int BITS>
+hipError_t launch_two_stage_db(const pqi::TwoStageArgs& a, int grid, int cpg, size_t lds, hipStream_t s) {
+  if (a.m > 0) hipLaunchKernelGGL((pq_score_kernel<D, BITS, true>), grid, kThreads, lds, s, a, cpg);
+  else hipLaunchKernelGGL((pq_score_kernel<D, BITS, false>), grid, kThreads, lds, s, a, cpg);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_two_stage_d(int bits, const pqi::TwoStageArgs& a, int grid, int cpg, size_t lds, hipStream_t s) {
+  switch (bits) {
+    case 1: return launch_two_stage_db<D, 1>(a, grid, cpg, lds, s);
+    case 2: return launch_two_stage_db<D, 2>(a, grid, cpg, lds, s);
+    case 3: return launch_two_stage_db<D, 3>(a, grid, cpg, lds, s);
+    case 4: return launch_two_stage_db<D, 4>(a, grid, cpg, lds, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 namespace pqi {
+
+hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(pq_query_rotate_kernel, a.n_heads * kScoreRows, 256, 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pq_query_quant_kernel, a.n_heads, 256, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const LaunchCfg& c, hipStream_t s) {
+  const int64_t n_tiles = (a.n_tok + 15) >> 4;
+  int64_t per_group = ((int64_t)c.cu_count * 2 + a.n_heads - 1) / a.n_heads;
+  const int64_t max_per_group = (n_tiles + kWaves - 1) / kWaves;
+  if (per_group > max_per_group) per_group = max_per_group;
+  if (per_group < 1) per_group = 1;
+  const int grid = (int)(per_group * a.n_heads);
+  const size_t lds = (size_t)(prep_head_bytes(d, a.m) - prep_off_meta(d, a.m));
+  switch (d) {
+    case 64: return launch_two_stage_d<64>(bits, a, grid, (int)per_group, lds, s);
+    case 128: return launch_two_stage_d<128>(bits, a, grid, (int)per_group, lds, s);
+    case 256: return launch_two_stage_d<256>(bits, a, grid, (int)per_group, lds, s);
+    case 512: return launch_two_stage_d<512>(bits, a, grid, (int)per_group, lds, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 
 hipError_t launch_quantize(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {
   switch (d) {

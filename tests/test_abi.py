@@ -111,6 +111,32 @@ def test_other_entry_points_validate():
     assert lib.qjl_score(96, 4, 8, 32, 64, P16, P16, P16, P16, NUL) == pq.PQ_EUNSUPPORTED   # m % 64
 
 
+def test_two_stage_entry_points_validate():
+    lib = pq.lib()
+    assert lib.pq_query_prep_bytes(100, 0, 1) == -1
+    assert lib.pq_query_prep_bytes(128, 96, 1) == -1
+    assert lib.pq_query_prep_bytes(128, 0, 2) == 2 * (112 * 128 + 256)
+    assert lib.pq_query_prep_bytes(512, 512, 8) == 8 * (112 * 1024 + 256)
+    # pq_query_prep(d, m, n_heads, n_q, q, signs, proj, prep, stream)
+    assert lib.pq_query_prep(128, 128, 2, 17, P16, P16, P16, P16, NUL) == pq.PQ_EINVAL      # n_q > 16
+    assert lib.pq_query_prep(128, 0, 2, 4, P16, P16, P16, P16, NUL) == pq.PQ_EINVAL         # proj without m
+    assert lib.pq_query_prep(128, 96, 2, 4, P16, P16, P16, P16, NUL) == pq.PQ_EUNSUPPORTED  # m % 64
+    assert lib.pq_query_prep(128, 128, 2, 4, P16, P16, P16, P2, NUL) == pq.PQ_EINVAL        # prep alignment
+    assert lib.pq_query_prep(128, 128, 0, 4, NUL, NUL, NUL, NUL, NUL) == pq.PQ_OK           # no heads
+    # pq_score(d, bits, m, n_heads, n_q, n_tok, prep, codes, norms, qbits, rnorms, scores, stream)
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("d", 256), ("bits", 3), ("m", 256), ("h", 2), ("nq", 16), ("t", 100), ("prep", P16), ("codes", P16),
+        ("norms", P16), ("qb", P16), ("rn", P16), ("out", P16), ("s", NUL))]
+    assert lib.pq_score(*args(bits=5)) == pq.PQ_EUNSUPPORTED
+    assert lib.pq_score(*args(bits=0)) == pq.PQ_EINVAL
+    assert lib.pq_score(*args(d=512, m=1024)) == pq.PQ_EUNSUPPORTED                        # d + m > 1344
+    assert lib.pq_score(*args(nq=17)) == pq.PQ_EINVAL
+    assert lib.pq_score(*args(m=0)) == pq.PQ_EINVAL                                         # bits without m
+    assert lib.pq_score(*args(qb=NUL)) == pq.PQ_EINVAL
+    assert lib.pq_score(*args(codes=ctypes.c_void_p(0x10008))) == pq.PQ_EINVAL
+    assert lib.pq_score(*args(t=0, prep=NUL, codes=NUL)) == pq.PQ_OK
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="needs a machine without a GPU")
 def test_valid_call_without_gpu_reports_hip_error():
     # arguments pass validation, so the library reaches the HIP runtime, which has no device
