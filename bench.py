@@ -6,7 +6,8 @@ m = 64 residual projections), all inputs resident in HBM.  Eight buffer sets
 are rotated so that no step finds its data in the 256 MB Infinity Cache.
 
 Prints one JSON line.  ``value`` is input bytes / (quantize + dequantize
-kernel time), in GB/s.  The roofline entry is for the quantize kernel:
+kernel time), in GB/s.  ``parts`` adds the QJL half of the metric on the
+config-4 key cache: sketch and score rates in keys/s.  The roofline entry is for the quantize kernel:
 algorithmic bytes per launch (input read + codes, norms, sign bits and residual
 norms written) over its average duration measured with HIP events on the
 stream the kernels run on.  ``cpu_baseline`` times the oracle on the host on a
@@ -26,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 N_SETS = 8
 
 
@@ -37,6 +39,7 @@ def _args():
     ap.add_argument("--cpu-sample-blocks", type=int, default=131072,
                     help="blocks of the workload the oracle baseline processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-qjl", action="store_true", help="skip the config-4 QJL sketch/score leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -90,6 +93,58 @@ def cpu_baseline(n_blocks):
     return {"value": round(in_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": "first %d of 131072 blocks of the 4096x4096 weight (%.1f MB of bf16 input), "
                       "quantize + QJL residual + dequantize, %.2f s" % (n_blocks, in_bytes / 1e6, dt)}
+
+
+def qjl_leg(pq, synth, torch, steps, warmup):
+    """Config 4: QJL sketch of the 4x8x32768x128 bf16 key cache (m=256), then the
+    GQA score of one query token (32 heads) against every key.  Returns the timings
+    and rates for the JSON line."""
+    c = synth.config4()
+    B, Hkv, T, d = c["keys"].shape
+    Hq, m = c["q"].shape[1], c["m"]
+    n_keys = B * Hkv * T
+    dev = torch.device("cuda:0")
+    keys_host = torch.from_numpy(c["keys"].view(np.int16)).view(torch.bfloat16)
+    G = torch.from_numpy(c["G"].view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(c["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+    key_sets = [keys_host.to(dev) for _ in range(2)]          # 2 x 256 MiB: beyond the last-level cache
+    bits0, norms0 = pq.qjl_sketch(key_sets[0], G)
+    sketch_out = [(torch.empty_like(bits0), torch.empty_like(norms0)) for _ in range(2)]
+    score_in = [(bits0.clone(), norms0.clone()) for _ in range(N_SETS)]   # 8 x 34 MiB of bits and norms
+    sq = pq.qjl_project(q, G)
+    scores = [torch.empty((B, Hq, T), dtype=torch.float32, device=dev) for _ in range(2)]
+    for k in range(warmup):
+        pq.qjl_sketch(key_sets[k % 2], G, out=sketch_out[k % 2])
+        pq.qjl_score(pq.qjl_project(q, G, out=sq), *score_in[k % N_SETS], B, Hkv, Hq, T, out=scores[k % 2])
+    big = torch.randn(8192, 8192, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    _ = big @ big
+    for k in range(steps):
+        ev[k][0].record()
+        pq.qjl_sketch(key_sets[k % 2], G, out=sketch_out[k % 2])
+        ev[k][1].record()
+        pq.qjl_project(q, G, out=sq)
+        ev[k][2].record()
+        pq.qjl_score(sq, *score_in[k % N_SETS], B, Hkv, Hq, T, out=scores[k % 2])
+        ev[k][3].record()
+    torch.cuda.synchronize()
+    t_sk = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(steps)])) * 1e-3
+    t_pr = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(steps)])) * 1e-3
+    t_sc = float(np.mean([ev[k][2].elapsed_time(ev[k][3]) for k in range(steps)])) * 1e-3
+    sk_bytes = n_keys * d * 2 + n_keys * (m // 8) + n_keys * 2
+    sc_bytes = n_keys * (m // 8) + n_keys * 2 + B * Hq * T * 4 + B * Hq * m * 4
+    sk_flops = 2.0 * n_keys * d * m
+    return {
+        "qjl_config": "config4: keys 4x8x32768x128 bf16, m=256, 32 query heads (GQA 4:1)",
+        "qjl_sketch_us": round(t_sk * 1e6, 3), "qjl_sketch_keys_per_s": round(n_keys / t_sk, 1),
+        "qjl_sketch_hbm_frac": round(sk_bytes / t_sk / 1e9 / HBM_PEAK_GBS, 4),
+        "qjl_sketch_mfma_frac": round(sk_flops / t_sk / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "qjl_project_us": round(t_pr * 1e6, 3),
+        "qjl_score_us": round(t_sc * 1e6, 3), "qjl_score_keys_per_s": round(n_keys / t_sc, 1),
+        "qjl_score_hbm_frac": round(sc_bytes / t_sc / 1e9 / HBM_PEAK_GBS, 4),
+        "qjl_sketch_algorithmic_bytes": sk_bytes, "qjl_score_algorithmic_bytes": sc_bytes,
+    }
 
 
 def main():
@@ -198,6 +253,8 @@ def main():
                      "algorithmic_bytes_per_launch": q_bytes},
         "kernel_source": kernel_source_hash(),
     }
+    if not args.no_qjl:
+        rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_blocks)
     print(json.dumps(rec), flush=True)
