@@ -40,6 +40,8 @@ def _args():
                     help="blocks of the workload the oracle baseline processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qjl", action="store_true", help="skip the config-4 QJL sketch/score leg")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 output under DIR, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -67,9 +69,10 @@ def counter_traffic(kernel_name):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(n_blocks):
+def cpu_baseline(n_blocks, min_seconds=10.0):
     """Time the oracle (quantize + QJL residual + dequantize) on the first n_blocks of
-    the workload, on the host cores; returns the record for the JSON line."""
+    the workload, on the host cores, repeating the pass until min_seconds have elapsed;
+    returns the record for the JSON line."""
     import synth
     import oracle
     from oracle import numerics, hadamard
@@ -83,16 +86,101 @@ def cpu_baseline(n_blocks):
     x = numerics.bf16_from_bits(c["x"].reshape(-1, d)[:n_blocks])
     D = hadamard.signs_from_mask(c["signs"], d)
     G = numerics.bf16_from_bits(c["G"])
-    t0 = time.perf_counter()
-    q = oracle.codec.quantize(x, bits, D)
-    r = oracle.codec.qjl_residual(x, q["codes"], q["n16"], bits, D, G)
-    xh = oracle.codec.dequantize(q["codes"], q["n16"], bits, D)
-    dt = time.perf_counter() - t0
-    assert r["bits"].shape[0] == n_blocks and xh.shape == x.shape
+    reps, dt = 0, 0.0
+    while dt < min_seconds:
+        t0 = time.perf_counter()
+        q = oracle.codec.quantize(x, bits, D)
+        r = oracle.codec.qjl_residual(x, q["codes"], q["n16"], bits, D, G)
+        xh = oracle.codec.dequantize(q["codes"], q["n16"], bits, D)
+        dt += time.perf_counter() - t0
+        reps += 1
+        assert r["bits"].shape[0] == n_blocks and xh.shape == x.shape
     in_bytes = n_blocks * d * 2
-    return {"value": round(in_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(in_bytes * reps / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": "first %d of 131072 blocks of the 4096x4096 weight (%.1f MB of bf16 input), "
-                      "quantize + QJL residual + dequantize, %.2f s" % (n_blocks, in_bytes / 1e6, dt)}
+                      "quantize + QJL residual + dequantize, %d passes in %.2f s" % (
+                          n_blocks, in_bytes / 1e6, reps, dt)}
+
+
+def summarize(run_dir):
+    """Write the committed profile summaries from the rocprofv3 output of the commands
+    listed in them (run_dir holds prof_trace/, pmc_q_fetch/, pmc_q_write/, pmc_c_fetch/,
+    pmc_c_write/ as written there)."""
+    import csv
+    out_dir = os.path.join(ROOT, "profiles")
+
+    def rows(sub, name):
+        with open(os.path.join(run_dir, sub, name)) as fh:
+            return list(csv.DictReader(fh))
+
+    def short(name):
+        return name.replace("void ", "").replace("(anonymous namespace)::", "").split("(pqi::")[0]
+
+    trace_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/prof_trace -o trace -- "
+                 "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
+    lines = ["# Kernel durations of the benchmark (config 2 codec + config 4 QJL leg), one MI355X",
+             "", "command: " + trace_cmd, "kernel source hash: " + kernel_source_hash(), "",
+             "%-58s %6s %12s %10s %10s" % ("kernel", "calls", "average_ns", "min_ns", "max_ns")]
+    for r in rows("prof_trace", "trace_kernel_stats.csv"):
+        n = short(r["Name"])
+        if any(k in n for k in ("pq_", "qjl_")):
+            lines.append("%-58s %6s %12.1f %10s %10s" % (n, r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"]))
+    with open(os.path.join(out_dir, "bench_kernels_config2_config4_trace.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    def counter(sub, prefix, kernel):
+        vals = [float(r["Counter_Value"]) for r in rows(sub, prefix + "_counter_collection.csv")
+                if kernel in r["Kernel_Name"]]
+        return sum(vals) / len(vals), len(vals)
+
+    copy_bytes = 512 << 20
+    cf, _ = counter("pmc_c_fetch", "c_fetch", "__amd_rocclr_copyBuffer")
+    cw, _ = counter("pmc_c_write", "c_write", "__amd_rocclr_copyBuffer")
+    f_fetch, f_write = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    rec = {"source_hash": kernel_source_hash(),
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_q_fetch -o q_fetch -- "
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_q_write -o q_write -- "
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_c_fetch -o c_fetch -- "
+               "python3 bench.py --calibrate-copy",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_c_write -o c_write -- "
+               "python3 bench.py --calibrate-copy"],
+           "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib": cf, "write_size_kib": cw,
+                           "fetch_factor": f_fetch, "write_factor": f_write},
+           "kernels": {}}
+    for kname, key in (("pq_quantize_kernel", "pq_quantize_kernel"), ("pq_dequantize_kernel", "pq_dequantize_kernel")):
+        fk, nf = counter("pmc_q_fetch", "q_fetch", kname)
+        wk, nw = counter("pmc_q_write", "q_write", kname)
+        rec["kernels"][key] = {"dispatches": [nf, nw], "fetch_size_kib": fk, "write_size_kib": wk,
+                               "hbm_bytes_per_launch": round(fk * 1024 * f_fetch + wk * 1024 * f_write)}
+    with open(os.path.join(out_dir, "pq_quantize_config2_counters.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print("\n".join(lines))
+    print(json.dumps(rec["kernels"]))
+
+
+_BIG = {}
+
+
+def timed(torch, fn, steps):
+    """Average duration (s) of fn(k), k = 0..steps-1, launched back to back on the current
+    stream with HIP events recorded only before the first and after the last launch.  A
+    large matmul queued first keeps the GPU busy while the launches are enqueued."""
+    if "m" not in _BIG:
+        _BIG["m"] = torch.randn(8192, 8192, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    _ = _BIG["m"] @ _BIG["m"]
+    e0.record()
+    for k in range(steps):
+        fn(k)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
 
 
 def qjl_leg(pq, synth, torch, steps, warmup):
@@ -116,22 +204,18 @@ def qjl_leg(pq, synth, torch, steps, warmup):
     for k in range(warmup):
         pq.qjl_sketch(key_sets[k % 2], G, out=sketch_out[k % 2])
         pq.qjl_score(pq.qjl_project(q, G, out=sq), *score_in[k % N_SETS], B, Hkv, Hq, T, out=scores[k % 2])
-    big = torch.randn(8192, 8192, device=dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    _ = big @ big
-    for k in range(steps):
-        ev[k][0].record()
+    def sketch(k):
         pq.qjl_sketch(key_sets[k % 2], G, out=sketch_out[k % 2])
-        ev[k][1].record()
+
+    def project(k):
         pq.qjl_project(q, G, out=sq)
-        ev[k][2].record()
+
+    def score(k):
         pq.qjl_score(sq, *score_in[k % N_SETS], B, Hkv, Hq, T, out=scores[k % 2])
-        ev[k][3].record()
-    torch.cuda.synchronize()
-    t_sk = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(steps)])) * 1e-3
-    t_pr = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(steps)])) * 1e-3
-    t_sc = float(np.mean([ev[k][2].elapsed_time(ev[k][3]) for k in range(steps)])) * 1e-3
+
+    t_sk = timed(torch, sketch, steps)
+    t_pr = timed(torch, project, steps)
+    t_sc = timed(torch, score, steps)
     sk_bytes = n_keys * d * 2 + n_keys * (m // 8) + n_keys * 2
     sc_bytes = n_keys * (m // 8) + n_keys * 2 + B * Hq * T * 4 + B * Hq * m * 4
     sk_flops = 2.0 * n_keys * d * m
@@ -149,6 +233,9 @@ def qjl_leg(pq, synth, torch, steps, warmup):
 
 def main():
     args = _args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
               "(the codec shards by blocks with no exchange, see DESIGN.md)" % args.gpus, file=sys.stderr)
@@ -189,39 +276,29 @@ def main():
         out = torch.empty((n_blocks, d), dtype=torch.bfloat16, device=dev)
         sets.append((x, codes, norms, qb, rn, out))
 
-    def step(k, evs=None):
-        x, codes, norms, qb, rn, out = sets[k % N_SETS]
-        if evs is not None:
-            evs[0].record()
+    def quant(k):
+        x, codes, norms, qb, rn, _ = sets[k % N_SETS]
         pq.quantize(x, d, bits, signs, proj, out=(codes, norms, qb, rn))
-        if evs is not None:
-            evs[1].record()
+
+    def dequant(k):
+        _, codes, norms, _, _, out = sets[k % N_SETS]
         pq.dequantize(codes, norms, d, bits, signs, out=out)
-        if evs is not None:
-            evs[2].record()
+
+    def step(k):
+        quant(k)
+        dequant(k)
 
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-
-    # keep the GPU busy while the timed steps are enqueued, so that no kernel waits for its launch
-    big = torch.randn(8192, 8192, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    _ = big @ big
-    for k in range(args.steps):
-        step(k, evs[k])
-    torch.cuda.synchronize()
-
-    tq = np.array([evs[k][0].elapsed_time(evs[k][1]) for k in range(args.steps)]) * 1e-3   # s
-    td = np.array([evs[k][1].elapsed_time(evs[k][2]) for k in range(args.steps)]) * 1e-3
-    total = evs[0][0].elapsed_time(evs[-1][2]) * 1e-3
-    t_q, t_d = float(np.mean(tq)), float(np.mean(td))
+    t_q = timed(torch, quant, args.steps)
+    t_d = timed(torch, dequant, args.steps)
+    t_step = timed(torch, step, args.steps)
 
     in_bytes = n_blocks * d * 2
     q_bytes = in_bytes + n_blocks * d + n_blocks * 2 + n_blocks * (m // 8) + n_blocks * 2
     dq_bytes = n_blocks * d + n_blocks * 2 + in_bytes
-    value = in_bytes / (t_q + t_d) / 1e9
+    value = in_bytes / t_step / 1e9
     q_gbs = q_bytes / t_q / 1e9
     traffic = counter_traffic("pq_quantize_kernel")
 
@@ -232,7 +309,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(total / args.steps * 1e3, 5),
+        "ms_per_step": round(t_step * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
