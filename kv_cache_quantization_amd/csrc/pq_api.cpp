@@ -248,7 +248,7 @@ int qjl_project(int d, int m, const uint16_t* q, int64_t n_q, const uint16_t* pr
   if (n_q < 0 || n_q > (int64_t)INT32_MAX / m) return PQ_EINVAL;
   if (n_q == 0) return PQ_OK;
   if (!q || !proj || !sq) return PQ_EINVAL;
-  if (!aligned(q, 2) || !aligned(proj, 2) || !aligned(sq, 4)) return PQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(proj, 16) || !aligned(sq, 4)) return PQ_EINVAL;
   pqi::ProjectArgs a;
   a.q = q; a.n_q = n_q; a.proj = proj; a.sq = sq; a.d = d; a.m = m;
   return hip_status(pqi::launch_project(a, (hipStream_t)stream));
@@ -265,7 +265,7 @@ int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const
   if (n_keys > kMaxElems / ((int64_t)batch * q_heads + 1)) return PQ_EINVAL;
   if (batch == 0 || n_keys == 0) return PQ_OK;
   if (!sq || !bits || !norms || !scores) return PQ_EINVAL;
-  if (!aligned(sq, 4) || !aligned(scores, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  if (!aligned(sq, 4) || !aligned(bits, 16) || !aligned(scores, 4) || !aligned(norms, 2)) return PQ_EINVAL;
   pqi::LaunchCfg cfg;
   int st2 = launch_cfg(&cfg);
   if (st2) return st2;

@@ -26,7 +26,7 @@ constexpr int kWaves = kThreads / 64;
 #define PQ_QUANT_WAVES_PER_EU 1
 #endif
 #ifndef PQ_SKETCH_WG_PER_CU
-#define PQ_SKETCH_WG_PER_CU 4
+#define PQ_SKETCH_WG_PER_CU 2
 #endif
 
 // ------------------------------------------------------------------------------------------
@@ -134,29 +134,6 @@ __device__ __forceinline__ bf16x8 load_gfrag(const uint4* gl, const uint16_t* pr
     if (row < m) w = reinterpret_cast<const uint4*>(proj)[row * (D / 8) + col8];
   }
   return __builtin_bit_cast(bf16x8, w);
-}
-
-// Write the sign bits of one 16-column N tile for the 16 block rows of a wave.
-// acc[i] of lane l is P[4 (l>>4) + i][16 nt + (l & 15)]; a ballot per i gives,
-// in bits 16 g .. 16 g + 15, the 16 signs of block row 4 g + i, which are the
-// little-endian 16-bit value at byte 2 nt of that row (bit j <-> column j, LSB first).
-__device__ __forceinline__ void store_sign_tile(const f32x4& acc, int lane, int64_t row0, int64_t nrows,
-                                                uint8_t* bits, int mb, int nt) {
-  const uint64_t b0 = __ballot(acc[0] > 0.0f);
-  const uint64_t b1 = __ballot(acc[1] > 0.0f);
-  const uint64_t b2 = __ballot(acc[2] > 0.0f);
-  const uint64_t b3 = __ballot(acc[3] > 0.0f);
-  if (lane < 16) {
-    const int i = lane & 3, gg = lane >> 2;
-    const uint64_t b = i == 0 ? b0 : i == 1 ? b1 : i == 2 ? b2 : b3;
-    const uint32_t chunk = (uint32_t)(b >> (16 * gg)) & 0xffffu;
-    const int64_t row = row0 + lane;
-    if (row < nrows) {
-      uint8_t* dst = bits + row * (int64_t)mb + 2 * nt;
-      dst[0] = (uint8_t)chunk;
-      if (2 * nt + 1 < mb) dst[1] = (uint8_t)(chunk >> 8);
-    }
-  }
 }
 
 // Sign bits of one 16-column N tile: b_i is the ballot of acc[i] > 0, whose bits
@@ -535,11 +512,13 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 }
 
 // ------------------------------------------------------------------------------------------
-// QJL key sketch: norm + sign(G k), keys feed the MFMA directly (bf16 products are exact)
+// QJL key sketch: norm + sign(G k), keys feed the MFMA directly (bf16 products are exact).
+// A wave takes NT key tiles per pass, so every G fragment read from LDS feeds NT MFMAs.
 // ------------------------------------------------------------------------------------------
 template <int D, bool G_LDS>
 __global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchArgs a) {
   constexpr int KS = D / 32;
+  constexpr int NT = D <= 128 ? 4 : (D == 256 ? 2 : 1);
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* gl = reinterpret_cast<uint4*>(smem);
   const int m = a.m, m_pad = (m + 15) & ~15, mb = m >> 3;
@@ -549,73 +528,178 @@ __global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchA
   }
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
+  const int myq = lane >> 4, ri = r & 3, rg = r >> 2;
+  const int ntiles = m_pad >> 4;
   const int64_t n_keys = a.n_keys;
   const int64_t n_tiles = (n_keys + 15) >> 4;
+  const int64_t n_pass = (n_tiles + NT - 1) / NT;
   const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)gridDim.x * kWaves;
 
-  for (int64_t T = wave_id; T < n_tiles; T += n_waves) {
-    const int64_t key = T * 16 + r;
-    const bool valid = key < n_keys;
-    bf16x8 kf[KS];
-    float ss = 0.0f;
-    const uint4* src = reinterpret_cast<const uint4*>(a.keys + key * D);
+  // keys of pass P: lane quarter g holds elements 32 s + 8 g .. +7 of key row r of each tile
+  auto load_pass = [&](int64_t P, u32x4 (&w)[NT][KS]) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (valid) w = src[4 * s + g];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float lo = bf16_lo(ww[u]), hi = bf16_hi(ww[u]);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
-      kf[s] = __builtin_bit_cast(bf16x8, w);
-    }
-    ss = sum4(ss);
-    if (valid && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
-    for (int nt = 0; nt < (m_pad >> 4); ++nt) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      const int row = 16 * nt + r;
+    for (int t = 0; t < NT; ++t) {
+      const int64_t key = (P * NT + t) * 16 + r;
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.keys + key * D);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 b = load_gfrag<D, G_LDS>(gl, a.proj, m, row, 4 * s + g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], b, acc, 0, 0, 0);
+        w[t][s] = u32x4{0, 0, 0, 0};
+        if (P < n_pass && key < n_keys) w[t][s] = __builtin_nontemporal_load(src + 4 * s + g);
       }
-      store_sign_tile(acc, lane, T * 16, n_keys, a.bits, mb, nt);
+    }
+  };
+  u32x4 kw[NT][KS];
+  load_pass(wave_id, kw);
+  for (int64_t P = wave_id; P < n_pass; P += n_waves) {
+    bf16x8 kf[NT][KS];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[t][s] = __builtin_bit_cast(bf16x8, kw[t][s]);
+    // the next pass's keys are in flight while this one is sketched
+    load_pass(P + n_waves, kw);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t key = (P * NT + t) * 16 + r;
+      float ss = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 w = __builtin_bit_cast(u32x4, kf[t][s]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float lo = bf16_lo(w[u]), hi = bf16_hi(w[u]);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+      }
+      ss = sum4(ss);
+      if (key < n_keys && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
+    }
+    for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
+      uint32_t mychunk[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) mychunk[t] = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (nt0 + q < ntiles) {
+          const int row = 16 * (nt0 + q) + r;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const bf16x8 b = load_gfrag<D, G_LDS>(gl, a.proj, m, row, 4 * s + g);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], b, acc[t], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint32_t c = sign_chunk(__ballot(acc[t][0] > 0.0f), __ballot(acc[t][1] > 0.0f),
+                                        __ballot(acc[t][2] > 0.0f), __ballot(acc[t][3] > 0.0f), ri, rg);
+          mychunk[t] = myq == q ? c : mychunk[t];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) store_sign_chunk(mychunk[t], lane, (P * NT + t) * 16, n_keys, a.bits, mb, nt0);
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Query projection sq = G q (fp32), one thread per output value
+// Query projection sq = G q (fp32) on the bf16 matrix cores: one wave per 16 x 16 tile of
+// (query, projection row); the bf16 products are exact and accumulate in fp32.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void qjl_project_kernel(const pqi::ProjectArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.n_q * a.m) return;
-  const int64_t qi = idx / a.m;
-  const int n = (int)(idx % a.m);
-  const uint16_t* q = a.q + qi * a.d;
-  const uint16_t* gr = a.proj + (int64_t)n * a.d;
-  float acc = 0.0f;
-  for (int e = 0; e < a.d; ++e) acc = fmaf(bf16_to_f32(gr[e]), bf16_to_f32(q[e]), acc);
-  a.sq[idx] = acc;
+__global__ __launch_bounds__(64) void qjl_project_kernel(const pqi::ProjectArgs a) {
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t q0 = (int64_t)blockIdx.x * 16;
+  const int n0 = blockIdx.y * 16;
+  const int d = a.d;
+  const int64_t qrow = q0 + r;
+  const int nrow = n0 + r;
+  const uint4* qs = reinterpret_cast<const uint4*>(a.q + qrow * d);
+  const uint4* gs = reinterpret_cast<const uint4*>(a.proj + (int64_t)nrow * d);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < d / 32; ++s) {
+    const uint4 qa = qrow < a.n_q ? qs[4 * s + g] : make_uint4(0, 0, 0, 0);
+    const uint4 gb = nrow < a.m ? gs[4 * s + g] : make_uint4(0, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, gb),
+                                                 acc, 0, 0, 0);
+  }
+  // acc[i] = sq[q0 + 4 g + i][n0 + r]
+  if (nrow < a.m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t qi = q0 + 4 * g + i;
+      if (qi < a.n_q) a.sq[qi * a.m + nrow] = acc[i];
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // QJL score for grouped-query attention on the int8 matrix cores.
 //
 // sum_i (2 b_i - 1) sq_i = 2 sum_i b_i sq_i - sum_i sq_i.  Each projected query
-// is quantized to integers Q_i = rint(sq_i / s), s = max|sq| / 2080768, and
+// is quantized to integers Q_i = rint(sq_i / s), s = max|sq| / kLimbRange, and
 // split into three int8 limbs Q = 16384 h2 + 128 h1 + h0; the bit vectors,
 // expanded to bytes {0, 1}, meet the limbs in v_mfma_i32_16x16x64_i8 with exact
 // int32 accumulation.  A rows: 4 query heads x 4 slots (h2, h1, h0, 0); B columns:
-// 16 keys.  Lane group gq holds bits [m/4 gq, m/4 (gq+1)) of its key.
+// 16 keys.  Lane group gq holds bits [m/4 gq, m/4 (gq+1)) of its key, K step k the
+// 16 bits from m/4 gq + 16 k.  The limbs are built once per workgroup in LDS in
+// A-fragment order (K step k, lane L: 16 bytes at 16 (64 k + L)).
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t spread_nibble(uint32_t nib) {
   // 4 bits -> 4 bytes of value 0/1 (bit j -> byte j)
   return (nib * 0x204081u) & 0x01010101u;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ int wave_sum(int x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ int quant_int(float x, float s) { return s > 0.0f ? (int)rintf(x / s) : 0; }
+
+__device__ __forceinline__ int limb_of(int Q, int l) {
+  const int h2 = (int)rintf((float)Q * (1.0f / 16384.0f));
+  const int rem = Q - 16384 * h2;
+  const int h1 = (int)rintf((float)rem * (1.0f / 128.0f));
+  const int h0 = rem - 128 * h1;
+  return l == 0 ? h2 : l == 1 ? h1 : h0;
+}
+
+// The 2 KS bytes of packed key bits of lane group gq (K steps 0 .. KS-1, 16 bits each).
+template <int KS>
+__device__ __forceinline__ void load_key_bits(const uint8_t* kb, bool valid, uint32_t (&w)[(KS + 1) / 2]) {
+#pragma unroll
+  for (int j = 0; j < (KS + 1) / 2; ++j) w[j] = 0;
+  if (!valid) return;
+  if constexpr (KS % 8 == 0) {
+#pragma unroll
+    for (int j = 0; j < KS / 8; ++j) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb) + j);
+      w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+    }
+  } else if constexpr (KS % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < KS / 4; ++j) {
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kb) + j);
+      w[2 * j] = v.x; w[2 * j + 1] = v.y;
+    }
+  } else if constexpr (KS % 2 == 0) {
+#pragma unroll
+    for (int j = 0; j < KS / 2; ++j) w[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb) + j);
+  } else {
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      w[k >> 1] |= (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(kb) + k) << (16 * (k & 1));
+  }
 }
 
 template <int KS>
@@ -625,83 +709,78 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
   const int grp = blockIdx.x / chunks_per_group;          // (batch, kv head) pair
   const int chunk = blockIdx.x % chunks_per_group;
   const int b = grp / a.kv_heads, gk = grp % a.kv_heads;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 
-  __shared__ float sqs[4][1024];
+  __shared__ i32x4 frag[KS * 64];
   __shared__ float scl[4];
-  __shared__ double sumq[4];
-  for (int i = threadIdx.x; i < 4 * m; i += blockDim.x) {
-    const int hh = i / m, n = i % m;
-    sqs[hh][n] = hh < group ? a.sq[((int64_t)b * a.q_heads + gk * group + hh) * m + n] : 0.0f;
-  }
+  __shared__ int isum[4];
+  for (int i = threadIdx.x; i < KS * 64; i += blockDim.x) frag[i] = i32x4{0, 0, 0, 0};
   __syncthreads();
-  if (threadIdx.x < 4) {
-    const int hh = threadIdx.x;
+  // wave wv quantizes query head wv of the group into A rows 4 wv + limb
+  if (wv < group) {
+    const float* src = a.sq + ((int64_t)b * a.q_heads + gk * group + wv) * m;
     float amax = 0.0f;
-    for (int n = 0; n < m; ++n) amax = fmaxf(amax, fabsf(sqs[hh][n]));
-    const float s = amax / 2080768.0f;
-    double sq_int = 0.0;                                  // exact: integers, |sum| < 2^31
-    for (int n = 0; n < m; ++n) sq_int += s > 0.0f ? (double)rintf(sqs[hh][n] / s) : 0.0;
-    scl[threadIdx.x] = s;
-    sumq[threadIdx.x] = sq_int;
+    for (int e = lane; e < m; e += 64) amax = fmaxf(amax, fabsf(src[e]));
+    const float s = wave_max(amax) / pqi::kLimbRange;
+    int acc = 0;
+    unsigned char* fb = reinterpret_cast<unsigned char*>(frag);
+    for (int e = lane; e < m; e += 64) {
+      const int Q = quant_int(src[e], s);
+      acc += Q;
+      const int gq = e / (m / 4), k = (e % (m / 4)) >> 4, i = e & 15;
+#pragma unroll
+      for (int l = 0; l < 3; ++l) fb[(k * 64 + 16 * gq + 4 * wv + l) * 16 + i] = (unsigned char)(limb_of(Q, l) & 0xff);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      scl[wv] = s;
+      isum[wv] = acc;
+    }
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
   const int r = lane & 15, gq = lane >> 4;
-  // A fragments in registers: row r = 4 hh + limb
-  const int hh = r >> 2, limb = r & 3;
-  const float s_h = scl[hh];
   i32x4 af[KS];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    uint32_t wd[4];
-    for (int u = 0; u < 4; ++u) {
-      uint32_t word = 0;
-      for (int bb = 0; bb < 4; ++bb) {
-        const int i = (m >> 2) * gq + 16 * k + 4 * u + bb;
-        int q = s_h > 0.0f ? (int)rintf(sqs[hh][i] / s_h) : 0;
-        const int h2 = (int)rintf((float)q / 16384.0f);
-        const int rem = q - 16384 * h2;
-        const int h1 = (int)rintf((float)rem / 128.0f);
-        const int h0 = rem - 128 * h1;
-        const int lv = limb == 0 ? h2 : limb == 1 ? h1 : limb == 2 ? h0 : 0;
-        word |= ((uint32_t)(lv & 0xff)) << (8 * bb);
-      }
-      wd[u] = word;
-    }
-    af[k] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
-  }
+  for (int k = 0; k < KS; ++k) af[k] = frag[k * 64 + lane];
 
   const int64_t T = a.n_keys;
   const int64_t n_tiles = (T + 15) >> 4;
   const uint8_t* bits = a.bits + (int64_t)grp * T * mb;
   const uint16_t* norms = a.norms + (int64_t)grp * T;
-  const float c0 = 1.2533141373155003f / (float)m;       // sqrt(pi/2) / m
-  const int lane_bytes = mb >> 2;                          // bytes of one lane group (m/32)
-  const int h_out = gk * group + gq;
+  const double c0 = 1.2533141373155003 / (double)m;       // sqrt(pi/2) / m
+  const bool out_lane = gq < group;
+  const int h_out = gk * group + (out_lane ? gq : 0);
   float* out = a.scores + ((int64_t)b * a.q_heads + h_out) * T;
-  const float s_out = scl[gq & 3];
-  const double sumq_out = sumq[gq & 3];
+  const double s_out = out_lane ? (double)scl[gq] * c0 : 0.0;
+  const double sumq_out = out_lane ? (double)isum[gq] : 0.0;
 
-  for (int64_t tile = (int64_t)chunk * kWaves + (threadIdx.x >> 6); tile < n_tiles;
-       tile += (int64_t)chunks_per_group * kWaves) {
+  const int64_t stride = (int64_t)chunks_per_group * kWaves;
+  int64_t tile = (int64_t)chunk * kWaves + wv;
+  uint32_t wn[(KS + 1) / 2];
+  load_key_bits<KS>(bits + (tile * 16 + r) * mb + (mb >> 2) * gq, tile < n_tiles && tile * 16 + r < T, wn);
+  for (; tile < n_tiles; tile += stride) {
     const int64_t key = tile * 16 + r;
     const bool valid = key < T;
+    uint32_t w[(KS + 1) / 2];
+#pragma unroll
+    for (int j = 0; j < (KS + 1) / 2; ++j) w[j] = wn[j];
+    // the next tile's bits are in flight while this one is scored
+    const int64_t nkey = (tile + stride) * 16 + r;
+    load_key_bits<KS>(bits + nkey * mb + (mb >> 2) * gq, tile + stride < n_tiles && nkey < T, wn);
     i32x4 acc = {0, 0, 0, 0};
-    const uint8_t* kb = bits + key * mb + lane_bytes * gq;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      uint32_t w16 = 0;
-      if (valid) w16 = (uint32_t)kb[2 * k] | ((uint32_t)kb[2 * k + 1] << 8);
+      const uint32_t w16 = (w[k >> 1] >> (16 * (k & 1))) & 0xffffu;
       const i32x4 bf = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
                         (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[k], bf, acc, 0, 0, 0);
     }
-    // lane (gq, key r): acc[i] = sum_i bit * limb_i of head gq
-    if (valid && gq < group) {
+    // lane (gq, key r): acc[l] = sum_i bit_i * limb_l of query head gq
+    if (valid && out_lane) {
       const double S = 16384.0 * (double)acc[0] + 128.0 * (double)acc[1] + (double)acc[2];
       const double nu = (double)f16_to_f32(norms[key]);
-      out[key] = (float)(nu * (double)c0 * (double)s_out * (2.0 * S - sumq_out));
+      out[key] = (float)(nu * s_out * (2.0 * S - sumq_out));
     }
   }
 }
@@ -753,24 +832,6 @@ __global__ __launch_bounds__(256) void pq_query_rotate_kernel(const pqi::QueryPr
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ int wave_sum(int x) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-__device__ __forceinline__ int quant_int(float x, float s) { return s > 0.0f ? (int)rintf(x / s) : 0; }
-
-__device__ __forceinline__ int limb_of(int Q, int l) {
-  const int h2 = (int)rintf((float)Q * (1.0f / 16384.0f));
-  const int rem = Q - 16384 * h2;
-  const int h1 = (int)rintf((float)rem * (1.0f / 128.0f));
-  const int h0 = rem - 128 * h1;
-  return l == 0 ? h2 : l == 1 ? h1 : h0;
-}
 
 __global__ __launch_bounds__(256) void pq_query_quant_kernel(const pqi::QueryPrepArgs a) {
   const int h = blockIdx.x;
@@ -1092,16 +1153,15 @@ hipError_t launch_sketch(int d, const SketchArgs& a, const LaunchCfg& c, hipStre
 }
 
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
-  const int64_t total = a.n_q * a.m;
-  const int grid = (int)((total + 255) / 256);
-  hipLaunchKernelGGL(qjl_project_kernel, grid, 256, 0, s, a);
+  const dim3 grid((unsigned)((a.n_q + 15) / 16), (unsigned)((a.m + 15) / 16));
+  hipLaunchKernelGGL(qjl_project_kernel, grid, 64, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s) {
   const int groups = a.batch * a.kv_heads;
   const int64_t n_tiles = (a.n_keys + 15) >> 4;
-  // enough workgroups to fill the chip, at most one wave per tile
+  // eight workgroups per CU, at most one wave per tile
   int64_t per_group = ((int64_t)c.cu_count * 8 + groups - 1) / groups;
   const int64_t max_per_group = (n_tiles + kWaves - 1) / kWaves;
   if (per_group > max_per_group) per_group = max_per_group;
