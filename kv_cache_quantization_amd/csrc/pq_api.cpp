@@ -195,7 +195,7 @@ int pq_quantize(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, 
   if (!x || !signs || !codes || !norms) return PQ_EINVAL;
   if (m > 0 && (!proj || !qjl_bits || !rnorms)) return PQ_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(norms, 2)) return PQ_EINVAL;
-  if (m > 0 && (!aligned(proj, 16) || !aligned(rnorms, 2))) return PQ_EINVAL;
+  if (m > 0 && (!aligned(proj, 16) || !aligned(qjl_bits, 16) || !aligned(rnorms, 2))) return PQ_EINVAL;
   pqi::LaunchCfg cfg;
   if ((st = launch_cfg(&cfg))) return st;
   pqi::QuantArgs a;
@@ -231,7 +231,7 @@ int qjl_sketch(int d, int m, const uint16_t* keys, int64_t n_keys, const uint16_
   if (n_keys < 0 || n_keys > kMaxElems / d) return PQ_EINVAL;
   if (n_keys == 0) return PQ_OK;
   if (!keys || !proj || !bits || !norms) return PQ_EINVAL;
-  if (!aligned(keys, 16) || !aligned(proj, 16) || !aligned(norms, 2)) return PQ_EINVAL;
+  if (!aligned(keys, 16) || !aligned(proj, 16) || !aligned(bits, 16) || !aligned(norms, 2)) return PQ_EINVAL;
   pqi::LaunchCfg cfg;
   if ((st = launch_cfg(&cfg))) return st;
   pqi::SketchArgs a;

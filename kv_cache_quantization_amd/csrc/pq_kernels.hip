@@ -136,35 +136,43 @@ __device__ __forceinline__ bf16x8 load_gfrag(const uint4* gl, const uint16_t* pr
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Sign bits of one 16-column N tile: b_i is the ballot of acc[i] > 0, whose bits
-// 16 g .. 16 g + 15 hold the signs of block row 4 g + i, i.e. the little-endian
-// 16-bit value at byte 2 nt of that row (column j <-> bit j, least significant first).
-// Returns that chunk for block row rr = 4 gg + i.
-__device__ __forceinline__ uint32_t sign_chunk(uint64_t b0, uint64_t b1, uint64_t b2, uint64_t b3, int i,
-                                               int gg) {
-  const bool hi = (gg & 2) != 0;
-  const uint32_t w0 = hi ? (uint32_t)(b0 >> 32) : (uint32_t)b0;
-  const uint32_t w1 = hi ? (uint32_t)(b1 >> 32) : (uint32_t)b1;
-  const uint32_t w2 = hi ? (uint32_t)(b2 >> 32) : (uint32_t)b2;
-  const uint32_t w3 = hi ? (uint32_t)(b3 >> 32) : (uint32_t)b3;
-  const uint32_t w = (i & 2) ? ((i & 1) ? w3 : w2) : ((i & 1) ? w1 : w0);
-  return __builtin_amdgcn_ubfe(w, 16 * (gg & 1), 16);
+// Sign bits of four 16-column N tiles nt0 .. nt0+3 of G x for 16 blocks (or keys), from
+// MFMAs with G rows as the A operand and the 16 blocks as B: acc[q][i] of lane
+// (block r, quarter gg) is p[r][16 (nt0 + q) + 4 gg + i].  A bit is p > 0, read off the
+// fp32 pattern as med3(int, 0, 1) (+0 and -0 give 0).  Lane quarter gg builds byte q of
+// its word from its 4 bits (nibble gg of the 16-bit chunk of N tile nt0 + q); one
+// permlane16 swap pairs quarters (0,1) and (2,3) into the even and odd output bytes,
+// one permlane32 swap brings both to every quarter, and two byte permutes interleave
+// them.  Returns the 8 output bytes (bits 64 (nt0/4) .. +63, LSB first) in every lane
+// of block r.
+__device__ __forceinline__ uint2 sign_bytes4(const f32x4 (&acc)[4]) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = __float_as_int(acc[q][i]);
+      x |= (uint32_t)min(max(v, 0), 1) << (8 * q + i);
+    }
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const uint32_t z = a[0] | (a[1] << 4);          // quarters (0,1): even bytes, (2,3): odd bytes
+  const auto b = __builtin_amdgcn_permlane32_swap(z, z, false, false);
+  const uint32_t E = b[0], O = b[1];
+  return make_uint2(__builtin_amdgcn_perm(O, E, 0x05010400u), __builtin_amdgcn_perm(O, E, 0x07030602u));
 }
 
-// Lane (q, rr) of the wave stores the chunk of N tile nt0 + q of block row rr.
-__device__ __forceinline__ void store_sign_chunk(uint32_t chunk, int lane, int64_t row0, int64_t nrows,
-                                                 uint8_t* bits, int mb, int nt0) {
-  const int q = lane >> 4, rr = lane & 15;
-  const int64_t row = row0 + rr;
-  const int byte = 2 * (nt0 + q);
-  if (row < nrows && byte < mb) {
-    uint8_t* dst = bits + row * (int64_t)mb + byte;
-    if ((mb & 1) == 0) {
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)chunk;
-    } else {
-      dst[0] = (uint8_t)chunk;
-      if (byte + 1 < mb) dst[1] = (uint8_t)(chunk >> 8);
-    }
+// Lane quarter 0 of block row r writes the 8 bytes at byte 2 nt0 of that row (fewer at
+// the end of a row of mb bytes).
+__device__ __forceinline__ void store_sign_bytes(uint2 w, int lane, int64_t row0, int64_t nrows, uint8_t* bits,
+                                                 int mb, int nt0) {
+  const int64_t row = row0 + (lane & 15);
+  const int byte0 = 2 * nt0;
+  if ((lane >> 4) != 0 || row >= nrows) return;
+  uint8_t* dst = bits + row * (int64_t)mb + byte0;
+  if ((mb & 7) == 0 && byte0 + 8 <= mb) {
+    *reinterpret_cast<uint2*>(dst) = w;
+  } else {
+    for (int j = 0; j < 8 && byte0 + j < mb; ++j) dst[j] = (uint8_t)((j < 4 ? w.x : w.y) >> (8 * (j & 3)));
   }
 }
 
@@ -367,26 +375,22 @@ struct Quantizer {
         }
       }
       const int ntiles = m_pad >> 4;
-      const int myq = lane >> 4, ri = r & 3, rg = r >> 2;
       for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
-        uint32_t mychunk = 0;
+        f32x4 acc[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+          acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           if (nt0 + q < ntiles) {
             const int row = 16 * (nt0 + q) + r;
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
               const f16x8 b = load_gfrag_f16<D, G_LDS>(gl, a.proj, a.signs, m, row, res_col8<D>(g, k));
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ahi[k]), b, acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, alo[k]), b, acc, 0, 0, 0);
+              acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, ahi[k]), acc[q], 0, 0, 0);
+              acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, alo[k]), acc[q], 0, 0, 0);
             }
           }
-          const uint32_t c = sign_chunk(__ballot(acc[0] > 0.0f), __ballot(acc[1] > 0.0f),
-                                        __ballot(acc[2] > 0.0f), __ballot(acc[3] > 0.0f), ri, rg);
-          mychunk = myq == q ? c : mychunk;
         }
-        store_sign_chunk(mychunk, lane, T * 16, n_blocks, a.qbits, mb, nt0);
+        store_sign_bytes(sign_bytes4(acc), lane, T * 16, n_blocks, a.qbits, mb, nt0);
       }
     }
   }
@@ -513,7 +517,8 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 
 // ------------------------------------------------------------------------------------------
 // QJL key sketch: norm + sign(G k), keys feed the MFMA directly (bf16 products are exact).
-// A wave takes NT key tiles per pass, so every G fragment read from LDS feeds NT MFMAs.
+// A wave takes NT key tiles per pass, so every G fragment read from LDS feeds NT MFMAs;
+// G rows are the A operand so that each lane ends with projections of its own key.
 // ------------------------------------------------------------------------------------------
 template <int D, bool G_LDS>
 __global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchArgs a) {
@@ -528,7 +533,6 @@ __global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchA
   }
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int myq = lane >> 4, ri = r & 3, rg = r >> 2;
   const int ntiles = m_pad >> 4;
   const int64_t n_keys = a.n_keys;
   const int64_t n_tiles = (n_keys + 15) >> 4;
@@ -536,73 +540,51 @@ __global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchA
   const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)gridDim.x * kWaves;
 
-  // keys of pass P: lane quarter g holds elements 32 s + 8 g .. +7 of key row r of each tile
-  auto load_pass = [&](int64_t P, u32x4 (&w)[NT][KS]) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int64_t key = (P * NT + t) * 16 + r;
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.keys + key * D);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        w[t][s] = u32x4{0, 0, 0, 0};
-        if (P < n_pass && key < n_keys) w[t][s] = __builtin_nontemporal_load(src + 4 * s + g);
-      }
-    }
-  };
-  u32x4 kw[NT][KS];
-  load_pass(wave_id, kw);
   for (int64_t P = wave_id; P < n_pass; P += n_waves) {
+    // lane quarter g holds elements 32 s + 8 g .. +7 of key row r of each tile
     bf16x8 kf[NT][KS];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[t][s] = __builtin_bit_cast(bf16x8, kw[t][s]);
-    // the next pass's keys are in flight while this one is sketched
-    load_pass(P + n_waves, kw);
+    const bool full = (P + 1) * NT * 16 <= n_keys;          // uniform
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t key = (P * NT + t) * 16 + r;
+      const bool valid = full || key < n_keys;
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.keys + key * D);
       float ss = 0.0f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const u32x4 w = __builtin_bit_cast(u32x4, kf[t][s]);
+        u32x4 w = {0, 0, 0, 0};
+        if (valid) w = __builtin_nontemporal_load(src + 4 * s + g);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float lo = bf16_lo(w[u]), hi = bf16_hi(w[u]);
           ss = fmaf(lo, lo, ss);
           ss = fmaf(hi, hi, ss);
         }
+        kf[t][s] = __builtin_bit_cast(bf16x8, w);
       }
       ss = sum4(ss);
-      if (key < n_keys && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
+      if (valid && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
     }
     for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
-      uint32_t mychunk[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) mychunk[t] = 0;
+      f32x4 acc[NT][4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f32x4 acc[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < NT; ++t) acc[t][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if (nt0 + q < ntiles) {
           const int row = 16 * (nt0 + q) + r;
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             const bf16x8 b = load_gfrag<D, G_LDS>(gl, a.proj, m, row, 4 * s + g);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], b, acc[t], 0, 0, 0);
+            for (int t = 0; t < NT; ++t)
+              acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, kf[t][s], acc[t][q], 0, 0, 0);
           }
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint32_t c = sign_chunk(__ballot(acc[t][0] > 0.0f), __ballot(acc[t][1] > 0.0f),
-                                        __ballot(acc[t][2] > 0.0f), __ballot(acc[t][3] > 0.0f), ri, rg);
-          mychunk[t] = myq == q ? c : mychunk[t];
         }
       }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) store_sign_chunk(mychunk[t], lane, (P * NT + t) * 16, n_keys, a.bits, mb, nt0);
+      for (int t = 0; t < NT; ++t)
+        store_sign_bytes(sign_bytes4(acc[t]), lane, (P * NT + t) * 16, n_keys, a.bits, mb, nt0);
     }
   }
 }
