@@ -19,6 +19,8 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-result",
     # no packed fp32 VALU instructions (v_pk_add/mul/fma_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the kernels read every accumulator with VALU code
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -145,20 +145,28 @@ __device__ __forceinline__ bf16x8 load_gfrag(const uint4* gl, const uint16_t* pr
 // one permlane32 swap brings both to every quarter, and two byte permutes interleave
 // them.  Returns the 8 output bytes (bits 64 (nt0/4) .. +63, LSB first) in every lane
 // of block r.
-__device__ __forceinline__ uint2 sign_bytes4(const f32x4 (&acc)[4]) {
+// Byte q (low nibble) of the word: the four bits of N tile nt0 + q held by this lane.
+__device__ __forceinline__ uint32_t sign_nibble(const f32x4& acc, int q) {
   uint32_t x = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = __float_as_int(acc[q][i]);
-      x |= (uint32_t)min(max(v, 0), 1) << (8 * q + i);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int v = __float_as_int(acc[i]);
+    x |= (uint32_t)min(max(v, 0), 1) << (8 * q + i);
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint2 sign_bytes_of(uint32_t x) {
   const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
   const uint32_t z = a[0] | (a[1] << 4);          // quarters (0,1): even bytes, (2,3): odd bytes
   const auto b = __builtin_amdgcn_permlane32_swap(z, z, false, false);
   const uint32_t E = b[0], O = b[1];
   return make_uint2(__builtin_amdgcn_perm(O, E, 0x05010400u), __builtin_amdgcn_perm(O, E, 0x07030602u));
+}
+
+__device__ __forceinline__ uint2 sign_bytes4(const f32x4 (&acc)[4]) {
+  return sign_bytes_of(sign_nibble(acc[0], 0) | sign_nibble(acc[1], 1) | sign_nibble(acc[2], 2) |
+                       sign_nibble(acc[3], 3));
 }
 
 // Lane quarter 0 of block row r writes the 8 bytes at byte 2 nt0 of that row (fewer at
@@ -518,12 +526,27 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 // ------------------------------------------------------------------------------------------
 // QJL key sketch: norm + sign(G k), keys feed the MFMA directly (bf16 products are exact).
 // A wave takes NT key tiles per pass, so every G fragment read from LDS feeds NT MFMAs;
-// G rows are the A operand so that each lane ends with projections of its own key.
+// G rows are the A operand so that each lane ends with projections of its own key, and
+// the sign bits of each N tile are taken as soon as it is done (16 live accumulators).
+// Eight waves per workgroup share one LDS copy of G.
 // ------------------------------------------------------------------------------------------
+#ifndef PQ_SKETCH_THREADS
+#define PQ_SKETCH_THREADS 512
+#endif
+#ifndef PQ_SKETCH_WAVES_PER_EU
+#define PQ_SKETCH_WAVES_PER_EU 4
+#endif
+constexpr int kSketchThreads = PQ_SKETCH_THREADS;
+
 template <int D, bool G_LDS>
-__global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchArgs a) {
+__global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(PQ_SKETCH_WAVES_PER_EU)))
+void qjl_sketch_kernel(const pqi::SketchArgs a) {
   constexpr int KS = D / 32;
-  constexpr int NT = D <= 128 ? 4 : (D == 256 ? 2 : 1);
+#ifndef PQ_SKETCH_NT128
+#define PQ_SKETCH_NT128 4
+#endif
+  constexpr int NT = (D <= 128 && G_LDS) ? PQ_SKETCH_NT128 : (D <= 256 ? 2 : 1);
+  constexpr int WAVES = kSketchThreads / 64;
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* gl = reinterpret_cast<uint4*>(smem);
   const int m = a.m, m_pad = (m + 15) & ~15, mb = m >> 3;
@@ -531,14 +554,15 @@ __global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchA
     stage_projection<D>(a.proj, m, m_pad, gl);
     __syncthreads();
   }
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = m_pad >> 4;
   const int64_t n_keys = a.n_keys;
   const int64_t n_tiles = (n_keys + 15) >> 4;
   const int64_t n_pass = (n_tiles + NT - 1) / NT;
-  const int64_t wave_id = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+  const int64_t wave_id = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * WAVES;
 
   for (int64_t P = wave_id; P < n_pass; P += n_waves) {
     // lane quarter g holds elements 32 s + 8 g .. +7 of key row r of each tile
@@ -549,42 +573,58 @@ __global__ __launch_bounds__(kThreads) void qjl_sketch_kernel(const pqi::SketchA
       const int64_t key = (P * NT + t) * 16 + r;
       const bool valid = full || key < n_keys;
       const u32x4* src = reinterpret_cast<const u32x4*>(a.keys + key * D);
-      float ss = 0.0f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 w = {0, 0, 0, 0};
         if (valid) w = __builtin_nontemporal_load(src + 4 * s + g);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float lo = bf16_lo(w[u]), hi = bf16_hi(w[u]);
-          ss = fmaf(lo, lo, ss);
-          ss = fmaf(hi, hi, ss);
-        }
         kf[t][s] = __builtin_bit_cast(bf16x8, w);
       }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t key = (P * NT + t) * 16 + r;
+      float ss = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 w = __builtin_bit_cast(u32x4, kf[t][s]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // element copied to a scalar first: a bit cast of the vector element itself
+          // is lowered to a read of element 0 by this compiler
+          const uint32_t wu = w[u];
+          const bf16x2 h = __builtin_bit_cast(bf16x2, wu);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
+        }
+      }
       ss = sum4(ss);
-      if (valid && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
+      if (key < n_keys && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
     }
     for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
-      f32x4 acc[NT][4];
+      uint32_t x[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) x[t] = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (nt0 + q < ntiles) {
+        if (nt0 + q < ntiles) {                               // uniform
           const int row = 16 * (nt0 + q) + r;
+          f32x4 acc[NT];
+          const bf16x8 b0 = load_gfrag<D, G_LDS>(gl, a.proj, m, row, g);
 #pragma unroll
-          for (int s = 0; s < KS; ++s) {
+          for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, kf[t][0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+          for (int s = 1; s < KS; ++s) {
             const bf16x8 b = load_gfrag<D, G_LDS>(gl, a.proj, m, row, 4 * s + g);
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-              acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, kf[t][s], acc[t][q], 0, 0, 0);
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, kf[t][s], acc[t], 0, 0, 0);
           }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) x[t] |= sign_nibble(acc[t], q);
         }
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        store_sign_bytes(sign_bytes4(acc[t]), lane, (P * NT + t) * 16, n_keys, a.bits, mb, nt0);
+        store_sign_bytes(sign_bytes_of(x[t]), lane, (P * NT + t) * 16, n_keys, a.bits, mb, nt0);
     }
   }
 }
@@ -1051,8 +1091,8 @@ hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hi
   const size_t glb = (size_t)m_pad * D * 2;
   const bool g_lds = glb <= (size_t)c.max_lds && glb <= 65536;
   const int grid = grid_for(n_tiles, c, PQ_SKETCH_WG_PER_CU);
-  if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true>), grid, kThreads, glb, s, a);
-  else hipLaunchKernelGGL((qjl_sketch_kernel<D, false>), grid, kThreads, 0, s, a);
+  if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true>), grid, kSketchThreads, glb, s, a);
+  else hipLaunchKernelGGL((qjl_sketch_kernel<D, false>), grid, kSketchThreads, 0, s, a);
   return hipGetLastError();
 }
 
