@@ -143,11 +143,13 @@ __host__ __device__ constexpr int cperm(int j) {
                   : j;
 }
 
-// Forward transform for quantize: load layout in, contiguous layout out.
-template <int D>
+// Forward transform for quantize: load layout in, contiguous layout out.  STAGE0 = false
+// skips the butterfly along register bit 0 (done by the caller while unpacking).
+template <int D, bool STAGE0 = true>
 __device__ __forceinline__ void wht_forward(float (&v)[D / 4]) {
   constexpr int E = D / 4;
-  bfly<E, 0>(v); bfly<E, 1>(v); bfly<E, 2>(v);
+  if constexpr (STAGE0) bfly<E, 0>(v);
+  bfly<E, 1>(v); bfly<E, 2>(v);
   bfly<E, 3>(v);
   if constexpr (E >= 32) bfly<E, 4>(v);
   if constexpr (E >= 64) bfly<E, 5>(v);

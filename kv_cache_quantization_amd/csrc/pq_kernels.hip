@@ -222,6 +222,15 @@ __device__ __forceinline__ void load_tile(uint4 (&raw)[IN_BF16 ? D / 32 : D / 16
 }
 
 
+// x0 s0 + x1 s1 for bf16 pairs x = (x0, x1), s = (s0, s1): the three-operand form of
+// v_dot2_f32_bf16 with an inline zero addend (the builtin is lowered to the accumulating
+// two-operand form, which needs the zero moved into the destination first).
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t s) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(s));
+  return r;
+}
+
 // Two fp32 values -> packed fp16 high parts (round to nearest even).
 __device__ __forceinline__ uint32_t split_hi_f16x2(float x0, float x1) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -265,7 +274,9 @@ struct Quantizer {
       const int e = load_e(g, 2 * p);
       const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
       const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
-      smask[p] = (s0 << 15) | (s1 << 31);
+      // bf16 input: the pair (D_e, D_e+1) as bf16 +-1.0; fp32 input: sign-bit masks
+      smask[p] = IN_BF16 ? ((s0 ? 0xBF80u : 0x3F80u) | ((s1 ? 0xBF80u : 0x3F80u) << 16))
+                         : ((s0 << 15) | (s1 << 31));
     }
     inv_w = a.t.cell_inv_w;
     offM = (float)a.t.half + kMagic;
@@ -279,17 +290,26 @@ struct Quantizer {
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
     float v[E];
+    float ss;
     if constexpr (IN_BF16) {
+      // signs, bf16 -> fp32 and the first butterfly (register bit 0 pairs the two halves of
+      // a word) in two exact dot products per pair: (x0 D0 + x1 D1, x0 D0 - x1 D1)
+      typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+      float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NR; ++s) {
-        const uint32_t w[4] = {raw[s].x ^ smask[4 * s + 0], raw[s].y ^ smask[4 * s + 1],
-                               raw[s].z ^ smask[4 * s + 2], raw[s].w ^ smask[4 * s + 3]};
+        const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          v[8 * s + 2 * u] = bf16_lo(w[u]);
-          v[8 * s + 2 * u + 1] = bf16_hi(w[u]);
+          const int p = 4 * s + u;
+          const bf16x2 x = __builtin_bit_cast(bf16x2, w[u]);
+          v[2 * p] = dot2_bf16(w[u], smask[p]);
+          v[2 * p + 1] = dot2_bf16(w[u], smask[p] ^ 0x80000000u);
+          sq[u] = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq[u], false);
         }
       }
+      ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+      wht_forward<D, false>(v);            // v = z = H (D x), unnormalised
     } else {
 #pragma unroll
       for (int s = 0; s < NR / 2; ++s) {
@@ -301,10 +321,9 @@ struct Quantizer {
           v[8 * s + t] = __uint_as_float(f[t] ^ sm);
         }
       }
+      ss = tree_sumsq<E>(v);
+      wht_forward<D>(v);                   // v = z = H (D x), unnormalised
     }
-    float ss = tree_sumsq<E>(v);
-
-    wht_forward<D>(v);                     // v = z = H (D x), unnormalised
 
     ss = sum4(ss);
     const float n = sqrtf(ss);
