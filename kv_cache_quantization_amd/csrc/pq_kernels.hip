@@ -3,6 +3,8 @@
 // Every kernel is persistent: each wave walks over tiles of 16 blocks (keys)
 // with a grid stride, so the per-workgroup set-up (codebook, search grid and
 // projection matrix staged in LDS) is paid once per workgroup.
+#include <algorithm>
+
 #include "pq_device.h"
 #include "pq_internal.h"
 
@@ -99,18 +101,6 @@ __device__ __forceinline__ uint4 gd_chunk_f16(const uint4* src, const uint8_t* s
                     bf16x2_to_f16x2_signed(b.z, sb, 2), bf16x2_to_f16x2_signed(b.w, sb, 3));
 }
 
-template <int D>
-__device__ void stage_projection_f16(const uint16_t* proj, const uint8_t* signs, int m, int m_pad, uint4* gl) {
-  constexpr int CPR = D / 8;
-  const uint4* src = reinterpret_cast<const uint4*>(proj);
-  for (int i = threadIdx.x; i < m_pad * CPR; i += blockDim.x) {
-    const int n = i / CPR, c = i % CPR;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (n < m) w = gd_chunk_f16(src, signs, CPR, n, c);
-    gl[g_swizzle<D>(n, c)] = w;
-  }
-}
-
 template <int D, bool G_LDS>
 __device__ __forceinline__ f16x8 load_gfrag_f16(const uint4* gl, const uint16_t* proj, const uint8_t* signs, int m,
                                                 int row, int col8) {
@@ -184,11 +174,14 @@ __device__ __forceinline__ void store_sign_bytes(uint2 w, int lane, int64_t row0
   }
 }
 
+// Inverse of cperm (a permutation of register-index bits), in closed form so that it folds
+// to a constant inside unrolled loops.
 template <int D>
 __host__ __device__ constexpr int cperm_inv(int o) {
-  for (int j = 0; j < D / 4; ++j)
-    if (cperm<D>(j) == o) return j;
-  return -1;
+  return D == 256 ? ((o & 7) | (((o >> 5) & 1) << 3) | (((o >> 3) & 1) << 4) | (((o >> 4) & 1) << 5))
+       : D == 512 ? ((o & 7) | (((o >> 5) & 1) << 3) | (((o >> 6) & 1) << 4) | (((o >> 3) & 1) << 5) |
+                     (((o >> 4) & 1) << 6))
+                  : o;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -256,7 +249,11 @@ struct Quantizer {
   const pqi::QuantArgs& a;
   const unsigned char* smem;
   const uint4* gl;
-  uint32_t smask[E / 2];
+  // rotation signs of this lane's element pairs: per pair, bf16 +-1.0 pairs (bf16 input) or
+  // sign-bit masks (fp32 input); for d = 512 only the sign bytes (elements 32 s + 8 g .. +7)
+  // are held and the pair values are formed when used, which keeps 48 registers free
+  static constexpr bool kCompactSigns = D == 512;
+  uint32_t smask[kCompactSigns ? D / 32 : E / 2];
   int lane, r, g, m, m_pad, mb;
   float inv_w, offM, topM, inv_sqrt_d;
   uint32_t lane_off;
@@ -269,14 +266,17 @@ struct Quantizer {
     m = a.m;
     m_pad = (m + 15) & ~15;
     mb = m >> 3;
+    if constexpr (kCompactSigns) {
 #pragma unroll
-    for (int p = 0; p < E / 2; ++p) {
-      const int e = load_e(g, 2 * p);
-      const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
-      const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
-      // bf16 input: the pair (D_e, D_e+1) as bf16 +-1.0; fp32 input: sign-bit masks
-      smask[p] = IN_BF16 ? ((s0 ? 0xBF80u : 0x3F80u) | ((s1 ? 0xBF80u : 0x3F80u) << 16))
-                         : ((s0 << 15) | (s1 << 31));
+      for (int s = 0; s < D / 32; ++s) smask[s] = a.signs[4 * s + g];
+    } else {
+#pragma unroll
+      for (int p = 0; p < E / 2; ++p) {
+        const int e = load_e(g, 2 * p);
+        const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
+        const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
+        smask[p] = (s0 << 15) | (s1 << 31) | (IN_BF16 ? 0x3F803F80u : 0u);
+      }
     }
     inv_w = a.t.cell_inv_w;
     offM = (float)a.t.half + kMagic;
@@ -285,11 +285,23 @@ struct Quantizer {
     lane_off = (REP ? 16u * (uint32_t)(lane & 15) : 0u) - (kMagicBits << kRepShift);
   }
 
-  __device__ __forceinline__ void tile(const uint4 (&raw)[NR], int64_t T) {
+  // Codes and norm of the tile's 16 blocks (stored), and with the QJL stage the residual
+  // norm (stored) and the rotated residual left in v, scaled by a power of two.
+
+  // the value described above for element pair p (registers 2p, 2p+1 of the load layout)
+  __device__ __forceinline__ uint32_t sgn(int p) const {
+    if constexpr (kCompactSigns) {
+      const uint32_t b = (smask[p >> 2] >> (2 * (p & 3))) & 3u;
+      return ((b & 1u) << 15) | ((b & 2u) << 30) | (IN_BF16 ? 0x3F803F80u : 0u);
+    } else {
+      return smask[p];
+    }
+  }
+
+  __device__ __forceinline__ void decide(const uint4 (&raw)[NR], int64_t T, float (&v)[E]) {
     const int64_t n_blocks = a.n_blocks;
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
-    float v[E];
     float ss;
     if constexpr (IN_BF16) {
       // signs, bf16 -> fp32 and the first butterfly (register bit 0 pairs the two halves of
@@ -303,8 +315,9 @@ struct Quantizer {
         for (int u = 0; u < 4; ++u) {
           const int p = 4 * s + u;
           const bf16x2 x = __builtin_bit_cast(bf16x2, w[u]);
-          v[2 * p] = dot2_bf16(w[u], smask[p]);
-          v[2 * p + 1] = dot2_bf16(w[u], smask[p] ^ 0x80000000u);
+          const uint32_t sp = sgn(p);
+          v[2 * p] = dot2_bf16(w[u], sp);
+          v[2 * p + 1] = dot2_bf16(w[u], sp ^ 0x80000000u);
           sq[u] = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq[u], false);
         }
       }
@@ -317,7 +330,8 @@ struct Quantizer {
                                raw[2 * s + 1].x, raw[2 * s + 1].y, raw[2 * s + 1].z, raw[2 * s + 1].w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const uint32_t sm = (t & 1) ? (smask[4 * s + t / 2] & 0x80000000u) : (smask[4 * s + t / 2] << 16);
+          const uint32_t sp = sgn(4 * s + t / 2);
+          const uint32_t sm = (t & 1) ? (sp & 0x80000000u) : (sp << 16);
           v[8 * s + t] = __uint_as_float(f[t] ^ sm);
         }
       }
@@ -382,46 +396,130 @@ struct Quantizer {
       const float rss = sum4(tree_sumsq<E>(v));
       const float rn = sqrtf(rss) / rscale * inv_sqrt_d;    // ||r|| = ||H D r|| / sqrt(d)
       if (valid && g == 0) a.rnorms[blk] = f32_to_f16(rn);
-      // back to the block's coordinates: w = H rho = d D r (times rscale).  The signs D
-      // are folded into the staged G, so the products below give d rscale 2^10 (G r).
-      float w[E];
+    }
+  }
+
+  // The rotated residual back in the block's coordinates, w = H rho = d D r (times the
+  // power-of-two scale), split into fp16 high and low parts (22 significant bits) as MFMA
+  // B fragments: register chunk k of quarter g holds columns 8 res_col8(g, k) + 0..7.
+  // The signs D are folded into the staged copy of G, so the products give a positive
+  // multiple of G r.
+  __device__ __forceinline__ void residual_frags(const float (&v)[E], u32x4 (&ahi)[KS], u32x4 (&alo)[KS]) {
+    float w[E];
 #pragma unroll
-      for (int i = 0; i < E; ++i) w[i] = v[cperm_inv<D>(i)];
-      wht_dequant<D>(w);
-      // split into fp16 high and low parts (22 significant bits), MFMA A fragments;
-      // register chunk k of quarter g holds columns 8 res_col8(g, k) + 0..7
-      u32x4 ahi[KS], alo[KS];
+    for (int i = 0; i < E; ++i) w[i] = v[cperm_inv<D>(i)];
+    wht_dequant<D>(w);
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
+    for (int k = 0; k < KS; ++k) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float x0 = w[8 * k + 2 * t], x1 = w[8 * k + 2 * t + 1];
-          const uint32_t hp = split_hi_f16x2(x0, x1);
-          ahi[k][t] = hp;
-          alo[k][t] = split_lo_f16x2(hp, x0, x1);
-        }
-      }
-      const int ntiles = m_pad >> 4;
-      for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
-        f32x4 acc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          if (nt0 + q < ntiles) {
-            const int row = 16 * (nt0 + q) + r;
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-              const f16x8 b = load_gfrag_f16<D, G_LDS>(gl, a.proj, a.signs, m, row, res_col8<D>(g, k));
-              acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, ahi[k]), acc[q], 0, 0, 0);
-              acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, alo[k]), acc[q], 0, 0, 0);
-            }
-          }
-        }
-        store_sign_bytes(sign_bytes4(acc), lane, T * 16, n_blocks, a.qbits, mb, nt0);
+      for (int t = 0; t < 4; ++t) {
+        const float x0 = w[8 * k + 2 * t], x1 = w[8 * k + 2 * t + 1];
+        const uint32_t hp = split_hi_f16x2(x0, x1);
+        ahi[k][t] = hp;
+        alo[k][t] = split_lo_f16x2(hp, x0, x1);
       }
     }
   }
+
+  // The rotated residual back in the block's coordinates, unsplit (see residual_frags).
+  __device__ __forceinline__ void residual_block(float (&v)[E]) {
+    float w[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) w[i] = v[cperm_inv<D>(i)];
+    wht_dequant<D>(w);
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = w[i];
+  }
+
+  // Sign bits of the NTC N tiles from nt_begin (a multiple of 4, fewer at the end of G) with
+  // the K steps outermost: each K step splits its 8 residual values once and feeds all NTC
+  // accumulators, so only those (not the whole split residual) are live.  G rows come from
+  // the LDS buffer gb, whose row 0 is row row0 of G.
+  template <int NTC>
+  __device__ __forceinline__ void project_kouter(const float (&w)[E], int64_t T, const uint4* gb, int row0,
+                                                 int nt_begin, int nt_end) {
+    f32x4 acc[NTC];
+#pragma unroll
+    for (int q = 0; q < NTC; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float x0 = w[8 * k + 2 * t], x1 = w[8 * k + 2 * t + 1];
+        hi[t] = split_hi_f16x2(x0, x1);
+        lo[t] = split_lo_f16x2(hi[t], x0, x1);
+      }
+#pragma unroll
+      for (int q = 0; q < NTC; ++q) {
+        if (nt_begin + q < nt_end) {                                  // uniform
+          const int row = 16 * (nt_begin + q) + r;
+          const f16x8 b = __builtin_bit_cast(f16x8, gb[g_swizzle<D>(row - row0, res_col8<D>(g, k))]);
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, hi), acc[q], 0, 0, 0);
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, lo), acc[q], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int q0 = 0; q0 < NTC; q0 += 4) {
+      if (nt_begin + q0 < nt_end) {
+        const f32x4 grp[4] = {acc[q0], acc[q0 + 1], acc[q0 + 2], acc[q0 + 3]};
+        store_sign_bytes(sign_bytes4(grp), lane, T * 16, a.n_blocks, a.qbits, mb, nt_begin + q0);
+      }
+    }
+  }
+
+  // Sign bits of N tiles [nt_begin, nt_end) (nt_begin a multiple of 4).  G rows come from
+  // the LDS buffer gb, whose row 0 is row row0 of G, or (without LDS) from global memory.
+  template <bool FROM_LDS>
+  __device__ __forceinline__ void project(const u32x4 (&ahi)[KS], const u32x4 (&alo)[KS], int64_t T,
+                                          const uint4* gb, int row0, int nt_begin, int nt_end) {
+    for (int nt0 = nt_begin; nt0 < nt_end; nt0 += 4) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (nt0 + q < nt_end) {
+          const int row = 16 * (nt0 + q) + r;
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
+            f16x8 b;
+            if constexpr (FROM_LDS) b = __builtin_bit_cast(f16x8, gb[g_swizzle<D>(row - row0, res_col8<D>(g, k))]);
+            else b = load_gfrag_f16<D, false>(gb, a.proj, a.signs, m, row, res_col8<D>(g, k));
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, ahi[k]), acc[q], 0, 0, 0);
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, alo[k]), acc[q], 0, 0, 0);
+          }
+        }
+      }
+      store_sign_bytes(sign_bytes4(acc), lane, T * 16, a.n_blocks, a.qbits, mb, nt0);
+    }
+  }
+
+  __device__ __forceinline__ void tile(const uint4 (&raw)[NR], int64_t T) {
+    float v[E];
+    decide(raw, T, v);
+    if constexpr (QJL) {
+      u32x4 ahi[KS], alo[KS];
+      residual_frags(v, ahi, alo);
+      project<G_LDS>(ahi, alo, T, gl, 0, 0, m_pad >> 4);
+    }
+  }
 };
+
+// Rows [row0, row0 + rows) of G D as fp16 scaled by 2^10 (rows >= m zero), swizzled rows
+// of D/8 16-byte chunks, into gb.
+template <int D>
+__device__ void stage_projection_rows(const uint16_t* proj, const uint8_t* signs, int m, int row0, int rows,
+                                      uint4* gb) {
+  constexpr int CPR = D / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(proj);
+  for (int i = threadIdx.x; i < rows * CPR; i += blockDim.x) {
+    const int nl = i / CPR, c = i % CPR, n = row0 + nl;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < m) w = gd_chunk_f16(src, signs, CPR, n, c);
+    gb[g_swizzle<D>(nl, c)] = w;
+  }
+}
 
 template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUANT_WAVES_PER_EU))) void pq_quantize_kernel(const pqi::QuantArgs a) {
@@ -430,7 +528,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUA
   uint4* tab = reinterpret_cast<uint4*>(smem);
   uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
   build_search_grid(a.t, tab);
-  if constexpr (QJL && G_LDS) stage_projection_f16<D>(a.proj, a.signs, a.m, (a.m + 15) & ~15, gl);
+  if constexpr (QJL && G_LDS) stage_projection_rows<D>(a.proj, a.signs, a.m, 0, (a.m + 15) & ~15, gl);
   __syncthreads();
 
   Q q(a, smem, gl);
@@ -443,6 +541,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUA
   for (; T < n_tiles; T += n_waves) {
     load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
     q.tile(raw, T);
+  }
+}
+
+// Quantize with a QJL projection too large to keep in LDS: a workgroup takes four tiles at
+// a time (one per wave), each wave keeps its tile's residual fragments in registers, and
+// the workgroup walks over G in chunks of chunk_rows rows (a multiple of 64) staged in LDS,
+// so every chunk read from L2 serves 64 blocks.
+#ifndef PQ_QUANT_CHUNK_WAVES_PER_EU
+#define PQ_QUANT_CHUNK_WAVES_PER_EU 1
+#endif
+constexpr int kChunkRows = 128;
+
+template <int D, bool IN_BF16, bool REP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUANT_CHUNK_WAVES_PER_EU)))
+void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
+  using Q = Quantizer<D, IN_BF16, true, true, REP>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint4* tab = reinterpret_cast<uint4*>(smem);
+  uint4* gb = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
+  build_search_grid(a.t, tab);
+  Q q(a, smem, gb);
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t full_tiles = a.n_blocks >> 4;
+  const int64_t n_groups = (n_tiles + kWaves - 1) / kWaves;
+  const int ntiles = q.m_pad >> 4;
+  for (int64_t TG = blockIdx.x; TG < n_groups; TG += gridDim.x) {   // uniform over the workgroup
+    const int64_t T = TG * kWaves + (threadIdx.x >> 6);              // may lie past the end: no stores
+    __syncthreads();                                                  // search grid built / chunk free
+    uint4 raw[Q::NR];
+    load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
+    float v[Q::E];
+    q.decide(raw, T, v);
+    q.residual_block(v);
+    for (int row0 = 0; row0 < q.m_pad; row0 += kChunkRows) {
+      const int rows = min(kChunkRows, q.m_pad - row0);
+      __syncthreads();                                                // previous chunk consumed
+      stage_projection_rows<D>(a.proj, a.signs, a.m, row0, rows, gb);
+      __syncthreads();
+      q.template project_kouter<kChunkRows / 16>(v, T, gb, row0, row0 >> 4, min(ntiles, (row0 + rows) >> 4));
+    }
   }
 }
 
@@ -1087,9 +1225,27 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   const size_t base = (size_t)a.t.ncell * a.t.nrep * 16;
   const size_t glb = (size_t)m_pad * D * 2;
   const bool qjl = a.m > 0;
-  const bool g_lds = qjl && base + glb <= (size_t)c.max_lds && base + glb <= 65536;
+  // G kept in LDS for the whole launch when it fits beside the search grid (several
+  // workgroups per CU while it takes at most 64 KiB), else walked in chunks
+  const bool g_lds = qjl && base + glb <= (size_t)c.max_lds;
+  if (qjl && !g_lds) {
+    // G in chunks of kChunkRows rows beside the search grid
+    const size_t lds = base + (size_t)kChunkRows * D * 2;
+    if (lds > (size_t)c.max_lds) return hipErrorInvalidConfiguration;
+    const int64_t n_groups = (n_tiles + kWaves - 1) / kWaves;
+    const int per_cu = std::max(1, (int)((size_t)c.max_lds / lds));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(n_groups, (int64_t)c.cu_count * per_cu));
+    if (a.t.nrep == 16) {
+      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, true>), grid, kThreads, lds, s, a);
+      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, true>), grid, kThreads, lds, s, a);
+    } else {
+      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, false>), grid, kThreads, lds, s, a);
+      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, false>), grid, kThreads, lds, s, a);
+    }
+    return hipGetLastError();
+  }
   const size_t lds = base + (g_lds ? glb : 0);
-  const int grid = grid_for(n_tiles, c, PQ_QUANT_WG_PER_CU);
+  const int grid = grid_for(n_tiles, c, lds > 65536 ? 1 : PQ_QUANT_WG_PER_CU);
   if (a.t.nrep == 16) return launch_quantize_r<D, true>(in_bf16, qjl, g_lds, grid, lds, a, s);
   return launch_quantize_r<D, false>(in_bf16, qjl, g_lds, grid, lds, a, s);
 }
