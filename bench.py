@@ -7,7 +7,9 @@ are rotated so that no step finds its data in the 256 MB Infinity Cache.
 
 Prints one JSON line.  ``value`` is input bytes / (quantize + dequantize
 kernel time), in GB/s.  ``parts`` adds the QJL half of the metric on the
-config-4 key cache: sketch and score rates in keys/s.  The roofline entry is for the quantize kernel:
+config-4 key cache (sketch and score rates in keys/s) and the config-5 two-stage
+path (quantize, dequantize, query preparation, score), each with its fraction of
+the HBM (or matrix-core) peak.  The roofline entry is for the quantize kernel:
 algorithmic bytes per launch (input read + codes, norms, sign bits and residual
 norms written) over its average duration measured with HIP events on the
 stream the kernels run on.  ``cpu_baseline`` times the oracle on the host on a
@@ -28,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP16_PEAK_TFLOPS = 2500.0
 N_SETS = 8
 
 
@@ -40,6 +43,7 @@ def _args():
                     help="blocks of the workload the oracle baseline processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qjl", action="store_true", help="skip the config-4 QJL sketch/score leg")
+    ap.add_argument("--no-tsq", action="store_true", help="skip the config-5 two-stage leg")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -118,14 +122,14 @@ def summarize(run_dir):
 
     trace_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/prof_trace -o trace -- "
                  "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
-    lines = ["# Kernel durations of the benchmark (config 2 codec + config 4 QJL leg), one MI355X",
+    lines = ["# Kernel durations of the benchmark (config 2 codec, config 4 QJL leg, config 5 two-stage leg), one MI355X",
              "", "command: " + trace_cmd, "kernel source hash: " + kernel_source_hash(), "",
              "%-58s %6s %12s %10s %10s" % ("kernel", "calls", "average_ns", "min_ns", "max_ns")]
     for r in rows("prof_trace", "trace_kernel_stats.csv"):
         n = short(r["Name"])
         if any(k in n for k in ("pq_", "qjl_")):
             lines.append("%-58s %6s %12.1f %10s %10s" % (n, r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"]))
-    with open(os.path.join(out_dir, "bench_kernels_config2_config4_trace.txt"), "w") as fh:
+    with open(os.path.join(out_dir, "bench_kernels_config2_config4_config5_trace.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
     def counter(sub, prefix, kernel):
@@ -140,9 +144,9 @@ def summarize(run_dir):
     rec = {"source_hash": kernel_source_hash(),
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_q_fetch -o q_fetch -- "
-               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl",
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_q_write -o q_write -- "
-               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl",
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq",
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_c_fetch -o c_fetch -- "
                "python3 bench.py --calibrate-copy",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_c_write -o c_write -- "
@@ -229,6 +233,64 @@ def qjl_leg(pq, synth, torch, steps, warmup):
         "qjl_score_hbm_frac": round(sc_bytes / t_sc / 1e9 / HBM_PEAK_GBS, 4),
         "qjl_sketch_algorithmic_bytes": sk_bytes, "qjl_score_algorithmic_bytes": sc_bytes,
     }
+
+
+def tsq_leg(pq, synth, torch, steps, warmup):
+    """Config 5: per tensor ([8][65536][256] and [8][65536][512] bf16, 3-bit codes, QJL m=d),
+    quantize, dequantize, query preparation (16 queries per KV head) and the two-stage
+    score of every query against every vector."""
+    dev = torch.device("cuda:0")
+    out = {"tsq_config": "config5: bf16 KV vectors [8][65536][256] and [8][65536][512], log-normal channel "
+                         "scales, 3-bit codes, QJL m=d, 16 queries per KV head"}
+    for d in (256, 512):
+        c = synth.config5_tensor(d)
+        H, T, _ = c["x"].shape
+        n_q, bits, m = c["q"].shape[1], c["bits"], c["m"]
+        st = torch.from_numpy(c["signs"]).to(dev)
+        G = torch.from_numpy(c["G"].view(np.int16)).view(torch.bfloat16).to(dev)
+        xs = [torch.from_numpy(c["x"].view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(2)]
+        q = torch.from_numpy(c["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+        del c
+        enc = [pq.quantize(xs[i], d, bits, st, G) for i in range(2)]
+        deq = [torch.empty((H * T, d), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        prep = pq.query_prep(q, st, G)
+        sc = torch.empty((H, n_q, T), dtype=torch.float32, device=dev)
+
+        def quant(k):
+            pq.quantize(xs[k % 2], d, bits, st, G, out=enc[k % 2])
+
+        def dequant(k):
+            pq.dequantize(enc[k % 2][0], enc[k % 2][1], d, bits, st, out=deq[k % 2])
+
+        def prepare(k):
+            pq.query_prep(q, st, G, out=prep)
+
+        def score(k):
+            e = enc[k % 2]
+            pq.score(prep, e[0], e[1], d, bits, H, n_q, T, e[2], e[3], m=m, out=sc)
+
+        for k in range(warmup):
+            quant(k), dequant(k), prepare(k), score(k)
+        t = {name: timed(torch, fn, steps) for name, fn in
+             (("quantize", quant), ("dequantize", dequant), ("query_prep", prepare), ("score", score))}
+        nb = H * T
+        qb = nb * d * 2 + nb * d + nb * 2 + nb * (m // 8) + nb * 2
+        db = nb * d + nb * 2 + nb * d * 2
+        sb = nb * (d + 2 + m // 8 + 2) + H * n_q * T * 4
+        out.update({
+            "tsq_d%d_quantize_us" % d: round(t["quantize"] * 1e6, 2),
+            "tsq_d%d_quantize_hbm_frac" % d: round(qb / t["quantize"] / 1e9 / HBM_PEAK_GBS, 4),
+            "tsq_d%d_quantize_mfma_frac" % d: round(2.0 * 2 * nb * d * m / t["quantize"] / 1e12 / FP16_PEAK_TFLOPS, 4),
+            "tsq_d%d_dequantize_us" % d: round(t["dequantize"] * 1e6, 2),
+            "tsq_d%d_dequantize_hbm_frac" % d: round(db / t["dequantize"] / 1e9 / HBM_PEAK_GBS, 4),
+            "tsq_d%d_query_prep_us" % d: round(t["query_prep"] * 1e6, 2),
+            "tsq_d%d_score_us" % d: round(t["score"] * 1e6, 2),
+            "tsq_d%d_score_vectors_per_s" % d: round(nb / t["score"], 1),
+            "tsq_d%d_score_hbm_frac" % d: round(sb / t["score"] / 1e9 / HBM_PEAK_GBS, 4),
+        })
+        del xs, enc, deq, prep, sc
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -332,6 +394,8 @@ def main():
     }
     if not args.no_qjl:
         rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
+    if not args.no_tsq:
+        rec["parts"].update(tsq_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_blocks)
     print(json.dumps(rec), flush=True)

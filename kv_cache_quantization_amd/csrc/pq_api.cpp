@@ -251,6 +251,7 @@ int qjl_project(int d, int m, const uint16_t* q, int64_t n_q, const uint16_t* pr
   if (!aligned(q, 16) || !aligned(proj, 16) || !aligned(sq, 4)) return PQ_EINVAL;
   pqi::ProjectArgs a;
   a.q = q; a.n_q = n_q; a.proj = proj; a.sq = sq; a.d = d; a.m = m;
+  a.rows_per_group = n_q; a.group_stride = n_q * m;
   return hip_status(pqi::launch_project(a, (hipStream_t)stream));
 }
 
@@ -291,7 +292,7 @@ int pq_query_prep(int d, int m, int n_heads, int n_q, const uint16_t* q, const u
   if (m == 0 && proj) return PQ_EINVAL;
   if (n_heads == 0) return PQ_OK;
   if (!signs || !prep || (n_q > 0 && !q) || (m > 0 && !proj)) return PQ_EINVAL;
-  if (!aligned(prep, 16) || (q && !aligned(q, 2)) || (proj && !aligned(proj, 2))) return PQ_EINVAL;
+  if (!aligned(prep, 16) || (q && !aligned(q, 16)) || (proj && !aligned(proj, 16))) return PQ_EINVAL;
   pqi::QueryPrepArgs a;
   a.q = q; a.signs = signs; a.proj = proj; a.prep = static_cast<unsigned char*>(prep);
   a.n_heads = n_heads; a.n_q = n_q; a.d = d; a.m = m;

@@ -62,9 +62,11 @@ struct ProjectArgs {
   const uint16_t* q;
   int64_t n_q;
   const uint16_t* proj;
-  float* sq;
+  float* sq;               // row i at sq + (i / rows_per_group) * group_stride + (i % rows_per_group) * m
   int d;
   int m;
+  int64_t rows_per_group;  // n_q for a plain [n_q][m] output
+  int64_t group_stride;    // in floats
 };
 
 struct ScoreArgs {

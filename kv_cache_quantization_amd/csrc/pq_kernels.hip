@@ -812,7 +812,8 @@ __global__ __launch_bounds__(64) void qjl_project_kernel(const pqi::ProjectArgs 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t qi = q0 + 4 * g + i;
-      if (qi < a.n_q) a.sq[qi * a.m + nrow] = acc[i];
+      if (qi < a.n_q)
+        a.sq[(qi / a.rows_per_group) * a.group_stride + (qi % a.rows_per_group) * a.m + nrow] = acc[i];
     }
   }
 }
@@ -981,12 +982,10 @@ __global__ __launch_bounds__(256) void pq_query_rotate_kernel(const pqi::QueryPr
   float* qrot = reinterpret_cast<float*>(base) + (int64_t)r * d;
   float* sq = reinterpret_cast<float*>(base + pqi::prep_off_sq(d)) + (int64_t)r * m;
   __shared__ float v[512];
-  __shared__ float qv[512];
   const bool live = r < a.n_q;
   const uint16_t* q = a.q + ((int64_t)h * a.n_q + r) * d;
   for (int e = threadIdx.x; e < d; e += blockDim.x) {
     float x = live ? bf16_to_f32(q[e]) : 0.0f;
-    qv[e] = x;
     if ((a.signs[e >> 3] >> (e & 7)) & 1) x = -x;
     v[e] = x;
   }
@@ -1002,39 +1001,44 @@ __global__ __launch_bounds__(256) void pq_query_rotate_kernel(const pqi::QueryPr
     __syncthreads();
   }
   for (int e = threadIdx.x; e < d; e += blockDim.x) qrot[e] = v[e];
-  for (int n = threadIdx.x; n < m; n += blockDim.x) {
-    const uint16_t* gr = a.proj + (int64_t)n * d;
-    float acc = 0.0f;
-    if (live)
-      for (int e = 0; e < d; ++e) acc = fmaf(bf16_to_f32(gr[e]), qv[e], acc);
-    sq[n] = acc;
-  }
+  // G q of the live rows comes from the projection kernel; the padding rows stay zero
+  if (!live)
+    for (int n = threadIdx.x; n < m; n += blockDim.x) sq[n] = 0.0f;
 }
 
 
-__global__ __launch_bounds__(256) void pq_query_quant_kernel(const pqi::QueryPrepArgs a) {
-  const int h = blockIdx.x;
+// One workgroup per (head, 1024-word slice of the fragments): every workgroup finds the 32
+// row scales itself, the first slice of a head also stores them.
+constexpr int kPrepWordsPerGroup = 1024;
+
+__global__ __launch_bounds__(256) void pq_query_quant_kernel(const pqi::QueryPrepArgs a, int slices) {
+  const int h = blockIdx.x / slices, slice = blockIdx.x % slices;
   const int d = a.d, m = a.m;
   unsigned char* base = a.prep + (int64_t)h * pqi::prep_head_bytes(d, m);
   const float* qrot = reinterpret_cast<const float*>(base);
   const float* sq = reinterpret_cast<const float*>(base + pqi::prep_off_sq(d));
-  float* scale = reinterpret_cast<float*>(base + pqi::prep_off_meta(d, m));    // [2][16]
-  int* isum = reinterpret_cast<int*>(base + pqi::prep_off_meta(d, m) + 128);    // [2][16]
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int job = wv; job < 2 * pqi::kScoreRows; job += 4) {
-    const int term = job / pqi::kScoreRows, r = job % pqi::kScoreRows;
+  float* scale_out = reinterpret_cast<float*>(base + pqi::prep_off_meta(d, m));    // [2][16]
+  int* isum_out = reinterpret_cast<int*>(base + pqi::prep_off_meta(d, m) + 128);    // [2][16]
+  __shared__ float scale[2 * pqi::kScoreRows];
+  // row scales: 16 threads per query row (a quarter of a wave), both terms in turn
+  const int row = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  for (int term = 0; term < 2; ++term) {
     const int len = term == 0 ? d : m;
-    const float* src = term == 0 ? qrot + (int64_t)r * d : sq + (int64_t)r * m;
+    const float* src = term == 0 ? qrot + (int64_t)row * d : sq + (int64_t)row * m;
     float amax = 0.0f;
-    for (int e = lane; e < len; e += 64) amax = fmaxf(amax, fabsf(src[e]));
-    amax = wave_max(amax);
-    const float s = amax / pqi::kLimbRange;
+    for (int e = sub; e < len; e += 16) amax = fmaxf(amax, fabsf(src[e]));
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const float sc = amax / pqi::kLimbRange;
     int acc = 0;
-    for (int e = lane; e < len; e += 64) acc += quant_int(src[e], s);
-    acc = wave_sum(acc);
-    if (lane == 0) {
-      scale[job] = s;
-      isum[job] = acc;
+    for (int e = sub; e < len; e += 16) acc += quant_int(src[e], sc);
+    for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
+    if (sub == 0) {
+      const int job = term * pqi::kScoreRows + row;
+      scale[job] = sc;
+      if (slice == 0) {
+        scale_out[job] = sc;
+        isum_out[job] = acc;
+      }
     }
   }
   __syncthreads();
@@ -1043,7 +1047,8 @@ __global__ __launch_bounds__(256) void pq_query_quant_kernel(const pqi::QueryPre
   uint32_t* fc = reinterpret_cast<uint32_t*>(base + pqi::prep_off_frag_c(d, m));
   uint32_t* fq = reinterpret_cast<uint32_t*>(base + pqi::prep_off_frag_q(d, m));
   const int words_c = 3 * kc * 256, words_q = 3 * kq * 256;
-  for (int wi = threadIdx.x; wi < words_c + words_q; wi += blockDim.x) {
+  const int w_end = min(words_c + words_q, (slice + 1) * kPrepWordsPerGroup);
+  for (int wi = slice * kPrepWordsPerGroup + threadIdx.x; wi < w_end; wi += blockDim.x) {
     const bool qjl = wi >= words_c;
     const int w = qjl ? wi - words_c : wi;
     const int blk = w >> 8, inblk = w & 255;          // 1 KiB block = 256 words
@@ -1297,7 +1302,18 @@ hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(pq_query_rotate_kernel, a.n_heads * kScoreRows, 256, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pq_query_quant_kernel, a.n_heads, 256, 0, s, a);
+  if (a.m > 0 && a.n_q > 0) {
+    // G q of every live row into the sq block of its head
+    ProjectArgs pa;
+    pa.q = a.q; pa.n_q = (int64_t)a.n_heads * a.n_q; pa.proj = a.proj;
+    pa.sq = reinterpret_cast<float*>(a.prep + prep_off_sq(a.d));
+    pa.d = a.d; pa.m = a.m; pa.rows_per_group = a.n_q; pa.group_stride = prep_head_bytes(a.d, a.m) / 4;
+    e = launch_project(pa, s);
+    if (e != hipSuccess) return e;
+  }
+  const int words = 3 * (a.d / 64 + a.m / 64) * 256;
+  const int slices = (words + kPrepWordsPerGroup - 1) / kPrepWordsPerGroup;
+  hipLaunchKernelGGL(pq_query_quant_kernel, a.n_heads * slices, 256, 0, s, a, slices);
   return hipGetLastError();
 }
 
