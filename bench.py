@@ -7,9 +7,9 @@ are rotated so that no step finds its data in the 256 MB Infinity Cache.
 
 Prints one JSON line.  ``value`` is input bytes / (quantize + dequantize
 kernel time), in GB/s.  ``parts`` adds the QJL half of the metric on the
-config-4 key cache (sketch and score rates in keys/s) and the config-5 two-stage
-path (quantize, dequantize, query preparation, score), each with its fraction of
-the HBM (or matrix-core) peak.  The roofline entry is for the quantize kernel:
+config-4 key cache (sketch and score rates in keys/s), the config-5 two-stage
+path (quantize, dequantize, query preparation, score) and the config-3 grouped
+pass over 224 tensors, each with its fraction of the HBM (or matrix-core) peak.  The roofline entry is for the quantize kernel:
 algorithmic bytes per launch (input read + codes, norms, sign bits and residual
 norms written) over its average duration measured with HIP events on the
 stream the kernels run on.  ``cpu_baseline`` times the oracle on the host on a
@@ -44,6 +44,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qjl", action="store_true", help="skip the config-4 QJL sketch/score leg")
     ap.add_argument("--no-tsq", action="store_true", help="skip the config-5 two-stage leg")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the config-3 grouped pass")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -144,9 +145,9 @@ def summarize(run_dir):
     rec = {"source_hash": kernel_source_hash(),
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_q_fetch -o q_fetch -- "
-               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq",
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq --no-grouped",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_q_write -o q_write -- "
-               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq",
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq --no-grouped",
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_c_fetch -o c_fetch -- "
                "python3 bench.py --calibrate-copy",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_c_write -o c_write -- "
@@ -293,6 +294,47 @@ def tsq_leg(pq, synth, torch, steps, warmup):
     return out
 
 
+def grouped_leg(pq, synth, torch, reps):
+    """Config 3: one streamed quantize pass and one dequantize pass over the 224 tensors of
+    a 32-layer 7B-style decoder (4-bit codes, d=128), each tensor one launch with its own
+    rotation signs.  Kernel time depends only on the shapes, so the seven tensors of layer
+    0 (seeded as in the parity tests) stand in for every layer; returns the pass times."""
+    dev = torch.device("cuda:0")
+    layout = synth.config3_layout()
+    d, bits = 128, 4
+    ins, outs = [], []
+    for t, _, _, rows, cols in layout[:7]:
+        xu, _ = synth.config3_tensor(t, rows, cols)
+        x = torch.from_numpy(xu.view(np.int16)).view(torch.bfloat16).to(dev)
+        n = x.numel() // d
+        ins.append(x)
+        outs.append((torch.empty((n, d), dtype=torch.uint8, device=dev), torch.empty((n,), dtype=torch.float16, device=dev),
+                     torch.empty((n, d), dtype=torch.bfloat16, device=dev)))
+    signs = [torch.from_numpy(synth.sign_mask(synth.BASE_SEED + t, d)).to(dev) for t, _, _, _, _ in layout]
+    total = sum(r * c for _, _, _, r, c in layout)
+
+    def qpass(k):
+        for t in range(len(layout)):
+            i = t % 7
+            pq.quantize(ins[i], d, bits, signs[t], out=(outs[i][0], outs[i][1], None, None))
+
+    def dpass(k):
+        for t in range(len(layout)):
+            i = t % 7
+            pq.dequantize(outs[i][0], outs[i][1], d, bits, signs[t], out=outs[i][2])
+
+    qpass(0), dpass(0)
+    tq, td = timed(torch, qpass, reps), timed(torch, dpass, reps)
+    nb = total // d
+    q_bytes = total * 2 + total + nb * 2
+    d_bytes = total + nb * 2 + total * 2
+    return {"grouped_config": "config3: 224 bf16 tensors (32 layers x q,k,v,o,gate,up,down), 6,979,321,856 "
+                              "values, d=128, 4-bit, one launch per tensor",
+            "grouped_quantize_ms": round(tq * 1e3, 3), "grouped_quantize_hbm_frac": round(q_bytes / tq / 1e9 / HBM_PEAK_GBS, 4),
+            "grouped_dequantize_ms": round(td * 1e3, 3), "grouped_dequantize_hbm_frac": round(d_bytes / td / 1e9 / HBM_PEAK_GBS, 4),
+            "grouped_input_gb_per_s": round(total * 2 / (tq + td) / 1e9, 1)}
+
+
 def main():
     args = _args()
     if args.summarize:
@@ -396,6 +438,8 @@ def main():
         rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
     if not args.no_tsq:
         rec["parts"].update(tsq_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+    if not args.no_grouped:
+        rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50)))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_blocks)
     print(json.dumps(rec), flush=True)
