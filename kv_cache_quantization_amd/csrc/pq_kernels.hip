@@ -899,13 +899,20 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
   // wave wv quantizes query head wv of the group into A rows 4 wv + limb
   if (wv < group) {
     const float* src = a.sq + ((int64_t)b * a.q_heads + gk * group + wv) * m;
+    float x[KS];                                          // element lane + 64 j of the head
+#pragma unroll
+    for (int j = 0; j < KS; ++j) x[j] = src[lane + 64 * j];
     float amax = 0.0f;
-    for (int e = lane; e < m; e += 64) amax = fmaxf(amax, fabsf(src[e]));
+#pragma unroll
+    for (int j = 0; j < KS; ++j) amax = fmaxf(amax, fabsf(x[j]));
     const float s = wave_max(amax) / pqi::kLimbRange;
+    const float inv_s = s > 0.0f ? 1.0f / s : 0.0f;
     int acc = 0;
     unsigned char* fb = reinterpret_cast<unsigned char*>(frag);
-    for (int e = lane; e < m; e += 64) {
-      const int Q = quant_int(src[e], s);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const int e = lane + 64 * j;
+      const int Q = (int)rintf(x[j] * inv_s);
       acc += Q;
       const int gq = e / (m / 4), k = (e % (m / 4)) >> 4, i = e & 15;
 #pragma unroll
@@ -928,39 +935,59 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
   const int64_t n_tiles = (T + 15) >> 4;
   const uint8_t* bits = a.bits + (int64_t)grp * T * mb;
   const uint16_t* norms = a.norms + (int64_t)grp * T;
-  const double c0 = 1.2533141373155003 / (double)m;       // sqrt(pi/2) / m
+  const float c0 = 1.2533141373155003f / (float)m;        // sqrt(pi/2) / m
   const bool out_lane = gq < group;
   const int h_out = gk * group + (out_lane ? gq : 0);
   float* out = a.scores + ((int64_t)b * a.q_heads + h_out) * T;
-  const double s_out = out_lane ? (double)scl[gq] * c0 : 0.0;
-  const double sumq_out = out_lane ? (double)isum[gq] : 0.0;
+  const float s_out = out_lane ? scl[gq] * c0 : 0.0f;
+  const float sumq_out = out_lane ? (float)isum[gq] : 0.0f;
 
+  // U tiles per iteration, the next U tiles' bits and norms in flight meanwhile
+  constexpr int U = 4;
   const int64_t stride = (int64_t)chunks_per_group * kWaves;
-  int64_t tile = (int64_t)chunk * kWaves + wv;
-  uint32_t wn[(KS + 1) / 2];
-  load_key_bits<KS>(bits + (tile * 16 + r) * mb + (mb >> 2) * gq, tile < n_tiles && tile * 16 + r < T, wn);
-  for (; tile < n_tiles; tile += stride) {
-    const int64_t key = tile * 16 + r;
-    const bool valid = key < T;
-    uint32_t w[(KS + 1) / 2];
+  // loads of clamped keys (always in bounds, no branches, so several stay in flight); a
+  // key past the end only feeds its own output column, which is not stored
+  auto fetch = [&](int64_t t0, uint32_t (&w)[U][(KS + 1) / 2], uint16_t (&nu)[U]) {
 #pragma unroll
-    for (int j = 0; j < (KS + 1) / 2; ++j) w[j] = wn[j];
-    // the next tile's bits are in flight while this one is scored
-    const int64_t nkey = (tile + stride) * 16 + r;
-    load_key_bits<KS>(bits + nkey * mb + (mb >> 2) * gq, tile + stride < n_tiles && nkey < T, wn);
-    i32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const uint32_t w16 = (w[k >> 1] >> (16 * (k & 1))) & 0xffffu;
-      const i32x4 bf = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
-                        (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[k], bf, acc, 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = min((t0 + u * stride) * 16 + r, T - 1);
+      load_key_bits<KS>(bits + key * mb + (mb >> 2) * gq, true, w[u]);
+      nu[u] = norms[key];
     }
-    // lane (gq, key r): acc[l] = sum_i bit_i * limb_l of query head gq
-    if (valid && out_lane) {
-      const double S = 16384.0 * (double)acc[0] + 128.0 * (double)acc[1] + (double)acc[2];
-      const double nu = (double)f16_to_f32(norms[key]);
-      out[key] = (float)(nu * s_out * (2.0 * S - sumq_out));
+  };
+  uint32_t wn[U][(KS + 1) / 2];
+  uint16_t nn[U];
+  int64_t tile = (int64_t)chunk * kWaves + wv;
+  fetch(tile, wn, nn);
+  for (; tile < n_tiles; tile += U * stride) {
+    uint32_t w[U][(KS + 1) / 2];
+    uint16_t nu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      nu[u] = nn[u];
+#pragma unroll
+      for (int j = 0; j < (KS + 1) / 2; ++j) w[u][j] = wn[u][j];
+    }
+    fetch(tile + U * stride, wn, nn);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = tile + u * stride;
+      if (t >= n_tiles) break;                                        // uniform
+      const int64_t key = t * 16 + r;
+      i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const uint32_t w16 = (w[u][k >> 1] >> (16 * (k & 1))) & 0xffffu;
+        const i32x4 bf = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
+                          (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[k], bf, acc, 0, 0, 0);
+      }
+      // lane (gq, key r): acc[l] = sum_i bit_i * limb_l of query head gq.  S = sum_i bit_i Q_i is
+      // exact in int32 (|S| <= m * kLimbRange < 2^31); 2 S - sum Q then carries one fp32 rounding.
+      if (key < T && out_lane) {
+        const int S = acc[0] * 16384 + acc[1] * 128 + acc[2];
+        out[key] = f16_to_f32(nu[u]) * s_out * fmaf(2.0f, (float)S, -sumq_out);
+      }
     }
   }
 }
@@ -1375,7 +1402,10 @@ hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s) {
   const int groups = a.batch * a.kv_heads;
   const int64_t n_tiles = (a.n_keys + 15) >> 4;
   // eight workgroups per CU, at most one wave per tile
-  int64_t per_group = ((int64_t)c.cu_count * 8 + groups - 1) / groups;
+#ifndef PQ_SCORE_WG_PER_CU
+#define PQ_SCORE_WG_PER_CU 4
+#endif
+  int64_t per_group = ((int64_t)c.cu_count * PQ_SCORE_WG_PER_CU + groups - 1) / groups;
   const int64_t max_per_group = (n_tiles + kWaves - 1) / kWaves;
   if (per_group > max_per_group) per_group = max_per_group;
   if (per_group < 1) per_group = 1;
