@@ -1120,10 +1120,14 @@ __device__ __forceinline__ i32x4 plane_frag(const uint4& w, uint32_t mask) {
   return i32x4{plane_bytes(w.x, mask), plane_bytes(w.y, mask), plane_bytes(w.z, mask), plane_bytes(w.w, mask)};
 }
 
-template <int D, int BITS, bool QJL>
+// KQT: 0 = no QJL term, D/64 = the QJL term with m = d (bits of a key loaded as one vector),
+// -1 = any other m (bits read per K step).
+template <int D, int BITS, int KQT>
 __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageArgs a, int chunks_per_group) {
   constexpr int KC = D / 64;
   constexpr int NP = 1 << (BITS - 1);
+  constexpr bool QJL = KQT != 0;
+  constexpr int KQB = KQT > 0 ? KQT : 1;                  // register words for the fixed-m bits
   const int m = QJL ? a.m : 0;
   const int KQ = m >> 6, mb = m >> 3;
   const int grp = blockIdx.x / chunks_per_group, chunk = blockIdx.x % chunks_per_group;
@@ -1154,19 +1158,34 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
   float* out = a.scores + (int64_t)grp * a.n_q * T;
   const double cq = QJL ? 1.2533141373155003 / (double)m : 0.0;     // sqrt(pi/2) / m
 
-  for (int64_t tile = (int64_t)chunk * kWaves + (threadIdx.x >> 6); tile < n_tiles;
-       tile += (int64_t)chunks_per_group * kWaves) {
-    const int64_t tok = tile * 16 + r;
-    const bool valid = tok < T;
+  // one tile's inputs; tokens past the end are clamped to the last token (always in bounds,
+  // no branches); such a token only feeds its own output column, which is not stored
+  struct Inputs {
     uint4 cw[KC];
+    uint32_t qb[(KQB + 1) / 2];
+    uint16_t n16, rn16;
+  };
+  auto fetch = [&](int64_t tile, Inputs& in) {
+    const int64_t tok = min(tile * 16 + r, T - 1);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      cw[k] = make_uint4(0, 0, 0, 0);
-      if (valid) {
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + tok * D + 64 * k + 16 * gq));
-        cw[k] = make_uint4(w.x, w.y, w.z, w.w);
-      }
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + tok * D + 64 * k + 16 * gq));
+      in.cw[k] = make_uint4(w.x, w.y, w.z, w.w);
     }
+    in.n16 = norms[tok];
+    if constexpr (QJL) in.rn16 = rnorms[tok];
+    if constexpr (KQT > 0) load_key_bits<KQT>(qbits + tok * mb + (mb >> 2) * gq, true, in.qb);
+  };
+
+  const int64_t stride = (int64_t)chunks_per_group * kWaves;
+  int64_t tile = (int64_t)chunk * kWaves + (threadIdx.x >> 6);
+  Inputs nxt;
+  if (tile < n_tiles) fetch(tile, nxt);
+  for (; tile < n_tiles; tile += stride) {
+    const Inputs in = nxt;
+    if (tile + stride < n_tiles) fetch(tile + stride, nxt);   // uniform
+    const int64_t tok = tile * 16 + r;
+    const bool valid = tok < T;
     i32x4 acc[NP][3];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -1179,28 +1198,30 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
       const i32x4 a2 = fc[(2 * KC + k) * 64 + lane];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const i32x4 b = plane_frag(cw[k], pqi::plane_mask(BITS, p));
+        const i32x4 b = plane_frag(in.cw[k], pqi::plane_mask(BITS, p));
         acc[p][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc[p][0], 0, 0, 0);
         acc[p][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc[p][1], 0, 0, 0);
         acc[p][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b, acc[p][2], 0, 0, 0);
       }
     }
     i32x4 accq[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-    if constexpr (QJL) {
-      const uint8_t* kb = qbits + tok * mb + (mb >> 2) * gq;
-      for (int k = 0; k < KQ; ++k) {
-        uint32_t w16 = 0;
-        if (valid) w16 = *reinterpret_cast<const uint16_t*>(kb + 2 * k);
-        const i32x4 b = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
-                         (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
-        accq[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(0 * KQ + k) * 64 + lane], b, accq[0], 0, 0, 0);
-        accq[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(1 * KQ + k) * 64 + lane], b, accq[1], 0, 0, 0);
-        accq[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(2 * KQ + k) * 64 + lane], b, accq[2], 0, 0, 0);
-      }
+    auto qstep = [&](int k, uint32_t w16) {
+      const i32x4 b = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
+                       (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
+      accq[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(0 * KQ + k) * 64 + lane], b, accq[0], 0, 0, 0);
+      accq[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(1 * KQ + k) * 64 + lane], b, accq[1], 0, 0, 0);
+      accq[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fq[(2 * KQ + k) * 64 + lane], b, accq[2], 0, 0, 0);
+    };
+    if constexpr (KQT > 0) {
+#pragma unroll
+      for (int k = 0; k < KQT; ++k) qstep(k, (in.qb[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+    } else if constexpr (KQT < 0) {
+      const uint8_t* kb = qbits + min(tok, T - 1) * mb + (mb >> 2) * gq;
+      for (int k = 0; k < KQ; ++k) qstep(k, *reinterpret_cast<const uint16_t*>(kb + 2 * k));
     }
     if (valid) {
-      const double n16 = (double)f16_to_f32(norms[tok]) / (double)D;
-      const double rn = QJL ? (double)f16_to_f32(rnorms[tok]) * cq : 0.0;
+      const double n16 = (double)f16_to_f32(in.n16) / (double)D;
+      const double rn = QJL ? (double)f16_to_f32(in.rn16) * cq : 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qi = 4 * gq + i;
@@ -1305,8 +1326,9 @@ hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hi
 
 template <int D, int BITS>
 hipError_t launch_two_stage_db(const pqi::TwoStageArgs& a, int grid, int cpg, size_t lds, hipStream_t s) {
-  if (a.m > 0) hipLaunchKernelGGL((pq_score_kernel<D, BITS, true>), grid, kThreads, lds, s, a, cpg);
-  else hipLaunchKernelGGL((pq_score_kernel<D, BITS, false>), grid, kThreads, lds, s, a, cpg);
+  if (a.m == 0) hipLaunchKernelGGL((pq_score_kernel<D, BITS, 0>), grid, kThreads, lds, s, a, cpg);
+  else if (a.m == D) hipLaunchKernelGGL((pq_score_kernel<D, BITS, D / 64>), grid, kThreads, lds, s, a, cpg);
+  else hipLaunchKernelGGL((pq_score_kernel<D, BITS, -1>), grid, kThreads, lds, s, a, cpg);
   return hipGetLastError();
 }
 
