@@ -133,6 +133,17 @@ pqi::CodecTables make_tables(int bits) {
   }
   t.half = (int)std::ceil(Y / w);
   t.ncell = 2 * t.half + 1;
+  // nearest boundary to each cell centre (k - half) w, as the kernels compute it in fp32
+  for (int k = 0; k < t.ncell; ++k) {
+    const float c = (float)(k - t.half) * (float)w;
+    int best = 0;
+    float bd = std::fabs(t.beta[0] - c);
+    for (int j = 1; j < t.nbound; ++j) {
+      const float dd = std::fabs(t.beta[j] - c);
+      if (dd < bd) { bd = dd; best = j; }
+    }
+    t.cell_best[k] = (uint8_t)best;
+  }
   // one copy of the grid per lane of a 16-lane LDS access group when it fits in 64 KiB
   t.nrep = (size_t)t.ncell * 16 * 16 <= 65536 ? 16 : 1;
   t.cell_w = (float)w;

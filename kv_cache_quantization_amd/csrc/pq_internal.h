@@ -8,7 +8,7 @@
 namespace pqi {
 
 constexpr int kMaxBits = 8;
-constexpr int kMaxCells = 4096;
+constexpr int kMaxCells = 640;          // 583 cells at 8 bits
 
 // fp32 codebook and the geometry of the uniform search grid the kernels build
 // in LDS: cell k (0 <= k < ncell) is centred on (k - half) w and stores the
@@ -19,6 +19,7 @@ constexpr int kMaxCells = 4096;
 struct CodecTables {
   float cent[1 << kMaxBits];
   float beta[(1 << kMaxBits) - 1];
+  uint8_t cell_best[kMaxCells];   // index of the boundary nearest to each cell's centre
   int nbound;
   int ncell;        // 2 * half + 1
   int half;

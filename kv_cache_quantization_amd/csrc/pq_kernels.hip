@@ -34,18 +34,13 @@ constexpr int kWaves = kThreads / 64;
 // ------------------------------------------------------------------------------------------
 // LDS set-up shared by quantize and dequantize
 // ------------------------------------------------------------------------------------------
+// One entry per thread step; the nearest boundary of every cell comes with the tables.
 __device__ void build_search_grid(const CodecTables& t, uint4* tab) {
-  for (int k = threadIdx.x; k < t.ncell; k += blockDim.x) {
-    const float c = (float)(k - t.half) * t.cell_w;
-    int best = 0;
-    float bd = fabsf(t.beta[0] - c);
-    for (int j = 1; j < t.nbound; ++j) {
-      const float dd = fabsf(t.beta[j] - c);
-      if (dd < bd) { bd = dd; best = j; }
-    }
-    const uint4 e = make_uint4(__float_as_uint(t.beta[best]), (uint32_t)best, __float_as_uint(t.cent[best]),
-                               __float_as_uint(t.cent[best + 1]));
-    for (int rep = 0; rep < t.nrep; ++rep) tab[k * t.nrep + rep] = e;
+  const int rep_shift = t.nrep == 16 ? 4 : 0;
+  for (int i = threadIdx.x; i < t.ncell * t.nrep; i += blockDim.x) {
+    const int best = t.cell_best[i >> rep_shift];
+    tab[i] = make_uint4(__float_as_uint(t.beta[best]), (uint32_t)best, __float_as_uint(t.cent[best]),
+                        __float_as_uint(t.cent[best + 1]));
   }
 }
 
