@@ -539,40 +539,74 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUA
   }
 }
 
-// Quantize with a QJL projection too large to keep in LDS: a workgroup takes four tiles at
-// a time (one per wave), each wave keeps its tile's residual fragments in registers, and
-// the workgroup walks over G in chunks of chunk_rows rows (a multiple of 64) staged in LDS,
-// so every chunk read from L2 serves 64 blocks.
-#ifndef PQ_QUANT_CHUNK_WAVES_PER_EU
-#define PQ_QUANT_CHUNK_WAVES_PER_EU 1
-#endif
+// Quantize with a QJL projection too large to keep in LDS: a workgroup takes one tile per
+// wave at a time, each wave keeps its tile's block-coordinate residual in registers with the
+// rotation signs applied (D w = d r, times the power-of-two scale), and the workgroup walks
+// over G in chunks of kChunkRows rows staged in LDS as plain fp16, so every chunk read from
+// L2 serves all of the workgroup's blocks.
 constexpr int kChunkRows = 128;
+// eight waves where two per SIMD fit in the register file, else four with all of it
+template <int D>
+constexpr int chunk_threads() { return D <= 128 ? 512 : 256; }
+
+// Rows [row0, row0 + rows) of G as fp16 (rows >= m zero), swizzled rows of D/8 16-byte chunks.
+// bf16 values in the fp16 normal range convert exactly; smaller ones keep fp16's absolute
+// precision (6e-8), far below what decides a sign.
+template <int D>
+__device__ void stage_projection_rows_plain(const uint16_t* proj, int m, int row0, int rows, uint4* gb) {
+  constexpr int CPR = D / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(proj);
+  for (int i = threadIdx.x; i < rows * CPR; i += blockDim.x) {
+    const int nl = i / CPR, c = i % CPR, n = row0 + nl;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (n < m) {
+      const uint4 b = src[n * CPR + c];
+      w = make_uint4(split_hi_f16x2(bf16_lo(b.x), bf16_hi(b.x)), split_hi_f16x2(bf16_lo(b.y), bf16_hi(b.y)),
+                     split_hi_f16x2(bf16_lo(b.z), bf16_hi(b.z)), split_hi_f16x2(bf16_lo(b.w), bf16_hi(b.w)));
+    }
+    gb[g_swizzle<D>(nl, c)] = w;
+  }
+}
 
 template <int D, bool IN_BF16, bool REP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUANT_CHUNK_WAVES_PER_EU)))
+__global__ __launch_bounds__(chunk_threads<D>()) __attribute__((amdgpu_waves_per_eu(chunk_threads<D>() / 256)))
 void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
   using Q = Quantizer<D, IN_BF16, true, true, REP>;
+  constexpr int WAVES = chunk_threads<D>() / 64;
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* tab = reinterpret_cast<uint4*>(smem);
   uint4* gb = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
   build_search_grid(a.t, tab);
   Q q(a, smem, gb);
+  // rotation signs of this lane's residual registers: chunk k holds columns 8 res_col8(g, k) + 0..7
+  uint32_t rsg[(Q::KS + 3) / 4];
+#pragma unroll
+  for (int k = 0; k < (Q::KS + 3) / 4; ++k) rsg[k] = 0;
+#pragma unroll
+  for (int k = 0; k < Q::KS; ++k) rsg[k >> 2] |= (uint32_t)a.signs[res_col8<D>(q.g, k)] << (8 * (k & 3));
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
   const int64_t full_tiles = a.n_blocks >> 4;
-  const int64_t n_groups = (n_tiles + kWaves - 1) / kWaves;
+  const int64_t n_groups = (n_tiles + WAVES - 1) / WAVES;
   const int ntiles = q.m_pad >> 4;
   for (int64_t TG = blockIdx.x; TG < n_groups; TG += gridDim.x) {   // uniform over the workgroup
-    const int64_t T = TG * kWaves + (threadIdx.x >> 6);              // may lie past the end: no stores
+    const int64_t T = TG * WAVES + (threadIdx.x >> 6);               // may lie past the end: no stores
     __syncthreads();                                                  // search grid built / chunk free
     uint4 raw[Q::NR];
     load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
     float v[Q::E];
     q.decide(raw, T, v);
     q.residual_block(v);
+#pragma unroll
+    for (int k = 0; k < Q::KS; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sb = (rsg[k >> 2] >> (8 * (k & 3) + i)) & 1u;
+        v[8 * k + i] = __uint_as_float(__float_as_uint(v[8 * k + i]) ^ (sb << 31));
+      }
     for (int row0 = 0; row0 < q.m_pad; row0 += kChunkRows) {
       const int rows = min(kChunkRows, q.m_pad - row0);
       __syncthreads();                                                // previous chunk consumed
-      stage_projection_rows<D>(a.proj, a.signs, a.m, row0, rows, gb);
+      stage_projection_rows_plain<D>(a.proj, a.m, row0, rows, gb);
       __syncthreads();
       q.template project_kouter<kChunkRows / 16>(v, T, gb, row0, row0 >> 4, min(ntiles, (row0 + rows) >> 4));
     }
@@ -1280,15 +1314,15 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
     // G in chunks of kChunkRows rows beside the search grid
     const size_t lds = base + (size_t)kChunkRows * D * 2;
     if (lds > (size_t)c.max_lds) return hipErrorInvalidConfiguration;
-    const int64_t n_groups = (n_tiles + kWaves - 1) / kWaves;
+    const int64_t n_groups = (n_tiles + chunk_threads<D>() / 64 - 1) / (chunk_threads<D>() / 64);
     const int per_cu = std::max(1, (int)((size_t)c.max_lds / lds));
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(n_groups, (int64_t)c.cu_count * per_cu));
     if (a.t.nrep == 16) {
-      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, true>), grid, kThreads, lds, s, a);
-      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, true>), grid, kThreads, lds, s, a);
+      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, true>), grid, chunk_threads<D>(), lds, s, a);
+      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, true>), grid, chunk_threads<D>(), lds, s, a);
     } else {
-      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, false>), grid, kThreads, lds, s, a);
-      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, false>), grid, kThreads, lds, s, a);
+      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, false>), grid, chunk_threads<D>(), lds, s, a);
+      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, false>), grid, chunk_threads<D>(), lds, s, a);
     }
     return hipGetLastError();
   }
