@@ -59,6 +59,10 @@ CODEC_CASES = [
     (128, 1, "bf16", 16 * 8 + 3, 8),
     (128, 8, "bf16", 16 * 6 + 13, 24),
     (128, 2, "bf16", 16 * 5, 1024),
+    # projections beyond LDS (walked in 128-row chunks): fp32 input, a partial last chunk and
+    # N-tile group (m = 600: 38 N tiles, 75-byte bit rows), and d = 256
+    (128, 3, "f32", 16 * 3 + 7, 600),
+    (256, 4, "f32", 16 * 5 + 3, 512),
 ]
 
 
