@@ -122,7 +122,7 @@ def summarize(run_dir):
         return name.replace("void ", "").replace("(anonymous namespace)::", "").split("(pqi::")[0]
 
     trace_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/prof_trace -o trace -- "
-                 "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
+                 "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-grouped")
     lines = ["# Kernel durations of the benchmark (config 2 codec, config 4 QJL leg, config 5 two-stage leg), one MI355X",
              "", "command: " + trace_cmd, "kernel source hash: " + kernel_source_hash(), "",
              "%-58s %6s %12s %10s %10s" % ("kernel", "calls", "average_ns", "min_ns", "max_ns")]

@@ -873,7 +873,6 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-__device__ __forceinline__ int quant_int(float x, float s) { return s > 0.0f ? (int)rintf(x / s) : 0; }
 
 __device__ __forceinline__ int limb_of(int Q, int l) {
   const int h2 = (int)rintf((float)Q * (1.0f / 16384.0f));
@@ -1085,12 +1084,13 @@ __global__ __launch_bounds__(256) void pq_query_quant_kernel(const pqi::QueryPre
     for (int e = sub; e < len; e += 16) amax = fmaxf(amax, fabsf(src[e]));
     for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
     const float sc = amax / pqi::kLimbRange;
+    const float inv = sc > 0.0f ? 1.0f / sc : 0.0f;
     int acc = 0;
-    for (int e = sub; e < len; e += 16) acc += quant_int(src[e], sc);
+    for (int e = sub; e < len; e += 16) acc += (int)rintf(src[e] * inv);
     for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
     if (sub == 0) {
       const int job = term * pqi::kScoreRows + row;
-      scale[job] = sc;
+      scale[job] = inv;                                  // the reciprocal, used below
       if (slice == 0) {
         scale_out[job] = sc;
         isum_out[job] = acc;
@@ -1113,12 +1113,12 @@ __global__ __launch_bounds__(256) void pq_query_quant_kernel(const pqi::QueryPre
     const int L = inblk >> 2, byte0 = 4 * (inblk & 3);
     const int r = L & 15, gq = L >> 4;
     const float* src = qjl ? sq + (int64_t)r * m : qrot + (int64_t)r * d;
-    const float s = scale[(qjl ? pqi::kScoreRows : 0) + r];
+    const float inv = scale[(qjl ? pqi::kScoreRows : 0) + r];
     uint32_t word = 0;
     for (int b = 0; b < 4; ++b) {
       const int i = byte0 + b;
       const int e = qjl ? (m / 4) * gq + 16 * k + i : 64 * k + 16 * gq + i;
-      word |= (uint32_t)(limb_of(quant_int(src[e], s), l) & 0xff) << (8 * b);
+      word |= (uint32_t)(limb_of((int)rintf(src[e] * inv), l) & 0xff) << (8 * b);
     }
     (qjl ? fq : fc)[w] = word;
   }
