@@ -516,9 +516,13 @@ __device__ void stage_projection_rows(const uint16_t* proj, const uint8_t* signs
   }
 }
 
-template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUANT_WAVES_PER_EU))) void pq_quantize_kernel(const pqi::QuantArgs a) {
+// THREADS = 512 when G takes most of the LDS: one workgroup per CU then still runs two waves
+// per SIMD.
+template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP, int THREADS = kThreads>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU)))
+void pq_quantize_kernel(const pqi::QuantArgs a) {
   using Q = Quantizer<D, IN_BF16, QJL, G_LDS, REP>;
+  constexpr int WAVES = THREADS / 64;
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* tab = reinterpret_cast<uint4*>(smem);
   uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
@@ -529,8 +533,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUA
   Q q(a, smem, gl);
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
   const int64_t full_tiles = a.n_blocks >> 4;
-  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
-  int64_t T = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * WAVES;
+  int64_t T = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
   // several waves per SIMD overlap one wave's loads with another's arithmetic
   uint4 raw[Q::NR];
   for (; T < n_tiles; T += n_waves) {
@@ -1290,6 +1294,14 @@ hipError_t launch_quantize_r(bool in_bf16, bool qjl, bool g_lds, int grid, size_
   if (!qjl) {
     if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, false, false, REP>), grid, kThreads, lds, s, a);
     else hipLaunchKernelGGL((pq_quantize_kernel<D, false, false, false, REP>), grid, kThreads, lds, s, a);
+  } else if (D <= 256 && g_lds && lds > 65536) {
+    // one workgroup per CU: eight waves (d = 512 would spill at two waves per SIMD)
+    if constexpr (D <= 256) {
+      const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+      const int g8 = (int)std::max<int64_t>(1, std::min<int64_t>(grid, (n_tiles + 7) / 8));
+      if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true, REP, 512>), g8, 512, lds, s, a);
+      else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true, REP, 512>), g8, 512, lds, s, a);
+    }
   } else if (g_lds) {
     if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true, REP>), grid, kThreads, lds, s, a);
     else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true, REP>), grid, kThreads, lds, s, a);
