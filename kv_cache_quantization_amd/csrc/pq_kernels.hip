@@ -65,16 +65,40 @@ __device__ __forceinline__ int g_swizzle(int n, int c) {
   return n * CPR + (c ^ (n & SW));
 }
 
-template <int D>
-__device__ void stage_projection(const uint16_t* proj, int m, int m_pad, uint4* gl) {
+// Rows [row0, row0 + rows) of G into the swizzled LDS buffer gb (rows >= m zero), each
+// 16-byte chunk passed through cvt(chunk, sign byte of its 8 columns).  A thread first
+// issues BATCH loads, clamped in bounds so that none waits behind a branch, and only then
+// converts and stores them: the loads of a batch are in flight together.
+template <int D, int BATCH, typename Cvt>
+__device__ __forceinline__ void stage_rows(const uint16_t* proj, const uint8_t* signs, int m, int row0, int rows,
+                                           uint4* gb, Cvt cvt) {
   constexpr int CPR = D / 8;
   const uint4* src = reinterpret_cast<const uint4*>(proj);
-  for (int i = threadIdx.x; i < m_pad * CPR; i += blockDim.x) {
-    const int n = i / CPR, c = i % CPR;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (n < m) w = src[i];
-    gl[g_swizzle<D>(n, c)] = w;
+  const int total = rows * CPR, nt = blockDim.x;
+  for (int i0 = threadIdx.x; i0 < total; i0 += BATCH * nt) {
+    uint4 b[BATCH];
+    uint32_t sb[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = min(i0 + u * nt, total - 1);
+      const int n = min(row0 + i / CPR, m - 1);
+      b[u] = src[n * CPR + i % CPR];
+      sb[u] = signs ? signs[i % CPR] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int i = i0 + u * nt;
+      if (i < total) {
+        const int nl = i / CPR, c = i % CPR;
+        gb[g_swizzle<D>(nl, c)] = row0 + nl < m ? cvt(b[u], sb[u]) : make_uint4(0, 0, 0, 0);
+      }
+    }
   }
+}
+
+template <int D>
+__device__ void stage_projection(const uint16_t* proj, int m, int m_pad, uint4* gl) {
+  stage_rows<D, 8>(proj, nullptr, m, 0, m_pad, gl, [](const uint4& b, uint32_t) { return b; });
 }
 
 // fp16 copy of a bf16 pair of G scaled by 2^10 (exact for |G| >= 2^-24; the bf16
@@ -87,13 +111,14 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2_signed(uint32_t w, uint32_t 
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
-// Columns 8 c .. 8 c + 7 of row n of G D (the rotation signs applied to the columns
-// of G; byte c of the sign mask covers exactly these 8 columns), fp16, scaled by 2^10.
-__device__ __forceinline__ uint4 gd_chunk_f16(const uint4* src, const uint8_t* signs, int cpr, int n, int c) {
-  const uint4 b = src[n * cpr + c];
-  const uint32_t sb = signs[c];
+// A 16-byte chunk of G (8 columns, whose rotation signs are the bits of sb) as the same
+// columns of G D in fp16, scaled by 2^10.  Byte c of the sign mask covers columns 8c..8c+7.
+__device__ __forceinline__ uint4 gd_f16(const uint4& b, uint32_t sb) {
   return make_uint4(bf16x2_to_f16x2_signed(b.x, sb, 0), bf16x2_to_f16x2_signed(b.y, sb, 1),
                     bf16x2_to_f16x2_signed(b.z, sb, 2), bf16x2_to_f16x2_signed(b.w, sb, 3));
+}
+__device__ __forceinline__ uint4 gd_chunk_f16(const uint4* src, const uint8_t* signs, int cpr, int n, int c) {
+  return gd_f16(src[n * cpr + c], signs[c]);
 }
 
 template <int D, bool G_LDS>
@@ -427,39 +452,61 @@ struct Quantizer {
   }
 
   // Sign bits of the NTC N tiles from nt_begin (a multiple of 4, fewer at the end of G) with
-  // the K steps outermost: each K step splits its 8 residual values once and feeds all NTC
-  // accumulators, so only those (not the whole split residual) are live.  G rows come from
-  // the LDS buffer gb, whose row 0 is row row0 of G.
+  // the K steps outermost: each K step splits its 8 residual values once and feeds a group
+  // of accumulators, so only those (not the whole split residual) are live.  G rows come
+  // from the LDS buffer gb (NTC * 16 rows), whose row 0 is row row0 of G.
   template <int NTC>
   __device__ __forceinline__ void project_kouter(const float (&w)[E], int64_t T, const uint4* gb, int row0,
                                                  int nt_begin, int nt_end) {
-    f32x4 acc[NTC];
+    // N tiles in groups of NG; all NTC tiles of the buffer are multiplied (rows past the
+    // chunk's end hold stale values whose signs are not stored), so the K loop has no
+    // branches.  The G fragments of step k + 1 are read while step k multiplies, and a
+    // scheduling barrier per step keeps that overlap and the register count fixed.
+    constexpr int NG = (D >= 512 || NTC < 8) ? 4 : 8;
 #pragma unroll
-    for (int q = 0; q < NTC; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q0 = 0; q0 < NTC; q0 += NG) {
+      if (nt_begin + q0 >= nt_end) break;                             // uniform
+      f32x4 acc[NG];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      u32x4 hi, lo;
+      for (int q = 0; q < NG; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      auto frag = [&](int k, int q) {
+        return __builtin_bit_cast(f16x8, gb[g_swizzle<D>(16 * (nt_begin + q0 + q) + r - row0, res_col8<D>(g, k))]);
+      };
+      f16x8 b[NG];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float x0 = w[8 * k + 2 * t], x1 = w[8 * k + 2 * t + 1];
-        hi[t] = split_hi_f16x2(x0, x1);
-        lo[t] = split_lo_f16x2(hi[t], x0, x1);
-      }
+      for (int q = 0; q < NG; ++q) b[q] = frag(0, q);
 #pragma unroll
-      for (int q = 0; q < NTC; ++q) {
-        if (nt_begin + q < nt_end) {                                  // uniform
-          const int row = 16 * (nt_begin + q) + r;
-          const f16x8 b = __builtin_bit_cast(f16x8, gb[g_swizzle<D>(row - row0, res_col8<D>(g, k))]);
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, hi), acc[q], 0, 0, 0);
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, __builtin_bit_cast(f16x8, lo), acc[q], 0, 0, 0);
+      for (int k = 0; k < KS; ++k) {
+        f16x8 bn[NG];
+        if (k + 1 < KS) {
+#pragma unroll
+          for (int q = 0; q < NG; ++q) bn[q] = frag(k + 1, q);
         }
-      }
-    }
+        u32x4 hi, lo;
 #pragma unroll
-    for (int q0 = 0; q0 < NTC; q0 += 4) {
-      if (nt_begin + q0 < nt_end) {
-        const f32x4 grp[4] = {acc[q0], acc[q0 + 1], acc[q0 + 2], acc[q0 + 3]};
-        store_sign_bytes(sign_bytes4(grp), lane, T * 16, a.n_blocks, a.qbits, mb, nt_begin + q0);
+        for (int t = 0; t < 4; ++t) {
+          const float x0 = w[8 * k + 2 * t], x1 = w[8 * k + 2 * t + 1];
+          hi[t] = split_hi_f16x2(x0, x1);
+          lo[t] = split_lo_f16x2(hi[t], x0, x1);
+        }
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[q], __builtin_bit_cast(f16x8, hi), acc[q], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[q], __builtin_bit_cast(f16x8, lo), acc[q], 0, 0, 0);
+        if (k + 1 < KS) {
+#pragma unroll
+          for (int q = 0; q < NG; ++q) b[q] = bn[q];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int q1 = 0; q1 < NG; q1 += 4) {
+        if (nt_begin + q0 + q1 < nt_end) {
+          const f32x4 grp[4] = {acc[q1], acc[q1 + 1], acc[q1 + 2], acc[q1 + 3]};
+          store_sign_bytes(sign_bytes4(grp), lane, T * 16, a.n_blocks, a.qbits, mb, nt_begin + q0 + q1);
+        }
       }
     }
   }
@@ -506,14 +553,7 @@ struct Quantizer {
 template <int D>
 __device__ void stage_projection_rows(const uint16_t* proj, const uint8_t* signs, int m, int row0, int rows,
                                       uint4* gb) {
-  constexpr int CPR = D / 8;
-  const uint4* src = reinterpret_cast<const uint4*>(proj);
-  for (int i = threadIdx.x; i < rows * CPR; i += blockDim.x) {
-    const int nl = i / CPR, c = i % CPR, n = row0 + nl;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (n < m) w = gd_chunk_f16(src, signs, CPR, n, c);
-    gb[g_swizzle<D>(nl, c)] = w;
-  }
+  stage_rows<D, 8>(proj, signs, m, row0, rows, gb, [](const uint4& b, uint32_t sb) { return gd_f16(b, sb); });
 }
 
 // THREADS = 512 when G takes most of the LDS: one workgroup per CU then still runs two waves
@@ -550,6 +590,9 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
 // L2 serves all of the workgroup's blocks.
 constexpr int kChunkRows = 128;
 // eight waves where two per SIMD fit in the register file, else four with all of it
+#ifndef PQ_CHUNK_STAGE_BATCH
+#define PQ_CHUNK_STAGE_BATCH 8
+#endif
 template <int D>
 constexpr int chunk_threads() { return D <= 128 ? 512 : 256; }
 
@@ -558,18 +601,10 @@ constexpr int chunk_threads() { return D <= 128 ? 512 : 256; }
 // precision (6e-8), far below what decides a sign.
 template <int D>
 __device__ void stage_projection_rows_plain(const uint16_t* proj, int m, int row0, int rows, uint4* gb) {
-  constexpr int CPR = D / 8;
-  const uint4* src = reinterpret_cast<const uint4*>(proj);
-  for (int i = threadIdx.x; i < rows * CPR; i += blockDim.x) {
-    const int nl = i / CPR, c = i % CPR, n = row0 + nl;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (n < m) {
-      const uint4 b = src[n * CPR + c];
-      w = make_uint4(split_hi_f16x2(bf16_lo(b.x), bf16_hi(b.x)), split_hi_f16x2(bf16_lo(b.y), bf16_hi(b.y)),
-                     split_hi_f16x2(bf16_lo(b.z), bf16_hi(b.z)), split_hi_f16x2(bf16_lo(b.w), bf16_hi(b.w)));
-    }
-    gb[g_swizzle<D>(nl, c)] = w;
-  }
+  stage_rows<D, PQ_CHUNK_STAGE_BATCH>(proj, nullptr, m, row0, rows, gb, [](const uint4& b, uint32_t) {
+    return make_uint4(split_hi_f16x2(bf16_lo(b.x), bf16_hi(b.x)), split_hi_f16x2(bf16_lo(b.y), bf16_hi(b.y)),
+                      split_hi_f16x2(bf16_lo(b.z), bf16_hi(b.z)), split_hi_f16x2(bf16_lo(b.w), bf16_hi(b.w)));
+  });
 }
 
 template <int D, bool IN_BF16, bool REP>
