@@ -195,6 +195,16 @@ __host__ __device__ constexpr int dq_out_chunk(int s) {
                   : (((s & 1) << 7) | (((s >> 1) & 1) << 8) | (((s >> 2) & 1) << 5) | (((s >> 3) & 1) << 6));
 }
 
+// The register chunk whose elements follow those of chunk s (dq_out_chunk + 32): chunks s
+// and dq_partner(s), s with dq_out_chunk(s) a multiple of 64, make up one 128-byte line of
+// bf16 output.
+template <int D>
+__host__ __device__ constexpr int dq_partner(int s) {
+  for (int t = 0; t < D / 32; ++t)
+    if (dq_out_chunk<D>(t) == dq_out_chunk<D>(s) + 32) return t;
+  return -1;
+}
+
 // The quantize kernel takes the rotated residual rho (contiguous layout, registers
 // renamed to offset order) back through the dequantize butterflies: register chunk k
 // (registers 8k .. 8k+7) of quarter g then holds elements 8 res_col8(k) + 0..7 of

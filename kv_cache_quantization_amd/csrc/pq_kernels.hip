@@ -653,7 +653,8 @@ void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Dequantize
+// Dequantize.  Outputs are written with non-temporal stores: they stream to HBM without
+// displacing the codes and tables in the caches.
 // ------------------------------------------------------------------------------------------
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
@@ -699,8 +700,6 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
     uint16_t nbn;
     load(qn, nbn, T + n_waves);
 
-    const int64_t blk = T * 16 + r;
-    const bool valid = blk < n_blocks;
     float v[E];
 #pragma unroll
     for (int w = 0; w < NR; ++w) {
@@ -714,32 +713,51 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 
     wht_dequant<D>(v);
 
-    if (valid) {
-      if constexpr (OUT_BF16) {
-        uint16_t* out = static_cast<uint16_t*>(a.out) + blk * D + 8 * g;
+    // Stores write whole 128-byte lines: a line of a block is two 16-byte pieces (a, b) in
+    // each of its four lanes; the neighbouring blocks r & ~1 and r | 1 (lanes l, l ^ 1) trade
+    // pieces, so that one store writes block r & ~1's line from both lanes and the next
+    // block r | 1's.  Half-line stores would reach HBM as partial lines.
+    const bool odd = r & 1;
+    const int64_t blk_e = T * 16 + (r & ~1);
+    const bool ok_e = blk_e < n_blocks, ok_o = blk_e + 1 < n_blocks;
+    auto put = [&](auto* row_e, const u32x4& pa, const u32x4& pb, int off_a, int off_b) {
+      u32x4 x, y;
 #pragma unroll
-        for (int s = 0; s < E / 8; ++s) {
-          uint4 w;
-          w.x = pack_bf16x2(v[8 * s + 0] * scale, v[8 * s + 1] * scale) ^ smask[4 * s + 0];
-          w.y = pack_bf16x2(v[8 * s + 2] * scale, v[8 * s + 3] * scale) ^ smask[4 * s + 1];
-          w.z = pack_bf16x2(v[8 * s + 4] * scale, v[8 * s + 5] * scale) ^ smask[4 * s + 2];
-          w.w = pack_bf16x2(v[8 * s + 6] * scale, v[8 * s + 7] * scale) ^ smask[4 * s + 3];
-          *reinterpret_cast<uint4*>(out + dq_out_chunk<D>(s)) = w;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? pa[i] : pb[i]), 0xB1, 0xF, 0xF, true);
+        x[i] = odd ? recv : pa[i];                                    // block r & ~1: its a, then its b
+        y[i] = odd ? pb[i] : recv;                                    // block r | 1
+      }
+      const int off = odd ? off_b : off_a;
+      if (ok_e) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(row_e + off));
+      if (ok_o) __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(row_e + D + off));
+    };
+    if constexpr (OUT_BF16) {
+      uint16_t* row_e = static_cast<uint16_t*>(a.out) + blk_e * D + 8 * g;
+      auto pack = [&](int s) {
+        u32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          w[t] = pack_bf16x2(v[8 * s + 2 * t] * scale, v[8 * s + 2 * t + 1] * scale) ^ smask[4 * s + t];
+        return w;
+      };
+      // chunk s and chunk dq_partner(s) hold the two halves of one output line
+#pragma unroll
+      for (int s = 0; s < E / 8; ++s)
+        if (dq_out_chunk<D>(s) % 64 == 0) put(row_e, pack(s), pack(dq_partner<D>(s)), dq_out_chunk<D>(s), dq_out_chunk<D>(s) + 32);
+    } else {
+      float* row_e = static_cast<float*>(a.out) + blk_e * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < E / 8; ++s) {
+        float f[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t sb = (smask[4 * s + t / 2] >> (t & 1)) & 1u;
+          f[t] = __uint_as_float(__float_as_uint(v[8 * s + t] * scale) ^ (sb << 31));
         }
-      } else {
-        float* out = static_cast<float*>(a.out) + blk * D + 8 * g;
-#pragma unroll
-        for (int s = 0; s < E / 8; ++s) {
-          float f[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const uint32_t sb = (smask[4 * s + t / 2] >> (t & 1)) & 1u;
-            f[t] = __uint_as_float(__float_as_uint(v[8 * s + t] * scale) ^ (sb << 31));
-          }
-          float4* o4 = reinterpret_cast<float4*>(out + dq_out_chunk<D>(s));
-          o4[0] = make_float4(f[0], f[1], f[2], f[3]);
-          o4[1] = make_float4(f[4], f[5], f[6], f[7]);
-        }
+        const u32x4 pa = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+        const u32x4 pb = {__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7])};
+        put(row_e, pa, pb, dq_out_chunk<D>(s), dq_out_chunk<D>(s) + 4);
       }
     }
 #pragma unroll
