@@ -404,7 +404,24 @@ struct Quantizer {
     // the store branch below and keeps every lookup result live until then
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) asm volatile("" : "+v"(cw[w]));
-    if (valid) {
+    if constexpr (D == 128) {
+      // a block's codes are one 128-byte line, two 16-byte pieces per lane: the neighbouring
+      // blocks r & ~1 and r | 1 (lanes l, l ^ 1) trade pieces so that each store writes
+      // whole lines (half-line stores reach HBM as partial lines)
+      const bool odd = r & 1;
+      const int64_t blk_e = T * 16 + (r & ~1);
+      u32x4 x, y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? cw[i] : cw[4 + i]), 0xB1, 0xF, 0xF, true);
+        x[i] = odd ? recv : cw[i];
+        y[i] = odd ? cw[4 + i] : recv;
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(a.codes + blk_e * D + E * qpos<D>(g) + (odd ? 16 : 0));
+      if (blk_e < n_blocks) dst[0] = x;
+      if (blk_e + 1 < n_blocks) dst[D / 16] = y;
+      if (valid && g == 0) a.norms[blk] = n16;
+    } else if (valid) {
       uint4* dst = reinterpret_cast<uint4*>(a.codes + blk * D + E * qpos<D>(g));
 #pragma unroll
       for (int w = 0; w < E / 16; ++w)
