@@ -1034,7 +1034,6 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
   for (int k = 0; k < KS; ++k) af[k] = frag[k * 64 + lane];
 
   const int64_t T = a.n_keys;
-  const int64_t n_tiles = (T + 15) >> 4;
   const uint8_t* bits = a.bits + (int64_t)grp * T * mb;
   const uint16_t* norms = a.norms + (int64_t)grp * T;
   const float c0 = 1.2533141373155003f / (float)m;        // sqrt(pi/2) / m
@@ -1044,24 +1043,29 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
   const float s_out = out_lane ? scl[gq] * c0 : 0.0f;
   const float sumq_out = out_lane ? (float)isum[gq] : 0.0f;
 
-  // U tiles per iteration, the next U tiles' bits and norms in flight meanwhile
+  // A wave takes 32 keys at a time as two 16-key tiles, the even keys and the odd keys, so
+  // that lane (gq, r) ends with keys 2r and 2r + 1 and stores them together: 16 lanes write
+  // a whole 128-byte line of a query head's scores.  U tiles (U/2 pairs) per iteration, the
+  // next U tiles' bits and norms in flight meanwhile.
   constexpr int U = 4;
+  const int64_t n_pairs = (T + 31) >> 5;
   const int64_t stride = (int64_t)chunks_per_group * kWaves;
   // loads of clamped keys (always in bounds, no branches, so several stay in flight); a
   // key past the end only feeds its own output column, which is not stored
-  auto fetch = [&](int64_t t0, uint32_t (&w)[U][(KS + 1) / 2], uint16_t (&nu)[U]) {
+  auto fetch = [&](int64_t p0, uint32_t (&w)[U][(KS + 1) / 2], uint16_t (&nu)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t key = min((t0 + u * stride) * 16 + r, T - 1);
+      const int64_t key = min((p0 + (u >> 1) * stride) * 32 + 2 * r + (u & 1), T - 1);
       load_key_bits<KS>(bits + key * mb + (mb >> 2) * gq, true, w[u]);
       nu[u] = norms[key];
     }
   };
+  const bool pairs_aligned = (T & 1) == 0;                // float2 stores stay 8-byte aligned
   uint32_t wn[U][(KS + 1) / 2];
   uint16_t nn[U];
-  int64_t tile = (int64_t)chunk * kWaves + wv;
-  fetch(tile, wn, nn);
-  for (; tile < n_tiles; tile += U * stride) {
+  int64_t pair = (int64_t)chunk * kWaves + wv;
+  fetch(pair, wn, nn);
+  for (; pair < n_pairs; pair += (U / 2) * stride) {
     uint32_t w[U][(KS + 1) / 2];
     uint16_t nu[U];
 #pragma unroll
@@ -1070,25 +1074,37 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
 #pragma unroll
       for (int j = 0; j < (KS + 1) / 2; ++j) w[u][j] = wn[u][j];
     }
-    fetch(tile + U * stride, wn, nn);
+    fetch(pair + (U / 2) * stride, wn, nn);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t = tile + u * stride;
-      if (t >= n_tiles) break;                                        // uniform
-      const int64_t key = t * 16 + r;
-      i32x4 acc = {0, 0, 0, 0};
+    for (int up = 0; up < U / 2; ++up) {
+      const int64_t pp = pair + up * stride;
+      if (pp >= n_pairs) break;                                       // uniform
+      float val[2];
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const uint32_t w16 = (w[u][k >> 1] >> (16 * (k & 1))) & 0xffffu;
-        const i32x4 bf = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
-                          (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[k], bf, acc, 0, 0, 0);
-      }
-      // lane (gq, key r): acc[l] = sum_i bit_i * limb_l of query head gq.  S = sum_i bit_i Q_i is
-      // exact in int32 (|S| <= m * kLimbRange < 2^31); 2 S - sum Q then carries one fp32 rounding.
-      if (key < T && out_lane) {
+      for (int sub = 0; sub < 2; ++sub) {
+        const int u = 2 * up + sub;
+        i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const uint32_t w16 = (w[u][k >> 1] >> (16 * (k & 1))) & 0xffffu;
+          const i32x4 bf = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
+                            (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[k], bf, acc, 0, 0, 0);
+        }
+        // lane (gq, key): acc[l] = sum_i bit_i * limb_l of query head gq.  S = sum_i bit_i Q_i
+        // is exact in int32 (|S| <= m * kLimbRange < 2^31); 2 S - sum Q then carries one fp32
+        // rounding.
         const int S = acc[0] * 16384 + acc[1] * 128 + acc[2];
-        out[key] = f16_to_f32(nu[u]) * s_out * fmaf(2.0f, (float)S, -sumq_out);
+        val[sub] = f16_to_f32(nu[u]) * s_out * fmaf(2.0f, (float)S, -sumq_out);
+      }
+      const int64_t key = pp * 32 + 2 * r;
+      if (out_lane) {
+        if (pairs_aligned && key + 1 < T) {
+          *reinterpret_cast<float2*>(out + key) = make_float2(val[0], val[1]);
+        } else {
+          if (key < T) out[key] = val[0];
+          if (key + 1 < T) out[key + 1] = val[1];
+        }
       }
     }
   }
@@ -1533,13 +1549,13 @@ hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
 
 hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s) {
   const int groups = a.batch * a.kv_heads;
-  const int64_t n_tiles = (a.n_keys + 15) >> 4;
-  // eight workgroups per CU, at most one wave per tile
+  // PQ_SCORE_WG_PER_CU workgroups per CU, at most one wave per 32 keys
 #ifndef PQ_SCORE_WG_PER_CU
 #define PQ_SCORE_WG_PER_CU 4
 #endif
   int64_t per_group = ((int64_t)c.cu_count * PQ_SCORE_WG_PER_CU + groups - 1) / groups;
-  const int64_t max_per_group = (n_tiles + kWaves - 1) / kWaves;
+  const int64_t n_pairs = (a.n_keys + 31) >> 5;             // a wave takes 32 keys at a time
+  const int64_t max_per_group = (n_pairs + kWaves - 1) / kWaves;
   if (per_group > max_per_group) per_group = max_per_group;
   if (per_group < 1) per_group = 1;
   const int grid = (int)(per_group * groups);
