@@ -468,66 +468,6 @@ struct Quantizer {
     for (int i = 0; i < E; ++i) v[i] = w[i];
   }
 
-  // Sign bits of the NTC N tiles from nt_begin (a multiple of 4, fewer at the end of G) with
-  // the K steps outermost: each K step splits its 8 residual values once and feeds a group
-  // of accumulators, so only those (not the whole split residual) are live.  G rows come
-  // from the LDS buffer gb (NTC * 16 rows), whose row 0 is row row0 of G.
-  template <int NTC>
-  __device__ __forceinline__ void project_kouter(const float (&w)[E], int64_t T, const uint4* gb, int row0,
-                                                 int nt_begin, int nt_end) {
-    // N tiles in groups of NG; all NTC tiles of the buffer are multiplied (rows past the
-    // chunk's end hold stale values whose signs are not stored), so the K loop has no
-    // branches.  The G fragments of step k + 1 are read while step k multiplies, and a
-    // scheduling barrier per step keeps that overlap and the register count fixed.
-    constexpr int NG = (D >= 512 || NTC < 8) ? 4 : 8;
-#pragma unroll
-    for (int q0 = 0; q0 < NTC; q0 += NG) {
-      if (nt_begin + q0 >= nt_end) break;                             // uniform
-      f32x4 acc[NG];
-#pragma unroll
-      for (int q = 0; q < NG; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      auto frag = [&](int k, int q) {
-        return __builtin_bit_cast(f16x8, gb[g_swizzle<D>(16 * (nt_begin + q0 + q) + r - row0, res_col8<D>(g, k))]);
-      };
-      f16x8 b[NG];
-#pragma unroll
-      for (int q = 0; q < NG; ++q) b[q] = frag(0, q);
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        f16x8 bn[NG];
-        if (k + 1 < KS) {
-#pragma unroll
-          for (int q = 0; q < NG; ++q) bn[q] = frag(k + 1, q);
-        }
-        u32x4 hi, lo;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float x0 = w[8 * k + 2 * t], x1 = w[8 * k + 2 * t + 1];
-          hi[t] = split_hi_f16x2(x0, x1);
-          lo[t] = split_lo_f16x2(hi[t], x0, x1);
-        }
-#pragma unroll
-        for (int q = 0; q < NG; ++q)
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[q], __builtin_bit_cast(f16x8, hi), acc[q], 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < NG; ++q)
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[q], __builtin_bit_cast(f16x8, lo), acc[q], 0, 0, 0);
-        if (k + 1 < KS) {
-#pragma unroll
-          for (int q = 0; q < NG; ++q) b[q] = bn[q];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int q1 = 0; q1 < NG; q1 += 4) {
-        if (nt_begin + q0 + q1 < nt_end) {
-          const f32x4 grp[4] = {acc[q1], acc[q1 + 1], acc[q1 + 2], acc[q1 + 3]};
-          store_sign_bytes(sign_bytes4(grp), lane, T * 16, a.n_blocks, a.qbits, mb, nt_begin + q0 + q1);
-        }
-      }
-    }
-  }
-
   // Sign bits of N tiles [nt_begin, nt_end) (nt_begin a multiple of 4).  G rows come from
   // the LDS buffer gb, whose row 0 is row row0 of G, or (without LDS) from global memory.
   template <bool FROM_LDS>
@@ -600,71 +540,121 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
   }
 }
 
-// Quantize with a QJL projection too large to keep in LDS: a workgroup takes one tile per
-// wave at a time, each wave keeps its tile's block-coordinate residual in registers with the
-// rotation signs applied (D w = d r, times the power-of-two scale), and the workgroup walks
-// over G in chunks of kChunkRows rows staged in LDS as plain fp16, so every chunk read from
-// L2 serves all of the workgroup's blocks.
-constexpr int kChunkRows = 128;
+// Quantize with a QJL projection too large to keep in LDS (config 5: m = d = 512 would need
+// 512 KiB).  A workgroup quantizes one tile per wave; each wave writes its tile's
+// block-coordinate residual (rotation signs applied, D w = d r times the power-of-two scale)
+// to LDS as fp16 high and low MFMA B fragments.  The workgroup then multiplies G by the
+// residuals of all its tiles: wave w takes the groups of four N tiles w, w + WAVES, ...,
+// reads their G fragments straight from L2 into registers (bf16 -> fp16, two K steps ahead),
+// and every G fragment feeds 2 x 4 tiles of MFMAs while every residual fragment read from
+// LDS feeds four N tiles.  bf16 values in the fp16 normal range convert exactly; smaller ones
+// keep fp16's absolute precision (6e-8), far below what decides a sign.
 // eight waves where two per SIMD fit in the register file, else four with all of it
-#ifndef PQ_CHUNK_STAGE_BATCH
-#define PQ_CHUNK_STAGE_BATCH 8
-#endif
 template <int D>
 constexpr int chunk_threads() { return D <= 128 ? 512 : 256; }
-
-// Rows [row0, row0 + rows) of G as fp16 (rows >= m zero), swizzled rows of D/8 16-byte chunks.
-// bf16 values in the fp16 normal range convert exactly; smaller ones keep fp16's absolute
-// precision (6e-8), far below what decides a sign.
+// LDS bytes of the residual fragments of one workgroup
 template <int D>
-__device__ void stage_projection_rows_plain(const uint16_t* proj, int m, int row0, int rows, uint4* gb) {
-  stage_rows<D, PQ_CHUNK_STAGE_BATCH>(proj, nullptr, m, row0, rows, gb, [](const uint4& b, uint32_t) {
-    return make_uint4(split_hi_f16x2(bf16_lo(b.x), bf16_hi(b.x)), split_hi_f16x2(bf16_lo(b.y), bf16_hi(b.y)),
-                      split_hi_f16x2(bf16_lo(b.z), bf16_hi(b.z)), split_hi_f16x2(bf16_lo(b.w), bf16_hi(b.w)));
-  });
+constexpr size_t chunk_frag_bytes() { return (size_t)(chunk_threads<D>() / 64) * (D / 32) * 2 * 64 * 16; }
+
+__device__ __forceinline__ f16x8 bf16x8_to_f16(const uint4& b) {
+  const u32x4 h = {split_hi_f16x2(bf16_lo(b.x), bf16_hi(b.x)), split_hi_f16x2(bf16_lo(b.y), bf16_hi(b.y)),
+                   split_hi_f16x2(bf16_lo(b.z), bf16_hi(b.z)), split_hi_f16x2(bf16_lo(b.w), bf16_hi(b.w))};
+  return __builtin_bit_cast(f16x8, h);
 }
 
 template <int D, bool IN_BF16, bool REP>
 __global__ __launch_bounds__(chunk_threads<D>()) __attribute__((amdgpu_waves_per_eu(chunk_threads<D>() / 256)))
 void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
   using Q = Quantizer<D, IN_BF16, true, true, REP>;
-  constexpr int WAVES = chunk_threads<D>() / 64;
+  constexpr int THREADS = chunk_threads<D>();
+  constexpr int WAVES = THREADS / 64;
+  constexpr int KS = Q::KS;
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* tab = reinterpret_cast<uint4*>(smem);
-  uint4* gb = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
+  u32x4* rf = reinterpret_cast<u32x4*>(smem + a.t.ncell * a.t.nrep * 16);   // [WAVES][KS][2][64]
   build_search_grid(a.t, tab);
-  Q q(a, smem, gb);
+  Q q(a, smem, nullptr);
+  const int lane = q.lane, r = q.r, g = q.g, wv = threadIdx.x >> 6;
   // rotation signs of this lane's residual registers: chunk k holds columns 8 res_col8(g, k) + 0..7
-  uint32_t rsg[(Q::KS + 3) / 4];
+  uint32_t rsg[(KS + 3) / 4];
 #pragma unroll
-  for (int k = 0; k < (Q::KS + 3) / 4; ++k) rsg[k] = 0;
+  for (int k = 0; k < (KS + 3) / 4; ++k) rsg[k] = 0;
 #pragma unroll
-  for (int k = 0; k < Q::KS; ++k) rsg[k >> 2] |= (uint32_t)a.signs[res_col8<D>(q.g, k)] << (8 * (k & 3));
+  for (int k = 0; k < KS; ++k) rsg[k >> 2] |= (uint32_t)a.signs[res_col8<D>(g, k)] << (8 * (k & 3));
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
   const int64_t full_tiles = a.n_blocks >> 4;
   const int64_t n_groups = (n_tiles + WAVES - 1) / WAVES;
-  const int ntiles = q.m_pad >> 4;
+  const int m = a.m, ngrp = (q.m_pad + 63) >> 6;                    // groups of four N tiles
+  const uint4* gsrc = reinterpret_cast<const uint4*>(a.proj);
   for (int64_t TG = blockIdx.x; TG < n_groups; TG += gridDim.x) {   // uniform over the workgroup
-    const int64_t T = TG * WAVES + (threadIdx.x >> 6);               // may lie past the end: no stores
-    __syncthreads();                                                  // search grid built / chunk free
-    uint4 raw[Q::NR];
-    load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
-    float v[Q::E];
-    q.decide(raw, T, v);
-    q.residual_block(v);
+    const int64_t T = TG * WAVES + wv;                               // may lie past the end: no stores
+    __syncthreads();                                                  // search grid built / fragments consumed
+    {
+      uint4 raw[Q::NR];
+      load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, r, g);
+      float v[Q::E];
+      q.decide(raw, T, v);
+      q.residual_block(v);
+      u32x4* my = rf + (size_t)wv * KS * 2 * 64;
 #pragma unroll
-    for (int k = 0; k < Q::KS; ++k)
+      for (int k = 0; k < KS; ++k) {
+        u32x4 hi, lo;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sb = (rsg[k >> 2] >> (8 * (k & 3) + i)) & 1u;
-        v[8 * k + i] = __uint_as_float(__float_as_uint(v[8 * k + i]) ^ (sb << 31));
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t s0 = (rsg[k >> 2] >> (8 * (k & 3) + 2 * t)) & 1u;
+          const uint32_t s1 = (rsg[k >> 2] >> (8 * (k & 3) + 2 * t + 1)) & 1u;
+          const float x0 = __uint_as_float(__float_as_uint(v[8 * k + 2 * t]) ^ (s0 << 31));
+          const float x1 = __uint_as_float(__float_as_uint(v[8 * k + 2 * t + 1]) ^ (s1 << 31));
+          hi[t] = split_hi_f16x2(x0, x1);
+          lo[t] = split_lo_f16x2(hi[t], x0, x1);
+        }
+        my[(2 * k) * 64 + lane] = hi;
+        my[(2 * k + 1) * 64 + lane] = lo;
       }
-    for (int row0 = 0; row0 < q.m_pad; row0 += kChunkRows) {
-      const int rows = min(kChunkRows, q.m_pad - row0);
-      __syncthreads();                                                // previous chunk consumed
-      stage_projection_rows_plain<D>(a.proj, a.m, row0, rows, gb);
-      __syncthreads();
-      q.template project_kouter<kChunkRows / 16>(v, T, gb, row0, row0 >> 4, min(ntiles, (row0 + rows) >> 4));
+    }
+    __syncthreads();                                                  // every tile's fragments written
+    for (int grp = wv; grp < ngrp; grp += WAVES) {
+      // G fragment (N tile 4 grp + j, K step k): row 16 (4 grp + j) + r, columns 8 res_col8(g, k) + 0..7;
+      // rows past m read row m - 1 (their signs are not stored)
+      auto gload = [&](int k, uint4 (&ga)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = min(16 * (4 * grp + j) + r, m - 1);
+          ga[j] = gsrc[(int64_t)row * (D / 8) + res_col8<D>(g, k)];
+        }
+      };
+#pragma unroll
+      for (int t0 = 0; t0 < WAVES; t0 += 4) {
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[tt][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        uint4 ga[2][4];
+        gload(0, ga[0]);
+        if (KS > 1) gload(1, ga[1]);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          f16x8 af[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) af[j] = bf16x8_to_f16(ga[k & 1][j]);
+          if (k + 2 < KS) gload(k + 2, ga[k & 1]);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const u32x4* f = rf + ((size_t)(t0 + tt) * KS + k) * 2 * 64 + lane;
+            const f16x8 bh = __builtin_bit_cast(f16x8, f[0]);
+            const f16x8 bl = __builtin_bit_cast(f16x8, f[64]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bh, acc[tt][j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bl, acc[tt][j], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);                          // keeps the loads two steps ahead, no further
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          store_sign_bytes(sign_bytes4(acc[tt]), lane, (TG * WAVES + t0 + tt) * 16, a.n_blocks, a.qbits, q.mb, 4 * grp);
+      }
     }
   }
 }
@@ -1409,8 +1399,8 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   // workgroups per CU while it takes at most 64 KiB), else walked in chunks
   const bool g_lds = qjl && base + glb <= (size_t)c.max_lds;
   if (qjl && !g_lds) {
-    // G in chunks of kChunkRows rows beside the search grid
-    const size_t lds = base + (size_t)kChunkRows * D * 2;
+    // residual fragments of every tile of the workgroup beside the search grid
+    const size_t lds = base + chunk_frag_bytes<D>();
     if (lds > (size_t)c.max_lds) return hipErrorInvalidConfiguration;
     const int64_t n_groups = (n_tiles + chunk_threads<D>() / 64 - 1) / (chunk_threads<D>() / 64);
     const int per_cu = std::max(1, (int)((size_t)c.max_lds / lds));
