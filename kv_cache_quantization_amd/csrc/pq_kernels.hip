@@ -552,6 +552,9 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
 // eight waves where two per SIMD fit in the register file, else four with all of it
 template <int D>
 constexpr int chunk_threads() { return D <= 128 ? 512 : 256; }
+#ifndef PQ_CHUNK_GDEPTH
+#define PQ_CHUNK_GDEPTH 3
+#endif
 // LDS bytes of the residual fragments of one workgroup
 template <int D>
 constexpr size_t chunk_frag_bytes() { return (size_t)(chunk_threads<D>() / 64) * (D / 32) * 2 * 64 * 16; }
@@ -630,26 +633,41 @@ void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[tt][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        uint4 ga[2][4];
-        gload(0, ga[0]);
-        if (KS > 1) gload(1, ga[1]);
+        // G fragments PQ_CHUNK_GDEPTH K steps ahead, residual fragments one K step ahead
+        constexpr int GD = PQ_CHUNK_GDEPTH;
+        uint4 ga[GD][4];
+#pragma unroll
+        for (int k = 0; k < GD && k < KS; ++k) gload(k, ga[k]);
+        auto bload = [&](int k, f16x8 (&b)[4][2]) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const u32x4* f = rf + ((size_t)(t0 + tt) * KS + k) * 2 * 64 + lane;
+            b[tt][0] = __builtin_bit_cast(f16x8, f[0]);
+            b[tt][1] = __builtin_bit_cast(f16x8, f[64]);
+          }
+        };
+        f16x8 bc[4][2];
+        bload(0, bc);
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
           f16x8 af[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) af[j] = bf16x8_to_f16(ga[k & 1][j]);
-          if (k + 2 < KS) gload(k + 2, ga[k & 1]);
+          for (int j = 0; j < 4; ++j) af[j] = bf16x8_to_f16(ga[k % GD][j]);
+          if (k + GD < KS) gload(k + GD, ga[k % GD]);
+          f16x8 bn[4][2];
+          if (k + 1 < KS) bload(k + 1, bn);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            const u32x4* f = rf + ((size_t)(t0 + tt) * KS + k) * 2 * 64 + lane;
-            const f16x8 bh = __builtin_bit_cast(f16x8, f[0]);
-            const f16x8 bl = __builtin_bit_cast(f16x8, f[64]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bh, acc[tt][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bc[tt][0], acc[tt][j], 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bl, acc[tt][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) acc[tt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[j], bc[tt][1], acc[tt][j], 0, 0, 0);
           }
-          __builtin_amdgcn_sched_barrier(0);                          // keeps the loads two steps ahead, no further
+          if (k + 1 < KS) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) { bc[tt][0] = bn[tt][0]; bc[tt][1] = bn[tt][1]; }
+          }
+          __builtin_amdgcn_sched_barrier(0);                          // keeps the loads where they are issued
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
