@@ -130,6 +130,41 @@ def qjl_residual(x, codes, n16, bits, D, G):
             "bits": pack_bits_lsb(p > 0)}
 
 
+def pack_codes(codes, bits):
+    """Codes [n, d] (each below 2^bits) -> packed bytes [n, d * bits / 8].
+
+    eliza quantization README, TurboQuant, "Algorithm in one paragraph", step 4: the indices
+    are bit-packed into bytes, two per byte at 4 bits and four per byte at 2 bits.  Reading
+    (the pages fix the density, not the order): each block is a little-endian bit stream,
+    bit j of code i is stream bit bits * i + j, and stream bit p is bit p mod 8 of byte
+    p div 8 -- at 4 bits code 2k is the low nibble of byte k, as for the QJL sign bits the
+    first element takes the least significant bit."""
+    codes = np.asarray(codes, dtype=np.int64)
+    n, d = codes.shape
+    if (d * bits) % 8:
+        raise ValueError("d * bits must be a multiple of 8")
+    if codes.size and (codes.min() < 0 or codes.max() >= (1 << bits)):
+        raise ValueError("code out of range")
+    out = np.zeros((n, d * bits // 8), dtype=np.uint8)
+    for i in range(d):
+        for j in range(bits):
+            p = bits * i + j
+            out[:, p // 8] |= (((codes[:, i] >> j) & 1) << (p % 8)).astype(np.uint8)
+    return out
+
+
+def unpack_codes(packed, bits, d):
+    """Inverse of ``pack_codes``: packed bytes [n, d * bits / 8] -> codes [n, d] (uint8)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    n = packed.shape[0]
+    codes = np.zeros((n, d), dtype=np.int64)
+    for i in range(d):
+        for j in range(bits):
+            p = bits * i + j
+            codes[:, i] |= ((packed[:, p // 8].astype(np.int64) >> (p % 8)) & 1) << j
+    return codes.astype(np.uint8)
+
+
 def storage_bytes_per_block(d, bits_per_code_byte=8, m=0):
     """Bytes the codec stores per block: d code bytes + fp16 norm, plus m/8 sign
     bytes + fp16 residual norm when the QJL stage is on."""

@@ -172,3 +172,41 @@ def test_storage_accounting():
     # codes-only payload: 1 byte per coordinate + fp16 norm per block
     assert codec.storage_bytes_per_block(128) == 130
     assert codec.storage_bytes_per_block(128, m=64) == 130 + 8 + 2
+
+
+# --- packed codes ---------------------------------------------------------------------
+# eliza quantization README, TurboQuant, "Algorithm in one paragraph", step 4: indices are
+# bit-packed into bytes, two per byte at 4 bits, four per byte at 2 bits.
+
+def test_pack_codes_hand_fixture():
+    """Bytes worked out by hand from the stated bit order (first index, lowest bits)."""
+    four = codec.pack_codes(np.array([[1, 2, 3, 15, 0, 7, 8, 9]]), 4)
+    assert four.tolist() == [[0x21, 0xF3, 0x70, 0x98]]
+    two = codec.pack_codes(np.array([[0, 1, 2, 3, 3, 2, 1, 0]]), 2)
+    assert two.tolist() == [[0xE4, 0x1B]]
+    three = codec.pack_codes(np.array([[5, 6, 7, 1, 0, 2, 4, 3]]), 3)
+    assert three.tolist() == [[0xF5, 0x03, 0x71]]
+    one = codec.pack_codes(np.array([[1, 0, 0, 1, 1, 1, 0, 1]]), 1)
+    assert one.tolist() == [[0xB9]]
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("d", [8, 64, 128, 512])
+def test_pack_codes_against_numpy_packbits(bits, d):
+    """The packed stream equals numpy's little-endian packbits of the explicit bit matrix;
+    the size is d * bits / 8 bytes (d / 2 at 4 bits, d / 4 at 2 bits); unpack inverts."""
+    rng = np.random.default_rng(bits * 1000 + d)
+    codes = rng.integers(0, 1 << bits, size=(37, d))
+    bitmat = ((codes[:, :, None] >> np.arange(bits)) & 1).reshape(37, d * bits).astype(np.uint8)
+    ref = np.packbits(bitmat, axis=1, bitorder="little")
+    got = codec.pack_codes(codes, bits)
+    assert got.shape == (37, d * bits // 8)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(codec.unpack_codes(got, bits, d), codes.astype(np.uint8))
+
+
+def test_pack_codes_rejects_bad_input():
+    with pytest.raises(ValueError):
+        codec.pack_codes(np.array([[16, 0]]), 4)
+    with pytest.raises(ValueError):
+        codec.pack_codes(np.zeros((1, 3)), 3)
