@@ -132,6 +132,26 @@ int pq_dequantize(int d, int bits, const uint8_t* codes, const uint16_t* norms, 
                   const uint8_t* signs, int out_dtype, void* out, void* stream);
 
 /*
+ * pq_quantize / pq_dequantize with the codes bit-packed (eliza quantization
+ * README, TurboQuant, "Algorithm in one paragraph", step 4: indices packed into
+ * bytes, two per byte at 4 bits and four per byte at 2 bits).  Arguments,
+ * outputs other than the codes, and errors as in pq_quantize / pq_dequantize,
+ * except:
+ *   bits       1, 2, 4 or 8 (a whole number of codes per byte; 8 is the
+ *              unpacked layout); 3, 5, 6, 7 -> PQ_EUNSUPPORTED
+ *   codes      n_blocks * d*bits/8 bytes (16-byte aligned); block b at
+ *              codes + b*d*bits/8 is a little-endian bit stream: bit j of code i
+ *              is stream bit bits*i + j, stream bit p is bit p%8 of byte p/8
+ *              (at 4 bits code 2k is the low nibble of byte k)
+ */
+int pq_quantize_packed(int d, int bits, int in_dtype, const void* x, int64_t n_blocks,
+                       const uint8_t* signs, int m, const uint16_t* proj,
+                       uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits, uint16_t* rnorms,
+                       void* stream);
+int pq_dequantize_packed(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                         const uint8_t* signs, int out_dtype, void* out, void* stream);
+
+/*
  * QJL key sketch (eliza quantization README, QJL, "Algorithm in one paragraph").
  *   keys       n_keys*d bf16, key t at keys + t*d
  *   proj       G, m x d bf16

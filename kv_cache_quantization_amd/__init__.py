@@ -1,7 +1,7 @@
 """MI355X (gfx950) rotate-then-quantize block codec and QJL sketch.
 
 Python binding of the C ABI in ``include/pq.h`` (library ``libpqhip.so`` built
-in this directory by ``python -m kv_cache_quantization_amd.build``).  The
+in this directory by ``python kv_cache_quantization_amd/build.py``).  The
 binding only marshals arguments: every step of the path runs in the library's
 HIP kernels.  torch supplies device memory and the current HIP stream.
 
@@ -33,7 +33,7 @@ class PQError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("kv_cache_quantization_amd: %s is not built "
-                          "(run python -m kv_cache_quantization_amd.build)" % LIB_PATH)
+                          "(run python kv_cache_quantization_amd/build.py)" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
     sig = {
@@ -43,6 +43,8 @@ def _load():
         "pq_codebook": ([I, D, D, D], I),
         "pq_quantize": ([I, I, I, P, L, P, I, P, P, P, P, P, P], I),
         "pq_dequantize": ([I, I, P, P, L, P, I, P, P], I),
+        "pq_quantize_packed": ([I, I, I, P, L, P, I, P, P, P, P, P, P], I),
+        "pq_dequantize_packed": ([I, I, P, P, L, P, I, P, P], I),
         "qjl_sketch": ([I, I, P, L, P, P, P, P], I),
         "qjl_project": ([I, I, P, L, P, P, P], I),
         "qjl_score": ([I, I, I, I, L, P, P, P, P, P], I),
@@ -59,8 +61,8 @@ def _load():
 
 _lib = _load()
 EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_quantize",
-           "pq_dequantize", "qjl_sketch", "qjl_project", "qjl_score", "pq_query_prep_bytes",
-           "pq_query_prep", "pq_score")
+           "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
+           "qjl_score", "pq_query_prep_bytes", "pq_query_prep", "pq_score")
 
 
 def lib():
@@ -101,12 +103,13 @@ def codebook(bits):
     return list(c), list(b)[:L - 1], mse.value
 
 
-def quantize(x, d, bits, signs, proj=None, out=None):
+def quantize(x, d, bits, signs, proj=None, out=None, packed=False):
     """Quantize the contiguous d-element blocks of ``x`` (fp32 or bf16).
 
     Returns (codes uint8 [n, d], norms fp16 [n], qjl_bits uint8 [n, m/8] or None,
     rnorms fp16 [n] or None).  ``proj`` (bf16 [m, d]) turns on the QJL residual stage.
-    ``out`` may hold preallocated (codes, norms, qjl_bits, rnorms).
+    ``out`` may hold preallocated (codes, norms, qjl_bits, rnorms).  ``packed`` calls
+    pq_quantize_packed: codes are then uint8 [n, d * bits / 8] (bits 1, 2, 4 or 8).
     """
     _dev(x, "x", (torch.float32, torch.bfloat16))
     _dev(signs, "signs", (torch.uint8,))
@@ -118,30 +121,34 @@ def quantize(x, d, bits, signs, proj=None, out=None):
         _dev(proj, "proj", (torch.bfloat16,))
         m = proj.shape[0]
     if out is None:
-        codes = torch.empty((n, d), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((n, d * bits // 8 if packed else d), dtype=torch.uint8, device=x.device)
         norms = torch.empty((n,), dtype=torch.float16, device=x.device)
         qb = torch.empty((n, m // 8), dtype=torch.uint8, device=x.device) if m else None
         rn = torch.empty((n,), dtype=torch.float16, device=x.device) if m else None
     else:
         codes, norms, qb, rn = out
     dt = PQ_BF16 if x.dtype == torch.bfloat16 else PQ_F32
-    _check(_lib.pq_quantize(d, bits, dt, _ptr(x), n, _ptr(signs), m, _ptr(proj), _ptr(codes), _ptr(norms),
-                            _ptr(qb), _ptr(rn), _stream()), "pq_quantize")
+    fn, name = (_lib.pq_quantize_packed, "pq_quantize_packed") if packed else (_lib.pq_quantize, "pq_quantize")
+    _check(fn(d, bits, dt, _ptr(x), n, _ptr(signs), m, _ptr(proj), _ptr(codes), _ptr(norms),
+              _ptr(qb), _ptr(rn), _stream()), name)
     return codes, norms, qb, rn
 
 
-def dequantize(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None):
-    """Reconstruct blocks from codes (uint8 [n, d]) and fp16 norms; returns [n, d]."""
+def dequantize(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None, packed=False):
+    """Reconstruct blocks from codes (uint8 [n, d], or [n, d * bits / 8] with ``packed``,
+    which calls pq_dequantize_packed) and fp16 norms; returns [n, d]."""
     _dev(codes, "codes", (torch.uint8,))
     _dev(norms, "norms", (torch.float16,))
     _dev(signs, "signs", (torch.uint8,))
-    n = codes.numel() // d
+    n = norms.numel()
+    if codes.numel() != n * (d * bits // 8 if packed else d):
+        raise ValueError("codes do not match norms")
     if out is None:
         out = torch.empty((n, d), dtype=out_dtype, device=codes.device)
     _dev(out, "out", (torch.float32, torch.bfloat16))
     dt = PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32
-    _check(_lib.pq_dequantize(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs), dt, _ptr(out), _stream()),
-           "pq_dequantize")
+    fn, name = (_lib.pq_dequantize_packed, "pq_dequantize_packed") if packed else (_lib.pq_dequantize, "pq_dequantize")
+    _check(fn(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs), dt, _ptr(out), _stream()), name)
     return out
 
 

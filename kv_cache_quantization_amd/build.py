@@ -1,7 +1,8 @@
 """Build the HIP library in-tree: kv_cache_quantization_amd/libpqhip.so for gfx950.
 
-Run as ``python -m kv_cache_quantization_amd.build`` (or through
-``__graft_entry__.build()``).  hipcc cross-compiles for gfx950 without a GPU.
+Run as ``python kv_cache_quantization_amd/build.py`` (or through
+``__graft_entry__.build()``); importing the package first would load the library
+being rebuilt.  hipcc cross-compiles for gfx950 without a GPU.
 """
 
 import os

@@ -166,6 +166,55 @@ constexpr int64_t kMaxElems = INT64_MAX / 8;
 
 }  // namespace
 
+namespace {
+
+// codes per byte of the packed layout: 8 / bits for bits dividing 8, else 0 (unsupported)
+int packed_cpb(int bits) { return (bits == 1 || bits == 2 || bits == 4 || bits == 8) ? 8 / bits : 0; }
+
+int quantize_impl(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs, int m,
+                  const uint16_t* proj, uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits, uint16_t* rnorms,
+                  int cpb, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (in_dtype != PQ_F32 && in_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (m < 0 || (m % 8) != 0) return PQ_EINVAL;
+  if (m > 1024) return PQ_EUNSUPPORTED;
+  if (m == 0 && (proj || qjl_bits || rnorms)) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!x || !signs || !codes || !norms) return PQ_EINVAL;
+  if (m > 0 && (!proj || !qjl_bits || !rnorms)) return PQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(norms, 2)) return PQ_EINVAL;
+  if (m > 0 && (!aligned(proj, 16) || !aligned(qjl_bits, 16) || !aligned(rnorms, 2))) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::QuantArgs a;
+  a.x = x; a.n_blocks = n_blocks; a.signs = signs; a.proj = proj; a.codes = codes; a.norms = norms;
+  a.qbits = qjl_bits; a.rnorms = rnorms; a.m = m; a.cpb = cpb; a.t = make_tables(bits);
+  return hip_status(pqi::launch_quantize(d, in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+int dequantize_impl(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                    const uint8_t* signs, int out_dtype, void* out, int cpb, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (out_dtype != PQ_F32 && out_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!codes || !norms || !signs || !out) return PQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::DequantArgs a;
+  a.codes = codes; a.norms = norms; a.n_blocks = n_blocks; a.signs = signs; a.out = out; a.cpb = cpb;
+  a.t = make_tables(bits);
+  return hip_status(pqi::launch_dequantize(d, out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+}  // namespace
+
 extern "C" {
 
 int pq_abi_version(void) { return PQ_ABI_VERSION; }
@@ -191,46 +240,33 @@ int pq_codebook(int bits, double* centroids, double* boundaries, double* mse) {
   return PQ_OK;
 }
 
+
 int pq_quantize(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
                 int m, const uint16_t* proj, uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits,
                 uint16_t* rnorms, void* stream) {
-  int st = check_d(d);
-  if (st) return st;
-  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
-  if (in_dtype != PQ_F32 && in_dtype != PQ_BF16) return PQ_EINVAL;
-  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
-  if (m < 0 || (m % 8) != 0) return PQ_EINVAL;
-  if (m > 1024) return PQ_EUNSUPPORTED;
-  if (m == 0 && (proj || qjl_bits || rnorms)) return PQ_EINVAL;
-  if (n_blocks == 0) return PQ_OK;
-  if (!x || !signs || !codes || !norms) return PQ_EINVAL;
-  if (m > 0 && (!proj || !qjl_bits || !rnorms)) return PQ_EINVAL;
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(norms, 2)) return PQ_EINVAL;
-  if (m > 0 && (!aligned(proj, 16) || !aligned(qjl_bits, 16) || !aligned(rnorms, 2))) return PQ_EINVAL;
-  pqi::LaunchCfg cfg;
-  if ((st = launch_cfg(&cfg))) return st;
-  pqi::QuantArgs a;
-  a.x = x; a.n_blocks = n_blocks; a.signs = signs; a.proj = proj; a.codes = codes; a.norms = norms;
-  a.qbits = qjl_bits; a.rnorms = rnorms; a.m = m; a.t = make_tables(bits);
-  return hip_status(pqi::launch_quantize(d, in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+  return quantize_impl(d, bits, in_dtype, x, n_blocks, signs, m, proj, codes, norms, qjl_bits, rnorms, 1, stream);
 }
 
 int pq_dequantize(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
                   const uint8_t* signs, int out_dtype, void* out, void* stream) {
-  int st = check_d(d);
-  if (st) return st;
+  return dequantize_impl(d, bits, codes, norms, n_blocks, signs, out_dtype, out, 1, stream);
+}
+
+int pq_quantize_packed(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
+                       int m, const uint16_t* proj, uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits,
+                       uint16_t* rnorms, void* stream) {
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
-  if (out_dtype != PQ_F32 && out_dtype != PQ_BF16) return PQ_EINVAL;
-  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
-  if (n_blocks == 0) return PQ_OK;
-  if (!codes || !norms || !signs || !out) return PQ_EINVAL;
-  if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(norms, 2)) return PQ_EINVAL;
-  pqi::LaunchCfg cfg;
-  if ((st = launch_cfg(&cfg))) return st;
-  pqi::DequantArgs a;
-  a.codes = codes; a.norms = norms; a.n_blocks = n_blocks; a.signs = signs; a.out = out;
-  a.t = make_tables(bits);
-  return hip_status(pqi::launch_dequantize(d, out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+  const int cpb = packed_cpb(bits);
+  if (!cpb) return PQ_EUNSUPPORTED;
+  return quantize_impl(d, bits, in_dtype, x, n_blocks, signs, m, proj, codes, norms, qjl_bits, rnorms, cpb, stream);
+}
+
+int pq_dequantize_packed(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                         const uint8_t* signs, int out_dtype, void* out, void* stream) {
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  const int cpb = packed_cpb(bits);
+  if (!cpb) return PQ_EUNSUPPORTED;
+  return dequantize_impl(d, bits, codes, norms, n_blocks, signs, out_dtype, out, cpb, stream);
 }
 
 int qjl_sketch(int d, int m, const uint16_t* keys, int64_t n_keys, const uint16_t* proj, uint8_t* bits,

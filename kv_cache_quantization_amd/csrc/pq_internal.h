@@ -38,6 +38,7 @@ struct QuantArgs {
   uint8_t* qbits;
   uint16_t* rnorms;
   int m;
+  int cpb;            // codes per byte: 1 (a byte per code), or 2, 4, 8 (bit-packed, 8 / cpb bits each)
   CodecTables t;
 };
 
@@ -47,6 +48,7 @@ struct DequantArgs {
   int64_t n_blocks;
   const uint8_t* signs;
   void* out;
+  int cpb;            // codes per byte, as in QuantArgs
   CodecTables t;
 };
 

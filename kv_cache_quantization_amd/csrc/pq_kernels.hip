@@ -259,6 +259,37 @@ __device__ __forceinline__ uint32_t split_lo_f16x2(uint32_t hp, float x0, float 
   return lo;
 }
 
+// Bit packing of codes (8 / CPB bits each): four byte codes of one dword -> 32 / CPB bits,
+// code k of the dword in bits [k * 8 / CPB, (k + 1) * 8 / CPB).
+template <int CPB>
+__device__ __forceinline__ uint32_t pack_code_dword(uint32_t w) {
+  uint32_t t;
+  if constexpr (CPB == 2) {
+    t = w & 0x0F0F0F0Fu; t = (t | (t >> 4)) & 0x00FF00FFu; t = (t | (t >> 8)) & 0xFFFFu;
+  } else if constexpr (CPB == 4) {
+    t = w & 0x03030303u; t = (t | (t >> 6)) & 0x000F000Fu; t = (t | (t >> 12)) & 0xFFu;
+  } else {
+    t = w & 0x01010101u; t = (t | (t >> 7)) & 0x00030003u; t = (t | (t >> 14)) & 0xFu;
+  }
+  return t;
+}
+
+// NB bytes of packed codes from / to 4-byte aligned memory (NB = 2, 4, 8 or a multiple of 16).
+template <int NB>
+__device__ __forceinline__ void store_code_bytes(uint8_t* dst, const uint32_t (&w)[NB >= 4 ? NB / 4 : 1]) {
+  if constexpr (NB >= 16) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i)
+      reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else if constexpr (NB == 8) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else if constexpr (NB == 4) {
+    *reinterpret_cast<uint32_t*>(dst) = w[0];
+  } else {
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+  }
+}
+
 template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP>
 struct Quantizer {
   static constexpr int E = D / 4;
@@ -404,7 +435,15 @@ struct Quantizer {
     // the store branch below and keeps every lookup result live until then
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) asm volatile("" : "+v"(cw[w]));
-    if constexpr (D == 128) {
+    if (a.cpb > 1) {
+      // bit-packed codes: the lane's run of E codes is E / cpb contiguous bytes
+      switch (a.cpb) {
+        case 2: store_packed<2>(cw, blk, valid); break;
+        case 4: store_packed<4>(cw, blk, valid); break;
+        default: store_packed<8>(cw, blk, valid); break;
+      }
+      if (valid && g == 0) a.norms[blk] = n16;
+    } else if constexpr (D == 128) {
       // a block's codes are one 128-byte line, two 16-byte pieces per lane: the neighbouring
       // blocks r & ~1 and r | 1 (lanes l, l ^ 1) trade pieces so that each store writes
       // whole lines (half-line stores reach HBM as partial lines)
@@ -434,6 +473,19 @@ struct Quantizer {
       const float rn = sqrtf(rss) / rscale * inv_sqrt_d;    // ||r|| = ||H D r|| / sqrt(d)
       if (valid && g == 0) a.rnorms[blk] = f32_to_f16(rn);
     }
+  }
+
+  // The lane's E byte codes (cw, run order) packed CPB to a byte and stored at their place
+  // in the block's bit stream: the run starts E qpos(g) codes into the block.
+  template <int CPB>
+  __device__ __forceinline__ void store_packed(const uint32_t (&cw)[E / 4], int64_t blk, bool valid) {
+    constexpr int NB = E / CPB;                           // packed bytes of the run
+    uint32_t pw[NB >= 4 ? NB / 4 : 1];
+#pragma unroll
+    for (int i = 0; i < (NB >= 4 ? NB / 4 : 1); ++i) pw[i] = 0;
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) pw[j / CPB] |= pack_code_dword<CPB>(cw[j]) << ((j % CPB) * (32 / CPB));
+    if (valid) store_code_bytes<NB>(a.codes + blk * (D / CPB) + E * qpos<D>(g) / CPB, pw);
   }
 
   // The rotated residual back in the block's coordinates, w = H rho = d D r (times the
@@ -681,10 +733,12 @@ void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
 // Dequantize.  Outputs are written with non-temporal stores: they stream to HBM without
 // displacing the codes and tables in the caches.
 // ------------------------------------------------------------------------------------------
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, int CPB>
 __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
   constexpr int E = D / 4;
-  constexpr int NR = E / 16;                          // 16-byte code loads per lane per tile
+  constexpr int NB = E / CPB;                         // code bytes of the lane's run (CPB per byte)
+  constexpr int NQ = NB >= 4 ? NB / 4 : 1;            // ... as dwords
+  constexpr int CB = 8 / CPB;                         // bits per code
   __shared__ float cent[1 << pqi::kMaxBits];
   copy_centroids(a.t, cent);
   __syncthreads();
@@ -706,34 +760,42 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
   const int64_t n_tiles = (n_blocks + 15) >> 4;
   const int64_t n_waves = (int64_t)gridDim.x * kWaves;
 
-  auto load = [&](uint4 (&q)[NR], uint16_t& nb, int64_t T) {
+  // the lane's run: codes E g .. E g + E - 1 of the block, CPB to a byte (a bit stream for
+  // CPB > 1, code k of a dword in bits CB k ..)
+  auto load = [&](uint32_t (&q)[NQ], uint16_t& nb, int64_t T) {
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
-    const uint4* src = reinterpret_cast<const uint4*>(a.codes + blk * D + E * g);
+    const uint8_t* src = a.codes + blk * (D / CPB) + E * g / CPB;
+    if constexpr (NB >= 16) {
 #pragma unroll
-    for (int w = 0; w < NR; ++w) q[w] = valid ? src[w] : make_uint4(0, 0, 0, 0);
+      for (int w = 0; w < NB / 16; ++w) {
+        const uint4 x = valid ? reinterpret_cast<const uint4*>(src)[w] : make_uint4(0, 0, 0, 0);
+        q[4 * w] = x.x; q[4 * w + 1] = x.y; q[4 * w + 2] = x.z; q[4 * w + 3] = x.w;
+      }
+    } else if constexpr (NB == 8) {
+      const uint2 x = valid ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+      q[0] = x.x; q[1] = x.y;
+    } else if constexpr (NB == 4) {
+      q[0] = valid ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+    } else {
+      q[0] = valid ? *reinterpret_cast<const uint16_t*>(src) : 0u;
+    }
     nb = valid ? a.norms[blk] : (uint16_t)0;
   };
 
   int64_t T = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  uint4 q[NR];
+  uint32_t q[NQ];
   uint16_t nb;
   load(q, nb, T);
 
   for (; T < n_tiles; T += n_waves) {
-    uint4 qn[NR];
+    uint32_t qn[NQ];
     uint16_t nbn;
     load(qn, nbn, T + n_waves);
 
     float v[E];
 #pragma unroll
-    for (int w = 0; w < NR; ++w) {
-      const uint32_t qq[4] = {q[w].x, q[w].y, q[w].z, q[w].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v[16 * w + 4 * u + b] = cent[(qq[u] >> (8 * b)) & 0xffu];
-    }
+    for (int j = 0; j < E; ++j) v[j] = cent[(q[j / (4 * CPB)] >> (CB * (j % (4 * CPB)))) & ((1u << CB) - 1u)];
     const float scale = f16_to_f32(nb) * (1.0f / (float)D);
 
     wht_dequant<D>(v);
@@ -786,7 +848,7 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
       }
     }
 #pragma unroll
-    for (int w = 0; w < NR; ++w) q[w] = qn[w];
+    for (int w = 0; w < NQ; ++w) q[w] = qn[w];
     nb = nbn;
   }
 }
@@ -1442,8 +1504,17 @@ template <int D>
 hipError_t launch_dequantize_d(bool out_bf16, const pqi::DequantArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
   const int grid = grid_for(n_tiles, c, PQ_DEQUANT_WG_PER_CU);
-  if (out_bf16) hipLaunchKernelGGL((pq_dequantize_kernel<D, true>), grid, kThreads, 0, s, a);
-  else hipLaunchKernelGGL((pq_dequantize_kernel<D, false>), grid, kThreads, 0, s, a);
+#define PQ_DQ_LAUNCH(CPB)                                                                         \
+  if (out_bf16) hipLaunchKernelGGL((pq_dequantize_kernel<D, true, CPB>), grid, kThreads, 0, s, a); \
+  else hipLaunchKernelGGL((pq_dequantize_kernel<D, false, CPB>), grid, kThreads, 0, s, a);
+  switch (a.cpb) {
+    case 1: PQ_DQ_LAUNCH(1) break;
+    case 2: PQ_DQ_LAUNCH(2) break;
+    case 4: PQ_DQ_LAUNCH(4) break;
+    case 8: PQ_DQ_LAUNCH(8) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef PQ_DQ_LAUNCH
   return hipGetLastError();
 }
 
