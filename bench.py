@@ -294,21 +294,23 @@ def tsq_leg(pq, synth, torch, steps, warmup):
     return out
 
 
-def grouped_leg(pq, synth, torch, reps):
+def grouped_leg(pq, synth, torch, reps, packed=False):
     """Config 3: one streamed quantize pass and one dequantize pass over the 224 tensors of
     a 32-layer 7B-style decoder (4-bit codes, d=128), each tensor one launch with its own
     rotation signs.  Kernel time depends only on the shapes, so the seven tensors of layer
-    0 (seeded as in the parity tests) stand in for every layer; returns the pass times."""
+    0 (seeded as in the parity tests) stand in for every layer; returns the pass times.
+    ``packed``: the codes bit-packed two to a byte (pq_quantize_packed / pq_dequantize_packed)."""
     dev = torch.device("cuda:0")
     layout = synth.config3_layout()
     d, bits = 128, 4
+    cb = d * bits // 8 if packed else d                   # code bytes per block
     ins, outs = [], []
     for t, _, _, rows, cols in layout[:7]:
         xu, _ = synth.config3_tensor(t, rows, cols)
         x = torch.from_numpy(xu.view(np.int16)).view(torch.bfloat16).to(dev)
         n = x.numel() // d
         ins.append(x)
-        outs.append((torch.empty((n, d), dtype=torch.uint8, device=dev), torch.empty((n,), dtype=torch.float16, device=dev),
+        outs.append((torch.empty((n, cb), dtype=torch.uint8, device=dev), torch.empty((n,), dtype=torch.float16, device=dev),
                      torch.empty((n, d), dtype=torch.bfloat16, device=dev)))
     signs = [torch.from_numpy(synth.sign_mask(synth.BASE_SEED + t, d)).to(dev) for t, _, _, _, _ in layout]
     total = sum(r * c for _, _, _, r, c in layout)
@@ -316,23 +318,26 @@ def grouped_leg(pq, synth, torch, reps):
     def qpass(k):
         for t in range(len(layout)):
             i = t % 7
-            pq.quantize(ins[i], d, bits, signs[t], out=(outs[i][0], outs[i][1], None, None))
+            pq.quantize(ins[i], d, bits, signs[t], out=(outs[i][0], outs[i][1], None, None), packed=packed)
 
     def dpass(k):
         for t in range(len(layout)):
             i = t % 7
-            pq.dequantize(outs[i][0], outs[i][1], d, bits, signs[t], out=outs[i][2])
+            pq.dequantize(outs[i][0], outs[i][1], d, bits, signs[t], out=outs[i][2], packed=packed)
 
     qpass(0), dpass(0)
     tq, td = timed(torch, qpass, reps), timed(torch, dpass, reps)
     nb = total // d
-    q_bytes = total * 2 + total + nb * 2
-    d_bytes = total + nb * 2 + total * 2
-    return {"grouped_config": "config3: 224 bf16 tensors (32 layers x q,k,v,o,gate,up,down), 6,979,321,856 "
-                              "values, d=128, 4-bit, one launch per tensor",
-            "grouped_quantize_ms": round(tq * 1e3, 3), "grouped_quantize_hbm_frac": round(q_bytes / tq / 1e9 / HBM_PEAK_GBS, 4),
-            "grouped_dequantize_ms": round(td * 1e3, 3), "grouped_dequantize_hbm_frac": round(d_bytes / td / 1e9 / HBM_PEAK_GBS, 4),
-            "grouped_input_gb_per_s": round(total * 2 / (tq + td) / 1e9, 1)}
+    code_bytes = nb * cb
+    q_bytes = total * 2 + code_bytes + nb * 2
+    d_bytes = code_bytes + nb * 2 + total * 2
+    key = "grouped_packed" if packed else "grouped"
+    return {key + "_config": "config3: 224 bf16 tensors (32 layers x q,k,v,o,gate,up,down), 6,979,321,856 "
+                             "values, d=128, 4-bit%s, one launch per tensor" % (
+                                 ", codes packed two per byte" if packed else ""),
+            key + "_quantize_ms": round(tq * 1e3, 3), key + "_quantize_hbm_frac": round(q_bytes / tq / 1e9 / HBM_PEAK_GBS, 4),
+            key + "_dequantize_ms": round(td * 1e3, 3), key + "_dequantize_hbm_frac": round(d_bytes / td / 1e9 / HBM_PEAK_GBS, 4),
+            key + "_input_gb_per_s": round(total * 2 / (tq + td) / 1e9, 1)}
 
 
 def main():
@@ -440,6 +445,7 @@ def main():
         rec["parts"].update(tsq_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_grouped:
         rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50)))
+        rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50), packed=True))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_blocks)
     print(json.dumps(rec), flush=True)
