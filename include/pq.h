@@ -134,15 +134,14 @@ int pq_dequantize(int d, int bits, const uint8_t* codes, const uint16_t* norms, 
 /*
  * pq_quantize / pq_dequantize with the codes bit-packed (eliza quantization
  * README, TurboQuant, "Algorithm in one paragraph", step 4: indices packed into
- * bytes, two per byte at 4 bits and four per byte at 2 bits).  Arguments,
- * outputs other than the codes, and errors as in pq_quantize / pq_dequantize,
- * except:
- *   bits       1, 2, 4 or 8 (a whole number of codes per byte; 8 is the
- *              unpacked layout); 3, 5, 6, 7 -> PQ_EUNSUPPORTED
+ * bytes, two per byte at 4 bits and four per byte at 2 bits; the same stream
+ * carries any width).  Arguments, outputs other than the codes, and errors as in
+ * pq_quantize / pq_dequantize, except:
  *   codes      n_blocks * d*bits/8 bytes (16-byte aligned); block b at
  *              codes + b*d*bits/8 is a little-endian bit stream: bit j of code i
  *              is stream bit bits*i + j, stream bit p is bit p%8 of byte p/8
- *              (at 4 bits code 2k is the low nibble of byte k)
+ *              (at 4 bits code 2k is the low nibble of byte k; at 8 bits the
+ *              layout of pq_quantize)
  */
 int pq_quantize_packed(int d, int bits, int in_dtype, const void* x, int64_t n_blocks,
                        const uint8_t* signs, int m, const uint16_t* proj,

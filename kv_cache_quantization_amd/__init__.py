@@ -109,7 +109,7 @@ def quantize(x, d, bits, signs, proj=None, out=None, packed=False):
     Returns (codes uint8 [n, d], norms fp16 [n], qjl_bits uint8 [n, m/8] or None,
     rnorms fp16 [n] or None).  ``proj`` (bf16 [m, d]) turns on the QJL residual stage.
     ``out`` may hold preallocated (codes, norms, qjl_bits, rnorms).  ``packed`` calls
-    pq_quantize_packed: codes are then uint8 [n, d * bits / 8] (bits 1, 2, 4 or 8).
+    pq_quantize_packed: codes are then uint8 [n, d * bits / 8], a bit stream per block.
     """
     _dev(x, "x", (torch.float32, torch.bfloat16))
     _dev(signs, "signs", (torch.uint8,))

@@ -168,12 +168,9 @@ constexpr int64_t kMaxElems = INT64_MAX / 8;
 
 namespace {
 
-// codes per byte of the packed layout: 8 / bits for bits dividing 8, else 0 (unsupported)
-int packed_cpb(int bits) { return (bits == 1 || bits == 2 || bits == 4 || bits == 8) ? 8 / bits : 0; }
-
 int quantize_impl(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs, int m,
                   const uint16_t* proj, uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits, uint16_t* rnorms,
-                  int cpb, void* stream) {
+                  int pbits, void* stream) {
   int st = check_d(d);
   if (st) return st;
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
@@ -191,12 +188,12 @@ int quantize_impl(int d, int bits, int in_dtype, const void* x, int64_t n_blocks
   if ((st = launch_cfg(&cfg))) return st;
   pqi::QuantArgs a;
   a.x = x; a.n_blocks = n_blocks; a.signs = signs; a.proj = proj; a.codes = codes; a.norms = norms;
-  a.qbits = qjl_bits; a.rnorms = rnorms; a.m = m; a.cpb = cpb; a.t = make_tables(bits);
+  a.qbits = qjl_bits; a.rnorms = rnorms; a.m = m; a.pbits = pbits; a.t = make_tables(bits);
   return hip_status(pqi::launch_quantize(d, in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
 }
 
 int dequantize_impl(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
-                    const uint8_t* signs, int out_dtype, void* out, int cpb, void* stream) {
+                    const uint8_t* signs, int out_dtype, void* out, int pbits, void* stream) {
   int st = check_d(d);
   if (st) return st;
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
@@ -208,7 +205,7 @@ int dequantize_impl(int d, int bits, const uint8_t* codes, const uint16_t* norms
   pqi::LaunchCfg cfg;
   if ((st = launch_cfg(&cfg))) return st;
   pqi::DequantArgs a;
-  a.codes = codes; a.norms = norms; a.n_blocks = n_blocks; a.signs = signs; a.out = out; a.cpb = cpb;
+  a.codes = codes; a.norms = norms; a.n_blocks = n_blocks; a.signs = signs; a.out = out; a.pbits = pbits;
   a.t = make_tables(bits);
   return hip_status(pqi::launch_dequantize(d, out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
 }
@@ -244,29 +241,27 @@ int pq_codebook(int bits, double* centroids, double* boundaries, double* mse) {
 int pq_quantize(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
                 int m, const uint16_t* proj, uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits,
                 uint16_t* rnorms, void* stream) {
-  return quantize_impl(d, bits, in_dtype, x, n_blocks, signs, m, proj, codes, norms, qjl_bits, rnorms, 1, stream);
+  return quantize_impl(d, bits, in_dtype, x, n_blocks, signs, m, proj, codes, norms, qjl_bits, rnorms, 0, stream);
 }
 
 int pq_dequantize(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
                   const uint8_t* signs, int out_dtype, void* out, void* stream) {
-  return dequantize_impl(d, bits, codes, norms, n_blocks, signs, out_dtype, out, 1, stream);
+  return dequantize_impl(d, bits, codes, norms, n_blocks, signs, out_dtype, out, 0, stream);
 }
 
 int pq_quantize_packed(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
                        int m, const uint16_t* proj, uint8_t* codes, uint16_t* norms, uint8_t* qjl_bits,
                        uint16_t* rnorms, void* stream) {
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
-  const int cpb = packed_cpb(bits);
-  if (!cpb) return PQ_EUNSUPPORTED;
-  return quantize_impl(d, bits, in_dtype, x, n_blocks, signs, m, proj, codes, norms, qjl_bits, rnorms, cpb, stream);
+  // at 8 bits the stream is one byte per code
+  return quantize_impl(d, bits, in_dtype, x, n_blocks, signs, m, proj, codes, norms, qjl_bits, rnorms,
+                       bits == 8 ? 0 : bits, stream);
 }
 
 int pq_dequantize_packed(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
                          const uint8_t* signs, int out_dtype, void* out, void* stream) {
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
-  const int cpb = packed_cpb(bits);
-  if (!cpb) return PQ_EUNSUPPORTED;
-  return dequantize_impl(d, bits, codes, norms, n_blocks, signs, out_dtype, out, cpb, stream);
+  return dequantize_impl(d, bits, codes, norms, n_blocks, signs, out_dtype, out, bits == 8 ? 0 : bits, stream);
 }
 
 int qjl_sketch(int d, int m, const uint16_t* keys, int64_t n_keys, const uint16_t* proj, uint8_t* bits,

@@ -38,7 +38,7 @@ struct QuantArgs {
   uint8_t* qbits;
   uint16_t* rnorms;
   int m;
-  int cpb;            // codes per byte: 1 (a byte per code), or 2, 4, 8 (bit-packed, 8 / cpb bits each)
+  int pbits;          // 0: a byte per code; 1..7: codes bit-packed at pbits bits each
   CodecTables t;
 };
 
@@ -48,7 +48,7 @@ struct DequantArgs {
   int64_t n_blocks;
   const uint8_t* signs;
   void* out;
-  int cpb;            // codes per byte, as in QuantArgs
+  int pbits;          // as in QuantArgs
   CodecTables t;
 };
 

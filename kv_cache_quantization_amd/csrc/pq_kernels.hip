@@ -259,35 +259,58 @@ __device__ __forceinline__ uint32_t split_lo_f16x2(uint32_t hp, float x0, float 
   return lo;
 }
 
-// Bit packing of codes (8 / CPB bits each): four byte codes of one dword -> 32 / CPB bits,
-// code k of the dword in bits [k * 8 / CPB, (k + 1) * 8 / CPB).
-template <int CPB>
-__device__ __forceinline__ uint32_t pack_code_dword(uint32_t w) {
-  uint32_t t;
-  if constexpr (CPB == 2) {
-    t = w & 0x0F0F0F0Fu; t = (t | (t >> 4)) & 0x00FF00FFu; t = (t | (t >> 8)) & 0xFFFFu;
-  } else if constexpr (CPB == 4) {
-    t = w & 0x03030303u; t = (t | (t >> 6)) & 0x000F000Fu; t = (t | (t >> 12)) & 0xFFu;
-  } else {
-    t = w & 0x01010101u; t = (t | (t >> 7)) & 0x00030003u; t = (t | (t >> 14)) & 0xFu;
-  }
-  return t;
-}
-
-// NB bytes of packed codes from / to 4-byte aligned memory (NB = 2, 4, 8 or a multiple of 16).
+// Bit-packed code runs: a lane's run of codes is a little-endian bit stream of B bits per
+// code.  NB bytes of it move as the widest accesses the run's alignment allows (a run starts
+// at a multiple of NB bytes).
 template <int NB>
-__device__ __forceinline__ void store_code_bytes(uint8_t* dst, const uint32_t (&w)[NB >= 4 ? NB / 4 : 1]) {
-  if constexpr (NB >= 16) {
+__device__ __forceinline__ void store_code_bytes(uint8_t* dst, const uint32_t (&w)[(NB + 3) / 4]) {
+  if constexpr (NB % 16 == 0) {
 #pragma unroll
     for (int i = 0; i < NB / 16; ++i)
       reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-  } else if constexpr (NB == 8) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-  } else if constexpr (NB == 4) {
-    *reinterpret_cast<uint32_t*>(dst) = w[0];
+  } else if constexpr (NB % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 8; ++i) reinterpret_cast<uint2*>(dst)[i] = make_uint2(w[2 * i], w[2 * i + 1]);
+  } else if constexpr (NB % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 4; ++i) reinterpret_cast<uint32_t*>(dst)[i] = w[i];
   } else {
-    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+#pragma unroll
+    for (int i = 0; i < NB / 2; ++i) reinterpret_cast<uint16_t*>(dst)[i] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
   }
+}
+template <int NB>
+__device__ __forceinline__ void load_code_bytes(const uint8_t* src, bool valid, uint32_t (&w)[(NB + 3) / 4]) {
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) {
+      const uint4 x = valid ? reinterpret_cast<const uint4*>(src)[i] : make_uint4(0, 0, 0, 0);
+      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+    }
+  } else if constexpr (NB % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 8; ++i) {
+      const uint2 x = valid ? reinterpret_cast<const uint2*>(src)[i] : make_uint2(0, 0);
+      w[2 * i] = x.x; w[2 * i + 1] = x.y;
+    }
+  } else if constexpr (NB % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 4; ++i) w[i] = valid ? reinterpret_cast<const uint32_t*>(src)[i] : 0u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < (NB + 3) / 4; ++i) w[i] = 0;
+#pragma unroll
+    for (int i = 0; i < NB / 2; ++i)
+      w[i >> 1] |= (uint32_t)(valid ? reinterpret_cast<const uint16_t*>(src)[i] : 0) << (16 * (i & 1));
+  }
+}
+// Code j of a B-bit stream held in dwords (B <= 8; a code may straddle two dwords).
+template <int B, int N>
+__device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[N], int j) {
+  const int pos = B * j, k = pos >> 5, sh = pos & 31;
+  uint32_t c = w[k] >> sh;
+  if (sh + B > 32) c |= w[k + 1] << (32 - sh);
+  return c & ((1u << B) - 1u);
 }
 
 template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP>
@@ -435,12 +458,16 @@ struct Quantizer {
     // the store branch below and keeps every lookup result live until then
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) asm volatile("" : "+v"(cw[w]));
-    if (a.cpb > 1) {
-      // bit-packed codes: the lane's run of E codes is E / cpb contiguous bytes
-      switch (a.cpb) {
+    if (a.pbits) {
+      // bit-packed codes: the lane's run of E codes is E pbits / 8 contiguous bytes
+      switch (a.pbits) {
+        case 1: store_packed<1>(cw, blk, valid); break;
         case 2: store_packed<2>(cw, blk, valid); break;
+        case 3: store_packed<3>(cw, blk, valid); break;
         case 4: store_packed<4>(cw, blk, valid); break;
-        default: store_packed<8>(cw, blk, valid); break;
+        case 5: store_packed<5>(cw, blk, valid); break;
+        case 6: store_packed<6>(cw, blk, valid); break;
+        default: store_packed<7>(cw, blk, valid); break;
       }
       if (valid && g == 0) a.norms[blk] = n16;
     } else if constexpr (D == 128) {
@@ -475,17 +502,22 @@ struct Quantizer {
     }
   }
 
-  // The lane's E byte codes (cw, run order) packed CPB to a byte and stored at their place
+  // The lane's E byte codes (cw, run order) packed at B bits each and stored at their place
   // in the block's bit stream: the run starts E qpos(g) codes into the block.
-  template <int CPB>
+  template <int B>
   __device__ __forceinline__ void store_packed(const uint32_t (&cw)[E / 4], int64_t blk, bool valid) {
-    constexpr int NB = E / CPB;                           // packed bytes of the run
-    uint32_t pw[NB >= 4 ? NB / 4 : 1];
+    constexpr int NB = E * B / 8;                         // packed bytes of the run
+    uint32_t pw[(NB + 3) / 4];
 #pragma unroll
-    for (int i = 0; i < (NB >= 4 ? NB / 4 : 1); ++i) pw[i] = 0;
+    for (int i = 0; i < (NB + 3) / 4; ++i) pw[i] = 0;
 #pragma unroll
-    for (int j = 0; j < E / 4; ++j) pw[j / CPB] |= pack_code_dword<CPB>(cw[j]) << ((j % CPB) * (32 / CPB));
-    if (valid) store_code_bytes<NB>(a.codes + blk * (D / CPB) + E * qpos<D>(g) / CPB, pw);
+    for (int i = 0; i < E; ++i) {
+      const uint32_t c = (cw[i >> 2] >> (8 * (i & 3))) & 0xffu;
+      const int pos = B * i, k = pos >> 5, sh = pos & 31;
+      pw[k] |= c << sh;
+      if (sh + B > 32) pw[k + 1] |= c >> (32 - sh);
+    }
+    if (valid) store_code_bytes<NB>(a.codes + blk * (D * B / 8) + E * qpos<D>(g) * B / 8, pw);
   }
 
   // The rotated residual back in the block's coordinates, w = H rho = d D r (times the
@@ -733,12 +765,12 @@ void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
 // Dequantize.  Outputs are written with non-temporal stores: they stream to HBM without
 // displacing the codes and tables in the caches.
 // ------------------------------------------------------------------------------------------
-template <int D, bool OUT_BF16, int CPB>
+template <int D, bool OUT_BF16, int PB>
 __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
   constexpr int E = D / 4;
-  constexpr int NB = E / CPB;                         // code bytes of the lane's run (CPB per byte)
-  constexpr int NQ = NB >= 4 ? NB / 4 : 1;            // ... as dwords
-  constexpr int CB = 8 / CPB;                         // bits per code
+  constexpr int CB = PB ? PB : 8;                     // bits per stored code (PB = 0: a byte each)
+  constexpr int NB = E * CB / 8;                      // code bytes of the lane's run
+  constexpr int NQ = (NB + 3) / 4;                    // ... as dwords
   __shared__ float cent[1 << pqi::kMaxBits];
   copy_centroids(a.t, cent);
   __syncthreads();
@@ -760,26 +792,11 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
   const int64_t n_tiles = (n_blocks + 15) >> 4;
   const int64_t n_waves = (int64_t)gridDim.x * kWaves;
 
-  // the lane's run: codes E g .. E g + E - 1 of the block, CPB to a byte (a bit stream for
-  // CPB > 1, code k of a dword in bits CB k ..)
+  // the lane's run: codes E g .. E g + E - 1 of the block (a CB-bit stream)
   auto load = [&](uint32_t (&q)[NQ], uint16_t& nb, int64_t T) {
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
-    const uint8_t* src = a.codes + blk * (D / CPB) + E * g / CPB;
-    if constexpr (NB >= 16) {
-#pragma unroll
-      for (int w = 0; w < NB / 16; ++w) {
-        const uint4 x = valid ? reinterpret_cast<const uint4*>(src)[w] : make_uint4(0, 0, 0, 0);
-        q[4 * w] = x.x; q[4 * w + 1] = x.y; q[4 * w + 2] = x.z; q[4 * w + 3] = x.w;
-      }
-    } else if constexpr (NB == 8) {
-      const uint2 x = valid ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
-      q[0] = x.x; q[1] = x.y;
-    } else if constexpr (NB == 4) {
-      q[0] = valid ? *reinterpret_cast<const uint32_t*>(src) : 0u;
-    } else {
-      q[0] = valid ? *reinterpret_cast<const uint16_t*>(src) : 0u;
-    }
+    load_code_bytes<NB>(a.codes + blk * (D * CB / 8) + E * g * CB / 8, valid, q);
     nb = valid ? a.norms[blk] : (uint16_t)0;
   };
 
@@ -795,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 
     float v[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) v[j] = cent[(q[j / (4 * CPB)] >> (CB * (j % (4 * CPB)))) & ((1u << CB) - 1u)];
+    for (int j = 0; j < E; ++j) v[j] = cent[stream_code<CB>(q, j)];
     const float scale = f16_to_f32(nb) * (1.0f / (float)D);
 
     wht_dequant<D>(v);
@@ -1504,14 +1521,18 @@ template <int D>
 hipError_t launch_dequantize_d(bool out_bf16, const pqi::DequantArgs& a, const pqi::LaunchCfg& c, hipStream_t s) {
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
   const int grid = grid_for(n_tiles, c, PQ_DEQUANT_WG_PER_CU);
-#define PQ_DQ_LAUNCH(CPB)                                                                         \
-  if (out_bf16) hipLaunchKernelGGL((pq_dequantize_kernel<D, true, CPB>), grid, kThreads, 0, s, a); \
-  else hipLaunchKernelGGL((pq_dequantize_kernel<D, false, CPB>), grid, kThreads, 0, s, a);
-  switch (a.cpb) {
+#define PQ_DQ_LAUNCH(PB)                                                                         \
+  if (out_bf16) hipLaunchKernelGGL((pq_dequantize_kernel<D, true, PB>), grid, kThreads, 0, s, a); \
+  else hipLaunchKernelGGL((pq_dequantize_kernel<D, false, PB>), grid, kThreads, 0, s, a);
+  switch (a.pbits) {
+    case 0: PQ_DQ_LAUNCH(0) break;
     case 1: PQ_DQ_LAUNCH(1) break;
     case 2: PQ_DQ_LAUNCH(2) break;
+    case 3: PQ_DQ_LAUNCH(3) break;
     case 4: PQ_DQ_LAUNCH(4) break;
-    case 8: PQ_DQ_LAUNCH(8) break;
+    case 5: PQ_DQ_LAUNCH(5) break;
+    case 6: PQ_DQ_LAUNCH(6) break;
+    case 7: PQ_DQ_LAUNCH(7) break;
     default: return hipErrorInvalidValue;
   }
 #undef PQ_DQ_LAUNCH

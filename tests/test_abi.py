@@ -147,7 +147,7 @@ def test_valid_call_without_gpu_reports_hip_error():
 
 
 def test_packed_entry_points_validate():
-    """Packed codes exist for bits dividing 8; other widths are refused before any HIP call."""
+    """Packed codes exist at every width 1..8; bad arguments are refused before any HIP call."""
     lib = pq.lib()
 
     def qp(bits, n=16, **kw):
@@ -156,16 +156,16 @@ def test_packed_entry_points_validate():
         return lib.pq_quantize_packed(a["d"], bits, a["dt"], a["x"], n, a["signs"], a["m"], a["proj"],
                                       a["codes"], a["norms"], a["qb"], a["rn"], NUL)
 
-    for bits in (3, 5, 6, 7):
-        assert qp(bits) == pq.PQ_EUNSUPPORTED
-        assert lib.pq_dequantize_packed(128, bits, P16, P16, 16, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_EUNSUPPORTED
     for bits in (0, 9, -1):
         assert qp(bits) == pq.PQ_EINVAL
         assert lib.pq_dequantize_packed(128, bits, P16, P16, 16, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_EINVAL
-    for bits in (1, 2, 4, 8):
+    for bits in range(1, 9):
         assert qp(bits, n=0) == pq.PQ_OK
         assert lib.pq_dequantize_packed(128, bits, P16, P16, 0, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_OK
         assert qp(bits, d=96) == pq.PQ_EINVAL
+        assert qp(bits, d=1024) == pq.PQ_EUNSUPPORTED
         assert qp(bits, codes=NUL) == pq.PQ_EINVAL
         assert qp(bits, codes=ctypes.c_void_p(0x10008)) == pq.PQ_EINVAL
+        assert qp(bits, m=64) == pq.PQ_EINVAL
         assert lib.pq_dequantize_packed(128, bits, P16, P16, 16, P16, 3, P16, NUL) == pq.PQ_EINVAL
+        assert lib.pq_dequantize_packed(128, bits, NUL, P16, 16, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_EINVAL

@@ -1,7 +1,7 @@
 """GPU parity of pq_quantize_packed / pq_dequantize_packed against the oracle (needs an
 MI355X).  Codes bit-packed into bytes (eliza quantization README, TurboQuant, "Algorithm in
-one paragraph", step 4) at 1, 2, 4 and 8 bits: the packed bytes are unpacked with the
-oracle's own unpacker and held to the same rule as byte codes."""
+one paragraph", step 4) at every width 1..8: the packed bytes are unpacked with the oracle's
+own unpacker and held to the same rule as byte codes."""
 
 import numpy as np
 import pytest
@@ -29,6 +29,15 @@ PACKED_CASES = [
     (256, 2, "f32", 16 * 4 + 15, 0),
     (512, 4, "bf16", 16 * 4 + 9, 512),          # projection walked from L2
     (512, 1, "f32", 16 * 2 + 1, 0),
+    # widths that do not divide a byte: codes straddle bytes and dwords
+    (128, 5, "bf16", 16 * 9 + 5, 64),
+    (128, 3, "f32", 16 * 4 + 1, 0),
+    (64, 3, "bf16", 16 * 5 + 3, 0),             # 6-byte runs per lane (16-bit accesses)
+    (64, 7, "bf16", 16 * 2 + 9, 16),
+    (256, 3, "bf16", 16 * 4 + 7, 256),
+    (256, 6, "f32", 16 * 3, 0),
+    (512, 3, "bf16", 16 * 2 + 5, 512),
+    (512, 5, "bf16", 16 * 2 + 11, 0),
 ]
 
 
@@ -62,7 +71,8 @@ def test_packed_quantize_dequantize(d, bits, dtype, n, m):
                                 out.float().cpu().numpy().astype(np.float64), bf, label="packed dequant")
 
 
-@pytest.mark.parametrize("d,bits", [(64, 1), (128, 2), (256, 4), (512, 4), (128, 8)])
+@pytest.mark.parametrize("d,bits", [(64, 1), (128, 2), (256, 4), (512, 4), (128, 8), (64, 5), (128, 3),
+                                    (256, 7), (512, 6)])
 def test_packed_dequantize_oracle_codes(d, bits):
     """Codes drawn and packed on the oracle side, dequantized from the packed bytes."""
     _case("packed dequantize oracle codes d=%d bits=%d" % (d, bits))
