@@ -253,6 +253,7 @@ def tsq_leg(pq, synth, torch, steps, warmup):
         q = torch.from_numpy(c["q"].view(np.int16)).view(torch.bfloat16).to(dev)
         del c
         enc = [pq.quantize(xs[i], d, bits, st, G) for i in range(2)]
+        pk = [pq.quantize(xs[i], d, bits, st, G, packed=True) for i in range(2)]   # 3-bit codes bit-packed
         deq = [torch.empty((H * T, d), dtype=torch.bfloat16, device=dev) for _ in range(2)]
         prep = pq.query_prep(q, st, G)
         sc = torch.empty((H, n_q, T), dtype=torch.float32, device=dev)
@@ -262,6 +263,12 @@ def tsq_leg(pq, synth, torch, steps, warmup):
 
         def dequant(k):
             pq.dequantize(enc[k % 2][0], enc[k % 2][1], d, bits, st, out=deq[k % 2])
+
+        def quant_packed(k):
+            pq.quantize(xs[k % 2], d, bits, st, G, out=pk[k % 2], packed=True)
+
+        def dequant_packed(k):
+            pq.dequantize(pk[k % 2][0], pk[k % 2][1], d, bits, st, out=deq[k % 2], packed=True)
 
         def prepare(k):
             pq.query_prep(q, st, G, out=prep)
@@ -273,10 +280,12 @@ def tsq_leg(pq, synth, torch, steps, warmup):
         for k in range(warmup):
             quant(k), dequant(k), prepare(k), score(k)
         t = {name: timed(torch, fn, steps) for name, fn in
-             (("quantize", quant), ("dequantize", dequant), ("query_prep", prepare), ("score", score))}
+             (("quantize", quant), ("dequantize", dequant), ("query_prep", prepare), ("score", score),
+              ("quantize_packed", quant_packed), ("dequantize_packed", dequant_packed))}
         nb = H * T
         qb = nb * d * 2 + nb * d + nb * 2 + nb * (m // 8) + nb * 2
         db = nb * d + nb * 2 + nb * d * 2
+        pcb = nb * d * bits // 8                         # packed code bytes
         sb = nb * (d + 2 + m // 8 + 2) + H * n_q * T * 4
         out.update({
             "tsq_d%d_quantize_us" % d: round(t["quantize"] * 1e6, 2),
@@ -288,8 +297,12 @@ def tsq_leg(pq, synth, torch, steps, warmup):
             "tsq_d%d_score_us" % d: round(t["score"] * 1e6, 2),
             "tsq_d%d_score_vectors_per_s" % d: round(nb / t["score"], 1),
             "tsq_d%d_score_hbm_frac" % d: round(sb / t["score"] / 1e9 / HBM_PEAK_GBS, 4),
+            "tsq_d%d_quantize_packed_us" % d: round(t["quantize_packed"] * 1e6, 2),
+            "tsq_d%d_dequantize_packed_us" % d: round(t["dequantize_packed"] * 1e6, 2),
+            "tsq_d%d_dequantize_packed_hbm_frac" % d: round((db - nb * d + pcb) / t["dequantize_packed"] / 1e9
+                                                            / HBM_PEAK_GBS, 4),
         })
-        del xs, enc, deq, prep, sc
+        del xs, enc, pk, deq, prep, sc
         torch.cuda.empty_cache()
     return out
 
@@ -383,15 +396,24 @@ def main():
         qb = torch.empty((n_blocks, m // 8), dtype=torch.uint8, device=dev)
         rn = torch.empty((n_blocks,), dtype=torch.float16, device=dev)
         out = torch.empty((n_blocks, d), dtype=torch.bfloat16, device=dev)
-        sets.append((x, codes, norms, qb, rn, out))
+        pcodes = torch.empty((n_blocks, d * bits // 8), dtype=torch.uint8, device=dev)
+        sets.append((x, codes, norms, qb, rn, out, pcodes))
 
     def quant(k):
-        x, codes, norms, qb, rn, _ = sets[k % N_SETS]
+        x, codes, norms, qb, rn, _, _ = sets[k % N_SETS]
         pq.quantize(x, d, bits, signs, proj, out=(codes, norms, qb, rn))
 
     def dequant(k):
-        _, codes, norms, _, _, out = sets[k % N_SETS]
+        _, codes, norms, _, _, out, _ = sets[k % N_SETS]
         pq.dequantize(codes, norms, d, bits, signs, out=out)
+
+    def quant_packed(k):
+        x, _, norms, qb, rn, _, pcodes = sets[k % N_SETS]
+        pq.quantize(x, d, bits, signs, proj, out=(pcodes, norms, qb, rn), packed=True)
+
+    def dequant_packed(k):
+        _, _, norms, _, _, out, pcodes = sets[k % N_SETS]
+        pq.dequantize(pcodes, norms, d, bits, signs, out=out, packed=True)
 
     def step(k):
         quant(k)
@@ -403,6 +425,9 @@ def main():
     t_q = timed(torch, quant, args.steps)
     t_d = timed(torch, dequant, args.steps)
     t_step = timed(torch, step, args.steps)
+    quant_packed(0), dequant_packed(0)
+    t_qp = timed(torch, quant_packed, args.steps)
+    t_dp = timed(torch, dequant_packed, args.steps)
 
     in_bytes = n_blocks * d * 2
     q_bytes = in_bytes + n_blocks * d + n_blocks * 2 + n_blocks * (m // 8) + n_blocks * 2
@@ -432,6 +457,8 @@ def main():
             "quantize_hbm_frac": round(q_gbs / HBM_PEAK_GBS, 4),
             "dequantize_hbm_frac": round(dq_bytes / t_d / 1e9 / HBM_PEAK_GBS, 4),
             "quantize_algorithmic_bytes": q_bytes, "dequantize_algorithmic_bytes": dq_bytes,
+            "quantize_packed_us": round(t_qp * 1e6, 3), "dequantize_packed_us": round(t_dp * 1e6, 3),
+            "packed_input_gb_per_s": round(in_bytes / (t_qp + t_dp) / 1e9, 1),
         },
         "roofline": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(q_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,

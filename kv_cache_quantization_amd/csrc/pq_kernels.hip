@@ -313,8 +313,12 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[N], int j) {
   return c & ((1u << B) - 1u);
 }
 
-template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP>
+// MODE: 0 = search grid stored once, 1 = replicated per lane of a 16-lane LDS group,
+// 2 = codes bit-packed, the grid's replication read from the tables at run time
+template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE>
 struct Quantizer {
+  static constexpr bool REP = MODE == 1;
+  static constexpr bool PK = MODE == 2;
   static constexpr int E = D / 4;
   static constexpr int KS = D / 32;                         // MFMA K steps per block
   static constexpr int NR = IN_BF16 ? D / 32 : D / 16;      // 16-byte loads per lane per tile
@@ -330,7 +334,7 @@ struct Quantizer {
   uint32_t smask[kCompactSigns ? D / 32 : E / 2];
   int lane, r, g, m, m_pad, mb;
   float inv_w, offM, topM, inv_sqrt_d;
-  uint32_t lane_off;
+  uint32_t lane_off, rep_shift;
 
   __device__ Quantizer(const pqi::QuantArgs& args, const unsigned char* sm, const uint4* g_lds)
       : a(args), smem(sm), gl(g_lds) {
@@ -356,7 +360,9 @@ struct Quantizer {
     offM = (float)a.t.half + kMagic;
     topM = kMagic + (float)(a.t.ncell - 1);
     inv_sqrt_d = 1.0f / sqrtf((float)D);
-    lane_off = (REP ? 16u * (uint32_t)(lane & 15) : 0u) - (kMagicBits << kRepShift);
+    const bool rep = PK ? a.t.nrep == 16 : REP;
+    rep_shift = PK ? (rep ? 8u : 4u) : kRepShift;
+    lane_off = (rep ? 16u * (uint32_t)(lane & 15) : 0u) - (kMagicBits << rep_shift);
   }
 
   // Codes and norm of the tile's 16 blocks (stored), and with the QJL stage the residual
@@ -434,7 +440,7 @@ struct Quantizer {
     for (int j = 0; j < E; ++j) {
       const float y = v[j] * inv_n;
       const float u = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
-      const uint32_t addr = (__float_as_uint(u) << kRepShift) + lane_off;
+      const uint32_t addr = (__float_as_uint(u) << (PK ? rep_shift : kRepShift)) + lane_off;
       uint32_t code;
       if constexpr (QJL) {
         u32x4 te = *static_cast<const u32x4*>(__builtin_assume_aligned(smem + addr, 16));
@@ -458,7 +464,7 @@ struct Quantizer {
     // the store branch below and keeps every lookup result live until then
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) asm volatile("" : "+v"(cw[w]));
-    if (a.pbits) {
+    if constexpr (PK) {
       // bit-packed codes: the lane's run of E codes is E pbits / 8 contiguous bytes
       switch (a.pbits) {
         case 1: store_packed<1>(cw, blk, valid); break;
@@ -599,10 +605,10 @@ __device__ void stage_projection_rows(const uint16_t* proj, const uint8_t* signs
 
 // THREADS = 512 when G takes most of the LDS: one workgroup per CU then still runs two waves
 // per SIMD.
-template <int D, bool IN_BF16, bool QJL, bool G_LDS, bool REP, int THREADS = kThreads>
+template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE, int THREADS = kThreads>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU)))
 void pq_quantize_kernel(const pqi::QuantArgs a) {
-  using Q = Quantizer<D, IN_BF16, QJL, G_LDS, REP>;
+  using Q = Quantizer<D, IN_BF16, QJL, G_LDS, MODE>;
   constexpr int WAVES = THREADS / 64;
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* tab = reinterpret_cast<uint4*>(smem);
@@ -649,10 +655,10 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(const uint4& b) {
   return __builtin_bit_cast(f16x8, h);
 }
 
-template <int D, bool IN_BF16, bool REP>
+template <int D, bool IN_BF16, int MODE>
 __global__ __launch_bounds__(chunk_threads<D>()) __attribute__((amdgpu_waves_per_eu(chunk_threads<D>() / 256)))
 void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
-  using Q = Quantizer<D, IN_BF16, true, true, REP>;
+  using Q = Quantizer<D, IN_BF16, true, true, MODE>;
   constexpr int THREADS = chunk_threads<D>();
   constexpr int WAVES = THREADS / 64;
   constexpr int KS = Q::KS;
@@ -1461,26 +1467,26 @@ int grid_for(int64_t n_tiles, const pqi::LaunchCfg& c, int per_cu) {
   return (int)want;
 }
 
-template <int D, bool REP>
+template <int D, int MODE>
 hipError_t launch_quantize_r(bool in_bf16, bool qjl, bool g_lds, int grid, size_t lds, const pqi::QuantArgs& a,
                              hipStream_t s) {
   if (!qjl) {
-    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, false, false, REP>), grid, kThreads, lds, s, a);
-    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, false, false, REP>), grid, kThreads, lds, s, a);
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, false, false, MODE>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, false, false, MODE>), grid, kThreads, lds, s, a);
   } else if (D <= 256 && g_lds && lds > 65536) {
     // one workgroup per CU: eight waves (d = 512 would spill at two waves per SIMD)
     if constexpr (D <= 256) {
       const int64_t n_tiles = (a.n_blocks + 15) >> 4;
       const int g8 = (int)std::max<int64_t>(1, std::min<int64_t>(grid, (n_tiles + 7) / 8));
-      if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true, REP, 512>), g8, 512, lds, s, a);
-      else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true, REP, 512>), g8, 512, lds, s, a);
+      if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true, MODE, 512>), g8, 512, lds, s, a);
+      else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true, MODE, 512>), g8, 512, lds, s, a);
     }
   } else if (g_lds) {
-    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true, REP>), grid, kThreads, lds, s, a);
-    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true, REP>), grid, kThreads, lds, s, a);
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, true, MODE>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, true, MODE>), grid, kThreads, lds, s, a);
   } else {
-    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, REP>), grid, kThreads, lds, s, a);
-    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, REP>), grid, kThreads, lds, s, a);
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, MODE>), grid, kThreads, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, MODE>), grid, kThreads, lds, s, a);
   }
   return hipGetLastError();
 }
@@ -1495,6 +1501,7 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   // G kept in LDS for the whole launch when it fits beside the search grid (several
   // workgroups per CU while it takes at most 64 KiB), else walked in chunks
   const bool g_lds = qjl && base + glb <= (size_t)c.max_lds;
+  const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
   if (qjl && !g_lds) {
     // residual fragments of every tile of the workgroup beside the search grid
     const size_t lds = base + chunk_frag_bytes<D>();
@@ -1502,19 +1509,20 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
     const int64_t n_groups = (n_tiles + chunk_threads<D>() / 64 - 1) / (chunk_threads<D>() / 64);
     const int per_cu = std::max(1, (int)((size_t)c.max_lds / lds));
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(n_groups, (int64_t)c.cu_count * per_cu));
-    if (a.t.nrep == 16) {
-      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, true>), grid, chunk_threads<D>(), lds, s, a);
-      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, true>), grid, chunk_threads<D>(), lds, s, a);
-    } else {
-      if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, false>), grid, chunk_threads<D>(), lds, s, a);
-      else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, false>), grid, chunk_threads<D>(), lds, s, a);
-    }
+#define PQ_CHUNK_LAUNCH(MODE)                                                                               \
+  if (in_bf16) hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, true, MODE>), grid, chunk_threads<D>(), lds, s, a); \
+  else hipLaunchKernelGGL((pq_quantize_chunked_kernel<D, false, MODE>), grid, chunk_threads<D>(), lds, s, a);
+    if (mode == 2) { PQ_CHUNK_LAUNCH(2) }
+    else if (mode == 1) { PQ_CHUNK_LAUNCH(1) }
+    else { PQ_CHUNK_LAUNCH(0) }
+#undef PQ_CHUNK_LAUNCH
     return hipGetLastError();
   }
   const size_t lds = base + (g_lds ? glb : 0);
   const int grid = grid_for(n_tiles, c, lds > 65536 ? 1 : PQ_QUANT_WG_PER_CU);
-  if (a.t.nrep == 16) return launch_quantize_r<D, true>(in_bf16, qjl, g_lds, grid, lds, a, s);
-  return launch_quantize_r<D, false>(in_bf16, qjl, g_lds, grid, lds, a, s);
+  if (mode == 2) return launch_quantize_r<D, 2>(in_bf16, qjl, g_lds, grid, lds, a, s);
+  if (mode == 1) return launch_quantize_r<D, 1>(in_bf16, qjl, g_lds, grid, lds, a, s);
+  return launch_quantize_r<D, 0>(in_bf16, qjl, g_lds, grid, lds, a, s);
 }
 
 template <int D>
