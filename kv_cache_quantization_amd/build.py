@@ -13,10 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpqhip.so")
-SOURCES = ["pq_kernels.hip", "pq_api.cpp"]
 
-HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMMON_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-result",
     # no packed fp32 VALU instructions (v_pk_add/mul/fma_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -24,26 +23,44 @@ HIPCC_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
+# compile units, built in parallel: the kernel file in three parts (see PQ_UNIT in it) and the C ABI
+UNITS = [("pq_kernels.hip", ["-DPQ_UNIT=0"], "kernels_0.o"), ("pq_kernels.hip", ["-DPQ_UNIT=1"], "kernels_1.o"),
+         ("pq_kernels.hip", ["-DPQ_UNIT=2"], "kernels_2.o"), ("pq_api.cpp", [], "api.o")]
+NOISE = "is not a recognized feature for this target"
+
+
+def _errors(stderr):
+    return "\n".join(l for l in stderr.splitlines() if NOISE not in l)
 
 
 def build(verbose=False):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = []
-    for s in SOURCES:
-        p = os.path.join(CSRC, s)
-        # hipcc treats .cpp as host C++ unless told otherwise; compile both as HIP
-        srcs += ["-x", "hip", p]
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    procs = []
+    for src, extra, obj in UNITS:
+        # hipcc treats .cpp as host C++ unless told otherwise; every unit compiles as HIP
+        cmd = [hipcc] + COMMON_FLAGS + extra + ["-c", "-x", "hip", os.path.join(CSRC, src),
+                                                "-o", os.path.join(obj_dir, obj)]
+        if verbose:
+            print(" ".join(cmd))
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    failed = []
+    for (src, extra, _), p in zip(UNITS, procs):
+        _, err = p.communicate()
+        err = _errors(err)
+        if p.returncode != 0:
+            failed.append("%s %s:\n%s" % (src, " ".join(extra), err))
+        elif err.strip() and verbose:
+            print(err)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc] + HIPCC_FLAGS + srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd))
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + [os.path.join(obj_dir, o) for _, _, o in UNITS] + \
+        ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if err.strip() and verbose:
-        print(err)
+        raise RuntimeError("link failed:\n" + _errors(res.stderr))
     os.replace(tmp, LIB)
     return LIB
 

@@ -143,6 +143,8 @@ struct LaunchCfg {
 };
 
 hipError_t launch_quantize(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_quantize_lo(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s);  // d <= 128
+hipError_t launch_quantize_hi(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s);  // d >= 256
 hipError_t launch_dequantize(int d, bool out_bf16, const DequantArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_sketch(int d, const SketchArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);

@@ -1580,8 +1580,37 @@ hipError_t launch_two_stage_d(int bits, const pqi::TwoStageArgs& a, int grid, in
 
 }  // namespace
 
+// The library is compiled as three units of this file (PQ_UNIT 0, 1, 2) in parallel: the
+// quantize kernels for d = 64, 128; those for d = 256, 512; everything else.  Without
+// PQ_UNIT one unit holds all of it.  Kernels are templates or file-local, so each unit
+// carries only the kernels its launch functions instantiate (plus the few non-template ones).
+#ifndef PQ_UNIT
+#define PQ_UNIT -1
+#endif
+
 namespace pqi {
 
+#if PQ_UNIT < 0 || PQ_UNIT == 0
+hipError_t launch_quantize_lo(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_quantize_d<64>(in_bf16, a, c, s);
+    case 128: return launch_quantize_d<128>(in_bf16, a, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+#endif
+
+#if PQ_UNIT < 0 || PQ_UNIT == 1
+hipError_t launch_quantize_hi(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {
+  switch (d) {
+    case 256: return launch_quantize_d<256>(in_bf16, a, c, s);
+    case 512: return launch_quantize_d<512>(in_bf16, a, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+#endif
+
+#if PQ_UNIT < 0 || PQ_UNIT == 2
 hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(pq_query_rotate_kernel, a.n_heads * kScoreRows, 256, 0, s, a);
   hipError_t e = hipGetLastError();
@@ -1620,13 +1649,7 @@ hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const Launch
 
 
 hipError_t launch_quantize(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {
-  switch (d) {
-    case 64: return launch_quantize_d<64>(in_bf16, a, c, s);
-    case 128: return launch_quantize_d<128>(in_bf16, a, c, s);
-    case 256: return launch_quantize_d<256>(in_bf16, a, c, s);
-    case 512: return launch_quantize_d<512>(in_bf16, a, c, s);
-  }
-  return hipErrorInvalidValue;
+  return d <= 128 ? launch_quantize_lo(d, in_bf16, a, c, s) : launch_quantize_hi(d, in_bf16, a, c, s);
 }
 
 hipError_t launch_dequantize(int d, bool out_bf16, const DequantArgs& a, const LaunchCfg& c, hipStream_t s) {
@@ -1680,5 +1703,7 @@ hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+#endif  // PQ_UNIT 2
 
 }  // namespace pqi
