@@ -264,6 +264,10 @@ def tsq_leg(pq, synth, torch, steps, warmup):
         def dequant(k):
             pq.dequantize(enc[k % 2][0], enc[k % 2][1], d, bits, st, out=deq[k % 2])
 
+        def score_packed(k):
+            e = pk[k % 2]
+            pq.score(prep, e[0], e[1], d, bits, H, n_q, T, e[2], e[3], m=m, out=sc, packed=True)
+
         def quant_packed(k):
             pq.quantize(xs[k % 2], d, bits, st, G, out=pk[k % 2], packed=True)
 
@@ -281,7 +285,8 @@ def tsq_leg(pq, synth, torch, steps, warmup):
             quant(k), dequant(k), prepare(k), score(k)
         t = {name: timed(torch, fn, steps) for name, fn in
              (("quantize", quant), ("dequantize", dequant), ("query_prep", prepare), ("score", score),
-              ("quantize_packed", quant_packed), ("dequantize_packed", dequant_packed))}
+              ("quantize_packed", quant_packed), ("dequantize_packed", dequant_packed),
+              ("score_packed", score_packed))}
         nb = H * T
         qb = nb * d * 2 + nb * d + nb * 2 + nb * (m // 8) + nb * 2
         db = nb * d + nb * 2 + nb * d * 2
@@ -301,6 +306,9 @@ def tsq_leg(pq, synth, torch, steps, warmup):
             "tsq_d%d_dequantize_packed_us" % d: round(t["dequantize_packed"] * 1e6, 2),
             "tsq_d%d_dequantize_packed_hbm_frac" % d: round((db - nb * d + pcb) / t["dequantize_packed"] / 1e9
                                                             / HBM_PEAK_GBS, 4),
+            "tsq_d%d_score_packed_us" % d: round(t["score_packed"] * 1e6, 2),
+            "tsq_d%d_score_packed_vectors_per_s" % d: round(nb / t["score_packed"], 1),
+            "tsq_d%d_score_packed_hbm_frac" % d: round((sb - nb * d + pcb) / t["score_packed"] / 1e9 / HBM_PEAK_GBS, 4),
         })
         del xs, enc, pk, deq, prep, sc
         torch.cuda.empty_cache()

@@ -220,6 +220,17 @@ int pq_score(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const 
              const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits, const uint16_t* rnorms,
              float* scores, void* stream);
 
+/*
+ * pq_score reading bit-packed codes (eliza README, TurboQuant, "Algorithm in one
+ * paragraph", step 4; eliza README, "Fused TurboQuant": scores straight from the
+ * packed indices).  As pq_score, except:
+ *   codes      n_heads * n_tok * d*bits/8 bytes (16-byte aligned), each token's
+ *              codes one little-endian bit stream as written by pq_quantize_packed
+ */
+int pq_score_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                    const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits,
+                    const uint16_t* rnorms, float* scores, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,7 @@ def _load():
         "pq_query_prep_bytes": ([I, I, I], L),
         "pq_query_prep": ([I, I, I, I, P, P, P, P, P], I),
         "pq_score": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
+        "pq_score_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -62,7 +63,7 @@ def _load():
 _lib = _load()
 EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_quantize",
            "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
-           "qjl_score", "pq_query_prep_bytes", "pq_query_prep", "pq_score")
+           "qjl_score", "pq_query_prep_bytes", "pq_query_prep", "pq_score", "pq_score_packed")
 
 
 def lib():
@@ -229,9 +230,11 @@ def prep_views(prep, d, m, n_heads):
     return qrot, sq
 
 
-def score(prep, codes, norms, d, bits, n_heads, n_q, n_tok, qjl_bits=None, rnorms=None, m=0, out=None):
-    """Two-stage scores fp32 [n_heads, n_q, n_tok] from codes [n_heads, n_tok, d], norms,
-    and (with m > 0) the QJL residual bits and residual norms."""
+def score(prep, codes, norms, d, bits, n_heads, n_q, n_tok, qjl_bits=None, rnorms=None, m=0, out=None,
+          packed=False):
+    """Two-stage scores fp32 [n_heads, n_q, n_tok] from codes [n_heads, n_tok, d] (or bit-packed,
+    d * bits / 8 bytes per token, with ``packed``: pq_score_packed), norms, and (with m > 0)
+    the QJL residual bits and residual norms."""
     _dev(prep, "prep", (torch.uint8,))
     _dev(codes, "codes", (torch.uint8,))
     _dev(norms, "norms", (torch.float16,))
@@ -241,6 +244,9 @@ def score(prep, codes, norms, d, bits, n_heads, n_q, n_tok, qjl_bits=None, rnorm
     if out is None:
         out = torch.empty((n_heads, n_q, n_tok), dtype=torch.float32, device=codes.device)
     _dev(out, "out", (torch.float32,))
-    _check(_lib.pq_score(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(codes), _ptr(norms), _ptr(qjl_bits),
-                         _ptr(rnorms), _ptr(out), _stream()), "pq_score")
+    if codes.numel() != n_heads * n_tok * (d * bits // 8 if packed else d):
+        raise ValueError("codes do not match n_heads, n_tok, d")
+    fn, name = (_lib.pq_score_packed, "pq_score_packed") if packed else (_lib.pq_score, "pq_score")
+    _check(fn(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(codes), _ptr(norms), _ptr(qjl_bits),
+              _ptr(rnorms), _ptr(out), _stream()), name)
     return out

@@ -17,15 +17,16 @@ LIB = os.path.join(HERE, "libpqhip.so")
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-result",
+    # each kernel unit leaves out the file-local helpers the other units use
+    "-Wno-unneeded-internal-declaration",
     # no packed fp32 VALU instructions (v_pk_add/mul/fma_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results in ordinary VGPRs: the kernels read every accumulator with VALU code
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
-# compile units, built in parallel: the kernel file in three parts (see PQ_UNIT in it) and the C ABI
-UNITS = [("pq_kernels.hip", ["-DPQ_UNIT=0"], "kernels_0.o"), ("pq_kernels.hip", ["-DPQ_UNIT=1"], "kernels_1.o"),
-         ("pq_kernels.hip", ["-DPQ_UNIT=2"], "kernels_2.o"), ("pq_api.cpp", [], "api.o")]
+# compile units, built in parallel: the kernel file in four parts (see PQ_UNIT in it) and the C ABI
+UNITS = [("pq_kernels.hip", ["-DPQ_UNIT=%d" % u], "kernels_%d.o" % u) for u in range(4)] + [("pq_api.cpp", [], "api.o")]
 NOISE = "is not a recognized feature for this target"
 
 

@@ -341,9 +341,9 @@ int pq_query_prep(int d, int m, int n_heads, int n_q, const uint16_t* q, const u
   return hip_status(pqi::launch_query_prep(a, (hipStream_t)stream));
 }
 
-int pq_score(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
-             const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits, const uint16_t* rnorms,
-             float* scores, void* stream) {
+static int score_impl(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                      const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits, const uint16_t* rnorms,
+                      float* scores, int packed, void* stream) {
   int st = check_d(d);
   if (st) return st;
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
@@ -365,7 +365,7 @@ int pq_score(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const 
   std::memset(&a, 0, sizeof(a));
   a.prep = static_cast<const unsigned char*>(prep);
   a.codes = codes; a.norms = norms; a.qbits = qjl_bits; a.rnorms = rnorms; a.scores = scores;
-  a.n_tok = n_tok; a.n_heads = n_heads; a.n_q = n_q; a.m = m;
+  a.n_tok = n_tok; a.n_heads = n_heads; a.n_q = n_q; a.m = m; a.packed = packed;
   // Walsh coefficients of the codebook over the odd subsets of the code bits:
   // alpha_p = 2^-b sum_k c_k s_p(k); the even subsets vanish by antisymmetry
   const Codebook& cb = codebook(bits);
@@ -377,6 +377,18 @@ int pq_score(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const 
     a.alpha[p] = acc / (double)L;
   }
   return hip_status(pqi::launch_two_stage(d, bits, a, cfg, (hipStream_t)stream));
+}
+
+int pq_score(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+             const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits, const uint16_t* rnorms,
+             float* scores, void* stream) {
+  return score_impl(d, bits, m, n_heads, n_q, n_tok, prep, codes, norms, qjl_bits, rnorms, scores, 0, stream);
+}
+
+int pq_score_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                    const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits, const uint16_t* rnorms,
+                    float* scores, void* stream) {
+  return score_impl(d, bits, m, n_heads, n_q, n_tok, prep, codes, norms, qjl_bits, rnorms, scores, 1, stream);
 }
 
 }  // extern "C"

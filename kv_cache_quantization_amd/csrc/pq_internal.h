@@ -132,6 +132,7 @@ struct TwoStageArgs {
   float* scores;           // [n_heads][n_q][n_tok]
   int64_t n_tok;
   int n_heads, n_q, m;
+  int packed;              // codes bit-packed at the code width ([n_heads][n_tok][d*bits/8])
   // c[code] = sum_p alpha[p] s_p(code), s_p = +1 when popcount(code & plane_mask[p]) is odd,
   // else -1 (the odd-subset Walsh expansion of an antisymmetric codebook)
   double alpha[kMaxPlanes];

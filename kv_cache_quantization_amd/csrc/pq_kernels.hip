@@ -1333,8 +1333,9 @@ __device__ __forceinline__ i32x4 plane_frag(const uint4& w, uint32_t mask) {
 }
 
 // KQT: 0 = no QJL term, D/64 = the QJL term with m = d (bits of a key loaded as one vector),
-// -1 = any other m (bits read per K step).
-template <int D, int BITS, int KQT>
+// -1 = any other m (bits read per K step).  PK: codes bit-packed at BITS bits; a lane's 16
+// codes of a K step are 2 BITS bytes of the token's stream, unpacked to bytes when used.
+template <int D, int BITS, int KQT, bool PK>
 __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageArgs a, int chunks_per_group) {
   constexpr int KC = D / 64;
   constexpr int NP = 1 << (BITS - 1);
@@ -1363,7 +1364,7 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
   const int r = lane & 15, gq = lane >> 4;
   const int64_t T = a.n_tok;
   const int64_t n_tiles = (T + 15) >> 4;
-  const uint8_t* codes = a.codes + (int64_t)grp * T * D;
+  const uint8_t* codes = a.codes + (int64_t)grp * T * (PK ? D * BITS / 8 : D);
   const uint16_t* norms = a.norms + (int64_t)grp * T;
   const uint8_t* qbits = QJL ? a.qbits + (int64_t)grp * T * mb : nullptr;
   const uint16_t* rnorms = QJL ? a.rnorms + (int64_t)grp * T : nullptr;
@@ -1372,8 +1373,9 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
 
   // one tile's inputs; tokens past the end are clamped to the last token (always in bounds,
   // no branches); such a token only feeds its own output column, which is not stored
+  constexpr int PW = PK ? (2 * BITS + 3) / 4 : 4;       // dwords of a lane's 16 codes
   struct Inputs {
-    uint4 cw[KC];
+    uint32_t cw[KC][PW];
     uint32_t qb[(KQB + 1) / 2];
     uint16_t n16, rn16;
   };
@@ -1381,8 +1383,12 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
     const int64_t tok = min(tile * 16 + r, T - 1);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + tok * D + 64 * k + 16 * gq));
-      in.cw[k] = make_uint4(w.x, w.y, w.z, w.w);
+      if constexpr (PK) {
+        load_code_bytes<2 * BITS>(codes + tok * (D * BITS / 8) + (64 * k + 16 * gq) * BITS / 8, true, in.cw[k]);
+      } else {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + tok * D + 64 * k + 16 * gq));
+        in.cw[k][0] = w.x; in.cw[k][1] = w.y; in.cw[k][2] = w.z; in.cw[k][3] = w.w;
+      }
     }
     in.n16 = norms[tok];
     if constexpr (QJL) in.rn16 = rnorms[tok];
@@ -1408,9 +1414,18 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
       const i32x4 a0 = fc[(0 * KC + k) * 64 + lane];
       const i32x4 a1 = fc[(1 * KC + k) * 64 + lane];
       const i32x4 a2 = fc[(2 * KC + k) * 64 + lane];
+      uint4 cb;                                           // the 16 codes as bytes
+      if constexpr (PK) {
+        uint32_t u[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) u[i >> 2] |= stream_code<BITS>(in.cw[k], i) << (8 * (i & 3));
+        cb = make_uint4(u[0], u[1], u[2], u[3]);
+      } else {
+        cb = make_uint4(in.cw[k][0], in.cw[k][1], in.cw[k][2], in.cw[k][3]);
+      }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const i32x4 b = plane_frag(in.cw[k], pqi::plane_mask(BITS, p));
+        const i32x4 b = plane_frag(cb, pqi::plane_mask(BITS, p));
         acc[p][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc[p][0], 0, 0, 0);
         acc[p][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc[p][1], 0, 0, 0);
         acc[p][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b, acc[p][2], 0, 0, 0);
@@ -1559,12 +1574,18 @@ hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hi
   return hipGetLastError();
 }
 
+template <int D, int BITS, bool PK>
+hipError_t launch_two_stage_dbp(const pqi::TwoStageArgs& a, int grid, int cpg, size_t lds, hipStream_t s) {
+  if (a.m == 0) hipLaunchKernelGGL((pq_score_kernel<D, BITS, 0, PK>), grid, kThreads, lds, s, a, cpg);
+  else if (a.m == D) hipLaunchKernelGGL((pq_score_kernel<D, BITS, D / 64, PK>), grid, kThreads, lds, s, a, cpg);
+  else hipLaunchKernelGGL((pq_score_kernel<D, BITS, -1, PK>), grid, kThreads, lds, s, a, cpg);
+  return hipGetLastError();
+}
+
 template <int D, int BITS>
 hipError_t launch_two_stage_db(const pqi::TwoStageArgs& a, int grid, int cpg, size_t lds, hipStream_t s) {
-  if (a.m == 0) hipLaunchKernelGGL((pq_score_kernel<D, BITS, 0>), grid, kThreads, lds, s, a, cpg);
-  else if (a.m == D) hipLaunchKernelGGL((pq_score_kernel<D, BITS, D / 64>), grid, kThreads, lds, s, a, cpg);
-  else hipLaunchKernelGGL((pq_score_kernel<D, BITS, -1>), grid, kThreads, lds, s, a, cpg);
-  return hipGetLastError();
+  if (a.packed) return launch_two_stage_dbp<D, BITS, true>(a, grid, cpg, lds, s);
+  return launch_two_stage_dbp<D, BITS, false>(a, grid, cpg, lds, s);
 }
 
 template <int D>
@@ -1580,8 +1601,9 @@ hipError_t launch_two_stage_d(int bits, const pqi::TwoStageArgs& a, int grid, in
 
 }  // namespace
 
-// The library is compiled as three units of this file (PQ_UNIT 0, 1, 2) in parallel: the
-// quantize kernels for d = 64, 128; those for d = 256, 512; everything else.  Without
+// The library is compiled as four units of this file (PQ_UNIT 0 .. 3) in parallel: the
+// quantize kernels for d = 64, 128; those for d = 256, 512; everything else but the
+// two-stage score; the two-stage score.  Without
 // PQ_UNIT one unit holds all of it.  Kernels are templates or file-local, so each unit
 // carries only the kernels its launch functions instantiate (plus the few non-template ones).
 #ifndef PQ_UNIT
@@ -1630,6 +1652,9 @@ hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#endif  // PQ_UNIT 2
+
+#if PQ_UNIT < 0 || PQ_UNIT == 3
 hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const LaunchCfg& c, hipStream_t s) {
   const int64_t n_tiles = (a.n_tok + 15) >> 4;
   int64_t per_group = ((int64_t)c.cu_count * 2 + a.n_heads - 1) / a.n_heads;
@@ -1646,6 +1671,9 @@ hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const Launch
   }
   return hipErrorInvalidValue;
 }
+#endif  // PQ_UNIT 3
+
+#if PQ_UNIT < 0 || PQ_UNIT == 2
 
 
 hipError_t launch_quantize(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {

@@ -169,3 +169,12 @@ def test_packed_entry_points_validate():
         assert qp(bits, m=64) == pq.PQ_EINVAL
         assert lib.pq_dequantize_packed(128, bits, P16, P16, 16, P16, 3, P16, NUL) == pq.PQ_EINVAL
         assert lib.pq_dequantize_packed(128, bits, NUL, P16, 16, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_EINVAL
+
+
+def test_packed_score_validates_like_score():
+    lib = pq.lib()
+    args = (P16, P16, P16, P16, P16, P16, NUL)
+    assert lib.pq_score_packed(256, 3, 256, 2, 16, 0, *args) == pq.PQ_OK                  # no tokens
+    assert lib.pq_score_packed(256, 5, 256, 2, 16, 64, *args) == pq.PQ_EUNSUPPORTED       # bits > 4
+    assert lib.pq_score_packed(100, 3, 0, 2, 16, 64, P16, P16, P16, NUL, NUL, P16, NUL) == pq.PQ_EINVAL
+    assert lib.pq_score_packed(256, 3, 256, 2, 17, 64, *args) == pq.PQ_EINVAL             # n_q > 16

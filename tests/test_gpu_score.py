@@ -90,6 +90,13 @@ def test_two_stage_random_codes(d, bits, m, n_heads, n_q, n_tok):
     for h in range(n_heads):
         ref, scale = _reference(codes[h], n16[h], qbits[h], rn16[h], q[h], bits, D, G, m)
         parity.check_scores(got[h], ref, np.maximum(scale, 1e-30), label="two-stage h%d" % h)
+    # the same codes bit-packed on the oracle side: identical integer sums, identical scores
+    pk = codec.pack_codes(codes.reshape(n_heads * n_tok, d), bits)
+    outp = pq.score(prep, parity.u8_tensor(pk), torch.from_numpy(n16.astype(np.float16)).cuda(), d, bits,
+                    n_heads, n_q, n_tok, parity.u8_tensor(qbits) if m else None,
+                    torch.from_numpy(rn16.astype(np.float16)).cuda() if m else None, m=m, packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(outp, out)
 
 
 @pytest.mark.parametrize("d", [256, 512])
@@ -117,3 +124,8 @@ def test_two_stage_end_to_end_config5_shape(d):
     for h in range(n_heads):
         ref, scale = qjl.two_stage(codes_np[h], n16[h], qbits[h], rn16[h], q[h], bits, D, G)
         parity.check_scores(got[h], ref, np.maximum(scale, 1e-30), label="e2e two-stage h%d" % h)
+    # quantize and score with packed codes: the same scores
+    pcodes, _, _, _ = pq.quantize(parity.bf16_tensor(c["x"]), d, bits, st, Gt, packed=True)
+    outp = pq.score(prep, pcodes, norms, d, bits, n_heads, n_q, n_tok, qb, rn, m=m, packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(outp, out)
