@@ -155,10 +155,14 @@ def summarize(run_dir):
            "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib": cf, "write_size_kib": cw,
                            "fetch_factor": f_fetch, "write_factor": f_write},
            "kernels": {}}
-    for kname, key in (("pq_quantize_kernel", "pq_quantize_kernel"), ("pq_dequantize_kernel", "pq_dequantize_kernel")):
+    # the byte-code instantiations the roofline is quoted on (the same run also times the
+    # packed-code kernels, whose traffic differs)
+    for kname, key in (("pq_quantize_kernel<128, true, true, true, 1, 256>", "pq_quantize_kernel"),
+                       ("pq_dequantize_kernel<128, true, 0>", "pq_dequantize_kernel")):
         fk, nf = counter("pmc_q_fetch", "q_fetch", kname)
         wk, nw = counter("pmc_q_write", "q_write", kname)
-        rec["kernels"][key] = {"dispatches": [nf, nw], "fetch_size_kib": fk, "write_size_kib": wk,
+        rec["kernels"][key] = {"instantiation": kname, "dispatches": [nf, nw], "fetch_size_kib": fk,
+                               "write_size_kib": wk,
                                "hbm_bytes_per_launch": round(fk * 1024 * f_fetch + wk * 1024 * f_write)}
     with open(os.path.join(out_dir, "pq_quantize_config2_counters.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
