@@ -100,3 +100,56 @@ def two_stage(codes, n16, qbits, rnorm16, q, bits, D, G):
 def storage_ratio(head_dim, m, norm_bytes=2, elem_bytes=2):
     """Bytes of a bf16 key over bytes of its sketch: head_dim*2 / (m/8 + 2)."""
     return head_dim * elem_bytes / (m / 8 + norm_bytes)
+
+
+# --- outlier channels --------------------------------------------------------------------
+# eliza quantization README, QJL, "Algorithm in one paragraph": a few head_dim indices carry
+# disproportionately large norms; per group of group_size consecutive tokens the top-k
+# outlier channels get a sketch of their own, with its own JL projection (dim_outlier).
+# qjl_apply.py, calibrate_key_outliers: the channel norms are taken over the group's tokens
+# and the indices come from a top-k over them, stored as uint8.
+# Readings: a trailing group shorter than group_size is a group of its own; top-k order is
+# decreasing norm with ties to the lower channel; the inlier part of a key is the key with
+# its group's outlier channels zeroed, the outlier part the key on those channels only
+# (zero elsewhere), each sketched as a QJL key with its own matrix (S for the inliers,
+# S_o for the outliers) and its own fp16 norm, and the score is the sum of the two QJL
+# estimators -- q.k = q.k_in + q.k_out, each term estimated without bias.
+
+def outlier_channels(keys, group_size, n_out):
+    """keys (T, d) of one head -> (n_groups, n_out) channel indices per group."""
+    keys = np.asarray(keys, dtype=np.float64)
+    T, d = keys.shape
+    groups = []
+    for g0 in range(0, T, group_size):
+        nrm = np.sqrt(np.sum(keys[g0:g0 + group_size] ** 2, axis=0))
+        order = sorted(range(d), key=lambda c: (-nrm[c], c))      # decreasing norm, lower channel first
+        groups.append(order[:n_out])
+    return np.asarray(groups, dtype=np.int64).reshape(-1, n_out)
+
+
+def outlier_mask(idx, T, d, group_size):
+    """(n_groups, n_out) indices -> boolean (T, d), True on each token's outlier channels."""
+    idx = np.asarray(idx, dtype=np.int64)
+    mask = np.zeros((T, d), dtype=bool)
+    for g in range(idx.shape[0]):
+        mask[g * group_size:(g + 1) * group_size, idx[g]] = True
+    return mask
+
+
+def split_sketch(keys, idx, group_size, S, S_o):
+    """Inlier and outlier sketches of one head's keys (T, d): dict(in=sketch(k_in, S),
+    out=sketch(k_out, S_o)) with k_in + k_out = k."""
+    keys = np.asarray(keys, dtype=np.float64)
+    mask = outlier_mask(idx, keys.shape[0], keys.shape[1], group_size)
+    k_out = np.where(mask, keys, 0.0)
+    k_in = keys - k_out
+    return {"in": sketch(k_in, S), "out": sketch(k_out, S_o), "k_in": k_in, "k_out": k_out}
+
+
+def estimate_split(sk, q, S, S_o):
+    """Scores (nq, T) of queries q (nq, d) from a split sketch: the two QJL estimators summed."""
+    q = np.asarray(q, dtype=np.float64)
+    m, m_o = np.asarray(S).shape[0], np.asarray(S_o).shape[0]
+    a = estimate(sk["in"]["bits"], sk["in"]["norm16"], q @ np.asarray(S, dtype=np.float64).T, m)
+    b = estimate(sk["out"]["bits"], sk["out"]["norm16"], q @ np.asarray(S_o, dtype=np.float64).T, m_o)
+    return a + b

@@ -126,3 +126,84 @@ def test_two_stage_estimator_unbiased_given_codes():
     assert abs(est.var() / var - 1.0) < 0.05
     # and the estimate is unbiased for <q, x> up to the fp16 rounding of ||r||
     assert abs(est.mean() - float((q @ x.T)[0, 0])) <= 4.5 * math.sqrt(var / N_MC) + abs(qr) * abs(ratio - 1)
+
+
+# --- outlier channels (eliza README, QJL, "Algorithm in one paragraph"; qjl_apply.py,
+# calibrate_key_outliers) ---------------------------------------------------------------
+
+def test_outlier_channels_fixture_and_ties():
+    d, gs = 8, 4
+    keys = np.tile(np.arange(1.0, d + 1.0), (10, 1))        # channel norm grows with the channel
+    keys[4:8, 2] = 100.0                                     # group 1: channel 2 dominates
+    idx = qjl.outlier_channels(keys, gs, 3)
+    assert idx.tolist() == [[7, 6, 5], [2, 7, 6], [7, 6, 5]]  # 10 tokens: groups of 4, 4 and 2
+    flat = np.ones((4, d))
+    assert qjl.outlier_channels(flat, gs, 3).tolist() == [[0, 1, 2]]   # equal norms: lower channels
+
+
+@pytest.mark.parametrize("d,gs,n_out", [(16, 8, 3), (64, 32, 8), (128, 32, 8)])
+def test_outlier_channels_against_pairwise_ranks(d, gs, n_out):
+    """A channel is chosen iff fewer than n_out channels outrank it (larger norm, or equal
+    norm and a lower index) -- ranks counted pairwise, no sorting."""
+    rng = np.random.default_rng(d + gs)
+    keys = rng.standard_normal((3 * gs + 5, d))
+    keys[:, 5] *= 6.0
+    idx = qjl.outlier_channels(keys, gs, n_out)
+    for g in range(idx.shape[0]):
+        blk = keys[g * gs:(g + 1) * gs]
+        nrm = np.sqrt((blk ** 2).sum(axis=0))
+        outrank = (nrm[None, :] > nrm[:, None]) | ((nrm[None, :] == nrm[:, None]) &
+                                                    (np.arange(d)[None, :] < np.arange(d)[:, None]))
+        rank = outrank.sum(axis=1)                          # channels outranking each channel
+        assert set(idx[g].tolist()) == set(np.nonzero(rank < n_out)[0].tolist())
+        assert np.all(np.diff(nrm[idx[g]]) <= 0)            # decreasing norm
+
+
+def test_split_sketch_partitions_each_key():
+    rng = np.random.default_rng(3)
+    T, d, gs = 40, 32, 16
+    keys = rng.standard_normal((T, d))
+    idx = qjl.outlier_channels(keys, gs, 4)
+    S, S_o = rng.standard_normal((64, d)), rng.standard_normal((32, d))
+    sk = qjl.split_sketch(keys, idx, gs, S, S_o)
+    assert np.array_equal(sk["k_in"] + sk["k_out"], keys)
+    for t in range(T):
+        nz = set(np.nonzero(sk["k_out"][t])[0].tolist())
+        assert nz <= set(idx[t // gs].tolist())
+        assert np.all(sk["k_in"][t, idx[t // gs]] == 0.0)
+    assert np.allclose(sk["in"]["norm"] ** 2 + sk["out"]["norm"] ** 2, (keys ** 2).sum(axis=1))
+    # no outlier channels: the inlier part is the whole key and the score is the plain estimator
+    none = qjl.split_sketch(keys, np.zeros((3, 0), dtype=np.int64), gs, S, S_o)
+    q = rng.standard_normal((5, d))
+    plain = qjl.estimate(qjl.sketch(keys, S)["bits"], qjl.sketch(keys, S)["norm16"], q @ S.T, 64)
+    assert np.array_equal(qjl.estimate_split(none, q, S, S_o), plain)
+
+
+def test_split_estimator_unbiased():
+    """Monte Carlo over both matrices: mean -> q.k, variance -> the sum of the two terms'
+    closed forms."""
+    d, m, m_o, gs = 32, 64, 32, 1
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal(d)
+    k[[2, 9]] *= 15.0
+    k /= np.linalg.norm(k)
+    q = rng.standard_normal(d)
+    idx = qjl.outlier_channels(k[None, :], gs, 2)
+    assert sorted(idx[0].tolist()) == [2, 9]
+    n = 12000
+    est = np.empty(n)
+    for t in range(n):
+        S, S_o = rng.standard_normal((m, d)), rng.standard_normal((m_o, d))
+        sk = qjl.split_sketch(k[None, :], idx, gs, S, S_o)
+        est[t] = qjl.estimate_split(sk, q[None, :], S, S_o)[0, 0]
+    k_out = np.zeros(d)
+    k_out[[2, 9]] = k[[2, 9]]
+    k_in = k - k_out
+    n_in, n_o = numerics.round_fp16(np.linalg.norm(k_in)), numerics.round_fp16(np.linalg.norm(k_out))
+    # the stored norms are fp16: the estimator is unbiased for q.k_in * n_in/|k_in| + ...
+    mean = np.dot(q, k_in) * n_in / np.linalg.norm(k_in) + np.dot(q, k_out) * n_o / np.linalg.norm(k_out)
+    var = (_closed_form_var(q, k_in * n_in / np.linalg.norm(k_in), m)
+           + _closed_form_var(q, k_out * n_o / np.linalg.norm(k_out), m_o))
+    assert abs(est.mean() - mean) <= 4.5 * math.sqrt(var / n)
+    assert abs(est.var() / var - 1.0) < 0.06
+    assert abs(mean - np.dot(q, k)) < 1e-3 * np.linalg.norm(q)
