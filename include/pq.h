@@ -183,6 +183,41 @@ int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const
               const uint8_t* bits, const uint16_t* norms, float* scores, void* stream);
 
 /*
+ * Outlier channels of the keys (eliza quantization README, QJL, "Algorithm in one
+ * paragraph": a top-k outlier sketch per group of group_size consecutive tokens;
+ * qjl_apply.py, calibrate_key_outliers: channel norms over the group's tokens, top-k
+ * indices as uint8).  Per head and group of group_size consecutive tokens (the last
+ * group may be shorter), the n_out channels of largest L2 norm over the group's
+ * tokens, in decreasing norm (sums of squares in fp32; ties to the lower channel).
+ *   d          64, 128 or 256 (indices are bytes); 512 -> PQ_EUNSUPPORTED
+ *   keys       n_heads*seq_len*d bf16, head h, token t at keys + (h*seq_len + t)*d
+ *   idx        out, n_heads * ceil(seq_len/group_size) * n_out bytes, [head][group][rank]
+ *   n_out      1 .. d
+ */
+int qjl_outlier_channels(int d, const uint16_t* keys, int64_t n_heads, int64_t seq_len, int group_size,
+                         int n_out, uint8_t* idx, void* stream);
+
+/*
+ * qjl_sketch of one part of each key, split by its group's outlier channels (idx as
+ * written by qjl_outlier_channels): part 0 sketches the key with those channels set
+ * to zero (with G = S, m projections), part 1 the key on those channels only (with
+ * its own matrix S_o, dim_outlier = m projections).  bits and norms as in qjl_sketch,
+ * over n_heads*seq_len keys.  The score of a key is the sum of the two estimators
+ * (qjl_score on part 0, then qjl_score_add on part 1): q.k = q.k_in + q.k_out.
+ *   d          64, 128 or 256; part 0 or 1; other arguments as above
+ */
+int qjl_sketch_split(int d, int m, const uint16_t* keys, int64_t n_heads, int64_t seq_len, int group_size,
+                     int n_out, const uint8_t* idx, int part, const uint16_t* proj, uint8_t* bits,
+                     uint16_t* norms, void* stream);
+
+/*
+ * qjl_score that adds its estimate to the scores already in `scores` (the second
+ * term of the split estimator).  Arguments and errors as in qjl_score.
+ */
+int qjl_score_add(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
+                  const uint8_t* bits, const uint16_t* norms, float* scores, void* stream);
+
+/*
  * Two-stage estimator of <q, x> from the stored codes and QJL residual bits,
  * without reconstructing x (eliza quantization README, TurboQuant, "Algorithm in
  * one paragraph"; scores straight from the packed indices: same README, "Fused

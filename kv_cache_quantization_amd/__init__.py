@@ -48,6 +48,9 @@ def _load():
         "qjl_sketch": ([I, I, P, L, P, P, P, P], I),
         "qjl_project": ([I, I, P, L, P, P, P], I),
         "qjl_score": ([I, I, I, I, L, P, P, P, P, P], I),
+        "qjl_score_add": ([I, I, I, I, L, P, P, P, P, P], I),
+        "qjl_outlier_channels": ([I, P, L, L, I, I, P, P], I),
+        "qjl_sketch_split": ([I, I, P, L, L, I, I, P, I, P, P, P, P], I),
         "pq_query_prep_bytes": ([I, I, I], L),
         "pq_query_prep": ([I, I, I, I, P, P, P, P, P], I),
         "pq_score": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
@@ -63,7 +66,8 @@ def _load():
 _lib = _load()
 EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_quantize",
            "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
-           "qjl_score", "pq_query_prep_bytes", "pq_query_prep", "pq_score", "pq_score_packed")
+           "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
+           "pq_query_prep", "pq_score", "pq_score_packed")
 
 
 def lib():
@@ -153,8 +157,12 @@ def dequantize(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None,
     return out
 
 
-def qjl_sketch(keys, proj, out=None):
-    """keys bf16 [..., d]; returns (bits uint8 [n, m/8], norms fp16 [n])."""
+def qjl_sketch(keys, proj, out=None, split=None):
+    """keys bf16 [..., d]; returns (bits uint8 [n, m/8], norms fp16 [n]).
+
+    ``split`` = (idx, seq_len, group_size, part) sketches one part of each key split by its
+    group's outlier channels (qjl_sketch_split): part 0 without them, part 1 only them;
+    keys are then [heads, seq_len, d] and idx as from ``qjl_outlier_channels``."""
     _dev(keys, "keys", (torch.bfloat16,))
     _dev(proj, "proj", (torch.bfloat16,))
     m, d = proj.shape
@@ -164,8 +172,30 @@ def qjl_sketch(keys, proj, out=None):
         norms = torch.empty((n,), dtype=torch.float16, device=keys.device)
     else:
         bits, norms = out
-    _check(_lib.qjl_sketch(d, m, _ptr(keys), n, _ptr(proj), _ptr(bits), _ptr(norms), _stream()), "qjl_sketch")
+    if split is None:
+        _check(_lib.qjl_sketch(d, m, _ptr(keys), n, _ptr(proj), _ptr(bits), _ptr(norms), _stream()), "qjl_sketch")
+    else:
+        idx, seq_len, group_size, part = split
+        _dev(idx, "idx", (torch.uint8,))
+        if n % seq_len:
+            raise ValueError("keys are not [heads, seq_len, d]")
+        _check(_lib.qjl_sketch_split(d, m, _ptr(keys), n // seq_len, seq_len, group_size, idx.shape[-1], _ptr(idx),
+                                     part, _ptr(proj), _ptr(bits), _ptr(norms), _stream()), "qjl_sketch_split")
     return bits, norms
+
+
+def qjl_outlier_channels(keys, group_size, n_out, out=None):
+    """keys bf16 [..., seq_len, d] -> uint8 [..., ceil(seq_len / group_size), n_out]: per group of
+    group_size consecutive tokens, the n_out channels of largest norm, decreasing."""
+    _dev(keys, "keys", (torch.bfloat16,))
+    seq_len, d = keys.shape[-2], keys.shape[-1]
+    heads = keys.numel() // (seq_len * d)
+    n_groups = (seq_len + group_size - 1) // group_size
+    if out is None:
+        out = torch.empty(tuple(keys.shape[:-2]) + (n_groups, n_out), dtype=torch.uint8, device=keys.device)
+    _check(_lib.qjl_outlier_channels(d, _ptr(keys), heads, seq_len, group_size, n_out, _ptr(out), _stream()),
+           "qjl_outlier_channels")
+    return out
 
 
 def qjl_project(q, proj, out=None):
@@ -180,16 +210,19 @@ def qjl_project(q, proj, out=None):
     return out
 
 
-def qjl_score(sq, bits, norms, batch, kv_heads, q_heads, n_keys, out=None):
-    """QJL scores [batch, q_heads, n_keys] fp32 from projected queries and packed key bits."""
+def qjl_score(sq, bits, norms, batch, kv_heads, q_heads, n_keys, out=None, accumulate=False):
+    """QJL scores [batch, q_heads, n_keys] fp32 from projected queries and packed key bits;
+    ``accumulate`` adds them to ``out`` (qjl_score_add)."""
     _dev(sq, "sq", (torch.float32,))
     _dev(bits, "bits", (torch.uint8,))
     _dev(norms, "norms", (torch.float16,))
     m = sq.shape[-1]
+    if accumulate and out is None:
+        raise ValueError("accumulate needs out")
     if out is None:
         out = torch.empty((batch, q_heads, n_keys), dtype=torch.float32, device=sq.device)
-    _check(_lib.qjl_score(m, batch, kv_heads, q_heads, n_keys, _ptr(sq), _ptr(bits), _ptr(norms), _ptr(out),
-                          _stream()), "qjl_score")
+    fn, name = (_lib.qjl_score_add, "qjl_score_add") if accumulate else (_lib.qjl_score, "qjl_score")
+    _check(fn(m, batch, kv_heads, q_heads, n_keys, _ptr(sq), _ptr(bits), _ptr(norms), _ptr(out), _stream()), name)
     return out
 
 

@@ -277,7 +277,47 @@ int qjl_sketch(int d, int m, const uint16_t* keys, int64_t n_keys, const uint16_
   pqi::LaunchCfg cfg;
   if ((st = launch_cfg(&cfg))) return st;
   pqi::SketchArgs a;
+  std::memset(&a, 0, sizeof(a));
   a.keys = keys; a.n_keys = n_keys; a.proj = proj; a.bits = bits; a.norms = norms; a.m = m;
+  return hip_status(pqi::launch_sketch(d, a, cfg, (hipStream_t)stream));
+}
+
+int qjl_outlier_channels(int d, const uint16_t* keys, int64_t n_heads, int64_t seq_len, int group_size, int n_out,
+                         uint8_t* idx, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (d > 256) return PQ_EUNSUPPORTED;                    // channel indices are bytes
+  if (n_heads < 0 || seq_len < 0 || group_size < 1 || n_out < 1 || n_out > d) return PQ_EINVAL;
+  if (n_heads > 0 && seq_len > kMaxElems / d / n_heads) return PQ_EINVAL;
+  if (n_heads == 0 || seq_len == 0) return PQ_OK;
+  if (!keys || !idx) return PQ_EINVAL;
+  if (!aligned(keys, 16)) return PQ_EINVAL;
+  pqi::OutlierArgs a;
+  a.keys = keys; a.n_heads = n_heads; a.seq_len = seq_len; a.n_groups = (seq_len + group_size - 1) / group_size;
+  a.d = d; a.group_size = group_size; a.n_out = n_out; a.oidx = idx;
+  return hip_status(pqi::launch_outliers(a, (hipStream_t)stream));
+}
+
+int qjl_sketch_split(int d, int m, const uint16_t* keys, int64_t n_heads, int64_t seq_len, int group_size,
+                     int n_out, const uint8_t* idx, int part, const uint16_t* proj, uint8_t* bits, uint16_t* norms,
+                     void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (d > 256) return PQ_EUNSUPPORTED;
+  if (m <= 0 || (m % 8) != 0) return PQ_EINVAL;
+  if (m > 1024) return PQ_EUNSUPPORTED;
+  if (n_heads < 0 || seq_len < 0 || group_size < 1 || n_out < 1 || n_out > d || (part != 0 && part != 1))
+    return PQ_EINVAL;
+  if (n_heads > 0 && seq_len > kMaxElems / d / n_heads) return PQ_EINVAL;
+  if (n_heads == 0 || seq_len == 0) return PQ_OK;
+  if (!keys || !idx || !proj || !bits || !norms) return PQ_EINVAL;
+  if (!aligned(keys, 16) || !aligned(proj, 16) || !aligned(bits, 16) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::SketchArgs a;
+  a.keys = keys; a.n_keys = n_heads * seq_len; a.proj = proj; a.bits = bits; a.norms = norms; a.m = m;
+  a.oidx = idx; a.seq_len = seq_len; a.n_groups = (seq_len + group_size - 1) / group_size;
+  a.group_size = group_size; a.n_out = n_out; a.part = part;
   return hip_status(pqi::launch_sketch(d, a, cfg, (hipStream_t)stream));
 }
 
@@ -297,8 +337,8 @@ int qjl_project(int d, int m, const uint16_t* q, int64_t n_q, const uint16_t* pr
   return hip_status(pqi::launch_project(a, (hipStream_t)stream));
 }
 
-int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
-              const uint8_t* bits, const uint16_t* norms, float* scores, void* stream) {
+static int score_qjl_impl(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
+                          const uint8_t* bits, const uint16_t* norms, float* scores, int accumulate, void* stream) {
   if (m <= 0 || (m % 8) != 0) return PQ_EINVAL;
   if ((m % 64) != 0 || m > 1024) return PQ_EUNSUPPORTED;
   if (batch < 0 || kv_heads <= 0 || q_heads <= 0 || n_keys < 0) return PQ_EINVAL;
@@ -314,8 +354,18 @@ int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const
   if (st2) return st2;
   pqi::ScoreArgs a;
   a.sq = sq; a.bits = bits; a.norms = norms; a.scores = scores; a.n_keys = n_keys; a.m = m;
-  a.batch = batch; a.kv_heads = kv_heads; a.q_heads = q_heads;
+  a.batch = batch; a.kv_heads = kv_heads; a.q_heads = q_heads; a.accumulate = accumulate;
   return hip_status(pqi::launch_score(a, cfg, (hipStream_t)stream));
+}
+
+int qjl_score(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
+              const uint8_t* bits, const uint16_t* norms, float* scores, void* stream) {
+  return score_qjl_impl(m, batch, kv_heads, q_heads, n_keys, sq, bits, norms, scores, 0, stream);
+}
+
+int qjl_score_add(int m, int batch, int kv_heads, int q_heads, int64_t n_keys, const float* sq,
+                  const uint8_t* bits, const uint16_t* norms, float* scores, void* stream) {
+  return score_qjl_impl(m, batch, kv_heads, q_heads, n_keys, sq, bits, norms, scores, 1, stream);
 }
 
 int64_t pq_query_prep_bytes(int d, int m, int n_heads) {

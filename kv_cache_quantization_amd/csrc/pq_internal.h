@@ -59,6 +59,20 @@ struct SketchArgs {
   uint8_t* bits;
   uint16_t* norms;
   int m;
+  // optional split by outlier channels (oidx == nullptr: the whole key): key t of a head
+  // (n_keys = heads * seq_len) belongs to group t / group_size, whose n_out channels are
+  // oidx[(head * n_groups + group) * n_out ..]; part 0 sketches the key without them,
+  // part 1 the key on them only
+  const uint8_t* oidx;
+  int64_t seq_len, n_groups;
+  int group_size, n_out, part;
+};
+
+struct OutlierArgs {
+  const uint16_t* keys;    // [n_heads][seq_len][d] bf16
+  int64_t n_heads, seq_len, n_groups;
+  int d, group_size, n_out;
+  uint8_t* oidx;           // [n_heads][n_groups][n_out]
 };
 
 struct ProjectArgs {
@@ -82,6 +96,7 @@ struct ScoreArgs {
   int batch;
   int kv_heads;
   int q_heads;
+  int accumulate;          // add the estimate to the scores already there
 };
 
 // Prepared queries of the two-stage score, per KV head (byte offsets from the head's
@@ -148,6 +163,7 @@ hipError_t launch_quantize_lo(int d, bool in_bf16, const QuantArgs& a, const Lau
 hipError_t launch_quantize_hi(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s);  // d >= 256
 hipError_t launch_dequantize(int d, bool out_bf16, const DequantArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_sketch(int d, const SketchArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_outliers(const OutlierArgs& a, hipStream_t s);
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s);

@@ -891,7 +891,9 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 #endif
 constexpr int kSketchThreads = PQ_SKETCH_THREADS;
 
-template <int D, bool G_LDS>
+// SPLIT: the keys are masked to their group's outlier channels (part 1) or to the other
+// channels (part 0) as they are loaded, so norm and signs are those of the masked key.
+template <int D, bool G_LDS, bool SPLIT>
 __global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(PQ_SKETCH_WAVES_PER_EU)))
 void qjl_sketch_kernel(const pqi::SketchArgs a) {
   constexpr int KS = D / 32;
@@ -926,10 +928,35 @@ void qjl_sketch_kernel(const pqi::SketchArgs a) {
       const int64_t key = (P * NT + t) * 16 + r;
       const bool valid = full || key < n_keys;
       const u32x4* src = reinterpret_cast<const u32x4*>(a.keys + key * D);
+      // element 8 s + i of this lane (column 32 s + 8 g + i) is an outlier channel of the key's
+      // group when bit 8 s + i of om is set
+      uint32_t om[(KS * 8 + 31) / 32];
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int w = 0; w < (KS * 8 + 31) / 32; ++w) om[w] = 0;
+        const int64_t kc = min(key, n_keys - 1);
+        const int64_t head = kc / a.seq_len, grp = (kc % a.seq_len) / a.group_size;
+        const uint8_t* ix = a.oidx + (head * a.n_groups + grp) * a.n_out;
+        for (int j = 0; j < a.n_out; ++j) {
+          const int c = ix[j];
+          if (((c >> 3) & 3) == g) {
+            const int b = 8 * (c >> 5) + (c & 7);
+#pragma unroll
+            for (int w = 0; w < (KS * 8 + 31) / 32; ++w) om[w] |= (b >> 5) == w ? 1u << (b & 31) : 0u;
+          }
+        }
+      }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         u32x4 w = {0, 0, 0, 0};
         if (valid) w = __builtin_nontemporal_load(src + 4 * s + g);
+        if constexpr (SPLIT) {
+          const uint32_t bs = om[(8 * s) >> 5] >> ((8 * s) & 31);      // this chunk's 8 bits
+          const uint32_t keep = a.part ? bs : ~bs;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            w[u] &= ((keep >> (2 * u)) & 1u ? 0x0000FFFFu : 0u) | ((keep >> (2 * u + 1)) & 1u ? 0xFFFF0000u : 0u);
+        }
         kf[t][s] = __builtin_bit_cast(bf16x8, w);
       }
     }
@@ -979,6 +1006,54 @@ void qjl_sketch_kernel(const pqi::SketchArgs a) {
       for (int t = 0; t < NT; ++t)
         store_sign_bytes(sign_bytes_of(x[t]), lane, (P * NT + t) * 16, n_keys, a.bits, mb, nt0);
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Outlier channels: one wave per (head, group of group_size tokens).  Lane l holds channels
+// D/64 l .. D/64 (l+1) - 1 and sums their squares over the group's tokens in fp32; then
+// n_out rounds each take the wave-wide maximum of (sum of squares, lower channel first) as
+// one 64-bit key (the fp32 pattern of a non-negative sum orders as an integer).
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void qjl_outlier_kernel(const pqi::OutlierArgs a) {
+  constexpr int CPL = D / 64;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wid >= a.n_heads * a.n_groups) return;                     // whole waves only
+  const int64_t head = wid / a.n_groups, grp = wid % a.n_groups;
+  const int64_t t0 = grp * a.group_size, t1 = min(t0 + (int64_t)a.group_size, a.seq_len);
+  float ss[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) ss[c] = 0.0f;
+  const uint16_t* base = a.keys + (head * a.seq_len) * D + CPL * lane;
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint16_t* p = base + t * D;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float v = bf16_to_f32(p[c]);
+      ss[c] = fmaf(v, v, ss[c]);
+    }
+  }
+  uint32_t taken = 0;
+  uint8_t* out = a.oidx + wid * a.n_out;
+  for (int j = 0; j < a.n_out; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const uint64_t k = ((taken >> c) & 1u) ? 0ull
+                         : ((uint64_t)__float_as_uint(ss[c]) << 32) | (uint64_t)(0xFFFFu - (CPL * lane + c));
+      best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), off), lo = __shfl_xor((uint32_t)best, off);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      best = o > best ? o : best;
+    }
+    const int ch = 0xFFFF - (int)(best & 0xFFFFu);
+    if (ch / CPL == lane) taken |= 1u << (ch % CPL);
+    if (lane == 0) out[j] = (uint8_t)ch;
   }
 }
 
@@ -1077,7 +1152,7 @@ __device__ __forceinline__ void load_key_bits(const uint8_t* kb, bool valid, uin
   }
 }
 
-template <int KS>
+template <int KS, bool ADD>
 __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArgs a, int chunks_per_group) {
   constexpr int m = 64 * KS, mb = m >> 3;
   const int group = a.q_heads / a.kv_heads;
@@ -1193,10 +1268,16 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
       const int64_t key = pp * 32 + 2 * r;
       if (out_lane) {
         if (pairs_aligned && key + 1 < T) {
-          *reinterpret_cast<float2*>(out + key) = make_float2(val[0], val[1]);
+          float2* o = reinterpret_cast<float2*>(out + key);
+          if constexpr (ADD) {
+            const float2 prev = *o;
+            *o = make_float2(prev.x + val[0], prev.y + val[1]);
+          } else {
+            *o = make_float2(val[0], val[1]);
+          }
         } else {
-          if (key < T) out[key] = val[0];
-          if (key + 1 < T) out[key + 1] = val[1];
+          if (key < T) out[key] = ADD ? out[key] + val[0] : val[0];
+          if (key + 1 < T) out[key + 1] = ADD ? out[key + 1] + val[1] : val[1];
         }
       }
     }
@@ -1569,8 +1650,13 @@ hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hi
   const size_t glb = (size_t)m_pad * D * 2;
   const bool g_lds = glb <= (size_t)c.max_lds && glb <= 65536;
   const int grid = grid_for(n_tiles, c, PQ_SKETCH_WG_PER_CU);
-  if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true>), grid, kSketchThreads, glb, s, a);
-  else hipLaunchKernelGGL((qjl_sketch_kernel<D, false>), grid, kSketchThreads, 0, s, a);
+  if (a.oidx) {
+    if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true, true>), grid, kSketchThreads, glb, s, a);
+    else hipLaunchKernelGGL((qjl_sketch_kernel<D, false, true>), grid, kSketchThreads, 0, s, a);
+  } else {
+    if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true, false>), grid, kSketchThreads, glb, s, a);
+    else hipLaunchKernelGGL((qjl_sketch_kernel<D, false, false>), grid, kSketchThreads, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -1700,6 +1786,18 @@ hipError_t launch_sketch(int d, const SketchArgs& a, const LaunchCfg& c, hipStre
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_outliers(const OutlierArgs& a, hipStream_t s) {
+  const int64_t waves = a.n_heads * a.n_groups;
+  const int grid = (int)((waves + 3) / 4);
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL(qjl_outlier_kernel<64>, grid, 256, 0, s, a); break;
+    case 128: hipLaunchKernelGGL(qjl_outlier_kernel<128>, grid, 256, 0, s, a); break;
+    case 256: hipLaunchKernelGGL(qjl_outlier_kernel<256>, grid, 256, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.n_q + 15) / 16), (unsigned)((a.m + 15) / 16));
   hipLaunchKernelGGL(qjl_project_kernel, grid, 64, 0, s, a);
@@ -1720,8 +1818,11 @@ hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s) {
   const int grid = (int)(per_group * groups);
   const int cpg = (int)per_group;
   switch (a.m >> 6) {
-#define PQ_SCORE_CASE(K) \
-    case K: hipLaunchKernelGGL(qjl_score_kernel<K>, grid, kThreads, 0, s, a, cpg); break;
+#define PQ_SCORE_CASE(K)                                                                          \
+    case K:                                                                                       \
+      if (a.accumulate) hipLaunchKernelGGL((qjl_score_kernel<K, true>), grid, kThreads, 0, s, a, cpg); \
+      else hipLaunchKernelGGL((qjl_score_kernel<K, false>), grid, kThreads, 0, s, a, cpg);             \
+      break;
     PQ_SCORE_CASE(1) PQ_SCORE_CASE(2) PQ_SCORE_CASE(3) PQ_SCORE_CASE(4)
     PQ_SCORE_CASE(5) PQ_SCORE_CASE(6) PQ_SCORE_CASE(7) PQ_SCORE_CASE(8)
     PQ_SCORE_CASE(9) PQ_SCORE_CASE(10) PQ_SCORE_CASE(11) PQ_SCORE_CASE(12)

@@ -178,3 +178,26 @@ def test_packed_score_validates_like_score():
     assert lib.pq_score_packed(256, 5, 256, 2, 16, 64, *args) == pq.PQ_EUNSUPPORTED       # bits > 4
     assert lib.pq_score_packed(100, 3, 0, 2, 16, 64, P16, P16, P16, NUL, NUL, P16, NUL) == pq.PQ_EINVAL
     assert lib.pq_score_packed(256, 3, 256, 2, 17, 64, *args) == pq.PQ_EINVAL             # n_q > 16
+
+
+def test_outlier_entry_points_validate():
+    lib = pq.lib()
+    # qjl_outlier_channels(d, keys, heads, seq_len, group_size, n_out, idx, stream)
+    assert lib.qjl_outlier_channels(128, P16, 0, 64, 32, 8, P16, NUL) == pq.PQ_OK
+    assert lib.qjl_outlier_channels(512, P16, 2, 64, 32, 8, P16, NUL) == pq.PQ_EUNSUPPORTED
+    assert lib.qjl_outlier_channels(96, P16, 2, 64, 32, 8, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_outlier_channels(128, P16, 2, 64, 0, 8, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_outlier_channels(128, P16, 2, 64, 32, 0, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_outlier_channels(128, P16, 2, 64, 32, 129, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_outlier_channels(128, NUL, 2, 64, 32, 8, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_outlier_channels(128, P2, 2, 64, 32, 8, P16, NUL) == pq.PQ_EINVAL
+    # qjl_sketch_split(d, m, keys, heads, seq_len, gs, n_out, idx, part, proj, bits, norms, stream)
+    assert lib.qjl_sketch_split(128, 256, P16, 2, 0, 32, 8, P16, 0, P16, P16, P16, NUL) == pq.PQ_OK
+    assert lib.qjl_sketch_split(128, 256, P16, 2, 64, 32, 8, P16, 2, P16, P16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_sketch_split(128, 12, P16, 2, 64, 32, 8, P16, 0, P16, P16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_sketch_split(512, 256, P16, 2, 64, 32, 8, P16, 0, P16, P16, P16, NUL) == pq.PQ_EUNSUPPORTED
+    assert lib.qjl_sketch_split(128, 256, P16, 2, 64, 32, 8, NUL, 1, P16, P16, P16, NUL) == pq.PQ_EINVAL
+    # qjl_score_add validates as qjl_score
+    assert lib.qjl_score_add(256, 4, 8, 32, 0, P16, P16, P16, P16, NUL) == pq.PQ_OK
+    assert lib.qjl_score_add(256, 4, 8, 30, 64, P16, P16, P16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.qjl_score_add(256, 4, 8, 64, 64, P16, P16, P16, P16, NUL) == pq.PQ_EUNSUPPORTED
