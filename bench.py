@@ -228,7 +228,39 @@ def qjl_leg(pq, synth, torch, steps, warmup):
     sk_bytes = n_keys * d * 2 + n_keys * (m // 8) + n_keys * 2
     sc_bytes = n_keys * (m // 8) + n_keys * 2 + B * Hq * T * 4 + B * Hq * m * 4
     sk_flops = 2.0 * n_keys * d * m
+
+    # outlier channels (group of 32 tokens, top 8, their own 256-row projection): channel
+    # selection, the inlier and outlier sketches, and the two-term score
+    gs, n_out, m_o = 32, 8, 256
+    Go = torch.from_numpy(synth.projection(synth.BASE_SEED + 1000, m_o, d).view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = [k.view(B * Hkv, T, d) for k in key_sets]
+    oidx = [pq.qjl_outlier_channels(kv[i], gs, n_out) for i in range(2)]
+    sp_in = [(torch.empty_like(bits0), torch.empty_like(norms0)) for _ in range(2)]
+    sp_out = [(torch.empty((n_keys, m_o // 8), dtype=torch.uint8, device=dev), torch.empty_like(norms0))
+              for _ in range(2)]
+    sqo = pq.qjl_project(q, Go)
+
+    def outliers(k):
+        pq.qjl_outlier_channels(kv[k % 2], gs, n_out, out=oidx[k % 2])
+
+    def split_sketch(k):
+        pq.qjl_sketch(kv[k % 2], G, out=sp_in[k % 2], split=(oidx[k % 2], T, gs, 0))
+        pq.qjl_sketch(kv[k % 2], Go, out=sp_out[k % 2], split=(oidx[k % 2], T, gs, 1))
+
+    def split_score(k):
+        pq.qjl_score(sq, *sp_in[k % 2], B, Hkv, Hq, T, out=scores[k % 2])
+        pq.qjl_score(sqo, *sp_out[k % 2], B, Hkv, Hq, T, out=scores[k % 2], accumulate=True)
+
+    outliers(0), split_sketch(0), split_score(0)
+    t_oc = timed(torch, outliers, steps)
+    t_ss = timed(torch, split_sketch, steps)
+    t_so = timed(torch, split_score, steps)
     return {
+        "qjl_outlier_config": "config4 keys, outlier channels: groups of 32 tokens, top 8 channels, "
+                              "256-row outlier projection; inlier and outlier sketch, two-term score",
+        "qjl_outlier_channels_us": round(t_oc * 1e6, 3),
+        "qjl_split_sketch_us": round(t_ss * 1e6, 3), "qjl_split_score_us": round(t_so * 1e6, 3),
+        "qjl_split_score_keys_per_s": round(n_keys / t_so, 1),
         "qjl_config": "config4: keys 4x8x32768x128 bf16, m=256, 32 query heads (GQA 4:1)",
         "qjl_sketch_us": round(t_sk * 1e6, 3), "qjl_sketch_keys_per_s": round(n_keys / t_sk, 1),
         "qjl_sketch_hbm_frac": round(sk_bytes / t_sk / 1e9 / HBM_PEAK_GBS, 4),

@@ -1027,12 +1027,23 @@ __global__ __launch_bounds__(256) void qjl_outlier_kernel(const pqi::OutlierArgs
 #pragma unroll
   for (int c = 0; c < CPL; ++c) ss[c] = 0.0f;
   const uint16_t* base = a.keys + (head * a.seq_len) * D + CPL * lane;
-  for (int64_t t = t0; t < t1; ++t) {
-    const uint16_t* p = base + t * D;
+  // eight tokens' loads in flight at a time (clamped to the group, masked when past it)
+  for (int64_t t = t0; t < t1; t += 8) {
+    uint16_t x[8][CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float v = bf16_to_f32(p[c]);
-      ss[c] = fmaf(v, v, ss[c]);
+    for (int u = 0; u < 8; ++u) {
+      const uint16_t* p = base + min(t + u, t1 - 1) * D;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) x[u][c] = p[c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = t + u < t1 ? 1.0f : 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float v = bf16_to_f32(x[u][c]) * w;
+        ss[c] = fmaf(v, v, ss[c]);
+      }
     }
   }
   uint32_t taken = 0;
