@@ -403,8 +403,8 @@ def main():
         summarize(args.summarize)
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the codec shards by blocks with no exchange, see DESIGN.md)" % args.gpus, file=sys.stderr)
+        print("bench.py: runs on one GPU only; --gpus %d is not supported "
+              "(the codec would shard by blocks, with no exchange between GPUs)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
