@@ -209,3 +209,76 @@ def test_single_launch_beyond_4gib():
     parity.check_quantize(xs, bits, D, codes[sel].cpu().numpy(), parity.f16_values(norms[sel]), label="4GiB")
     parity.check_dequantize(codes[sel].cpu().numpy(), parity.f16_values(norms[sel]), bits, D,
                             out[sel].float().cpu().numpy().astype(np.float64), True, label="4GiB dq")
+
+
+@pytest.mark.parametrize("d", [256, 512])
+def test_config5_packed_full(d):
+    """Config 5 with the 3-bit codes bit-packed: the packed quantize equals the byte-code one
+    packed by the oracle (sampled blocks), and dequantize and two-stage scores from the
+    packed codes equal the byte-code results over the whole tensor."""
+    from oracle import codec
+    _case("config5 packed d=%d full" % d)
+    c = synth.config5_tensor(d)
+    H, T, _ = c["x"].shape
+    n_q, bits, m = c["q"].shape[1], c["bits"], c["m"]
+    st = parity.u8_tensor(c["signs"])
+    Gt = parity.bf16_tensor(c["G"])
+    x = parity.bf16_tensor(c["x"])
+    codes, norms, qb, rn = pq.quantize(x, d, bits, st, Gt)
+    pk, norms_p, qb_p, rn_p = pq.quantize(x, d, bits, st, Gt, packed=True)
+    assert torch.equal(norms, norms_p) and torch.equal(qb, qb_p) and torch.equal(rn, rn_p)
+    assert torch.equal(pq.dequantize(pk, norms, d, bits, st, packed=True), pq.dequantize(codes, norms, d, bits, st))
+    prep = pq.query_prep(parity.bf16_tensor(c["q"]), st, Gt)
+    s_b = pq.score(prep, codes, norms, d, bits, H, n_q, T, qb, rn, m=m)
+    s_p = pq.score(prep, pk, norms, d, bits, H, n_q, T, qb, rn, m=m, packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s_b, s_p)
+    n = codes.shape[0]
+    idx = _sample(n, 2000, 90 + d)
+    sel = torch.from_numpy(idx).cuda()
+    assert np.array_equal(pk[sel].cpu().numpy(), codec.pack_codes(codes[sel].cpu().numpy(), bits))
+
+
+def test_config4_outliers_full_sampled():
+    """Config-4 keys (4 x 8 x 32768 x 128) with outlier channels (groups of 32 tokens, top 8,
+    a 256-row outlier projection): sampled groups, keys and scores against the oracle."""
+    from tests.test_gpu_outliers import _check_outliers
+    _case("config4 outliers full: groups of 32, top 8, m_o=256")
+    c = synth.config4()
+    B, Hkv, T, d = c["keys"].shape
+    Hq, m = c["q"].shape[1], c["m"]
+    gs, n_out, m_o = 32, 8, 256
+    Gou = synth.projection(synth.BASE_SEED + 1000, m_o, d)
+    kt = parity.bf16_tensor(c["keys"]).view(B * Hkv, T, d)
+    Gt, Got = parity.bf16_tensor(c["G"]), parity.bf16_tensor(Gou)
+    idx = pq.qjl_outlier_channels(kt, gs, n_out)
+    b_in, n_in = pq.qjl_sketch(kt, Gt, split=(idx, T, gs, 0))
+    b_out, n_o = pq.qjl_sketch(kt, Got, split=(idx, T, gs, 1))
+    qt = parity.bf16_tensor(c["q"])
+    sc = pq.qjl_score(pq.qjl_project(qt, Gt), b_in, n_in, B, Hkv, Hq, T)
+    sc = pq.qjl_score(pq.qjl_project(qt, Got), b_out, n_o, B, Hkv, Hq, T, out=sc, accumulate=True)
+    torch.cuda.synchronize()
+    G, Go = numerics.bf16_from_bits(c["G"]), numerics.bf16_from_bits(Gou)
+    q = numerics.bf16_from_bits(c["q"])
+    n_groups = T // gs
+    gi = idx.cpu().numpy()
+    rng = np.random.default_rng(44)
+    for hh in (0, 5, B * Hkv - 1):
+        b, g = divmod(hh, Hkv)
+        groups = np.unique(np.concatenate([[0, n_groups - 1], rng.integers(0, n_groups, 40)]))
+        toks = np.concatenate([np.arange(gg * gs, (gg + 1) * gs) for gg in groups])
+        keys = numerics.bf16_from_bits(c["keys"][b, g][toks])
+        sub_idx = gi[hh][groups]
+        _check_outliers(keys, sub_idx, gs, n_out, "config4 head %d" % hh)
+        sk = qjl.split_sketch(keys, sub_idx, gs, G, Go)
+        tsel = torch.from_numpy(hh * T + toks).cuda()
+        bi, ni = b_in[tsel].cpu().numpy(), parity.f16_values(n_in[tsel])
+        bo, no = b_out[tsel].cpu().numpy(), parity.f16_values(n_o[tsel])
+        parity.check_sketch(sk["k_in"], G, bi, ni, label="config4 inliers h%d" % hh)
+        parity.check_sketch(sk["k_out"], Go, bo, no, label="config4 outliers h%d" % hh)
+        got = sc[b][:, torch.from_numpy(toks).cuda()].cpu().numpy().astype(np.float64)
+        for h in range(g * (Hq // Hkv), (g + 1) * (Hq // Hkv)):
+            Sq, Soq = (G @ q[b, h])[None, :], (Go @ q[b, h])[None, :]
+            ref = qjl.estimate(bi, ni, Sq, m)[0] + qjl.estimate(bo, no, Soq, m_o)[0]
+            scale = qjl.estimate_scale(ni, Sq, m)[0] + qjl.estimate_scale(no, Soq, m_o)[0]
+            parity.check_scores(got[h], ref, np.maximum(scale, 1e-30), label="config4 split score b%d h%d" % (b, h))
