@@ -20,6 +20,9 @@ order and notation, in float64, with no blocking or fusion:
 * ``qjl``        - QJL key sketch, the asymmetric inner-product estimator and
   the two-stage estimator (eliza quantization README, QJL, "Algorithm in one paragraph";
   qjl_apply.py, ``_qjl_decode_keys`` for the bit order).
+* ``attention``  - decode attention over the quantized cache plus an unquantized recent
+  window (eliza quantization README, TurboQuant and Fused TurboQuant; glq 0.7.2 README,
+  "Inline-dequant E8 KV").
 * ``numerics``   - IEEE round-to-nearest-even to fp16 / bf16 / fp32 and the
   LSB-first bit packing.
 
@@ -27,4 +30,4 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, textbook identities or brute force.
 """
 
-from . import numerics, lloyd_max, hadamard, codec, qjl  # noqa: F401
+from . import numerics, lloyd_max, hadamard, codec, qjl, attention  # noqa: F401
