@@ -266,6 +266,60 @@ int pq_score_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok,
                     const uint8_t* codes, const uint16_t* norms, const uint8_t* qjl_bits,
                     const uint16_t* rnorms, float* scores, void* stream);
 
+/*
+ * Decode attention over the quantized cache plus an unquantized recent window, fused
+ * (eliza quantization README, TurboQuant, "Algorithm in one paragraph": the cache holds
+ * codes and norms, decoded by centroid lookup and inverse rotation at attention time, the
+ * last residual_length tokens unquantized; same README, "Fused TurboQuant": scores straight
+ * from the stored codes; glq 0.7.2 README, "Inline-dequant E8 KV": K/V decoded inside the
+ * attention kernel, each read once, no workspace of decoded vectors).  For every head h and
+ * query row i < n_q:
+ *   s_t = the pq_score estimate of <q, k_t> (t < n_tok), s_w = <q, k_win[w]> (w < n_win),
+ *   p   = softmax(sm_scale * [s_t ; s_w]),
+ *   out[h][i] = sum_t p_t dequantize(v_t) + sum_w p_w v_win[w].
+ * The value codes are read once and never decoded to memory: the kernel sums
+ * p_t n16_t / d c[code_t] in the rotated basis and rotates back once per query.
+ *
+ * pq_attention_work_bytes: bytes of the work buffer (partial maxima, sums and rotated
+ * outputs of the fused kernel; 0 when n_tok == 0, -1 for invalid arguments).
+ *
+ * pq_attention:
+ *   d, bits, m  the codec of the keys (bits 1..4; m = 0: no QJL residual); the values
+ *               use the same d and bits without a residual
+ *   prep        pq_query_prep of q with the KEY signs (and G when m > 0)
+ *   k_codes     n_heads * n_tok * d bytes [head][token][d], 16-byte aligned
+ *   k_norms     n_heads * n_tok fp16; k_qjl_bits n_heads * n_tok * m/8 bytes and
+ *               k_rnorms n_heads * n_tok fp16 (both NULL when m == 0)
+ *   v_codes, v_norms  the values, as k_codes and k_norms (pq_quantize with m = 0)
+ *   v_signs     the rotation sign mask of the values, d/8 bytes of device memory
+ *   n_win       window tokens, 0 .. 4096; k_win, v_win bf16 [head][n_win][d], q the
+ *               bf16 queries [head][n_q][d] (all three may be NULL when n_win == 0)
+ *   sm_scale    softmax scale (finite; 1/sqrt(d) in the usual attention)
+ *   work        pq_attention_work_bytes(d, n_heads, n_tok) bytes, 16-byte aligned,
+ *               device memory; its contents on entry do not matter
+ *   out         n_heads * n_q * d fp32, layout [head][query][d]
+ * n_tok + n_win must be at least 1 (PQ_EINVAL); n_q <= 16 per call.  All device pointers
+ * are caller-owned; the call is asynchronous on `stream` and allocates nothing.  Scores
+ * carry pq_score's precision; the probabilities and centroids enter the matrix cores as
+ * fp16 pairs (about 22 significant bits) and accumulate in fp32; merging in double.
+ */
+int64_t pq_attention_work_bytes(int d, int n_heads, int64_t n_tok);
+int pq_attention(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                 const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits, const uint16_t* k_rnorms,
+                 const uint8_t* v_codes, const uint16_t* v_norms, const uint8_t* v_signs, int64_t n_win,
+                 const uint16_t* k_win, const uint16_t* v_win, const uint16_t* q, float sm_scale, void* work,
+                 float* out, void* stream);
+
+/*
+ * pq_attention over bit-packed key and value codes (d*bits/8 bytes per token, as written
+ * by pq_quantize_packed; eliza README, TurboQuant, "Algorithm in one paragraph", step 4).
+ */
+int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                        const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits,
+                        const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,
+                        const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
+                        const uint16_t* q, float sm_scale, void* work, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

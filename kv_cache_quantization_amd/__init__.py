@@ -55,6 +55,10 @@ def _load():
         "pq_query_prep": ([I, I, I, I, P, P, P, P, P], I),
         "pq_score": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
         "pq_score_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
+        "pq_attention_work_bytes": ([I, I, L], L),
+        "pq_attention": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P], I),
+        "pq_attention_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P],
+                                I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -67,7 +71,8 @@ _lib = _load()
 EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_quantize",
            "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
            "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
-           "pq_query_prep", "pq_score", "pq_score_packed")
+           "pq_query_prep", "pq_score", "pq_score_packed", "pq_attention_work_bytes", "pq_attention",
+           "pq_attention_packed")
 
 
 def lib():
@@ -282,4 +287,63 @@ def score(prep, codes, norms, d, bits, n_heads, n_q, n_tok, qjl_bits=None, rnorm
     fn, name = (_lib.pq_score_packed, "pq_score_packed") if packed else (_lib.pq_score, "pq_score")
     _check(fn(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(codes), _ptr(norms), _ptr(qjl_bits),
               _ptr(rnorms), _ptr(out), _stream()), name)
+    return out
+
+
+def attention_work_bytes(d, n_heads, n_tok):
+    """Bytes of the work buffer ``attention`` needs (partial results of the fused kernel)."""
+    nb = _lib.pq_attention_work_bytes(d, n_heads, n_tok)
+    if nb < 0:
+        raise PQError(PQ_EINVAL, "pq_attention_work_bytes")
+    return nb
+
+
+def attention(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m=0, k_win=None, v_win=None,
+              q=None, sm_scale=None, packed=False, work=None, out=None):
+    """Decode attention over a quantized cache plus an unquantized recent window.
+
+    prep: ``query_prep`` of the queries with the key signs (and G when m > 0).
+    keys: (codes, norms, qjl_bits, rnorms) of the quantized keys, [n_heads, n_tok, ...]
+    (qjl_bits and rnorms None when m == 0); values: (codes, norms), quantized without QJL.
+    k_win, v_win: bf16 [n_heads, n_win, d] (or None); q: the bf16 queries [n_heads, n_q, d],
+    needed with a window.  Returns fp32 [n_heads, n_q, d]; sm_scale defaults to 1/sqrt(d).
+    ``packed``: codes bit-packed at the code width (pq_attention_packed).
+    """
+    k_codes, k_norms, k_bits, k_rn = keys
+    v_codes, v_norms = values
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _dev(t, name, (torch.uint8,))
+        if n_tok and t.numel() != n_heads * n_tok * (d * bits // 8 if packed else d):
+            raise ValueError("%s do not match n_heads, n_tok, d" % name)
+    _dev(k_norms, "k_norms", (torch.float16,))
+    _dev(v_norms, "v_norms", (torch.float16,))
+    _dev(v_signs, "v_signs", (torch.uint8,))
+    if n_tok:
+        _dev(prep, "prep", (torch.uint8,))
+    if m:
+        _dev(k_bits, "k_qjl_bits", (torch.uint8,))
+        _dev(k_rn, "k_rnorms", (torch.float16,))
+    n_win = 0
+    if k_win is not None:
+        _dev(k_win, "k_win", (torch.bfloat16,))
+        _dev(v_win, "v_win", (torch.bfloat16,))
+        _dev(q, "q", (torch.bfloat16,))
+        n_win = k_win.shape[1]
+        if k_win.shape != (n_heads, n_win, d) or v_win.shape != k_win.shape or q.shape != (n_heads, n_q, d):
+            raise ValueError("window or query shape does not match n_heads, n_q, d")
+    if sm_scale is None:
+        sm_scale = 1.0 / float(d) ** 0.5
+    dev = v_codes.device
+    if work is None:
+        work = torch.empty((max(16, attention_work_bytes(d, n_heads, n_tok)),), dtype=torch.uint8, device=dev)
+    _dev(work, "work", (torch.uint8,))
+    if work.numel() < attention_work_bytes(d, n_heads, n_tok):
+        raise ValueError("work buffer too small")
+    if out is None:
+        out = torch.empty((n_heads, n_q, d), dtype=torch.float32, device=dev)
+    _dev(out, "out", (torch.float32,))
+    fn, name = (_lib.pq_attention_packed, "pq_attention_packed") if packed else (_lib.pq_attention, "pq_attention")
+    _check(fn(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(k_codes), _ptr(k_norms), _ptr(k_bits), _ptr(k_rn),
+              _ptr(v_codes), _ptr(v_norms), _ptr(v_signs), n_win, _ptr(k_win), _ptr(v_win), _ptr(q),
+              float(sm_scale), _ptr(work), _ptr(out), _stream()), name)
     return out

@@ -441,4 +441,84 @@ int pq_score_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok,
   return score_impl(d, bits, m, n_heads, n_q, n_tok, prep, codes, norms, qjl_bits, rnorms, scores, 1, stream);
 }
 
+int64_t pq_attention_work_bytes(int d, int n_heads, int64_t n_tok) {
+  if (check_d(d) || n_heads < 0 || n_heads > INT32_MAX / pqi::kScoreRows || n_tok < 0) return -1;
+  if (n_tok > kMaxElems / ((int64_t)d * (n_heads + 1))) return -1;
+  return pqi::attn_work_bytes(d, n_heads, n_tok);
+}
+
+static int attention_impl(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                          const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits,
+                          const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,
+                          const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
+                          const uint16_t* q, float sm_scale, void* work, float* out, int packed, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (bits > pqi::kMaxScoreBits) return PQ_EUNSUPPORTED;
+  if (m < 0 || (m % 8) != 0) return PQ_EINVAL;
+  if ((m % 64) != 0 || m > 1024) return PQ_EUNSUPPORTED;
+  if (pqi::prep_head_bytes(d, m) - pqi::prep_off_meta(d, m) > 65536) return PQ_EUNSUPPORTED;
+  if (n_heads < 0 || n_heads > INT32_MAX / pqi::kScoreRows || n_q < 0 || n_q > pqi::kScoreRows) return PQ_EINVAL;
+  if (n_tok < 0 || n_win < 0) return PQ_EINVAL;
+  if (n_tok > kMaxElems / ((int64_t)d * (n_heads + 1))) return PQ_EINVAL;
+  if (n_win > pqi::kAttnMaxWin) return PQ_EUNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return PQ_EINVAL;
+  if (m == 0 && (k_qjl_bits || k_rnorms)) return PQ_EINVAL;
+  if (n_heads == 0 || n_q == 0) return PQ_OK;
+  if (n_tok + n_win == 0) return PQ_EINVAL;             // softmax over no token
+  if (!v_signs || !out) return PQ_EINVAL;
+  if (n_tok > 0) {
+    if (!prep || !k_codes || !k_norms || !v_codes || !v_norms || !work) return PQ_EINVAL;
+    if (m > 0 && (!k_qjl_bits || !k_rnorms)) return PQ_EINVAL;
+    if (!aligned(prep, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_norms, 2) ||
+        !aligned(v_norms, 2) || !aligned(work, 16))
+      return PQ_EINVAL;
+    if (m > 0 && (!aligned(k_qjl_bits, 2) || !aligned(k_rnorms, 2))) return PQ_EINVAL;
+  }
+  if (n_win > 0 && (!k_win || !v_win || !q || !aligned(k_win, 2) || !aligned(v_win, 2) || !aligned(q, 2)))
+    return PQ_EINVAL;
+  if (!aligned(out, 4)) return PQ_EINVAL;
+  const pqi::AttnPlan plan = pqi::attn_plan(d, n_heads, n_tok);
+  pqi::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.prep = static_cast<const unsigned char*>(prep);
+  a.k_codes = k_codes; a.k_norms = k_norms; a.k_qbits = k_qjl_bits; a.k_rnorms = k_rnorms;
+  a.v_codes = v_codes; a.v_norms = v_norms; a.v_signs = v_signs;
+  a.k_win = k_win; a.v_win = v_win; a.q = q; a.out = out;
+  a.work_ml = static_cast<float*>(work);
+  a.work_o = plan.n_ranges ? a.work_ml + (int64_t)n_heads * plan.n_ranges * pqi::kScoreRows * 2 : nullptr;
+  a.n_tok = n_tok; a.n_win = n_win; a.tiles_per_range = plan.tiles_per_range;
+  a.n_heads = n_heads; a.n_q = n_q; a.m = m; a.n_ranges = plan.n_ranges; a.packed = packed;
+  a.scale_log2 = (double)sm_scale * 1.4426950408889634;          // log2(e)
+  const Codebook& cb = codebook(bits);
+  const int L = 1 << bits;
+  for (int p = 0; p < (L >> 1); ++p) {
+    const uint32_t mask = pqi::plane_mask(bits, p);
+    double acc = 0.0;
+    for (int k = 0; k < L; ++k) acc += (__builtin_popcount((uint32_t)k & mask) & 1) ? cb.c[k] : -cb.c[k];
+    a.alpha[p] = acc / (double)L;
+  }
+  for (int k = 0; k < L; ++k) a.vcent[k] = (float)cb.c[k];
+  return hip_status(pqi::launch_attention(d, bits, a, (hipStream_t)stream));
+}
+
+int pq_attention(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                 const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits, const uint16_t* k_rnorms,
+                 const uint8_t* v_codes, const uint16_t* v_norms, const uint8_t* v_signs, int64_t n_win,
+                 const uint16_t* k_win, const uint16_t* v_win, const uint16_t* q, float sm_scale, void* work,
+                 float* out, void* stream) {
+  return attention_impl(d, bits, m, n_heads, n_q, n_tok, prep, k_codes, k_norms, k_qjl_bits, k_rnorms, v_codes,
+                        v_norms, v_signs, n_win, k_win, v_win, q, sm_scale, work, out, 0, stream);
+}
+
+int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                        const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits,
+                        const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,
+                        const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
+                        const uint16_t* q, float sm_scale, void* work, float* out, void* stream) {
+  return attention_impl(d, bits, m, n_heads, n_q, n_tok, prep, k_codes, k_norms, k_qjl_bits, k_rnorms, v_codes,
+                        v_norms, v_signs, n_win, k_win, v_win, q, sm_scale, work, out, 1, stream);
+}
+
 }  // extern "C"

@@ -153,6 +153,62 @@ struct TwoStageArgs {
   double alpha[kMaxPlanes];
 };
 
+// Decode attention over the quantized cache.  The fused kernel gives each wave a range of
+// tiles_per_range 16-token tiles of one KV head and one slice of attn_cols(d) value columns;
+// each (head, range) leaves a partial result in the work buffer:
+//   ml  float2[n_heads][n_ranges][16]      running max (base-2 logits) and sum of exp2
+//   o   float[n_heads][n_ranges][16][d]    sum_t exp2(z_t - max) n16_t / d c[code_t], rotated basis
+// and the combine kernel merges them with the window and rotates back.
+constexpr int kAttnMaxWin = 4096;         // window tokens held in LDS by the combine kernel
+constexpr int kAttnTargetWaves = 2048;    // fused-kernel waves aimed for over all heads
+
+__host__ __device__ constexpr int attn_cols(int d) { return d <= 128 ? d : 128; }
+
+struct AttnPlan {
+  int n_ranges;              // per head
+  int64_t tiles_per_range;
+};
+
+inline AttnPlan attn_plan(int d, int n_heads, int64_t n_tok) {
+  AttnPlan p{0, 0};
+  const int64_t n_tiles = (n_tok + 15) >> 4;
+  if (n_tiles == 0 || n_heads <= 0) return p;
+  const int64_t slices = d / attn_cols(d);
+  int64_t want = kAttnTargetWaves / ((int64_t)n_heads * slices);
+  if (want < 1) want = 1;
+  if (want > n_tiles) want = n_tiles;
+  p.tiles_per_range = (n_tiles + want - 1) / want;
+  p.n_ranges = (int)((n_tiles + p.tiles_per_range - 1) / p.tiles_per_range);
+  return p;
+}
+
+inline int64_t attn_work_bytes(int d, int n_heads, int64_t n_tok) {
+  const AttnPlan p = attn_plan(d, n_heads, n_tok);
+  return (int64_t)n_heads * p.n_ranges * kScoreRows * (8 + (int64_t)d * 4);
+}
+
+struct AttnArgs {
+  const unsigned char* prep;  // pq_query_prep of the queries with the key signs (and G)
+  const uint8_t* k_codes;     // [n_heads][n_tok][d] (packed: [n_heads][n_tok][d*bits/8])
+  const uint16_t* k_norms;    // [n_heads][n_tok] fp16
+  const uint8_t* k_qbits;     // [n_heads][n_tok][m/8]
+  const uint16_t* k_rnorms;   // [n_heads][n_tok] fp16
+  const uint8_t* v_codes;     // like k_codes
+  const uint16_t* v_norms;    // [n_heads][n_tok] fp16
+  const uint8_t* v_signs;     // d/8 bytes
+  const uint16_t* k_win;      // [n_heads][n_win][d] bf16
+  const uint16_t* v_win;      // [n_heads][n_win][d] bf16
+  const uint16_t* q;          // [n_heads][n_q][d] bf16
+  float* work_ml;             // partial maxima and sums
+  float* work_o;              // partial outputs
+  float* out;                 // [n_heads][n_q][d] fp32
+  int64_t n_tok, n_win, tiles_per_range;
+  int n_heads, n_q, m, n_ranges, packed;
+  double scale_log2;          // softmax scale times log2(e)
+  double alpha[kMaxPlanes];   // key codebook, odd-Walsh coefficients (as TwoStageArgs)
+  float vcent[1 << kMaxScoreBits];   // value codebook centroids
+};
+
 struct LaunchCfg {
   int cu_count;
   int max_lds;       // bytes of LDS one workgroup may use
@@ -168,5 +224,6 @@ hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s);
 hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_attention(int d, int bits, const AttnArgs& a, hipStream_t s);
 
 }  // namespace pqi

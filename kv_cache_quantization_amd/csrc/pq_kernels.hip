@@ -1564,6 +1564,352 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
 }
 
 // ------------------------------------------------------------------------------------------
+// Decode attention over the quantized cache, fused: every key code is scored and every value
+// code accumulated in one pass, and nothing is decoded to memory.
+//
+// A wave takes a range of 16-token tiles of one KV head, the head's 16 query rows and one
+// slice of attn_cols(d) value columns.  The scores are the two-stage products above with the
+// operands swapped, so they come out transposed: lane (query c = lane & 15, g = lane >> 4)
+// holds the scores of tokens 4 g + i, i = 0..3, which is the A-operand layout of
+// v_mfma_f32_16x16x16_f16 for the probability tile P[query][token].  The dequantized value is
+// linear in its centroid vector, so
+//     sum_t p_t vhat_t = D . H (sum_t p_t n16_t / d . c[code_t]),
+// and the wave accumulates O = P' C on the matrix cores in the rotated basis
+// (P'[q][t] = p_qt n16_t / d, C[t][e] = c[code_te]); the combine kernel applies the inverse
+// rotation once per query.  P' and C enter as fp16 hi + lo pairs (products hi.hi + hi.lo +
+// lo.hi), about 22 significant bits each.  Value column e of N-tile j sits in lane n = lane & 15
+// as e = (d/16) n + slice * NT + j, so a lane reads NT consecutive codes of a token.  Softmax
+// is online in base 2 (logits times log2 e).
+// ------------------------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+__device__ __forceinline__ uint32_t f16_split_pair(float x0, float x1, uint32_t& lo) {
+  const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+  const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+  lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+}
+
+__device__ __forceinline__ f16x4 as_f16x4(uint32_t w0, uint32_t w1) {
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+  return __builtin_bit_cast(f16x4, (u32x2){w0, w1});
+}
+
+template <int D, int BITS, int KQT, bool PK>
+__global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs a, int waves_per_head) {
+  constexpr int KC = D / 64;
+  constexpr int NP = 1 << (BITS - 1);
+  constexpr bool QJL = KQT != 0;
+  constexpr int KQB = KQT > 0 ? KQT : 1;
+  constexpr int DC = pqi::attn_cols(D), CS = D / DC, NT = DC / 16, RUN = D / 16;
+  constexpr uint32_t CMASK = (1u << BITS) - 1u;
+  const int m = QJL ? a.m : 0;
+  const int KQ = m >> 6, mb = m >> 3;
+  const int wg_per_head = (waves_per_head + kWaves - 1) / kWaves;
+  const int head = blockIdx.x / wg_per_head;
+  const int wih = (blockIdx.x % wg_per_head) * kWaves + (int)(threadIdx.x >> 6);
+  const int range = wih / CS, cs = wih % CS;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int64_t meta = pqi::prep_off_meta(D, m);
+  const int nbytes = (int)(pqi::prep_head_bytes(D, m) - meta);
+  {
+    const uint4* s4 = reinterpret_cast<const uint4*>(a.prep + (int64_t)head * pqi::prep_head_bytes(D, m) + meta);
+    uint4* d4 = reinterpret_cast<uint4*>(smem);
+    for (int i = threadIdx.x; i < nbytes / 16; i += blockDim.x) d4[i] = s4[i];
+  }
+  // value centroids as fp16 pairs, hi | lo << 16
+  uint32_t* tab = reinterpret_cast<uint32_t*>(smem + nbytes);
+  if (threadIdx.x < (1 << BITS)) {
+    uint32_t lo;
+    const uint32_t hi = f16_split_pair(a.vcent[threadIdx.x], 0.0f, lo);
+    tab[threadIdx.x] = (hi & 0xffffu) | (lo << 16);
+  }
+  __syncthreads();
+  if (wih >= waves_per_head) return;
+
+  const float* scale = reinterpret_cast<const float*>(smem);
+  const int* isum = reinterpret_cast<const int*>(smem + 128);
+  const i32x4* fc = reinterpret_cast<const i32x4*>(smem + 256);
+  const i32x4* fq = fc + 3 * KC * 64;
+
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t T = a.n_tok;
+  const int64_t n_tiles = (T + 15) >> 4;
+  const int64_t t_begin = (int64_t)range * a.tiles_per_range;
+  const int64_t t_end = min(n_tiles, t_begin + a.tiles_per_range);
+  const int64_t hoff = (int64_t)head * T;
+  constexpr int RB = PK ? D * BITS / 8 : D;              // code bytes of a token
+  const uint8_t* kcodes = a.k_codes + hoff * RB;
+  const uint8_t* vcodes = a.v_codes + hoff * RB;
+  const uint16_t* knorms = a.k_norms + hoff;
+  const uint16_t* vnorms = a.v_norms + hoff;
+  const uint8_t* qbits = QJL ? a.k_qbits + hoff * mb : nullptr;
+  const uint16_t* rnorms = QJL ? a.k_rnorms + hoff : nullptr;
+  const double cq = QJL ? 1.2533141373155003 / (double)m : 0.0;     // sqrt(pi/2) / m
+
+  // one tile's inputs; tokens past the end are clamped to the last token (always in bounds),
+  // and their probabilities are set to zero
+  constexpr int PW = PK ? (2 * BITS + 3) / 4 : 4;       // dwords of a lane's 16 key codes
+  constexpr int VW = PK ? 1 : NT / 4;                    // dwords of a lane's NT value codes
+  struct Inputs {
+    uint32_t cw[KC][PW];
+    uint32_t qb[(KQB + 1) / 2];
+    uint32_t vr[4][VW];
+    uint32_t kn;          // key norm | residual norm << 16, token r of the tile
+    uint32_t vn;          // value norm, token r of the tile
+  };
+  auto fetch = [&](int64_t tile, Inputs& in) {
+    const int64_t tok = min(tile * 16 + r, T - 1);
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      if constexpr (PK) {
+        load_code_bytes<2 * BITS>(kcodes + tok * RB + (64 * k + 16 * g) * BITS / 8, true, in.cw[k]);
+      } else {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kcodes + tok * RB + 64 * k + 16 * g));
+        in.cw[k][0] = w.x; in.cw[k][1] = w.y; in.cw[k][2] = w.z; in.cw[k][3] = w.w;
+      }
+    }
+    in.kn = (uint32_t)knorms[tok] | (QJL ? (uint32_t)rnorms[tok] << 16 : 0u);
+    in.vn = vnorms[tok];
+    if constexpr (KQT > 0) load_key_bits<KQT>(qbits + tok * mb + (mb >> 2) * g, true, in.qb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t vt = min(tile * 16 + 4 * g + i, T - 1);
+      const int e0 = RUN * r + cs * NT;                  // first value column of the lane
+      if constexpr (PK) {
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(vcodes + vt * RB);
+        const int s = e0 * BITS;
+        const uint32_t w0 = row[s >> 5], w1 = row[(s + NT * BITS - 1) >> 5];
+        in.vr[i][0] = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)(s & 31));
+      } else if constexpr (NT == 8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(vcodes + vt * RB + e0);
+        in.vr[i][0] = w.x; in.vr[i][1] = w.y;
+      } else {
+        in.vr[i][0] = *reinterpret_cast<const uint32_t*>(vcodes + vt * RB + e0);
+      }
+    }
+  };
+
+  const float isc = scale[r], isq = QJL ? scale[16 + r] : 0.0f;
+  const int sum_c = isum[r], sum_q = QJL ? isum[16 + r] : 0;
+  float mx = -INFINITY, ls = 0.0f;
+  f32x4 o[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  Inputs nxt;
+  fetch(t_begin, nxt);                                   // every range holds at least one tile
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+    const Inputs in = nxt;
+    if (tile + 1 < t_end) fetch(tile + 1, nxt);          // uniform
+    // --- scores S^T: rows = tokens, columns = queries
+    i32x4 acc[NP][3];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int l = 0; l < 3; ++l) acc[p][l] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const i32x4 a0 = fc[(0 * KC + k) * 64 + lane];
+      const i32x4 a1 = fc[(1 * KC + k) * 64 + lane];
+      const i32x4 a2 = fc[(2 * KC + k) * 64 + lane];
+      uint4 cb;
+      if constexpr (PK) {
+        uint32_t u[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) u[i >> 2] |= stream_code<BITS>(in.cw[k], i) << (8 * (i & 3));
+        cb = make_uint4(u[0], u[1], u[2], u[3]);
+      } else {
+        cb = make_uint4(in.cw[k][0], in.cw[k][1], in.cw[k][2], in.cw[k][3]);
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const i32x4 b = plane_frag(cb, pqi::plane_mask(BITS, p));
+        acc[p][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a0, acc[p][0], 0, 0, 0);
+        acc[p][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a1, acc[p][1], 0, 0, 0);
+        acc[p][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a2, acc[p][2], 0, 0, 0);
+      }
+    }
+    i32x4 accq[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+    auto qstep = [&](int k, uint32_t w16) {
+      const i32x4 b = {(int)spread_nibble(w16 & 0xf), (int)spread_nibble((w16 >> 4) & 0xf),
+                       (int)spread_nibble((w16 >> 8) & 0xf), (int)spread_nibble(w16 >> 12)};
+      accq[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, fq[(0 * KQ + k) * 64 + lane], accq[0], 0, 0, 0);
+      accq[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, fq[(1 * KQ + k) * 64 + lane], accq[1], 0, 0, 0);
+      accq[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, fq[(2 * KQ + k) * 64 + lane], accq[2], 0, 0, 0);
+    };
+    if constexpr (KQT > 0) {
+#pragma unroll
+      for (int k = 0; k < KQT; ++k) qstep(k, (in.qb[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+    } else if constexpr (KQT < 0) {
+      const uint8_t* kb = qbits + min(tile * 16 + r, T - 1) * mb + (mb >> 2) * g;
+      for (int k = 0; k < KQ; ++k) qstep(k, *reinterpret_cast<const uint16_t*>(kb + 2 * k));
+    }
+    // --- logits of query r at tokens 4 g + i (base 2); the norms come from the lanes that
+    // fetched those tokens
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t kn = (uint32_t)__shfl((int)in.kn, 4 * g + i);
+      double first = 0.0;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const double S = 16384.0 * (double)acc[p][0][i] + 128.0 * (double)acc[p][1][i] + (double)acc[p][2][i];
+        first += a.alpha[p] * (2.0 * S - (double)sum_c);
+      }
+      double val = (double)f16_to_f32((uint16_t)(kn & 0xffffu)) / (double)D * (double)isc * first;
+      if constexpr (QJL) {
+        const double S = 16384.0 * (double)accq[0][i] + 128.0 * (double)accq[1][i] + (double)accq[2][i];
+        val += (double)f16_to_f32((uint16_t)(kn >> 16)) * cq * (double)isq * (2.0 * S - (double)sum_q);
+      }
+      z[i] = tile * 16 + 4 * g + i < T ? (float)(val * a.scale_log2) : -INFINITY;
+    }
+    // --- online softmax; every tile holds a live token, so the tile maximum is finite
+    float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(mx, mt);
+    const float al = exp2f(mx - mn);
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = exp2f(z[i] - mn);
+    ls = ls * al + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+    mx = mn;
+    if (__any(al != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(al, 4 * g + i);          // scale of query row 4 g + i
+#pragma unroll
+        for (int j = 0; j < NT; ++j) o[j][i] *= ai;
+      }
+    }
+    // --- P' = p . n16_v / d as fp16 hi + lo
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t vn = (uint32_t)__shfl((int)in.vn, 4 * g + i);
+      w[i] = pv[i] * (f16_to_f32((uint16_t)vn) * (1.0f / (float)D));
+    }
+    uint32_t pl0, pl1;
+    const uint32_t ph0 = f16_split_pair(w[0], w[1], pl0);
+    const uint32_t ph1 = f16_split_pair(w[2], w[3], pl1);
+    const f16x4 Ah = as_f16x4(ph0, ph1), Al = as_f16x4(pl0, pl1);
+    // --- O += P' C, N-tile by N-tile
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      uint32_t t4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = PK ? (in.vr[i][0] >> (BITS * j)) & CMASK : (in.vr[i][j >> 2] >> (8 * (j & 3))) & CMASK;
+        t4[i] = tab[code];
+      }
+      const f16x4 Bh = as_f16x4(__builtin_amdgcn_perm(t4[1], t4[0], 0x05040100u),
+                                __builtin_amdgcn_perm(t4[3], t4[2], 0x05040100u));
+      const f16x4 Bl = as_f16x4(__builtin_amdgcn_perm(t4[1], t4[0], 0x07060302u),
+                                __builtin_amdgcn_perm(t4[3], t4[2], 0x07060302u));
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ah, Bh, o[j], 0, 0, 0);
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ah, Bl, o[j], 0, 0, 0);
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Al, Bh, o[j], 0, 0, 0);
+    }
+  }
+  // partial result of the range: (max, sum) per query, O rows 4 g + i at the lane's columns
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  const int64_t part = (int64_t)head * a.n_ranges + range;
+  if (cs == 0 && g == 0) reinterpret_cast<float2*>(a.work_ml)[part * 16 + r] = make_float2(mx, ls);
+  float* po = a.work_o + part * 16 * D + RUN * r + cs * NT;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; j += 4)
+      *reinterpret_cast<float4*>(po + (4 * g + i) * D + j) = make_float4(o[j][i], o[j + 1][i], o[j + 2][i], o[j + 3][i]);
+}
+
+// Merge the partial results of one (head, query) with the unquantized window, rotate back and
+// normalise.  Sums in double; the window scores in fp32 (products of bf16 values are exact).
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnArgs a) {
+  const int h = blockIdx.x / a.n_q, qi = blockIdx.x % a.n_q;
+  const int R = a.n_ranges, W = (int)a.n_win;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ float x[D];
+  __shared__ float ew[pqi::kAttnMaxWin];
+  __shared__ float red_f[4];
+  __shared__ double red_d[4];
+  extern __shared__ float wr[];                          // [R] weights of the partials
+  // window logits (base 2)
+  for (int w = wv; w < W; w += 4) {
+    const uint16_t* q = a.q + ((int64_t)h * a.n_q + qi) * D;
+    const uint16_t* kw = a.k_win + ((int64_t)h * W + w) * D;
+    float s = 0.0f;
+    for (int e = lane; e < D; e += 64) s = fmaf(bf16_to_f32(q[e]), bf16_to_f32(kw[e]), s);
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) ew[w] = (float)((double)s * a.scale_log2);
+  }
+  __syncthreads();
+  const float2* ml = reinterpret_cast<const float2*>(a.work_ml) + (int64_t)h * R * 16 + qi;
+  float mloc = -INFINITY;
+  for (int t = tid; t < R; t += 256) mloc = fmaxf(mloc, ml[t * 16].x);
+  for (int t = tid; t < W; t += 256) mloc = fmaxf(mloc, ew[t]);
+  const float M = block_max(mloc, red_f);
+  double lsum = 0.0;
+  for (int t = tid; t < R; t += 256) {
+    const float2 v = ml[t * 16];
+    const float f = exp2f(v.x - M);
+    wr[t] = f;
+    lsum += (double)f * (double)v.y;
+  }
+  for (int t = tid; t < W; t += 256) {
+    const float f = exp2f(ew[t] - M);
+    ew[t] = f;
+    lsum += (double)f;
+  }
+  const double L = block_sum(lsum, red_d);               // its barriers also publish wr and ew
+  const float* po = a.work_o + (int64_t)h * R * 16 * D + (int64_t)qi * D;
+  for (int e = tid; e < D; e += 256) {
+    double acc = 0.0;
+    for (int t = 0; t < R; ++t) acc += (double)wr[t] * (double)po[(int64_t)t * 16 * D + e];
+    x[e] = (float)acc;
+  }
+  __syncthreads();
+  // inverse rotation: Walsh-Hadamard butterflies in Sylvester order, then the value signs
+  for (int half = 1; half < D; half <<= 1) {
+    for (int t = tid; t < D / 2; t += 256) {
+      const int i = (t / half) * 2 * half + (t % half);
+      const float x0 = x[i], x1 = x[i + half];
+      x[i] = x0 + x1;
+      x[i + half] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  float* out = a.out + ((int64_t)h * a.n_q + qi) * D;
+  for (int e = tid; e < D; e += 256) {
+    double acc = ((a.v_signs[e >> 3] >> (e & 7)) & 1) ? -(double)x[e] : (double)x[e];
+    const uint16_t* vw = a.v_win + (int64_t)h * W * D + e;
+    for (int w = 0; w < W; ++w) acc += (double)ew[w] * (double)bf16_to_f32(vw[(int64_t)w * D]);
+    out[e] = (float)(acc / L);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // launch helpers
 // ------------------------------------------------------------------------------------------
 int grid_for(int64_t n_tiles, const pqi::LaunchCfg& c, int per_cu) {
@@ -1696,11 +2042,45 @@ hipError_t launch_two_stage_d(int bits, const pqi::TwoStageArgs& a, int grid, in
   return hipErrorInvalidValue;
 }
 
+template <int D, int BITS, bool PK>
+hipError_t launch_attend_dbp(const pqi::AttnArgs& a, int grid, int wph, size_t lds, hipStream_t s) {
+  if (a.m == 0) hipLaunchKernelGGL((pq_attend_kernel<D, BITS, 0, PK>), grid, kThreads, lds, s, a, wph);
+  else if (a.m == D) hipLaunchKernelGGL((pq_attend_kernel<D, BITS, D / 64, PK>), grid, kThreads, lds, s, a, wph);
+  else hipLaunchKernelGGL((pq_attend_kernel<D, BITS, -1, PK>), grid, kThreads, lds, s, a, wph);
+  return hipGetLastError();
+}
+
+template <int D, int BITS>
+hipError_t launch_attend_db(const pqi::AttnArgs& a, int grid, int wph, size_t lds, hipStream_t s) {
+  if (a.packed) return launch_attend_dbp<D, BITS, true>(a, grid, wph, lds, s);
+  return launch_attend_dbp<D, BITS, false>(a, grid, wph, lds, s);
+}
+
+template <int D>
+hipError_t launch_attend_d(int bits, const pqi::AttnArgs& a, hipStream_t s) {
+  if (a.n_ranges > 0) {
+    const int wph = a.n_ranges * (D / pqi::attn_cols(D));           // waves per head
+    const int grid = a.n_heads * ((wph + kWaves - 1) / kWaves);
+    const size_t lds = (size_t)(pqi::prep_head_bytes(D, a.m) - pqi::prep_off_meta(D, a.m)) +
+                       4 * (1 << pqi::kMaxScoreBits);
+    hipError_t e = hipErrorInvalidValue;
+    switch (bits) {
+      case 1: e = launch_attend_db<D, 1>(a, grid, wph, lds, s); break;
+      case 2: e = launch_attend_db<D, 2>(a, grid, wph, lds, s); break;
+      case 3: e = launch_attend_db<D, 3>(a, grid, wph, lds, s); break;
+      case 4: e = launch_attend_db<D, 4>(a, grid, wph, lds, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(pq_attend_combine_kernel<D>, a.n_heads * a.n_q, 256, (size_t)a.n_ranges * 4, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// The library is compiled as four units of this file (PQ_UNIT 0 .. 3) in parallel: the
+// The library is compiled as five units of this file (PQ_UNIT 0 .. 4) in parallel: the
 // quantize kernels for d = 64, 128; those for d = 256, 512; everything else but the
-// two-stage score; the two-stage score.  Without
+// two-stage score and the attention; the two-stage score; the fused decode attention.  Without
 // PQ_UNIT one unit holds all of it.  Kernels are templates or file-local, so each unit
 // carries only the kernels its launch functions instantiate (plus the few non-template ones).
 #ifndef PQ_UNIT
@@ -1770,9 +2150,19 @@ hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const Launch
 }
 #endif  // PQ_UNIT 3
 
+#if PQ_UNIT < 0 || PQ_UNIT == 4
+hipError_t launch_attention(int d, int bits, const AttnArgs& a, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_attend_d<64>(bits, a, s);
+    case 128: return launch_attend_d<128>(bits, a, s);
+    case 256: return launch_attend_d<256>(bits, a, s);
+    case 512: return launch_attend_d<512>(bits, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+#endif  // PQ_UNIT 4
+
 #if PQ_UNIT < 0 || PQ_UNIT == 2
-
-
 hipError_t launch_quantize(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {
   return d <= 128 ? launch_quantize_lo(d, in_bf16, a, c, s) : launch_quantize_hi(d, in_bf16, a, c, s);
 }

@@ -139,3 +139,16 @@ def config5_tensor(d, seed=0, kv_heads=8, tokens=65536, n_q=16):
     q = rng(s, TAG_QUERY).standard_normal((kv_heads, n_q, d), dtype=np.float32)
     return {"x": bf16_from_f32(x), "q": bf16_from_f32(q), "d": d, "bits": 3, "m": d,
             "signs": sign_mask(BASE_SEED + d, d), "G": projection(BASE_SEED + d, d, d)}
+
+
+def config5_attention(d, seed=0, kv_heads=8, tokens=65536, n_q=16, window=128):
+    """Decode-attention inputs on the config-5 recipe: keys and values are two tensors of that
+    recipe (seeds ``seed`` and ``seed + 1``, so each has its own channel scales) of
+    tokens + window rows per head; the first ``tokens`` rows go to the quantized cache, the last
+    ``window`` rows stay unquantized.  Values get their own sign mask."""
+    keys = config5_tensor(d, seed, kv_heads, tokens + window, n_q)
+    vals = config5_tensor(d, seed + 1, kv_heads, tokens + window, n_q)
+    return {"k": np.ascontiguousarray(keys["x"][:, :tokens]), "v": np.ascontiguousarray(vals["x"][:, :tokens]),
+            "k_win": np.ascontiguousarray(keys["x"][:, tokens:]), "v_win": np.ascontiguousarray(vals["x"][:, tokens:]),
+            "q": keys["q"], "d": d, "bits": keys["bits"], "m": keys["m"], "k_signs": keys["signs"], "G": keys["G"],
+            "v_signs": sign_mask(BASE_SEED + d + 1, d)}

@@ -201,3 +201,47 @@ def test_outlier_entry_points_validate():
     assert lib.qjl_score_add(256, 4, 8, 32, 0, P16, P16, P16, P16, NUL) == pq.PQ_OK
     assert lib.qjl_score_add(256, 4, 8, 30, 64, P16, P16, P16, P16, NUL) == pq.PQ_EINVAL
     assert lib.qjl_score_add(256, 4, 8, 64, 64, P16, P16, P16, P16, NUL) == pq.PQ_EUNSUPPORTED
+
+
+def test_attention_entry_points_validate():
+    """Decode attention: work size, and bad arguments refused before any HIP call."""
+    lib = pq.lib()
+    assert lib.pq_attention_work_bytes(100, 2, 64) == -1
+    assert lib.pq_attention_work_bytes(128, -1, 64) == -1
+    assert lib.pq_attention_work_bytes(128, 2, 0) == 0
+    # one range of one tile: 16 query rows of (max, sum) and of d floats
+    assert lib.pq_attention_work_bytes(128, 1, 5) == 16 * (8 + 128 * 4)
+    nb = lib.pq_attention_work_bytes(256, 8, 65536)
+    assert nb > 0 and nb % (16 * (8 + 256 * 4)) == 0
+    F = ctypes.c_float
+    names = ("d", "bits", "m", "h", "nq", "t", "prep", "kc", "kn", "kb", "kr", "vc", "vn", "vs", "w", "kw", "vw",
+             "q", "scale", "work", "out", "s")
+    base = dict(d=128, bits=3, m=128, h=2, nq=16, t=100, prep=P16, kc=P16, kn=P16, kb=P16, kr=P16, vc=P16,
+                vn=P16, vs=P16, w=4, kw=P16, vw=P16, q=P16, scale=F(0.1), work=P16, out=P16, s=NUL)
+
+    def att(fn=lib.pq_attention, **kw):
+        a = dict(base)
+        a.update(kw)
+        return fn(*[a[n] for n in names])
+
+    for fn in (lib.pq_attention, lib.pq_attention_packed):
+        assert att(fn, bits=5) == pq.PQ_EUNSUPPORTED
+        assert att(fn, bits=0) == pq.PQ_EINVAL
+        assert att(fn, d=96) == pq.PQ_EINVAL
+        assert att(fn, nq=17) == pq.PQ_EINVAL
+        assert att(fn, m=0) == pq.PQ_EINVAL                          # residual bits without m
+        assert att(fn, m=96) == pq.PQ_EUNSUPPORTED
+        assert att(fn, kb=NUL) == pq.PQ_EINVAL
+        assert att(fn, vc=NUL) == pq.PQ_EINVAL
+        assert att(fn, vs=NUL) == pq.PQ_EINVAL
+        assert att(fn, work=NUL) == pq.PQ_EINVAL
+        assert att(fn, work=ctypes.c_void_p(0x10008)) == pq.PQ_EINVAL
+        assert att(fn, kc=ctypes.c_void_p(0x10008)) == pq.PQ_EINVAL
+        assert att(fn, q=NUL) == pq.PQ_EINVAL                        # window without queries
+        assert att(fn, w=5000) == pq.PQ_EUNSUPPORTED
+        assert att(fn, w=-1) == pq.PQ_EINVAL
+        assert att(fn, t=0, w=0) == pq.PQ_EINVAL                     # softmax over no token
+        assert att(fn, scale=F(float("nan"))) == pq.PQ_EINVAL
+        assert att(fn, scale=F(float("inf"))) == pq.PQ_EINVAL
+        assert att(fn, h=0) == pq.PQ_OK
+        assert att(fn, nq=0) == pq.PQ_OK
