@@ -292,8 +292,9 @@ int pq_score_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok,
  *               k_rnorms n_heads * n_tok fp16 (both NULL when m == 0)
  *   v_codes, v_norms  the values, as k_codes and k_norms (pq_quantize with m = 0)
  *   v_signs     the rotation sign mask of the values, d/8 bytes of device memory
- *   n_win       window tokens, 0 .. 4096; k_win, v_win bf16 [head][n_win][d], q the
- *               bf16 queries [head][n_q][d] (all three may be NULL when n_win == 0)
+ *   n_win       window tokens, 0 .. 4096; k_win, v_win bf16 [head][n_win][d] (k_win 16-byte
+ *               aligned), q the bf16 queries [head][n_q][d] (all three may be NULL when
+ *               n_win == 0)
  *   sm_scale    softmax scale (finite; 1/sqrt(d) in the usual attention)
  *   work        pq_attention_work_bytes(d, n_heads, n_tok) bytes, 16-byte aligned,
  *               device memory; its contents on entry do not matter
@@ -301,7 +302,7 @@ int pq_score_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok,
  * n_tok + n_win must be at least 1 (PQ_EINVAL); n_q <= 16 per call.  All device pointers
  * are caller-owned; the call is asynchronous on `stream` and allocates nothing.  Scores
  * carry pq_score's precision; the probabilities and centroids enter the matrix cores as
- * fp16 pairs (about 22 significant bits) and accumulate in fp32; merging in double.
+ * fp16 pairs (about 22 significant bits) and accumulate in fp32.
  */
 int64_t pq_attention_work_bytes(int d, int n_heads, int64_t n_tok);
 int pq_attention(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,

@@ -476,7 +476,7 @@ static int attention_impl(int d, int bits, int m, int n_heads, int n_q, int64_t 
       return PQ_EINVAL;
     if (m > 0 && (!aligned(k_qjl_bits, 2) || !aligned(k_rnorms, 2))) return PQ_EINVAL;
   }
-  if (n_win > 0 && (!k_win || !v_win || !q || !aligned(k_win, 2) || !aligned(v_win, 2) || !aligned(q, 2)))
+  if (n_win > 0 && (!k_win || !v_win || !q || !aligned(k_win, 16) || !aligned(v_win, 2) || !aligned(q, 2)))
     return PQ_EINVAL;
   if (!aligned(out, 4)) return PQ_EINVAL;
   const pqi::AttnPlan plan = pqi::attn_plan(d, n_heads, n_tok);
@@ -487,9 +487,10 @@ static int attention_impl(int d, int bits, int m, int n_heads, int n_q, int64_t 
   a.v_codes = v_codes; a.v_norms = v_norms; a.v_signs = v_signs;
   a.k_win = k_win; a.v_win = v_win; a.q = q; a.out = out;
   a.work_ml = static_cast<float*>(work);
-  a.work_o = plan.n_ranges ? a.work_ml + (int64_t)n_heads * plan.n_ranges * pqi::kScoreRows * 2 : nullptr;
+  a.work_o = plan.n_parts ? a.work_ml + (int64_t)n_heads * plan.n_parts * pqi::kScoreRows * 2 : nullptr;
   a.n_tok = n_tok; a.n_win = n_win; a.tiles_per_range = plan.tiles_per_range;
-  a.n_heads = n_heads; a.n_q = n_q; a.m = m; a.n_ranges = plan.n_ranges; a.packed = packed;
+  a.n_heads = n_heads; a.n_q = n_q; a.m = m; a.n_ranges = plan.n_ranges; a.n_parts = plan.n_parts;
+  a.packed = packed;
   a.scale_log2 = (double)sm_scale * 1.4426950408889634;          // log2(e)
   const Codebook& cb = codebook(bits);
   const int L = 1 << bits;

@@ -155,22 +155,29 @@ struct TwoStageArgs {
 
 // Decode attention over the quantized cache.  The fused kernel gives each wave a range of
 // tiles_per_range 16-token tiles of one KV head and one slice of attn_cols(d) value columns;
-// each (head, range) leaves a partial result in the work buffer:
-//   ml  float2[n_heads][n_ranges][16]      running max (base-2 logits) and sum of exp2
-//   o   float[n_heads][n_ranges][16][d]    sum_t exp2(z_t - max) n16_t / d c[code_t], rotated basis
-// and the combine kernel merges them with the window and rotates back.
+// the kAttnWaves ranges of a workgroup merge into one partial result in the work buffer:
+//   ml  float2[n_heads][n_parts][16]      running max (base-2 logits) and sum of exp2
+//   o   float[n_heads][n_parts][16][d]    sum_t exp2(z_t - max) n16_t / d c[code_t], rotated basis
+// and the combine kernel merges those with the window and rotates back.
 constexpr int kAttnMaxWin = 4096;         // window tokens held in LDS by the combine kernel
 constexpr int kAttnTargetWaves = 2048;    // fused-kernel waves aimed for over all heads
+constexpr int kAttnWaves = 4;             // ranges (waves) per workgroup
 
-__host__ __device__ constexpr int attn_cols(int d) { return d <= 128 ? d : 128; }
+#ifndef PQ_ATTN_MAX_COLS
+#define PQ_ATTN_MAX_COLS 512       // value columns one wave of the fused kernel accumulates
+#endif
+__host__ __device__ constexpr int attn_cols(int d) { return d <= PQ_ATTN_MAX_COLS ? d : PQ_ATTN_MAX_COLS; }
+// LDS of the in-workgroup merge: maxima and sums of every wave, two slots of 16 x attn_cols(d)
+__host__ __device__ constexpr int attn_merge_lds(int d) { return 2 * kAttnWaves * 16 * 4 + 2 * 16 * attn_cols(d) * 4; }
 
 struct AttnPlan {
   int n_ranges;              // per head
+  int n_parts;               // per head: workgroups of kAttnWaves ranges
   int64_t tiles_per_range;
 };
 
 inline AttnPlan attn_plan(int d, int n_heads, int64_t n_tok) {
-  AttnPlan p{0, 0};
+  AttnPlan p{0, 0, 0};
   const int64_t n_tiles = (n_tok + 15) >> 4;
   if (n_tiles == 0 || n_heads <= 0) return p;
   const int64_t slices = d / attn_cols(d);
@@ -179,12 +186,13 @@ inline AttnPlan attn_plan(int d, int n_heads, int64_t n_tok) {
   if (want > n_tiles) want = n_tiles;
   p.tiles_per_range = (n_tiles + want - 1) / want;
   p.n_ranges = (int)((n_tiles + p.tiles_per_range - 1) / p.tiles_per_range);
+  p.n_parts = (p.n_ranges + kAttnWaves - 1) / kAttnWaves;
   return p;
 }
 
 inline int64_t attn_work_bytes(int d, int n_heads, int64_t n_tok) {
   const AttnPlan p = attn_plan(d, n_heads, n_tok);
-  return (int64_t)n_heads * p.n_ranges * kScoreRows * (8 + (int64_t)d * 4);
+  return (int64_t)n_heads * p.n_parts * kScoreRows * (8 + (int64_t)d * 4);
 }
 
 struct AttnArgs {
@@ -203,7 +211,7 @@ struct AttnArgs {
   float* work_o;              // partial outputs
   float* out;                 // [n_heads][n_q][d] fp32
   int64_t n_tok, n_win, tiles_per_range;
-  int n_heads, n_q, m, n_ranges, packed;
+  int n_heads, n_q, m, n_ranges, n_parts, packed;
   double scale_log2;          // softmax scale times log2(e)
   double alpha[kMaxPlanes];   // key codebook, odd-Walsh coefficients (as TwoStageArgs)
   float vcent[1 << kMaxScoreBits];   // value codebook centroids

@@ -1596,7 +1596,7 @@ __device__ __forceinline__ f16x4 as_f16x4(uint32_t w0, uint32_t w1) {
 }
 
 template <int D, int BITS, int KQT, bool PK>
-__global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs a, int waves_per_head) {
+__global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs a) {
   constexpr int KC = D / 64;
   constexpr int NP = 1 << (BITS - 1);
   constexpr bool QJL = KQT != 0;
@@ -1605,10 +1605,13 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
   constexpr uint32_t CMASK = (1u << BITS) - 1u;
   const int m = QJL ? a.m : 0;
   const int KQ = m >> 6, mb = m >> 3;
-  const int wg_per_head = (waves_per_head + kWaves - 1) / kWaves;
-  const int head = blockIdx.x / wg_per_head;
-  const int wih = (blockIdx.x % wg_per_head) * kWaves + (int)(threadIdx.x >> 6);
-  const int range = wih / CS, cs = wih % CS;
+  // workgroup = (head, column slice, group of kWaves ranges); wave = one range
+  const int grp = blockIdx.x % a.n_parts;
+  const int cs = (blockIdx.x / a.n_parts) % CS;
+  const int head = blockIdx.x / (a.n_parts * CS);
+  const int wv = (int)(threadIdx.x >> 6);
+  const int range = grp * kWaves + wv;
+  const bool live = range < a.n_ranges;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t meta = pqi::prep_off_meta(D, m);
@@ -1626,7 +1629,6 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
     tab[threadIdx.x] = (hi & 0xffffu) | (lo << 16);
   }
   __syncthreads();
-  if (wih >= waves_per_head) return;
 
   const float* scale = reinterpret_cast<const float*>(smem);
   const int* isum = reinterpret_cast<const int*>(smem + 128);
@@ -1637,8 +1639,8 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
   const int r = lane & 15, g = lane >> 4;
   const int64_t T = a.n_tok;
   const int64_t n_tiles = (T + 15) >> 4;
-  const int64_t t_begin = (int64_t)range * a.tiles_per_range;
-  const int64_t t_end = min(n_tiles, t_begin + a.tiles_per_range);
+  const int64_t t_begin = live ? (int64_t)range * a.tiles_per_range : 0;
+  const int64_t t_end = live ? min(n_tiles, t_begin + a.tiles_per_range) : 0;
   const int64_t hoff = (int64_t)head * T;
   constexpr int RB = PK ? D * BITS / 8 : D;              // code bytes of a token
   const uint8_t* kcodes = a.k_codes + hoff * RB;
@@ -1650,17 +1652,23 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
   const double cq = QJL ? 1.2533141373155003 / (double)m : 0.0;     // sqrt(pi/2) / m
 
   // one tile's inputs; tokens past the end are clamped to the last token (always in bounds),
-  // and their probabilities are set to zero
+  // and their probabilities are set to zero.  The key inputs of the next tile are fetched once
+  // the current ones are used (they load during the softmax and the value product), the value
+  // inputs once the value product is done (they load during the next scores): one copy of each
+  // is live at a time.
   constexpr int PW = PK ? (2 * BITS + 3) / 4 : 4;       // dwords of a lane's 16 key codes
-  constexpr int VW = PK ? 1 : NT / 4;                    // dwords of a lane's NT value codes
-  struct Inputs {
+  constexpr int VL = NT * BITS;                          // bits of a lane's packed value-code run
+  constexpr int VW = PK ? (VL + 31) / 32 : NT / 4;       // dwords of a lane's NT value codes
+  struct KeyIn {
     uint32_t cw[KC][PW];
     uint32_t qb[(KQB + 1) / 2];
-    uint32_t vr[4][VW];
     uint32_t kn;          // key norm | residual norm << 16, token r of the tile
+  };
+  struct ValIn {
+    uint32_t vr[4][VW];
     uint32_t vn;          // value norm, token r of the tile
   };
-  auto fetch = [&](int64_t tile, Inputs& in) {
+  auto fetch_k = [&](int64_t tile, KeyIn& in) {
     const int64_t tok = min(tile * 16 + r, T - 1);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
@@ -1672,22 +1680,33 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       }
     }
     in.kn = (uint32_t)knorms[tok] | (QJL ? (uint32_t)rnorms[tok] << 16 : 0u);
-    in.vn = vnorms[tok];
     if constexpr (KQT > 0) load_key_bits<KQT>(qbits + tok * mb + (mb >> 2) * g, true, in.qb);
+  };
+  auto fetch_v = [&](int64_t tile, ValIn& in) {
+    in.vn = vnorms[min(tile * 16 + r, T - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t vt = min(tile * 16 + 4 * g + i, T - 1);
       const int e0 = RUN * r + cs * NT;                  // first value column of the lane
       if constexpr (PK) {
+        // the dwords holding bits s .. s + VL - 1 of the token's stream, shifted down by s
         const uint32_t* row = reinterpret_cast<const uint32_t*>(vcodes + vt * RB);
-        const int s = e0 * BITS;
-        const uint32_t w0 = row[s >> 5], w1 = row[(s + NT * BITS - 1) >> 5];
-        in.vr[i][0] = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)(s & 31));
-      } else if constexpr (NT == 8) {
-        const uint2 w = *reinterpret_cast<const uint2*>(vcodes + vt * RB + e0);
-        in.vr[i][0] = w.x; in.vr[i][1] = w.y;
+        const int s = e0 * BITS, k0 = s >> 5, kl = (s + VL - 1) >> 5;
+        uint32_t w[VW + 1];
+#pragma unroll
+        for (int u = 0; u <= VW; ++u) w[u] = row[min(k0 + u, kl)];
+#pragma unroll
+        for (int u = 0; u < VW; ++u) in.vr[i][u] = __builtin_amdgcn_alignbit(w[u + 1], w[u], (uint32_t)(s & 31));
       } else {
-        in.vr[i][0] = *reinterpret_cast<const uint32_t*>(vcodes + vt * RB + e0);
+#pragma unroll
+        for (int u = 0; u < VW; u += 2) {
+          if (u + 1 < VW) {
+            const uint2 w = *reinterpret_cast<const uint2*>(vcodes + vt * RB + e0 + 4 * u);
+            in.vr[i][u] = w.x; in.vr[i][u + 1] = w.y;
+          } else {
+            in.vr[i][u] = *reinterpret_cast<const uint32_t*>(vcodes + vt * RB + e0 + 4 * u);
+          }
+        }
       }
     }
   };
@@ -1699,11 +1718,17 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
 #pragma unroll
   for (int j = 0; j < NT; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  Inputs nxt;
-  fetch(t_begin, nxt);                                   // every range holds at least one tile
+  KeyIn kin;
+  ValIn vin;
+  if (live) {                                            // every live range holds at least one tile
+    fetch_k(t_begin, kin);
+    fetch_v(t_begin, vin);
+  }
   for (int64_t tile = t_begin; tile < t_end; ++tile) {
-    const Inputs in = nxt;
-    if (tile + 1 < t_end) fetch(tile + 1, nxt);          // uniform
+    // the query fragments are read from LDS in every tile rather than held in registers
+    // across the loop (3 (d + m) / 16 registers that would cost the wave its occupancy)
+    asm volatile("" ::: "memory");
+    const bool more = tile + 1 < t_end;                 // uniform
     // --- scores S^T: rows = tokens, columns = queries
     i32x4 acc[NP][3];
 #pragma unroll
@@ -1719,10 +1744,10 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       if constexpr (PK) {
         uint32_t u[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) u[i >> 2] |= stream_code<BITS>(in.cw[k], i) << (8 * (i & 3));
+        for (int i = 0; i < 16; ++i) u[i >> 2] |= stream_code<BITS>(kin.cw[k], i) << (8 * (i & 3));
         cb = make_uint4(u[0], u[1], u[2], u[3]);
       } else {
-        cb = make_uint4(in.cw[k][0], in.cw[k][1], in.cw[k][2], in.cw[k][3]);
+        cb = make_uint4(kin.cw[k][0], kin.cw[k][1], kin.cw[k][2], kin.cw[k][3]);
       }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
@@ -1742,7 +1767,7 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
     };
     if constexpr (KQT > 0) {
 #pragma unroll
-      for (int k = 0; k < KQT; ++k) qstep(k, (in.qb[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+      for (int k = 0; k < KQT; ++k) qstep(k, (kin.qb[k >> 1] >> (16 * (k & 1))) & 0xffffu);
     } else if constexpr (KQT < 0) {
       const uint8_t* kb = qbits + min(tile * 16 + r, T - 1) * mb + (mb >> 2) * g;
       for (int k = 0; k < KQ; ++k) qstep(k, *reinterpret_cast<const uint16_t*>(kb + 2 * k));
@@ -1752,7 +1777,7 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
     float z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t kn = (uint32_t)__shfl((int)in.kn, 4 * g + i);
+      const uint32_t kn = (uint32_t)__shfl((int)kin.kn, 4 * g + i);
       double first = 0.0;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
@@ -1766,6 +1791,7 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       }
       z[i] = tile * 16 + 4 * g + i < T ? (float)(val * a.scale_log2) : -INFINITY;
     }
+    if (more) fetch_k(tile + 1, kin);
     // --- online softmax; every tile holds a live token, so the tile maximum is finite
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -1789,7 +1815,7 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
     float w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t vn = (uint32_t)__shfl((int)in.vn, 4 * g + i);
+      const uint32_t vn = (uint32_t)__shfl((int)vin.vn, 4 * g + i);
       w[i] = pv[i] * (f16_to_f32((uint16_t)vn) * (1.0f / (float)D));
     }
     uint32_t pl0, pl1;
@@ -1802,7 +1828,7 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       uint32_t t4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t code = PK ? (in.vr[i][0] >> (BITS * j)) & CMASK : (in.vr[i][j >> 2] >> (8 * (j & 3))) & CMASK;
+        const uint32_t code = PK ? stream_code<BITS>(vin.vr[i], j) : (vin.vr[i][j >> 2] >> (8 * (j & 3))) & CMASK;
         t4[i] = tab[code];
       }
       const f16x4 Bh = as_f16x4(__builtin_amdgcn_perm(t4[1], t4[0], 0x05040100u),
@@ -1813,22 +1839,76 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ah, Bl, o[j], 0, 0, 0);
       o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Al, Bh, o[j], 0, 0, 0);
     }
+    if (more) fetch_v(tile + 1, vin);
   }
-  // partial result of the range: (max, sum) per query, O rows 4 g + i at the lane's columns
+  // merge the kWaves ranges of the workgroup (a wave without tiles holds max -inf, sum 0, O 0)
+  // into one partial result: rescale to the common maximum, then sum in a fixed order through
+  // two LDS slots (waves 2, 3 into 0, 1; then wave 1 into 0).  The prep region is reused.
   ls += __shfl_xor(ls, 16);
   ls += __shfl_xor(ls, 32);
-  const int64_t part = (int64_t)head * a.n_ranges + range;
-  if (cs == 0 && g == 0) reinterpret_cast<float2*>(a.work_ml)[part * 16 + r] = make_float2(mx, ls);
-  float* po = a.work_o + part * 16 * D + RUN * r + cs * NT;
+  __syncthreads();
+  float* xm = reinterpret_cast<float*>(smem);           // [kWaves][16] maxima, then [kWaves][16] sums
+  float* slot = xm + 2 * kWaves * 16;                    // [2][16][DC]
+  if (g == 0) {
+    xm[wv * 16 + r] = mx;
+    xm[(kWaves + wv) * 16 + r] = ls;
+  }
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int qr = 4 * g + i;
+    float M = xm[qr];
 #pragma unroll
-    for (int j = 0; j < NT; j += 4)
-      *reinterpret_cast<float4*>(po + (4 * g + i) * D + j) = make_float4(o[j][i], o[j + 1][i], o[j + 2][i], o[j + 3][i]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, xm[w * 16 + qr]);
+    const float f = exp2f(xm[wv * 16 + qr] - M);        // 0 for a wave without tiles
+#pragma unroll
+    for (int j = 0; j < NT; ++j) o[j][i] *= f;
+  }
+  auto put = [&](float* dst) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; j += 4)
+        *reinterpret_cast<float4*>(dst + (4 * g + i) * DC + NT * r + j) =
+            make_float4(o[j][i], o[j + 1][i], o[j + 2][i], o[j + 3][i]);
+  };
+  auto add = [&](const float* src) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; j += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + (4 * g + i) * DC + NT * r + j);
+        o[j][i] += v.x; o[j + 1][i] += v.y; o[j + 2][i] += v.z; o[j + 3][i] += v.w;
+      }
+  };
+  if (wv >= 2) put(slot + (wv - 2) * 16 * DC);
+  __syncthreads();
+  if (wv < 2) add(slot + wv * 16 * DC);
+  __syncthreads();
+  if (wv == 1) put(slot);
+  __syncthreads();
+  if (wv == 0) {
+    add(slot);
+    const int64_t part = (int64_t)head * a.n_parts + grp;
+    if (cs == 0 && g == 0) {
+      float M = xm[r], L = 0.0f;
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, xm[w * 16 + r]);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) L += xm[(kWaves + w) * 16 + r] * exp2f(xm[w * 16 + r] - M);
+      reinterpret_cast<float2*>(a.work_ml)[part * 16 + r] = make_float2(M, L);
+    }
+    float* po = a.work_o + part * 16 * D + RUN * r + cs * NT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; j += 4)
+        *reinterpret_cast<float4*>(po + (4 * g + i) * D + j) = make_float4(o[j][i], o[j + 1][i], o[j + 2][i], o[j + 3][i]);
+  }
 }
 
 // Merge the partial results of one (head, query) with the unquantized window, rotate back and
-// normalise.  Sums in double; the window scores in fp32 (products of bf16 values are exact).
+// normalise.
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   __syncthreads();
@@ -1848,21 +1928,33 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 template <int D>
 __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnArgs a) {
   const int h = blockIdx.x / a.n_q, qi = blockIdx.x % a.n_q;
-  const int R = a.n_ranges, W = (int)a.n_win;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int R = a.n_parts, W = (int)a.n_win;
+  const int tid = threadIdx.x;
   __shared__ float x[D];
   __shared__ float ew[pqi::kAttnMaxWin];
   __shared__ float red_f[4];
   __shared__ double red_d[4];
   extern __shared__ float wr[];                          // [R] weights of the partials
-  // window logits (base 2)
-  for (int w = wv; w < W; w += 4) {
+  // window logits (base 2): one thread per window token, the query in LDS as fp32
+  if (W > 0) {
     const uint16_t* q = a.q + ((int64_t)h * a.n_q + qi) * D;
-    const uint16_t* kw = a.k_win + ((int64_t)h * W + w) * D;
-    float s = 0.0f;
-    for (int e = lane; e < D; e += 64) s = fmaf(bf16_to_f32(q[e]), bf16_to_f32(kw[e]), s);
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) ew[w] = (float)((double)s * a.scale_log2);
+    for (int e = tid; e < D; e += 256) x[e] = bf16_to_f32(q[e]);
+    __syncthreads();
+    for (int w = tid; w < W; w += 256) {
+      const uint4* kw = reinterpret_cast<const uint4*>(a.k_win + ((int64_t)h * W + w) * D);
+      // products of bf16 values are exact in fp32; the sums run in double
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll 4
+      for (int c = 0; c < D / 8; ++c) {
+        const uint4 u = kw[c];
+        const float* qq = x + 8 * c;
+        s0 += (double)(qq[0] * bf16_lo(u.x)) + (double)(qq[2] * bf16_lo(u.y));
+        s1 += (double)(qq[1] * bf16_hi(u.x)) + (double)(qq[3] * bf16_hi(u.y));
+        s0 += (double)(qq[4] * bf16_lo(u.z)) + (double)(qq[6] * bf16_lo(u.w));
+        s1 += (double)(qq[5] * bf16_hi(u.z)) + (double)(qq[7] * bf16_hi(u.w));
+      }
+      ew[w] = (float)((s0 + s1) * a.scale_log2);
+    }
   }
   __syncthreads();
   const float2* ml = reinterpret_cast<const float2*>(a.work_ml) + (int64_t)h * R * 16 + qi;
@@ -1885,9 +1977,14 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
   const double L = block_sum(lsum, red_d);               // its barriers also publish wr and ew
   const float* po = a.work_o + (int64_t)h * R * 16 * D + (int64_t)qi * D;
   for (int e = tid; e < D; e += 256) {
-    double acc = 0.0;
-    for (int t = 0; t < R; ++t) acc += (double)wr[t] * (double)po[(int64_t)t * 16 * D + e];
-    x[e] = (float)acc;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int t = 0;
+    for (; t + 4 <= R; t += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = fmaf(wr[t + u], po[(int64_t)(t + u) * 16 * D + e], acc[u]);
+    }
+    for (; t < R; ++t) acc[0] = fmaf(wr[t], po[(int64_t)t * 16 * D + e], acc[0]);
+    x[e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   __syncthreads();
   // inverse rotation: Walsh-Hadamard butterflies in Sylvester order, then the value signs
@@ -1902,10 +1999,16 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
   }
   float* out = a.out + ((int64_t)h * a.n_q + qi) * D;
   for (int e = tid; e < D; e += 256) {
-    double acc = ((a.v_signs[e >> 3] >> (e & 7)) & 1) ? -(double)x[e] : (double)x[e];
+    const float y = ((a.v_signs[e >> 3] >> (e & 7)) & 1) ? -x[e] : x[e];
+    float acc[4] = {y, 0.0f, 0.0f, 0.0f};
     const uint16_t* vw = a.v_win + (int64_t)h * W * D + e;
-    for (int w = 0; w < W; ++w) acc += (double)ew[w] * (double)bf16_to_f32(vw[(int64_t)w * D]);
-    out[e] = (float)(acc / L);
+    int w = 0;
+    for (; w + 4 <= W; w += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = fmaf(ew[w + u], bf16_to_f32(vw[(int64_t)(w + u) * D]), acc[u]);
+    }
+    for (; w < W; ++w) acc[0] = fmaf(ew[w], bf16_to_f32(vw[(int64_t)w * D]), acc[0]);
+    out[e] = (float)((double)((acc[0] + acc[1]) + (acc[2] + acc[3])) / L);
   }
 }
 
@@ -2043,36 +2146,37 @@ hipError_t launch_two_stage_d(int bits, const pqi::TwoStageArgs& a, int grid, in
 }
 
 template <int D, int BITS, bool PK>
-hipError_t launch_attend_dbp(const pqi::AttnArgs& a, int grid, int wph, size_t lds, hipStream_t s) {
-  if (a.m == 0) hipLaunchKernelGGL((pq_attend_kernel<D, BITS, 0, PK>), grid, kThreads, lds, s, a, wph);
-  else if (a.m == D) hipLaunchKernelGGL((pq_attend_kernel<D, BITS, D / 64, PK>), grid, kThreads, lds, s, a, wph);
-  else hipLaunchKernelGGL((pq_attend_kernel<D, BITS, -1, PK>), grid, kThreads, lds, s, a, wph);
+hipError_t launch_attend_dbp(const pqi::AttnArgs& a, int grid, size_t lds, hipStream_t s) {
+  if (a.m == 0) hipLaunchKernelGGL((pq_attend_kernel<D, BITS, 0, PK>), grid, kThreads, lds, s, a);
+  else if (a.m == D) hipLaunchKernelGGL((pq_attend_kernel<D, BITS, D / 64, PK>), grid, kThreads, lds, s, a);
+  else hipLaunchKernelGGL((pq_attend_kernel<D, BITS, -1, PK>), grid, kThreads, lds, s, a);
   return hipGetLastError();
 }
 
 template <int D, int BITS>
-hipError_t launch_attend_db(const pqi::AttnArgs& a, int grid, int wph, size_t lds, hipStream_t s) {
-  if (a.packed) return launch_attend_dbp<D, BITS, true>(a, grid, wph, lds, s);
-  return launch_attend_dbp<D, BITS, false>(a, grid, wph, lds, s);
+hipError_t launch_attend_db(const pqi::AttnArgs& a, int grid, size_t lds, hipStream_t s) {
+  if (a.packed) return launch_attend_dbp<D, BITS, true>(a, grid, lds, s);
+  return launch_attend_dbp<D, BITS, false>(a, grid, lds, s);
 }
 
 template <int D>
 hipError_t launch_attend_d(int bits, const pqi::AttnArgs& a, hipStream_t s) {
-  if (a.n_ranges > 0) {
-    const int wph = a.n_ranges * (D / pqi::attn_cols(D));           // waves per head
-    const int grid = a.n_heads * ((wph + kWaves - 1) / kWaves);
-    const size_t lds = (size_t)(pqi::prep_head_bytes(D, a.m) - pqi::prep_off_meta(D, a.m)) +
-                       4 * (1 << pqi::kMaxScoreBits);
+  static_assert(kWaves == pqi::kAttnWaves, "ranges per workgroup");
+  if (a.n_parts > 0) {
+    const int grid = a.n_heads * (D / pqi::attn_cols(D)) * a.n_parts;
+    const size_t lds = std::max<size_t>((size_t)(pqi::prep_head_bytes(D, a.m) - pqi::prep_off_meta(D, a.m)) +
+                                            4 * (1 << pqi::kMaxScoreBits),
+                                        pqi::attn_merge_lds(D));
     hipError_t e = hipErrorInvalidValue;
     switch (bits) {
-      case 1: e = launch_attend_db<D, 1>(a, grid, wph, lds, s); break;
-      case 2: e = launch_attend_db<D, 2>(a, grid, wph, lds, s); break;
-      case 3: e = launch_attend_db<D, 3>(a, grid, wph, lds, s); break;
-      case 4: e = launch_attend_db<D, 4>(a, grid, wph, lds, s); break;
+      case 1: e = launch_attend_db<D, 1>(a, grid, lds, s); break;
+      case 2: e = launch_attend_db<D, 2>(a, grid, lds, s); break;
+      case 3: e = launch_attend_db<D, 3>(a, grid, lds, s); break;
+      case 4: e = launch_attend_db<D, 4>(a, grid, lds, s); break;
     }
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pq_attend_combine_kernel<D>, a.n_heads * a.n_q, 256, (size_t)a.n_ranges * 4, s, a);
+  hipLaunchKernelGGL(pq_attend_combine_kernel<D>, a.n_heads * a.n_q, 256, (size_t)a.n_parts * 4, s, a);
   return hipGetLastError();
 }
 
