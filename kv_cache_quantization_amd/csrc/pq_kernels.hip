@@ -1662,11 +1662,12 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
   struct KeyIn {
     uint32_t cw[KC][PW];
     uint32_t qb[(KQB + 1) / 2];
-    uint32_t kn;          // key norm | residual norm << 16, token r of the tile
+    uint16_t kn, rn;      // key norm and residual norm of token r of the tile (raw loads: no
+                          // arithmetic on them here, which would wait for the whole fetch)
   };
   struct ValIn {
     uint32_t vr[4][VW];
-    uint32_t vn;          // value norm, token r of the tile
+    uint16_t vn;          // value norm of token r of the tile
   };
   auto fetch_k = [&](int64_t tile, KeyIn& in) {
     const int64_t tok = min(tile * 16 + r, T - 1);
@@ -1679,7 +1680,8 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
         in.cw[k][0] = w.x; in.cw[k][1] = w.y; in.cw[k][2] = w.z; in.cw[k][3] = w.w;
       }
     }
-    in.kn = (uint32_t)knorms[tok] | (QJL ? (uint32_t)rnorms[tok] << 16 : 0u);
+    in.kn = knorms[tok];
+    if constexpr (QJL) in.rn = rnorms[tok];
     if constexpr (KQT > 0) load_key_bits<KQT>(qbits + tok * mb + (mb >> 2) * g, true, in.qb);
   };
   auto fetch_v = [&](int64_t tile, ValIn& in) {
@@ -1728,7 +1730,9 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
     // the query fragments are read from LDS in every tile rather than held in registers
     // across the loop (3 (d + m) / 16 registers that would cost the wave its occupancy)
     asm volatile("" ::: "memory");
-    const bool more = tile + 1 < t_end;                 // uniform
+    // next tile, or this one again on the last pass: the fetches stay unconditional, so the
+    // count of loads in flight is the same on every path and each wait covers only its data
+    const int64_t nt = tile + 1 < t_end ? tile + 1 : tile;
     // --- scores S^T: rows = tokens, columns = queries
     i32x4 acc[NP][3];
 #pragma unroll
@@ -1777,7 +1781,7 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
     float z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t kn = (uint32_t)__shfl((int)kin.kn, 4 * g + i);
+      const uint32_t kn = (uint32_t)__shfl((int)((uint32_t)kin.kn | (QJL ? (uint32_t)kin.rn << 16 : 0u)), 4 * g + i);
       double first = 0.0;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
@@ -1791,7 +1795,8 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       }
       z[i] = tile * 16 + 4 * g + i < T ? (float)(val * a.scale_log2) : -INFINITY;
     }
-    if (more) fetch_k(tile + 1, kin);
+    fetch_k(nt, kin);
+    asm volatile("" ::: "memory");                      // issue those loads here, not after the product
     // --- online softmax; every tile holds a live token, so the tile maximum is finite
     float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -1839,7 +1844,7 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ah, Bl, o[j], 0, 0, 0);
       o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Al, Bh, o[j], 0, 0, 0);
     }
-    if (more) fetch_v(tile + 1, vin);
+    fetch_v(nt, vin);
   }
   // merge the kWaves ranges of the workgroup (a wave without tiles holds max -inf, sum 0, O 0)
   // into one partial result: rescale to the common maximum, then sum in a fixed order through
