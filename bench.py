@@ -45,6 +45,7 @@ def _args():
     ap.add_argument("--no-qjl", action="store_true", help="skip the config-4 QJL sketch/score leg")
     ap.add_argument("--no-tsq", action="store_true", help="skip the config-5 two-stage leg")
     ap.add_argument("--no-grouped", action="store_true", help="skip the config-3 grouped pass")
+    ap.add_argument("--no-attn", action="store_true", help="skip the config-5 decode-attention leg")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -123,7 +124,8 @@ def summarize(run_dir):
 
     trace_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/prof_trace -o trace -- "
                  "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-grouped")
-    lines = ["# Kernel durations of the benchmark (config 2 codec, config 4 QJL leg, config 5 two-stage leg), one MI355X",
+    lines = ["# Kernel durations of the benchmark (config 2 codec, config 4 QJL leg, config 5 two-stage and "
+             "decode-attention legs), one MI355X",
              "", "command: " + trace_cmd, "kernel source hash: " + kernel_source_hash(), "",
              "%-58s %6s %12s %10s %10s" % ("kernel", "calls", "average_ns", "min_ns", "max_ns")]
     for r in rows("prof_trace", "trace_kernel_stats.csv"):
@@ -145,8 +147,12 @@ def summarize(run_dir):
     rec = {"source_hash": kernel_source_hash(),
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_q_fetch -o q_fetch -- "
-               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq --no-grouped",
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq --no-grouped --no-attn",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_q_write -o q_write -- "
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq --no-grouped --no-attn",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_a_fetch -o a_fetch -- "
+               "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq --no-grouped",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_a_write -o a_write -- "
                "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-qjl --no-tsq --no-grouped",
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_c_fetch -o c_fetch -- "
                "python3 bench.py --calibrate-copy",
@@ -161,6 +167,15 @@ def summarize(run_dir):
                        ("pq_dequantize_kernel<128, true, 0>", "pq_dequantize_kernel")):
         fk, nf = counter("pmc_q_fetch", "q_fetch", kname)
         wk, nw = counter("pmc_q_write", "q_write", kname)
+        rec["kernels"][key] = {"instantiation": kname, "dispatches": [nf, nw], "fetch_size_kib": fk,
+                               "write_size_kib": wk,
+                               "hbm_bytes_per_launch": round(fk * 1024 * f_fetch + wk * 1024 * f_write)}
+    # the fused decode-attention kernels of the config-5 attention leg (byte codes)
+    for kname, key in (("pq_attend_kernel<256, 3, 4, false>", "pq_attend_kernel_d256"),
+                       ("pq_attend_kernel<512, 3, 8, false>", "pq_attend_kernel_d512"),
+                       ("pq_attend_combine_kernel<512>", "pq_attend_combine_kernel_d512")):
+        fk, nf = counter("pmc_a_fetch", "a_fetch", kname)
+        wk, nw = counter("pmc_a_write", "a_write", kname)
         rec["kernels"][key] = {"instantiation": kname, "dispatches": [nf, nw], "fetch_size_kib": fk,
                                "write_size_kib": wk,
                                "hbm_bytes_per_launch": round(fk * 1024 * f_fetch + wk * 1024 * f_write)}
@@ -351,6 +366,64 @@ def tsq_leg(pq, synth, torch, steps, warmup):
     return out
 
 
+def attn_leg(pq, synth, torch, steps, warmup):
+    """Decode attention on the config-5 shapes: per KV head 65536 quantized tokens (keys 3-bit with
+    QJL m=d, values 3-bit without) plus a 128-token bf16 window, 16 queries per head, for d=256
+    and d=512; byte codes and bit-packed codes.  Algorithmic bytes: every key and value code,
+    norm and residual bit read once, the window and queries read once, the output written."""
+    dev = torch.device("cuda:0")
+    out = {"attn_config": "config5 shapes: 8 KV heads x 65536 quantized tokens + 128-token bf16 window, "
+                          "16 queries per head, keys 3-bit + QJL m=d, values 3-bit, softmax scale 1/sqrt(d)"}
+    t16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    for d in (256, 512):
+        c = synth.config5_attention(d)
+        H, T, _ = c["k"].shape
+        W, n_q, bits, m = c["k_win"].shape[1], c["q"].shape[1], c["bits"], c["m"]
+        kst = torch.from_numpy(c["k_signs"]).to(dev)
+        vst = torch.from_numpy(c["v_signs"]).to(dev)
+        G = t16(c["G"])
+        kx, vx = t16(c["k"]), t16(c["v"])
+        kw, vw, q = t16(c["k_win"]), t16(c["v_win"]), t16(c["q"])
+        del c
+        keys = pq.quantize(kx, d, bits, kst, G)
+        vals = pq.quantize(vx, d, bits, vst)[:2]
+        kp = pq.quantize(kx, d, bits, kst, G, packed=True)[0]
+        vp = pq.quantize(vx, d, bits, vst, packed=True)[0]
+        del kx, vx
+        prep = pq.query_prep(q, kst, G)
+        work = torch.empty((pq.attention_work_bytes(d, H, T),), dtype=torch.uint8, device=dev)
+        o = torch.empty((H, n_q, d), dtype=torch.float32, device=dev)
+
+        def attend(k):
+            pq.attention(prep, keys, vals, vst, d, bits, H, n_q, T, m=m, k_win=kw, v_win=vw, q=q, work=work, out=o)
+
+        def attend_packed(k):
+            pq.attention(prep, (kp,) + tuple(keys[1:]), (vp, vals[1]), vst, d, bits, H, n_q, T, m=m, k_win=kw,
+                         v_win=vw, q=q, work=work, out=o, packed=True)
+
+        for k in range(warmup):
+            attend(k), attend_packed(k)
+        ta, tp = timed(torch, attend, steps), timed(torch, attend_packed, steps)
+        nb = H * T
+        side = nb * (2 + m // 8 + 2 + 2) + 2 * H * W * d * 2 + H * n_q * d * 2 + H * n_q * d * 4
+        ab = 2 * nb * d + side
+        apb = 2 * nb * d * bits // 8 + side
+        out.update({
+            "attn_d%d_us" % d: round(ta * 1e6, 2),
+            "attn_d%d_hbm_frac" % d: round(ab / ta / 1e9 / HBM_PEAK_GBS, 4),
+            "attn_d%d_tokens_per_s" % d: round(nb / ta, 1),
+            "attn_d%d_packed_us" % d: round(tp * 1e6, 2),
+            "attn_d%d_packed_hbm_frac" % d: round(apb / tp / 1e9 / HBM_PEAK_GBS, 4),
+            "attn_d%d_algorithmic_bytes" % d: ab,
+            "attn_d%d_packed_algorithmic_bytes" % d: apb,
+            "attn_d%d_work_bytes" % d: work.numel(),
+            "attn_d%d_fused_kernel_hbm_bytes" % d: counter_traffic("pq_attend_kernel_d%d" % d),
+        })
+        del keys, vals, kp, vp, prep, work, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def grouped_leg(pq, synth, torch, reps, packed=False):
     """Config 3: one streamed quantize pass and one dequantize pass over the 224 tensors of
     a 32-layer 7B-style decoder (4-bit codes, d=128), each tensor one launch with its own
@@ -514,6 +587,8 @@ def main():
         rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
     if not args.no_tsq:
         rec["parts"].update(tsq_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+    if not args.no_attn:
+        rec["parts"].update(attn_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_grouped:
         rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50)))
         rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50), packed=True))

@@ -292,7 +292,7 @@ int pq_score_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok,
  *               k_rnorms n_heads * n_tok fp16 (both NULL when m == 0)
  *   v_codes, v_norms  the values, as k_codes and k_norms (pq_quantize with m = 0)
  *   v_signs     the rotation sign mask of the values, d/8 bytes of device memory
- *   n_win       window tokens, 0 .. 4096; k_win, v_win bf16 [head][n_win][d] (k_win 16-byte
+ *   n_win       window tokens, 0 .. 4096; k_win, v_win bf16 [head][n_win][d] (16-byte
  *               aligned), q the bf16 queries [head][n_q][d] (all three may be NULL when
  *               n_win == 0)
  *   sm_scale    softmax scale (finite; 1/sqrt(d) in the usual attention)

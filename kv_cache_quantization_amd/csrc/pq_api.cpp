@@ -476,7 +476,7 @@ static int attention_impl(int d, int bits, int m, int n_heads, int n_q, int64_t 
       return PQ_EINVAL;
     if (m > 0 && (!aligned(k_qjl_bits, 2) || !aligned(k_rnorms, 2))) return PQ_EINVAL;
   }
-  if (n_win > 0 && (!k_win || !v_win || !q || !aligned(k_win, 16) || !aligned(v_win, 2) || !aligned(q, 2)))
+  if (n_win > 0 && (!k_win || !v_win || !q || !aligned(k_win, 16) || !aligned(v_win, 16) || !aligned(q, 2)))
     return PQ_EINVAL;
   if (!aligned(out, 4)) return PQ_EINVAL;
   const pqi::AttnPlan plan = pqi::attn_plan(d, n_heads, n_tok);

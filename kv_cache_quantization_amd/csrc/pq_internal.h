@@ -160,7 +160,9 @@ struct TwoStageArgs {
 //   o   float[n_heads][n_parts][16][d]    sum_t exp2(z_t - max) n16_t / d c[code_t], rotated basis
 // and the combine kernel merges those with the window and rotates back.
 constexpr int kAttnMaxWin = 4096;         // window tokens held in LDS by the combine kernel
-constexpr int kAttnTargetWaves = 2048;    // fused-kernel waves aimed for over all heads
+// fused-kernel waves aimed for over all heads: every wave resident at once on the 256 CUs
+// (two per SIMD; one at d = 512, whose register use allows one)
+__host__ __device__ constexpr int attn_target_waves(int d) { return d >= 512 ? 1024 : 2048; }
 constexpr int kAttnWaves = 4;             // ranges (waves) per workgroup
 
 #ifndef PQ_ATTN_MAX_COLS
@@ -181,7 +183,7 @@ inline AttnPlan attn_plan(int d, int n_heads, int64_t n_tok) {
   const int64_t n_tiles = (n_tok + 15) >> 4;
   if (n_tiles == 0 || n_heads <= 0) return p;
   const int64_t slices = d / attn_cols(d);
-  int64_t want = kAttnTargetWaves / ((int64_t)n_heads * slices);
+  int64_t want = attn_target_waves(d) / ((int64_t)n_heads * slices);
   if (want < 1) want = 1;
   if (want > n_tiles) want = n_tiles;
   p.tiles_per_range = (n_tiles + want - 1) / want;

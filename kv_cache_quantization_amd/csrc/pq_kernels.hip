@@ -1980,19 +1980,31 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
     lsum += (double)f;
   }
   const double L = block_sum(lsum, red_d);               // its barriers also publish wr and ew
-  const float* po = a.work_o + (int64_t)h * R * 16 * D + (int64_t)qi * D;
-  for (int e = tid; e < D; e += 256) {
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int t = 0;
-    for (; t + 4 <= R; t += 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = fmaf(wr[t + u], po[(int64_t)(t + u) * 16 * D + e], acc[u]);
+  // weighted sum of the partial outputs: thread (column group cg, row class par) sums float4
+  // columns over partials par, par + NPAR, ...; the row classes meet in LDS
+  constexpr int C4 = D / 4, NPAR = 256 / C4;
+  __shared__ float4 red4[NPAR][C4];
+  const int cg = tid % C4, par = tid / C4;
+  {
+    const float4* po4 = reinterpret_cast<const float4*>(a.work_o + (int64_t)h * R * 16 * D + (int64_t)qi * D);
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+    for (int t = par; t < R; t += NPAR) {
+      const float4 v = po4[(int64_t)t * 16 * C4 + cg];
+      const float w = wr[t];
+      acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
     }
-    for (; t < R; ++t) acc[0] = fmaf(wr[t], po[(int64_t)t * 16 * D + e], acc[0]);
-    x[e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    red4[par][cg] = acc;
   }
   __syncthreads();
-  // inverse rotation: Walsh-Hadamard butterflies in Sylvester order, then the value signs
+  for (int e = tid; e < D; e += 256) {
+    float v = 0.0f;
+    for (int p = 0; p < NPAR; ++p) v += reinterpret_cast<const float*>(red4[p])[e];
+    x[e] = v;
+  }
+  __syncthreads();
+  // inverse rotation: Walsh-Hadamard butterflies in Sylvester order
   for (int half = 1; half < D; half <<= 1) {
     for (int t = tid; t < D / 2; t += 256) {
       const int i = (t / half) * 2 * half + (t % half);
@@ -2002,18 +2014,25 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
     }
     __syncthreads();
   }
+  // window values, same thread layout (four bf16 columns per load)
+  {
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const uint2* vw = reinterpret_cast<const uint2*>(a.v_win + (int64_t)h * W * D);
+#pragma unroll 8
+    for (int w = par; w < W; w += NPAR) {
+      const uint2 u = vw[(int64_t)w * C4 + cg];
+      const float f = ew[w];
+      acc.x = fmaf(f, bf16_lo(u.x), acc.x); acc.y = fmaf(f, bf16_hi(u.x), acc.y);
+      acc.z = fmaf(f, bf16_lo(u.y), acc.z); acc.w = fmaf(f, bf16_hi(u.y), acc.w);
+    }
+    red4[par][cg] = acc;
+  }
+  __syncthreads();
   float* out = a.out + ((int64_t)h * a.n_q + qi) * D;
   for (int e = tid; e < D; e += 256) {
-    const float y = ((a.v_signs[e >> 3] >> (e & 7)) & 1) ? -x[e] : x[e];
-    float acc[4] = {y, 0.0f, 0.0f, 0.0f};
-    const uint16_t* vw = a.v_win + (int64_t)h * W * D + e;
-    int w = 0;
-    for (; w + 4 <= W; w += 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = fmaf(ew[w + u], bf16_to_f32(vw[(int64_t)(w + u) * D]), acc[u]);
-    }
-    for (; w < W; ++w) acc[0] = fmaf(ew[w], bf16_to_f32(vw[(int64_t)w * D]), acc[0]);
-    out[e] = (float)((double)((acc[0] + acc[1]) + (acc[2] + acc[3])) / L);
+    float v = ((a.v_signs[e >> 3] >> (e & 7)) & 1) ? -x[e] : x[e];
+    for (int p = 0; p < NPAR; ++p) v += reinterpret_cast<const float*>(red4[p])[e];
+    out[e] = (float)((double)v / L);
   }
 }
 
