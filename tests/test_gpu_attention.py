@@ -200,3 +200,40 @@ def test_attention_reuses_work_and_output():
             _check(got[h], q[h], kc[h], kn[h], vc[h], vn[h], bits, hadamard.signs_from_mask(ks, d),
                    hadamard.signs_from_mask(vs, d), None, None, 1.0 / math.sqrt(d), label="reuse h%d" % h)
         res.append(got)
+
+
+@pytest.mark.parametrize("d", [256, 512])
+def test_attention_config5_full_sampled(d):
+    """Config-5 attention shapes at full size (8 KV heads x 65,536 quantized tokens + a 128-token
+    window, 16 queries), one call as the benchmark makes it; the oracle checks the first and last
+    heads (all their queries) from the GPU's stored codes; every output is finite."""
+    _case("attention config-5 full size d=%d" % d)
+    c = synth.config5_attention(d)
+    H, T, _ = c["k"].shape
+    n_q, bits, m = c["q"].shape[1], c["bits"], c["m"]
+    kst, vst = parity.u8_tensor(c["k_signs"]), parity.u8_tensor(c["v_signs"])
+    Gt = parity.bf16_tensor(c["G"])
+    kcod, knrm, kqb, krn = pq.quantize(parity.bf16_tensor(c["k"]), d, bits, kst, Gt)
+    vcod, vnrm, _, _ = pq.quantize(parity.bf16_tensor(c["v"]), d, bits, vst)
+    qt = parity.bf16_tensor(c["q"])
+    prep = pq.query_prep(qt, kst, Gt)
+    out = pq.attention(prep, (kcod, knrm, kqb, krn), (vcod, vnrm), vst, d, bits, H, n_q, T, m=m,
+                       k_win=parity.bf16_tensor(c["k_win"]), v_win=parity.bf16_tensor(c["v_win"]), q=qt)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    q = numerics.bf16_from_bits(c["q"])
+    D_k = hadamard.signs_from_mask(c["k_signs"], d)
+    D_v = hadamard.signs_from_mask(c["v_signs"], d)
+    G = numerics.bf16_from_bits(c["G"])
+    for h in (0, H - 1):
+        kc = kcod[h * T:(h + 1) * T].cpu().numpy()
+        vc = vcod[h * T:(h + 1) * T].cpu().numpy()
+        kn = parity.f16_values(knrm[h * T:(h + 1) * T])
+        vn = parity.f16_values(vnrm[h * T:(h + 1) * T])
+        qb = kqb[h * T:(h + 1) * T].cpu().numpy()
+        rn = parity.f16_values(krn[h * T:(h + 1) * T])
+        worst = _check(got[h], q[h], kc, kn, vc, vn, bits, D_k, D_v, numerics.bf16_from_bits(c["k_win"][h]),
+                       numerics.bf16_from_bits(c["v_win"][h]), 1.0 / math.sqrt(d), qb, rn, G,
+                       label="full d=%d head %d" % (d, h))
+        print("[head %d worst err/tol] %.3g" % (h, worst), flush=True)
