@@ -1613,26 +1613,28 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
   const int range = grp * kWaves + wv;
   const bool live = range < a.n_ranges;
 
+  // LDS: the value centroids first (so a code times 4 is its entry's address), then the
+  // query fragments of the head
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int TAB = 4 << pqi::kMaxScoreBits;           // bytes of the centroid table
   const int64_t meta = pqi::prep_off_meta(D, m);
   const int nbytes = (int)(pqi::prep_head_bytes(D, m) - meta);
   {
     const uint4* s4 = reinterpret_cast<const uint4*>(a.prep + (int64_t)head * pqi::prep_head_bytes(D, m) + meta);
-    uint4* d4 = reinterpret_cast<uint4*>(smem);
+    uint4* d4 = reinterpret_cast<uint4*>(smem + TAB);
     for (int i = threadIdx.x; i < nbytes / 16; i += blockDim.x) d4[i] = s4[i];
   }
   // value centroids as fp16 pairs, hi | lo << 16
-  uint32_t* tab = reinterpret_cast<uint32_t*>(smem + nbytes);
   if (threadIdx.x < (1 << BITS)) {
     uint32_t lo;
     const uint32_t hi = f16_split_pair(a.vcent[threadIdx.x], 0.0f, lo);
-    tab[threadIdx.x] = (hi & 0xffffu) | (lo << 16);
+    reinterpret_cast<uint32_t*>(smem)[threadIdx.x] = (hi & 0xffffu) | (lo << 16);
   }
   __syncthreads();
 
-  const float* scale = reinterpret_cast<const float*>(smem);
-  const int* isum = reinterpret_cast<const int*>(smem + 128);
-  const i32x4* fc = reinterpret_cast<const i32x4*>(smem + 256);
+  const float* scale = reinterpret_cast<const float*>(smem + TAB);
+  const int* isum = reinterpret_cast<const int*>(smem + TAB + 128);
+  const i32x4* fc = reinterpret_cast<const i32x4*>(smem + TAB + 256);
   const i32x4* fq = fc + 3 * KC * 64;
 
   const int lane = threadIdx.x & 63;
@@ -1782,16 +1784,18 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t kn = (uint32_t)__shfl((int)((uint32_t)kin.kn | (QJL ? (uint32_t)kin.rn << 16 : 0u)), 4 * g + i);
+      // 2 S - isum = sum_e Q_e (2 u_e - 1) is an int32 (|.| <= sum |Q_e| < 2^31): formed in
+      // wrapping 32-bit arithmetic from the limb sums, exact, then one conversion per plane
       double first = 0.0;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const double S = 16384.0 * (double)acc[p][0][i] + 128.0 * (double)acc[p][1][i] + (double)acc[p][2][i];
-        first += a.alpha[p] * (2.0 * S - (double)sum_c);
+        const uint32_t S = 16384u * (uint32_t)acc[p][0][i] + 128u * (uint32_t)acc[p][1][i] + (uint32_t)acc[p][2][i];
+        first += a.alpha[p] * (double)(int)(2u * S - (uint32_t)sum_c);
       }
       double val = (double)f16_to_f32((uint16_t)(kn & 0xffffu)) / (double)D * (double)isc * first;
       if constexpr (QJL) {
-        const double S = 16384.0 * (double)accq[0][i] + 128.0 * (double)accq[1][i] + (double)accq[2][i];
-        val += (double)f16_to_f32((uint16_t)(kn >> 16)) * cq * (double)isq * (2.0 * S - (double)sum_q);
+        const uint32_t S = 16384u * (uint32_t)accq[0][i] + 128u * (uint32_t)accq[1][i] + (uint32_t)accq[2][i];
+        val += (double)f16_to_f32((uint16_t)(kn >> 16)) * cq * (double)isq * (double)(int)(2u * S - (uint32_t)sum_q);
       }
       z[i] = tile * 16 + 4 * g + i < T ? (float)(val * a.scale_log2) : -INFINITY;
     }
@@ -1827,14 +1831,20 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
     const uint32_t ph0 = f16_split_pair(w[0], w[1], pl0);
     const uint32_t ph1 = f16_split_pair(w[2], w[3], pl1);
     const f16x4 Ah = as_f16x4(ph0, ph1), Al = as_f16x4(pl0, pl1);
-    // --- O += P' C, N-tile by N-tile
+    // --- O += P' C, N-tile by N-tile; byte codes are masked and scaled by 4 a dword at a
+    // time, so each entry address is one byte extract
+    uint32_t va[4][VW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int u = 0; u < VW; ++u) va[i][u] = PK ? vin.vr[i][u] : (vin.vr[i][u] & (CMASK * 0x01010101u)) << 2;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       uint32_t t4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t code = PK ? stream_code<BITS>(vin.vr[i], j) : (vin.vr[i][j >> 2] >> (8 * (j & 3))) & CMASK;
-        t4[i] = tab[code];
+        const uint32_t addr = PK ? stream_code<BITS>(va[i], j) * 4u : __builtin_amdgcn_ubfe(va[i][j >> 2], 8 * (j & 3), 8);
+        t4[i] = *reinterpret_cast<const uint32_t*>(smem + addr);
       }
       const f16x4 Bh = as_f16x4(__builtin_amdgcn_perm(t4[1], t4[0], 0x05040100u),
                                 __builtin_amdgcn_perm(t4[3], t4[2], 0x05040100u));
