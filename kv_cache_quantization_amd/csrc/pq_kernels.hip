@@ -1545,16 +1545,18 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
       for (int i = 0; i < 4; ++i) {
         const int qi = 4 * gq + i;
         if (qi < a.n_q) {
+          // 2 S - isum = sum_e Q_e (2 u_e - 1) is an int32 (|.| <= sum |Q_e| < 2^31): formed in
+          // wrapping 32-bit arithmetic from the limb sums, exact, then one conversion per plane
           double first = 0.0;
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            const double S = 16384.0 * (double)acc[p][0][i] + 128.0 * (double)acc[p][1][i] + (double)acc[p][2][i];
-            first += a.alpha[p] * (2.0 * S - (double)isum[qi]);
+            const uint32_t S = 16384u * (uint32_t)acc[p][0][i] + 128u * (uint32_t)acc[p][1][i] + (uint32_t)acc[p][2][i];
+            first += a.alpha[p] * (double)(int)(2u * S - (uint32_t)isum[qi]);
           }
           double val = n16 * (double)scale[qi] * first;
           if constexpr (QJL) {
-            const double S = 16384.0 * (double)accq[0][i] + 128.0 * (double)accq[1][i] + (double)accq[2][i];
-            val += rn * (double)scale[16 + qi] * (2.0 * S - (double)isum[16 + qi]);
+            const uint32_t S = 16384u * (uint32_t)accq[0][i] + 128u * (uint32_t)accq[1][i] + (uint32_t)accq[2][i];
+            val += rn * (double)scale[16 + qi] * (double)(int)(2u * S - (uint32_t)isum[16 + qi]);
           }
           out[(int64_t)qi * T + tok] = (float)val;
         }
