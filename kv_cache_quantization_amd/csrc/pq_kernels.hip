@@ -1597,6 +1597,11 @@ __device__ __forceinline__ f16x4 as_f16x4(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(f16x4, (u32x2){w0, w1});
 }
 
+// Byte k of x as a 32-bit value (one v_perm_b32: selector 0x0c is a zero byte).
+__device__ __forceinline__ uint32_t byte_at(uint32_t x, int k) {
+  return __builtin_amdgcn_perm(0u, x, 0x0c0c0c00u | (uint32_t)k);
+}
+
 template <int D, int BITS, int KQT, bool PK>
 __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs a) {
   constexpr int KC = D / 64;
@@ -1615,28 +1620,28 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
   const int range = grp * kWaves + wv;
   const bool live = range < a.n_ranges;
 
-  // LDS: the value centroids first (so a code times 4 is its entry's address), then the
-  // query fragments of the head
+  // LDS: the value centroids as a fixed array (a code times 4 is its entry's address, with
+  // no base to add), the query fragments of the head after them
+  __shared__ uint32_t ctab[1 << pqi::kMaxScoreBits];
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int TAB = 4 << pqi::kMaxScoreBits;           // bytes of the centroid table
   const int64_t meta = pqi::prep_off_meta(D, m);
   const int nbytes = (int)(pqi::prep_head_bytes(D, m) - meta);
   {
     const uint4* s4 = reinterpret_cast<const uint4*>(a.prep + (int64_t)head * pqi::prep_head_bytes(D, m) + meta);
-    uint4* d4 = reinterpret_cast<uint4*>(smem + TAB);
+    uint4* d4 = reinterpret_cast<uint4*>(smem);
     for (int i = threadIdx.x; i < nbytes / 16; i += blockDim.x) d4[i] = s4[i];
   }
   // value centroids as fp16 pairs, hi | lo << 16
   if (threadIdx.x < (1 << BITS)) {
     uint32_t lo;
     const uint32_t hi = f16_split_pair(a.vcent[threadIdx.x], 0.0f, lo);
-    reinterpret_cast<uint32_t*>(smem)[threadIdx.x] = (hi & 0xffffu) | (lo << 16);
+    ctab[threadIdx.x] = (hi & 0xffffu) | (lo << 16);
   }
   __syncthreads();
 
-  const float* scale = reinterpret_cast<const float*>(smem + TAB);
-  const int* isum = reinterpret_cast<const int*>(smem + TAB + 128);
-  const i32x4* fc = reinterpret_cast<const i32x4*>(smem + TAB + 256);
+  const float* scale = reinterpret_cast<const float*>(smem);
+  const int* isum = reinterpret_cast<const int*>(smem + 128);
+  const i32x4* fc = reinterpret_cast<const i32x4*>(smem + 256);
   const i32x4* fq = fc + 3 * KC * 64;
 
   const int lane = threadIdx.x & 63;
@@ -1845,8 +1850,11 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
       uint32_t t4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t addr = PK ? stream_code<BITS>(va[i], j) * 4u : __builtin_amdgcn_ubfe(va[i][j >> 2], 8 * (j & 3), 8);
-        t4[i] = *reinterpret_cast<const uint32_t*>(smem + addr);
+        // (a byte select per code is faster up to d = 256; at d = 512, at one wave per SIMD,
+        // the compiler's shift-and-mask measured faster)
+        const uint32_t addr = PK ? stream_code<BITS>(va[i], j) * 4u
+                                 : D >= 512 ? __builtin_amdgcn_ubfe(va[i][j >> 2], 8 * (j & 3), 8) : byte_at(va[i][j >> 2], j & 3);
+        t4[i] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(ctab) + addr);
       }
       const f16x4 Bh = as_f16x4(__builtin_amdgcn_perm(t4[1], t4[0], 0x05040100u),
                                 __builtin_amdgcn_perm(t4[3], t4[2], 0x05040100u));
@@ -2200,8 +2208,7 @@ hipError_t launch_attend_d(int bits, const pqi::AttnArgs& a, hipStream_t s) {
   static_assert(kWaves == pqi::kAttnWaves, "ranges per workgroup");
   if (a.n_parts > 0) {
     const int grid = a.n_heads * (D / pqi::attn_cols(D)) * a.n_parts;
-    const size_t lds = std::max<size_t>((size_t)(pqi::prep_head_bytes(D, a.m) - pqi::prep_off_meta(D, a.m)) +
-                                            4 * (1 << pqi::kMaxScoreBits),
+    const size_t lds = std::max<size_t>((size_t)(pqi::prep_head_bytes(D, a.m) - pqi::prep_off_meta(D, a.m)),
                                         pqi::attn_merge_lds(D));
     hipError_t e = hipErrorInvalidValue;
     switch (bits) {
