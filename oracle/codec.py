@@ -15,6 +15,9 @@ of d = 2^k values:
 Dequantize undoes the steps: centroid lookup, divide by sqrt(d), inverse
 rotation, multiply by the stored norm:
         xhat = n16 . R^T c[code] / sqrt(d) = (n16 / d) . D * (H c[code]).
+For a d that is not a power of two R is block diagonal (see ``hadamard``):
+sqrt(d) R = diag(w) H_b diag(D) with H_b = blockdiag(H_{d_k}) and w = sqrt(d / d_k) on
+block k, so y = w * H_b (D * x) / n and xhat = (n16 / d) . D * (H_b (w * c[code])).
 
 Readings where the pages leave a step open:
   * normalisation uses the unrounded norm n; dequantize and the residual use n16;
@@ -34,7 +37,7 @@ import math
 import numpy as np
 
 from . import lloyd_max
-from .hadamard import sylvester
+from .hadamard import block_sylvester, block_weights
 from .numerics import round_fp16, round_fp32, pack_bits_lsb
 
 BAND = 1e-4   # coordinates this close to a boundary may take either side (parity rule)
@@ -63,11 +66,14 @@ def quantize(x, bits, D):
     norm = np.sqrt(np.sum(x * x, axis=1))
     n16 = round_fp16(norm)
     safe = np.where(norm > 0, norm, 1.0)
-    H = sylvester(d)
+    H = block_sylvester(d)             # sylvester(d) when d is a power of two
     # the rotation is linear, so H (D * x) / n equals H (D * u); rotating the exact
     # input first keeps coordinates that are exactly zero (ties at the middle
     # boundary of a structured block) exactly zero instead of +-1e-17
     z = (x * np.asarray(D, dtype=np.float64)[None, :]) @ H.T
+    w = block_weights(d)               # all ones when d is a power of two
+    if np.any(w != 1.0):
+        z = z * w[None, :]
     y = np.where(norm[:, None] > 0, z / safe[:, None], 0.0)
     y32 = round_fp32(y)
     beta32 = round_fp32(beta)
@@ -100,7 +106,10 @@ def dequantize(codes, n16, bits, D):
     d = codes.shape[1]
     centroids, _, _ = lloyd_max.codebook(bits)
     c = centroids[codes.astype(np.int64)]
-    H = sylvester(d)
+    H = block_sylvester(d)             # sylvester(d) when d is a power of two
+    w = block_weights(d)               # all ones when d is a power of two
+    if np.any(w != 1.0):
+        c = c * w[None, :]
     return (np.asarray(n16, dtype=np.float64)[:, None] / d) * (c @ H.T) * np.asarray(D, dtype=np.float64)[None, :]
 
 

@@ -12,6 +12,13 @@ H[i, j] = (-1)^popcount(i AND j), which satisfies H H^T = d I, and
 R = H . diag(D) / sqrt(d) with D the +-1 sign vector (signs applied first).
 The oracle applies H as a dense matrix: the fast transform is only a faster
 way of computing the same product.
+
+Block sizes that are not powers of two (glq 0.7.2 README, "Advanced / Bit widths": a
+non-power-of-two size is split into power-of-two blocks, 2688 = 2048 + 512 + 128;
+turbopress 0.4.2 README, "Package layout": block-diagonal Walsh-Hadamard times Rademacher
+signs): d is split into the powers of two of its binary expansion, largest first, and
+R = blockdiag(H_{d_1} / sqrt(d_1), H_{d_2} / sqrt(d_2), ...) . diag(D), still orthogonal.
+For a power of two this is the single-block R above.
 """
 
 import math
@@ -46,3 +53,30 @@ def rotation(d, D):
     """R = H . diag(D) / sqrt(d) as a dense float64 matrix."""
     H = sylvester(d)
     return H * np.asarray(D, dtype=np.float64)[None, :] / math.sqrt(d)
+
+
+def block_sizes(d):
+    """Powers of two of d's binary expansion, largest first (2688 -> [2048, 512, 128])."""
+    if d < 1:
+        raise ValueError("d must be positive")
+    return [1 << b for b in range(d.bit_length() - 1, -1, -1) if (d >> b) & 1]
+
+
+def block_sylvester(d):
+    """blockdiag(H_{d_1}, H_{d_2}, ...) over block_sizes(d), entries +-1 or 0 (float64)."""
+    H = np.zeros((d, d))
+    o = 0
+    for s in block_sizes(d):
+        H[o:o + s, o:o + s] = sylvester(s)
+        o += s
+    return H
+
+
+def block_weights(d):
+    """sqrt(d / d_k) for every coordinate of block k: sqrt(d) R = diag(w) . H_b . diag(D)."""
+    return np.concatenate([np.full(s, math.sqrt(d / s)) for s in block_sizes(d)])
+
+
+def block_rotation(d, D):
+    """R = blockdiag(H_{d_k} / sqrt(d_k)) . diag(D) as a dense float64 matrix."""
+    return (block_weights(d)[:, None] / math.sqrt(d)) * block_sylvester(d) * np.asarray(D, dtype=np.float64)[None, :]

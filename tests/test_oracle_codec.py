@@ -210,3 +210,44 @@ def test_pack_codes_rejects_bad_input():
         codec.pack_codes(np.array([[16, 0]]), 4)
     with pytest.raises(ValueError):
         codec.pack_codes(np.zeros((1, 3)), 3)
+
+
+# ---- block sizes that are not powers of two (block-diagonal rotation) ------------------------
+
+@pytest.mark.parametrize("d,bits", [(192, 4), (320, 3), (96, 2), (576, 5)])
+def test_block_diagonal_codec_matches_per_block_rotation(d, bits):
+    """y = sqrt(d) R x / ||x|| with R the block-diagonal rotation, each block rotated by its own
+    power-of-two H (the pinned single-block rotation); dequantize = n16 R^T c / sqrt(d)."""
+    from oracle import hadamard, lloyd_max
+    rng = np.random.default_rng(d * 3 + bits)
+    D = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    x = rng.standard_normal((5, d)) * np.exp(rng.standard_normal((5, 1)))
+    q = codec.quantize(x, bits, D)
+    o = 0
+    y = np.zeros_like(x)
+    for s in hadamard.block_sizes(d):
+        y[:, o:o + s] = math.sqrt(d) * (x[:, o:o + s] @ hadamard.rotation(s, D[o:o + s]).T) / q["norm"][:, None]
+        o += s
+    np.testing.assert_allclose(q["y"], y, atol=1e-12)
+    c = lloyd_max.codebook(bits)[0][q["codes"].astype(np.int64)]
+    ref = np.zeros_like(x)
+    o = 0
+    for s in hadamard.block_sizes(d):
+        ref[:, o:o + s] = (c[:, o:o + s] @ hadamard.rotation(s, D[o:o + s])) * q["n16"][:, None] / math.sqrt(d)
+        o += s
+    np.testing.assert_allclose(codec.dequantize(q["codes"], q["n16"], bits, D), ref, atol=1e-12)
+
+
+def test_block_diagonal_round_trip_mse_near_table():
+    """Isotropic Gaussian blocks of d = 192: the rotated coordinates are close to N(0, 1), so
+    the per-coordinate error of a 4-bit round trip is close to the Lloyd-Max table MSE."""
+    from oracle import lloyd_max
+    d, bits = 192, 4
+    rng = np.random.default_rng(11)
+    D = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    x = rng.standard_normal((4000, d))
+    q = codec.quantize(x, bits, D)
+    xhat = codec.dequantize(q["codes"], q["n16"], bits, D)
+    mse = np.mean(np.sum((x - xhat) ** 2, axis=1) / np.sum(x ** 2, axis=1))
+    table = lloyd_max.codebook(bits)[2]
+    assert abs(mse - table) < 0.05 * table

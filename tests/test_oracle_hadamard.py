@@ -87,3 +87,40 @@ def test_rotated_gaussian_coordinates_are_standard_normal():
     y = math.sqrt(d) * (u @ hadamard.rotation(d, D).T)
     assert abs(np.mean(y)) < 0.01
     assert abs(np.var(y) - 1.0) < 0.01
+
+
+# ---- block-diagonal rotation for sizes that are not powers of two ----------------------------
+
+def test_block_sizes_page_example():
+    """glq 0.7.2 README, "Advanced / Bit widths": 2688 is split as 2048 + 512 + 128."""
+    assert hadamard.block_sizes(2688) == [2048, 512, 128]
+
+
+@pytest.mark.parametrize("d", [1, 3, 96, 192, 320, 448, 576, 1000, 1024])
+def test_block_sizes_binary_expansion(d):
+    s = hadamard.block_sizes(d)
+    assert sum(s) == d and s == sorted(s, reverse=True) and len(set(s)) == len(s)
+    assert all(b & (b - 1) == 0 for b in s)
+    if d & (d - 1) == 0:
+        assert s == [d]
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_block_sylvester_is_sylvester_for_powers_of_two(d):
+    assert np.array_equal(hadamard.block_sylvester(d), hadamard.sylvester(d))
+    assert np.all(hadamard.block_weights(d) == 1.0)
+
+
+@pytest.mark.parametrize("d", [3, 96, 192, 320, 576])
+def test_block_rotation_orthogonal_and_per_block(d):
+    rng = np.random.default_rng(d)
+    D = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    R = hadamard.block_rotation(d, D)
+    np.testing.assert_allclose(R @ R.T, np.eye(d), atol=1e-12)
+    # built slice by slice from the power-of-two rotation of each block
+    x = rng.standard_normal(d)
+    o = 0
+    for s in hadamard.block_sizes(d):
+        ref = hadamard.rotation(s, D[o:o + s]) @ x[o:o + s]
+        np.testing.assert_allclose((R @ x)[o:o + s], ref, atol=1e-12)
+        o += s
