@@ -321,6 +321,30 @@ int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_
                         const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
                         const uint16_t* q, float sm_scale, void* work, float* out, void* stream);
 
+/*
+ * Block sizes that are not powers of two (glq 0.7.2 README, "Advanced / Bit widths": a size
+ * split into power-of-two blocks, 2688 = 2048 + 512 + 128; turbopress 0.4.2 README, "Package
+ * layout": block-diagonal Walsh-Hadamard times Rademacher signs).  The codec of pq_quantize
+ * with R = blockdiag(H_{d_k} / sqrt(d_k)) diag(D), d_k the powers of two of d's binary
+ * expansion, largest first:
+ *   y_k = sqrt(d / d_k) H_k (D x)_k / ||x||,  code_i = #{j : y_i > beta_j},  n16 = fp16(||x||),
+ *   xhat_k = n16 / sqrt(d d_k) . D_k * (H_k c_k).
+ * For a power of two this is the pq_quantize codec (codes may differ from pq_quantize's only
+ * where a coordinate lies on the fp32 rounding edge of a boundary).
+ *   d          a multiple of 32 in 64 .. 4096 (PQ_EINVAL if not a multiple of 32,
+ *              PQ_EUNSUPPORTED outside the range)
+ *   bits       1 .. 8; no QJL residual stage
+ *   x          n_blocks * d values, fp32 or bf16 (in_dtype), 4-byte aligned
+ *   signs      d/8-byte rotation sign mask (device)
+ *   codes      out, n_blocks * d bytes; norms out, n_blocks fp16
+ * pq_dequantize_bd: codes and norms as written above -> out, n_blocks * d values of
+ * out_dtype (fp32 or bf16 RNE), 4-byte aligned.  Asynchronous on `stream`, no allocation.
+ */
+int pq_quantize_bd(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
+                   uint8_t* codes, uint16_t* norms, void* stream);
+int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                     const uint8_t* signs, int out_dtype, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

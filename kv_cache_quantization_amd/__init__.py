@@ -56,6 +56,8 @@ def _load():
         "pq_score": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
         "pq_score_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
         "pq_attention_work_bytes": ([I, I, L], L),
+        "pq_quantize_bd": ([I, I, I, P, L, P, P, P, P], I),
+        "pq_dequantize_bd": ([I, I, P, P, L, P, I, P, P], I),
         "pq_attention": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P], I),
         "pq_attention_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P],
                                 I),
@@ -72,7 +74,7 @@ EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", 
            "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
            "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
            "pq_query_prep", "pq_score", "pq_score_packed", "pq_attention_work_bytes", "pq_attention",
-           "pq_attention_packed")
+           "pq_attention_packed", "pq_quantize_bd", "pq_dequantize_bd")
 
 
 def lib():
@@ -346,4 +348,39 @@ def attention(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m=0, k_
     _check(fn(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(k_codes), _ptr(k_norms), _ptr(k_bits), _ptr(k_rn),
               _ptr(v_codes), _ptr(v_norms), _ptr(v_signs), n_win, _ptr(k_win), _ptr(v_win), _ptr(q),
               float(sm_scale), _ptr(work), _ptr(out), _stream()), name)
+    return out
+
+
+def quantize_bd(x, d, bits, signs, out=None):
+    """Codec with the block-diagonal rotation, for block sizes d that are not powers of two
+    (any multiple of 32 in 64..4096): x fp32 or bf16 with numel a multiple of d.
+    Returns (codes uint8 [n_blocks, d], norms fp16 [n_blocks])."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(signs, "signs", (torch.uint8,))
+    if x.numel() % d:
+        raise ValueError("x.numel() must be a multiple of d")
+    n = x.numel() // d
+    if out is None:
+        out = (torch.empty((n, d), dtype=torch.uint8, device=x.device),
+               torch.empty((n,), dtype=torch.float16, device=x.device))
+    codes, norms = out
+    _check(_lib.pq_quantize_bd(d, bits, PQ_BF16 if x.dtype == torch.bfloat16 else PQ_F32, _ptr(x), n,
+                               _ptr(signs), _ptr(codes), _ptr(norms), _stream()), "pq_quantize_bd")
+    return codes, norms
+
+
+def dequantize_bd(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None):
+    """Inverse of ``quantize_bd``: [n_blocks, d] of out_dtype (fp32 or bf16)."""
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(norms, "norms", (torch.float16,))
+    _dev(signs, "signs", (torch.uint8,))
+    n = norms.numel()
+    if codes.numel() != n * d:
+        raise ValueError("codes do not match norms and d")
+    if out is None:
+        out = torch.empty((n, d), dtype=out_dtype, device=codes.device)
+    _dev(out, "out", (torch.float32, torch.bfloat16))
+    _check(_lib.pq_dequantize_bd(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs),
+                                 PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32, _ptr(out), _stream()),
+           "pq_dequantize_bd")
     return out

@@ -210,6 +210,19 @@ int dequantize_impl(int d, int bits, const uint8_t* codes, const uint16_t* norms
   return hip_status(pqi::launch_dequantize(d, out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
 }
 
+// block-diagonal rotation: d a multiple of 32 in [64, 4096]
+int check_d_bd(int d) {
+  if (d <= 0 || (d % 32) != 0) return PQ_EINVAL;
+  if (d < pqi::kBdMinD || d > pqi::kBdMaxD) return PQ_EUNSUPPORTED;
+  return PQ_OK;
+}
+
+void fill_bd_codebook(int bits, pqi::BdArgs& a) {
+  const Codebook& cb = codebook(bits);
+  for (int k = 0; k < (1 << bits); ++k) a.cent[k] = (float)cb.c[k];
+  for (int k = 0; k + 1 < (1 << bits); ++k) a.beta[k] = (float)cb.beta[k];
+}
+
 }  // namespace
 
 extern "C" {
@@ -520,6 +533,44 @@ int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_
                         const uint16_t* q, float sm_scale, void* work, float* out, void* stream) {
   return attention_impl(d, bits, m, n_heads, n_q, n_tok, prep, k_codes, k_norms, k_qjl_bits, k_rnorms, v_codes,
                         v_norms, v_signs, n_win, k_win, v_win, q, sm_scale, work, out, 1, stream);
+}
+
+int pq_quantize_bd(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
+                   uint8_t* codes, uint16_t* norms, void* stream) {
+  int st = check_d_bd(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (in_dtype != PQ_F32 && in_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!x || !signs || !codes || !norms) return PQ_EINVAL;
+  if (!aligned(x, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::BdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = x; a.codes = codes; a.norms = norms; a.signs = signs; a.n_blocks = n_blocks; a.d = d; a.bits = bits;
+  fill_bd_codebook(bits, a);
+  return hip_status(pqi::launch_quantize_bd(in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                     const uint8_t* signs, int out_dtype, void* out, void* stream) {
+  int st = check_d_bd(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (out_dtype != PQ_F32 && out_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!codes || !norms || !signs || !out) return PQ_EINVAL;
+  if (!aligned(out, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::BdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ccodes = codes; a.cnorms = norms; a.signs = signs; a.out = out; a.n_blocks = n_blocks; a.d = d; a.bits = bits;
+  fill_bd_codebook(bits, a);
+  return hip_status(pqi::launch_dequantize_bd(out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -219,6 +219,25 @@ struct AttnArgs {
   float vcent[1 << kMaxScoreBits];   // value codebook centroids
 };
 
+// Block-diagonal rotation for block sizes d that are not powers of two: d is split into the
+// powers of two of its binary expansion, largest first, and each part gets its own
+// Walsh-Hadamard transform; y = sqrt(d / d_k) H_k (D x)_k / ||x|| on part k.
+constexpr int kBdMinD = 64, kBdMaxD = 4096;   // d a multiple of 32 in this range
+
+struct BdArgs {
+  const void* x;              // quantize input [n_blocks][d], fp32 or bf16
+  uint8_t* codes;             // [n_blocks][d], one code per byte
+  const uint8_t* ccodes;      // dequantize input codes
+  uint16_t* norms;            // quantize output, fp16
+  const uint16_t* cnorms;     // dequantize input norms
+  void* out;                  // dequantize output [n_blocks][d], fp32 or bf16
+  const uint8_t* signs;       // d/8 bytes
+  int64_t n_blocks;
+  int d, bits;
+  float cent[1 << kMaxBits];  // centroids, ascending
+  float beta[(1 << kMaxBits) - 1];   // boundaries, ascending
+};
+
 struct LaunchCfg {
   int cu_count;
   int max_lds;       // bytes of LDS one workgroup may use
@@ -235,5 +254,7 @@ hipError_t launch_score(const ScoreArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s);
 hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_attention(int d, int bits, const AttnArgs& a, hipStream_t s);
+hipError_t launch_quantize_bd(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
 
 }  // namespace pqi

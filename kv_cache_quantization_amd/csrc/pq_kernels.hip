@@ -2057,6 +2057,108 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
 }
 
 // ------------------------------------------------------------------------------------------
+// Block-diagonal rotation (block sizes that are not powers of two).  One wave per block with a
+// grid stride; the block lives in LDS as fp32 (d floats per wave), each power-of-two part is
+// transformed by in-LDS butterflies (a wave's LDS operations complete in program order, so no
+// barrier is needed between stages), and the per-part factor sqrt(d / d_k) comes from a table
+// shared by the workgroup.  Codes by bisection over the boundaries (count of boundaries below).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void bd_butterflies(float* xb, int d, int lane) {
+  int o = 0;
+  for (int b = 31 - __builtin_clz((unsigned)d); b >= 0; --b) {
+    if (!((d >> b) & 1)) continue;
+    const int s = 1 << b;
+    for (int lh = 0; (1 << lh) < s; ++lh) {
+      const int half = 1 << lh;
+      for (int t = lane; t < s / 2; t += 64) {
+        const int i = o + ((t >> lh) << (lh + 1)) + (t & (half - 1));
+        const float x0 = xb[i], x1 = xb[i + half];
+        xb[i] = x0 + x1;
+        xb[i + half] = x0 - x1;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    o += s;
+  }
+}
+
+// weight sqrt(d / d_k) of every element (part k holds it), for the workgroup
+__device__ __forceinline__ void bd_weights(float* wt, int d) {
+  for (int e = threadIdx.x; e < d; e += blockDim.x) {
+    int o = 0, s = 0;
+    for (int b = 31 - __builtin_clz((unsigned)d); b >= 0; --b) {
+      if (!((d >> b) & 1)) continue;
+      s = 1 << b;
+      if (e < o + s) break;
+      o += s;
+    }
+    wt[e] = sqrtf((float)d / (float)s);
+  }
+}
+
+template <bool IN_BF16>
+__global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a) {
+  extern __shared__ float bsm[];                         // [d] weights, then [4 waves][d] blocks
+  const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ float beta[(1 << pqi::kMaxBits) - 1];
+  float* wt = bsm;
+  float* xb = bsm + d + wv * d;
+  const int nb = (1 << a.bits) - 1;
+  for (int j = threadIdx.x; j < nb; j += blockDim.x) beta[j] = a.beta[j];
+  bd_weights(wt, d);
+  __syncthreads();
+  const int64_t n_waves = (int64_t)gridDim.x * 4;
+  for (int64_t blk = (int64_t)blockIdx.x * 4 + wv; blk < a.n_blocks; blk += n_waves) {
+    double ss = 0.0;
+    for (int e = lane; e < d; e += 64) {
+      const float v = IN_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[blk * d + e])
+                              : static_cast<const float*>(a.x)[blk * d + e];
+      ss += (double)v * (double)v;
+      xb[e] = ((a.signs[e >> 3] >> (e & 7)) & 1) ? -v : v;
+    }
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float n = (float)sqrt(ss);
+    const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+    bd_butterflies(xb, d, lane);
+    for (int e = lane; e < d; e += 64) {
+      const float y = xb[e] * wt[e] * inv;
+      int code = 0;
+      for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
+        if (y > beta[code + step - 1]) code += step;
+      a.codes[blk * d + e] = (uint8_t)code;
+    }
+    if (lane == 0) a.norms[blk] = f32_to_f16((float)sqrt(ss));
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs a) {
+  extern __shared__ float bsm[];
+  const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ float cent[1 << pqi::kMaxBits];
+  float* wt = bsm;
+  float* xb = bsm + d + wv * d;
+  const uint32_t cmask = (1u << a.bits) - 1u;
+  for (int j = threadIdx.x; j < (1 << a.bits); j += blockDim.x) cent[j] = a.cent[j];
+  bd_weights(wt, d);
+  __syncthreads();
+  const int64_t n_waves = (int64_t)gridDim.x * 4;
+  for (int64_t blk = (int64_t)blockIdx.x * 4 + wv; blk < a.n_blocks; blk += n_waves) {
+    for (int e = lane; e < d; e += 64) xb[e] = cent[a.ccodes[blk * d + e] & cmask] * wt[e];
+    bd_butterflies(xb, d, lane);
+    const float scale = f16_to_f32(a.cnorms[blk]) * (1.0f / (float)d);
+    for (int e = lane; e < d; e += 64) {
+      float v = xb[e] * scale;
+      if ((a.signs[e >> 3] >> (e & 7)) & 1) v = -v;
+      if (OUT_BF16) static_cast<uint16_t*>(a.out)[blk * d + e] = f32_to_bf16(v);
+      else static_cast<float*>(a.out)[blk * d + e] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // launch helpers
 // ------------------------------------------------------------------------------------------
 int grid_for(int64_t n_tiles, const pqi::LaunchCfg& c, int per_cu) {
@@ -2310,6 +2412,24 @@ hipError_t launch_attention(int d, int bits, const AttnArgs& a, hipStream_t s) {
 #endif  // PQ_UNIT 4
 
 #if PQ_UNIT < 0 || PQ_UNIT == 2
+hipError_t launch_quantize_bd(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  const size_t lds = (size_t)a.d * 5 * sizeof(float);
+  const int64_t want = (a.n_blocks + 3) / 4;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
+  if (in_bf16) hipLaunchKernelGGL(pq_quantize_bd_kernel<true>, grid, 256, lds, s, a);
+  else hipLaunchKernelGGL(pq_quantize_bd_kernel<false>, grid, 256, lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  const size_t lds = (size_t)a.d * 5 * sizeof(float);
+  const int64_t want = (a.n_blocks + 3) / 4;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
+  if (out_bf16) hipLaunchKernelGGL(pq_dequantize_bd_kernel<true>, grid, 256, lds, s, a);
+  else hipLaunchKernelGGL(pq_dequantize_bd_kernel<false>, grid, 256, lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(int d, bool in_bf16, const QuantArgs& a, const LaunchCfg& c, hipStream_t s) {
   return d <= 128 ? launch_quantize_lo(d, in_bf16, a, c, s) : launch_quantize_hi(d, in_bf16, a, c, s);
 }

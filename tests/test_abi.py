@@ -245,3 +245,24 @@ def test_attention_entry_points_validate():
         assert att(fn, scale=F(float("inf"))) == pq.PQ_EINVAL
         assert att(fn, h=0) == pq.PQ_OK
         assert att(fn, nq=0) == pq.PQ_OK
+
+
+def test_block_diagonal_entry_points_validate():
+    lib = pq.lib()
+    # pq_quantize_bd(d, bits, in_dtype, x, n, signs, codes, norms, stream)
+    q = lambda d=192, bits=4, dt=pq.PQ_BF16, x=P16, n=16, s=P16, c=P16, nm=P16: lib.pq_quantize_bd(
+        d, bits, dt, x, n, s, c, nm, NUL)
+    assert q(d=100) == pq.PQ_EINVAL
+    assert q(d=32) == pq.PQ_EUNSUPPORTED
+    assert q(d=4128) == pq.PQ_EUNSUPPORTED
+    assert q(bits=0) == pq.PQ_EINVAL and q(bits=9) == pq.PQ_EINVAL
+    assert q(dt=7) == pq.PQ_EINVAL
+    assert q(x=NUL) == pq.PQ_EINVAL and q(c=NUL) == pq.PQ_EINVAL
+    assert q(nm=ctypes.c_void_p(0x10001)) == pq.PQ_EINVAL
+    assert q(n=-1) == pq.PQ_EINVAL
+    assert q(n=0) == pq.PQ_OK
+    # pq_dequantize_bd(d, bits, codes, norms, n, signs, out_dtype, out, stream)
+    assert lib.pq_dequantize_bd(100, 4, P16, P16, 16, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.pq_dequantize_bd(192, 4, P16, P16, 16, P16, 3, P16, NUL) == pq.PQ_EINVAL
+    assert lib.pq_dequantize_bd(192, 4, NUL, P16, 16, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_EINVAL
+    assert lib.pq_dequantize_bd(192, 4, P16, P16, 0, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_OK
