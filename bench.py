@@ -46,6 +46,7 @@ def _args():
     ap.add_argument("--no-tsq", action="store_true", help="skip the config-5 two-stage leg")
     ap.add_argument("--no-grouped", action="store_true", help="skip the config-3 grouped pass")
     ap.add_argument("--no-attn", action="store_true", help="skip the config-5 decode-attention leg")
+    ap.add_argument("--no-bd", action="store_true", help="skip the block-diagonal rotation leg (d=2688)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -424,6 +425,37 @@ def attn_leg(pq, synth, torch, steps, warmup):
     return out
 
 
+def bd_leg(pq, synth, torch, steps, warmup):
+    """Block-diagonal rotation for a block size that is not a power of two: a 16384 x 2688 bf16
+    weight (the config-2 recipe at the pages' 2688 width) in blocks of d = 2688 = 2048 + 512 +
+    128, 4-bit codes; quantize and dequantize (bf16 out)."""
+    dev = torch.device("cuda:0")
+    d, bits, rows = 2688, 4, 16384
+    xu, _ = synth.weight_with_outlier_entries(5, rows, d)
+    x = torch.from_numpy(xu.view(np.int16)).view(torch.bfloat16).to(dev)
+    del xu
+    st = torch.from_numpy(synth.sign_mask(synth.BASE_SEED + d, d)).to(dev)
+    codes, norms = pq.quantize_bd(x, d, bits, st)
+    out = torch.empty((rows, d), dtype=torch.bfloat16, device=dev)
+
+    def quant(k):
+        pq.quantize_bd(x, d, bits, st, out=(codes, norms))
+
+    def dequant(k):
+        pq.dequantize_bd(codes, norms, d, bits, st, out=out)
+
+    for k in range(warmup):
+        quant(k), dequant(k)
+    tq, td = timed(torch, quant, steps), timed(torch, dequant, steps)
+    n = rows * d
+    qb = n * 2 + n + rows * 2
+    db = n + rows * 2 + n * 2
+    return {"bd_config": "16384 x 2688 bf16 weight (config-2 recipe), blocks of d=2688 = 2048+512+128, 4-bit",
+            "bd_quantize_us": round(tq * 1e6, 2), "bd_quantize_hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4),
+            "bd_dequantize_us": round(td * 1e6, 2), "bd_dequantize_hbm_frac": round(db / td / 1e9 / HBM_PEAK_GBS, 4),
+            "bd_quantize_algorithmic_bytes": qb, "bd_dequantize_algorithmic_bytes": db}
+
+
 def grouped_leg(pq, synth, torch, reps, packed=False):
     """Config 3: one streamed quantize pass and one dequantize pass over the 224 tensors of
     a 32-layer 7B-style decoder (4-bit codes, d=128), each tensor one launch with its own
@@ -587,6 +619,8 @@ def main():
         rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
     if not args.no_tsq:
         rec["parts"].update(tsq_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+    if not args.no_bd:
+        rec["parts"].update(bd_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_attn:
         rec["parts"].update(attn_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_grouped:

@@ -2063,21 +2063,44 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
 // barrier is needed between stages), and the per-part factor sqrt(d / d_k) comes from a table
 // shared by the workgroup.  Codes by bisection over the boundaries (count of boundaries below).
 // ------------------------------------------------------------------------------------------
+// R stages of the butterfly of one part (offset o, size s) starting at element bit b0: each
+// lane takes groups of 2^R elements spaced 2^b0 apart, transforms them in registers and writes
+// them back (R stages per LDS round trip instead of one).
+template <int R>
+__device__ __forceinline__ void bd_pass(float* xb, int o, int s, int b0, int lane) {
+  const int groups = s >> R;
+  for (int t = lane; t < groups; t += 64) {
+    const int lo = t & ((1 << b0) - 1);
+    const int i0 = o + ((t >> b0) << (b0 + R)) + lo;
+    float v[1 << R];
+#pragma unroll
+    for (int k = 0; k < (1 << R); ++k) v[k] = xb[i0 + (k << b0)];
+#pragma unroll
+    for (int h = 1; h < (1 << R); h <<= 1)
+#pragma unroll
+      for (int k = 0; k < (1 << R); ++k)
+        if (!(k & h)) {
+          const float x0 = v[k], x1 = v[k + h];
+          v[k] = x0 + x1;
+          v[k + h] = x0 - x1;
+        }
+#pragma unroll
+    for (int k = 0; k < (1 << R); ++k) xb[i0 + (k << b0)] = v[k];
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Walsh-Hadamard transform of every power-of-two part of the block in LDS (parts largest
+// first, as d's binary expansion), three stages per pass.
 __device__ __forceinline__ void bd_butterflies(float* xb, int d, int lane) {
   int o = 0;
   for (int b = 31 - __builtin_clz((unsigned)d); b >= 0; --b) {
     if (!((d >> b) & 1)) continue;
     const int s = 1 << b;
-    for (int lh = 0; (1 << lh) < s; ++lh) {
-      const int half = 1 << lh;
-      for (int t = lane; t < s / 2; t += 64) {
-        const int i = o + ((t >> lh) << (lh + 1)) + (t & (half - 1));
-        const float x0 = xb[i], x1 = xb[i + half];
-        xb[i] = x0 + x1;
-        xb[i + half] = x0 - x1;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
+    int b0 = 0;
+    for (; b0 + 3 <= b; b0 += 3) bd_pass<3>(xb, o, s, b0, lane);
+    if (b - b0 == 2) bd_pass<2>(xb, o, s, b0, lane);
+    else if (b - b0 == 1) bd_pass<1>(xb, o, s, b0, lane);
     o += s;
   }
 }
@@ -2120,12 +2143,25 @@ __global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a
     const float n = (float)sqrt(ss);
     const float inv = n > 0.0f ? 1.0f / n : 0.0f;
     bd_butterflies(xb, d, lane);
-    for (int e = lane; e < d; e += 64) {
-      const float y = xb[e] * wt[e] * inv;
-      int code = 0;
+    // eight coordinates per lane bisect in lockstep (eight boundary reads in flight per step)
+    for (int base = 0; base < d; base += 512) {
+      float y[8];
+      int code[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(base + 64 * u + lane, d - 1);
+        y[u] = xb[e] * wt[e] * inv;
+        code[u] = 0;
+      }
       for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
-        if (y > beta[code + step - 1]) code += step;
-      a.codes[blk * d + e] = (uint8_t)code;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (y[u] > beta[code[u] + step - 1]) code[u] += step;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = base + 64 * u + lane;
+        if (e < d) a.codes[blk * d + e] = (uint8_t)code[u];
+      }
     }
     if (lane == 0) a.norms[blk] = f32_to_f16((float)sqrt(ss));
     __builtin_amdgcn_wave_barrier();
