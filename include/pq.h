@@ -334,11 +334,11 @@ int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_
  *   d          a multiple of 32 in 64 .. 4096 (PQ_EINVAL if not a multiple of 32,
  *              PQ_EUNSUPPORTED outside the range)
  *   bits       1 .. 8; no QJL residual stage
- *   x          n_blocks * d values, fp32 or bf16 (in_dtype), 4-byte aligned
+ *   x          n_blocks * d values, fp32 or bf16 (in_dtype), 16-byte aligned
  *   signs      d/8-byte rotation sign mask (device)
- *   codes      out, n_blocks * d bytes; norms out, n_blocks fp16
+ *   codes      out, n_blocks * d bytes, 16-byte aligned; norms out, n_blocks fp16
  * pq_dequantize_bd: codes and norms as written above -> out, n_blocks * d values of
- * out_dtype (fp32 or bf16 RNE), 4-byte aligned.  Asynchronous on `stream`, no allocation.
+ * out_dtype (fp32 or bf16 RNE), 16-byte aligned.  Asynchronous on `stream`, no allocation.
  */
 int pq_quantize_bd(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,
                    uint8_t* codes, uint16_t* norms, void* stream);

@@ -544,7 +544,7 @@ int pq_quantize_bd(int d, int bits, int in_dtype, const void* x, int64_t n_block
   if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
   if (n_blocks == 0) return PQ_OK;
   if (!x || !signs || !codes || !norms) return PQ_EINVAL;
-  if (!aligned(x, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(norms, 2)) return PQ_EINVAL;
   pqi::LaunchCfg cfg;
   if ((st = launch_cfg(&cfg))) return st;
   pqi::BdArgs a;
@@ -563,7 +563,7 @@ int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norm
   if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
   if (n_blocks == 0) return PQ_OK;
   if (!codes || !norms || !signs || !out) return PQ_EINVAL;
-  if (!aligned(out, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(norms, 2)) return PQ_EINVAL;
   pqi::LaunchCfg cfg;
   if ((st = launch_cfg(&cfg))) return st;
   pqi::BdArgs a;

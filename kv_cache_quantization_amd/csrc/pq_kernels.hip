@@ -2069,38 +2069,81 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
 template <int R>
 __device__ __forceinline__ void bd_pass(float* xb, int o, int s, int b0, int lane) {
   const int groups = s >> R;
-  for (int t = lane; t < groups; t += 64) {
-    const int lo = t & ((1 << b0) - 1);
-    const int i0 = o + ((t >> b0) << (b0 + R)) + lo;
-    float v[1 << R];
+  // four groups per lane at a time: all their reads are issued before any write
+  for (int t0 = 0; t0 < groups; t0 += 256) {
+    float v[4][1 << R];
+    int i0[4];
 #pragma unroll
-    for (int k = 0; k < (1 << R); ++k) v[k] = xb[i0 + (k << b0)];
+    for (int q = 0; q < 4; ++q) {
+      const int t = min(t0 + 64 * q + lane, groups - 1);
+      i0[q] = o + ((t >> b0) << (b0 + R)) + (t & ((1 << b0) - 1));
 #pragma unroll
-    for (int h = 1; h < (1 << R); h <<= 1)
+      for (int k = 0; k < (1 << R); ++k) v[q][k] = xb[i0[q] + (k << b0)];
+    }
 #pragma unroll
-      for (int k = 0; k < (1 << R); ++k)
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int h = 1; h < (1 << R); h <<= 1)
+#pragma unroll
+        for (int k = 0; k < (1 << R); ++k)
+          if (!(k & h)) {
+            const float x0 = v[q][k], x1 = v[q][k + h];
+            v[q][k] = x0 + x1;
+            v[q][k + h] = x0 - x1;
+          }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (t0 + 64 * q + lane < groups)
+#pragma unroll
+        for (int k = 0; k < (1 << R); ++k) xb[i0[q] + (k << b0)] = v[q][k];
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The first log2(G) stages of a part: each lane takes G consecutive elements (16-byte LDS
+// accesses, no bank conflicts) and transforms them in registers.
+template <int G>
+__device__ __forceinline__ void bd_pass_low(float* xb, int o, int s, int lane) {
+  if (lane < s / G) {
+    float4* p = reinterpret_cast<float4*>(xb + o + lane * G);
+    float v[G];
+#pragma unroll
+    for (int q = 0; q < G / 4; ++q) {
+      const float4 w = p[q];
+      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+#pragma unroll
+    for (int h = 1; h < G; h <<= 1)
+#pragma unroll
+      for (int k = 0; k < G; ++k)
         if (!(k & h)) {
           const float x0 = v[k], x1 = v[k + h];
           v[k] = x0 + x1;
           v[k + h] = x0 - x1;
         }
 #pragma unroll
-    for (int k = 0; k < (1 << R); ++k) xb[i0 + (k << b0)] = v[k];
+    for (int q = 0; q < G / 4; ++q) p[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
   }
   __builtin_amdgcn_wave_barrier();
 }
 
 // Walsh-Hadamard transform of every power-of-two part of the block in LDS (parts largest
-// first, as d's binary expansion), three stages per pass.
+// first, as d's binary expansion): the six lowest stages per lane in registers, then three
+// stages per pass over groups whose lanes touch consecutive words.
 __device__ __forceinline__ void bd_butterflies(float* xb, int d, int lane) {
   int o = 0;
   for (int b = 31 - __builtin_clz((unsigned)d); b >= 0; --b) {
     if (!((d >> b) & 1)) continue;
     const int s = 1 << b;
-    int b0 = 0;
-    for (; b0 + 3 <= b; b0 += 3) bd_pass<3>(xb, o, s, b0, lane);
-    if (b - b0 == 2) bd_pass<2>(xb, o, s, b0, lane);
-    else if (b - b0 == 1) bd_pass<1>(xb, o, s, b0, lane);
+    if (s == 32) {
+      bd_pass_low<32>(xb, o, s, lane);
+    } else {
+      bd_pass_low<64>(xb, o, s, lane);
+      int b0 = 6;
+      for (; b0 + 3 <= b; b0 += 3) bd_pass<3>(xb, o, s, b0, lane);
+      if (b - b0 == 2) bd_pass<2>(xb, o, s, b0, lane);
+      else if (b - b0 == 1) bd_pass<1>(xb, o, s, b0, lane);
+    }
     o += s;
   }
 }
@@ -2119,8 +2162,11 @@ __device__ __forceinline__ void bd_weights(float* wt, int d) {
   }
 }
 
+// Global accesses are 16 bytes per lane, every load of a block issued before the first use.
 template <bool IN_BF16>
 __global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a) {
+  constexpr int CH = IN_BF16 ? 8 : 4;                    // input values per 16-byte load
+  constexpr int ML = pqi::kBdMaxD / CH / 64;             // loads per lane per block, at most
   extern __shared__ float bsm[];                         // [d] weights, then [4 waves][d] blocks
   const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   __shared__ float beta[(1 << pqi::kMaxBits) - 1];
@@ -2130,37 +2176,74 @@ __global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a
   for (int j = threadIdx.x; j < nb; j += blockDim.x) beta[j] = a.beta[j];
   bd_weights(wt, d);
   __syncthreads();
+  const int nch = d / CH, n16 = d / 16;
   const int64_t n_waves = (int64_t)gridDim.x * 4;
+  // the next block's input loads while this one is transformed and coded
+  auto fetch = [&](int64_t blk, uint4 (&raw)[ML]) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(a.x) +
+                                                      min(blk, a.n_blocks - 1) * d * (IN_BF16 ? 2 : 4));
+#pragma unroll
+    for (int u = 0; u < ML; ++u) {
+      const int c = lane + 64 * u;
+      raw[u] = c < nch ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 raw[ML];
+  fetch((int64_t)blockIdx.x * 4 + wv, raw);
   for (int64_t blk = (int64_t)blockIdx.x * 4 + wv; blk < a.n_blocks; blk += n_waves) {
     double ss = 0.0;
-    for (int e = lane; e < d; e += 64) {
-      const float v = IN_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[blk * d + e])
-                              : static_cast<const float*>(a.x)[blk * d + e];
-      ss += (double)v * (double)v;
-      xb[e] = ((a.signs[e >> 3] >> (e & 7)) & 1) ? -v : v;
+#pragma unroll
+    for (int u = 0; u < ML; ++u) {
+      const int c = lane + 64 * u;
+      if (c < nch) {
+        float v[CH];
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          v[j] = IN_BF16 ? ((j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1])) : __uint_as_float(w[j]);
+        const uint32_t sb = a.signs[(c * CH) >> 3] >> ((c * CH) & 7);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          ss += (double)v[j] * (double)v[j];
+          if ((sb >> j) & 1) v[j] = -v[j];
+        }
+        float4* dst = reinterpret_cast<float4*>(xb + c * CH);
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
     }
+    fetch(blk + n_waves, raw);
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
     const float n = (float)sqrt(ss);
     const float inv = n > 0.0f ? 1.0f / n : 0.0f;
     bd_butterflies(xb, d, lane);
-    // eight coordinates per lane bisect in lockstep (eight boundary reads in flight per step)
-    for (int base = 0; base < d; base += 512) {
-      float y[8];
-      int code[8];
+    // sixteen consecutive coordinates per lane bisect in lockstep; their codes leave as one
+    // 16-byte store
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = min(base + 64 * u + lane, d - 1);
-        y[u] = xb[e] * wt[e] * inv;
-        code[u] = 0;
-      }
-      for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
+    for (int u = 0; u < pqi::kBdMaxD / 16 / 64; ++u) {
+      const int c = lane + 64 * u;
+      if (c < n16) {
+        float y[16];
+        int code[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (y[u] > beta[code[u] + step - 1]) code[u] += step;
+        for (int q = 0; q < 4; ++q) {
+          const float4 xv = reinterpret_cast<const float4*>(xb + 16 * c)[q];
+          const float4 wq = reinterpret_cast<const float4*>(wt + 16 * c)[q];
+          y[4 * q] = xv.x * wq.x * inv; y[4 * q + 1] = xv.y * wq.y * inv;
+          y[4 * q + 2] = xv.z * wq.z * inv; y[4 * q + 3] = xv.w * wq.w * inv;
+        }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = base + 64 * u + lane;
-        if (e < d) a.codes[blk * d + e] = (uint8_t)code[u];
+        for (int j = 0; j < 16; ++j) code[j] = 0;
+        for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (y[j] > beta[code[j] + step - 1]) code[j] += step;
+        uint32_t pk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pk[q] = (uint32_t)code[4 * q] | ((uint32_t)code[4 * q + 1] << 8) | ((uint32_t)code[4 * q + 2] << 16) |
+                  ((uint32_t)code[4 * q + 3] << 24);
+        reinterpret_cast<uint4*>(a.codes + blk * d)[c] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     }
     if (lane == 0) a.norms[blk] = f32_to_f16((float)sqrt(ss));
@@ -2170,6 +2253,7 @@ __global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs a) {
+  constexpr int CH = OUT_BF16 ? 8 : 4;                   // output values per 16-byte store
   extern __shared__ float bsm[];
   const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   __shared__ float cent[1 << pqi::kMaxBits];
@@ -2179,16 +2263,63 @@ __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs
   for (int j = threadIdx.x; j < (1 << a.bits); j += blockDim.x) cent[j] = a.cent[j];
   bd_weights(wt, d);
   __syncthreads();
+  const int n16 = d / 16, nch = d / CH;
   const int64_t n_waves = (int64_t)gridDim.x * 4;
+  constexpr int ML = pqi::kBdMaxD / 16 / 64;
+  // the next block's codes load while this one is transformed and written
+  auto fetch = [&](int64_t blk, uint4 (&raw)[ML]) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.ccodes + min(blk, a.n_blocks - 1) * d);
+#pragma unroll
+    for (int u = 0; u < ML; ++u) {
+      const int c = lane + 64 * u;
+      raw[u] = c < n16 ? src[c] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 raw[ML];
+  fetch((int64_t)blockIdx.x * 4 + wv, raw);
   for (int64_t blk = (int64_t)blockIdx.x * 4 + wv; blk < a.n_blocks; blk += n_waves) {
-    for (int e = lane; e < d; e += 64) xb[e] = cent[a.ccodes[blk * d + e] & cmask] * wt[e];
+#pragma unroll
+    for (int u = 0; u < ML; ++u) {
+      const int c = lane + 64 * u;
+      if (c < n16) {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 wq = reinterpret_cast<const float4*>(wt + 16 * c)[q];
+          reinterpret_cast<float4*>(xb + 16 * c)[q] =
+              make_float4(cent[w[q] & cmask] * wq.x, cent[(w[q] >> 8) & cmask] * wq.y,
+                          cent[(w[q] >> 16) & cmask] * wq.z, cent[(w[q] >> 24) & cmask] * wq.w);
+        }
+      }
+    }
+    fetch(blk + n_waves, raw);
     bd_butterflies(xb, d, lane);
     const float scale = f16_to_f32(a.cnorms[blk]) * (1.0f / (float)d);
-    for (int e = lane; e < d; e += 64) {
-      float v = xb[e] * scale;
-      if ((a.signs[e >> 3] >> (e & 7)) & 1) v = -v;
-      if (OUT_BF16) static_cast<uint16_t*>(a.out)[blk * d + e] = f32_to_bf16(v);
-      else static_cast<float*>(a.out)[blk * d + e] = v;
+#pragma unroll
+    for (int u = 0; u < pqi::kBdMaxD / CH / 64; ++u) {
+      const int c = lane + 64 * u;
+      if (c < nch) {
+        float v[CH];
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) {
+          const float4 xv = reinterpret_cast<const float4*>(xb + CH * c)[q];
+          v[4 * q] = xv.x; v[4 * q + 1] = xv.y; v[4 * q + 2] = xv.z; v[4 * q + 3] = xv.w;
+        }
+        const uint32_t sb = a.signs[(c * CH) >> 3] >> ((c * CH) & 7);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          v[j] *= scale;
+          if ((sb >> j) & 1) v[j] = -v[j];
+        }
+        uint4 o;
+        if constexpr (OUT_BF16) {
+          o = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7]));
+        } else {
+          o = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+        }
+        reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.out) + blk * d * (OUT_BF16 ? 2 : 4))[c] = o;
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }

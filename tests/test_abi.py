@@ -259,6 +259,7 @@ def test_block_diagonal_entry_points_validate():
     assert q(dt=7) == pq.PQ_EINVAL
     assert q(x=NUL) == pq.PQ_EINVAL and q(c=NUL) == pq.PQ_EINVAL
     assert q(nm=ctypes.c_void_p(0x10001)) == pq.PQ_EINVAL
+    assert q(x=ctypes.c_void_p(0x10008)) == pq.PQ_EINVAL and q(c=ctypes.c_void_p(0x10008)) == pq.PQ_EINVAL
     assert q(n=-1) == pq.PQ_EINVAL
     assert q(n=0) == pq.PQ_OK
     # pq_dequantize_bd(d, bits, codes, norms, n, signs, out_dtype, out, stream)
