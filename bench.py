@@ -126,7 +126,7 @@ def summarize(run_dir):
     trace_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/prof_trace -o trace -- "
                  "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-grouped")
     lines = ["# Kernel durations of the benchmark (config 2 codec, config 4 QJL leg, config 5 two-stage and "
-             "decode-attention legs), one MI355X",
+             "decode-attention legs, block-diagonal leg), one MI355X",
              "", "command: " + trace_cmd, "kernel source hash: " + kernel_source_hash(), "",
              "%-58s %6s %12s %10s %10s" % ("kernel", "calls", "average_ns", "min_ns", "max_ns")]
     for r in rows("prof_trace", "trace_kernel_stats.csv"):
