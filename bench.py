@@ -374,10 +374,12 @@ def attn_leg(pq, synth, torch, steps, warmup):
     norm and residual bit read once, the window and queries read once, the output written."""
     dev = torch.device("cuda:0")
     out = {"attn_config": "config5 shapes: 8 KV heads x 65536 quantized tokens + 128-token bf16 window, "
-                          "16 queries per head, keys 3-bit + QJL m=d, values 3-bit, softmax scale 1/sqrt(d)"}
+                          "16 queries per head, keys 3-bit + QJL m=d, values 3-bit, softmax scale 1/sqrt(d); "
+                          "d128: the config-4 decode shape (batch 4 x 8 KV heads = 32 heads x 32768 tokens, "
+                          "4 queries per KV head) on the same recipe"}
     t16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-    for d in (256, 512):
-        c = synth.config5_attention(d)
+    for d, kv, toks, nq in ((256, 8, 65536, 16), (512, 8, 65536, 16), (128, 32, 32768, 4)):
+        c = synth.config5_attention(d, kv_heads=kv, tokens=toks, n_q=nq)
         H, T, _ = c["k"].shape
         W, n_q, bits, m = c["k_win"].shape[1], c["q"].shape[1], c["bits"], c["m"]
         kst = torch.from_numpy(c["k_signs"]).to(dev)
