@@ -1934,12 +1934,17 @@ __global__ __launch_bounds__(kThreads) void pq_attend_kernel(const pqi::AttnArgs
 
 // Merge the partial results of one (head, query) with the unquantized window, rotate back and
 // normalise.
+constexpr int kCombineThreads = 512;
+
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
 }
 
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -1947,30 +1952,39 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  double r = 0.0;
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) r += red[w];
+  return r;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void pq_attend_combine_kernel(const pqi::AttnArgs a) {
   const int h = blockIdx.x / a.n_q, qi = blockIdx.x % a.n_q;
   const int R = a.n_parts, W = (int)a.n_win;
   const int tid = threadIdx.x;
   __shared__ float x[D];
   __shared__ float ew[pqi::kAttnMaxWin];
-  __shared__ float red_f[4];
-  __shared__ double red_d[4];
+  __shared__ float red_f[kCombineThreads / 64];
+  __shared__ double red_d[kCombineThreads / 64];
   extern __shared__ float wr[];                          // [R] weights of the partials
-  // window logits (base 2): one thread per window token, the query in LDS as fp32
+  // window logits (base 2): tpt threads per window token (neighbouring lanes, at most 16), each
+  // summing every tpt-th 8-value chunk; the query in LDS as fp32
   if (W > 0) {
     const uint16_t* q = a.q + ((int64_t)h * a.n_q + qi) * D;
-    for (int e = tid; e < D; e += 256) x[e] = bf16_to_f32(q[e]);
+    for (int e = tid; e < D; e += kCombineThreads) x[e] = bf16_to_f32(q[e]);
     __syncthreads();
-    for (int w = tid; w < W; w += 256) {
+    int tpt = 1;
+    while (tpt < 16 && tpt * 2 * W <= kCombineThreads) tpt *= 2;
+    const int part = tid % tpt;
+    // the lanes of a token group run the same trips (they share w), so the group's shuffles
+    // below always find their partners active
+    for (int w = tid / tpt; w < W; w += kCombineThreads / tpt) {
       const uint4* kw = reinterpret_cast<const uint4*>(a.k_win + ((int64_t)h * W + w) * D);
       // products of bf16 values are exact in fp32; the sums run in double
       double s0 = 0.0, s1 = 0.0;
 #pragma unroll 4
-      for (int c = 0; c < D / 8; ++c) {
+      for (int c = part; c < D / 8; c += tpt) {
         const uint4 u = kw[c];
         const float* qq = x + 8 * c;
         s0 += (double)(qq[0] * bf16_lo(u.x)) + (double)(qq[2] * bf16_lo(u.y));
@@ -1978,23 +1992,25 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
         s0 += (double)(qq[4] * bf16_lo(u.z)) + (double)(qq[6] * bf16_lo(u.w));
         s1 += (double)(qq[5] * bf16_hi(u.z)) + (double)(qq[7] * bf16_hi(u.w));
       }
-      ew[w] = (float)((s0 + s1) * a.scale_log2);
+      double sw = s0 + s1;
+      for (int o = 1; o < tpt; o <<= 1) sw += __shfl_xor(sw, o);
+      if (part == 0) ew[w] = (float)(sw * a.scale_log2);
     }
   }
   __syncthreads();
   const float2* ml = reinterpret_cast<const float2*>(a.work_ml) + (int64_t)h * R * 16 + qi;
   float mloc = -INFINITY;
-  for (int t = tid; t < R; t += 256) mloc = fmaxf(mloc, ml[t * 16].x);
-  for (int t = tid; t < W; t += 256) mloc = fmaxf(mloc, ew[t]);
+  for (int t = tid; t < R; t += kCombineThreads) mloc = fmaxf(mloc, ml[t * 16].x);
+  for (int t = tid; t < W; t += kCombineThreads) mloc = fmaxf(mloc, ew[t]);
   const float M = block_max(mloc, red_f);
   double lsum = 0.0;
-  for (int t = tid; t < R; t += 256) {
+  for (int t = tid; t < R; t += kCombineThreads) {
     const float2 v = ml[t * 16];
     const float f = exp2f(v.x - M);
     wr[t] = f;
     lsum += (double)f * (double)v.y;
   }
-  for (int t = tid; t < W; t += 256) {
+  for (int t = tid; t < W; t += kCombineThreads) {
     const float f = exp2f(ew[t] - M);
     ew[t] = f;
     lsum += (double)f;
@@ -2002,7 +2018,7 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
   const double L = block_sum(lsum, red_d);               // its barriers also publish wr and ew
   // weighted sum of the partial outputs: thread (column group cg, row class par) sums float4
   // columns over partials par, par + NPAR, ...; the row classes meet in LDS
-  constexpr int C4 = D / 4, NPAR = 256 / C4;
+  constexpr int C4 = D / 4, NPAR = kCombineThreads / C4;
   __shared__ float4 red4[NPAR][C4];
   const int cg = tid % C4, par = tid / C4;
   {
@@ -2018,7 +2034,7 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
     red4[par][cg] = acc;
   }
   __syncthreads();
-  for (int e = tid; e < D; e += 256) {
+  for (int e = tid; e < D; e += kCombineThreads) {
     float v = 0.0f;
     for (int p = 0; p < NPAR; ++p) v += reinterpret_cast<const float*>(red4[p])[e];
     x[e] = v;
@@ -2026,7 +2042,7 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
   __syncthreads();
   // inverse rotation: Walsh-Hadamard butterflies in Sylvester order
   for (int half = 1; half < D; half <<= 1) {
-    for (int t = tid; t < D / 2; t += 256) {
+    for (int t = tid; t < D / 2; t += kCombineThreads) {
       const int i = (t / half) * 2 * half + (t % half);
       const float x0 = x[i], x1 = x[i + half];
       x[i] = x0 + x1;
@@ -2049,7 +2065,7 @@ __global__ __launch_bounds__(256) void pq_attend_combine_kernel(const pqi::AttnA
   }
   __syncthreads();
   float* out = a.out + ((int64_t)h * a.n_q + qi) * D;
-  for (int e = tid; e < D; e += 256) {
+  for (int e = tid; e < D; e += kCombineThreads) {
     float v = ((a.v_signs[e >> 3] >> (e & 7)) & 1) ? -x[e] : x[e];
     for (int p = 0; p < NPAR; ++p) v += reinterpret_cast<const float*>(red4[p])[e];
     out[e] = (float)((double)v / L);
@@ -2488,7 +2504,7 @@ hipError_t launch_attend_d(int bits, const pqi::AttnArgs& a, hipStream_t s) {
     }
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pq_attend_combine_kernel<D>, a.n_heads * a.n_q, 256, (size_t)a.n_parts * 4, s, a);
+  hipLaunchKernelGGL(pq_attend_combine_kernel<D>, a.n_heads * a.n_q, kCombineThreads, (size_t)a.n_parts * 4, s, a);
   return hipGetLastError();
 }
 
