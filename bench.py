@@ -174,6 +174,7 @@ def summarize(run_dir):
     # the fused decode-attention kernels of the config-5 attention leg (byte codes)
     for kname, key in (("pq_attend_kernel<256, 3, 4, false>", "pq_attend_kernel_d256"),
                        ("pq_attend_kernel<512, 3, 8, false>", "pq_attend_kernel_d512"),
+                       ("pq_attend_kernel<128, 3, 2, false>", "pq_attend_kernel_d128"),
                        ("pq_attend_combine_kernel<512>", "pq_attend_combine_kernel_d512")):
         fk, nf = counter("pmc_a_fetch", "a_fetch", kname)
         wk, nw = counter("pmc_a_write", "a_write", kname)
