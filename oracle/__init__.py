@@ -23,6 +23,8 @@ order and notation, in float64, with no blocking or fusion:
 * ``attention``  - decode attention over the quantized cache plus an unquantized recent
   window (eliza quantization README, TurboQuant and Fused TurboQuant; glq 0.7.2 README,
   "Inline-dequant E8 KV").
+* ``dense``      - dense random rotation with the Beta-distribution codebook (eliza
+  quantization README, TurboQuant, "Algorithm in one paragraph").
 * ``numerics``   - IEEE round-to-nearest-even to fp16 / bf16 / fp32 and the
   LSB-first bit packing.
 
@@ -30,4 +32,4 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, textbook identities or brute force.
 """
 
-from . import numerics, lloyd_max, hadamard, codec, qjl, attention  # noqa: F401
+from . import numerics, lloyd_max, hadamard, codec, qjl, attention, dense  # noqa: F401
