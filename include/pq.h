@@ -345,6 +345,30 @@ int pq_quantize_bd(int d, int bits, int in_dtype, const void* x, int64_t n_block
 int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
                      const uint8_t* signs, int out_dtype, void* out, void* stream);
 
+/*
+ * Dense random rotation with the sphere-coordinate codebook (eliza quantization README,
+ * TurboQuant, "Algorithm in one paragraph": the unit vector is rotated by a fixed random
+ * orthogonal matrix Pi drawn by QR with a sign fix; each coordinate then follows the law of one
+ * coordinate of a uniform point on the sphere, density proportional to (1 - t^2)^((d-3)/2), and
+ * is bucketed against that law's Lloyd-Max centroids; x comes back as ||x|| Pi^T c).
+ *   y = Pi x / ||x||,  code_i = #{j : y_i > beta_j},  n16 = fp16(||x||),  xhat = n16 Pi^T c.
+ * pq_sphere_codebook: that law's Lloyd-Max centroids (2^bits, ascending) and boundaries
+ *   (2^bits - 1) for bits 1..8 and d >= 3, host arrays (either may be NULL).
+ * pq_quantize_dense / pq_dequantize_dense:
+ *   d          a multiple of 16 up to 128 (PQ_EINVAL / PQ_EUNSUPPORTED otherwise)
+ *   bits       1 .. 8
+ *   rot        Pi, d x d fp32 row-major, device memory (the caller draws it; any orthogonal
+ *              matrix is accepted and not checked)
+ *   x          n_blocks * d values, fp32 or bf16 (in_dtype); codes n_blocks * d bytes;
+ *              norms n_blocks fp16; out n_blocks * d values of out_dtype (fp32 or bf16 RNE)
+ * Asynchronous on `stream`, no allocation.
+ */
+int pq_sphere_codebook(int bits, int d, double* centroids, double* boundaries);
+int pq_quantize_dense(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const float* rot,
+                      uint8_t* codes, uint16_t* norms, void* stream);
+int pq_dequantize_dense(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                        const float* rot, int out_dtype, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,9 @@ def _load():
         "pq_score_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P], I),
         "pq_attention_work_bytes": ([I, I, L], L),
         "pq_quantize_bd": ([I, I, I, P, L, P, P, P, P], I),
+        "pq_sphere_codebook": ([I, I, D, D], I),
+        "pq_quantize_dense": ([I, I, I, P, L, P, P, P, P], I),
+        "pq_dequantize_dense": ([I, I, P, P, L, P, I, P, P], I),
         "pq_dequantize_bd": ([I, I, P, P, L, P, I, P, P], I),
         "pq_attention": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P], I),
         "pq_attention_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P],
@@ -74,7 +77,8 @@ EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", 
            "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
            "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
            "pq_query_prep", "pq_score", "pq_score_packed", "pq_attention_work_bytes", "pq_attention",
-           "pq_attention_packed", "pq_quantize_bd", "pq_dequantize_bd")
+           "pq_attention_packed", "pq_quantize_bd", "pq_dequantize_bd", "pq_sphere_codebook",
+           "pq_quantize_dense", "pq_dequantize_dense")
 
 
 def lib():
@@ -383,4 +387,46 @@ def dequantize_bd(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=No
     _check(_lib.pq_dequantize_bd(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs),
                                  PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32, _ptr(out), _stream()),
            "pq_dequantize_bd")
+    return out
+
+
+def sphere_codebook(bits, d):
+    """(centroids, boundaries) float64 of the Lloyd-Max quantizer of one sphere coordinate in R^d."""
+    c = (ctypes.c_double * (1 << bits))()
+    b = (ctypes.c_double * max(1, (1 << bits) - 1))()
+    _check(_lib.pq_sphere_codebook(bits, d, c, b), "pq_sphere_codebook")
+    return list(c), list(b)[: (1 << bits) - 1]
+
+
+def quantize_dense(x, d, bits, rot, out=None):
+    """Codec with a dense rotation rot (fp32 [d, d], row-major, device) and the sphere-coordinate
+    codebook.  Returns (codes uint8 [n_blocks, d], norms fp16 [n_blocks])."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(rot, "rot", (torch.float32,))
+    if x.numel() % d or rot.numel() != d * d:
+        raise ValueError("x.numel() must be a multiple of d and rot must be d x d")
+    n = x.numel() // d
+    if out is None:
+        out = (torch.empty((n, d), dtype=torch.uint8, device=x.device),
+               torch.empty((n,), dtype=torch.float16, device=x.device))
+    codes, norms = out
+    _check(_lib.pq_quantize_dense(d, bits, PQ_BF16 if x.dtype == torch.bfloat16 else PQ_F32, _ptr(x), n, _ptr(rot),
+                                  _ptr(codes), _ptr(norms), _stream()), "pq_quantize_dense")
+    return codes, norms
+
+
+def dequantize_dense(codes, norms, d, bits, rot, out_dtype=torch.bfloat16, out=None):
+    """Inverse of ``quantize_dense``: [n_blocks, d] of out_dtype (fp32 or bf16)."""
+    _dev(codes, "codes", (torch.uint8,))
+    _dev(norms, "norms", (torch.float16,))
+    _dev(rot, "rot", (torch.float32,))
+    n = norms.numel()
+    if codes.numel() != n * d:
+        raise ValueError("codes do not match norms and d")
+    if out is None:
+        out = torch.empty((n, d), dtype=out_dtype, device=codes.device)
+    _dev(out, "out", (torch.float32, torch.bfloat16))
+    _check(_lib.pq_dequantize_dense(d, bits, _ptr(codes), _ptr(norms), n, _ptr(rot),
+                                    PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32, _ptr(out), _stream()),
+           "pq_dequantize_dense")
     return out

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -208,6 +209,110 @@ int dequantize_impl(int d, int bits, const uint8_t* codes, const uint16_t* norms
   a.codes = codes; a.norms = norms; a.n_blocks = n_blocks; a.signs = signs; a.out = out; a.pbits = pbits;
   a.t = make_tables(bits);
   return hip_status(pqi::launch_dequantize(d, out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+// Lloyd-Max quantizer of one coordinate of a uniform unit vector in R^d (eliza quantization
+// README, TurboQuant, "Algorithm in one paragraph": the coordinates after a random rotation
+// follow this law, and the codes use its Lloyd-Max centroids).  Density
+// f(t) = K (1 - t^2)^((d-3)/2) on (-1, 1); the distribution function comes from a fine
+// trapezoid table (2^21 steps), the first moment of a cell in closed form,
+// int t f = -K (1 - t^2)^((d-1)/2) / (d - 1); iterated to a fixed point and made exactly
+// antisymmetric (the law is symmetric).
+struct SphereTable {
+  std::vector<double> cdf;   // at t_i = -1 + 2 i / n
+  double K = 0.0;
+  int d = 0;
+};
+
+Codebook solve_sphere_codebook(int bits, int d) {
+  const int n = 1 << 21;
+  SphereTable tb;
+  tb.d = d;
+  tb.K = std::exp(std::lgamma(d / 2.0) - std::lgamma((d - 1) / 2.0)) / std::sqrt(M_PI);
+  tb.cdf.resize(n + 1);
+  const double h = 2.0 / n, ex = (d - 3) / 2.0;
+  auto f = [&](double t) { const double u = 1.0 - t * t; return u > 0.0 ? tb.K * std::pow(u, ex) : 0.0; };
+  double acc = 0.0, prev = f(-1.0);
+  tb.cdf[0] = 0.0;
+  for (int i = 1; i <= n; ++i) {
+    const double cur = f(-1.0 + h * i);
+    acc += 0.5 * h * (prev + cur);
+    tb.cdf[i] = acc;
+    prev = cur;
+  }
+  for (int i = 0; i <= n; ++i) tb.cdf[i] /= acc;          // the table's own normalisation
+  auto cdf = [&](double t) {
+    if (t <= -1.0) return 0.0;
+    if (t >= 1.0) return 1.0;
+    const double x = (t + 1.0) / h;
+    const int i = std::min(n - 1, (int)x);
+    const double w = x - i;
+    return tb.cdf[i] * (1.0 - w) + tb.cdf[i + 1] * w;
+  };
+  auto mom = [&](double t) {
+    const double u = std::max(0.0, 1.0 - t * t);
+    return -tb.K * std::pow(u, (d - 1) / 2.0) / (d - 1);
+  };
+  const int L = 1 << bits;
+  std::vector<double> beta(L - 1), c(L);
+  for (int k = 0; k + 1 < L; ++k) {                      // equal-mass start
+    double lo = -1.0, hi = 1.0;
+    const double q = (double)(k + 1) / L;
+    for (int it = 0; it < 200; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      (cdf(mid) < q ? lo : hi) = mid;
+    }
+    beta[k] = 0.5 * (lo + hi);
+  }
+  auto cells = [&]() {
+    for (int k = 0; k < L; ++k) {
+      const double a = k ? beta[k - 1] : -1.0, b = k + 1 < L ? beta[k] : 1.0;
+      c[k] = (mom(b) - mom(a)) / (cdf(b) - cdf(a));
+    }
+  };
+  for (int it = 0; it < 200000; ++it) {
+    cells();
+    double change = 0.0;
+    for (int k = 0; k + 1 < L; ++k) {
+      const double nb = 0.5 * (c[k] + c[k + 1]);
+      change = std::max(change, std::fabs(nb - beta[k]));
+      beta[k] = nb;
+    }
+    if (change < 1e-13) break;
+  }
+  for (int k = 0; k < (L - 1) / 2; ++k) {
+    const double v = 0.5 * (beta[L - 2 - k] - beta[k]);
+    beta[k] = -v;
+    beta[L - 2 - k] = v;
+  }
+  if (L > 2) beta[(L - 2) / 2] = 0.0;
+  if (L == 2) beta[0] = 0.0;
+  cells();
+  for (int k = 0; k < L / 2; ++k) {
+    const double v = 0.5 * (c[L - 1 - k] - c[k]);
+    c[k] = -v;
+    c[L - 1 - k] = v;
+  }
+  Codebook cb;
+  cb.c = c;
+  cb.beta = beta;
+  return cb;
+}
+
+const Codebook& sphere_codebook(int bits, int d) {
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, Codebook> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(bits, d);
+  auto it = cache.find(key);
+  if (it == cache.end()) it = cache.emplace(key, solve_sphere_codebook(bits, d)).first;
+  return it->second;
+}
+
+int check_d_dense(int d) {
+  if (d <= 0 || (d % 16) != 0) return PQ_EINVAL;
+  if (d > pqi::kDenseMaxD) return PQ_EUNSUPPORTED;
+  return PQ_OK;
 }
 
 // block-diagonal rotation: d a multiple of 32 in [64, 4096]
@@ -571,6 +676,55 @@ int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norm
   a.ccodes = codes; a.cnorms = norms; a.signs = signs; a.out = out; a.n_blocks = n_blocks; a.d = d; a.bits = bits;
   fill_bd_codebook(bits, a);
   return hip_status(pqi::launch_dequantize_bd(out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+int pq_quantize_dense(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const float* rot,
+                      uint8_t* codes, uint16_t* norms, void* stream) {
+  int st = check_d_dense(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (in_dtype != PQ_F32 && in_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!x || !rot || !codes || !norms) return PQ_EINVAL;
+  if (!aligned(x, 4) || !aligned(rot, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::BdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.x = x; a.codes = codes; a.norms = norms; a.rot = rot; a.n_blocks = n_blocks; a.d = d; a.bits = bits;
+  const Codebook& cb = sphere_codebook(bits, d);
+  for (int k = 0; k < (1 << bits); ++k) a.cent[k] = (float)cb.c[k];
+  for (int k = 0; k + 1 < (1 << bits); ++k) a.beta[k] = (float)cb.beta[k];
+  return hip_status(pqi::launch_quantize_dense(in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+int pq_dequantize_dense(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
+                        const float* rot, int out_dtype, void* out, void* stream) {
+  int st = check_d_dense(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (out_dtype != PQ_F32 && out_dtype != PQ_BF16) return PQ_EINVAL;
+  if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
+  if (n_blocks == 0) return PQ_OK;
+  if (!codes || !norms || !rot || !out) return PQ_EINVAL;
+  if (!aligned(out, 4) || !aligned(rot, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::BdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.ccodes = codes; a.cnorms = norms; a.rot = rot; a.out = out; a.n_blocks = n_blocks; a.d = d; a.bits = bits;
+  const Codebook& cb = sphere_codebook(bits, d);
+  for (int k = 0; k < (1 << bits); ++k) a.cent[k] = (float)cb.c[k];
+  return hip_status(pqi::launch_dequantize_dense(out_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
+}
+
+int pq_sphere_codebook(int bits, int d, double* centroids, double* boundaries) {
+  if (bits < 1 || bits > pqi::kMaxBits || d < 3) return PQ_EINVAL;
+  const Codebook& cb = sphere_codebook(bits, d);
+  if (centroids) for (int k = 0; k < (1 << bits); ++k) centroids[k] = cb.c[k];
+  if (boundaries) for (int k = 0; k + 1 < (1 << bits); ++k) boundaries[k] = cb.beta[k];
+  return PQ_OK;
 }
 
 }  // extern "C"

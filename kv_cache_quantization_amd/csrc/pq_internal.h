@@ -223,6 +223,9 @@ struct AttnArgs {
 // powers of two of its binary expansion, largest first, and each part gets its own
 // Walsh-Hadamard transform; y = sqrt(d / d_k) H_k (D x)_k / ||x|| on part k.
 constexpr int kBdMinD = 64, kBdMaxD = 4096;   // d a multiple of 32 in this range
+// Dense rotation (a d x d orthogonal matrix) with the codebook of one sphere coordinate's law:
+// d a multiple of 16 up to 128 (the matrix is held in LDS)
+constexpr int kDenseMaxD = 128;
 
 struct BdArgs {
   const void* x;              // quantize input [n_blocks][d], fp32 or bf16
@@ -231,7 +234,8 @@ struct BdArgs {
   uint16_t* norms;            // quantize output, fp16
   const uint16_t* cnorms;     // dequantize input norms
   void* out;                  // dequantize output [n_blocks][d], fp32 or bf16
-  const uint8_t* signs;       // d/8 bytes
+  const uint8_t* signs;       // d/8 bytes (block-diagonal rotation)
+  const float* rot;           // d x d row-major fp32 (dense rotation)
   int64_t n_blocks;
   int d, bits;
   float cent[1 << kMaxBits];  // centroids, ascending
@@ -256,5 +260,7 @@ hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const Launch
 hipError_t launch_attention(int d, int bits, const AttnArgs& a, hipStream_t s);
 hipError_t launch_quantize_bd(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_dequantize_dense(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
 
 }  // namespace pqi

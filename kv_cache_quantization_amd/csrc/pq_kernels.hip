@@ -2342,6 +2342,82 @@ __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs
 }
 
 // ------------------------------------------------------------------------------------------
+// Dense rotation with the sphere-coordinate codebook: y = Pi x / ||x||, codes against that
+// codebook, xhat = n16 Pi^T c.  One wave per block (grid stride); the workgroup holds Pi in LDS
+// (transposed for quantize, so lane i reads row i of Pi as consecutive words across lanes);
+// the products of fp32 inputs are exact in double and summed in double, so the code decision
+// sees y to double precision before its rounding to fp32.
+// ------------------------------------------------------------------------------------------
+template <bool IN_BF16>
+__global__ __launch_bounds__(256) void pq_quantize_dense_kernel(const pqi::BdArgs a) {
+  extern __shared__ float dsm[];                         // [d][d] Pi^T, then [4 waves][d] blocks
+  __shared__ float beta[(1 << pqi::kMaxBits) - 1];
+  const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float* pit = dsm;
+  float* xb = dsm + d * d + wv * d;
+  for (int idx = threadIdx.x; idx < d * d; idx += blockDim.x) pit[(idx % d) * d + idx / d] = a.rot[idx];
+  for (int j = threadIdx.x; j < (1 << a.bits) - 1; j += blockDim.x) beta[j] = a.beta[j];
+  __syncthreads();
+  const int64_t n_waves = (int64_t)gridDim.x * 4;
+  for (int64_t blk = (int64_t)blockIdx.x * 4 + wv; blk < a.n_blocks; blk += n_waves) {
+    double ss = 0.0;
+    for (int e = lane; e < d; e += 64) {
+      const float v = IN_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[blk * d + e])
+                              : static_cast<const float*>(a.x)[blk * d + e];
+      ss += (double)v * (double)v;
+      xb[e] = v;
+    }
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < d; i += 64) {
+      double s0 = 0.0, s1 = 0.0;
+      for (int j = 0; j < d; j += 2) {
+        s0 += (double)pit[j * d + i] * (double)xb[j];
+        s1 += (double)pit[(j + 1) * d + i] * (double)xb[j + 1];
+      }
+      const float y = (float)((s0 + s1) * inv);
+      int code = 0;
+      for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
+        if (y > beta[code + step - 1]) code += step;
+      a.codes[blk * d + i] = (uint8_t)code;
+    }
+    if (lane == 0) a.norms[blk] = f32_to_f16((float)sqrt(ss));
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdArgs a) {
+  extern __shared__ float dsm[];                         // [d][d] Pi, then [4 waves][d] centroids
+  __shared__ float cent[1 << pqi::kMaxBits];
+  const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float* pi = dsm;
+  float* cb = dsm + d * d + wv * d;
+  const uint32_t cmask = (1u << a.bits) - 1u;
+  for (int idx = threadIdx.x; idx < d * d; idx += blockDim.x) pi[idx] = a.rot[idx];
+  for (int j = threadIdx.x; j < (1 << a.bits); j += blockDim.x) cent[j] = a.cent[j];
+  __syncthreads();
+  const int64_t n_waves = (int64_t)gridDim.x * 4;
+  for (int64_t blk = (int64_t)blockIdx.x * 4 + wv; blk < a.n_blocks; blk += n_waves) {
+    for (int i = lane; i < d; i += 64) cb[i] = cent[a.ccodes[blk * d + i] & cmask];
+    const float n16 = f16_to_f32(a.cnorms[blk]);
+    __builtin_amdgcn_wave_barrier();
+    for (int j = lane; j < d; j += 64) {
+      float s0 = 0.0f, s1 = 0.0f;
+      for (int i = 0; i < d; i += 2) {
+        s0 = fmaf(pi[i * d + j], cb[i], s0);
+        s1 = fmaf(pi[(i + 1) * d + j], cb[i + 1], s1);
+      }
+      const float v = n16 * (s0 + s1);
+      if (OUT_BF16) static_cast<uint16_t*>(a.out)[blk * d + j] = f32_to_bf16(v);
+      else static_cast<float*>(a.out)[blk * d + j] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // launch helpers
 // ------------------------------------------------------------------------------------------
 int grid_for(int64_t n_tiles, const pqi::LaunchCfg& c, int per_cu) {
@@ -2610,6 +2686,24 @@ hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg&
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
   if (out_bf16) hipLaunchKernelGGL(pq_dequantize_bd_kernel<true>, grid, 256, lds, s, a);
   else hipLaunchKernelGGL(pq_dequantize_bd_kernel<false>, grid, 256, lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  const size_t lds = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float);
+  const int64_t want = (a.n_blocks + 3) / 4;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
+  if (in_bf16) hipLaunchKernelGGL(pq_quantize_dense_kernel<true>, grid, 256, lds, s, a);
+  else hipLaunchKernelGGL(pq_quantize_dense_kernel<false>, grid, 256, lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_dense(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  const size_t lds = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float);
+  const int64_t want = (a.n_blocks + 3) / 4;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
+  if (out_bf16) hipLaunchKernelGGL(pq_dequantize_dense_kernel<true>, grid, 256, lds, s, a);
+  else hipLaunchKernelGGL(pq_dequantize_dense_kernel<false>, grid, 256, lds, s, a);
   return hipGetLastError();
 }
 
