@@ -47,6 +47,7 @@ def _args():
     ap.add_argument("--no-grouped", action="store_true", help="skip the config-3 grouped pass")
     ap.add_argument("--no-attn", action="store_true", help="skip the config-5 decode-attention leg")
     ap.add_argument("--no-bd", action="store_true", help="skip the block-diagonal rotation leg (d=2688)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-rotation leg (d=128)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR, then exit")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -459,6 +460,42 @@ def bd_leg(pq, synth, torch, steps, warmup):
             "bd_quantize_algorithmic_bytes": qb, "bd_dequantize_algorithmic_bytes": db}
 
 
+def dense_leg(pq, synth, torch, steps, warmup):
+    """Dense random rotation with the sphere-coordinate codebook on a KV-cache tensor of the
+    config-5 recipe at head size 128: [8][65536][128] bf16, 3-bit; the rotation is a Haar matrix
+    (QR of a seeded Gaussian with the sign fix), an input of the codec."""
+    dev = torch.device("cuda:0")
+    d, bits = 128, 3
+    c = synth.config5_tensor(d)
+    x = torch.from_numpy(c["x"].view(np.int16)).view(torch.bfloat16).to(dev).reshape(-1, d)
+    del c
+    G = np.random.default_rng(synth.BASE_SEED + d).standard_normal((d, d))
+    Q, R = np.linalg.qr(G)
+    rot = torch.from_numpy((Q * np.sign(np.diag(R))[None, :]).astype(np.float32)).to(dev)
+    n = x.shape[0]
+    codes, norms = pq.quantize_dense(x, d, bits, rot)
+    out = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+
+    def quant(k):
+        pq.quantize_dense(x, d, bits, rot, out=(codes, norms))
+
+    def dequant(k):
+        pq.dequantize_dense(codes, norms, d, bits, rot, out=out)
+
+    for k in range(warmup):
+        quant(k), dequant(k)
+    tq, td = timed(torch, quant, steps), timed(torch, dequant, steps)
+    qb = n * d * 2 + n * d + n * 2
+    db = n * d + n * 2 + n * d * 2
+    flops = 2.0 * n * d * d
+    return {"dense_config": "[8][65536][128] bf16 (config-5 recipe at d=128), 3-bit sphere-coordinate codebook, "
+                            "Haar rotation",
+            "dense_quantize_us": round(tq * 1e6, 2), "dense_quantize_hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4),
+            "dense_quantize_fp64_tflops": round(flops / tq / 1e12, 2),
+            "dense_dequantize_us": round(td * 1e6, 2), "dense_dequantize_hbm_frac": round(db / td / 1e9 / HBM_PEAK_GBS, 4),
+            "dense_dequantize_fp32_tflops": round(flops / td / 1e12, 2)}
+
+
 def grouped_leg(pq, synth, torch, reps, packed=False):
     """Config 3: one streamed quantize pass and one dequantize pass over the 224 tensors of
     a 32-layer 7B-style decoder (4-bit codes, d=128), each tensor one launch with its own
@@ -622,6 +659,8 @@ def main():
         rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
     if not args.no_tsq:
         rec["parts"].update(tsq_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+    if not args.no_dense:
+        rec["parts"].update(dense_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_bd:
         rec["parts"].update(bd_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_attn:
