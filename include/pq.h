@@ -359,8 +359,9 @@ int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norm
  *   bits       1 .. 8
  *   rot        Pi, d x d fp32 row-major, device memory (the caller draws it; any orthogonal
  *              matrix is accepted and not checked)
- *   x          n_blocks * d values, fp32 or bf16 (in_dtype); codes n_blocks * d bytes;
- *              norms n_blocks fp16; out n_blocks * d values of out_dtype (fp32 or bf16 RNE)
+ *   x          n_blocks * d values, fp32 or bf16 (in_dtype); codes n_blocks * d bytes (16-byte
+ *              aligned for pq_dequantize_dense); norms n_blocks fp16; out n_blocks * d values
+ *              of out_dtype (fp32 or bf16 RNE)
  * Asynchronous on `stream`, no allocation.
  */
 int pq_sphere_codebook(int bits, int d, double* centroids, double* boundaries);

@@ -708,7 +708,7 @@ int pq_dequantize_dense(int d, int bits, const uint8_t* codes, const uint16_t* n
   if (n_blocks < 0 || n_blocks > kMaxElems / d) return PQ_EINVAL;
   if (n_blocks == 0) return PQ_OK;
   if (!codes || !norms || !rot || !out) return PQ_EINVAL;
-  if (!aligned(out, 4) || !aligned(rot, 4) || !aligned(norms, 2)) return PQ_EINVAL;
+  if (!aligned(codes, 16) || !aligned(out, 4) || !aligned(rot, 4) || !aligned(norms, 2)) return PQ_EINVAL;
   pqi::LaunchCfg cfg;
   if ((st = launch_cfg(&cfg))) return st;
   pqi::BdArgs a;

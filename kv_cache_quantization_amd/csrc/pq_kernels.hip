@@ -2417,6 +2417,61 @@ __global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdA
   }
 }
 
+// Dequantize on the matrix cores: a wave takes 16 blocks, Xhat (16 x d) = C (16 x d) Pi with
+// v_mfma_f32_16x16x4f32 (fp32 products and sums; the centroids are fp32 exact).  K step s takes
+// k = 4 s + g in lane group g; Pi sits in LDS with a row stride of d + 16 words, so the four lane
+// groups of a B operand read four different bank quarters.
+template <bool OUT_BF16, int D>
+__global__ __launch_bounds__(256) void pq_dequantize_dense_mfma_kernel(const pqi::BdArgs a) {
+  constexpr int PS = D + 16;                             // LDS row stride of Pi
+  constexpr int NT = D / 16;                             // N tiles
+  extern __shared__ float dsm[];
+  __shared__ float cent[1 << pqi::kMaxBits];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t cmask = (1u << a.bits) - 1u;
+  for (int idx = threadIdx.x; idx < D * D; idx += blockDim.x) dsm[(idx / D) * PS + idx % D] = a.rot[idx];
+  for (int j = threadIdx.x; j < (1 << a.bits); j += blockDim.x) cent[j] = a.cent[j];
+  __syncthreads();
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t n_waves = (int64_t)gridDim.x * 4;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + wv; tile < n_tiles; tile += n_waves) {
+    // the codes of block r of the tile (all of them: lane group g uses bytes 4 s + g)
+    const int64_t blk = min(tile * 16 + r, a.n_blocks - 1);
+    uint32_t cw[D / 4];
+    const uint4* src = reinterpret_cast<const uint4*>(a.ccodes + blk * D);
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q) {
+      const uint4 w = src[q];
+      cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
+    }
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int s = 0; s < D / 4; ++s) {
+      const float av = cent[(cw[s] >> (8 * g)) & cmask];
+      const float* prow = dsm + (4 * s + g) * PS + r;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, prow[16 * t], acc[t], 0, 0, 0);
+    }
+    // lane (column n = r, group g) holds rows 4 g + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t b = tile * 16 + 4 * g + i;
+      if (b < a.n_blocks) {
+        const float n16 = f16_to_f32(a.cnorms[b]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float v = n16 * acc[t][i];
+          if (OUT_BF16) static_cast<uint16_t*>(a.out)[b * D + 16 * t + r] = f32_to_bf16(v);
+          else static_cast<float*>(a.out)[b * D + 16 * t + r] = v;
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // launch helpers
 // ------------------------------------------------------------------------------------------
@@ -2699,6 +2754,17 @@ hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg&
 }
 
 hipError_t launch_dequantize_dense(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  if (a.d == 64 || a.d == 128) {
+    const size_t lds = (size_t)a.d * (a.d + 16) * sizeof(float);
+    const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n_tiles + 3) / 4, (int64_t)c.cu_count * 2));
+#define PQ_DENSE_MFMA(DD)                                                                                   \
+    if (out_bf16) hipLaunchKernelGGL((pq_dequantize_dense_mfma_kernel<true, DD>), grid, 256, lds, s, a);  \
+    else hipLaunchKernelGGL((pq_dequantize_dense_mfma_kernel<false, DD>), grid, 256, lds, s, a);
+    if (a.d == 64) { PQ_DENSE_MFMA(64) } else { PQ_DENSE_MFMA(128) }
+#undef PQ_DENSE_MFMA
+    return hipGetLastError();
+  }
   const size_t lds = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float);
   const int64_t want = (a.n_blocks + 3) / 4;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
