@@ -2417,6 +2417,89 @@ __global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdA
   }
 }
 
+// Quantize on the matrix cores: a wave takes 16 blocks, Y (16 x d) = X (16 x d) Pi^T with
+// v_mfma_f32_16x16x4f32 (layout as the dequantize kernel below, Pi^T in LDS).  An fp32 sum of
+// d products is within d 2^-24 ||x|| of the exact one, so a coordinate of y = Y / ||x|| farther
+// than twice that from every boundary takes the same code as the exact value; the few nearer
+// ones are recomputed from LDS with exact products summed in double, as the one-wave kernel.
+constexpr int kDenseQWaves = 8;                         // waves sharing one LDS copy of Pi^T
+
+template <bool IN_BF16, int D>
+__global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kernel(const pqi::BdArgs a) {
+  constexpr int PS = D + 16;                             // LDS row stride of Pi^T
+  constexpr int NT = D / 16;
+  constexpr float EPS = 2.0f * (float)D / 16777216.0f;   // twice the fp32 sum's error bound
+  extern __shared__ float dsm[];                         // [D][PS] Pi^T, then [waves][16][D] x
+  __shared__ float beta[(1 << pqi::kMaxBits) - 1];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nb = (1 << a.bits) - 1;
+  float* xs = dsm + D * PS + wv * 16 * D;
+  for (int idx = threadIdx.x; idx < D * D; idx += blockDim.x) dsm[(idx % D) * PS + idx / D] = a.rot[idx];
+  for (int j = threadIdx.x; j < nb; j += blockDim.x) beta[j] = a.beta[j];
+  __syncthreads();
+  auto decide = [&](float y) {
+    int code = 0;
+    for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
+      if (y > beta[code + step - 1]) code += step;
+    return code;
+  };
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t n_waves = (int64_t)gridDim.x * kDenseQWaves;
+  for (int64_t tile = (int64_t)blockIdx.x * kDenseQWaves + wv; tile < n_tiles; tile += n_waves) {
+    // block r of the tile: lane group g stages a quarter of the row in LDS and sums its squares
+    const int64_t blk = min(tile * 16 + r, a.n_blocks - 1);
+    double ss = 0.0;
+    for (int e = g; e < D; e += 4) {
+      const float v = IN_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[blk * D + e])
+                              : static_cast<const float*>(a.x)[blk * D + e];
+      xs[r * D + e] = v;
+      ss += (double)v * (double)v;
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);                            // the block's sum in all four lanes
+    __builtin_amdgcn_wave_barrier();
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int s = 0; s < D / 4; ++s) {
+      const float av = xs[r * D + 4 * s + g];
+      const float* prow = dsm + (4 * s + g) * PS + r;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, prow[16 * t], acc[t], 0, 0, 0);
+    }
+    // lane (column n = 16 t + r, group g) holds blocks 4 g + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bl = 4 * g + i;
+      const int64_t b = tile * 16 + bl;
+      const double sb = __shfl(ss, bl);                 // lane bl holds block bl's sum
+      const double invd = sb > 0.0 ? 1.0 / sqrt(sb) : 0.0;
+      const float inv = (float)invd;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int n = 16 * t + r;
+        float y = acc[t][i] * inv;
+        int code = decide(y);
+        const bool near = (code > 0 && fabsf(y - beta[code - 1]) < EPS) || (code < nb && fabsf(y - beta[code]) < EPS);
+        if (near) {
+          double s0 = 0.0, s1 = 0.0;
+          for (int j = 0; j < D; j += 2) {
+            s0 += (double)dsm[j * PS + n] * (double)xs[bl * D + j];
+            s1 += (double)dsm[(j + 1) * PS + n] * (double)xs[bl * D + j + 1];
+          }
+          y = (float)((s0 + s1) * invd);
+          code = decide(y);
+        }
+        if (b < a.n_blocks) a.codes[b * D + n] = (uint8_t)code;
+      }
+      if (r == 0 && b < a.n_blocks) a.norms[b] = f32_to_f16((float)sqrt(sb));
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Dequantize on the matrix cores: a wave takes 16 blocks, Xhat (16 x d) = C (16 x d) Pi with
 // v_mfma_f32_16x16x4f32 (fp32 products and sums; the centroids are fp32 exact).  K step s takes
 // k = 4 s + g in lane group g; Pi sits in LDS with a row stride of d + 16 words, so the four lane
@@ -2745,6 +2828,18 @@ hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg&
 }
 
 hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  if (a.d == 64 || a.d == 128) {
+    const size_t lds = ((size_t)a.d * (a.d + 16) + kDenseQWaves * 16 * (size_t)a.d) * sizeof(float);
+    const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+    const int grid = (int)std::max<int64_t>(
+        1, std::min<int64_t>((n_tiles + kDenseQWaves - 1) / kDenseQWaves, (int64_t)c.cu_count * 2));
+#define PQ_DENSE_MFMA(DD)                                                                                             \
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_dense_mfma_kernel<true, DD>), grid, 64 * kDenseQWaves, lds, s, a);  \
+    else hipLaunchKernelGGL((pq_quantize_dense_mfma_kernel<false, DD>), grid, 64 * kDenseQWaves, lds, s, a);
+    if (a.d == 64) { PQ_DENSE_MFMA(64) } else { PQ_DENSE_MFMA(128) }
+#undef PQ_DENSE_MFMA
+    return hipGetLastError();
+  }
   const size_t lds = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float);
   const int64_t want = (a.n_blocks + 3) / 4;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
