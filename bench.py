@@ -372,8 +372,9 @@ def tsq_leg(pq, synth, torch, steps, warmup):
 def attn_leg(pq, synth, torch, steps, warmup):
     """Decode attention on the config-5 shapes: per KV head 65536 quantized tokens (keys 3-bit with
     QJL m=d, values 3-bit without) plus a 128-token bf16 window, 16 queries per head, for d=256
-    and d=512; byte codes and bit-packed codes.  Algorithmic bytes: every key and value code,
-    norm and residual bit read once, the window and queries read once, the output written."""
+    and d=512; and at the config-4 decode shape, d=128 with 32 heads of 32768 tokens and 4
+    queries per head; byte codes and bit-packed codes.  Algorithmic bytes: every key and value
+    code, norm and residual bit read once, the window and queries read once, the output written."""
     dev = torch.device("cuda:0")
     out = {"attn_config": "config5 shapes: 8 KV heads x 65536 quantized tokens + 128-token bf16 window, "
                           "16 queries per head, keys 3-bit + QJL m=d, values 3-bit, softmax scale 1/sqrt(d); "
