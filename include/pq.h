@@ -17,7 +17,13 @@
  *   * the QJL key sketch, fp16(||k||) and packed sign(S k) (eliza quantization
  *     README, QJL, "Algorithm in one paragraph");
  *   * the QJL asymmetric estimator of <q, k> from the packed key bits and the
- *     two-stage estimator of <q, x> from codes + residual bits (same section).
+ *     two-stage estimator of <q, x> from codes + residual bits (same section);
+ *
+ * and around it: the codes bit-packed at their width, the QJL outlier-channel
+ * split sketch, fused decode attention over a quantized cache with an
+ * unquantized recent window, the codec with a block-diagonal rotation for block
+ * sizes that are not powers of two, and the codec with a dense random rotation
+ * and the sphere-coordinate codebook (each declaration below cites its passage).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -48,10 +54,11 @@
  *   Bits        QJL sign bits are packed 8 per byte, least significant bit
  *               first; bit value 1 means sign +1, a projection of exactly 0
  *               gives bit 0 (qjl_apply.py, `_qjl_decode_keys`).
- *   Limits      d in {64, 128, 256, 512}; bits in 1..8; m a multiple of 8 in
- *               [8, 1024] (QJL residual stage and key sketch), a multiple of
- *               64 in [64, 1024] for the score entry points; block norms must
- *               be finite (a norm >= 65520 is stored as fp16 +inf).
+ *   Limits      d in {64, 128, 256, 512} unless an entry point states other
+ *               sizes; bits in 1..8; m a multiple of 8 in [8, 1024] (QJL
+ *               residual stage and key sketch), a multiple of 64 in [64, 1024]
+ *               for the score entry points; block norms must be finite (a norm
+ *               >= 65520 is stored as fp16 +inf).
  */
 #ifndef PQ_H
 #define PQ_H
