@@ -23,9 +23,9 @@ Readings where the pages leave a step open:
   * normalisation uses the unrounded norm n; dequantize and the residual use n16;
   * a zero block has u = 0, hence y = 0 and code 2^(b-1) - 1, n16 = 0;
   * ties y_i == beta_j take the lower code (strict >);
-  * the code decision is taken in fp32 (the precision of the kernel):
-    fp32(y_i) is compared with fp32(beta_j).  ``boundary_distance`` gives the
-    float64 distance to the nearest boundary for the parity rule;
+  * the code decision is taken in float64: the float64 y_i is compared with the
+    float64 boundaries beta_j.  ``boundary_distance`` gives the float64 distance
+    to the nearest boundary and the code on its far side for the parity rule;
   * QJL residual: r = x - xhat in the block's own coordinates, rnorm16 =
     fp16(||r||), bits = [S r > 0] packed LSB-first, where S is the seeded
     m x d Gaussian matrix itself (stored as bf16 values), applied to r without
@@ -38,7 +38,7 @@ import numpy as np
 
 from . import lloyd_max
 from .hadamard import block_sylvester, block_weights
-from .numerics import round_fp16, round_fp32, pack_bits_lsb
+from .numerics import round_fp16, pack_bits_lsb
 
 BAND = 1e-4   # coordinates this close to a boundary may take either side (parity rule)
 
@@ -75,11 +75,9 @@ def quantize(x, bits, D):
     if np.any(w != 1.0):
         z = z * w[None, :]
     y = np.where(norm[:, None] > 0, z / safe[:, None], 0.0)
-    y32 = round_fp32(y)
-    beta32 = round_fp32(beta)
     codes = np.zeros(y.shape, dtype=np.int64)
-    for bj in beta32:                      # count the boundaries below each coordinate
-        codes += (y32 > bj)
+    for bj in beta:                        # count the boundaries below each coordinate
+        codes += (y > bj)
     return {"norm": norm, "n16": n16, "y": y, "codes": codes.astype(np.uint8)}
 
 

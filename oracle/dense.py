@@ -19,7 +19,7 @@ Readings where the pages leave a step open:
   * the Lloyd-Max conditions as for the Gaussian codebook: centroids are the conditional means
     of their cells, boundaries the midpoints of neighbouring centroids, iterated to a fixed point;
   * the norm is stored as fp16 (as the rest of the codec; the page names bf16), codes are
-    decided in fp32 against fp32 boundaries, ties to the lower code.
+    decided in float64 against the float64 boundaries, ties to the lower code.
 """
 
 import functools
@@ -28,7 +28,7 @@ import math
 import numpy as np
 from scipy import special
 
-from .numerics import round_fp16, round_fp32
+from .numerics import round_fp16
 
 
 def haar_rotation(G):
@@ -109,10 +109,9 @@ def quantize(x, bits, Pi):
     norm = np.sqrt(np.sum(x * x, axis=1))
     safe = np.where(norm > 0, norm, 1.0)
     y = np.where(norm[:, None] > 0, (x @ np.asarray(Pi, dtype=np.float64).T) / safe[:, None], 0.0)
-    y32, b32 = round_fp32(y), round_fp32(beta)
     codes = np.zeros(y.shape, dtype=np.int64)
-    for bj in b32:
-        codes += (y32 > bj)
+    for bj in beta:
+        codes += (y > bj)
     return {"norm": norm, "n16": round_fp16(norm), "y": y, "codes": codes.astype(np.uint8), "beta": beta}
 
 

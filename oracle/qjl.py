@@ -19,7 +19,8 @@ a query head h reads KV head h // (Hq / Hkv).
 
 The two-stage estimator combines the codec and the residual sketch:
         <q, x>  ~  <q, xhat> + rnorm16 . sqrt(pi/2) / m . < S q, sign(S r) >
-with xhat the dequantized block and S = G . R the residual projection.
+with xhat the dequantized block and S = G, the seeded Gaussian matrix itself, applied
+to the residual r = x - xhat in the block's own coordinates (no rotation enters S).
 """
 
 import math

@@ -251,3 +251,71 @@ def test_block_diagonal_round_trip_mse_near_table():
     mse = np.mean(np.sum((x - xhat) ** 2, axis=1) / np.sum(x ** 2, axis=1))
     table = lloyd_max.codebook(bits)[2]
     assert abs(mse - table) < 0.05 * table
+
+
+# ------------------------------------------------------------------ decision precision pins
+
+def _brute_boundary(y, beta):
+    """Nearest boundary by a scan over every boundary, and the code across it."""
+    dist = np.full(y.shape, np.inf)
+    other = np.zeros(y.shape, dtype=np.int64)
+    for idx, v in np.ndenumerate(y):
+        code = sum(1 for b in beta if v > b)          # strict >: a coordinate on a boundary is below it
+        best, bj = np.inf, -1
+        for j, b in enumerate(beta):
+            if abs(v - b) < best:
+                best, bj = abs(v - b), j
+        dist[idx] = best
+        other[idx] = code + 1 if v <= beta[bj] else code - 1
+    return dist, other
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 5, 8])
+def test_boundary_distance_against_a_scan(bits):
+    """Distance and far-side code of ``boundary_distance`` equal a scan over every boundary, for
+    random coordinates, coordinates exactly on a boundary and one fp32 ulp to either side."""
+    _, beta, _ = lloyd_max.codebook(bits)
+    rng = np.random.default_rng(50 + bits)
+    ys = [rng.standard_normal(400) * 1.5, beta.copy()]
+    b32 = beta.astype(np.float32)
+    ys.append(np.nextafter(b32, np.float32(np.inf)).astype(np.float64))
+    ys.append(np.nextafter(b32, np.float32(-np.inf)).astype(np.float64))
+    ys.append(np.array([-50.0, 50.0, 0.0]))
+    y = np.concatenate(ys)
+    dist, other = codec.boundary_distance(y, bits)
+    bdist, bother = _brute_boundary(y, beta)
+    np.testing.assert_array_equal(dist, bdist)
+    np.testing.assert_array_equal(other.astype(np.int64), bother)
+    # on a boundary: distance 0, the far side is the upper code
+    nb = len(beta)
+    d_on, o_on = codec.boundary_distance(beta, bits)
+    assert np.all(d_on == 0.0) and np.array_equal(o_on.astype(np.int64), np.arange(1, nb + 1))
+
+
+def test_codes_decided_in_float64():
+    """Coordinates 1e-9 above or below a boundary -- far below fp32 resolution -- take the code of
+    their float64 side.  The block is built backwards from a target t with ||t||^2 = d:
+    x = D * (H t) / d gives H (D * x) = t and ||x|| = ||t|| / sqrt(d), so y = t up to float64
+    rounding (~1e-15)."""
+    bits, d = 3, 32
+    _, beta, _ = lloyd_max.codebook(bits)
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        D = rng.choice([-1.0, 1.0], size=d)
+        j = rng.integers(0, len(beta), size=8)
+        delta = rng.choice([-1e-9, 1e-9], size=8)
+        t = np.empty(d)
+        t[:8] = beta[j] + delta
+        t[8:d - 1] = rng.choice([-0.3, 0.25, -0.2], size=d - 9)     # away from every boundary
+        rest = d - np.sum(t[:d - 1] ** 2)
+        assert rest > 0
+        t[d - 1] = math.sqrt(rest)
+        assert np.min(np.abs(t[d - 1] - beta)) > 1e-3
+        H = _kron_H(d)
+        x = D * (H @ t) / d
+        q = codec.quantize(x[None, :], bits, D)
+        assert np.max(np.abs(q["y"][0] - t)) < 1e-13
+        expect = np.where(delta > 0, j + 1, j)
+        np.testing.assert_array_equal(q["codes"][0, :8].astype(np.int64), expect)
+        # fp32 cannot separate these coordinates from their boundary
+        assert np.all(np.abs(np.float32(t[:8]).astype(np.float64) - beta[j]) < 2e-7)

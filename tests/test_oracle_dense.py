@@ -75,3 +75,26 @@ def test_codec_identities():
     u = x[1:] / q["norm"][1:, None]
     err = np.mean(np.sum((u - xhat[1:] / q["n16"][1:, None]) ** 2, axis=1)) / d
     assert abs(err - dense.beta_codebook(bits, d)[2]) < 0.05 * dense.beta_codebook(bits, d)[2]
+
+
+def test_orientation_with_a_non_symmetric_rotation():
+    """y = Pi x / ||x|| element by element, and xhat = n16 Pi^T c, with Pi a signed cyclic shift
+    (orthogonal, not symmetric): (Pi x)_i = s_i x_{(i+1) mod d}.  A transposed Pi would read
+    x_{i-1} instead and fail every coordinate."""
+    d, bits = 16, 3
+    rng = np.random.default_rng(3)
+    s = rng.choice([-1.0, 1.0], size=d)
+    Pi = np.zeros((d, d))
+    for i in range(d):
+        Pi[i, (i + 1) % d] = s[i]
+    assert not np.allclose(Pi, Pi.T)
+    x = rng.standard_normal((50, d))
+    q = dense.quantize(x, bits, Pi)
+    nrm = np.sqrt(np.sum(x * x, axis=1))
+    for i in range(d):
+        np.testing.assert_array_equal(q["y"][:, i], s[i] * x[:, (i + 1) % d] / nrm)
+    c, beta, _ = dense.beta_codebook(bits, d)
+    xhat = dense.dequantize(q["codes"], q["n16"], bits, Pi)
+    for i in range(d):
+        # (Pi^T c)_{(i+1) mod d} = s_i c_i
+        np.testing.assert_array_equal(xhat[:, (i + 1) % d], q["n16"] * (s[i] * c[q["codes"][:, i].astype(np.int64)]))
