@@ -83,7 +83,7 @@ def cpu_baseline(n_blocks, min_seconds=10.0):
     returns the record for the JSON line."""
     import synth
     import oracle
-    from oracle import numerics, hadamard
+    from oracle import numerics, seeds
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -92,8 +92,8 @@ def cpu_baseline(n_blocks, min_seconds=10.0):
     c = synth.config2()
     d, bits = c["d"], c["bits"]
     x = numerics.bf16_from_bits(c["x"].reshape(-1, d)[:n_blocks])
-    D = hadamard.signs_from_mask(c["signs"], d)
-    G = numerics.bf16_from_bits(c["G"])
+    D = seeds.signs(c["sign_seed"], d)
+    G = seeds.projection_values(c["proj_seed"], c["m"], d)
     reps, dt = 0, 0.0
     while dt < min_seconds:
         t0 = time.perf_counter()
@@ -220,7 +220,7 @@ def qjl_leg(pq, synth, torch, steps, warmup):
     n_keys = B * Hkv * T
     dev = torch.device("cuda:0")
     keys_host = torch.from_numpy(c["keys"].view(np.int16)).view(torch.bfloat16)
-    G = torch.from_numpy(c["G"].view(np.int16)).view(torch.bfloat16).to(dev)
+    G = pq.projection_tensor(c["proj_seed"], m, d, dev)
     q = torch.from_numpy(c["q"].view(np.int16)).view(torch.bfloat16).to(dev)
     key_sets = [keys_host.to(dev) for _ in range(2)]          # 2 x 256 MiB: beyond the last-level cache
     bits0, norms0 = pq.qjl_sketch(key_sets[0], G)
@@ -250,7 +250,7 @@ def qjl_leg(pq, synth, torch, steps, warmup):
     # outlier channels (group of 32 tokens, top 8, their own 256-row projection): channel
     # selection, the inlier and outlier sketches, and the two-term score
     gs, n_out, m_o = 32, 8, 256
-    Go = torch.from_numpy(synth.projection(synth.BASE_SEED + 1000, m_o, d).view(np.int16)).view(torch.bfloat16).to(dev)
+    Go = pq.projection_tensor(synth.OUTLIER_PROJ_SEED, m_o, d, dev)
     kv = [k.view(B * Hkv, T, d) for k in key_sets]
     oidx = [pq.qjl_outlier_channels(kv[i], gs, n_out) for i in range(2)]
     sp_in = [(torch.empty_like(bits0), torch.empty_like(norms0)) for _ in range(2)]
@@ -301,8 +301,8 @@ def tsq_leg(pq, synth, torch, steps, warmup):
         c = synth.config5_tensor(d)
         H, T, _ = c["x"].shape
         n_q, bits, m = c["q"].shape[1], c["bits"], c["m"]
-        st = torch.from_numpy(c["signs"]).to(dev)
-        G = torch.from_numpy(c["G"].view(np.int16)).view(torch.bfloat16).to(dev)
+        st = pq.signs_tensor(c["sign_seed"], d, dev)
+        G = pq.projection_tensor(c["proj_seed"], m, d, dev)
         xs = [torch.from_numpy(c["x"].view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(2)]
         q = torch.from_numpy(c["q"].view(np.int16)).view(torch.bfloat16).to(dev)
         del c
@@ -385,9 +385,9 @@ def attn_leg(pq, synth, torch, steps, warmup):
         c = synth.config5_attention(d, kv_heads=kv, tokens=toks, n_q=nq)
         H, T, _ = c["k"].shape
         W, n_q, bits, m = c["k_win"].shape[1], c["q"].shape[1], c["bits"], c["m"]
-        kst = torch.from_numpy(c["k_signs"]).to(dev)
-        vst = torch.from_numpy(c["v_signs"]).to(dev)
-        G = t16(c["G"])
+        kst = pq.signs_tensor(c["k_sign_seed"], d, dev)
+        vst = pq.signs_tensor(c["v_sign_seed"], d, dev)
+        G = pq.projection_tensor(c["proj_seed"], m, d, dev)
         kx, vx = t16(c["k"]), t16(c["v"])
         kw, vw, q = t16(c["k_win"]), t16(c["v_win"]), t16(c["q"])
         del c
@@ -439,7 +439,7 @@ def bd_leg(pq, synth, torch, steps, warmup):
     xu, _ = synth.weight_with_outlier_entries(5, rows, d)
     x = torch.from_numpy(xu.view(np.int16)).view(torch.bfloat16).to(dev)
     del xu
-    st = torch.from_numpy(synth.sign_mask(synth.BASE_SEED + d, d)).to(dev)
+    st = pq.signs_tensor(synth.BASE_SEED + d, d, dev)
     codes, norms = pq.quantize_bd(x, d, bits, st)
     out = torch.empty((rows, d), dtype=torch.bfloat16, device=dev)
 
@@ -515,7 +515,7 @@ def grouped_leg(pq, synth, torch, reps, packed=False):
         ins.append(x)
         outs.append((torch.empty((n, cb), dtype=torch.uint8, device=dev), torch.empty((n,), dtype=torch.float16, device=dev),
                      torch.empty((n, d), dtype=torch.bfloat16, device=dev)))
-    signs = [torch.from_numpy(synth.sign_mask(synth.BASE_SEED + t, d)).to(dev) for t, _, _, _, _ in layout]
+    signs = [pq.signs_tensor(synth.BASE_SEED + t, d, dev) for t, _, _, _, _ in layout]
     total = sum(r * c for _, _, _, r, c in layout)
 
     def qpass(k):
@@ -575,8 +575,8 @@ def main():
     d, bits, m = c["d"], c["bits"], c["m"]
     n_blocks = c["x"].size // d
     x_host = torch.from_numpy(c["x"].view(np.int16)).view(torch.bfloat16)
-    signs = torch.from_numpy(c["signs"]).to(dev)
-    proj = torch.from_numpy(c["G"].view(np.int16)).view(torch.bfloat16).to(dev)
+    signs = pq.signs_tensor(c["sign_seed"], d, dev)
+    proj = pq.projection_tensor(c["proj_seed"], m, d, dev)
 
     sets = []
     for _ in range(N_SETS):

@@ -103,6 +103,30 @@ int pq_last_hip_error(void);
  */
 int pq_codebook(int bits, double* centroids, double* boundaries, double* mse);
 
+/*
+ * The seeded random quantities of the codec, rebuilt from a 64-bit seed on the host (the
+ * seed is the state that must persist: eliza quantization README, TurboQuant, "CLI",
+ * --base-seed with layer i using seed base_seed + i, and dequantizing with other signs
+ * giving garbage; QJL, "CLI", --projection-seed; qjl_apply.py draws its JL matrix from a
+ * seeded generator per layer).  The generator is frozen so that any implementation
+ * reproduces the bytes:
+ *   mix(z)   = z3 ^ (z3 >> 31), z3 = (z2 ^ (z2 >> 27)) * 0x94D049BB133111EB,
+ *              z2 = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9          (SplitMix64, mod 2^64)
+ *   stream (seed, tag) starts in state s = mix(seed ^ tag); its output i is
+ *   mix(s + (i + 1) * 0x9E3779B97F4A7C15); tag 0x5349474E for signs, 0x50524F4A for G.
+ * pq_make_signs: D_j = -1 exactly when the top bit of output j is set; mask (host, d/8 bytes,
+ *   written whole) holds D_j as bit j%8 of byte j/8, the sign-mask layout every entry point
+ *   takes.  d a multiple of 8 in 8 .. 65536.
+ * qjl_make_projection: G (host, m*d bf16 bit patterns, row-major, written whole); element
+ *   k = i*d + j.  Outputs 2p and 2p+1 give u = ((out >> 11) + 0.5) 2^-53 in (0, 1) and the
+ *   Box-Muller pair sqrt(-2 ln u1) (cos, sin)(2 pi u2) in double, each rounded to the
+ *   nearest bf16 (ties to even).  m, d in 1 .. 65536 with m*d even.
+ * Both return PQ_EINVAL for a NULL pointer or sizes outside these ranges; they touch no
+ * device and are thread safe.
+ */
+int pq_make_signs(uint64_t seed, int d, uint8_t* mask);
+int qjl_make_projection(uint64_t seed, int m, int d, uint16_t* proj);
+
 /* ---------------------------------------------------------------- device side */
 
 /*

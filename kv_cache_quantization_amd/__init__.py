@@ -12,6 +12,7 @@ PQ_EHIP); importing fails loudly when the library has not been built.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +42,8 @@ def _load():
         "pq_strerror": ([I], ctypes.c_char_p),
         "pq_last_hip_error": ([], I),
         "pq_codebook": ([I, D, D, D], I),
+        "pq_make_signs": ([ctypes.c_uint64, I, P], I),
+        "qjl_make_projection": ([ctypes.c_uint64, I, I, P], I),
         "pq_quantize": ([I, I, I, P, L, P, I, P, P, P, P, P, P], I),
         "pq_dequantize": ([I, I, P, P, L, P, I, P, P], I),
         "pq_quantize_packed": ([I, I, I, P, L, P, I, P, P, P, P, P, P], I),
@@ -73,7 +76,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_quantize",
+EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_make_signs",
+           "qjl_make_projection", "pq_quantize",
            "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
            "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
            "pq_query_prep", "pq_score", "pq_score_packed", "pq_attention_work_bytes", "pq_attention",
@@ -117,6 +121,32 @@ def codebook(bits):
     mse = ctypes.c_double()
     _check(_lib.pq_codebook(bits, c, b, ctypes.byref(mse)), "pq_codebook")
     return list(c), list(b)[:L - 1], mse.value
+
+
+def make_signs(seed, d):
+    """Rotation sign mask of ``seed`` (pq_make_signs): numpy uint8 [d/8], bit j set <=> D_j = -1."""
+    mask = np.zeros(d // 8 if d > 0 else 0, dtype=np.uint8)
+    _check(_lib.pq_make_signs(int(seed) & 0xFFFFFFFFFFFFFFFF, d, mask.ctypes.data_as(ctypes.c_void_p)),
+           "pq_make_signs")
+    return mask
+
+
+def make_projection(seed, m, d):
+    """Gaussian JL matrix G of ``seed`` (qjl_make_projection): numpy uint16 [m, d] of bf16 bits."""
+    g = np.zeros((max(m, 0), max(d, 0)), dtype=np.uint16)
+    _check(_lib.qjl_make_projection(int(seed) & 0xFFFFFFFFFFFFFFFF, m, d, g.ctypes.data_as(ctypes.c_void_p)),
+           "qjl_make_projection")
+    return g
+
+
+def signs_tensor(seed, d, device="cuda"):
+    """``make_signs`` as a uint8 tensor on ``device``."""
+    return torch.from_numpy(make_signs(seed, d)).to(device)
+
+
+def projection_tensor(seed, m, d, device="cuda"):
+    """``make_projection`` as a bfloat16 tensor [m, d] on ``device``."""
+    return torch.from_numpy(make_projection(seed, m, d).view("int16")).view(torch.bfloat16).to(device)
 
 
 def quantize(x, d, bits, signs, proj=None, out=None, packed=False):

@@ -165,6 +165,53 @@ int launch_cfg(pqi::LaunchCfg* c) {
 
 constexpr int64_t kMaxElems = INT64_MAX / 8;
 
+// ------------------------------------------------------------------------------------------
+// Seeded rotation signs and JL matrix (eliza quantization README, TurboQuant "CLI": layer i
+// uses seed base_seed + i; QJL "CLI": --projection-seed).  A counter-based generator, so that
+// any consumer rebuilds the same bytes from the seed: SplitMix64 (Steele, Lea and Flood,
+// OOPSLA 2014), stream (seed, tag) started in state mix(seed ^ tag), output i =
+// mix(state + (i + 1) * golden gamma); signs from the top bit of each output; Gaussians by the
+// Box-Muller transform of output pairs taken as uniforms in (0, 1), rounded to bf16.
+// ------------------------------------------------------------------------------------------
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kTagSigns = 0x5349474Eull;   // "SIGN"
+constexpr uint64_t kTagProj = 0x50524F4Aull;    // "PROJ"
+
+uint64_t splitmix_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct SeedStream {
+  uint64_t state;
+  SeedStream(uint64_t seed, uint64_t tag) : state(splitmix_mix(seed ^ tag)) {}
+  uint64_t next() { return splitmix_mix(state += kGamma); }
+};
+
+// uniform in (0, 1) from the top 53 bits: ((z >> 11) + 1/2) 2^-53
+double unit_open(uint64_t z) { return ((double)(z >> 11) + 0.5) * 0x1p-53; }
+
+// double -> bf16 bits, round to nearest even, directly from the double (no fp32 step, which
+// would round twice); overflow to infinity, NaN to a quiet NaN.
+uint16_t bf16_rne(double v) {
+  uint64_t b;
+  std::memcpy(&b, &v, sizeof(b));
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  const double a = std::fabs(v);
+  if (std::isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+  if (a < 0x1p-126) {                      // bf16 subnormal range: quantum 2^-133
+    const double q = std::nearbyint(a * 0x1p133);
+    return (uint16_t)(sign | (uint16_t)q);  // q <= 128; 128 is the smallest normal
+  }
+  uint64_t m = b & 0x7FFFFFFFFFFFFFFFull;
+  m += (1ull << 44) - 1 + ((m >> 45) & 1);   // 45 dropped fraction bits, ties to even
+  m >>= 45;                                  // (double exponent << 7) | 7 fraction bits
+  const int64_t e = (int64_t)(m >> 7) - 1023 + 127;
+  if (e >= 255) return (uint16_t)(sign | 0x7F80u);
+  return (uint16_t)(sign | (uint16_t)((e << 7) | (int64_t)(m & 0x7F)));
+}
+
 }  // namespace
 
 namespace {
@@ -345,6 +392,30 @@ const char* pq_strerror(int status) {
 }
 
 int pq_last_hip_error(void) { return g_last_hip_error; }
+
+int pq_make_signs(uint64_t seed, int d, uint8_t* mask) {
+  if (d < 8 || d > 65536 || (d % 8) != 0 || !mask) return PQ_EINVAL;
+  SeedStream s(seed, kTagSigns);
+  std::memset(mask, 0, (size_t)d / 8);
+  for (int j = 0; j < d; ++j)
+    if (s.next() >> 63) mask[j >> 3] |= (uint8_t)(1u << (j & 7));
+  return PQ_OK;
+}
+
+int qjl_make_projection(uint64_t seed, int m, int d, uint16_t* proj) {
+  if (m < 1 || d < 1 || m > 65536 || d > 65536 || ((int64_t)m * d) % 2 != 0 || !proj) return PQ_EINVAL;
+  SeedStream s(seed, kTagProj);
+  const int64_t n = (int64_t)m * d;
+  for (int64_t k = 0; k < n; k += 2) {
+    const double u1 = unit_open(s.next());
+    const double u2 = unit_open(s.next());
+    const double rad = std::sqrt(-2.0 * std::log(u1));
+    const double th = 2.0 * M_PI * u2;
+    proj[k] = bf16_rne(rad * std::cos(th));
+    proj[k + 1] = bf16_rne(rad * std::sin(th));
+  }
+  return PQ_OK;
+}
 
 int pq_codebook(int bits, double* centroids, double* boundaries, double* mse) {
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;

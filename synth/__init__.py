@@ -2,10 +2,13 @@
 
 This module holds none of the method's arithmetic: it only draws random
 numbers and casts them to the storage dtypes.  The random quantities the
-method itself uses (the +-1 rotation signs D and the Gaussian JL matrix G) are
-drawn here too and handed to both sides as inputs.
+method itself draws (the +-1 rotation signs D and the Gaussian JL matrix G) are
+not drawn here: a config names their seeds, and each side rebuilds them with
+its own implementation of the same counter-based generator (the library's
+pq_make_signs / qjl_make_projection for the GPU side, ``oracle.seeds`` for the
+oracle side).
 
-Every array comes from numpy's PCG64 seeded with ``SeedSequence([seed, tag])``,
+Every data array comes from numpy's PCG64 seeded with ``SeedSequence([seed, tag])``,
 so each (seed, purpose) pair is an independent, reproducible stream.
 
 Workload recipes (sizes and distributions of the pages' workloads):
@@ -32,6 +35,7 @@ import numpy as np
 
 TAG_DATA, TAG_SIGNS, TAG_PROJ, TAG_OUTLIER, TAG_QUERY, TAG_SCALE = 1, 2, 3, 4, 5, 6
 BASE_SEED = 42          # rotation / projection seed base; tensor t uses BASE_SEED + t
+OUTLIER_PROJ_SEED = BASE_SEED + 1000    # the outlier channels' own projection (config-4 shape)
 
 
 def rng(seed, tag):
@@ -50,18 +54,6 @@ def bf16_to_f32(u):
     return (np.ascontiguousarray(u, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def sign_mask(seed, d):
-    """Rademacher rotation signs as a d/8-byte mask, bit j (LSB-first) set <=> D_j = -1."""
-    bits = rng(seed, TAG_SIGNS).integers(0, 2, size=d, dtype=np.uint8)
-    return np.packbits(bits, bitorder="little")
-
-
-def projection(seed, m, d):
-    """Gaussian JL matrix G, m x d row-major, N(0,1) rounded to bf16 (uint16 bits)."""
-    g = rng(seed, TAG_PROJ).standard_normal((m, d), dtype=np.float32)
-    return bf16_from_f32(g)
-
-
 def gaussian_bf16(seed, tag, shape, std=1.0):
     g = rng(seed, tag).standard_normal(shape, dtype=np.float32)
     if std != 1.0:
@@ -74,7 +66,7 @@ def gaussian_bf16(seed, tag, shape, std=1.0):
 def config1(seed=0):
     x = rng(seed, TAG_DATA).standard_normal((256, 512), dtype=np.float32) * np.float32(0.02)
     return {"name": "config1", "x": x, "dtype": "f32", "d": 128, "bits": 4, "m": 0,
-            "signs": sign_mask(BASE_SEED, 128)}
+            "sign_seed": BASE_SEED}
 
 
 def weight_with_outlier_entries(seed, rows, cols, frac=0.001, factor=10.0, std=0.02):
@@ -90,7 +82,7 @@ def weight_with_outlier_entries(seed, rows, cols, frac=0.001, factor=10.0, std=0
 def config2(seed=0, rows=4096, cols=4096):
     x, pos = weight_with_outlier_entries(seed, rows, cols)
     return {"name": "config2", "x": x, "dtype": "bf16", "d": 128, "bits": 5, "m": 64,
-            "signs": sign_mask(BASE_SEED, 128), "G": projection(BASE_SEED, 64, 128),
+            "sign_seed": BASE_SEED, "proj_seed": BASE_SEED,
             "outlier_positions": pos}
 
 
@@ -110,12 +102,13 @@ def config3_layout(n_layers=32):
 
 
 def config3_tensor(t, rows, cols, seed=0, n_cols_out=8, factor=8.0):
-    """Tensor t of config 3: bf16 N(0, 0.02^2), 8 seeded input columns scaled by 8."""
+    """Tensor t of config 3: bf16 N(0, 0.02^2), 8 seeded input columns scaled by 8.
+    Returns (bf16 bits, rotation sign seed)."""
     s = seed * 1000 + t
     g = rng(s, TAG_DATA).standard_normal((rows, cols), dtype=np.float32) * np.float32(0.02)
     colsel = rng(s, TAG_OUTLIER).choice(cols, size=n_cols_out, replace=False)
     g[:, colsel] *= np.float32(factor)
-    return bf16_from_f32(g), sign_mask(BASE_SEED + t, 128)
+    return bf16_from_f32(g), BASE_SEED + t
 
 
 def config4(seed=0, batch=4, kv_heads=8, tokens=32768, head_dim=128, q_heads=32, m=256):
@@ -126,7 +119,7 @@ def config4(seed=0, batch=4, kv_heads=8, tokens=32768, head_dim=128, q_heads=32,
         keys[:, h, :, chans[h]] *= np.float32(20.0)
     q = rng(seed, TAG_QUERY).standard_normal((batch, q_heads, head_dim), dtype=np.float32)
     return {"name": "config4", "keys": bf16_from_f32(keys), "q": bf16_from_f32(q),
-            "G": projection(BASE_SEED, m, head_dim), "d": head_dim, "m": m,
+            "proj_seed": BASE_SEED, "d": head_dim, "m": m,
             "outlier_channels": chans}
 
 
@@ -138,7 +131,7 @@ def config5_tensor(d, seed=0, kv_heads=8, tokens=65536, n_q=16):
     x *= scale
     q = rng(s, TAG_QUERY).standard_normal((kv_heads, n_q, d), dtype=np.float32)
     return {"x": bf16_from_f32(x), "q": bf16_from_f32(q), "d": d, "bits": 3, "m": d,
-            "signs": sign_mask(BASE_SEED + d, d), "G": projection(BASE_SEED + d, d, d)}
+            "sign_seed": BASE_SEED + d, "proj_seed": BASE_SEED + d}
 
 
 def config5_attention(d, seed=0, kv_heads=8, tokens=65536, n_q=16, window=128):
@@ -150,5 +143,5 @@ def config5_attention(d, seed=0, kv_heads=8, tokens=65536, n_q=16, window=128):
     vals = config5_tensor(d, seed + 1, kv_heads, tokens + window, n_q)
     return {"k": np.ascontiguousarray(keys["x"][:, :tokens]), "v": np.ascontiguousarray(vals["x"][:, :tokens]),
             "k_win": np.ascontiguousarray(keys["x"][:, tokens:]), "v_win": np.ascontiguousarray(vals["x"][:, tokens:]),
-            "q": keys["q"], "d": d, "bits": keys["bits"], "m": keys["m"], "k_signs": keys["signs"], "G": keys["G"],
-            "v_signs": sign_mask(BASE_SEED + d + 1, d)}
+            "q": keys["q"], "d": d, "bits": keys["bits"], "m": keys["m"], "k_sign_seed": keys["sign_seed"],
+            "proj_seed": keys["proj_seed"], "v_sign_seed": BASE_SEED + d + 1}

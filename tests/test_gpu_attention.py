@@ -23,7 +23,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import attention, codec, hadamard, lloyd_max, numerics
-from tests import parity
+from tests import parity, seeded
 
 pytestmark = pytest.mark.gpu
 
@@ -101,14 +101,12 @@ def test_attention_random_codes(d, bits, m, n_heads, n_q, n_tok, n_win, packed, 
     qu = synth.bf16_from_f32(qf)
     kw = synth.bf16_from_f32(2.0 * rng.standard_normal((n_heads, n_win, d)).astype(np.float32))
     vw = synth.bf16_from_f32(rng.standard_normal((n_heads, n_win, d)).astype(np.float32))
-    k_signs = synth.sign_mask(d + 3, d)
-    v_signs = synth.sign_mask(d + 4, d)
-    Gu = synth.projection(d + 5, m, d) if m else None
+    k_seed, v_seed, g_seed = d + 3, d + 4, d + 5
     sm = scale if scale is not None else 1.0 / math.sqrt(d)
 
-    Gt = parity.bf16_tensor(Gu) if m else None
+    Gt = seeded.gpu_proj(g_seed, m, d) if m else None
     qt = parity.bf16_tensor(qu)
-    prep = pq.query_prep(qt, parity.u8_tensor(k_signs), Gt) if n_tok else None
+    prep = pq.query_prep(qt, seeded.gpu_signs(k_seed, d), Gt) if n_tok else None
     if packed:
         kc_in = codec.pack_codes(kc.reshape(-1, d), bits) if n_tok else np.zeros((0, d * bits // 8), np.uint8)
         vc_in = codec.pack_codes(vc.reshape(-1, d), bits) if n_tok else np.zeros((0, d * bits // 8), np.uint8)
@@ -116,16 +114,16 @@ def test_attention_random_codes(d, bits, m, n_heads, n_q, n_tok, n_win, packed, 
         kc_in, vc_in = kc, vc
     keys = (parity.u8_tensor(kc_in), _f16(kn), parity.u8_tensor(qbits) if m else None, _f16(rn) if m else None)
     values = (parity.u8_tensor(vc_in), _f16(vn))
-    out = pq.attention(prep, keys, values, parity.u8_tensor(v_signs), d, bits, n_heads, n_q, n_tok, m=m,
+    out = pq.attention(prep, keys, values, seeded.gpu_signs(v_seed, d), d, bits, n_heads, n_q, n_tok, m=m,
                        k_win=parity.bf16_tensor(kw) if n_win else None, v_win=parity.bf16_tensor(vw) if n_win else None,
                        q=qt if n_win else None, sm_scale=scale, packed=packed)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got))
     q = numerics.bf16_from_bits(qu)
-    D_k = hadamard.signs_from_mask(k_signs, d)
-    D_v = hadamard.signs_from_mask(v_signs, d)
-    G = numerics.bf16_from_bits(Gu) if m else None
+    D_k = seeded.oracle_D(k_seed, d)
+    D_v = seeded.oracle_D(v_seed, d)
+    G = seeded.oracle_G(g_seed, m, d) if m else None
     worst = 0.0
     for h in range(n_heads):
         worst = max(worst, _check(got[h], q[h], kc[h], kn[h], vc[h], vn[h], bits, D_k, D_v,
@@ -143,8 +141,8 @@ def test_attention_end_to_end_config5_shape(d):
     _case("attention end to end d=%d tokens=%d window=%d" % (d, n_tok, n_win))
     c = synth.config5_attention(d, kv_heads=n_heads, tokens=n_tok, n_q=n_q, window=n_win)
     bits, m = c["bits"], c["m"]
-    kst, vst = parity.u8_tensor(c["k_signs"]), parity.u8_tensor(c["v_signs"])
-    Gt = parity.bf16_tensor(c["G"])
+    kst, vst = seeded.gpu_signs(c["k_sign_seed"], d), seeded.gpu_signs(c["v_sign_seed"], d)
+    Gt = seeded.gpu_proj(c["proj_seed"], m, d)
     kx, vx = parity.bf16_tensor(c["k"]), parity.bf16_tensor(c["v"])
     kcod, knrm, kqb, krn = pq.quantize(kx, d, bits, kst, Gt)
     vcod, vnrm, _, _ = pq.quantize(vx, d, bits, vst)
@@ -167,9 +165,9 @@ def test_attention_end_to_end_config5_shape(d):
     qb = kqb.cpu().numpy().reshape(n_heads, n_tok, m // 8)
     rn = parity.f16_values(krn).reshape(n_heads, n_tok)
     q = numerics.bf16_from_bits(c["q"])
-    D_k = hadamard.signs_from_mask(c["k_signs"], d)
-    D_v = hadamard.signs_from_mask(c["v_signs"], d)
-    G = numerics.bf16_from_bits(c["G"])
+    D_k = seeded.oracle_D(c["k_sign_seed"], d)
+    D_v = seeded.oracle_D(c["v_sign_seed"], d)
+    G = seeded.oracle_G(c["proj_seed"], m, d)
     for h in range(n_heads):
         _check(got[h], q[h], kc[h], kn[h], vc[h], vn[h], bits, D_k, D_v, numerics.bf16_from_bits(c["k_win"][h]),
                numerics.bf16_from_bits(c["v_win"][h]), 1.0 / math.sqrt(d), qb[h], rn[h], G, label="e2e head %d" % h)
@@ -189,30 +187,30 @@ def test_attention_reuses_work_and_output():
         kn = numerics.round_fp16(np.exp(rng.uniform(-1, 2, size=(n_heads, n_tok))))
         vn = numerics.round_fp16(np.exp(rng.uniform(-1, 2, size=(n_heads, n_tok))))
         qu = synth.bf16_from_f32(rng.standard_normal((n_heads, n_q, d)).astype(np.float32))
-        ks, vs = synth.sign_mask(7, d), synth.sign_mask(8, d)
-        prep = pq.query_prep(parity.bf16_tensor(qu), parity.u8_tensor(ks))
+        prep = pq.query_prep(parity.bf16_tensor(qu), seeded.gpu_signs(7, d))
         out = pq.attention(prep, (parity.u8_tensor(kc), _f16(kn), None, None), (parity.u8_tensor(vc), _f16(vn)),
-                           parity.u8_tensor(vs), d, bits, n_heads, n_q, n_tok, work=work)
+                           seeded.gpu_signs(8, d), d, bits, n_heads, n_q, n_tok, work=work)
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         q = numerics.bf16_from_bits(qu)
         for h in range(n_heads):
-            _check(got[h], q[h], kc[h], kn[h], vc[h], vn[h], bits, hadamard.signs_from_mask(ks, d),
-                   hadamard.signs_from_mask(vs, d), None, None, 1.0 / math.sqrt(d), label="reuse h%d" % h)
+            _check(got[h], q[h], kc[h], kn[h], vc[h], vn[h], bits, seeded.oracle_D(7, d),
+                   seeded.oracle_D(8, d), None, None, 1.0 / math.sqrt(d), label="reuse h%d" % h)
         res.append(got)
 
 
 @pytest.mark.parametrize("d", [256, 512])
 def test_attention_config5_full_sampled(d):
     """Config-5 attention shapes at full size (8 KV heads x 65,536 quantized tokens + a 128-token
-    window, 16 queries), one call as the benchmark makes it; the oracle checks the first and last
-    heads (all their queries) from the GPU's stored codes; every output is finite."""
+    window, 16 queries), one call as the benchmark makes it; the oracle checks every head at
+    d = 256 and the first and last heads at d = 512 (all their queries) from the GPU's stored
+    codes; every output is finite."""
     _case("attention config-5 full size d=%d" % d)
     c = synth.config5_attention(d)
     H, T, _ = c["k"].shape
     n_q, bits, m = c["q"].shape[1], c["bits"], c["m"]
-    kst, vst = parity.u8_tensor(c["k_signs"]), parity.u8_tensor(c["v_signs"])
-    Gt = parity.bf16_tensor(c["G"])
+    kst, vst = seeded.gpu_signs(c["k_sign_seed"], d), seeded.gpu_signs(c["v_sign_seed"], d)
+    Gt = seeded.gpu_proj(c["proj_seed"], m, d)
     kcod, knrm, kqb, krn = pq.quantize(parity.bf16_tensor(c["k"]), d, bits, kst, Gt)
     vcod, vnrm, _, _ = pq.quantize(parity.bf16_tensor(c["v"]), d, bits, vst)
     qt = parity.bf16_tensor(c["q"])
@@ -223,10 +221,10 @@ def test_attention_config5_full_sampled(d):
     got = out.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got))
     q = numerics.bf16_from_bits(c["q"])
-    D_k = hadamard.signs_from_mask(c["k_signs"], d)
-    D_v = hadamard.signs_from_mask(c["v_signs"], d)
-    G = numerics.bf16_from_bits(c["G"])
-    for h in (0, H - 1):
+    D_k = seeded.oracle_D(c["k_sign_seed"], d)
+    D_v = seeded.oracle_D(c["v_sign_seed"], d)
+    G = seeded.oracle_G(c["proj_seed"], m, d)
+    for h in (range(H) if d == 256 else (0, H - 1)):     # every head at d = 256
         kc = kcod[h * T:(h + 1) * T].cpu().numpy()
         vc = vcod[h * T:(h + 1) * T].cpu().numpy()
         kn = parity.f16_values(knrm[h * T:(h + 1) * T])

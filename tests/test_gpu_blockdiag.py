@@ -8,7 +8,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import hadamard
-from tests import parity
+from tests import parity, seeded
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +38,7 @@ def test_blockdiag_codec(d, bits, n, bf16):
     xf[0, : d // 3] *= 8.0                                  # an uneven block: energy in the first parts
     if n > 2:
         xf[1] = 0.0                                         # a zero block
-    signs = synth.sign_mask(d + 7, d)
-    D = hadamard.signs_from_mask(signs, d)
+    D = seeded.oracle_D(d + 7, d)
     if bf16:
         xu = synth.bf16_from_f32(xf)
         xt = parity.bf16_tensor(xu)
@@ -47,7 +46,7 @@ def test_blockdiag_codec(d, bits, n, bf16):
     else:
         xt = torch.from_numpy(xf).cuda()
         x = xf.astype(np.float64)
-    st = parity.u8_tensor(signs)
+    st = seeded.gpu_signs(d + 7, d)
     codes, norms = pq.quantize_bd(xt, d, bits, st)
     out32 = pq.dequantize_bd(codes, norms, d, bits, st, out_dtype=torch.float32)
     out16 = pq.dequantize_bd(codes, norms, d, bits, st, out_dtype=torch.bfloat16)
@@ -66,15 +65,14 @@ def test_blockdiag_weight_2688_sampled():
     d, bits, rows = 2688, 4, 16384
     _case("block-diagonal weight %dx%d" % (rows, d))
     c, _ = synth.weight_with_outlier_entries(5, rows, d)
-    signs = synth.sign_mask(synth.BASE_SEED + d, d)
-    st = parity.u8_tensor(signs)
+    st = seeded.gpu_signs(synth.BASE_SEED + d, d)
     codes, norms = pq.quantize_bd(parity.bf16_tensor(c), d, bits, st)
     out = pq.dequantize_bd(codes, norms, d, bits, st)
     torch.cuda.synchronize()
     idx = np.unique(np.concatenate([np.arange(32), np.arange(rows - 32, rows),
                                     np.random.default_rng(3).integers(0, rows, 96)]))
     x = synth.bf16_to_f32(c[idx]).astype(np.float64)
-    D = hadamard.signs_from_mask(signs, d)
+    D = seeded.oracle_D(synth.BASE_SEED + d, d)
     gc = codes.cpu().numpy()[idx]
     gn = parity.f16_values(norms)[idx]
     parity.check_quantize(x, bits, D, gc, gn, label="bd weight")

@@ -9,7 +9,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import hadamard, numerics
-from tests import parity
+from tests import parity, seeded
 
 pytestmark = pytest.mark.gpu
 
@@ -36,13 +36,13 @@ def _inputs(n, d, dtype, seed, std=0.02, special=True):
 
 
 def _signs(d, seed):
-    mask = synth.sign_mask(seed, d)
-    return parity.u8_tensor(mask), hadamard.signs_from_mask(mask, d)
+    """(GPU sign mask from the library's generator, oracle D from the oracle's)."""
+    return seeded.gpu_signs(seed, d), seeded.oracle_D(seed, d)
 
 
 def _proj(m, d, seed):
-    u = synth.projection(seed, m, d)
-    return parity.bf16_tensor(u), numerics.bf16_from_bits(u)
+    """(GPU G from the library's generator, oracle G from the oracle's)."""
+    return seeded.gpu_proj(seed, m, d), seeded.oracle_G(seed, m, d)
 
 
 CODEC_CASES = [

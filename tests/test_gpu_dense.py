@@ -16,7 +16,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import dense, numerics
-from tests import parity
+from tests import parity, seeded
 
 pytestmark = pytest.mark.gpu
 

@@ -10,7 +10,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import numerics, qjl
-from tests import parity
+from tests import parity, seeded
 
 pytestmark = pytest.mark.gpu
 
@@ -69,10 +69,8 @@ def test_outlier_channels_parity(d, gs, n_out, heads, T):
 def test_split_sketch_and_score(B, Hkv, Hq, T, d, m, m_o, gs, n_out):
     _case("split sketch + score B=%d Hkv=%d Hq=%d T=%d d=%d m=%d m_o=%d" % (B, Hkv, Hq, T, d, m, m_o))
     c = synth.config4(seed=3, batch=B, kv_heads=Hkv, tokens=T, head_dim=d, q_heads=Hq, m=m)
-    Gu = c["G"]
-    Gou = synth.projection(synth.BASE_SEED + 1000, m_o, d)
     kt, qt = parity.bf16_tensor(c["keys"]), parity.bf16_tensor(c["q"])
-    Gt, Got = parity.bf16_tensor(Gu), parity.bf16_tensor(Gou)
+    Gt, Got = seeded.gpu_proj(c["proj_seed"], m, d), seeded.gpu_proj(synth.OUTLIER_PROJ_SEED, m_o, d)
     idx = pq.qjl_outlier_channels(kt, gs, n_out)
     kf = kt.view(B * Hkv, T, d)
     ix = idx.view(B * Hkv, -1, n_out)
@@ -83,7 +81,7 @@ def test_split_sketch_and_score(B, Hkv, Hq, T, d, m, m_o, gs, n_out):
     sc = pq.qjl_score(sqo, b_out, n_out16, B, Hkv, Hq, T, out=sc, accumulate=True)
     torch.cuda.synchronize()
     keys = numerics.bf16_from_bits(c["keys"]).reshape(B * Hkv, T, d)
-    G, Go = numerics.bf16_from_bits(Gu), numerics.bf16_from_bits(Gou)
+    G, Go = seeded.oracle_G(c["proj_seed"], m, d), seeded.oracle_G(synth.OUTLIER_PROJ_SEED, m_o, d)
     q = numerics.bf16_from_bits(c["q"])
     gi = ix.cpu().numpy()
     bi, bo = b_in.view(B * Hkv, T, m // 8).cpu().numpy(), b_out.view(B * Hkv, T, m_o // 8).cpu().numpy()

@@ -10,7 +10,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import codec, numerics
-from tests import parity
+from tests import parity, seeded
 from tests.test_gpu_codec import _case, _inputs, _proj, _signs
 
 pytestmark = pytest.mark.gpu
@@ -97,10 +97,10 @@ def test_packed_config3_tensor_sampled():
     layout = synth.config3_layout()
     _, layer, name, rows, cols = layout[4]
     _case("packed config3 tensor 4 (%s %dx%d), d=128, 4-bit" % (name, rows, cols))
-    xu, signs = synth.config3_tensor(4, rows, cols)
+    xu, sseed = synth.config3_tensor(4, rows, cols)
     d, bits = 128, 4
     x = parity.bf16_tensor(xu)
-    st = parity.u8_tensor(signs)
+    st = seeded.gpu_signs(sseed, d)
     packed, norms, _, _ = pq.quantize(x, d, bits, st, packed=True)
     codes, _, _, _ = pq.quantize(x, d, bits, st)
     out = pq.dequantize(packed, norms, d, bits, st, packed=True)
@@ -116,8 +116,7 @@ def test_packed_config3_tensor_sampled():
                                     np.random.default_rng(77).integers(0, n, 1500)]))
     sel = torch.from_numpy(idx).cuda()
     xs = numerics.bf16_from_bits(xu.reshape(-1, d)[idx])
-    from oracle import hadamard
-    D = hadamard.signs_from_mask(signs, d)
+    D = seeded.oracle_D(sseed, d)
     gc = codec.unpack_codes(packed[sel].cpu().numpy(), bits, d)
     parity.check_quantize(xs, bits, D, gc, parity.f16_values(norms[sel]), label="packed config3")
     parity.check_dequantize(gc, parity.f16_values(norms[sel]), bits, D,

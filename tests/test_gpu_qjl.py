@@ -7,7 +7,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import numerics, qjl
-from tests import parity
+from tests import parity, seeded
 
 pytestmark = pytest.mark.gpu
 
@@ -25,10 +25,9 @@ def test_sketch_parity(d, m, n):
     k[:, 3] *= 20.0
     k[0] = 0.0
     ku = synth.bf16_from_f32(k)
-    Gu = synth.projection(7, m, d)
-    bits, norms = pq.qjl_sketch(parity.bf16_tensor(ku), parity.bf16_tensor(Gu))
+    bits, norms = pq.qjl_sketch(parity.bf16_tensor(ku), seeded.gpu_proj(7, m, d))
     torch.cuda.synchronize()
-    st = parity.check_sketch(numerics.bf16_from_bits(ku), numerics.bf16_from_bits(Gu), bits.cpu().numpy(),
+    st = parity.check_sketch(numerics.bf16_from_bits(ku), seeded.oracle_G(7, m, d), bits.cpu().numpy(),
                              parity.f16_values(norms), label="sketch")
     print("  stats", st, flush=True)
 
@@ -38,11 +37,11 @@ def test_project_parity(d, m):
     _case("project d=%d m=%d" % (d, m))
     rng = np.random.default_rng(5)
     q = synth.bf16_from_f32(rng.standard_normal((37, d)).astype(np.float32))
-    Gu = synth.projection(11, m, d)
-    sq = pq.qjl_project(parity.bf16_tensor(q), parity.bf16_tensor(Gu))
+    sq = pq.qjl_project(parity.bf16_tensor(q), seeded.gpu_proj(11, m, d))
     torch.cuda.synchronize()
-    ref = numerics.bf16_from_bits(q) @ numerics.bf16_from_bits(Gu).T
-    scale = np.abs(numerics.bf16_from_bits(q)) @ np.abs(numerics.bf16_from_bits(Gu)).T
+    G = seeded.oracle_G(11, m, d)
+    ref = numerics.bf16_from_bits(q) @ G.T
+    scale = np.abs(numerics.bf16_from_bits(q)) @ np.abs(G).T
     assert np.all(np.abs(sq.cpu().numpy() - ref) <= 1e-5 * scale + 1e-30)
 
 
@@ -78,12 +77,12 @@ def test_sketch_then_score_end_to_end():
     c = synth.config4(batch=B, kv_heads=Hkv, tokens=T, q_heads=Hq, m=m)
     kt = parity.bf16_tensor(c["keys"])
     qt = parity.bf16_tensor(c["q"])
-    Gt = parity.bf16_tensor(c["G"])
+    Gt = seeded.gpu_proj(c["proj_seed"], m, d)
     bits, norms = pq.qjl_sketch(kt, Gt)
     sq = pq.qjl_project(qt, Gt)
     sc = pq.qjl_score(sq, bits, norms, B, Hkv, Hq, T)
     torch.cuda.synchronize()
-    G = numerics.bf16_from_bits(c["G"])
+    G = seeded.oracle_G(c["proj_seed"], m, d)
     keys = numerics.bf16_from_bits(c["keys"])
     q = numerics.bf16_from_bits(c["q"])
     # the sketch itself

@@ -8,7 +8,7 @@ import torch
 import kv_cache_quantization_amd as pq
 import synth
 from oracle import codec, hadamard, numerics, qjl
-from tests import parity
+from tests import parity, seeded
 
 pytestmark = pytest.mark.gpu
 
@@ -33,17 +33,16 @@ def _reference(codes, n16, qbits, rn16, q, bits, D, G, m):
     return q @ xhat.T, np.abs(q) @ np.abs(xhat).T
 
 
-def _check_prep(prep, qu, signs, Gu, d, m, n_heads, n_q):
+def _check_prep(prep, qu, D, G, d, m, n_heads, n_q):
+    """prep's H (D q) and G q against the oracle (D, G from the oracle's generator)."""
     qrot, sq = pq.prep_views(prep, d, m, n_heads)
     qrot, sq = qrot.cpu().numpy().astype(np.float64), sq.cpu().numpy().astype(np.float64)
     q = numerics.bf16_from_bits(qu)
-    D = hadamard.signs_from_mask(signs, d)
     H = hadamard.sylvester(d)
     ref = (q * D) @ H.T                                   # H (D q)
     assert np.all(np.abs(qrot[:, :n_q] - ref) <= 1e-6 * (np.abs(q) @ np.abs(H).T) + 1e-30)
     assert np.all(qrot[:, n_q:] == 0.0)
     if m:
-        G = numerics.bf16_from_bits(Gu)
         ref = q @ G.T
         assert np.all(np.abs(sq[:, :n_q] - ref) <= 1e-5 * (np.abs(q) @ np.abs(G).T) + 1e-30)
         assert np.all(sq[:, n_q:] == 0.0)
@@ -73,20 +72,17 @@ def test_two_stage_random_codes(d, bits, m, n_heads, n_q, n_tok):
     qbits = rng.integers(0, 256, size=(n_heads, n_tok, m // 8), dtype=np.uint8)
     rn16 = numerics.round_fp16(n16 * rng.uniform(0.0, 0.3, size=(n_heads, n_tok)))
     qu = _queries(rng, n_heads, n_q, d)
-    signs = synth.sign_mask(d + 1, d)
-    Gu = synth.projection(d + 2, m, d) if m else None
-
-    st = parity.u8_tensor(signs)
-    prep = pq.query_prep(parity.bf16_tensor(qu), st, parity.bf16_tensor(Gu) if m else None)
+    st = seeded.gpu_signs(d + 1, d)
+    prep = pq.query_prep(parity.bf16_tensor(qu), st, seeded.gpu_proj(d + 2, m, d) if m else None)
     out = pq.score(prep, parity.u8_tensor(codes), torch.from_numpy(n16.astype(np.float16)).cuda(), d, bits,
                    n_heads, n_q, n_tok, parity.u8_tensor(qbits) if m else None,
                    torch.from_numpy(rn16.astype(np.float16)).cuda() if m else None, m=m)
     torch.cuda.synchronize()
-    _check_prep(prep, qu, signs, Gu, d, m, n_heads, n_q)
+    D = seeded.oracle_D(d + 1, d)
+    G = seeded.oracle_G(d + 2, m, d) if m else None
+    _check_prep(prep, qu, D, G, d, m, n_heads, n_q)
     got = out.cpu().numpy().astype(np.float64)
     q = numerics.bf16_from_bits(qu)
-    D = hadamard.signs_from_mask(signs, d)
-    G = numerics.bf16_from_bits(Gu) if m else None
     for h in range(n_heads):
         ref, scale = _reference(codes[h], n16[h], qbits[h], rn16[h], q[h], bits, D, G, m)
         parity.check_scores(got[h], ref, np.maximum(scale, 1e-30), label="two-stage h%d" % h)
@@ -107,8 +103,8 @@ def test_two_stage_end_to_end_config5_shape(d):
     _case("two-stage end to end d=%d tokens=%d" % (d, n_tok))
     c = synth.config5_tensor(d, kv_heads=n_heads, tokens=n_tok, n_q=n_q)
     bits, m = c["bits"], c["m"]
-    st = parity.u8_tensor(c["signs"])
-    Gt = parity.bf16_tensor(c["G"])
+    st = seeded.gpu_signs(c["sign_seed"], d)
+    Gt = seeded.gpu_proj(c["proj_seed"], m, d)
     codes, norms, qb, rn = pq.quantize(parity.bf16_tensor(c["x"]), d, bits, st, Gt)
     prep = pq.query_prep(parity.bf16_tensor(c["q"]), st, Gt)
     out = pq.score(prep, codes, norms, d, bits, n_heads, n_q, n_tok, qb, rn, m=m)
@@ -119,8 +115,8 @@ def test_two_stage_end_to_end_config5_shape(d):
     qbits = qb.cpu().numpy().reshape(n_heads, n_tok, m // 8)
     rn16 = parity.f16_values(rn).reshape(n_heads, n_tok)
     q = numerics.bf16_from_bits(c["q"])
-    D = hadamard.signs_from_mask(c["signs"], d)
-    G = numerics.bf16_from_bits(c["G"])
+    D = seeded.oracle_D(c["sign_seed"], d)
+    G = seeded.oracle_G(c["proj_seed"], m, d)
     for h in range(n_heads):
         ref, scale = qjl.two_stage(codes_np[h], n16[h], qbits[h], rn16[h], q[h], bits, D, G)
         parity.check_scores(got[h], ref, np.maximum(scale, 1e-30), label="e2e two-stage h%d" % h)

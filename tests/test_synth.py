@@ -6,13 +6,19 @@ import synth
 
 
 def test_streams_are_deterministic_and_distinct():
-    a = synth.projection(42, 64, 128)
-    b = synth.projection(42, 64, 128)
-    c = synth.projection(43, 64, 128)
+    a = synth.gaussian_bf16(42, synth.TAG_DATA, (64, 128))
+    b = synth.gaussian_bf16(42, synth.TAG_DATA, (64, 128))
+    c = synth.gaussian_bf16(43, synth.TAG_DATA, (64, 128))
     assert a.dtype == np.uint16 and a.shape == (64, 128)
     assert np.array_equal(a, b) and not np.array_equal(a, c)
-    m = synth.sign_mask(42, 128)
-    assert m.shape == (16,) and np.array_equal(m, synth.sign_mask(42, 128))
+    assert not np.array_equal(a, synth.gaussian_bf16(42, synth.TAG_QUERY, (64, 128)))
+
+
+def test_configs_name_seeds_not_matrices():
+    """D and G are rebuilt from seeds by each side; a config carries only the seeds."""
+    c = synth.config2(rows=16, cols=128)
+    assert c["sign_seed"] == synth.BASE_SEED and c["proj_seed"] == synth.BASE_SEED
+    assert "signs" not in c and "G" not in c
 
 
 def test_bf16_cast_is_round_to_nearest_even():
