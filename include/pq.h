@@ -39,8 +39,9 @@
  *   Memory      every pointer argument of a device entry point is device
  *               memory allocated and owned by the caller; the library allocates
  *               nothing, keeps no pointer after return and holds no mutable
- *               global state, so concurrent calls from several threads are
- *               safe.  Host helpers take host memory.
+ *               global state (pq_attention_noalloc aside: it works in a fixed
+ *               array of the library, see there), so concurrent calls from
+ *               several threads are safe.  Host helpers take host memory.
  *   Alignment   tensors must be aligned to 16 bytes, except `norms`,
  *               `rnorms` (2 bytes) and the sign mask (1 byte).
  *   Empty input n_blocks == 0 (or n_keys == 0, n_q == 0, batch == 0) returns
@@ -76,6 +77,10 @@ extern "C" {
 #define PQ_EINVAL 1        /* bad pointer, size, alignment, dtype or parameter */
 #define PQ_EUNSUPPORTED 2  /* valid request outside what the kernels implement */
 #define PQ_EHIP 3          /* a HIP runtime call failed, see pq_last_hip_error() */
+#define PQ_ETOOBIG 4       /* needs more than the fixed work array of pq_attention_noalloc */
+
+/* bytes of the fixed device work array behind pq_attention_noalloc (one copy per device) */
+#define PQ_ATTN_NOALLOC_MAX_WORK (16 << 20)
 
 #define PQ_F32 0
 #define PQ_BF16 1
@@ -351,6 +356,28 @@ int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_
                         const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,
                         const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
                         const uint16_t* q, float sm_scale, void* work, float* out, void* stream);
+
+/*
+ * pq_attention / pq_attention_packed for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the work
+ * buffer is not an argument but a fixed array of PQ_ATTN_NOALLOC_MAX_WORK bytes in device
+ * memory that the library holds on every device it runs on until the process ends.  The
+ * call allocates nothing and frees nothing.
+ *   packed     0: byte codes (as pq_attention), 1: bit-packed codes (as pq_attention_packed)
+ *   other arguments, outputs and errors as pq_attention without `work`
+ * Returns PQ_ETOOBIG, launching nothing, when pq_attention_work_bytes(d, n_heads, n_tok)
+ * exceeds PQ_ATTN_NOALLOC_MAX_WORK (8.4 MB at 8 heads x 65536 tokens, d = 256 or 512).
+ * Every call on one device shares that device's array and leaves its partial results there
+ * (their contents on entry do not matter): calls that overlap in time on one device -- on
+ * two streams, or from two threads -- race and give undefined results; calls on one stream
+ * run in order and are safe.  The first call on a device looks up the array's address
+ * there (a HIP runtime call, made after the arguments are validated).
+ */
+int pq_attention_noalloc(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                         const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits,
+                         const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,
+                         const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
+                         const uint16_t* q, float sm_scale, int packed, float* out, void* stream);
 
 /*
  * Block sizes that are not powers of two (glq 0.7.2 README, "Advanced / Bit widths": a size

@@ -18,7 +18,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpqhip.so")
 
-PQ_OK, PQ_EINVAL, PQ_EUNSUPPORTED, PQ_EHIP = 0, 1, 2, 3
+PQ_OK, PQ_EINVAL, PQ_EUNSUPPORTED, PQ_EHIP, PQ_ETOOBIG = 0, 1, 2, 3, 4
+ATTN_NOALLOC_MAX_WORK = 16 << 20      # PQ_ATTN_NOALLOC_MAX_WORK of include/pq.h
 PQ_F32, PQ_BF16 = 0, 1
 
 
@@ -67,6 +68,8 @@ def _load():
         "pq_attention": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P], I),
         "pq_attention_packed": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, P, P, P],
                                 I),
+        "pq_attention_noalloc": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, I, P, P],
+                                 I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -82,7 +85,7 @@ EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", 
            "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
            "pq_query_prep", "pq_score", "pq_score_packed", "pq_attention_work_bytes", "pq_attention",
            "pq_attention_packed", "pq_quantize_bd", "pq_dequantize_bd", "pq_sphere_codebook",
-           "pq_quantize_dense", "pq_dequantize_dense")
+           "pq_quantize_dense", "pq_dequantize_dense", "pq_attention_noalloc")
 
 
 def lib():
@@ -382,6 +385,47 @@ def attention(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m=0, k_
     _check(fn(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(k_codes), _ptr(k_norms), _ptr(k_bits), _ptr(k_rn),
               _ptr(v_codes), _ptr(v_norms), _ptr(v_signs), n_win, _ptr(k_win), _ptr(v_win), _ptr(q),
               float(sm_scale), _ptr(work), _ptr(out), _stream()), name)
+    return out
+
+
+def attention_noalloc(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m=0, k_win=None, v_win=None,
+                      q=None, sm_scale=None, packed=False, out=None):
+    """``attention`` through pq_attention_noalloc: no work buffer is allocated or passed; the
+    library's fixed device array serves (calls overlapping on one device race).  ``out`` may be
+    preallocated (fp32 [n_heads, n_q, d]); nothing else is allocated when it is."""
+    k_codes, k_norms, k_bits, k_rn = keys
+    v_codes, v_norms = values
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _dev(t, name, (torch.uint8,))
+        if n_tok and t.numel() != n_heads * n_tok * (d * bits // 8 if packed else d):
+            raise ValueError("%s do not match n_heads, n_tok, d" % name)
+    _dev(k_norms, "k_norms", (torch.float16,))
+    _dev(v_norms, "v_norms", (torch.float16,))
+    _dev(v_signs, "v_signs", (torch.uint8,))
+    if n_tok:
+        _dev(prep, "prep", (torch.uint8,))
+    if m:
+        _dev(k_bits, "k_qjl_bits", (torch.uint8,))
+        _dev(k_rn, "k_rnorms", (torch.float16,))
+    n_win = 0
+    if k_win is not None:
+        _dev(k_win, "k_win", (torch.bfloat16,))
+        _dev(v_win, "v_win", (torch.bfloat16,))
+        _dev(q, "q", (torch.bfloat16,))
+        n_win = k_win.shape[1]
+        if k_win.shape != (n_heads, n_win, d) or v_win.shape != k_win.shape or q.shape != (n_heads, n_q, d):
+            raise ValueError("window or query shape does not match n_heads, n_q, d")
+    if sm_scale is None:
+        sm_scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty((n_heads, n_q, d), dtype=torch.float32, device=v_codes.device)
+    _dev(out, "out", (torch.float32,))
+    if out.numel() != n_heads * n_q * d:
+        raise ValueError("out does not match n_heads, n_q, d")
+    _check(_lib.pq_attention_noalloc(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(k_codes), _ptr(k_norms),
+                                     _ptr(k_bits), _ptr(k_rn), _ptr(v_codes), _ptr(v_norms), _ptr(v_signs), n_win,
+                                     _ptr(k_win), _ptr(v_win), _ptr(q), float(sm_scale), 1 if packed else 0,
+                                     _ptr(out), _stream()), "pq_attention_noalloc")
     return out
 
 

@@ -387,6 +387,7 @@ const char* pq_strerror(int status) {
     case PQ_EINVAL: return "invalid argument (pointer, size, alignment, dtype or parameter)";
     case PQ_EUNSUPPORTED: return "unsupported parameter combination";
     case PQ_EHIP: return "HIP runtime error (see pq_last_hip_error)";
+    case PQ_ETOOBIG: return "request needs more work memory than the library's fixed work array";
   }
   return "unknown status";
 }
@@ -636,11 +637,43 @@ int64_t pq_attention_work_bytes(int d, int n_heads, int64_t n_tok) {
   return pqi::attn_work_bytes(d, n_heads, n_tok);
 }
 
+// Work buffer of pq_attention_noalloc: a fixed array in device memory (one copy per device, at
+// its own address on each), used by every call on that device.  Host code never passes the
+// array's name to a kernel: it reads the array's device address once per device with
+// hipGetSymbolAddress, with that device current, and passes that address.
+static constexpr int64_t kAttnScratchBytes = (int64_t)PQ_ATTN_NOALLOC_MAX_WORK;
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch`, looked up on the first call per device.
+static int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return PQ_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PQ_OK;
+}
+
+// work == nullptr with use_scratch: the work buffer is this device's `scratch` array, fetched
+// after every argument has been validated.
 static int attention_impl(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
                           const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits,
                           const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,
                           const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
-                          const uint16_t* q, float sm_scale, void* work, float* out, int packed, void* stream) {
+                          const uint16_t* q, float sm_scale, void* work, float* out, int packed, void* stream,
+                          bool use_scratch = false) {
   int st = check_d(d);
   if (st) return st;
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
@@ -658,16 +691,20 @@ static int attention_impl(int d, int bits, int m, int n_heads, int n_q, int64_t 
   if (n_tok + n_win == 0) return PQ_EINVAL;             // softmax over no token
   if (!v_signs || !out) return PQ_EINVAL;
   if (n_tok > 0) {
-    if (!prep || !k_codes || !k_norms || !v_codes || !v_norms || !work) return PQ_EINVAL;
+    if (!prep || !k_codes || !k_norms || !v_codes || !v_norms || (!work && !use_scratch)) return PQ_EINVAL;
     if (m > 0 && (!k_qjl_bits || !k_rnorms)) return PQ_EINVAL;
     if (!aligned(prep, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_norms, 2) ||
-        !aligned(v_norms, 2) || !aligned(work, 16))
+        !aligned(v_norms, 2) || (!use_scratch && !aligned(work, 16)))
       return PQ_EINVAL;
     if (m > 0 && (!aligned(k_qjl_bits, 2) || !aligned(k_rnorms, 2))) return PQ_EINVAL;
   }
   if (n_win > 0 && (!k_win || !v_win || !q || !aligned(k_win, 16) || !aligned(v_win, 16) || !aligned(q, 2)))
     return PQ_EINVAL;
   if (!aligned(out, 4)) return PQ_EINVAL;
+  if (use_scratch && n_tok > 0) {
+    if (pqi::attn_work_bytes(d, n_heads, n_tok) > kAttnScratchBytes) return PQ_ETOOBIG;
+    if ((st = scratch_address(&work))) return st;
+  }
   const pqi::AttnPlan plan = pqi::attn_plan(d, n_heads, n_tok);
   pqi::AttnArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -709,6 +746,16 @@ int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_
                         const uint16_t* q, float sm_scale, void* work, float* out, void* stream) {
   return attention_impl(d, bits, m, n_heads, n_q, n_tok, prep, k_codes, k_norms, k_qjl_bits, k_rnorms, v_codes,
                         v_norms, v_signs, n_win, k_win, v_win, q, sm_scale, work, out, 1, stream);
+}
+
+int pq_attention_noalloc(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
+                         const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits,
+                         const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,
+                         const uint8_t* v_signs, int64_t n_win, const uint16_t* k_win, const uint16_t* v_win,
+                         const uint16_t* q, float sm_scale, int packed, float* out, void* stream) {
+  if (packed != 0 && packed != 1) return PQ_EINVAL;
+  return attention_impl(d, bits, m, n_heads, n_q, n_tok, prep, k_codes, k_norms, k_qjl_bits, k_rnorms, v_codes,
+                        v_norms, v_signs, n_win, k_win, v_win, q, sm_scale, nullptr, out, packed, stream, true);
 }
 
 int pq_quantize_bd(int d, int bits, int in_dtype, const void* x, int64_t n_blocks, const uint8_t* signs,

@@ -288,3 +288,33 @@ def test_dense_entry_points_validate():
     assert q(n=0) == pq.PQ_OK
     assert lib.pq_dequantize_dense(128, 4, P16, P16, 16, NUL, pq.PQ_BF16, P16, NUL) == pq.PQ_EINVAL
     assert lib.pq_dequantize_dense(128, 4, P16, P16, 0, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_OK
+
+
+def _noalloc(**kw):
+    a = dict(d=256, bits=3, m=0, heads=8, nq=16, ntok=65536, prep=P16, kc=P16, kn=P16, kb=NUL, kr=NUL, vc=P16,
+             vn=P16, vs=P16, nwin=0, kw=NUL, vw=NUL, q=NUL, scale=0.0625, packed=0, out=P16)
+    a.update(kw)
+    return pq.lib().pq_attention_noalloc(a["d"], a["bits"], a["m"], a["heads"], a["nq"], a["ntok"], a["prep"],
+                                         a["kc"], a["kn"], a["kb"], a["kr"], a["vc"], a["vn"], a["vs"], a["nwin"],
+                                         a["kw"], a["vw"], a["q"], a["scale"], a["packed"], a["out"], NUL)
+
+
+@pytest.mark.parametrize("kw,st", [
+    (dict(d=512, heads=4096, ntok=64), pq.PQ_ETOOBIG),      # 134 MB of work: beyond the fixed array
+    (dict(packed=2), pq.PQ_EINVAL), (dict(prep=NUL), pq.PQ_EINVAL), (dict(out=NUL), pq.PQ_EINVAL),
+    (dict(bits=5), pq.PQ_EUNSUPPORTED), (dict(ntok=0, nwin=0), pq.PQ_EINVAL), (dict(heads=0), pq.PQ_OK),
+])
+def test_attention_noalloc_validation(kw, st):
+    """Validation and the size limit of the allocation-free attention are decided on the host,
+    before any HIP call (so they run without a GPU)."""
+    assert _noalloc(**kw) == st
+    if st == pq.PQ_ETOOBIG:
+        assert pq.attention_work_bytes(kw["d"], kw["heads"], kw["ntok"]) > pq.ATTN_NOALLOC_MAX_WORK
+        assert pq.lib().pq_strerror(st) != pq.lib().pq_strerror(99)
+
+
+def test_noalloc_limit_matches_the_header():
+    import re
+    with open(os.path.join(ROOT, "include", "pq.h")) as f:
+        m = re.search(r"#define PQ_ATTN_NOALLOC_MAX_WORK \((\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == pq.ATTN_NOALLOC_MAX_WORK
