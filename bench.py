@@ -39,7 +39,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-sample-blocks", type=int, default=131072,
+    ap.add_argument("--cpu-sample-blocks", type=int, default=32768,
                     help="blocks of the workload the oracle baseline processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qjl", action="store_true", help="skip the config-4 QJL sketch/score leg")
@@ -77,37 +77,57 @@ def counter_traffic(kernel_name):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(n_blocks, min_seconds=10.0):
-    """Time the oracle (quantize + QJL residual + dequantize) on the first n_blocks of
-    the workload, on the host cores, repeating the pass until min_seconds have elapsed;
-    returns the record for the JSON line."""
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(n_blocks, min_seconds=6.0):
+    """Time the oracle (quantize + QJL residual + dequantize) on the first n_blocks of the
+    workload on the host, twice: with numpy's BLAS held to one thread, then with all of its
+    threads (every host core it sees), each pass repeated until min_seconds have elapsed;
+    returns the record for the JSON line (value = the all-core rate)."""
     import synth
     import oracle
     from oracle import numerics, seeds
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     c = synth.config2()
     d, bits = c["d"], c["bits"]
     x = numerics.bf16_from_bits(c["x"].reshape(-1, d)[:n_blocks])
     D = seeds.signs(c["sign_seed"], d)
     G = seeds.projection_values(c["proj_seed"], c["m"], d)
-    reps, dt = 0, 0.0
-    while dt < min_seconds:
-        t0 = time.perf_counter()
-        q = oracle.codec.quantize(x, bits, D)
-        r = oracle.codec.qjl_residual(x, q["codes"], q["n16"], bits, D, G)
-        xh = oracle.codec.dequantize(q["codes"], q["n16"], bits, D)
-        dt += time.perf_counter() - t0
-        reps += 1
-        assert r["bits"].shape[0] == n_blocks and xh.shape == x.shape
+
+    def run():
+        reps, dt = 0, 0.0
+        while dt < min_seconds:
+            t0 = time.perf_counter()
+            q = oracle.codec.quantize(x, bits, D)
+            r = oracle.codec.qjl_residual(x, q["codes"], q["n16"], bits, D, G)
+            xh = oracle.codec.dequantize(q["codes"], q["n16"], bits, D)
+            dt += time.perf_counter() - t0
+            reps += 1
+            assert r["bits"].shape[0] == n_blocks and xh.shape == x.shape
+        return reps, dt
+
+    with threadpool_limits(limits=1):
+        r1, t1 = run()
+    ra, ta = run()
     in_bytes = n_blocks * d * 2
-    return {"value": round(in_bytes * reps / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "first %d of 131072 blocks of the 4096x4096 weight (%.1f MB of bf16 input), "
-                      "quantize + QJL residual + dequantize, %d passes in %.2f s" % (
-                          n_blocks, in_bytes / 1e6, reps, dt)}
+    return {"value": round(in_bytes * ra / ta / 1e9, 6), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "value_1thread": round(in_bytes * r1 / t1 / 1e9, 6), "cpu_model": _cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "sample": "first %d of 131072 blocks of the 4096x4096 weight (%.1f MB of bf16 input), quantize + QJL "
+                      "residual + dequantize in the float64 oracle: %d passes in %.2f s on %d BLAS threads "
+                      "(value), %d passes in %.2f s on 1 thread (value_1thread)" % (
+                          n_blocks, in_bytes / 1e6, ra, ta, threads, r1, t1)}
 
 
 def summarize(run_dir):
