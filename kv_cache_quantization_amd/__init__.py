@@ -106,14 +106,31 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dev(t, name, dtypes):
+def _dev(t, name, dtypes, numel=None, device=None, min_numel=None):
+    """Check a caller tensor before its pointer reaches a kernel: a contiguous device tensor of
+    one of ``dtypes`` on ``device``, with exactly ``numel`` (or at least ``min_numel``)
+    elements.  A buffer of the wrong size would become an out-of-bounds device access, which
+    the C ABI (raw pointers) cannot see."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError("%s must be a device tensor" % name)
     if t.dtype not in dtypes:
         raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s has %d elements, needs at least %d" % (name, t.numel(), min_numel))
     return t
+
+
+def _proj_shape(proj, d, name="proj"):
+    """m of a JL matrix proj (bf16 [m, d])."""
+    if proj.dim() != 2 or proj.shape[1] != d:
+        raise ValueError("%s must be [m, %d], got %s" % (name, d, tuple(proj.shape)))
+    return proj.shape[0]
 
 
 def codebook(bits):
@@ -161,21 +178,30 @@ def quantize(x, d, bits, signs, proj=None, out=None, packed=False):
     pq_quantize_packed: codes are then uint8 [n, d * bits / 8], a bit stream per block.
     """
     _dev(x, "x", (torch.float32, torch.bfloat16))
-    _dev(signs, "signs", (torch.uint8,))
-    if x.numel() % d:
+    dev = x.device
+    _dev(signs, "signs", (torch.uint8,), numel=d // 8, device=dev)
+    if d <= 0 or x.numel() % d:
         raise ValueError("x.numel() must be a multiple of d")
     n = x.numel() // d
     m = 0
     if proj is not None:
-        _dev(proj, "proj", (torch.bfloat16,))
-        m = proj.shape[0]
+        _dev(proj, "proj", (torch.bfloat16,), device=dev)
+        m = _proj_shape(proj, d)
+    cb = d * bits // 8 if packed else d
     if out is None:
-        codes = torch.empty((n, d * bits // 8 if packed else d), dtype=torch.uint8, device=x.device)
-        norms = torch.empty((n,), dtype=torch.float16, device=x.device)
-        qb = torch.empty((n, m // 8), dtype=torch.uint8, device=x.device) if m else None
-        rn = torch.empty((n,), dtype=torch.float16, device=x.device) if m else None
+        codes = torch.empty((n, cb), dtype=torch.uint8, device=dev)
+        norms = torch.empty((n,), dtype=torch.float16, device=dev)
+        qb = torch.empty((n, m // 8), dtype=torch.uint8, device=dev) if m else None
+        rn = torch.empty((n,), dtype=torch.float16, device=dev) if m else None
     else:
         codes, norms, qb, rn = out
+    _dev(codes, "codes", (torch.uint8,), numel=n * cb, device=dev)
+    _dev(norms, "norms", (torch.float16,), numel=n, device=dev)
+    if m:
+        _dev(qb, "qjl_bits", (torch.uint8,), numel=n * (m // 8), device=dev)
+        _dev(rn, "rnorms", (torch.float16,), numel=n, device=dev)
+    elif qb is not None or rn is not None:
+        raise ValueError("qjl_bits and rnorms need proj")
     dt = PQ_BF16 if x.dtype == torch.bfloat16 else PQ_F32
     fn, name = (_lib.pq_quantize_packed, "pq_quantize_packed") if packed else (_lib.pq_quantize, "pq_quantize")
     _check(fn(d, bits, dt, _ptr(x), n, _ptr(signs), m, _ptr(proj), _ptr(codes), _ptr(norms),
@@ -186,15 +212,14 @@ def quantize(x, d, bits, signs, proj=None, out=None, packed=False):
 def dequantize(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None, packed=False):
     """Reconstruct blocks from codes (uint8 [n, d], or [n, d * bits / 8] with ``packed``,
     which calls pq_dequantize_packed) and fp16 norms; returns [n, d]."""
-    _dev(codes, "codes", (torch.uint8,))
     _dev(norms, "norms", (torch.float16,))
-    _dev(signs, "signs", (torch.uint8,))
+    dev = norms.device
     n = norms.numel()
-    if codes.numel() != n * (d * bits // 8 if packed else d):
-        raise ValueError("codes do not match norms")
+    _dev(codes, "codes", (torch.uint8,), numel=n * (d * bits // 8 if packed else d), device=dev)
+    _dev(signs, "signs", (torch.uint8,), numel=d // 8, device=dev)
     if out is None:
-        out = torch.empty((n, d), dtype=out_dtype, device=codes.device)
-    _dev(out, "out", (torch.float32, torch.bfloat16))
+        out = torch.empty((n, d), dtype=out_dtype, device=dev)
+    _dev(out, "out", (torch.float32, torch.bfloat16), numel=n * d, device=dev)
     dt = PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32
     fn, name = (_lib.pq_dequantize_packed, "pq_dequantize_packed") if packed else (_lib.pq_dequantize, "pq_dequantize")
     _check(fn(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs), dt, _ptr(out), _stream()), name)
@@ -208,22 +233,31 @@ def qjl_sketch(keys, proj, out=None, split=None):
     group's outlier channels (qjl_sketch_split): part 0 without them, part 1 only them;
     keys are then [heads, seq_len, d] and idx as from ``qjl_outlier_channels``."""
     _dev(keys, "keys", (torch.bfloat16,))
-    _dev(proj, "proj", (torch.bfloat16,))
+    dev = keys.device
+    _dev(proj, "proj", (torch.bfloat16,), device=dev)
+    if proj.dim() != 2:
+        raise ValueError("proj must be [m, d]")
     m, d = proj.shape
+    if keys.numel() % d:
+        raise ValueError("keys.numel() must be a multiple of d")
     n = keys.numel() // d
     if out is None:
-        bits = torch.empty((n, m // 8), dtype=torch.uint8, device=keys.device)
-        norms = torch.empty((n,), dtype=torch.float16, device=keys.device)
+        bits = torch.empty((n, m // 8), dtype=torch.uint8, device=dev)
+        norms = torch.empty((n,), dtype=torch.float16, device=dev)
     else:
         bits, norms = out
+    _dev(bits, "bits", (torch.uint8,), numel=n * (m // 8), device=dev)
+    _dev(norms, "norms", (torch.float16,), numel=n, device=dev)
     if split is None:
         _check(_lib.qjl_sketch(d, m, _ptr(keys), n, _ptr(proj), _ptr(bits), _ptr(norms), _stream()), "qjl_sketch")
     else:
         idx, seq_len, group_size, part = split
-        _dev(idx, "idx", (torch.uint8,))
-        if n % seq_len:
+        if seq_len <= 0 or n % seq_len or group_size <= 0:
             raise ValueError("keys are not [heads, seq_len, d]")
-        _check(_lib.qjl_sketch_split(d, m, _ptr(keys), n // seq_len, seq_len, group_size, idx.shape[-1], _ptr(idx),
+        heads = n // seq_len
+        n_out = idx.shape[-1]
+        _dev(idx, "idx", (torch.uint8,), numel=heads * (-(-seq_len // group_size)) * n_out, device=dev)
+        _check(_lib.qjl_sketch_split(d, m, _ptr(keys), heads, seq_len, group_size, n_out, _ptr(idx),
                                      part, _ptr(proj), _ptr(bits), _ptr(norms), _stream()), "qjl_sketch_split")
     return bits, norms
 
@@ -232,11 +266,14 @@ def qjl_outlier_channels(keys, group_size, n_out, out=None):
     """keys bf16 [..., seq_len, d] -> uint8 [..., ceil(seq_len / group_size), n_out]: per group of
     group_size consecutive tokens, the n_out channels of largest norm, decreasing."""
     _dev(keys, "keys", (torch.bfloat16,))
+    if keys.dim() < 2 or group_size <= 0:
+        raise ValueError("keys must be [..., seq_len, d] and group_size positive")
     seq_len, d = keys.shape[-2], keys.shape[-1]
-    heads = keys.numel() // (seq_len * d)
+    heads = keys.numel() // (seq_len * d) if seq_len * d else 0
     n_groups = (seq_len + group_size - 1) // group_size
     if out is None:
         out = torch.empty(tuple(keys.shape[:-2]) + (n_groups, n_out), dtype=torch.uint8, device=keys.device)
+    _dev(out, "out", (torch.uint8,), numel=heads * n_groups * n_out, device=keys.device)
     _check(_lib.qjl_outlier_channels(d, _ptr(keys), heads, seq_len, group_size, n_out, _ptr(out), _stream()),
            "qjl_outlier_channels")
     return out
@@ -245,11 +282,16 @@ def qjl_outlier_channels(keys, group_size, n_out, out=None):
 def qjl_project(q, proj, out=None):
     """Project queries q (bf16 [..., d]) through G: fp32 [n_q, m]."""
     _dev(q, "q", (torch.bfloat16,))
-    _dev(proj, "proj", (torch.bfloat16,))
+    _dev(proj, "proj", (torch.bfloat16,), device=q.device)
+    if proj.dim() != 2:
+        raise ValueError("proj must be [m, d]")
     m, d = proj.shape
+    if q.numel() % d:
+        raise ValueError("q.numel() must be a multiple of d")
     nq = q.numel() // d
     if out is None:
         out = torch.empty((nq, m), dtype=torch.float32, device=q.device)
+    _dev(out, "out", (torch.float32,), numel=nq * m, device=q.device)
     _check(_lib.qjl_project(d, m, _ptr(q), nq, _ptr(proj), _ptr(out), _stream()), "qjl_project")
     return out
 
@@ -258,13 +300,16 @@ def qjl_score(sq, bits, norms, batch, kv_heads, q_heads, n_keys, out=None, accum
     """QJL scores [batch, q_heads, n_keys] fp32 from projected queries and packed key bits;
     ``accumulate`` adds them to ``out`` (qjl_score_add)."""
     _dev(sq, "sq", (torch.float32,))
-    _dev(bits, "bits", (torch.uint8,))
-    _dev(norms, "norms", (torch.float16,))
+    dev = sq.device
     m = sq.shape[-1]
+    _dev(sq, "sq", (torch.float32,), numel=batch * q_heads * m)
+    _dev(bits, "bits", (torch.uint8,), numel=batch * kv_heads * n_keys * (m // 8), device=dev)
+    _dev(norms, "norms", (torch.float16,), numel=batch * kv_heads * n_keys, device=dev)
     if accumulate and out is None:
         raise ValueError("accumulate needs out")
     if out is None:
-        out = torch.empty((batch, q_heads, n_keys), dtype=torch.float32, device=sq.device)
+        out = torch.empty((batch, q_heads, n_keys), dtype=torch.float32, device=dev)
+    _dev(out, "out", (torch.float32,), numel=batch * q_heads * n_keys, device=dev)
     fn, name = (_lib.qjl_score_add, "qjl_score_add") if accumulate else (_lib.qjl_score, "qjl_score")
     _check(fn(m, batch, kv_heads, q_heads, n_keys, _ptr(sq), _ptr(bits), _ptr(norms), _ptr(out), _stream()), name)
     return out
@@ -285,14 +330,19 @@ def query_prep(q, signs, proj=None, out=None):
     and G q as fp32 [16, m] (see ``prep_views``).
     """
     _dev(q, "q", (torch.bfloat16,))
-    _dev(signs, "signs", (torch.uint8,))
+    if q.dim() != 3:
+        raise ValueError("q must be [n_heads, n_q, d]")
     n_heads, n_q, d = q.shape
+    dev = q.device
+    _dev(signs, "signs", (torch.uint8,), numel=d // 8, device=dev)
     m = 0
     if proj is not None:
-        _dev(proj, "proj", (torch.bfloat16,))
-        m = proj.shape[0]
+        _dev(proj, "proj", (torch.bfloat16,), device=dev)
+        m = _proj_shape(proj, d)
+    need = query_prep_bytes(d, m, n_heads)
     if out is None:
-        out = torch.empty((query_prep_bytes(d, m, n_heads),), dtype=torch.uint8, device=q.device)
+        out = torch.empty((need,), dtype=torch.uint8, device=dev)
+    _dev(out, "out", (torch.uint8,), min_numel=need, device=dev)
     _check(_lib.pq_query_prep(d, m, n_heads, n_q, _ptr(q), _ptr(signs), _ptr(proj), _ptr(out), _stream()),
            "pq_query_prep")
     return out
@@ -301,7 +351,7 @@ def query_prep(q, signs, proj=None, out=None):
 def prep_views(prep, d, m, n_heads):
     """(qrot fp32 [n_heads, 16, d], sq fp32 [n_heads, 16, m]) views of a prepared-query buffer."""
     per = query_prep_bytes(d, m, 1)
-    heads = prep.view(n_heads, per)
+    heads = prep[:per * n_heads].view(n_heads, per)
     qrot = heads[:, :16 * d * 4].contiguous().view(torch.float32).view(n_heads, 16, d)
     sq = heads[:, 16 * d * 4:16 * (d + m) * 4].contiguous().view(torch.float32).view(n_heads, 16, m)
     return qrot, sq
@@ -312,17 +362,16 @@ def score(prep, codes, norms, d, bits, n_heads, n_q, n_tok, qjl_bits=None, rnorm
     """Two-stage scores fp32 [n_heads, n_q, n_tok] from codes [n_heads, n_tok, d] (or bit-packed,
     d * bits / 8 bytes per token, with ``packed``: pq_score_packed), norms, and (with m > 0)
     the QJL residual bits and residual norms."""
-    _dev(prep, "prep", (torch.uint8,))
-    _dev(codes, "codes", (torch.uint8,))
-    _dev(norms, "norms", (torch.float16,))
+    _dev(codes, "codes", (torch.uint8,), numel=n_heads * n_tok * (d * bits // 8 if packed else d))
+    dev = codes.device
+    _dev(prep, "prep", (torch.uint8,), min_numel=query_prep_bytes(d, m, n_heads), device=dev)
+    _dev(norms, "norms", (torch.float16,), numel=n_heads * n_tok, device=dev)
     if m:
-        _dev(qjl_bits, "qjl_bits", (torch.uint8,))
-        _dev(rnorms, "rnorms", (torch.float16,))
+        _dev(qjl_bits, "qjl_bits", (torch.uint8,), numel=n_heads * n_tok * (m // 8), device=dev)
+        _dev(rnorms, "rnorms", (torch.float16,), numel=n_heads * n_tok, device=dev)
     if out is None:
-        out = torch.empty((n_heads, n_q, n_tok), dtype=torch.float32, device=codes.device)
-    _dev(out, "out", (torch.float32,))
-    if codes.numel() != n_heads * n_tok * (d * bits // 8 if packed else d):
-        raise ValueError("codes do not match n_heads, n_tok, d")
+        out = torch.empty((n_heads, n_q, n_tok), dtype=torch.float32, device=dev)
+    _dev(out, "out", (torch.float32,), numel=n_heads * n_q * n_tok, device=dev)
     fn, name = (_lib.pq_score_packed, "pq_score_packed") if packed else (_lib.pq_score, "pq_score")
     _check(fn(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(codes), _ptr(norms), _ptr(qjl_bits),
               _ptr(rnorms), _ptr(out), _stream()), name)
@@ -337,6 +386,39 @@ def attention_work_bytes(d, n_heads, n_tok):
     return nb
 
 
+def _attention_inputs(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m, k_win, v_win, q, packed, out):
+    """Checks shared by ``attention`` and ``attention_noalloc``; returns (n_win, out)."""
+    k_codes, k_norms, k_bits, k_rn = keys
+    v_codes, v_norms = values
+    _dev(v_codes, "v_codes", (torch.uint8,))
+    dev = v_codes.device
+    cb = d * bits // 8 if packed else d
+    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _dev(t, name, (torch.uint8,), numel=n_heads * n_tok * cb, device=dev)
+    _dev(k_norms, "k_norms", (torch.float16,), numel=n_heads * n_tok, device=dev)
+    _dev(v_norms, "v_norms", (torch.float16,), numel=n_heads * n_tok, device=dev)
+    _dev(v_signs, "v_signs", (torch.uint8,), numel=d // 8, device=dev)
+    if n_tok:
+        _dev(prep, "prep", (torch.uint8,), min_numel=query_prep_bytes(d, m, n_heads), device=dev)
+    if m:
+        _dev(k_bits, "k_qjl_bits", (torch.uint8,), numel=n_heads * n_tok * (m // 8), device=dev)
+        _dev(k_rn, "k_rnorms", (torch.float16,), numel=n_heads * n_tok, device=dev)
+    n_win = 0
+    if k_win is not None:
+        _dev(k_win, "k_win", (torch.bfloat16,), device=dev)
+        _dev(v_win, "v_win", (torch.bfloat16,), device=dev)
+        _dev(q, "q", (torch.bfloat16,), device=dev)
+        if k_win.dim() != 3:
+            raise ValueError("k_win must be [n_heads, n_win, d]")
+        n_win = k_win.shape[1]
+        if k_win.shape != (n_heads, n_win, d) or v_win.shape != k_win.shape or q.shape != (n_heads, n_q, d):
+            raise ValueError("window or query shape does not match n_heads, n_q, d")
+    if out is None:
+        out = torch.empty((n_heads, n_q, d), dtype=torch.float32, device=dev)
+    _dev(out, "out", (torch.float32,), numel=n_heads * n_q * d, device=dev)
+    return n_win, out
+
+
 def attention(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m=0, k_win=None, v_win=None,
               q=None, sm_scale=None, packed=False, work=None, out=None):
     """Decode attention over a quantized cache plus an unquantized recent window.
@@ -348,39 +430,16 @@ def attention(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m=0, k_
     needed with a window.  Returns fp32 [n_heads, n_q, d]; sm_scale defaults to 1/sqrt(d).
     ``packed``: codes bit-packed at the code width (pq_attention_packed).
     """
+    n_win, out = _attention_inputs(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m, k_win, v_win, q,
+                                   packed, out)
     k_codes, k_norms, k_bits, k_rn = keys
     v_codes, v_norms = values
-    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
-        _dev(t, name, (torch.uint8,))
-        if n_tok and t.numel() != n_heads * n_tok * (d * bits // 8 if packed else d):
-            raise ValueError("%s do not match n_heads, n_tok, d" % name)
-    _dev(k_norms, "k_norms", (torch.float16,))
-    _dev(v_norms, "v_norms", (torch.float16,))
-    _dev(v_signs, "v_signs", (torch.uint8,))
-    if n_tok:
-        _dev(prep, "prep", (torch.uint8,))
-    if m:
-        _dev(k_bits, "k_qjl_bits", (torch.uint8,))
-        _dev(k_rn, "k_rnorms", (torch.float16,))
-    n_win = 0
-    if k_win is not None:
-        _dev(k_win, "k_win", (torch.bfloat16,))
-        _dev(v_win, "v_win", (torch.bfloat16,))
-        _dev(q, "q", (torch.bfloat16,))
-        n_win = k_win.shape[1]
-        if k_win.shape != (n_heads, n_win, d) or v_win.shape != k_win.shape or q.shape != (n_heads, n_q, d):
-            raise ValueError("window or query shape does not match n_heads, n_q, d")
     if sm_scale is None:
         sm_scale = 1.0 / float(d) ** 0.5
-    dev = v_codes.device
+    need = attention_work_bytes(d, n_heads, n_tok)
     if work is None:
-        work = torch.empty((max(16, attention_work_bytes(d, n_heads, n_tok)),), dtype=torch.uint8, device=dev)
-    _dev(work, "work", (torch.uint8,))
-    if work.numel() < attention_work_bytes(d, n_heads, n_tok):
-        raise ValueError("work buffer too small")
-    if out is None:
-        out = torch.empty((n_heads, n_q, d), dtype=torch.float32, device=dev)
-    _dev(out, "out", (torch.float32,))
+        work = torch.empty((max(16, need),), dtype=torch.uint8, device=out.device)
+    _dev(work, "work", (torch.uint8,), min_numel=need, device=out.device)
     fn, name = (_lib.pq_attention_packed, "pq_attention_packed") if packed else (_lib.pq_attention, "pq_attention")
     _check(fn(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(k_codes), _ptr(k_norms), _ptr(k_bits), _ptr(k_rn),
               _ptr(v_codes), _ptr(v_norms), _ptr(v_signs), n_win, _ptr(k_win), _ptr(v_win), _ptr(q),
@@ -393,35 +452,12 @@ def attention_noalloc(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok,
     """``attention`` through pq_attention_noalloc: no work buffer is allocated or passed; the
     library's fixed device array serves (calls overlapping on one device race).  ``out`` may be
     preallocated (fp32 [n_heads, n_q, d]); nothing else is allocated when it is."""
+    n_win, out = _attention_inputs(prep, keys, values, v_signs, d, bits, n_heads, n_q, n_tok, m, k_win, v_win, q,
+                                   packed, out)
     k_codes, k_norms, k_bits, k_rn = keys
     v_codes, v_norms = values
-    for t, name in ((k_codes, "k_codes"), (v_codes, "v_codes")):
-        _dev(t, name, (torch.uint8,))
-        if n_tok and t.numel() != n_heads * n_tok * (d * bits // 8 if packed else d):
-            raise ValueError("%s do not match n_heads, n_tok, d" % name)
-    _dev(k_norms, "k_norms", (torch.float16,))
-    _dev(v_norms, "v_norms", (torch.float16,))
-    _dev(v_signs, "v_signs", (torch.uint8,))
-    if n_tok:
-        _dev(prep, "prep", (torch.uint8,))
-    if m:
-        _dev(k_bits, "k_qjl_bits", (torch.uint8,))
-        _dev(k_rn, "k_rnorms", (torch.float16,))
-    n_win = 0
-    if k_win is not None:
-        _dev(k_win, "k_win", (torch.bfloat16,))
-        _dev(v_win, "v_win", (torch.bfloat16,))
-        _dev(q, "q", (torch.bfloat16,))
-        n_win = k_win.shape[1]
-        if k_win.shape != (n_heads, n_win, d) or v_win.shape != k_win.shape or q.shape != (n_heads, n_q, d):
-            raise ValueError("window or query shape does not match n_heads, n_q, d")
     if sm_scale is None:
         sm_scale = 1.0 / float(d) ** 0.5
-    if out is None:
-        out = torch.empty((n_heads, n_q, d), dtype=torch.float32, device=v_codes.device)
-    _dev(out, "out", (torch.float32,))
-    if out.numel() != n_heads * n_q * d:
-        raise ValueError("out does not match n_heads, n_q, d")
     _check(_lib.pq_attention_noalloc(d, bits, m, n_heads, n_q, n_tok, _ptr(prep), _ptr(k_codes), _ptr(k_norms),
                                      _ptr(k_bits), _ptr(k_rn), _ptr(v_codes), _ptr(v_norms), _ptr(v_signs), n_win,
                                      _ptr(k_win), _ptr(v_win), _ptr(q), float(sm_scale), 1 if packed else 0,
@@ -434,14 +470,16 @@ def quantize_bd(x, d, bits, signs, out=None):
     (any multiple of 32 in 64..4096): x fp32 or bf16 with numel a multiple of d.
     Returns (codes uint8 [n_blocks, d], norms fp16 [n_blocks])."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
-    _dev(signs, "signs", (torch.uint8,))
-    if x.numel() % d:
+    dev = x.device
+    _dev(signs, "signs", (torch.uint8,), numel=d // 8, device=dev)
+    if d <= 0 or x.numel() % d:
         raise ValueError("x.numel() must be a multiple of d")
     n = x.numel() // d
     if out is None:
-        out = (torch.empty((n, d), dtype=torch.uint8, device=x.device),
-               torch.empty((n,), dtype=torch.float16, device=x.device))
+        out = (torch.empty((n, d), dtype=torch.uint8, device=dev), torch.empty((n,), dtype=torch.float16, device=dev))
     codes, norms = out
+    _dev(codes, "codes", (torch.uint8,), numel=n * d, device=dev)
+    _dev(norms, "norms", (torch.float16,), numel=n, device=dev)
     _check(_lib.pq_quantize_bd(d, bits, PQ_BF16 if x.dtype == torch.bfloat16 else PQ_F32, _ptr(x), n,
                                _ptr(signs), _ptr(codes), _ptr(norms), _stream()), "pq_quantize_bd")
     return codes, norms
@@ -449,15 +487,14 @@ def quantize_bd(x, d, bits, signs, out=None):
 
 def dequantize_bd(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None):
     """Inverse of ``quantize_bd``: [n_blocks, d] of out_dtype (fp32 or bf16)."""
-    _dev(codes, "codes", (torch.uint8,))
     _dev(norms, "norms", (torch.float16,))
-    _dev(signs, "signs", (torch.uint8,))
+    dev = norms.device
     n = norms.numel()
-    if codes.numel() != n * d:
-        raise ValueError("codes do not match norms and d")
+    _dev(codes, "codes", (torch.uint8,), numel=n * d, device=dev)
+    _dev(signs, "signs", (torch.uint8,), numel=d // 8, device=dev)
     if out is None:
-        out = torch.empty((n, d), dtype=out_dtype, device=codes.device)
-    _dev(out, "out", (torch.float32, torch.bfloat16))
+        out = torch.empty((n, d), dtype=out_dtype, device=dev)
+    _dev(out, "out", (torch.float32, torch.bfloat16), numel=n * d, device=dev)
     _check(_lib.pq_dequantize_bd(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs),
                                  PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32, _ptr(out), _stream()),
            "pq_dequantize_bd")
@@ -476,14 +513,16 @@ def quantize_dense(x, d, bits, rot, out=None):
     """Codec with a dense rotation rot (fp32 [d, d], row-major, device) and the sphere-coordinate
     codebook.  Returns (codes uint8 [n_blocks, d], norms fp16 [n_blocks])."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
-    _dev(rot, "rot", (torch.float32,))
-    if x.numel() % d or rot.numel() != d * d:
-        raise ValueError("x.numel() must be a multiple of d and rot must be d x d")
+    dev = x.device
+    _dev(rot, "rot", (torch.float32,), numel=d * d, device=dev)
+    if d <= 0 or x.numel() % d:
+        raise ValueError("x.numel() must be a multiple of d")
     n = x.numel() // d
     if out is None:
-        out = (torch.empty((n, d), dtype=torch.uint8, device=x.device),
-               torch.empty((n,), dtype=torch.float16, device=x.device))
+        out = (torch.empty((n, d), dtype=torch.uint8, device=dev), torch.empty((n,), dtype=torch.float16, device=dev))
     codes, norms = out
+    _dev(codes, "codes", (torch.uint8,), numel=n * d, device=dev)
+    _dev(norms, "norms", (torch.float16,), numel=n, device=dev)
     _check(_lib.pq_quantize_dense(d, bits, PQ_BF16 if x.dtype == torch.bfloat16 else PQ_F32, _ptr(x), n, _ptr(rot),
                                   _ptr(codes), _ptr(norms), _stream()), "pq_quantize_dense")
     return codes, norms
@@ -491,15 +530,14 @@ def quantize_dense(x, d, bits, rot, out=None):
 
 def dequantize_dense(codes, norms, d, bits, rot, out_dtype=torch.bfloat16, out=None):
     """Inverse of ``quantize_dense``: [n_blocks, d] of out_dtype (fp32 or bf16)."""
-    _dev(codes, "codes", (torch.uint8,))
     _dev(norms, "norms", (torch.float16,))
-    _dev(rot, "rot", (torch.float32,))
+    dev = norms.device
     n = norms.numel()
-    if codes.numel() != n * d:
-        raise ValueError("codes do not match norms and d")
+    _dev(codes, "codes", (torch.uint8,), numel=n * d, device=dev)
+    _dev(rot, "rot", (torch.float32,), numel=d * d, device=dev)
     if out is None:
-        out = torch.empty((n, d), dtype=out_dtype, device=codes.device)
-    _dev(out, "out", (torch.float32, torch.bfloat16))
+        out = torch.empty((n, d), dtype=out_dtype, device=dev)
+    _dev(out, "out", (torch.float32, torch.bfloat16), numel=n * d, device=dev)
     _check(_lib.pq_dequantize_dense(d, bits, _ptr(codes), _ptr(norms), n, _ptr(rot),
                                     PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32, _ptr(out), _stream()),
            "pq_dequantize_dense")
