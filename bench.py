@@ -207,6 +207,100 @@ def summarize(run_dir):
         fh.write("\n")
     print("\n".join(lines))
     print(json.dumps(rec["kernels"]))
+    if os.path.isdir(os.path.join(run_dir, "pmc_sq_a")):
+        summarize_sq(run_dir)
+
+
+# the kernels whose instruction mix and matrix-core use the benchmark reports, with the units
+# (tiles of 16 blocks or keys) one launch processes in the benchmark's workload
+SQ_KERNELS = (
+    ("pq_quantize_kernel<128, true, true, false, 1, 1024, true>", "config-2 quantize + QJL (m=64)", 131072 // 16),
+    ("pq_dequantize_kernel<128, true, 0>", "config-2 dequantize", 131072 // 16),
+    ("pq_quantize_kernel<256, true, true, true, 1, 512, false>", "config-5 d=256 quantize + QJL (m=256)", 524288 // 16),
+    ("pq_quantize_chunked_kernel<512, true, 1>", "config-5 d=512 quantize + QJL (m=512)", 524288 // 16),
+    ("qjl_sketch_kernel<128, true, false>", "config-4 QJL sketch (m=256)", 1048576 // 16),
+    ("qjl_score_kernel<4, false>", "config-4 QJL score (4 query heads per KV head)", 1048576 // 16),
+    ("pq_score_kernel<256, 3, 4, false>", "config-5 d=256 two-stage score (16 queries)", 524288 // 16),
+    ("pq_score_kernel<512, 3, 8, false>", "config-5 d=512 two-stage score (16 queries)", 524288 // 16),
+    ("pq_attend_kernel<256, 3, 4, false>", "config-5 d=256 decode attention", 524288 // 16),
+    ("pq_attend_kernel<512, 3, 8, false>", "config-5 d=512 decode attention", 524288 // 16),
+)
+SQ_SET_A = "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_BUSY_CU_CYCLES SQ_WAVES GRBM_GUI_ACTIVE GRBM_COUNT"
+SQ_SET_B = ("SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_LDS SQ_WAVE_CYCLES "
+            "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_I8 GRBM_GUI_ACTIVE")
+SQ_BENCH_ARGS = "python3 bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-grouped --no-bd --no-dense"
+
+
+def summarize_sq(run_dir):
+    """profiles/sq_counters_bench_kernels.{json,txt} from two rocprofv3 --pmc runs of the
+    benchmark (run_dir/pmc_sq_a, run_dir/pmc_sq_b).  Derived figures follow rocprofv3's own
+    metric definitions: MfmaUtil = sum SQ_VALU_MFMA_BUSY_CYCLES / (max-per-XCC GRBM_GUI_ACTIVE x
+    1024 SIMDs), VALUBusy = sum SQ_ACTIVE_INST_VALU / 256 CUs / max-per-XCC GRBM_GUI_ACTIVE; the
+    per-dispatch GRBM_GUI_ACTIVE rows are sums over the 8 XCCs, so max-per-XCC is taken as 1/8 of
+    them (the XCCs run the kernel together)."""
+    import csv
+    out_dir = os.path.join(ROOT, "profiles")
+
+    def load(sub):
+        vals = {}
+        with open(os.path.join(run_dir, sub, "pmc_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "").split("(pqi::")[0]
+                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    a, b = load("pmc_sq_a"), load("pmc_sq_b")
+    rec = {"source_hash": kernel_source_hash(),
+           "commands": ["rocprofv3 --pmc %s --output-format csv -d <dir>/pmc_sq_a -o pmc -- %s" % (SQ_SET_A, SQ_BENCH_ARGS),
+                        "rocprofv3 --pmc %s --output-format csv -d <dir>/pmc_sq_b -o pmc -- %s" % (SQ_SET_B, SQ_BENCH_ARGS)],
+           "definitions": {"valu_insts_per_tile": "SQ_INSTS_VALU / tiles of 16 blocks (keys) per launch",
+                           "mfma_insts_per_tile": "SQ_INSTS_MFMA / tiles per launch",
+                           "mfma_util": "sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs)",
+                           "valu_busy": "sum SQ_ACTIVE_INST_VALU / 256 CUs / (GRBM_GUI_ACTIVE / 8)",
+                           "mfma_mops_per_launch": "(SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16 + _I8) x 512 flops (or int ops)"},
+           "kernels": {}}
+    lines = ["# SQ counters of the benchmark's hot kernels, one MI355X (per launch, means over dispatches)", "",
+             "commands:"] + ["  " + c for c in rec["commands"]] + ["kernel source hash: " + rec["source_hash"], "",
+             "%-58s %8s %9s %8s %9s %9s %12s" % ("kernel", "tiles", "VALU/tile", "MFMA/tl", "MfmaUtil", "VALUBusy",
+                                                "MFMA Mops")]
+    mean = lambda d, k: sum(d[k]) / len(d[k]) if k in d and d[k] else float("nan")
+    for kname, what, tiles in SQ_KERNELS:
+        if kname not in a or kname not in b:
+            continue
+        ka, kb = a[kname], b[kname]
+        grbm_a, grbm_b = mean(ka, "GRBM_GUI_ACTIVE") / 8.0, mean(kb, "GRBM_GUI_ACTIVE") / 8.0
+        mops = sum(mean(kb, c) for c in ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                         "SQ_INSTS_VALU_MFMA_MOPS_I8") if c in kb) * 512
+        e = {"workload": what, "tiles_per_launch": tiles, "dispatches": len(ka.get("SQ_INSTS_VALU", [])),
+             "raw": {k: mean(ka, k) for k in ka} | {k: mean(kb, k) for k in kb},
+             "valu_insts_per_tile": mean(ka, "SQ_INSTS_VALU") / tiles,
+             "mfma_insts_per_tile": mean(ka, "SQ_INSTS_MFMA") / tiles,
+             "mfma_util": mean(kb, "SQ_VALU_MFMA_BUSY_CYCLES") / (grbm_b * 1024),
+             "valu_busy": mean(kb, "SQ_ACTIVE_INST_VALU") / 256 / grbm_b,
+             "mfma_ops_per_launch": mops}
+        rec["kernels"][kname] = e
+        lines.append("%-58s %8d %9.1f %8.1f %9.3f %9.3f %12.4g" % (
+            kname, tiles, e["valu_insts_per_tile"], e["mfma_insts_per_tile"], e["mfma_util"], e["valu_busy"], mops))
+    with open(os.path.join(out_dir, "sq_counters_bench_kernels.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    with open(os.path.join(out_dir, "sq_counters_bench_kernels.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def sq_counters():
+    """Counter figures for the JSON line from the committed summary, or None when it is missing
+    or was taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "sq_counters_bench_kernels.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return {k: {f: round(v[f], 4) for f in ("valu_insts_per_tile", "mfma_insts_per_tile", "mfma_util", "valu_busy")}
+            for k, v in rec["kernels"].items()}
 
 
 _BIG = {}
@@ -517,36 +611,47 @@ def dense_leg(pq, synth, torch, steps, warmup):
             "dense_dequantize_fp32_tflops": round(flops / td / 1e12, 2)}
 
 
-def grouped_leg(pq, synth, torch, reps, packed=False):
-    """Config 3: one streamed quantize pass and one dequantize pass over the 224 tensors of
-    a 32-layer 7B-style decoder (4-bit codes, d=128), each tensor one launch with its own
-    rotation signs.  Kernel time depends only on the shapes, so the seven tensors of layer
-    0 (seeded as in the parity tests) stand in for every layer; returns the pass times.
-    ``packed``: the codes bit-packed two to a byte (pq_quantize_packed / pq_dequantize_packed)."""
+def config3_weights(synth, torch, dev):
+    """The 224 distinct bf16 tensors of config 3 (32 layers x q, k, v, o, gate, up, down; 14 GB),
+    generated on the GPU from torch's seeded generator on the recipe of synth.config3_tensor:
+    N(0, 0.02^2) and 8 seeded input columns per tensor scaled by 8 (7e9 values are too many to
+    draw on the host within the benchmark's time)."""
+    gen = torch.Generator(device=dev)
+    xs = []
+    for t, _, _, rows, cols in synth.config3_layout():
+        gen.manual_seed(1000 + t)
+        x = torch.randn((rows, cols), generator=gen, device=dev, dtype=torch.float32).mul_(0.02)
+        cols_out = torch.randperm(cols, generator=gen, device=dev)[:8]
+        x[:, cols_out] *= 8.0
+        xs.append(x.to(torch.bfloat16))
+        del x
+    return xs
+
+
+def grouped_leg(pq, synth, torch, reps, packed=False, xs=None):
+    """Config 3: one streamed quantize pass and one dequantize pass over the 224 distinct tensors
+    of a 32-layer 7B-style decoder (4-bit codes, d=128), each tensor with its own rotation signs
+    (seed 42 + t), as ONE grouped launch per pass (pq_quantize_many / pq_dequantize_many over a
+    device table of the 224 tensors).  ``packed``: codes bit-packed two to a byte."""
     dev = torch.device("cuda:0")
     layout = synth.config3_layout()
     d, bits = 128, 4
     cb = d * bits // 8 if packed else d                   # code bytes per block
-    ins, outs = [], []
-    for t, _, _, rows, cols in layout[:7]:
-        xu, _ = synth.config3_tensor(t, rows, cols)
-        x = torch.from_numpy(xu.view(np.int16)).view(torch.bfloat16).to(dev)
-        n = x.numel() // d
-        ins.append(x)
-        outs.append((torch.empty((n, cb), dtype=torch.uint8, device=dev), torch.empty((n,), dtype=torch.float16, device=dev),
-                     torch.empty((n, d), dtype=torch.bfloat16, device=dev)))
+    if xs is None:
+        xs = config3_weights(synth, torch, dev)
     signs = [pq.signs_tensor(synth.BASE_SEED + t, d, dev) for t, _, _, _, _ in layout]
+    enc = [(torch.empty((x.numel() // d, cb), dtype=torch.uint8, device=dev),
+            torch.empty((x.numel() // d,), dtype=torch.float16, device=dev)) for x in xs]
+    outs = [torch.empty((x.numel() // d, d), dtype=torch.bfloat16, device=dev) for x in xs]
+    codes, norms = [c for c, _ in enc], [n for _, n in enc]
     total = sum(r * c for _, _, _, r, c in layout)
+    assert total == sum(x.numel() for x in xs)
 
     def qpass(k):
-        for t in range(len(layout)):
-            i = t % 7
-            pq.quantize(ins[i], d, bits, signs[t], out=(outs[i][0], outs[i][1], None, None), packed=packed)
+        pq.quantize_many(xs, d, bits, signs, packed=packed, outs=enc)
 
     def dpass(k):
-        for t in range(len(layout)):
-            i = t % 7
-            pq.dequantize(outs[i][0], outs[i][1], d, bits, signs[t], out=outs[i][2], packed=packed)
+        pq.dequantize_many(codes, norms, d, bits, signs, packed=packed, outs=outs)
 
     qpass(0), dpass(0)
     tq, td = timed(torch, qpass, reps), timed(torch, dpass, reps)
@@ -554,9 +659,10 @@ def grouped_leg(pq, synth, torch, reps, packed=False):
     code_bytes = nb * cb
     q_bytes = total * 2 + code_bytes + nb * 2
     d_bytes = code_bytes + nb * 2 + total * 2
+    del outs, enc
     key = "grouped_packed" if packed else "grouped"
-    return {key + "_config": "config3: 224 bf16 tensors (32 layers x q,k,v,o,gate,up,down), 6,979,321,856 "
-                             "values, d=128, 4-bit%s, one launch per tensor" % (
+    return {key + "_config": "config3: 224 distinct bf16 tensors (32 layers x q,k,v,o,gate,up,down), "
+                             "6,979,321,856 values, d=128, 4-bit%s, one grouped launch per pass" % (
                                  ", codes packed two per byte" if packed else ""),
             key + "_quantize_ms": round(tq * 1e3, 3), key + "_quantize_hbm_frac": round(q_bytes / tq / 1e9 / HBM_PEAK_GBS, 4),
             key + "_dequantize_ms": round(td * 1e3, 3), key + "_dequantize_hbm_frac": round(d_bytes / td / 1e9 / HBM_PEAK_GBS, 4),
@@ -675,6 +781,7 @@ def main():
                      "kernel": "pq_quantize_kernel<128, bf16, qjl>",
                      "algorithmic_bytes_per_launch": q_bytes},
         "kernel_source": kernel_source_hash(),
+        "counters": sq_counters(),
     }
     if not args.no_qjl:
         rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
@@ -687,8 +794,10 @@ def main():
     if not args.no_attn:
         rec["parts"].update(attn_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
     if not args.no_grouped:
-        rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50)))
-        rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50), packed=True))
+        w3 = config3_weights(synth, torch, dev)
+        rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50), xs=w3))
+        rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50), packed=True, xs=w3))
+        del w3
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_blocks)
     print(json.dumps(rec), flush=True)

@@ -187,6 +187,39 @@ int pq_dequantize_packed(int d, int bits, const uint8_t* codes, const uint16_t* 
                          const uint8_t* signs, int out_dtype, void* out, void* stream);
 
 /*
+ * Grouped codec: many tensors of one codec quantized (or dequantized) in one launch, a whole
+ * weight set streamed in one pass (eliza quantization README, PolarQuant, "Algorithm in one
+ * paragraph": the procedure runs over every linear weight tensor of the model).  Each tensor is
+ * one pq_tensor record of a table in DEVICE memory (caller-owned, read by the kernels, not by
+ * the host); the tiles of all tensors are split over the grid in table order.
+ *   x          quantize input: n_blocks*d values of in_dtype (16-byte aligned)
+ *   codes      n_blocks*d bytes, or n_blocks*d*bits/8 bit-packed (packed = 1), 16-byte aligned:
+ *              written by pq_quantize_many, read by pq_dequantize_many
+ *   norms      n_blocks fp16 (2-byte aligned): written / read likewise
+ *   signs      d/8-byte rotation sign mask of this tensor (device), 4-byte aligned
+ *   out        dequantize output: n_blocks*d values of out_dtype (16-byte aligned); unused by
+ *              pq_quantize_many (may be NULL)
+ *   n_blocks   blocks of this tensor, >= 0 (a zero-block tensor is skipped)
+ * The result equals one pq_quantize / pq_dequantize (or their packed forms) per tensor, with
+ * no QJL stage.  The host validates d, bits, the dtype, packed, n_tensors and the table
+ * pointer (8-byte aligned); the records themselves live in device memory and are not
+ * checked: each must meet the conditions above, as for the single-tensor calls.
+ */
+typedef struct {
+  const void* x;
+  uint8_t* codes;
+  uint16_t* norms;
+  const uint8_t* signs;
+  void* out;
+  int64_t n_blocks;
+} pq_tensor;
+
+int pq_quantize_many(int d, int bits, int in_dtype, int packed, int n_tensors, const pq_tensor* table,
+                     void* stream);
+int pq_dequantize_many(int d, int bits, int out_dtype, int packed, int n_tensors, const pq_tensor* table,
+                       void* stream);
+
+/*
  * QJL key sketch (eliza quantization README, QJL, "Algorithm in one paragraph").
  *   keys       n_keys*d bf16, key t at keys + t*d
  *   proj       G, m x d bf16

@@ -48,6 +48,8 @@ def _load():
         "pq_quantize": ([I, I, I, P, L, P, I, P, P, P, P, P, P], I),
         "pq_dequantize": ([I, I, P, P, L, P, I, P, P], I),
         "pq_quantize_packed": ([I, I, I, P, L, P, I, P, P, P, P, P, P], I),
+        "pq_quantize_many": ([I, I, I, I, I, P, P], I),
+        "pq_dequantize_many": ([I, I, I, I, I, P, P], I),
         "pq_dequantize_packed": ([I, I, P, P, L, P, I, P, P], I),
         "qjl_sketch": ([I, I, P, L, P, P, P, P], I),
         "qjl_project": ([I, I, P, L, P, P, P], I),
@@ -80,7 +82,7 @@ def _load():
 
 _lib = _load()
 EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", "pq_make_signs",
-           "qjl_make_projection", "pq_quantize",
+           "qjl_make_projection", "pq_quantize", "pq_quantize_many", "pq_dequantize_many",
            "pq_dequantize", "pq_quantize_packed", "pq_dequantize_packed", "qjl_sketch", "qjl_project",
            "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
            "pq_query_prep", "pq_score", "pq_score_packed", "pq_attention_work_bytes", "pq_attention",
@@ -224,6 +226,78 @@ def dequantize(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, out=None,
     fn, name = (_lib.pq_dequantize_packed, "pq_dequantize_packed") if packed else (_lib.pq_dequantize, "pq_dequantize")
     _check(fn(d, bits, _ptr(codes), _ptr(norms), n, _ptr(signs), dt, _ptr(out), _stream()), name)
     return out
+
+
+def _tensor_table(rows, device):
+    """Device table of pq_tensor records (x, codes, norms, signs, out, n_blocks), 48 bytes each."""
+    tab = np.zeros((len(rows), 6), dtype=np.int64)
+    for i, (x, codes, norms, signs, out, n) in enumerate(rows):
+        tab[i] = [t.data_ptr() if t is not None else 0 for t in (x, codes, norms, signs, out)] + [n]
+    return torch.from_numpy(tab).to(device)
+
+
+def quantize_many(xs, d, bits, signs, packed=False, outs=None):
+    """Quantize many tensors (same codec, no QJL stage) in one launch (pq_quantize_many).
+
+    xs: list of fp32 or bf16 device tensors (one dtype), each of numel a multiple of d;
+    signs: list of uint8 [d/8] sign masks, one per tensor.  Returns [(codes, norms)], codes
+    uint8 [n, d] (or [n, d * bits / 8] with ``packed``), norms fp16 [n]; ``outs`` may hold them
+    preallocated."""
+    if len(xs) != len(signs) or (outs is not None and len(outs) != len(xs)):
+        raise ValueError("one sign mask (and output pair) per tensor")
+    if not xs:
+        return []
+    dev, dt = xs[0].device, xs[0].dtype
+    cb = d * bits // 8 if packed else d
+    rows, res = [], []
+    for i, x in enumerate(xs):
+        _dev(x, "xs[%d]" % i, (dt,), device=dev)
+        if dt not in (torch.float32, torch.bfloat16):
+            raise TypeError("xs must be fp32 or bf16")
+        if d <= 0 or x.numel() % d:
+            raise ValueError("xs[%d].numel() must be a multiple of d" % i)
+        n = x.numel() // d
+        _dev(signs[i], "signs[%d]" % i, (torch.uint8,), numel=d // 8, device=dev)
+        if outs is None:
+            codes = torch.empty((n, cb), dtype=torch.uint8, device=dev)
+            norms = torch.empty((n,), dtype=torch.float16, device=dev)
+        else:
+            codes, norms = outs[i]
+        _dev(codes, "codes[%d]" % i, (torch.uint8,), numel=n * cb, device=dev)
+        _dev(norms, "norms[%d]" % i, (torch.float16,), numel=n, device=dev)
+        rows.append((x, codes, norms, signs[i], None, n))
+        res.append((codes, norms))
+    tab = _tensor_table(rows, dev)
+    _check(_lib.pq_quantize_many(d, bits, PQ_BF16 if dt == torch.bfloat16 else PQ_F32, 1 if packed else 0, len(xs),
+                                 _ptr(tab), _stream()), "pq_quantize_many")
+    return res
+
+
+def dequantize_many(codes, norms, d, bits, signs, out_dtype=torch.bfloat16, packed=False, outs=None):
+    """Dequantize many tensors in one launch (pq_dequantize_many): lists of codes, norms and sign
+    masks, one entry per tensor; returns a list of [n, d] tensors of out_dtype (or fills ``outs``)."""
+    if not (len(codes) == len(norms) == len(signs)) or (outs is not None and len(outs) != len(codes)):
+        raise ValueError("one codes, norms and sign mask (and output) per tensor")
+    if not codes:
+        return []
+    dev = norms[0].device
+    cb = d * bits // 8 if packed else d
+    rows, res = [], []
+    for i in range(len(codes)):
+        _dev(norms[i], "norms[%d]" % i, (torch.float16,), device=dev)
+        n = norms[i].numel()
+        _dev(codes[i], "codes[%d]" % i, (torch.uint8,), numel=n * cb, device=dev)
+        _dev(signs[i], "signs[%d]" % i, (torch.uint8,), numel=d // 8, device=dev)
+        out = torch.empty((n, d), dtype=out_dtype, device=dev) if outs is None else outs[i]
+        _dev(out, "out[%d]" % i, (out_dtype,), numel=n * d, device=dev)
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out_dtype must be fp32 or bf16")
+        rows.append((None, codes[i], norms[i], signs[i], out, n))
+        res.append(out)
+    tab = _tensor_table(rows, dev)
+    _check(_lib.pq_dequantize_many(d, bits, PQ_BF16 if out_dtype == torch.bfloat16 else PQ_F32, 1 if packed else 0,
+                                   len(codes), _ptr(tab), _stream()), "pq_dequantize_many")
+    return res
 
 
 def qjl_sketch(keys, proj, out=None, split=None):

@@ -25,8 +25,8 @@ COMMON_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
-# compile units, built in parallel: the kernel file in five parts (see PQ_UNIT in it) and the C ABI
-UNITS = [("pq_kernels.hip", ["-DPQ_UNIT=%d" % u], "kernels_%d.o" % u) for u in range(5)] + [("pq_api.cpp", [], "api.o")]
+# compile units, built in parallel: the kernel file in six parts (see PQ_UNIT in it) and the C ABI
+UNITS = [("pq_kernels.hip", ["-DPQ_UNIT=%d" % u], "kernels_%d.o" % u) for u in range(6)] + [("pq_api.cpp", [], "api.o")]
 NOISE = "is not a recognized feature for this target"
 
 

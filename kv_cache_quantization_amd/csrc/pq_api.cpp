@@ -112,7 +112,18 @@ const Codebook& codebook(int bits) {
 }
 
 // fp32 tables and search-grid geometry for the kernels
-pqi::CodecTables make_tables(int bits) {
+pqi::CodecTables build_tables(int bits);
+
+std::once_flag g_tab_once[pqi::kMaxBits + 1];
+pqi::CodecTables g_tab[pqi::kMaxBits + 1];
+
+// built once per bit width (the codebook and grid never change)
+const pqi::CodecTables& make_tables(int bits) {
+  std::call_once(g_tab_once[bits], [bits] { g_tab[bits] = build_tables(bits); });
+  return g_tab[bits];
+}
+
+pqi::CodecTables build_tables(int bits) {
   const Codebook& cb = codebook(bits);
   pqi::CodecTables t;
   std::memset(&t, 0, sizeof(t));
@@ -152,14 +163,33 @@ pqi::CodecTables make_tables(int bits) {
   return t;
 }
 
+// CU count and LDS limit of the current device, read once per device
+constexpr int kCfgDevices = 64;
+std::mutex g_cfg_mu;
+pqi::LaunchCfg g_cfg[kCfgDevices];
+bool g_cfg_ok[kCfgDevices] = {};
+
 int launch_cfg(pqi::LaunchCfg* c) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e);
+  const bool cached = dev >= 0 && dev < kCfgDevices;
+  if (cached) {
+    std::lock_guard<std::mutex> lock(g_cfg_mu);
+    if (g_cfg_ok[dev]) {
+      *c = g_cfg[dev];
+      return PQ_OK;
+    }
+  }
   e = hipDeviceGetAttribute(&c->cu_count, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_status(e);
   e = hipDeviceGetAttribute(&c->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return hip_status(e);
+  if (cached) {
+    std::lock_guard<std::mutex> lock(g_cfg_mu);
+    g_cfg[dev] = *c;
+    g_cfg_ok[dev] = true;
+  }
   return PQ_OK;
 }
 
@@ -452,6 +482,43 @@ int pq_dequantize_packed(int d, int bits, const uint8_t* codes, const uint16_t* 
                          const uint8_t* signs, int out_dtype, void* out, void* stream) {
   if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
   return dequantize_impl(d, bits, codes, norms, n_blocks, signs, out_dtype, out, bits == 8 ? 0 : bits, stream);
+}
+
+int pq_quantize_many(int d, int bits, int in_dtype, int packed, int n_tensors, const pq_tensor* table, void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (in_dtype != PQ_F32 && in_dtype != PQ_BF16) return PQ_EINVAL;
+  if (packed != 0 && packed != 1) return PQ_EINVAL;
+  if (n_tensors < 0) return PQ_EINVAL;
+  if (n_tensors == 0) return PQ_OK;
+  if (!table || !aligned(table, 8)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.pbits = packed && bits < 8 ? bits : 0;                         // 8 bits packed is the byte layout
+  a.t = make_tables(bits);
+  return hip_status(pqi::launch_quantize_many(d, in_dtype == PQ_BF16, a, table, n_tensors, cfg, (hipStream_t)stream));
+}
+
+int pq_dequantize_many(int d, int bits, int out_dtype, int packed, int n_tensors, const pq_tensor* table,
+                       void* stream) {
+  int st = check_d(d);
+  if (st) return st;
+  if (bits < 1 || bits > pqi::kMaxBits) return PQ_EINVAL;
+  if (out_dtype != PQ_F32 && out_dtype != PQ_BF16) return PQ_EINVAL;
+  if (packed != 0 && packed != 1) return PQ_EINVAL;
+  if (n_tensors < 0) return PQ_EINVAL;
+  if (n_tensors == 0) return PQ_OK;
+  if (!table || !aligned(table, 8)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  if ((st = launch_cfg(&cfg))) return st;
+  pqi::DequantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.pbits = packed && bits < 8 ? bits : 0;                         // 8 bits packed is the byte layout
+  a.t = make_tables(bits);
+  return hip_status(pqi::launch_dequantize_many(d, out_dtype == PQ_BF16, a, table, n_tensors, cfg, (hipStream_t)stream));
 }
 
 int qjl_sketch(int d, int m, const uint16_t* keys, int64_t n_keys, const uint16_t* proj, uint8_t* bits,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pq.h"
+
 namespace pqi {
 
 constexpr int kMaxBits = 8;
@@ -242,6 +244,9 @@ struct BdArgs {
   float beta[(1 << kMaxBits) - 1];   // boundaries, ascending
 };
 
+// one tensor of a grouped call (the public pq_tensor record, in device memory)
+using TensorDesc = ::pq_tensor;
+
 struct LaunchCfg {
   int cu_count;
   int max_lds;       // bytes of LDS one workgroup may use
@@ -259,6 +264,10 @@ hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s);
 hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_attention(int d, int bits, const AttnArgs& a, hipStream_t s);
 hipError_t launch_quantize_bd(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_quantize_many(int d, bool in_bf16, const QuantArgs& a, const TensorDesc* tab, int n_tensors,
+                                const LaunchCfg& c, hipStream_t s);
+hipError_t launch_dequantize_many(int d, bool out_bf16, const DequantArgs& a, const TensorDesc* tab, int n_tensors,
+                                  const LaunchCfg& c, hipStream_t s);
 hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_dequantize_dense(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);

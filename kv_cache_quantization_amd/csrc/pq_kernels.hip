@@ -27,6 +27,9 @@ constexpr int kWaves = kThreads / 64;
 #ifndef PQ_QUANT_WAVES_PER_EU
 #define PQ_QUANT_WAVES_PER_EU 1
 #endif
+#ifndef PQ_LOOKUP_BATCH
+#define PQ_LOOKUP_BATCH 8        // grid lookups of the code decision in flight at once
+#endif
 #ifndef PQ_SKETCH_WG_PER_CU
 #define PQ_SKETCH_WG_PER_CU 2
 #endif
@@ -259,6 +262,19 @@ __device__ __forceinline__ uint32_t split_lo_f16x2(uint32_t hp, float x0, float 
   return lo;
 }
 
+// A d/8-byte sign mask read as D/32 dwords (the grouped calls require 4-byte aligned masks), and
+// byte i of it.
+template <int D>
+struct SignWords {
+  uint32_t w[D / 32];
+  __device__ __forceinline__ void load(const uint8_t* signs) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) w[i] = reinterpret_cast<const uint32_t*>(signs)[i];
+  }
+  // byte 4 dw + g (dw a compile-time index, g = 0..3 the lane quarter)
+  __device__ __forceinline__ uint32_t byte(int dw, int g) const { return (w[dw] >> (8 * g)) & 0xffu; }
+};
+
 // Bit-packed code runs: a lane's run of codes is a little-endian bit stream of B bits per
 // code.  NB bytes of it move as the widest accesses the run's alignment allows (a run starts
 // at a multiple of NB bytes).
@@ -315,7 +331,9 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[N], int j) {
 
 // MODE: 0 = search grid stored once, 1 = replicated per lane of a 16-lane LDS group,
 // 2 = codes bit-packed, the grid's replication read from the tables at run time
-template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE>
+// RB: the QJL projection runs in the rotated basis, p = G r = (G D H) rho / d, from rows of
+// G D H staged in LDS as fp16 high and low fragments (no inverse transform of the residual)
+template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE, bool RB = false>
 struct Quantizer {
   static constexpr bool REP = MODE == 1;
   static constexpr bool PK = MODE == 2;
@@ -327,14 +345,55 @@ struct Quantizer {
   const pqi::QuantArgs& a;
   const unsigned char* smem;
   const uint4* gl;
-  // rotation signs of this lane's element pairs: per pair, bf16 +-1.0 pairs (bf16 input) or
-  // sign-bit masks (fp32 input); for d = 512 only the sign bytes (elements 32 s + 8 g .. +7)
-  // are held and the pair values are formed when used, which keeps 48 registers free
+  // rotation signs of this lane's element pairs: per pair, the sign bits of its two elements
+  // (bits 15 and 31: ORed with a bf16 scale in both halves they make the +-rscale pair of the
+  // first butterfly; for fp32 input they flip the values directly); for d = 512 only the sign
+  // bytes (elements 32 s + 8 g .. +7) are held and the pairs are formed when used, which keeps
+  // 48 registers free
   static constexpr bool kCompactSigns = D == 512;
   uint32_t smask[kCompactSigns ? D / 32 : E / 2];
   int lane, r, g, m, m_pad, mb;
   float inv_w, offM, topM, inv_sqrt_d;
   uint32_t lane_off, rep_shift;
+  // the tensor being quantized: codes and norms out, its block count (retarget() switches)
+  uint8_t* codes;
+  uint16_t* norms;
+  int64_t n_blocks;
+
+  // pair p holds elements load_e(g, 2p) and +1: bits 2 (p & 3) and 2 (p & 3) + 1 of sign
+  // byte 4 (p >> 2) + g
+  __device__ __forceinline__ void load_signs(const uint8_t* signs) {
+    if constexpr (kCompactSigns) {
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) smask[s] = signs[4 * s + g];
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const uint32_t b = signs[4 * s + g];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) smask[4 * s + t] = (((b >> (2 * t)) & 1u) << 15) | (((b >> (2 * t + 1)) & 1u) << 31);
+      }
+    }
+  }
+
+  // another tensor of the same codec (grouped calls): its signs (loaded ahead), outputs and
+  // block count
+  __device__ __forceinline__ void retarget(const SignWords<D>& sw, uint8_t* c, uint16_t* nm, int64_t nb) {
+    if constexpr (kCompactSigns) {
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) smask[s] = sw.byte(s, g);
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const uint32_t b = sw.byte(s, g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) smask[4 * s + t] = (((b >> (2 * t)) & 1u) << 15) | (((b >> (2 * t + 1)) & 1u) << 31);
+      }
+    }
+    codes = c;
+    norms = nm;
+    n_blocks = nb;
+  }
 
   __device__ Quantizer(const pqi::QuantArgs& args, const unsigned char* sm, const uint4* g_lds)
       : a(args), smem(sm), gl(g_lds) {
@@ -344,18 +403,10 @@ struct Quantizer {
     m = a.m;
     m_pad = (m + 15) & ~15;
     mb = m >> 3;
-    if constexpr (kCompactSigns) {
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) smask[s] = a.signs[4 * s + g];
-    } else {
-#pragma unroll
-      for (int p = 0; p < E / 2; ++p) {
-        const int e = load_e(g, 2 * p);
-        const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
-        const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
-        smask[p] = (s0 << 15) | (s1 << 31) | (IN_BF16 ? 0x3F803F80u : 0u);
-      }
-    }
+    codes = a.codes;
+    norms = a.norms;
+    n_blocks = a.n_blocks;
+    if (a.signs) load_signs(a.signs);
     inv_w = a.t.cell_inv_w;
     offM = (float)a.t.half + kMagic;
     topM = kMagic + (float)(a.t.ncell - 1);
@@ -372,20 +423,22 @@ struct Quantizer {
   __device__ __forceinline__ uint32_t sgn(int p) const {
     if constexpr (kCompactSigns) {
       const uint32_t b = (smask[p >> 2] >> (2 * (p & 3))) & 3u;
-      return ((b & 1u) << 15) | ((b & 2u) << 30) | (IN_BF16 ? 0x3F803F80u : 0u);
+      return ((b & 1u) << 15) | ((b & 2u) << 30);
     } else {
       return smask[p];
     }
   }
 
   __device__ __forceinline__ void decide(const uint4 (&raw)[NR], int64_t T, float (&v)[E]) {
-    const int64_t n_blocks = a.n_blocks;
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
+    // The block norm comes first, from the raw values, so that the rotation can run on x scaled
+    // by rscale = 2^e (a power of two that brings n into [1, 2)): for bf16 input the scale rides
+    // on the +-1 sign pairs of the first butterfly (exact products), so z' = rscale H (D x)
+    // needs no per-element rescale, and the residual z' - rscale n16 c sits near 1 for the
+    // fp16 split of the QJL stage.
     float ss;
     if constexpr (IN_BF16) {
-      // signs, bf16 -> fp32 and the first butterfly (register bit 0 pairs the two halves of
-      // a word) in two exact dot products per pair: (x0 D0 + x1 D1, x0 D0 - x1 D1)
       typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
       float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -393,16 +446,49 @@ struct Quantizer {
         const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int p = 4 * s + u;
           const bf16x2 x = __builtin_bit_cast(bf16x2, w[u]);
-          const uint32_t sp = sgn(p);
-          v[2 * p] = dot2_bf16(w[u], sp);
-          v[2 * p + 1] = dot2_bf16(w[u], sp ^ 0x80000000u);
           sq[u] = __builtin_amdgcn_fdot2_f32_bf16(x, x, sq[u], false);
         }
       }
       ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-      wht_forward<D, false>(v);            // v = z = H (D x), unnormalised
+    } else {
+      float sq[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sq[i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        const uint32_t f[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sq[(4 * s + t) & 7] = fmaf(__uint_as_float(f[t]), __uint_as_float(f[t]), sq[(4 * s + t) & 7]);
+      }
+      ss = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+    }
+    ss = sum4(ss);
+    const float n = sqrtf(ss);
+    const uint16_t n16 = f32_to_f16(n);
+    // e in [-126, 126]: blocks with a norm below 2^-126 keep the largest scale that stays finite
+    const int e = n > 0.0f ? min(max(-ilogbf(n), -126), 126) : 0;
+    const float rscale = __uint_as_float((uint32_t)(127 + e) << 23);
+    const float nr = n * rscale;                                  // the norm on the scaled axis
+    const float nsc = f16_to_f32(n16) * rscale;                   // the stored norm, scaled
+    const float a_w = nr > 0.0f ? inv_w / nr : 0.0f;              // scaled coordinate -> grid cells
+
+    if constexpr (IN_BF16) {
+      // signs, bf16 -> fp32, the scale and the first butterfly (register bit 0 pairs the two
+      // halves of a word) in two dot products per pair: (x0 D0 + x1 D1, x0 D0 - x1 D1) rscale
+      const uint32_t scw = ((uint32_t)(127 + e) << 7) * 0x10001u;   // bf16 rscale in both halves
+#pragma unroll
+      for (int s = 0; s < NR; ++s) {
+        const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int p = 4 * s + u;
+          const uint32_t sp = sgn(p) | scw;
+          v[2 * p] = dot2_bf16(w[u], sp);
+          v[2 * p + 1] = dot2_bf16(w[u], sp ^ 0x80000000u);
+        }
+      }
+      wht_forward<D, false>(v);            // v = z' = rscale H (D x)
     } else {
 #pragma unroll
       for (int s = 0; s < NR / 2; ++s) {
@@ -412,53 +498,42 @@ struct Quantizer {
         for (int t = 0; t < 8; ++t) {
           const uint32_t sp = sgn(4 * s + t / 2);
           const uint32_t sm = (t & 1) ? (sp & 0x80000000u) : (sp << 16);
-          v[8 * s + t] = __uint_as_float(f[t] ^ sm);
+          v[8 * s + t] = __uint_as_float(f[t] ^ sm) * rscale;
         }
       }
-      ss = tree_sumsq<E>(v);
-      wht_forward<D>(v);                   // v = z = H (D x), unnormalised
+      wht_forward<D>(v);                   // v = z' = rscale H (D x)
     }
 
-    ss = sum4(ss);
-    const float n = sqrtf(ss);
-    const uint16_t n16 = f32_to_f16(n);
-    const float inv_n = n > 0.0f ? 1.0f / n : 0.0f;
-    // residual rho = z - n16 c[code] (= H D r) formed with one rounding and rescaled by a
-    // power of two so that it sits near 1 for the fp16 split
-    float rscale = 1.0f, nsc = 0.0f;
-    if constexpr (QJL) {
-      if (n > 0.0f) {
-        rscale = ldexpf(1.0f, -ilogbf(n));
-        nsc = f16_to_f32(n16) * rscale;
-      }
-    }
-
+    // code: y = z' / nr lies above boundary beta exactly when z' - beta nr > 0 (one fma, one
+    // rounding); the grid cell comes from z' a_w; with the QJL stage the scaled residual
+    // rho = z' - rscale n16 c[code] (= rscale H D r) replaces z' in v
     uint32_t cw[E / 4];
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) cw[w] = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const float y = v[j] * inv_n;
-      const float u = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
+      const float u = __builtin_amdgcn_fmed3f(fmaf(v[j], a_w, offM), kMagic, topM);
       const uint32_t addr = (__float_as_uint(u) << (PK ? rep_shift : kRepShift)) + lane_off;
       uint32_t code;
       if constexpr (QJL) {
         u32x4 te = *static_cast<const u32x4*>(__builtin_assume_aligned(smem + addr, 16));
         asm("" : "+v"(te));                // keep the cell as one 16-byte LDS read
-        const bool gt = y > __uint_as_float(te.x);
+        const bool gt = fmaf(-__uint_as_float(te.x), nr, v[j]) > 0.0f;
         code = te.y + (gt ? 1u : 0u);
         const float c = __uint_as_float(gt ? te.w : te.z);
-        v[j] = fmaf(-nsc, c, v[j] * rscale);
+        v[j] = fmaf(-nsc, c, v[j]);
         asm volatile("" : "+v"(v[j]));     // keep the residual next to its lookup
       } else {
         u32x2 te = *static_cast<const u32x2*>(__builtin_assume_aligned(smem + addr, 8));
         asm("" : "+v"(te));
-        code = te.y + (y > __uint_as_float(te.x) ? 1u : 0u);
+        code = te.y + (fmaf(-__uint_as_float(te.x), nr, v[j]) > 0.0f ? 1u : 0u);
       }
       const int o = cperm<D>(j);
       cw[o >> 2] |= code << (8 * (o & 3));
       // at most 8 grid lookups in flight: bounds the registers the scheduler may tie up
-      if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      // (twice as many without the QJL stage, whose lookups hold fewer registers)
+      constexpr int LB = QJL ? PQ_LOOKUP_BATCH : 2 * PQ_LOOKUP_BATCH;
+      if ((j % LB) == LB - 1) __builtin_amdgcn_sched_barrier(0);
     }
     // materialise the packed codes here: otherwise the whole decision chain sinks into
     // the store branch below and keeps every lookup result live until then
@@ -475,7 +550,7 @@ struct Quantizer {
         case 6: store_packed<6>(cw, blk, valid); break;
         default: store_packed<7>(cw, blk, valid); break;
       }
-      if (valid && g == 0) a.norms[blk] = n16;
+      if (valid && g == 0) norms[blk] = n16;
     } else if constexpr (D == 128) {
       // a block's codes are one 128-byte line, two 16-byte pieces per lane: the neighbouring
       // blocks r & ~1 and r | 1 (lanes l, l ^ 1) trade pieces so that each store writes
@@ -489,16 +564,16 @@ struct Quantizer {
         x[i] = odd ? recv : cw[i];
         y[i] = odd ? cw[4 + i] : recv;
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(a.codes + blk_e * D + E * qpos<D>(g) + (odd ? 16 : 0));
+      u32x4* dst = reinterpret_cast<u32x4*>(codes + blk_e * D + E * qpos<D>(g) + (odd ? 16 : 0));
       if (blk_e < n_blocks) dst[0] = x;
       if (blk_e + 1 < n_blocks) dst[D / 16] = y;
-      if (valid && g == 0) a.norms[blk] = n16;
+      if (valid && g == 0) norms[blk] = n16;
     } else if (valid) {
-      uint4* dst = reinterpret_cast<uint4*>(a.codes + blk * D + E * qpos<D>(g));
+      uint4* dst = reinterpret_cast<uint4*>(codes + blk * D + E * qpos<D>(g));
 #pragma unroll
       for (int w = 0; w < E / 16; ++w)
         dst[w] = make_uint4(cw[4 * w + 0], cw[4 * w + 1], cw[4 * w + 2], cw[4 * w + 3]);
-      if (g == 0) a.norms[blk] = n16;
+      if (g == 0) norms[blk] = n16;
     }
 
     if constexpr (QJL) {
@@ -523,7 +598,7 @@ struct Quantizer {
       pw[k] |= c << sh;
       if (sh + B > 32) pw[k + 1] |= c >> (32 - sh);
     }
-    if (valid) store_code_bytes<NB>(a.codes + blk * (D * B / 8) + E * qpos<D>(g) * B / 8, pw);
+    if (valid) store_code_bytes<NB>(codes + blk * (D * B / 8) + E * qpos<D>(g) * B / 8, pw);
   }
 
   // The rotated residual back in the block's coordinates, w = H rho = d D r (times the
@@ -545,6 +620,81 @@ struct Quantizer {
         ahi[k][t] = hp;
         alo[k][t] = split_lo_f16x2(hp, x0, x1);
       }
+    }
+  }
+
+  // The scaled rotated residual (registers in run order) split into fp16 high and low parts
+  // (22 significant bits) as MFMA B fragments: K step k takes registers 8 k .. 8 k + 7.
+  __device__ __forceinline__ void rotated_frags(const float (&v)[E], u32x4 (&bhi)[KS], u32x4 (&blo)[KS]) const {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float x0 = v[8 * k + 2 * t], x1 = v[8 * k + 2 * t + 1];
+        const uint32_t hp = split_hi_f16x2(x0, x1);
+        bhi[k][t] = hp;
+        blo[k][t] = split_lo_f16x2(hp, x0, x1);
+      }
+    }
+  }
+
+  // Rows of G D H into LDS for the rotated-basis projection: row i of G D H is H (D g_i), the
+  // transform decide() applies to a block, so a wave takes 16 rows of G at a time as a tile of
+  // blocks (rows >= m are zero), applies the signs and the forward transform (no scale), and
+  // stores register chunk k of each lane as fragment (row tile, k, lane), high parts first, then
+  // the low parts: the same element order as the residual fragments.
+  __device__ void stage_rotated(uint4* gp, int wv, int waves) const {
+    const int nt = m_pad >> 4;
+    uint4* glo = gp + (size_t)nt * KS * 64;
+    for (int rt = wv; rt < nt; rt += waves) {
+      uint4 raw[D / 32];
+      load_tile<D, true>(raw, a.proj, rt, m, m >> 4, r, g);
+      float v[E];
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int p = 4 * s + u;
+          const uint32_t sp = sgn(p) | 0x3F803F80u;           // +-1.0 pairs
+          v[2 * p] = dot2_bf16(w[u], sp);
+          v[2 * p + 1] = dot2_bf16(w[u], sp ^ 0x80000000u);
+        }
+      }
+      wht_forward<D, false>(v);
+      u32x4 hi[KS], lo[KS];
+      rotated_frags(v, hi, lo);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        gp[((size_t)rt * KS + k) * 64 + lane] = make_uint4(hi[k][0], hi[k][1], hi[k][2], hi[k][3]);
+        glo[((size_t)rt * KS + k) * 64 + lane] = make_uint4(lo[k][0], lo[k][1], lo[k][2], lo[k][3]);
+      }
+    }
+  }
+
+  // Sign bits of G r from the scaled rotated residual: three products per K step (high x high,
+  // high x low, low x high) against the staged rows of G D H; the positive factors rscale / d
+  // do not change a sign.  Output layout as in project().
+  __device__ __forceinline__ void project_rotated(const u32x4 (&bhi)[KS], const u32x4 (&blo)[KS], int64_t T) {
+    const int nt = m_pad >> 4;
+    const uint4* glo = gl + (size_t)nt * KS * 64;
+    for (int nt0 = 0; nt0 < nt; nt0 += 4) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (nt0 + q < nt) {
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
+            const f16x8 ah = __builtin_bit_cast(f16x8, gl[((size_t)(nt0 + q) * KS + k) * 64 + lane]);
+            const f16x8 al = __builtin_bit_cast(f16x8, glo[((size_t)(nt0 + q) * KS + k) * 64 + lane]);
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(f16x8, bhi[k]), acc[q], 0, 0, 0);
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(f16x8, blo[k]), acc[q], 0, 0, 0);
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(f16x8, bhi[k]), acc[q], 0, 0, 0);
+          }
+        }
+      }
+      store_sign_bytes(sign_bytes4(acc), lane, T * 16, n_blocks, a.qbits, mb, nt0);
     }
   }
 
@@ -580,14 +730,18 @@ struct Quantizer {
           }
         }
       }
-      store_sign_bytes(sign_bytes4(acc), lane, T * 16, a.n_blocks, a.qbits, mb, nt0);
+      store_sign_bytes(sign_bytes4(acc), lane, T * 16, n_blocks, a.qbits, mb, nt0);
     }
   }
 
   __device__ __forceinline__ void tile(const uint4 (&raw)[NR], int64_t T) {
     float v[E];
     decide(raw, T, v);
-    if constexpr (QJL) {
+    if constexpr (QJL && RB) {
+      u32x4 bhi[KS], blo[KS];
+      rotated_frags(v, bhi, blo);
+      project_rotated(bhi, blo, T);
+    } else if constexpr (QJL) {
       u32x4 ahi[KS], alo[KS];
       residual_frags(v, ahi, alo);
       project<G_LDS>(ahi, alo, T, gl, 0, 0, m_pad >> 4);
@@ -604,29 +758,47 @@ __device__ void stage_projection_rows(const uint16_t* proj, const uint8_t* signs
 }
 
 // THREADS = 512 when G takes most of the LDS: one workgroup per CU then still runs two waves
-// per SIMD.
-template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE, int THREADS = kThreads>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU)))
+// per SIMD.  RB (rotated-basis projection, G D H in LDS): sixteen-wave workgroups, one per CU
+// (four waves per SIMD), so the grid and G D H are built once per CU.
+template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE, int THREADS = kThreads, bool RB = false>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(RB ? THREADS / 256 : (THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU))))
 void pq_quantize_kernel(const pqi::QuantArgs a) {
-  using Q = Quantizer<D, IN_BF16, QJL, G_LDS, MODE>;
+  using Q = Quantizer<D, IN_BF16, QJL, G_LDS, MODE, RB>;
   constexpr int WAVES = THREADS / 64;
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* tab = reinterpret_cast<uint4*>(smem);
   uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
   build_search_grid(a.t, tab);
-  if constexpr (QJL && G_LDS) stage_projection_rows<D>(a.proj, a.signs, a.m, 0, (a.m + 15) & ~15, gl);
+  Q q(a, smem, gl);
+  if constexpr (QJL && RB) q.stage_rotated(gl, threadIdx.x >> 6, WAVES);
+  else if constexpr (QJL && G_LDS) stage_projection_rows<D>(a.proj, a.signs, a.m, 0, (a.m + 15) & ~15, gl);
   __syncthreads();
 
-  Q q(a, smem, gl);
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
   const int64_t full_tiles = a.n_blocks >> 4;
   const int64_t n_waves = (int64_t)gridDim.x * WAVES;
   int64_t T = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-  // several waves per SIMD overlap one wave's loads with another's arithmetic
   uint4 raw[Q::NR];
-  for (; T < n_tiles; T += n_waves) {
-    load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
-    q.tile(raw, T);
+  if constexpr (Q::NR <= 4) {
+    // the next tile's input is loaded before this tile is processed (16 more registers); two
+    // buffers take turns, so nothing is copied between them
+    uint4 alt[Q::NR];
+    if (T < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
+    while (T < n_tiles) {
+      if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(alt, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
+      q.tile(raw, T);
+      T += n_waves;
+      if (T >= n_tiles) break;
+      if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
+      q.tile(alt, T);
+      T += n_waves;
+    }
+  } else {
+    // several waves per SIMD overlap one wave's loads with another's arithmetic
+    for (; T < n_tiles; T += n_waves) {
+      load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
+      q.tile(raw, T);
+    }
   }
 }
 
@@ -771,51 +943,60 @@ void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
 // Dequantize.  Outputs are written with non-temporal stores: they stream to HBM without
 // displacing the codes and tables in the caches.
 // ------------------------------------------------------------------------------------------
+// One tensor's dequantize state in a wave: codes, norms and output of the tensor and the
+// output sign masks of this lane (register chunk s holds elements 8 g + dq_out_chunk(s) + 0..7).
 template <int D, bool OUT_BF16, int PB>
-__global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
-  constexpr int E = D / 4;
-  constexpr int CB = PB ? PB : 8;                     // bits per stored code (PB = 0: a byte each)
-  constexpr int NB = E * CB / 8;                      // code bytes of the lane's run
-  constexpr int NQ = (NB + 3) / 4;                    // ... as dwords
-  __shared__ float cent[1 << pqi::kMaxBits];
-  copy_centroids(a.t, cent);
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, g = lane >> 4;
-
-  // output sign masks: register chunk s holds elements 8 g + dq_out_chunk(s) + 0..7
+struct Dequantizer {
+  static constexpr int E = D / 4;
+  static constexpr int CB = PB ? PB : 8;                     // bits per stored code (PB = 0: a byte each)
+  static constexpr int NB = E * CB / 8;                      // code bytes of the lane's run
+  static constexpr int NQ = (NB + 3) / 4;                    // ... as dwords
+  const float* cent;
+  int r, g;
   uint32_t smask[E / 2];
+  const uint8_t* codes;
+  const uint16_t* norms;
+  void* out;
+  int64_t n_blocks;
+
+  __device__ __forceinline__ void retarget(const uint8_t* signs, const uint8_t* c, const uint16_t* nm, void* o,
+                                           int64_t nb) {
+    // byte loads (the mask may sit at any address): register chunk s is output elements
+    // 8 g + dq_out_chunk(s) + 0..7, sign byte g + dq_out_chunk(s) / 8
 #pragma unroll
-  for (int p = 0; p < E / 2; ++p) {
-    const int e = 8 * g + dq_out_chunk<D>(p >> 2) + 2 * (p & 3);
-    const uint32_t s0 = (a.signs[e >> 3] >> (e & 7)) & 1u;
-    const uint32_t s1 = (a.signs[(e + 1) >> 3] >> ((e + 1) & 7)) & 1u;
-    smask[p] = OUT_BF16 ? ((s0 << 15) | (s1 << 31)) : (s0 | (s1 << 1));
+    for (int s = 0; s < E / 8; ++s) set_chunk(s, signs[g + dq_out_chunk<D>(s) / 8]);
+    codes = c;
+    norms = nm;
+    out = o;
+    n_blocks = nb;
+  }
+  __device__ __forceinline__ void set_chunk(int s, uint32_t b) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t s0 = (b >> (2 * t)) & 1u, s1 = (b >> (2 * t + 1)) & 1u;
+      smask[4 * s + t] = OUT_BF16 ? ((s0 << 15) | (s1 << 31)) : (s0 | (s1 << 1));
+    }
+  }
+  __device__ __forceinline__ void retarget(const SignWords<D>& sw, const uint8_t* c, const uint16_t* nm, void* o,
+                                           int64_t nb) {
+    // register chunk s is output elements 8 g + dq_out_chunk(s) + 0..7: sign byte g + dq_out_chunk(s) / 8
+#pragma unroll
+    for (int s = 0; s < E / 8; ++s) set_chunk(s, sw.byte(dq_out_chunk<D>(s) / 32, g));
+    codes = c;
+    norms = nm;
+    out = o;
+    n_blocks = nb;
   }
 
-  const int64_t n_blocks = a.n_blocks;
-  const int64_t n_tiles = (n_blocks + 15) >> 4;
-  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
-
-  // the lane's run: codes E g .. E g + E - 1 of the block (a CB-bit stream)
-  auto load = [&](uint32_t (&q)[NQ], uint16_t& nb, int64_t T) {
+  // the lane's run: codes E g .. E g + E - 1 of block 16 T + r (a CB-bit stream)
+  __device__ __forceinline__ void load(uint32_t (&q)[NQ], uint16_t& nb, int64_t T) const {
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
-    load_code_bytes<NB>(a.codes + blk * (D * CB / 8) + E * g * CB / 8, valid, q);
-    nb = valid ? a.norms[blk] : (uint16_t)0;
-  };
+    load_code_bytes<NB>(codes + blk * (D * CB / 8) + E * g * CB / 8, valid, q);
+    nb = valid ? norms[blk] : (uint16_t)0;
+  }
 
-  int64_t T = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  uint32_t q[NQ];
-  uint16_t nb;
-  load(q, nb, T);
-
-  for (; T < n_tiles; T += n_waves) {
-    uint32_t qn[NQ];
-    uint16_t nbn;
-    load(qn, nbn, T + n_waves);
-
+  __device__ __forceinline__ void tile(const uint32_t (&q)[NQ], uint16_t nb, int64_t T) const {
     float v[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) v[j] = cent[stream_code<CB>(q, j)];
@@ -843,7 +1024,7 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
       if (ok_o) __builtin_nontemporal_store(y, reinterpret_cast<u32x4*>(row_e + D + off));
     };
     if constexpr (OUT_BF16) {
-      uint16_t* row_e = static_cast<uint16_t*>(a.out) + blk_e * D + 8 * g;
+      uint16_t* row_e = static_cast<uint16_t*>(out) + blk_e * D + 8 * g;
       auto pack = [&](int s) {
         u32x4 w;
 #pragma unroll
@@ -856,7 +1037,7 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
       for (int s = 0; s < E / 8; ++s)
         if (dq_out_chunk<D>(s) % 64 == 0) put(row_e, pack(s), pack(dq_partner<D>(s)), dq_out_chunk<D>(s), dq_out_chunk<D>(s) + 32);
     } else {
-      float* row_e = static_cast<float*>(a.out) + blk_e * D + 8 * g;
+      float* row_e = static_cast<float*>(out) + blk_e * D + 8 * g;
 #pragma unroll
       for (int s = 0; s < E / 8; ++s) {
         float f[8];
@@ -870,8 +1051,205 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
         put(row_e, pa, pb, dq_out_chunk<D>(s), dq_out_chunk<D>(s) + 4);
       }
     }
+  }
+};
+
+template <int D, bool OUT_BF16, int PB>
+__global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
+  using DQ = Dequantizer<D, OUT_BF16, PB>;
+  __shared__ float cent[1 << pqi::kMaxBits];
+  copy_centroids(a.t, cent);
+  __syncthreads();
+
+  DQ dq;
+  dq.cent = cent;
+  dq.r = threadIdx.x & 15;
+  dq.g = (threadIdx.x & 63) >> 4;
+  dq.retarget(a.signs, a.codes, a.norms, a.out, a.n_blocks);
+
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+  int64_t T = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  uint32_t q[DQ::NQ];
+  uint16_t nb;
+  dq.load(q, nb, T);
+  for (; T < n_tiles; T += n_waves) {
+    uint32_t qn[DQ::NQ];
+    uint16_t nbn;
+    dq.load(qn, nbn, T + n_waves);                   // the next tile's codes (zero past the end)
+    dq.tile(q, nb, T);
 #pragma unroll
-    for (int w = 0; w < NQ; ++w) q[w] = qn[w];
+    for (int w = 0; w < DQ::NQ; ++w) q[w] = qn[w];
+    nb = nbn;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Grouped codec over many tensors in one launch (a weight set streamed in one pass): the
+// tensors are listed in a device table and their tiles numbered in table order; wave w takes
+// the chunks of C consecutive tiles w, w + n_waves, ... and a cursor that only moves forward
+// finds each tile's tensor from the table's block counts (uniform loads).  Dequantize, bound by
+// memory, strides over the whole set in chunks of PQ_MANY_CHUNK tiles (as the single-tensor
+// kernels stride over one tensor); quantize, bound by vector issue, gives each wave one
+// contiguous range (C = total / waves), so it changes tensor at most a few times.
+// ------------------------------------------------------------------------------------------
+#ifndef PQ_MANY_CHUNK
+#define PQ_MANY_CHUNK 2
+#endif
+__device__ __forceinline__ int64_t tiles_of(int64_t n_blocks) { return (n_blocks + 15) >> 4; }
+
+struct ManyCursor {
+  const pqi::TensorDesc* tab;
+  int ti;                     // current tensor
+  int64_t base, end;          // its global tile range [base, end)
+  __device__ __forceinline__ void init(const pqi::TensorDesc* t) {
+    tab = t;
+    ti = 0;
+    base = 0;
+    end = tiles_of(tab[0].n_blocks);
+  }
+  // move to the tensor holding global tile Tg (Tg never decreases); true when it changed
+  __device__ __forceinline__ bool seek(int64_t Tg) {
+    bool moved = false;
+    while (Tg >= end) {
+      base = end;
+      ++ti;
+      end = base + tiles_of(tab[ti].n_blocks);
+      moved = true;
+    }
+    return moved;
+  }
+};
+
+__device__ __forceinline__ int64_t many_total(const pqi::TensorDesc* tab, int n_tensors) {
+  int64_t total = 0;
+  for (int i = 0; i < n_tensors; ++i) total += tiles_of(tab[i].n_blocks);
+  return total;
+}
+
+// global tile of step k of wave w: chunk w + (k / C) n_waves, tile k % C of the chunk
+__device__ __forceinline__ int64_t many_tile(int64_t w, int64_t k, int64_t n_waves, int64_t C) {
+  return (w + (k / C) * n_waves) * C + k % C;
+}
+
+// The record of the tensor a tile belongs to, read one tile ahead (with its sign words) so that
+// a change of tensor never waits on a load.
+template <int D>
+struct ManyRecord {
+  const void* x;
+  uint8_t* codes;
+  uint16_t* norms;
+  void* out;
+  int64_t n_blocks, base;
+  SignWords<D> sw;
+  __device__ __forceinline__ void read(const pqi::TensorDesc* tab, const ManyCursor& c) {
+    x = tab[c.ti].x;
+    codes = tab[c.ti].codes;
+    norms = tab[c.ti].norms;
+    out = tab[c.ti].out;
+    n_blocks = tab[c.ti].n_blocks;
+    base = c.base;
+    sw.load(tab[c.ti].signs);
+  }
+};
+
+template <int D, bool IN_BF16, int MODE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PQ_QUANT_WAVES_PER_EU)))
+void pq_quantize_many_kernel(const pqi::QuantArgs a, const pqi::TensorDesc* tab, int n_tensors) {
+  using Q = Quantizer<D, IN_BF16, false, false, MODE>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  build_search_grid(a.t, reinterpret_cast<uint4*>(smem));
+  __syncthreads();
+  Q q(a, smem, nullptr);
+  const int64_t total = many_total(tab, n_tensors);
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+  const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t C = (total + n_waves - 1) / n_waves;
+  ManyCursor cur;
+  cur.init(tab);
+  int64_t k = 0, T = many_tile(w, 0, n_waves, C);
+  if (T >= total) return;
+  cur.seek(T);
+  ManyRecord<D> rc, rn;                            // this tile's tensor, the next tile's
+  rc.read(tab, cur);
+  q.retarget(rc.sw, rc.codes, rc.norms, rc.n_blocks);
+  auto load = [&](uint4 (&raw)[Q::NR], const ManyRecord<D>& r, int64_t Tg) {
+    load_tile<D, IN_BF16>(raw, r.x, Tg - r.base, r.n_blocks, r.n_blocks >> 4, q.r, q.g);
+  };
+  uint4 raw[Q::NR], alt[Q::NR];
+  load(raw, rc, T);
+  // two buffers take turns: the next tile's input (and its tensor's record) loads while this
+  // tile is processed
+  auto step = [&](uint4 (&now)[Q::NR], uint4 (&next)[Q::NR]) {
+    const int64_t Tn = many_tile(w, k + 1, n_waves, C);
+    const bool more = Tn < total;
+    const bool moved = more && cur.seek(Tn);
+    if (moved) rn.read(tab, cur);
+    if (more) load(next, moved ? rn : rc, Tn);
+    q.tile(now, T - rc.base);
+    if (moved) {
+      rc = rn;
+      q.retarget(rc.sw, rc.codes, rc.norms, rc.n_blocks);
+    }
+    T = Tn;
+    ++k;
+    return more;
+  };
+  while (step(raw, alt) && step(alt, raw)) {
+  }
+}
+
+template <int D, bool OUT_BF16, int PB>
+__global__ __launch_bounds__(kThreads) void pq_dequantize_many_kernel(const pqi::DequantArgs a, const pqi::TensorDesc* tab,
+                                                                      int n_tensors) {
+  using DQ = Dequantizer<D, OUT_BF16, PB>;
+  __shared__ float cent[1 << pqi::kMaxBits];
+  copy_centroids(a.t, cent);
+  __syncthreads();
+  DQ dq;
+  dq.cent = cent;
+  dq.r = threadIdx.x & 15;
+  dq.g = (threadIdx.x & 63) >> 4;
+  const int64_t total = many_total(tab, n_tensors);
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+  const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  constexpr int64_t C = PQ_MANY_CHUNK;
+  ManyCursor cur;
+  cur.init(tab);
+  int64_t k = 0, T = many_tile(w, 0, n_waves, C);
+  if (T >= total) return;
+  cur.seek(T);
+  ManyRecord<D> rc, rn;
+  rc.read(tab, cur);
+  dq.retarget(rc.sw, rc.codes, rc.norms, rc.out, rc.n_blocks);
+  // the lane's codes and norm of tile Tg of the tensor of record r (zero past its end)
+  auto load = [&](uint32_t (&q)[DQ::NQ], uint16_t& nb, const ManyRecord<D>& r, int64_t Tg) {
+    const int64_t blk = (Tg - r.base) * 16 + dq.r;
+    const bool valid = blk < r.n_blocks;
+    load_code_bytes<DQ::NB>(r.codes + blk * (D * DQ::CB / 8) + DQ::E * dq.g * DQ::CB / 8, valid, q);
+    nb = valid ? r.norms[blk] : (uint16_t)0;
+  };
+  uint32_t q[DQ::NQ];
+  uint16_t nb;
+  load(q, nb, rc, T);
+  while (true) {
+    const int64_t Tn = many_tile(w, k + 1, n_waves, C);
+    const bool more = Tn < total;
+    const bool moved = more && cur.seek(Tn);
+    if (moved) rn.read(tab, cur);
+    uint32_t qn[DQ::NQ];
+    uint16_t nbn = 0;
+    if (more) load(qn, nbn, moved ? rn : rc, Tn);
+    dq.tile(q, nb, T - rc.base);
+    if (!more) break;
+    if (moved) {
+      rc = rn;
+      dq.retarget(rc.sw, rc.codes, rc.norms, rc.out, rc.n_blocks);
+    }
+    T = Tn;
+    ++k;
+#pragma unroll
+    for (int i = 0; i < DQ::NQ; ++i) q[i] = qn[i];
     nb = nbn;
   }
 }
@@ -2601,6 +2979,21 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   // workgroups per CU while it takes at most 64 KiB), else walked in chunks
   const bool g_lds = qjl && base + glb <= (size_t)c.max_lds;
   const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
+  // rotated-basis projection when G D H (fp16 high + low) fits beside the grid: one
+  // sixteen-wave workgroup per CU
+  const size_t grb = (size_t)m_pad * D * 4;
+  if (qjl && base + grb <= (size_t)c.max_lds && base + grb <= 98304) {
+    const size_t lds = base + grb;
+    const int g16 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count, (n_tiles + 15) / 16));
+#define PQ_RB_LAUNCH(MODE)                                                                                       \
+  if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, MODE, 1024, true>), g16, 1024, lds, s, a); \
+  else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, MODE, 1024, true>), g16, 1024, lds, s, a);
+    if (mode == 2) { PQ_RB_LAUNCH(2) }
+    else if (mode == 1) { PQ_RB_LAUNCH(1) }
+    else { PQ_RB_LAUNCH(0) }
+#undef PQ_RB_LAUNCH
+    return hipGetLastError();
+  }
   if (qjl && !g_lds) {
     // residual fragments of every tile of the workgroup beside the search grid
     const size_t lds = base + chunk_frag_bytes<D>();
@@ -2724,9 +3117,10 @@ hipError_t launch_attend_d(int bits, const pqi::AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// The library is compiled as five units of this file (PQ_UNIT 0 .. 4) in parallel: the
+// The library is compiled as six units of this file (PQ_UNIT 0 .. 5) in parallel: the
 // quantize kernels for d = 64, 128; those for d = 256, 512; everything else but the
-// two-stage score and the attention; the two-stage score; the fused decode attention.  Without
+// two-stage score, the attention and the grouped codec; the two-stage score; the fused decode
+// attention; the grouped (many-tensor) codec.  Without
 // PQ_UNIT one unit holds all of it.  Kernels are templates or file-local, so each unit
 // carries only the kernels its launch functions instantiate (plus the few non-template ones).
 #ifndef PQ_UNIT
@@ -2807,6 +3201,71 @@ hipError_t launch_attention(int d, int bits, const AttnArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 #endif  // PQ_UNIT 4
+
+#if PQ_UNIT < 0 || PQ_UNIT == 5
+}  // namespace pqi
+namespace {
+template <int D>
+hipError_t launch_quantize_many_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::TensorDesc* tab, int n_tensors,
+                                  const pqi::LaunchCfg& c, hipStream_t s) {
+  const size_t lds = (size_t)a.t.ncell * a.t.nrep * 16;
+  const int grid = c.cu_count * PQ_QUANT_WG_PER_CU;
+  const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
+#define PQ_MANY_Q(MODE)                                                                                          \
+  if (in_bf16) hipLaunchKernelGGL((pq_quantize_many_kernel<D, true, MODE>), grid, kThreads, lds, s, a, tab, n_tensors); \
+  else hipLaunchKernelGGL((pq_quantize_many_kernel<D, false, MODE>), grid, kThreads, lds, s, a, tab, n_tensors);
+  if (mode == 2) { PQ_MANY_Q(2) }
+  else if (mode == 1) { PQ_MANY_Q(1) }
+  else { PQ_MANY_Q(0) }
+#undef PQ_MANY_Q
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dequantize_many_d(bool out_bf16, const pqi::DequantArgs& a, const pqi::TensorDesc* tab, int n_tensors,
+                                    const pqi::LaunchCfg& c, hipStream_t s) {
+  const int grid = c.cu_count * PQ_DEQUANT_WG_PER_CU;
+#define PQ_MANY_DQ(PB)                                                                                            \
+  if (out_bf16) hipLaunchKernelGGL((pq_dequantize_many_kernel<D, true, PB>), grid, kThreads, 0, s, a, tab, n_tensors); \
+  else hipLaunchKernelGGL((pq_dequantize_many_kernel<D, false, PB>), grid, kThreads, 0, s, a, tab, n_tensors);
+  switch (a.pbits) {
+    case 0: PQ_MANY_DQ(0) break;
+    case 1: PQ_MANY_DQ(1) break;
+    case 2: PQ_MANY_DQ(2) break;
+    case 3: PQ_MANY_DQ(3) break;
+    case 4: PQ_MANY_DQ(4) break;
+    case 5: PQ_MANY_DQ(5) break;
+    case 6: PQ_MANY_DQ(6) break;
+    case 7: PQ_MANY_DQ(7) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef PQ_MANY_DQ
+  return hipGetLastError();
+}
+}  // namespace
+namespace pqi {
+hipError_t launch_quantize_many(int d, bool in_bf16, const QuantArgs& a, const TensorDesc* tab, int n_tensors,
+                                const LaunchCfg& c, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_quantize_many_d<64>(in_bf16, a, tab, n_tensors, c, s);
+    case 128: return launch_quantize_many_d<128>(in_bf16, a, tab, n_tensors, c, s);
+    case 256: return launch_quantize_many_d<256>(in_bf16, a, tab, n_tensors, c, s);
+    case 512: return launch_quantize_many_d<512>(in_bf16, a, tab, n_tensors, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequantize_many(int d, bool out_bf16, const DequantArgs& a, const TensorDesc* tab, int n_tensors,
+                                  const LaunchCfg& c, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_dequantize_many_d<64>(out_bf16, a, tab, n_tensors, c, s);
+    case 128: return launch_dequantize_many_d<128>(out_bf16, a, tab, n_tensors, c, s);
+    case 256: return launch_dequantize_many_d<256>(out_bf16, a, tab, n_tensors, c, s);
+    case 512: return launch_dequantize_many_d<512>(out_bf16, a, tab, n_tensors, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+#endif  // PQ_UNIT 5
 
 #if PQ_UNIT < 0 || PQ_UNIT == 2
 hipError_t launch_quantize_bd(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {

@@ -318,3 +318,27 @@ def test_noalloc_limit_matches_the_header():
     with open(os.path.join(ROOT, "include", "pq.h")) as f:
         m = re.search(r"#define PQ_ATTN_NOALLOC_MAX_WORK \((\d+) << (\d+)\)", f.read())
     assert m and int(m.group(1)) << int(m.group(2)) == pq.ATTN_NOALLOC_MAX_WORK
+
+
+@pytest.mark.parametrize("args,st", [
+    ((96, 4, pq.PQ_BF16, 0, 3, P16), pq.PQ_EINVAL), ((1024, 4, pq.PQ_BF16, 0, 3, P16), pq.PQ_EUNSUPPORTED),
+    ((128, 0, pq.PQ_BF16, 0, 3, P16), pq.PQ_EINVAL), ((128, 4, 7, 0, 3, P16), pq.PQ_EINVAL),
+    ((128, 4, pq.PQ_BF16, 2, 3, P16), pq.PQ_EINVAL), ((128, 4, pq.PQ_BF16, 0, -1, P16), pq.PQ_EINVAL),
+    ((128, 4, pq.PQ_BF16, 0, 3, NUL), pq.PQ_EINVAL), ((128, 4, pq.PQ_BF16, 0, 3, ctypes.c_void_p(0x10004)), pq.PQ_EINVAL),
+    ((128, 4, pq.PQ_BF16, 1, 0, NUL), pq.PQ_OK),
+])
+def test_grouped_validation(args, st):
+    """The grouped codec's host-side validation (no HIP call on these paths)."""
+    lib = pq.lib()
+    assert lib.pq_quantize_many(*args, NUL) == st
+    assert lib.pq_dequantize_many(*args, NUL) == st
+
+
+def test_tensor_record_layout():
+    """pq_tensor is six 8-byte fields, 48 bytes: the table the binding builds."""
+    import re
+    with open(os.path.join(ROOT, "include", "pq.h")) as f:
+        txt = f.read()
+    body = re.search(r"typedef struct \{([^}]*)\} pq_tensor;", txt).group(1)
+    fields = [l.strip().rstrip(";").split()[-1].lstrip("*") for l in body.strip().splitlines()]
+    assert fields == ["x", "codes", "norms", "signs", "out", "n_blocks"]
