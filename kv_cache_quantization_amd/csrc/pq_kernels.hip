@@ -531,9 +531,7 @@ struct Quantizer {
       const int o = cperm<D>(j);
       cw[o >> 2] |= code << (8 * (o & 3));
       // at most 8 grid lookups in flight: bounds the registers the scheduler may tie up
-      // (twice as many without the QJL stage, whose lookups hold fewer registers)
-      constexpr int LB = QJL ? PQ_LOOKUP_BATCH : 2 * PQ_LOOKUP_BATCH;
-      if ((j % LB) == LB - 1) __builtin_amdgcn_sched_barrier(0);
+      if ((j % PQ_LOOKUP_BATCH) == PQ_LOOKUP_BATCH - 1) __builtin_amdgcn_sched_barrier(0);
     }
     // materialise the packed codes here: otherwise the whole decision chain sinks into
     // the store branch below and keeps every lookup result live until then
@@ -1090,11 +1088,15 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::Dequ
 // the chunks of C consecutive tiles w, w + n_waves, ... and a cursor that only moves forward
 // finds each tile's tensor from the table's block counts (uniform loads).  Dequantize, bound by
 // memory, strides over the whole set in chunks of PQ_MANY_CHUNK tiles (as the single-tensor
-// kernels stride over one tensor); quantize, bound by vector issue, gives each wave one
-// contiguous range (C = total / waves), so it changes tensor at most a few times.
+// kernels stride over one tensor) and loads the next tile's record with its codes; quantize,
+// bound by vector issue, gives each wave one contiguous range, so it changes tensor at most a
+// few times.
 // ------------------------------------------------------------------------------------------
 #ifndef PQ_MANY_CHUNK
 #define PQ_MANY_CHUNK 2
+#endif
+#ifndef PQ_MANY_WG_PER_CU
+#define PQ_MANY_WG_PER_CU 4      // grouped quantize: workgroups per CU
 #endif
 __device__ __forceinline__ int64_t tiles_of(int64_t n_blocks) { return (n_blocks + 15) >> 4; }
 
@@ -1164,38 +1166,23 @@ void pq_quantize_many_kernel(const pqi::QuantArgs a, const pqi::TensorDesc* tab,
   const int64_t total = many_total(tab, n_tensors);
   const int64_t n_waves = (int64_t)gridDim.x * kWaves;
   const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t C = (total + n_waves - 1) / n_waves;
+  // one contiguous range per wave (few tensor changes; four waves per SIMD hide the loads)
+  const int64_t t0 = total * w / n_waves, t1 = total * (w + 1) / n_waves;
+  if (t0 >= t1) return;
   ManyCursor cur;
   cur.init(tab);
-  int64_t k = 0, T = many_tile(w, 0, n_waves, C);
-  if (T >= total) return;
-  cur.seek(T);
-  ManyRecord<D> rc, rn;                            // this tile's tensor, the next tile's
+  cur.seek(t0);
+  ManyRecord<D> rc;
   rc.read(tab, cur);
   q.retarget(rc.sw, rc.codes, rc.norms, rc.n_blocks);
-  auto load = [&](uint4 (&raw)[Q::NR], const ManyRecord<D>& r, int64_t Tg) {
-    load_tile<D, IN_BF16>(raw, r.x, Tg - r.base, r.n_blocks, r.n_blocks >> 4, q.r, q.g);
-  };
-  uint4 raw[Q::NR], alt[Q::NR];
-  load(raw, rc, T);
-  // two buffers take turns: the next tile's input (and its tensor's record) loads while this
-  // tile is processed
-  auto step = [&](uint4 (&now)[Q::NR], uint4 (&next)[Q::NR]) {
-    const int64_t Tn = many_tile(w, k + 1, n_waves, C);
-    const bool more = Tn < total;
-    const bool moved = more && cur.seek(Tn);
-    if (moved) rn.read(tab, cur);
-    if (more) load(next, moved ? rn : rc, Tn);
-    q.tile(now, T - rc.base);
-    if (moved) {
-      rc = rn;
+  for (int64_t T = t0; T < t1; ++T) {
+    if (cur.seek(T)) {
+      rc.read(tab, cur);
       q.retarget(rc.sw, rc.codes, rc.norms, rc.n_blocks);
     }
-    T = Tn;
-    ++k;
-    return more;
-  };
-  while (step(raw, alt) && step(alt, raw)) {
+    uint4 raw[Q::NR];
+    load_tile<D, IN_BF16>(raw, rc.x, T - rc.base, rc.n_blocks, rc.n_blocks >> 4, q.r, q.g);
+    q.tile(raw, T - rc.base);
   }
 }
 
@@ -3209,7 +3196,7 @@ template <int D>
 hipError_t launch_quantize_many_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::TensorDesc* tab, int n_tensors,
                                   const pqi::LaunchCfg& c, hipStream_t s) {
   const size_t lds = (size_t)a.t.ncell * a.t.nrep * 16;
-  const int grid = c.cu_count * PQ_QUANT_WG_PER_CU;
+  const int grid = c.cu_count * PQ_MANY_WG_PER_CU;
   const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
 #define PQ_MANY_Q(MODE)                                                                                          \
   if (in_bf16) hipLaunchKernelGGL((pq_quantize_many_kernel<D, true, MODE>), grid, kThreads, lds, s, a, tab, n_tensors); \
