@@ -185,7 +185,7 @@ def summarize(run_dir):
            "kernels": {}}
     # the byte-code instantiations the roofline is quoted on (the same run also times the
     # packed-code kernels, whose traffic differs)
-    for kname, key in (("pq_quantize_kernel<128, true, true, true, 1, 256>", "pq_quantize_kernel"),
+    for kname, key in (("pq_quantize_kernel<128, true, true, false, 1, 1024, true>", "pq_quantize_kernel"),
                        ("pq_dequantize_kernel<128, true, 0>", "pq_dequantize_kernel")):
         fk, nf = counter("pmc_q_fetch", "q_fetch", kname)
         wk, nw = counter("pmc_q_write", "q_write", kname)
@@ -745,6 +745,18 @@ def main():
     t_qp = timed(torch, quant_packed, args.steps)
     t_dp = timed(torch, dequant_packed, args.steps)
 
+    # the ceiling of a dequantize-shaped stream on this GPU, measured in the same run: torch's
+    # uint8 -> bf16 conversion reads 1 byte and writes 2 per value, the traffic of dequantize
+    # without its arithmetic (over the same 8 rotating buffer sets)
+    st_in = [bs[1] for bs in sets]                   # codes, uint8 [n, d]
+    st_out = [bs[5] for bs in sets]                  # output, bf16 [n, d]
+
+    def stream(k):
+        st_out[k % N_SETS].copy_(st_in[k % N_SETS])
+
+    stream(0)
+    t_stream = timed(torch, stream, args.steps)
+
     in_bytes = n_blocks * d * 2
     q_bytes = in_bytes + n_blocks * d + n_blocks * 2 + n_blocks * (m // 8) + n_blocks * 2
     dq_bytes = n_blocks * d + n_blocks * 2 + in_bytes
@@ -775,6 +787,8 @@ def main():
             "quantize_algorithmic_bytes": q_bytes, "dequantize_algorithmic_bytes": dq_bytes,
             "quantize_packed_us": round(t_qp * 1e6, 3), "dequantize_packed_us": round(t_dp * 1e6, 3),
             "packed_input_gb_per_s": round(in_bytes / (t_qp + t_dp) / 1e9, 1),
+            "stream_1B_in_2B_out_us": round(t_stream * 1e6, 3),
+            "stream_1B_in_2B_out_hbm_frac": round(3 * n_blocks * d / t_stream / 1e9 / HBM_PEAK_GBS, 4),
         },
         "roofline": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(q_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -783,21 +797,31 @@ def main():
         "kernel_source": kernel_source_hash(),
         "counters": sq_counters(),
     }
+    def progress(what):
+        print("[bench] %s done" % what, file=sys.stderr, flush=True)
+
+    progress("config-2 codec")
     if not args.no_qjl:
         rec["parts"].update(qjl_leg(pq, synth, torch, args.steps, args.warmup))
+        progress("config-4 QJL leg")
     if not args.no_tsq:
         rec["parts"].update(tsq_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+        progress("config-5 two-stage leg")
     if not args.no_dense:
         rec["parts"].update(dense_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+        progress("dense-rotation leg")
     if not args.no_bd:
         rec["parts"].update(bd_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+        progress("block-diagonal leg")
     if not args.no_attn:
         rec["parts"].update(attn_leg(pq, synth, torch, max(5, args.steps // 10), min(args.warmup, 3)))
+        progress("attention leg")
     if not args.no_grouped:
         w3 = config3_weights(synth, torch, dev)
         rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50), xs=w3))
         rec["parts"].update(grouped_leg(pq, synth, torch, max(3, args.steps // 50), packed=True, xs=w3))
         del w3
+        progress("config-3 grouped leg")
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.cpu_sample_blocks)
     print(json.dumps(rec), flush=True)
