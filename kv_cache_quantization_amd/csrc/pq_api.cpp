@@ -880,7 +880,10 @@ int pq_quantize_dense(int d, int bits, int in_dtype, const void* x, int64_t n_bl
   a.x = x; a.codes = codes; a.norms = norms; a.rot = rot; a.n_blocks = n_blocks; a.d = d; a.bits = bits;
   const Codebook& cb = sphere_codebook(bits, d);
   for (int k = 0; k < (1 << bits); ++k) a.cent[k] = (float)cb.c[k];
-  for (int k = 0; k + 1 < (1 << bits); ++k) a.beta[k] = (float)cb.beta[k];
+  for (int k = 0; k + 1 < (1 << bits); ++k) {
+    a.beta[k] = (float)cb.beta[k];
+    a.beta_lo[k] = (float)(cb.beta[k] - (double)a.beta[k]);
+  }
   return hip_status(pqi::launch_quantize_dense(in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
 }
 

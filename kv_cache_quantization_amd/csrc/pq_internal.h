@@ -241,7 +241,8 @@ struct BdArgs {
   int64_t n_blocks;
   int d, bits;
   float cent[1 << kMaxBits];  // centroids, ascending
-  float beta[(1 << kMaxBits) - 1];   // boundaries, ascending
+  float beta[(1 << kMaxBits) - 1];   // boundaries, ascending (fp32 rounding of the double ones)
+  float beta_lo[(1 << kMaxBits) - 1];   // double boundary - beta (the dense rotation's exact recheck)
 };
 
 // one tensor of a grouped call (the public pq_tensor record, in device memory)

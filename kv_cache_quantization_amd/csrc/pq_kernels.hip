@@ -759,7 +759,7 @@ __device__ void stage_projection_rows(const uint16_t* proj, const uint8_t* signs
 // per SIMD.  RB (rotated-basis projection, G D H in LDS): sixteen-wave workgroups, one per CU
 // (four waves per SIMD), so the grid and G D H are built once per CU.
 template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE, int THREADS = kThreads, bool RB = false>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(RB ? THREADS / 256 : (THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU))))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(RB ? (MODE == 2 ? 3 : 4) : (THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU))))
 void pq_quantize_kernel(const pqi::QuantArgs a) {
   using Q = Quantizer<D, IN_BF16, QJL, G_LDS, MODE, RB>;
   constexpr int WAVES = THREADS / 64;
@@ -778,18 +778,15 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
   int64_t T = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
   uint4 raw[Q::NR];
   if constexpr (Q::NR <= 4) {
-    // the next tile's input is loaded before this tile is processed (16 more registers); two
-    // buffers take turns, so nothing is copied between them
-    uint4 alt[Q::NR];
+    // the next tile's input is loaded before this tile is processed (16 more registers; a
+    // two-buffer unrolled loop would save the copies but pushes the kernel into spills)
     if (T < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
-    while (T < n_tiles) {
-      if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(alt, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
+    for (; T < n_tiles; T += n_waves) {
+      uint4 nxt[Q::NR];
+      if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(nxt, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
       q.tile(raw, T);
-      T += n_waves;
-      if (T >= n_tiles) break;
-      if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
-      q.tile(alt, T);
-      T += n_waves;
+#pragma unroll
+      for (int i = 0; i < Q::NR; ++i) raw[i] = nxt[i];
     }
   } else {
     // several waves per SIMD overlap one wave's loads with another's arithmetic
@@ -2710,18 +2707,19 @@ __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs
 // Dense rotation with the sphere-coordinate codebook: y = Pi x / ||x||, codes against that
 // codebook, xhat = n16 Pi^T c.  One wave per block (grid stride); the workgroup holds Pi in LDS
 // (transposed for quantize, so lane i reads row i of Pi as consecutive words across lanes);
-// the products of fp32 inputs are exact in double and summed in double, so the code decision
-// sees y to double precision before its rounding to fp32.
+// the products of fp32 inputs are exact in double and summed in double, and the code is decided
+// on that double y against the double boundaries (each held as an fp32 pair beta + beta_lo,
+// 48 significant bits).
 // ------------------------------------------------------------------------------------------
 template <bool IN_BF16>
 __global__ __launch_bounds__(256) void pq_quantize_dense_kernel(const pqi::BdArgs a) {
   extern __shared__ float dsm[];                         // [d][d] Pi^T, then [4 waves][d] blocks
-  __shared__ float beta[(1 << pqi::kMaxBits) - 1];
+  __shared__ double beta[(1 << pqi::kMaxBits) - 1];
   const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float* pit = dsm;
   float* xb = dsm + d * d + wv * d;
   for (int idx = threadIdx.x; idx < d * d; idx += blockDim.x) pit[(idx % d) * d + idx / d] = a.rot[idx];
-  for (int j = threadIdx.x; j < (1 << a.bits) - 1; j += blockDim.x) beta[j] = a.beta[j];
+  for (int j = threadIdx.x; j < (1 << a.bits) - 1; j += blockDim.x) beta[j] = (double)a.beta[j] + (double)a.beta_lo[j];
   __syncthreads();
   const int64_t n_waves = (int64_t)gridDim.x * 4;
   for (int64_t blk = (int64_t)blockIdx.x * 4 + wv; blk < a.n_blocks; blk += n_waves) {
@@ -2741,7 +2739,7 @@ __global__ __launch_bounds__(256) void pq_quantize_dense_kernel(const pqi::BdArg
         s0 += (double)pit[j * d + i] * (double)xb[j];
         s1 += (double)pit[(j + 1) * d + i] * (double)xb[j + 1];
       }
-      const float y = (float)((s0 + s1) * inv);
+      const double y = (s0 + s1) * inv;
       int code = 0;
       for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
         if (y > beta[code + step - 1]) code += step;
@@ -2783,10 +2781,13 @@ __global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdA
 }
 
 // Quantize on the matrix cores: a wave takes 16 blocks, Y (16 x d) = X (16 x d) Pi^T with
-// v_mfma_f32_16x16x4f32 (layout as the dequantize kernel below, Pi^T in LDS).  An fp32 sum of
-// d products is within d 2^-24 ||x|| of the exact one, so a coordinate of y = Y / ||x|| farther
-// than twice that from every boundary takes the same code as the exact value; the few nearer
-// ones are recomputed from LDS with exact products summed in double, as the one-wave kernel.
+// v_mfma_f32_16x16x4f32 (layout as the dequantize kernel below, Pi^T in LDS).  Each block is
+// staged scaled by a power of two that brings its norm into [1, 2) (exact; products of tiny
+// blocks would otherwise fall into fp32's subnormal range).  An fp32 sum of d products is then
+// within d 2^-24 ||x|| of the exact one, so a coordinate of y = Y / ||x|| farther than twice that
+// from every boundary takes the same code as the exact value; the few nearer ones are recomputed
+// from LDS with exact products summed in double and decided against the double boundaries, as
+// the one-wave kernel.
 constexpr int kDenseQWaves = 8;                         // waves sharing one LDS copy of Pi^T
 
 template <bool IN_BF16, int D>
@@ -2796,17 +2797,27 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
   constexpr float EPS = 2.0f * (float)D / 16777216.0f;   // twice the fp32 sum's error bound
   extern __shared__ float dsm[];                         // [D][PS] Pi^T, then [waves][16][D] x
   __shared__ float beta[(1 << pqi::kMaxBits) - 1];
+  __shared__ double beta_d[(1 << pqi::kMaxBits) - 1];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nb = (1 << a.bits) - 1;
   float* xs = dsm + D * PS + wv * 16 * D;
   for (int idx = threadIdx.x; idx < D * D; idx += blockDim.x) dsm[(idx % D) * PS + idx / D] = a.rot[idx];
-  for (int j = threadIdx.x; j < nb; j += blockDim.x) beta[j] = a.beta[j];
+  for (int j = threadIdx.x; j < nb; j += blockDim.x) {
+    beta[j] = a.beta[j];
+    beta_d[j] = (double)a.beta[j] + (double)a.beta_lo[j];
+  }
   __syncthreads();
   auto decide = [&](float y) {
     int code = 0;
     for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
       if (y > beta[code + step - 1]) code += step;
+    return code;
+  };
+  auto decide_d = [&](double y) {
+    int code = 0;
+    for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
+      if (y > beta_d[code + step - 1]) code += step;
     return code;
   };
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
@@ -2823,6 +2834,12 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);                            // the block's sum in all four lanes
+    // scale the staged block by 2^-floor(log2 ||x||) (each lane its own elements)
+    const int ex = ss > 0.0 ? min(max(-ilogb(sqrt(ss)), -1000), 1000) : 0;
+    const float sc = ex > 126 || ex < -126 ? 1.0f : ldexpf(1.0f, ex);
+    const double scd = ex > 126 || ex < -126 ? ldexp(1.0, ex) : (double)sc;
+    if (sc != 1.0f || scd != 1.0)
+      for (int e = g; e < D; e += 4) xs[r * D + e] = (float)((double)xs[r * D + e] * scd);
     __builtin_amdgcn_wave_barrier();
     f32x4 acc[NT];
 #pragma unroll
@@ -2840,7 +2857,9 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
       const int bl = 4 * g + i;
       const int64_t b = tile * 16 + bl;
       const double sb = __shfl(ss, bl);                 // lane bl holds block bl's sum
-      const double invd = sb > 0.0 ? 1.0 / sqrt(sb) : 0.0;
+      const int exb = __shfl(ex, bl);
+      // 1 / ||x_scaled|| = 1 / (||x|| 2^ex): y is the same whether x is scaled or not
+      const double invd = sb > 0.0 ? 1.0 / (sqrt(sb) * ldexp(1.0, exb)) : 0.0;
       const float inv = (float)invd;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -2854,8 +2873,7 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
             s0 += (double)dsm[j * PS + n] * (double)xs[bl * D + j];
             s1 += (double)dsm[(j + 1) * PS + n] * (double)xs[bl * D + j + 1];
           }
-          y = (float)((s0 + s1) * invd);
-          code = decide(y);
+          code = decide_d((s0 + s1) * invd);
         }
         if (b < a.n_blocks) a.codes[b * D + n] = (uint8_t)code;
       }
@@ -2967,16 +2985,22 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   const bool g_lds = qjl && base + glb <= (size_t)c.max_lds;
   const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
   // rotated-basis projection when G D H (fp16 high + low) fits beside the grid: one
-  // sixteen-wave workgroup per CU
+  // sixteen-wave workgroup per CU (four waves per SIMD at <= 128 VGPRs); packed codes hold
+  // more registers and run four-wave workgroups, three per CU (three waves per SIMD)
   const size_t grb = (size_t)m_pad * D * 4;
-  if (qjl && base + grb <= (size_t)c.max_lds && base + grb <= 98304) {
+  if (qjl && base + grb <= (size_t)c.max_lds && base + grb <= 98304 && (mode < 2 || 3 * (base + grb) <= (size_t)c.max_lds)) {
     const size_t lds = base + grb;
+    if (mode == 2) {
+      const int g4 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count * 3, (n_tiles + 3) / 4));
+      if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, 2, 256, true>), g4, 256, lds, s, a);
+      else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, 2, 256, true>), g4, 256, lds, s, a);
+      return hipGetLastError();
+    }
     const int g16 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count, (n_tiles + 15) / 16));
 #define PQ_RB_LAUNCH(MODE)                                                                                       \
   if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, MODE, 1024, true>), g16, 1024, lds, s, a); \
   else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, MODE, 1024, true>), g16, 1024, lds, s, a);
-    if (mode == 2) { PQ_RB_LAUNCH(2) }
-    else if (mode == 1) { PQ_RB_LAUNCH(1) }
+    if (mode == 1) { PQ_RB_LAUNCH(1) }
     else { PQ_RB_LAUNCH(0) }
 #undef PQ_RB_LAUNCH
     return hipGetLastError();

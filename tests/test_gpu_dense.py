@@ -77,3 +77,32 @@ def test_dense_codec(d, bits, n, bf16):
     ulp = np.ldexp(1.0, np.frexp(np.abs(r16))[1] - 8)
     e16 = np.abs(o16.float().cpu().numpy().astype(np.float64) - r16)
     assert np.all((e16 <= ulp) | (np.abs(o16.float().cpu().numpy() - refd) <= 2e-5 * gn[:, None] * cmax))
+
+
+@pytest.mark.parametrize("d", [128, 64, 48])
+def test_dense_tiny_blocks(d):
+    """fp32 blocks whose values sit far below 1 (1e-20, 1e-30, and 1e-41, in fp32's subnormal
+    range): the codes follow the rotation of the block's direction, as for unit-scale blocks
+    (the kernels scale each block by a power of two before the fp32 products)."""
+    _case("dense rotation tiny blocks d=%d" % d)
+    bits, n = 3, 96
+    rng = np.random.default_rng(d + 77)
+    xf = rng.standard_normal((n, d)).astype(np.float32)
+    xf[0:32] *= np.float32(1e-20)
+    xf[32:64] *= np.float32(1e-30)
+    xf[64:96] = (xf[64:96].astype(np.float64) * 1e-41).astype(np.float32)   # subnormal fp32 values
+    assert np.all(np.abs(xf[64:96]) < 1.2e-38)
+    Pi = _rotation(d + 5, d)
+    codes, norms = pq.quantize_dense(torch.from_numpy(xf).cuda(), d, bits, torch.from_numpy(Pi).cuda())
+    torch.cuda.synchronize()
+    gc = codes.cpu().numpy()
+    ref = dense.quantize(xf.astype(np.float64), bits, Pi.astype(np.float64))
+    diff = np.argwhere(gc != ref["codes"])
+    for b, i in diff:
+        lo = min(int(gc[b, i]), int(ref["codes"][b, i]))
+        assert abs(int(gc[b, i]) - int(ref["codes"][b, i])) == 1, "code off by more than one at %s" % ((b, i),)
+        # subnormal inputs carry fewer significant bits: their blocks get a wider band
+        band = 1e-4 if b < 64 else 1e-2
+        assert abs(ref["y"][b, i] - ref["beta"][lo]) < band / math.sqrt(d), "code differs away from a boundary at %s" % ((b, i),)
+    assert len(diff) <= max(1, int(1e-6 * gc.size)) + int(np.sum(diff[:, 0] >= 64))
+    assert np.all(parity.f16_values(norms) == 0.0)          # below fp16's range
