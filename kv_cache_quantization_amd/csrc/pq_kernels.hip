@@ -2781,13 +2781,13 @@ __global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdA
 }
 
 // Quantize on the matrix cores: a wave takes 16 blocks, Y (16 x d) = X (16 x d) Pi^T with
-// v_mfma_f32_16x16x4f32 (layout as the dequantize kernel below, Pi^T in LDS).  Each block is
-// staged scaled by a power of two that brings its norm into [1, 2) (exact; products of tiny
-// blocks would otherwise fall into fp32's subnormal range).  An fp32 sum of d products is then
-// within d 2^-24 ||x|| of the exact one, so a coordinate of y = Y / ||x|| farther than twice that
-// from every boundary takes the same code as the exact value; the few nearer ones are recomputed
-// from LDS with exact products summed in double and decided against the double boundaries, as
-// the one-wave kernel.
+// v_mfma_f32_16x16x4f32 (layout as the dequantize kernel below, Pi^T in LDS).  A block of
+// extreme norm is staged scaled by a power of two that brings its norm into [1, 2) (exact;
+// products of tiny blocks would otherwise fall into fp32's subnormal range).  An fp32 sum of d
+// products is then within d 2^-24 ||x|| of the exact one, so a coordinate of y = Y / ||x||
+// farther than twice that from every boundary takes the same code as the exact value; the few
+// nearer ones are recomputed from LDS with exact products summed in double and decided against
+// the double boundaries, as the one-wave kernel.
 constexpr int kDenseQWaves = 8;                         // waves sharing one LDS copy of Pi^T
 
 template <bool IN_BF16, int D>
@@ -2834,12 +2834,15 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);                            // the block's sum in all four lanes
-    // scale the staged block by 2^-floor(log2 ||x||) (each lane its own elements)
-    const int ex = ss > 0.0 ? min(max(-ilogb(sqrt(ss)), -1000), 1000) : 0;
-    const float sc = ex > 126 || ex < -126 ? 1.0f : ldexpf(1.0f, ex);
-    const double scd = ex > 126 || ex < -126 ? ldexp(1.0, ex) : (double)sc;
-    if (sc != 1.0f || scd != 1.0)
+    // a block whose norm lies outside [2^-60, 2^60] is staged scaled by 2^-floor(log2 ||x||)
+    // (each lane its own elements); inside that range no fp32 product or sum leaves the
+    // normal range and the block is used as it is
+    const int e0 = ss > 0.0 ? ilogb(sqrt(ss)) : 0;
+    const int ex = e0 < -60 || e0 > 60 ? -e0 : 0;
+    if (ex != 0) {
+      const double scd = ldexp(1.0, ex);
       for (int e = g; e < D; e += 4) xs[r * D + e] = (float)((double)xs[r * D + e] * scd);
+    }
     __builtin_amdgcn_wave_barrier();
     f32x4 acc[NT];
 #pragma unroll
