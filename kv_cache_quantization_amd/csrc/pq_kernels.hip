@@ -1253,8 +1253,93 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_many_kernel(const pqi:
 #endif
 constexpr int kSketchThreads = PQ_SKETCH_THREADS;
 
-// SPLIT: the keys are masked to their group's outlier channels (part 1) or to the other
-// channels (part 0) as they are loaded, so norm and signs are those of the masked key.
+// The keys of pass P (NT tiles of 16) as MFMA B fragments: lane quarter g holds elements
+// 32 s + 8 g .. +7 of key row r of each tile (zero past the last key).  SPLIT: the keys are
+// masked to their group's outlier channels (part 1) or to the other channels (part 0) as they
+// are loaded, so norm and signs are those of the masked key.  STREAM: non-temporal loads.
+template <int D, int NT, bool SPLIT, bool STREAM = true>
+__device__ __forceinline__ void sketch_load_keys(bf16x8 (&kf)[NT][D / 32], const pqi::SketchArgs& a, int64_t P,
+                                                 int r, int g) {
+  constexpr int KS = D / 32;
+  const int64_t n_keys = a.n_keys;
+  const bool full = (P + 1) * NT * 16 <= n_keys;          // uniform
+  // SPLIT: (head, token) of the pass's first key, once per pass
+  int64_t head0 = 0, tok0 = 0;
+  if constexpr (SPLIT) {
+    head0 = (P * NT * 16) / a.seq_len;
+    tok0 = P * NT * 16 - head0 * a.seq_len;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t key = (P * NT + t) * 16 + r;
+    const bool valid = full || key < n_keys;
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.keys + key * D);
+    // element 8 s + i of this lane (column 32 s + 8 g + i) is an outlier channel of the key's
+    // group when bit 8 s + i of om is set
+    uint32_t om[(KS * 8 + 31) / 32];
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int w = 0; w < (KS * 8 + 31) / 32; ++w) om[w] = 0;
+      // the key's (head, token): at most NT 16 tokens past the pass's first key (keys past the
+      // end take the last key's group)
+      int64_t head = head0, tok = tok0 + t * 16 + r;
+      while (tok >= a.seq_len) {
+        tok -= a.seq_len;
+        ++head;
+      }
+      if (!valid) {
+        head = n_keys / a.seq_len - 1;
+        tok = a.seq_len - 1;
+      }
+      const int64_t grp = a.seq_len <= 0xFFFFFFFFll ? (int64_t)((uint32_t)tok / (uint32_t)a.group_size)
+                                                    : tok / a.group_size;
+      const uint8_t* ix = a.oidx + (head * a.n_groups + grp) * a.n_out;
+#pragma unroll 8
+      for (int j = 0; j < a.n_out; ++j) {
+        const int c = ix[j];
+        if (((c >> 3) & 3) == g) {
+          const int b = 8 * (c >> 5) + (c & 7);
+#pragma unroll
+          for (int w = 0; w < (KS * 8 + 31) / 32; ++w) om[w] |= (b >> 5) == w ? 1u << (b & 31) : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 w = {0, 0, 0, 0};
+      if (valid) w = STREAM ? __builtin_nontemporal_load(src + 4 * s + g) : src[4 * s + g];
+      if constexpr (SPLIT) {
+        const uint32_t bs = om[(8 * s) >> 5] >> ((8 * s) & 31);      // this chunk's 8 bits
+        const uint32_t keep = a.part ? bs : ~bs;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          w[u] &= ((keep >> (2 * u)) & 1u ? 0x0000FFFFu : 0u) | ((keep >> (2 * u + 1)) & 1u ? 0xFFFF0000u : 0u);
+      }
+      kf[t][s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+// The squared norm of this lane's key of tile t (all four quarters summed).
+template <int D, int NT>
+__device__ __forceinline__ float sketch_sumsq(const bf16x8 (&kf)[NT][D / 32], int t) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  float ss = 0.0f;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    const u32x4 w = __builtin_bit_cast(u32x4, kf[t][s]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // element copied to a scalar first: a bit cast of the vector element itself
+      // is lowered to a read of element 0 by this compiler
+      const uint32_t wu = w[u];
+      const bf16x2 h = __builtin_bit_cast(bf16x2, wu);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
+    }
+  }
+  return sum4(ss);
+}
+
 template <int D, bool G_LDS, bool SPLIT>
 __global__ __launch_bounds__(kSketchThreads) __attribute__((amdgpu_waves_per_eu(PQ_SKETCH_WAVES_PER_EU)))
 void qjl_sketch_kernel(const pqi::SketchArgs a) {
@@ -1271,7 +1356,6 @@ void qjl_sketch_kernel(const pqi::SketchArgs a) {
     stage_projection<D>(a.proj, m, m_pad, gl);
     __syncthreads();
   }
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = m_pad >> 4;
@@ -1282,63 +1366,12 @@ void qjl_sketch_kernel(const pqi::SketchArgs a) {
   const int64_t n_waves = (int64_t)gridDim.x * WAVES;
 
   for (int64_t P = wave_id; P < n_pass; P += n_waves) {
-    // lane quarter g holds elements 32 s + 8 g .. +7 of key row r of each tile
     bf16x8 kf[NT][KS];
-    const bool full = (P + 1) * NT * 16 <= n_keys;          // uniform
+    sketch_load_keys<D, NT, SPLIT>(kf, a, P, r, g);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t key = (P * NT + t) * 16 + r;
-      const bool valid = full || key < n_keys;
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.keys + key * D);
-      // element 8 s + i of this lane (column 32 s + 8 g + i) is an outlier channel of the key's
-      // group when bit 8 s + i of om is set
-      uint32_t om[(KS * 8 + 31) / 32];
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int w = 0; w < (KS * 8 + 31) / 32; ++w) om[w] = 0;
-        const int64_t kc = min(key, n_keys - 1);
-        const int64_t head = kc / a.seq_len, grp = (kc % a.seq_len) / a.group_size;
-        const uint8_t* ix = a.oidx + (head * a.n_groups + grp) * a.n_out;
-        for (int j = 0; j < a.n_out; ++j) {
-          const int c = ix[j];
-          if (((c >> 3) & 3) == g) {
-            const int b = 8 * (c >> 5) + (c & 7);
-#pragma unroll
-            for (int w = 0; w < (KS * 8 + 31) / 32; ++w) om[w] |= (b >> 5) == w ? 1u << (b & 31) : 0u;
-          }
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        u32x4 w = {0, 0, 0, 0};
-        if (valid) w = __builtin_nontemporal_load(src + 4 * s + g);
-        if constexpr (SPLIT) {
-          const uint32_t bs = om[(8 * s) >> 5] >> ((8 * s) & 31);      // this chunk's 8 bits
-          const uint32_t keep = a.part ? bs : ~bs;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            w[u] &= ((keep >> (2 * u)) & 1u ? 0x0000FFFFu : 0u) | ((keep >> (2 * u + 1)) & 1u ? 0xFFFF0000u : 0u);
-        }
-        kf[t][s] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int64_t key = (P * NT + t) * 16 + r;
-      float ss = 0.0f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 w = __builtin_bit_cast(u32x4, kf[t][s]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          // element copied to a scalar first: a bit cast of the vector element itself
-          // is lowered to a read of element 0 by this compiler
-          const uint32_t wu = w[u];
-          const bf16x2 h = __builtin_bit_cast(bf16x2, wu);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
-        }
-      }
-      ss = sum4(ss);
+      const float ss = sketch_sumsq<D, NT>(kf, t);
       if (key < n_keys && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
     }
     for (int nt0 = 0; nt0 < ntiles; nt0 += 4) {
@@ -1367,6 +1400,143 @@ void qjl_sketch_kernel(const pqi::SketchArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         store_sign_bytes(sign_bytes_of(x[t]), lane, (P * NT + t) * 16, n_keys, a.bits, mb, nt0);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// QJL key sketch for m a multiple of 128 with G in LDS.  Row 128 c + 8 p + q of G is output row
+// p of N tile q (0..7) of row group c, so at the end of a row group lane quarter g of key r holds
+// the signs of rows 128 c + 32 g .. + 31 of that key as one word in bit order (byte i: rows
+// 128 c + 8 (4 g + i) + 0..7), stored without any exchange between lanes.  A sign is read from
+// the fp16 conversion of a projection rounded toward zero (which keeps the sign of every
+// nonzero value); one byte permute gathers the four signs of an accumulator.  The keys of the
+// wave's next pass are loaded while this pass is computed.
+// ------------------------------------------------------------------------------------------
+#ifndef PQ_SKETCH8_NT
+#define PQ_SKETCH8_NT 2                                     // key tiles per pass (d <= 128; half that above)
+#endif
+#ifndef PQ_SKETCH8_WAVES_PER_EU
+#define PQ_SKETCH8_WAVES_PER_EU 4
+#endif
+#ifndef PQ_SKETCH8_WG_PER_CU
+#define PQ_SKETCH8_WG_PER_CU 2
+#endif
+#ifndef PQ_SKETCH8_THREADS
+#define PQ_SKETCH8_THREADS 512
+#endif
+constexpr int kSketch8Threads = PQ_SKETCH8_THREADS;
+template <int D>
+constexpr int sketch8_nt() { return D <= 128 ? PQ_SKETCH8_NT : (PQ_SKETCH8_NT + 1) / 2; }
+
+// LDS position of 16-byte chunk c of G row n: the rows 8 p + q (p = 0..15) that one 16-lane
+// group reads together land on 16 different bank groups (8 for d = 64)
+template <int D>
+__device__ __forceinline__ int g_swizzle8(int n, int c) {
+  constexpr int CPR = D / 8;
+  constexpr int SW = CPR < 16 ? CPR - 1 : 15;
+  return n * CPR + (c ^ ((n >> 3) & SW));
+}
+
+// Sign bits of the four projections of an accumulator at the top bit of each byte (1 where
+// the projection is negative or -0).
+__device__ __forceinline__ uint32_t sign_tops(const f32x4& acc) {
+  const uint32_t h01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(acc[0], acc[1]));
+  const uint32_t h23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(acc[2], acc[3]));
+  return __builtin_amdgcn_perm(h23, h01, 0x07050301u);
+}
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(kSketch8Threads) __attribute__((amdgpu_waves_per_eu(PQ_SKETCH8_WAVES_PER_EU)))
+void qjl_sketch_rows_kernel(const pqi::SketchArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int NT = sketch8_nt<D>();
+  constexpr int WAVES = kSketch8Threads / 64;
+  constexpr int CPR = D / 8;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint4* gl = reinterpret_cast<uint4*>(smem);
+  const int m = a.m, mb = m >> 3, ngrp = m >> 7;
+  {
+    // G into LDS, four chunks in flight per thread
+    const uint4* src = reinterpret_cast<const uint4*>(a.proj);
+    const int total = m * CPR;
+    constexpr int S = kSketch8Threads;
+    int i = threadIdx.x;
+    for (; i + 3 * S < total; i += 4 * S) {
+      const uint4 b0 = src[i], b1 = src[i + S], b2 = src[i + 2 * S], b3 = src[i + 3 * S];
+      gl[g_swizzle8<D>(i / CPR, i % CPR)] = b0;
+      gl[g_swizzle8<D>((i + S) / CPR, (i + S) % CPR)] = b1;
+      gl[g_swizzle8<D>((i + 2 * S) / CPR, (i + 2 * S) % CPR)] = b2;
+      gl[g_swizzle8<D>((i + 3 * S) / CPR, (i + 3 * S) % CPR)] = b3;
+    }
+    for (; i < total; i += S) gl[g_swizzle8<D>(i / CPR, i % CPR)] = src[i];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n_keys = a.n_keys;
+  const int64_t n_pass = (n_keys + 16 * NT - 1) / (16 * NT);
+  const int64_t n_waves = (int64_t)gridDim.x * WAVES;
+  int64_t P = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+  if (P >= n_pass) return;                                  // no barrier follows
+  bf16x8 kf[NT][KS];
+  sketch_load_keys<D, NT, SPLIT, false>(kf, a, P, r, g);
+  for (; P < n_pass; P += n_waves) {
+    const bool more = P + n_waves < n_pass;
+    bf16x8 kn[NT][KS];
+    if (more) sketch_load_keys<D, NT, SPLIT, false>(kn, a, P + n_waves, r, g);
+    uint32_t live[NT];                                      // all ones unless the key is zero
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t key = (P * NT + t) * 16 + r;
+      const float ss = sketch_sumsq<D, NT>(kf, t);
+      if (key < n_keys && g == 0) a.norms[key] = f32_to_f16(sqrtf(ss));
+      live[t] = ss > 0.0f ? ~0u : 0u;
+    }
+    for (int c = 0; c < ngrp; ++c) {
+      uint32_t neg[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) neg[t] = 0;
+      // N tile q: MFMA row r is G row 128 c + 8 r + q
+      auto project = [&](int q, f32x4 (&acc)[NT]) {
+        const int row = 128 * c + 8 * r + q;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, gl[g_swizzle8<D>(row, 4 * s + g)]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, kf[t][s], s ? acc[t] : f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                             0, 0, 0);
+        }
+      };
+      // the products of N tile q + 1 are issued before the signs of N tile q are read off
+      f32x4 acc[2][NT];
+      project(0, acc[0]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q < 7) project(q + 1, acc[(q + 1) & 1]);
+        // projection rows 128 c + 8 (4 g + i) + q: sign of row i at bit 8 i + q
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          neg[t] |= (sign_tops(acc[q & 1][t]) >> (7 - q)) & (0x01010101u << q);
+          // taken here: otherwise the sign reads sink into the store branch below and keep
+          // every accumulator of the row group live until then
+          asm volatile("" : "+v"(neg[t]));
+        }
+        __builtin_amdgcn_sched_barrier(0);                  // one N tile in flight: bounds the live accumulators
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int64_t key = (P * NT + t) * 16 + r;
+        if (key < n_keys)
+          *reinterpret_cast<uint32_t*>(a.bits + key * mb + 16 * c + 4 * g) = ~neg[t] & live[t];
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[t][s] = kn[t][s];
     }
   }
 }
@@ -3059,6 +3229,17 @@ hipError_t launch_sketch_d(const pqi::SketchArgs& a, const pqi::LaunchCfg& c, hi
   const int m_pad = (a.m + 15) & ~15;
   const size_t glb = (size_t)m_pad * D * 2;
   const bool g_lds = glb <= (size_t)c.max_lds && glb <= 65536;
+  // m a multiple of 128 with G in LDS: the row-grouped kernel (bits are 16-byte aligned)
+  if constexpr (D <= 256) {
+    if (g_lds && a.m % 128 == 0) {
+      const int64_t n_pass = (a.n_keys + 16 * sketch8_nt<D>() - 1) / (16 * sketch8_nt<D>());
+      const int g8 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count * PQ_SKETCH8_WG_PER_CU,
+                                                                 (n_pass + kSketch8Threads / 64 - 1) / (kSketch8Threads / 64)));
+      if (a.oidx) hipLaunchKernelGGL((qjl_sketch_rows_kernel<D, true>), g8, kSketch8Threads, glb, s, a);
+      else hipLaunchKernelGGL((qjl_sketch_rows_kernel<D, false>), g8, kSketch8Threads, glb, s, a);
+      return hipGetLastError();
+    }
+  }
   const int grid = grid_for(n_tiles, c, PQ_SKETCH_WG_PER_CU);
   if (a.oidx) {
     if (g_lds) hipLaunchKernelGGL((qjl_sketch_kernel<D, true, true>), grid, kSketchThreads, glb, s, a);

@@ -17,7 +17,10 @@ def _case(label):
 
 
 @pytest.mark.parametrize("d,m,n", [(128, 256, 16 * 40 + 7), (64, 64, 16 * 8 + 1), (256, 128, 16 * 9 + 4),
-                                   (512, 512, 16 * 3 + 15), (128, 24, 16 * 5 + 2)])
+                                   (512, 512, 16 * 3 + 15), (128, 24, 16 * 5 + 2),
+                                   # m a multiple of 128 (row-grouped kernel), ragged pass tails
+                                   (64, 128, 16 * 4 * 3 + 17), (64, 512, 16 * 11 + 3), (128, 128, 16 * 4 * 5),
+                                   (128, 256, 5), (256, 128, 16 * 2 * 7 + 31)])
 def test_sketch_parity(d, m, n):
     _case("sketch d=%d m=%d n=%d" % (d, m, n))
     rng = np.random.default_rng(d + m)
