@@ -745,14 +745,14 @@ def main():
     t_qp = timed(torch, quant_packed, args.steps)
     t_dp = timed(torch, dequant_packed, args.steps)
 
-    # the ceiling of a dequantize-shaped stream on this GPU, measured in the same run: torch's
-    # uint8 -> bf16 conversion reads 1 byte and writes 2 per value, the traffic of dequantize
+    # the ceiling of a dequantize-shaped stream on this GPU, measured in the same run: the
+    # library's bandwidth probe reads 1 byte and writes 2 per value, the traffic of dequantize
     # without its arithmetic (over the same 8 rotating buffer sets)
-    st_in = [bs[1] for bs in sets]                   # codes, uint8 [n, d]
-    st_out = [bs[5] for bs in sets]                  # output, bf16 [n, d]
+    st_in = [bs[1].view(-1) for bs in sets]          # codes, uint8 [n d]
+    st_out = [bs[5].view(torch.int16).view(-1) for bs in sets]   # output buffer, 2 bytes a value
 
     def stream(k):
-        st_out[k % N_SETS].copy_(st_in[k % N_SETS])
+        pq.probe_stream(st_in[k % N_SETS], out=st_out[k % N_SETS])
 
     stream(0)
     t_stream = timed(torch, stream, args.steps)

@@ -54,7 +54,11 @@
  *   Projection  `proj` is the Gaussian JL matrix G, m x d row-major bf16.
  *   Bits        QJL sign bits are packed 8 per byte, least significant bit
  *               first; bit value 1 means sign +1, a projection of exactly 0
- *               gives bit 0 (qjl_apply.py, `_qjl_decode_keys`).
+ *               gives bit 0 (qjl_apply.py, `_qjl_decode_keys`): a zero key or
+ *               zero residual gives all-zero bits.  Projections are summed in
+ *               fp32, so a nonzero one that cancels to exactly 0 there lies far
+ *               inside the parity band of the exact value and may read either
+ *               way (the key sketch reads it as +1).
  *   Limits      d in {64, 128, 256, 512} unless an entry point states other
  *               sizes; bits in 1..8; m a multiple of 8 in [8, 1024] (QJL
  *               residual stage and key sketch), a multiple of 64 in [64, 1024]
@@ -460,6 +464,15 @@ int pq_quantize_dense(int d, int bits, int in_dtype, const void* x, int64_t n_bl
                       uint8_t* codes, uint16_t* norms, void* stream);
 int pq_dequantize_dense(int d, int bits, const uint8_t* codes, const uint16_t* norms, int64_t n_blocks,
                         const float* rot, int out_dtype, void* out, void* stream);
+
+/*
+ * Measurement aid, not part of the method: a stream with the memory traffic of dequantize
+ * (one byte read and two written per value) and none of its arithmetic, the ceiling that
+ * dequantize is measured against.  out[i] = in[i] zero-extended to 16 bits, i < n.
+ *   in         n bytes (16-byte aligned);  out  n uint16 (16-byte aligned)
+ * Asynchronous on `stream`, no allocation; PQ_EINVAL for n < 0 or a bad pointer.
+ */
+int pq_probe_stream(const uint8_t* in, uint16_t* out, int64_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,7 @@ def _load():
                                 I),
         "pq_attention_noalloc": ([I, I, I, I, I, L, P, P, P, P, P, P, P, P, L, P, P, P, ctypes.c_float, I, P, P],
                                  I),
+        "pq_probe_stream": ([P, P, L, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -87,7 +88,7 @@ EXPORTS = ("pq_abi_version", "pq_strerror", "pq_last_hip_error", "pq_codebook", 
            "qjl_score", "qjl_score_add", "qjl_outlier_channels", "qjl_sketch_split", "pq_query_prep_bytes",
            "pq_query_prep", "pq_score", "pq_score_packed", "pq_attention_work_bytes", "pq_attention",
            "pq_attention_packed", "pq_quantize_bd", "pq_dequantize_bd", "pq_sphere_codebook",
-           "pq_quantize_dense", "pq_dequantize_dense", "pq_attention_noalloc")
+           "pq_quantize_dense", "pq_dequantize_dense", "pq_attention_noalloc", "pq_probe_stream")
 
 
 def lib():
@@ -615,4 +616,16 @@ def dequantize_dense(codes, norms, d, bits, rot, out_dtype=torch.bfloat16, out=N
     _check(_lib.pq_dequantize_dense(d, bits, _ptr(codes), _ptr(norms), n, _ptr(rot),
                                     PQ_BF16 if out.dtype == torch.bfloat16 else PQ_F32, _ptr(out), _stream()),
            "pq_dequantize_dense")
+    return out
+
+
+def probe_stream(src, out=None):
+    """Bandwidth probe (pq_probe_stream): ``src`` uint8 [n] -> int16 [n], each byte
+    zero-extended; the memory traffic of dequantize with none of its arithmetic."""
+    _dev(src, "src", (torch.uint8,))
+    n = src.numel()
+    if out is None:
+        out = torch.empty((n,), dtype=torch.int16, device=src.device)
+    _dev(out, "out", (torch.int16,), numel=n, device=src.device)
+    _check(_lib.pq_probe_stream(_ptr(src), _ptr(out), n, _stream()), "pq_probe_stream")
     return out

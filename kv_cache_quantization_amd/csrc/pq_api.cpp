@@ -815,6 +815,16 @@ int pq_attention_packed(int d, int bits, int m, int n_heads, int n_q, int64_t n_
                         v_norms, v_signs, n_win, k_win, v_win, q, sm_scale, work, out, 1, stream);
 }
 
+int pq_probe_stream(const uint8_t* in, uint16_t* out, int64_t n, void* stream) {
+  if (n < 0 || n > kMaxElems) return PQ_EINVAL;
+  if (n == 0) return PQ_OK;
+  if (!in || !out || !aligned(in, 16) || !aligned(out, 16)) return PQ_EINVAL;
+  pqi::LaunchCfg cfg;
+  int st = launch_cfg(&cfg);
+  if (st) return st;
+  return hip_status(pqi::launch_stream_probe(in, out, n, cfg, (hipStream_t)stream));
+}
+
 int pq_attention_noalloc(int d, int bits, int m, int n_heads, int n_q, int64_t n_tok, const void* prep,
                          const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl_bits,
                          const uint16_t* k_rnorms, const uint8_t* v_codes, const uint16_t* v_norms,

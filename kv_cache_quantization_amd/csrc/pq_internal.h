@@ -272,5 +272,6 @@ hipError_t launch_dequantize_many(int d, bool out_bf16, const DequantArgs& a, co
 hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
 hipError_t launch_dequantize_dense(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s);
+hipError_t launch_stream_probe(const uint8_t* in, uint16_t* out, int64_t n, const LaunchCfg& c, hipStream_t s);
 
 }  // namespace pqi

@@ -4,6 +4,7 @@
 // with a grid stride, so the per-workgroup set-up (codebook, search grid and
 // projection matrix staged in LDS) is paid once per workgroup.
 #include <algorithm>
+#include <type_traits>
 
 #include "pq_device.h"
 #include "pq_internal.h"
@@ -29,6 +30,9 @@ constexpr int kWaves = kThreads / 64;
 #endif
 #ifndef PQ_LOOKUP_BATCH
 #define PQ_LOOKUP_BATCH 8        // grid lookups of the code decision in flight at once
+#endif
+#ifndef PQ_LOOKUP_BATCH_QJL
+#define PQ_LOOKUP_BATCH_QJL 2    // ... with the QJL stage at d <= 128 (16-byte entries; twice that above)
 #endif
 #ifndef PQ_SKETCH_WG_PER_CU
 #define PQ_SKETCH_WG_PER_CU 2
@@ -471,7 +475,10 @@ struct Quantizer {
     const float rscale = __uint_as_float((uint32_t)(127 + e) << 23);
     const float nr = n * rscale;                                  // the norm on the scaled axis
     const float nsc = f16_to_f32(n16) * rscale;                   // the stored norm, scaled
-    const float a_w = nr > 0.0f ? inv_w / nr : 0.0f;              // scaled coordinate -> grid cells
+    // scaled coordinate -> grid cells (a guess of the cell, the decision below is exact: a
+    // one-ulp reciprocal moves only values within an ulp of a cell edge to the neighbouring
+    // cell, whose entry decides them the same way unless a boundary sits on that edge)
+    const float a_w = nr > 0.0f ? inv_w * __builtin_amdgcn_rcpf(nr) : 0.0f;
 
     if constexpr (IN_BF16) {
       // signs, bf16 -> fp32, the scale and the first butterfly (register bit 0 pairs the two
@@ -510,28 +517,37 @@ struct Quantizer {
     uint32_t cw[E / 4];
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) cw[w] = 0;
+    // PQ_LOOKUP_BATCH grid lookups in flight: a batch issues all its LDS reads before it reads
+    // the first of them (bounds the registers the scheduler may tie up)
+    constexpr int LB = QJL ? (D <= 128 ? PQ_LOOKUP_BATCH_QJL : 2 * PQ_LOOKUP_BATCH_QJL) : PQ_LOOKUP_BATCH;
+    using TE = typename std::conditional<QJL, u32x4, u32x2>::type;
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const float u = __builtin_amdgcn_fmed3f(fmaf(v[j], a_w, offM), kMagic, topM);
-      const uint32_t addr = (__float_as_uint(u) << (PK ? rep_shift : kRepShift)) + lane_off;
-      uint32_t code;
-      if constexpr (QJL) {
-        u32x4 te = *static_cast<const u32x4*>(__builtin_assume_aligned(smem + addr, 16));
-        asm("" : "+v"(te));                // keep the cell as one 16-byte LDS read
-        const bool gt = fmaf(-__uint_as_float(te.x), nr, v[j]) > 0.0f;
-        code = te.y + (gt ? 1u : 0u);
-        const float c = __uint_as_float(gt ? te.w : te.z);
-        v[j] = fmaf(-nsc, c, v[j]);
-        asm volatile("" : "+v"(v[j]));     // keep the residual next to its lookup
-      } else {
-        u32x2 te = *static_cast<const u32x2*>(__builtin_assume_aligned(smem + addr, 8));
-        asm("" : "+v"(te));
-        code = te.y + (fmaf(-__uint_as_float(te.x), nr, v[j]) > 0.0f ? 1u : 0u);
+    for (int j0 = 0; j0 < E; j0 += LB) {
+      TE te[LB];
+#pragma unroll
+      for (int jj = 0; jj < LB; ++jj) {
+        const float u = __builtin_amdgcn_fmed3f(fmaf(v[j0 + jj], a_w, offM), kMagic, topM);
+        const uint32_t addr = (__float_as_uint(u) << (PK ? rep_shift : kRepShift)) + lane_off;
+        te[jj] = *static_cast<const TE*>(__builtin_assume_aligned(smem + addr, sizeof(TE)));
       }
-      const int o = cperm<D>(j);
-      cw[o >> 2] |= code << (8 * (o & 3));
-      // at most 8 grid lookups in flight: bounds the registers the scheduler may tie up
-      if ((j % PQ_LOOKUP_BATCH) == PQ_LOOKUP_BATCH - 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < LB; ++jj) {
+        const int j = j0 + jj;
+        asm("" : "+v"(te[jj]));            // keep the cell as one LDS read of the whole entry
+        uint32_t code;
+        if constexpr (QJL) {
+          const bool gt = fmaf(-__uint_as_float(te[jj].x), nr, v[j]) > 0.0f;
+          code = te[jj].y + (gt ? 1u : 0u);
+          const float c = __uint_as_float(gt ? te[jj].w : te[jj].z);
+          v[j] = fmaf(-nsc, c, v[j]);
+          asm volatile("" : "+v"(v[j]));   // keep the residual next to its lookup
+        } else {
+          code = te[jj].y + (fmaf(-__uint_as_float(te[jj].x), nr, v[j]) > 0.0f ? 1u : 0u);
+        }
+        const int o = cperm<D>(j);
+        cw[o >> 2] |= code << (8 * (o & 3));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // materialise the packed codes here: otherwise the whole decision chain sinks into
     // the store branch below and keeps every lookup result live until then
@@ -576,7 +592,8 @@ struct Quantizer {
 
     if constexpr (QJL) {
       const float rss = sum4(tree_sumsq<E>(v));
-      const float rn = sqrtf(rss) / rscale * inv_sqrt_d;    // ||r|| = ||H D r|| / sqrt(d)
+      // ||r|| = ||H D r|| / sqrt(d); the product with 2^-e is the exact quotient by rscale
+      const float rn = sqrtf(rss) * __uint_as_float((uint32_t)(127 - e) << 23) * inv_sqrt_d;
       if (valid && g == 0) a.rnorms[blk] = f32_to_f16(rn);
     }
   }
@@ -3161,22 +3178,26 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   // sixteen-wave workgroup per CU (four waves per SIMD at <= 128 VGPRs); packed codes hold
   // more registers and run four-wave workgroups, three per CU (three waves per SIMD)
   const size_t grb = (size_t)m_pad * D * 4;
-  if (qjl && base + grb <= (size_t)c.max_lds && base + grb <= 98304 && (mode < 2 || 3 * (base + grb) <= (size_t)c.max_lds)) {
-    const size_t lds = base + grb;
-    if (mode == 2) {
-      const int g4 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count * 3, (n_tiles + 3) / 4));
-      if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, 2, 256, true>), g4, 256, lds, s, a);
-      else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, 2, 256, true>), g4, 256, lds, s, a);
-      return hipGetLastError();
-    }
-    const int g16 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count, (n_tiles + 15) / 16));
+  // (d <= 128: wider blocks hold too many registers at four waves per SIMD)
+  if constexpr (D <= 128) {
+    if (qjl && base + grb <= (size_t)c.max_lds && base + grb <= 98304 &&
+        (mode < 2 || 3 * (base + grb) <= (size_t)c.max_lds)) {
+      const size_t lds = base + grb;
+      if (mode == 2) {
+        const int g4 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count * 3, (n_tiles + 3) / 4));
+        if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, 2, 256, true>), g4, 256, lds, s, a);
+        else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, 2, 256, true>), g4, 256, lds, s, a);
+        return hipGetLastError();
+      }
+      const int g16 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count, (n_tiles + 15) / 16));
 #define PQ_RB_LAUNCH(MODE)                                                                                       \
   if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, MODE, 1024, true>), g16, 1024, lds, s, a); \
   else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, MODE, 1024, true>), g16, 1024, lds, s, a);
-    if (mode == 1) { PQ_RB_LAUNCH(1) }
-    else { PQ_RB_LAUNCH(0) }
+      if (mode == 1) { PQ_RB_LAUNCH(1) }
+      else { PQ_RB_LAUNCH(0) }
 #undef PQ_RB_LAUNCH
-    return hipGetLastError();
+      return hipGetLastError();
+    }
   }
   if (qjl && !g_lds) {
     // residual fragments of every tile of the workgroup beside the search grid
@@ -3308,6 +3329,37 @@ hipError_t launch_attend_d(int bits, const pqi::AttnArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(pq_attend_combine_kernel<D>, a.n_heads * a.n_q, kCombineThreads, (size_t)a.n_parts * 4, s, a);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Bandwidth probe with the traffic of dequantize and none of its arithmetic: every byte in is
+// written back zero-extended to 16 bits (1 byte read, 2 written per value).  Lane i of a load
+// takes 8 consecutive bytes and writes the 16 bytes they become, so every load and store
+// instruction covers one contiguous run (whole lines); four of each in flight per thread,
+// non-temporal as in dequantize.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 widen8(const u32x2& a) {
+  return u32x4{__builtin_amdgcn_perm(0u, a.x, 0x0c010c00u), __builtin_amdgcn_perm(0u, a.x, 0x0c030c02u),
+               __builtin_amdgcn_perm(0u, a.y, 0x0c010c00u), __builtin_amdgcn_perm(0u, a.y, 0x0c030c02u)};
+}
+
+__global__ __launch_bounds__(256) void pq_stream_probe_kernel(const uint8_t* in, uint16_t* out, int64_t n) {
+  const u32x2* src = reinterpret_cast<const u32x2*>(in);
+  u32x4* dst = reinterpret_cast<u32x4*>(out);
+  const int64_t n8 = n >> 3;                                // whole 8-byte runs
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    u32x2 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(widen8(a[u]), dst + i + u * stride);
+  }
+  for (; i < n8; i += stride) __builtin_nontemporal_store(widen8(__builtin_nontemporal_load(src + i)), dst + i);
+  // the last n mod 8 values
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < (n & 7)) out[8 * n8 + t] = in[8 * n8 + t];
 }
 
 }  // namespace
@@ -3463,6 +3515,13 @@ hipError_t launch_dequantize_many(int d, bool out_bf16, const DequantArgs& a, co
 #endif  // PQ_UNIT 5
 
 #if PQ_UNIT < 0 || PQ_UNIT == 2
+hipError_t launch_stream_probe(const uint8_t* in, uint16_t* out, int64_t n, const LaunchCfg& c, hipStream_t s) {
+  const int64_t want = std::max<int64_t>(1, ((n >> 3) + 1023) / 1024);   // four runs per thread
+  const int grid = (int)std::min<int64_t>(want, (int64_t)c.cu_count * 16);
+  hipLaunchKernelGGL(pq_stream_probe_kernel, grid, 256, 0, s, in, out, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_bd(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
   const size_t lds = (size_t)a.d * 5 * sizeof(float);
   const int64_t want = (a.n_blocks + 3) / 4;

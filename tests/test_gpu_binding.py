@@ -96,3 +96,14 @@ def test_score_and_attention_reject():
         pq.attention_noalloc(prep, keys, vals, signs, D, bits, H, n_q, T, out=_t(H * n_q * D - 1, torch.float32))
     with pytest.raises(ValueError):
         pq.query_prep(q, signs, out=_t(16, torch.uint8))
+
+
+@pytest.mark.parametrize("n", [1, 15, 16 * 1023 + 7, 16 * 4096 * 9 + 3])
+def test_probe_stream_widens_every_byte(n):
+    """The bandwidth probe writes every byte zero-extended to 16 bits, ragged tails included."""
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    out = torch.full((n + 8,), -1, dtype=torch.int16, device="cuda")
+    pq.probe_stream(src, out=out[:n])
+    torch.cuda.synchronize()
+    assert torch.equal(out[:n], src.to(torch.int16))
+    assert torch.all(out[n:] == -1)                         # nothing past the end
