@@ -403,6 +403,10 @@ void fill_bd_codebook(int bits, pqi::BdArgs& a) {
   const Codebook& cb = codebook(bits);
   for (int k = 0; k < (1 << bits); ++k) a.cent[k] = (float)cb.c[k];
   for (int k = 0; k + 1 < (1 << bits); ++k) a.beta[k] = (float)cb.beta[k];
+  const pqi::CodecTables& t = make_tables(bits);
+  // a grid of at most 32 two-word cells sits in distinct LDS banks without copies per lane
+  a.ncell = t.ncell; a.half = t.half; a.nrep = t.ncell <= 32 ? 1 : t.nrep;
+  a.cell_w = t.cell_w; a.cell_inv_w = t.cell_inv_w;
 }
 
 }  // namespace

@@ -243,6 +243,10 @@ struct BdArgs {
   float cent[1 << kMaxBits];  // centroids, ascending
   float beta[(1 << kMaxBits) - 1];   // boundaries, ascending (fp32 rounding of the double ones)
   float beta_lo[(1 << kMaxBits) - 1];   // double boundary - beta (the dense rotation's exact recheck)
+  // search grid of the block-diagonal quantize (as CodecTables; the kernel finds each cell's
+  // nearest boundary itself)
+  int ncell, half, nrep;
+  float cell_w, cell_inv_w;
 };
 
 // one tensor of a grouped call (the public pq_tensor record, in device memory)

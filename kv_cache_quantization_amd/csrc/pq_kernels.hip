@@ -2628,25 +2628,34 @@ __global__ __launch_bounds__(kCombineThreads) void pq_attend_combine_kernel(cons
 // barrier is needed between stages), and the per-part factor sqrt(d / d_k) comes from a table
 // shared by the workgroup.  Codes by bisection over the boundaries (count of boundaries below).
 // ------------------------------------------------------------------------------------------
-// R stages of the butterfly of one part (offset o, size s) starting at element bit b0: each
-// lane takes groups of 2^R elements spaced 2^b0 apart, transforms them in registers and writes
-// them back (R stages per LDS round trip instead of one).
-template <int R>
+// Elements live in LDS with 4 words of padding after every 64: element e at word bd_pad(e),
+// so that lanes reading 64 consecutive elements each (the lowest stages) start on different
+// bank groups.
+__device__ __forceinline__ int bd_pad(int e) { return e + ((e >> 6) << 2); }
+// LDS words of one block (per wave)
+__host__ __device__ constexpr int bd_words(int d) { return d + (d >> 6) * 4 + 4; }
+
+// R stages of the butterfly of one part (offset o, size s) starting at element bit b0 >= 6:
+// each lane takes groups of 2^R elements spaced 2^b0 apart (padded spacing 2^b0 + 2^(b0-4)),
+// transforms them in registers and writes them back (R stages per LDS round trip instead of
+// one).
+template <int R, int QG>
 __device__ __forceinline__ void bd_pass(float* xb, int o, int s, int b0, int lane) {
   const int groups = s >> R;
-  // four groups per lane at a time: all their reads are issued before any write
-  for (int t0 = 0; t0 < groups; t0 += 256) {
-    float v[4][1 << R];
-    int i0[4];
+  const int step = (1 << b0) + (1 << (b0 - 4));
+  // QG groups per lane at a time: all their reads are issued before any write
+  for (int t0 = 0; t0 < groups; t0 += 64 * QG) {
+    float v[QG][1 << R];
+    int i0[QG];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QG; ++q) {
       const int t = min(t0 + 64 * q + lane, groups - 1);
-      i0[q] = o + ((t >> b0) << (b0 + R)) + (t & ((1 << b0) - 1));
+      i0[q] = bd_pad(o + ((t >> b0) << (b0 + R)) + (t & ((1 << b0) - 1)));
 #pragma unroll
-      for (int k = 0; k < (1 << R); ++k) v[q][k] = xb[i0[q] + (k << b0)];
+      for (int k = 0; k < (1 << R); ++k) v[q][k] = xb[i0[q] + k * step];
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < QG; ++q)
 #pragma unroll
       for (int h = 1; h < (1 << R); h <<= 1)
 #pragma unroll
@@ -2657,20 +2666,21 @@ __device__ __forceinline__ void bd_pass(float* xb, int o, int s, int b0, int lan
             v[q][k + h] = x0 - x1;
           }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < QG; ++q)
       if (t0 + 64 * q + lane < groups)
 #pragma unroll
-        for (int k = 0; k < (1 << R); ++k) xb[i0[q] + (k << b0)] = v[q][k];
+        for (int k = 0; k < (1 << R); ++k) xb[i0[q] + k * step] = v[q][k];
   }
   __builtin_amdgcn_wave_barrier();
 }
 
 // The first log2(G) stages of a part: each lane takes G consecutive elements (16-byte LDS
-// accesses, no bank conflicts) and transforms them in registers.
+// accesses; the padding puts the lanes of a 16-lane group on different bank groups) and
+// transforms them in registers.
 template <int G>
 __device__ __forceinline__ void bd_pass_low(float* xb, int o, int s, int lane) {
   if (lane < s / G) {
-    float4* p = reinterpret_cast<float4*>(xb + o + lane * G);
+    float4* p = reinterpret_cast<float4*>(xb + bd_pad(o + lane * G));
     float v[G];
 #pragma unroll
     for (int q = 0; q < G / 4; ++q) {
@@ -2695,6 +2705,7 @@ __device__ __forceinline__ void bd_pass_low(float* xb, int o, int s, int lane) {
 // Walsh-Hadamard transform of every power-of-two part of the block in LDS (parts largest
 // first, as d's binary expansion): the six lowest stages per lane in registers, then three
 // stages per pass over groups whose lanes touch consecutive words.
+template <int QG>
 __device__ __forceinline__ void bd_butterflies(float* xb, int d, int lane) {
   int o = 0;
   for (int b = 31 - __builtin_clz((unsigned)d); b >= 0; --b) {
@@ -2705,45 +2716,61 @@ __device__ __forceinline__ void bd_butterflies(float* xb, int d, int lane) {
     } else {
       bd_pass_low<64>(xb, o, s, lane);
       int b0 = 6;
-      for (; b0 + 3 <= b; b0 += 3) bd_pass<3>(xb, o, s, b0, lane);
-      if (b - b0 == 2) bd_pass<2>(xb, o, s, b0, lane);
-      else if (b - b0 == 1) bd_pass<1>(xb, o, s, b0, lane);
+      for (; b0 + 3 <= b; b0 += 3) bd_pass<3, QG>(xb, o, s, b0, lane);
+      if (b - b0 == 2) bd_pass<2, QG>(xb, o, s, b0, lane);
+      else if (b - b0 == 1) bd_pass<1, QG>(xb, o, s, b0, lane);
     }
     o += s;
   }
 }
 
-// weight sqrt(d / d_k) of every element (part k holds it), for the workgroup
-__device__ __forceinline__ void bd_weights(float* wt, int d) {
-  for (int e = threadIdx.x; e < d; e += blockDim.x) {
-    int o = 0, s = 0;
-    for (int b = 31 - __builtin_clz((unsigned)d); b >= 0; --b) {
-      if (!((d >> b) & 1)) continue;
-      s = 1 << b;
-      if (e < o + s) break;
-      o += s;
-    }
-    wt[e] = sqrtf((float)d / (float)s);
+// weight sqrt(d / d_k) of the part (of d's binary expansion, largest first) that holds element e
+__device__ __forceinline__ float bd_part_weight(int e, int d) {
+  int o = 0;
+  for (int b = 31 - __builtin_clz((unsigned)d); b >= 0; --b) {
+    if (!((d >> b) & 1)) continue;
+    const int s = 1 << b;
+    if (e < o + s) return sqrtf((float)d / (float)s);
+    o += s;
   }
+  return 0.0f;
 }
 
-// Global accesses are 16 bytes per lane, every load of a block issued before the first use.
+// Quantize: global accesses are 16 bytes per lane, the next block's loads issued before this
+// block is transformed.  Codes come from the search grid of the N(0,1) codebook (one LDS read
+// per coordinate, as the power-of-two codec): each lane codes four consecutive coordinates at
+// a time (conflict-free 16-byte LDS reads, one 4-byte store of codes, consecutive across lanes).
 template <bool IN_BF16>
-__global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN_BF16 ? 3 : 1)))
+void pq_quantize_bd_kernel(const pqi::BdArgs a) {
   constexpr int CH = IN_BF16 ? 8 : 4;                    // input values per 16-byte load
   constexpr int ML = pqi::kBdMaxD / CH / 64;             // loads per lane per block, at most
-  extern __shared__ float bsm[];                         // [d] weights, then [4 waves][d] blocks
+  constexpr int MG = pqi::kBdMaxD / 256;                 // groups of four coordinates per lane, at most
+  extern __shared__ __align__(16) unsigned char bsmem[];
   const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  __shared__ float beta[(1 << pqi::kMaxBits) - 1];
-  float* wt = bsm;
-  float* xb = bsm + d + wv * d;
-  const int nb = (1 << a.bits) - 1;
-  for (int j = threadIdx.x; j < nb; j += blockDim.x) beta[j] = a.beta[j];
-  bd_weights(wt, d);
+  const int ncell = a.ncell, nrep = a.nrep;
+  uint2* tab = reinterpret_cast<uint2*>(bsmem);           // [ncell][nrep] (boundary, its index)
+  float* gwt = reinterpret_cast<float*>(bsmem + (((size_t)ncell * nrep * 8 + 15) & ~(size_t)15));  // [d / 4]
+  float* xb = gwt + ((d / 4 + 3) & ~3) + wv * bd_words(d);
+  // search grid: cell k (centre (k - half) w) holds the boundary nearest to its centre
+  for (int i = threadIdx.x; i < ncell * nrep; i += blockDim.x) {
+    const float c = (float)(i / nrep - a.half) * a.cell_w;
+    int best = 0;
+    float bd = fabsf(a.beta[0] - c);
+    for (int j = 1; j < (1 << a.bits) - 1; ++j) {
+      const float dd = fabsf(a.beta[j] - c);
+      if (dd < bd) { bd = dd; best = j; }
+    }
+    tab[i] = make_uint2(__float_as_uint(a.beta[best]), (uint32_t)best);
+  }
+  const int rep_shift = nrep == 16 ? 7 : 3;               // log2(bytes per cell)
+  const uint32_t lane_off = (nrep == 16 ? 8u * (uint32_t)(lane & 15) : 0u) - (kMagicBits << rep_shift);
+  const float offM = (float)a.half + kMagic, topM = kMagic + (float)(ncell - 1), inv_w = a.cell_inv_w;
+  // the part weight of each group of four coordinates
+  for (int i = threadIdx.x; i < d / 4; i += blockDim.x) gwt[i] = bd_part_weight(4 * i, d);
   __syncthreads();
-  const int nch = d / CH, n16 = d / 16;
+  const int nch = d / CH, ng = d / 4;
   const int64_t n_waves = (int64_t)gridDim.x * 4;
-  // the next block's input loads while this one is transformed and coded
   auto fetch = [&](int64_t blk, uint4 (&raw)[ML]) {
     const uint4* src = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(a.x) +
                                                       min(blk, a.n_blocks - 1) * d * (IN_BF16 ? 2 : 4));
@@ -2772,7 +2799,7 @@ __global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a
           ss += (double)v[j] * (double)v[j];
           if ((sb >> j) & 1) v[j] = -v[j];
         }
-        float4* dst = reinterpret_cast<float4*>(xb + c * CH);
+        float4* dst = reinterpret_cast<float4*>(xb + bd_pad(c * CH));
 #pragma unroll
         for (int q = 0; q < CH / 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       }
@@ -2781,34 +2808,23 @@ __global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
     const float n = (float)sqrt(ss);
     const float inv = n > 0.0f ? 1.0f / n : 0.0f;
-    bd_butterflies(xb, d, lane);
-    // sixteen consecutive coordinates per lane bisect in lockstep; their codes leave as one
-    // 16-byte store
-#pragma unroll
-    for (int u = 0; u < pqi::kBdMaxD / 16 / 64; ++u) {
+    bd_butterflies<2>(xb, d, lane);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + blk * d);
+#pragma unroll 4
+    for (int u = 0; u < MG; ++u) {
       const int c = lane + 64 * u;
-      if (c < n16) {
-        float y[16];
-        int code[16];
+      if (c < ng) {
+        const float4 xv = *reinterpret_cast<const float4*>(xb + bd_pad(4 * c));
+        const float sc = gwt[c] * inv;
+        const float y[4] = {xv.x * sc, xv.y * sc, xv.z * sc, xv.w * sc};
+        uint32_t pk = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 xv = reinterpret_cast<const float4*>(xb + 16 * c)[q];
-          const float4 wq = reinterpret_cast<const float4*>(wt + 16 * c)[q];
-          y[4 * q] = xv.x * wq.x * inv; y[4 * q + 1] = xv.y * wq.y * inv;
-          y[4 * q + 2] = xv.z * wq.z * inv; y[4 * q + 3] = xv.w * wq.w * inv;
+        for (int j = 0; j < 4; ++j) {
+          const float cu = __builtin_amdgcn_fmed3f(fmaf(y[j], inv_w, offM), kMagic, topM);
+          const uint2 te = tab[((__float_as_uint(cu) << rep_shift) + lane_off) >> 3];
+          pk |= (te.y + (y[j] > __uint_as_float(te.x) ? 1u : 0u)) << (8 * j);
         }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) code[j] = 0;
-        for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (y[j] > beta[code[j] + step - 1]) code[j] += step;
-        uint32_t pk[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          pk[q] = (uint32_t)code[4 * q] | ((uint32_t)code[4 * q + 1] << 8) | ((uint32_t)code[4 * q + 2] << 16) |
-                  ((uint32_t)code[4 * q + 3] << 24);
-        reinterpret_cast<uint4*>(a.codes + blk * d)[c] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        dst[c] = pk;
       }
     }
     if (lane == 0) a.norms[blk] = f32_to_f16((float)sqrt(ss));
@@ -2816,21 +2832,25 @@ __global__ __launch_bounds__(256) void pq_quantize_bd_kernel(const pqi::BdArgs a
   }
 }
 
+// Dequantize: centroids times the part weight into LDS, the butterflies, then sign, scale and
+// the store, 16 bytes per lane.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs a) {
   constexpr int CH = OUT_BF16 ? 8 : 4;                   // output values per 16-byte store
-  extern __shared__ float bsm[];
+  constexpr int ML = pqi::kBdMaxD / 16 / 64;
+  extern __shared__ __align__(16) unsigned char bsmem[];
   const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   __shared__ float cent[1 << pqi::kMaxBits];
-  float* wt = bsm;
-  float* xb = bsm + d + wv * d;
+  float* xb = reinterpret_cast<float*>(bsmem) + wv * bd_words(d);
   const uint32_t cmask = (1u << a.bits) - 1u;
   for (int j = threadIdx.x; j < (1 << a.bits); j += blockDim.x) cent[j] = a.cent[j];
-  bd_weights(wt, d);
+  // the part weight of each 16-code chunk this lane stages
+  float cw[ML];
+#pragma unroll
+  for (int u = 0; u < ML; ++u) cw[u] = bd_part_weight(min(16 * (lane + 64 * u), d - 1), d);
   __syncthreads();
   const int n16 = d / 16, nch = d / CH;
   const int64_t n_waves = (int64_t)gridDim.x * 4;
-  constexpr int ML = pqi::kBdMaxD / 16 / 64;
   // the next block's codes load while this one is transformed and written
   auto fetch = [&](int64_t blk, uint4 (&raw)[ML]) {
     const uint4* src = reinterpret_cast<const uint4*>(a.ccodes + min(blk, a.n_blocks - 1) * d);
@@ -2848,17 +2868,16 @@ __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs
       const int c = lane + 64 * u;
       if (c < n16) {
         const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+        const float wq = cw[u];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 wq = reinterpret_cast<const float4*>(wt + 16 * c)[q];
-          reinterpret_cast<float4*>(xb + 16 * c)[q] =
-              make_float4(cent[w[q] & cmask] * wq.x, cent[(w[q] >> 8) & cmask] * wq.y,
-                          cent[(w[q] >> 16) & cmask] * wq.z, cent[(w[q] >> 24) & cmask] * wq.w);
-        }
+        for (int q = 0; q < 4; ++q)
+          reinterpret_cast<float4*>(xb + bd_pad(16 * c))[q] =
+              make_float4(cent[w[q] & cmask] * wq, cent[(w[q] >> 8) & cmask] * wq,
+                          cent[(w[q] >> 16) & cmask] * wq, cent[(w[q] >> 24) & cmask] * wq);
       }
     }
     fetch(blk + n_waves, raw);
-    bd_butterflies(xb, d, lane);
+    bd_butterflies<4>(xb, d, lane);
     const float scale = f16_to_f32(a.cnorms[blk]) * (1.0f / (float)d);
 #pragma unroll
     for (int u = 0; u < pqi::kBdMaxD / CH / 64; ++u) {
@@ -2867,7 +2886,7 @@ __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs
         float v[CH];
 #pragma unroll
         for (int q = 0; q < CH / 4; ++q) {
-          const float4 xv = reinterpret_cast<const float4*>(xb + CH * c)[q];
+          const float4 xv = reinterpret_cast<const float4*>(xb + bd_pad(CH * c))[q];
           v[4 * q] = xv.x; v[4 * q + 1] = xv.y; v[4 * q + 2] = xv.z; v[4 * q + 3] = xv.w;
         }
         const uint32_t sb = a.signs[(c * CH) >> 3] >> ((c * CH) & 7);
@@ -3523,18 +3542,23 @@ hipError_t launch_stream_probe(const uint8_t* in, uint16_t* out, int64_t n, cons
 }
 
 hipError_t launch_quantize_bd(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
-  const size_t lds = (size_t)a.d * 5 * sizeof(float);
+  // the search grid, the weights of the groups of four, then one block of fp32 per wave
+  const size_t lds = (((size_t)a.ncell * a.nrep * 8 + 15) & ~(size_t)15) +
+                     (size_t)(((a.d / 4 + 3) & ~3) + 4 * bd_words(a.d)) * sizeof(float);
+  if (lds > (size_t)c.max_lds) return hipErrorInvalidConfiguration;
   const int64_t want = (a.n_blocks + 3) / 4;
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
+  const int per_cu = std::max(1, std::min(4, (int)((size_t)c.max_lds / lds)));
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * per_cu));
   if (in_bf16) hipLaunchKernelGGL(pq_quantize_bd_kernel<true>, grid, 256, lds, s, a);
   else hipLaunchKernelGGL(pq_quantize_bd_kernel<false>, grid, 256, lds, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
-  const size_t lds = (size_t)a.d * 5 * sizeof(float);
+  const size_t lds = (size_t)4 * bd_words(a.d) * sizeof(float);      // one padded block of fp32 per wave
   const int64_t want = (a.n_blocks + 3) / 4;
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
+  const int per_cu = std::max(1, std::min(4, (int)((size_t)c.max_lds / (lds + 1024))));
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * per_cu));
   if (out_bf16) hipLaunchKernelGGL(pq_dequantize_bd_kernel<true>, grid, 256, lds, s, a);
   else hipLaunchKernelGGL(pq_dequantize_bd_kernel<false>, grid, 256, lds, s, a);
   return hipGetLastError();
