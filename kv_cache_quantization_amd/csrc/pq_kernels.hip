@@ -783,21 +783,24 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint4* tab = reinterpret_cast<uint4*>(smem);
   uint4* gl = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t full_tiles = a.n_blocks >> 4;
+  const int64_t n_waves = (int64_t)gridDim.x * WAVES;
+  int64_t T = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+  uint4 raw[Q::NR];
+  // the first tile's input is requested before the tables are built: its latency overlaps
+  // that work
+  if constexpr (Q::NR <= 4)
+    if (T < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, threadIdx.x & 15, (threadIdx.x >> 4) & 3);
   build_search_grid(a.t, tab);
   Q q(a, smem, gl);
   if constexpr (QJL && RB) q.stage_rotated(gl, threadIdx.x >> 6, WAVES);
   else if constexpr (QJL && G_LDS) stage_projection_rows<D>(a.proj, a.signs, a.m, 0, (a.m + 15) & ~15, gl);
   __syncthreads();
 
-  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
-  const int64_t full_tiles = a.n_blocks >> 4;
-  const int64_t n_waves = (int64_t)gridDim.x * WAVES;
-  int64_t T = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-  uint4 raw[Q::NR];
   if constexpr (Q::NR <= 4) {
     // the next tile's input is loaded before this tile is processed (16 more registers; a
     // two-buffer unrolled loop would save the copies but pushes the kernel into spills)
-    if (T < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, q.r, q.g);
     for (; T < n_tiles; T += n_waves) {
       uint4 nxt[Q::NR];
       if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(nxt, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
