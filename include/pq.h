@@ -450,7 +450,9 @@ int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norm
  * pq_sphere_codebook: that law's Lloyd-Max centroids (2^bits, ascending) and boundaries
  *   (2^bits - 1) for bits 1..8 and d >= 3, host arrays (either may be NULL).
  * pq_quantize_dense / pq_dequantize_dense:
- *   d          a multiple of 16 up to 128 (PQ_EINVAL / PQ_EUNSUPPORTED otherwise)
+ *   d          a multiple of 16 up to 512 (PQ_EINVAL / PQ_EUNSUPPORTED otherwise); d = 64 and
+ *              128 run on the matrix cores, other d one block per wave with Pi in LDS while it
+ *              fits (d <= 192) and read from global memory above
  *   bits       1 .. 8
  *   rot        Pi, d x d fp32 row-major, device memory (the caller draws it; any orthogonal
  *              matrix is accepted and not checked)

@@ -227,7 +227,7 @@ struct AttnArgs {
 constexpr int kBdMinD = 64, kBdMaxD = 4096;   // d a multiple of 32 in this range
 // Dense rotation (a d x d orthogonal matrix) with the codebook of one sphere coordinate's law:
 // d a multiple of 16 up to 128 (the matrix is held in LDS)
-constexpr int kDenseMaxD = 128;
+constexpr int kDenseMaxD = 512;
 
 struct BdArgs {
   const void* x;              // quantize input [n_blocks][d], fp32 or bf16

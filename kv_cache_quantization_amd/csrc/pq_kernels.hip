@@ -2920,14 +2920,17 @@ __global__ __launch_bounds__(256) void pq_dequantize_bd_kernel(const pqi::BdArgs
 // on that double y against the double boundaries (each held as an fp32 pair beta + beta_lo,
 // 48 significant bits).
 // ------------------------------------------------------------------------------------------
-template <bool IN_BF16>
+// PI_GLOBAL (d whose Pi does not fit in LDS, up to 512): every lane reads its own rows of Pi
+// from global memory (L2-resident: at most 1 MiB) instead of the LDS copy.
+template <bool IN_BF16, bool PI_GLOBAL>
 __global__ __launch_bounds__(256) void pq_quantize_dense_kernel(const pqi::BdArgs a) {
-  extern __shared__ float dsm[];                         // [d][d] Pi^T, then [4 waves][d] blocks
+  extern __shared__ float dsm[];                         // [d][d] Pi^T (in LDS), then [4 waves][d] blocks
   __shared__ double beta[(1 << pqi::kMaxBits) - 1];
   const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float* pit = dsm;
-  float* xb = dsm + d * d + wv * d;
-  for (int idx = threadIdx.x; idx < d * d; idx += blockDim.x) pit[(idx % d) * d + idx / d] = a.rot[idx];
+  float* xb = dsm + (PI_GLOBAL ? 0 : d * d) + wv * d;
+  if constexpr (!PI_GLOBAL)
+    for (int idx = threadIdx.x; idx < d * d; idx += blockDim.x) pit[(idx % d) * d + idx / d] = a.rot[idx];
   for (int j = threadIdx.x; j < (1 << a.bits) - 1; j += blockDim.x) beta[j] = (double)a.beta[j] + (double)a.beta_lo[j];
   __syncthreads();
   const int64_t n_waves = (int64_t)gridDim.x * 4;
@@ -2944,9 +2947,18 @@ __global__ __launch_bounds__(256) void pq_quantize_dense_kernel(const pqi::BdArg
     __builtin_amdgcn_wave_barrier();
     for (int i = lane; i < d; i += 64) {
       double s0 = 0.0, s1 = 0.0;
-      for (int j = 0; j < d; j += 2) {
-        s0 += (double)pit[j * d + i] * (double)xb[j];
-        s1 += (double)pit[(j + 1) * d + i] * (double)xb[j + 1];
+      if constexpr (PI_GLOBAL) {
+        // row i of Pi (rot is 4-byte aligned)
+        const float* row = a.rot + (int64_t)i * d;
+        for (int j = 0; j < d; j += 2) {
+          s0 += (double)row[j] * (double)xb[j];
+          s1 += (double)row[j + 1] * (double)xb[j + 1];
+        }
+      } else {
+        for (int j = 0; j < d; j += 2) {
+          s0 += (double)pit[j * d + i] * (double)xb[j];
+          s1 += (double)pit[(j + 1) * d + i] * (double)xb[j + 1];
+        }
       }
       const double y = (s0 + s1) * inv;
       int code = 0;
@@ -2959,15 +2971,17 @@ __global__ __launch_bounds__(256) void pq_quantize_dense_kernel(const pqi::BdArg
   }
 }
 
-template <bool OUT_BF16>
+// PI_GLOBAL: Pi read from global memory (rows i, consecutive columns across the lanes).
+template <bool OUT_BF16, bool PI_GLOBAL>
 __global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdArgs a) {
-  extern __shared__ float dsm[];                         // [d][d] Pi, then [4 waves][d] centroids
+  extern __shared__ float dsm[];                         // [d][d] Pi (in LDS), then [4 waves][d] centroids
   __shared__ float cent[1 << pqi::kMaxBits];
   const int d = a.d, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  float* pi = dsm;
-  float* cb = dsm + d * d + wv * d;
+  const float* pi = PI_GLOBAL ? a.rot : dsm;
+  float* cb = dsm + (PI_GLOBAL ? 0 : d * d) + wv * d;
   const uint32_t cmask = (1u << a.bits) - 1u;
-  for (int idx = threadIdx.x; idx < d * d; idx += blockDim.x) pi[idx] = a.rot[idx];
+  if constexpr (!PI_GLOBAL)
+    for (int idx = threadIdx.x; idx < d * d; idx += blockDim.x) dsm[idx] = a.rot[idx];
   for (int j = threadIdx.x; j < (1 << a.bits); j += blockDim.x) cent[j] = a.cent[j];
   __syncthreads();
   const int64_t n_waves = (int64_t)gridDim.x * 4;
@@ -3580,11 +3594,18 @@ hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg&
 #undef PQ_DENSE_MFMA
     return hipGetLastError();
   }
-  const size_t lds = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float);
+  // Pi^T in LDS when it fits, else read from global memory
+  const bool pg = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float) > (size_t)c.max_lds;
+  const size_t lds = ((pg ? 0 : (size_t)a.d * a.d) + 4 * (size_t)a.d) * sizeof(float);
   const int64_t want = (a.n_blocks + 3) / 4;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
-  if (in_bf16) hipLaunchKernelGGL(pq_quantize_dense_kernel<true>, grid, 256, lds, s, a);
-  else hipLaunchKernelGGL(pq_quantize_dense_kernel<false>, grid, 256, lds, s, a);
+  if (pg) {
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_dense_kernel<true, true>), grid, 256, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_dense_kernel<false, true>), grid, 256, lds, s, a);
+  } else {
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_dense_kernel<true, false>), grid, 256, lds, s, a);
+    else hipLaunchKernelGGL((pq_quantize_dense_kernel<false, false>), grid, 256, lds, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -3600,11 +3621,17 @@ hipError_t launch_dequantize_dense(bool out_bf16, const BdArgs& a, const LaunchC
 #undef PQ_DENSE_MFMA
     return hipGetLastError();
   }
-  const size_t lds = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float);
+  const bool pg = ((size_t)a.d * a.d + 4 * (size_t)a.d) * sizeof(float) > (size_t)c.max_lds;
+  const size_t lds = ((pg ? 0 : (size_t)a.d * a.d) + 4 * (size_t)a.d) * sizeof(float);
   const int64_t want = (a.n_blocks + 3) / 4;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)c.cu_count * 4));
-  if (out_bf16) hipLaunchKernelGGL(pq_dequantize_dense_kernel<true>, grid, 256, lds, s, a);
-  else hipLaunchKernelGGL(pq_dequantize_dense_kernel<false>, grid, 256, lds, s, a);
+  if (pg) {
+    if (out_bf16) hipLaunchKernelGGL((pq_dequantize_dense_kernel<true, true>), grid, 256, lds, s, a);
+    else hipLaunchKernelGGL((pq_dequantize_dense_kernel<false, true>), grid, 256, lds, s, a);
+  } else {
+    if (out_bf16) hipLaunchKernelGGL((pq_dequantize_dense_kernel<true, false>), grid, 256, lds, s, a);
+    else hipLaunchKernelGGL((pq_dequantize_dense_kernel<false, false>), grid, 256, lds, s, a);
+  }
   return hipGetLastError();
 }
 

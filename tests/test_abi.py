@@ -269,7 +269,7 @@ def test_block_diagonal_entry_points_validate():
     assert lib.pq_dequantize_bd(192, 4, P16, P16, 0, P16, pq.PQ_BF16, P16, NUL) == pq.PQ_OK
 
 
-@pytest.mark.parametrize("d,bits", [(64, 3), (128, 4), (16, 2)])
+@pytest.mark.parametrize("d,bits", [(64, 3), (128, 4), (16, 2), (256, 3), (512, 3), (208, 2)])
 def test_library_sphere_codebook_matches_oracle(d, bits):
     c, b = pq.sphere_codebook(bits, d)
     oc, ob, _ = oracle.dense.beta_codebook(bits, d)
@@ -282,7 +282,7 @@ def test_dense_entry_points_validate():
     q = lambda d=128, bits=4, dt=pq.PQ_BF16, x=P16, n=16, r=P16, c=P16, nm=P16: lib.pq_quantize_dense(
         d, bits, dt, x, n, r, c, nm, NUL)
     assert q(d=100) == pq.PQ_EINVAL and q(d=0) == pq.PQ_EINVAL
-    assert q(d=144) == pq.PQ_EUNSUPPORTED
+    assert q(d=528) == pq.PQ_EUNSUPPORTED and q(d=1024) == pq.PQ_EUNSUPPORTED
     assert q(bits=0) == pq.PQ_EINVAL and q(bits=9) == pq.PQ_EINVAL
     assert q(dt=5) == pq.PQ_EINVAL and q(r=NUL) == pq.PQ_EINVAL and q(c=NUL) == pq.PQ_EINVAL
     assert q(n=0) == pq.PQ_OK

@@ -34,7 +34,9 @@ def _rotation(seed, d):
 
 
 CASES = [(64, 3, 1000, True), (128, 4, 777, True), (128, 5, 64, False), (48, 2, 37, True), (16, 1, 1, False),
-         (128, 3, 16 * 4096 + 5, True)]
+         (128, 3, 16 * 4096 + 5, True),
+         # one block per wave: Pi in LDS (d <= 192), Pi read from global memory (d = 208 .. 512)
+         (192, 4, 50, True), (208, 2, 33, False), (256, 3, 301, True), (512, 3, 77, False), (512, 1, 5, True)]
 
 
 @pytest.mark.parametrize("d,bits,n,bf16", CASES)
@@ -79,7 +81,7 @@ def test_dense_codec(d, bits, n, bf16):
     assert np.all((e16 <= ulp) | (np.abs(o16.float().cpu().numpy() - refd) <= 2e-5 * gn[:, None] * cmax))
 
 
-@pytest.mark.parametrize("d", [128, 64, 48])
+@pytest.mark.parametrize("d", [128, 64, 48, 256])
 def test_dense_tiny_blocks(d):
     """fp32 blocks whose values sit far below 1 (1e-20, 1e-30, and 1e-41, in fp32's subnormal
     range): the codes follow the rotation of the block's direction, as for unit-scale blocks
