@@ -218,7 +218,7 @@ SQ_KERNELS = (
     ("pq_dequantize_kernel<128, true, 0>", "config-2 dequantize", 131072 // 16),
     ("pq_quantize_kernel<256, true, true, true, 1, 512, false>", "config-5 d=256 quantize + QJL (m=256)", 524288 // 16),
     ("pq_quantize_chunked_kernel<512, true, 1>", "config-5 d=512 quantize + QJL (m=512)", 524288 // 16),
-    ("qjl_sketch_kernel<128, true, false>", "config-4 QJL sketch (m=256)", 1048576 // 16),
+    ("qjl_sketch_rows_kernel<128, false>", "config-4 QJL sketch (m=256)", 1048576 // 16),
     ("qjl_score_kernel<4, false>", "config-4 QJL score (4 query heads per KV head)", 1048576 // 16),
     ("pq_score_kernel<256, 3, 4, false>", "config-5 d=256 two-stage score (16 queries)", 524288 // 16),
     ("pq_score_kernel<512, 3, 8, false>", "config-5 d=512 two-stage score (16 queries)", 524288 // 16),
