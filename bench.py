@@ -606,7 +606,7 @@ def dense_leg(pq, synth, torch, steps, warmup):
     return {"dense_config": "[8][65536][128] bf16 (config-5 recipe at d=128), 3-bit sphere-coordinate codebook, "
                             "Haar rotation",
             "dense_quantize_us": round(tq * 1e6, 2), "dense_quantize_hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4),
-            "dense_quantize_fp64_tflops": round(flops / tq / 1e12, 2),
+            "dense_quantize_fp32_mfma_tflops": round(flops / tq / 1e12, 2),
             "dense_dequantize_us": round(td * 1e6, 2), "dense_dequantize_hbm_frac": round(db / td / 1e9 / HBM_PEAK_GBS, 4),
             "dense_dequantize_fp32_tflops": round(flops / td / 1e12, 2)}
 
