@@ -749,13 +749,18 @@ struct Quantizer {
     }
   }
 
+  // the QJL projection of a tile whose codes decide() has taken (rotated basis)
+  __device__ __forceinline__ void project_tile(const float (&v)[E], int64_t T) {
+    u32x4 bhi[KS], blo[KS];
+    rotated_frags(v, bhi, blo);
+    project_rotated(bhi, blo, T);
+  }
+
   __device__ __forceinline__ void tile(const uint4 (&raw)[NR], int64_t T) {
     float v[E];
     decide(raw, T, v);
     if constexpr (QJL && RB) {
-      u32x4 bhi[KS], blo[KS];
-      rotated_frags(v, bhi, blo);
-      project_rotated(bhi, blo, T);
+      project_tile(v, T);
     } else if constexpr (QJL) {
       u32x4 ahi[KS], alo[KS];
       residual_frags(v, ahi, alo);
@@ -794,6 +799,27 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
     if (T < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, threadIdx.x & 15, (threadIdx.x >> 4) & 3);
   build_search_grid(a.t, tab);
   Q q(a, smem, gl);
+  if constexpr (QJL && RB && Q::NR <= 4) {
+    // the search grid first; the rows of G D H are then built (by the first waves) while
+    // every wave takes the codes of its first tile, and only that tile's projection waits
+    // for them
+    __syncthreads();
+    q.stage_rotated(gl, threadIdx.x >> 6, WAVES);
+    uint4 nxt[Q::NR];
+    if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(nxt, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
+    const bool first = T < n_tiles;
+    float v[Q::E];
+    if (first) q.decide(raw, T, v);
+    __syncthreads();
+    if (first) q.project_tile(v, T);
+    for (T += n_waves; T < n_tiles; T += n_waves) {
+#pragma unroll
+      for (int i = 0; i < Q::NR; ++i) raw[i] = nxt[i];
+      if (T + n_waves < n_tiles) load_tile<D, IN_BF16>(nxt, a.x, T + n_waves, a.n_blocks, full_tiles, q.r, q.g);
+      q.tile(raw, T);
+    }
+    return;
+  }
   if constexpr (QJL && RB) q.stage_rotated(gl, threadIdx.x >> 6, WAVES);
   else if constexpr (QJL && G_LDS) stage_projection_rows<D>(a.proj, a.signs, a.m, 0, (a.m + 15) & ~15, gl);
   __syncthreads();
