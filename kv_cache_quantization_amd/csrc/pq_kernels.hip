@@ -2033,7 +2033,6 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, gq = lane >> 4;
   const int64_t T = a.n_tok;
-  const int64_t n_tiles = (T + 15) >> 4;
   const uint8_t* codes = a.codes + (int64_t)grp * T * (PK ? D * BITS / 8 : D);
   const uint16_t* norms = a.norms + (int64_t)grp * T;
   const uint8_t* qbits = QJL ? a.qbits + (int64_t)grp * T * mb : nullptr;
@@ -2049,8 +2048,8 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
     uint32_t qb[(KQB + 1) / 2];
     uint16_t n16, rn16;
   };
-  auto fetch = [&](int64_t tile, Inputs& in) {
-    const int64_t tok = min(tile * 16 + r, T - 1);
+  auto fetch = [&](int64_t tok_u, Inputs& in) {
+    const int64_t tok = min(tok_u, T - 1);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       if constexpr (PK) {
@@ -2065,15 +2064,15 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
     if constexpr (KQT > 0) load_key_bits<KQT>(qbits + tok * mb + (mb >> 2) * gq, true, in.qb);
   };
 
-  const int64_t stride = (int64_t)chunks_per_group * kWaves;
-  int64_t tile = (int64_t)chunk * kWaves + (threadIdx.x >> 6);
-  Inputs nxt;
-  if (tile < n_tiles) fetch(tile, nxt);
-  for (; tile < n_tiles; tile += stride) {
-    const Inputs in = nxt;
-    if (tile + stride < n_tiles) fetch(tile + stride, nxt);   // uniform
-    const int64_t tok = tile * 16 + r;
-    const bool valid = tok < T;
+  // the first term's plane weights and the QJL factor in fp32: the integer sums are exact, and
+  // an fp32 combination of them lies within ~1e-6 of the scores' L1 size
+  float alpha_f[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) alpha_f[p] = (float)a.alpha[p];
+  const float cqf = (float)cq;
+
+  // the scores of the 16 tokens of one tile for this lane's four query rows
+  auto score_tile = [&](const Inputs& in, int64_t tok, float (&val)[4]) {
     i32x4 acc[NP][3];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -2100,6 +2099,8 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
         acc[p][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc[p][1], 0, 0, 0);
         acc[p][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b, acc[p][2], 0, 0, 0);
       }
+      // d = 512: one K chunk's fragments live at a time (two waves per SIMD instead of one)
+      if constexpr (D >= 512) __builtin_amdgcn_sched_barrier(0);
     }
     i32x4 accq[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
     auto qstep = [&](int k, uint32_t w16) {
@@ -2116,27 +2117,63 @@ __global__ __launch_bounds__(kThreads) void pq_score_kernel(const pqi::TwoStageA
       const uint8_t* kb = qbits + min(tok, T - 1) * mb + (mb >> 2) * gq;
       for (int k = 0; k < KQ; ++k) qstep(k, *reinterpret_cast<const uint16_t*>(kb + 2 * k));
     }
-    if (valid) {
-      const double n16 = (double)f16_to_f32(in.n16) / (double)D;
-      const double rn = QJL ? (double)f16_to_f32(in.rn16) * cq : 0.0;
+    const float n16 = f16_to_f32(in.n16) * (1.0f / (float)D);
+    const float rn = QJL ? f16_to_f32(in.rn16) * cqf : 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = 4 * gq + i;
-        if (qi < a.n_q) {
-          // 2 S - isum = sum_e Q_e (2 u_e - 1) is an int32 (|.| <= sum |Q_e| < 2^31): formed in
-          // wrapping 32-bit arithmetic from the limb sums, exact, then one conversion per plane
-          double first = 0.0;
+    for (int i = 0; i < 4; ++i) {
+      const int qi = min(4 * gq + i, 15);
+      // 2 S - isum = sum_e Q_e (2 u_e - 1) is an int32 (|.| <= sum |Q_e| < 2^31): formed in
+      // wrapping 32-bit arithmetic from the limb sums, exact, then one conversion per plane
+      float first = 0.0f;
 #pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            const uint32_t S = 16384u * (uint32_t)acc[p][0][i] + 128u * (uint32_t)acc[p][1][i] + (uint32_t)acc[p][2][i];
-            first += a.alpha[p] * (double)(int)(2u * S - (uint32_t)isum[qi]);
-          }
-          double val = n16 * (double)scale[qi] * first;
-          if constexpr (QJL) {
-            const uint32_t S = 16384u * (uint32_t)accq[0][i] + 128u * (uint32_t)accq[1][i] + (uint32_t)accq[2][i];
-            val += rn * (double)scale[16 + qi] * (double)(int)(2u * S - (uint32_t)isum[16 + qi]);
-          }
-          out[(int64_t)qi * T + tok] = (float)val;
+      for (int p = 0; p < NP; ++p) {
+        const uint32_t S = 16384u * (uint32_t)acc[p][0][i] + 128u * (uint32_t)acc[p][1][i] + (uint32_t)acc[p][2][i];
+        first = fmaf(alpha_f[p], (float)(int)(2u * S - (uint32_t)isum[qi]), first);
+      }
+      float v = n16 * scale[qi] * first;
+      if constexpr (QJL) {
+        const uint32_t S = 16384u * (uint32_t)accq[0][i] + 128u * (uint32_t)accq[1][i] + (uint32_t)accq[2][i];
+        v = fmaf(rn * scale[16 + qi], (float)(int)(2u * S - (uint32_t)isum[16 + qi]), v);
+      }
+      val[i] = v;
+    }
+  };
+
+  // A wave takes 32 tokens at a time as two tiles, the even tokens and the odd tokens, so that
+  // lane (gq, r) ends with tokens 2r and 2r + 1 of its query rows and stores them together:
+  // 16 lanes write a whole 128-byte line of a query row.  One tile's inputs are in flight
+  // while the other is scored.
+  const int64_t n_pairs = (T + 31) >> 5;
+  const int64_t stride = (int64_t)chunks_per_group * kWaves;
+  const bool pairs_aligned = (T & 1) == 0;               // a query row's pair starts 8-byte aligned
+  int64_t pair = (int64_t)chunk * kWaves + (threadIdx.x >> 6);
+  Inputs nxt;
+  if (pair < n_pairs) fetch(32 * pair + 2 * r, nxt);
+  for (; pair < n_pairs; pair += stride) {
+    float val[2][4];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const Inputs in = nxt;
+      if (sub == 0) fetch(32 * pair + 2 * r + 1, nxt);
+      else if (pair + stride < n_pairs) fetch(32 * (pair + stride) + 2 * r, nxt);   // uniform
+      score_tile(in, 32 * pair + 2 * r + sub, val[sub]);
+      // the scores are taken here: otherwise their arithmetic sinks to the paired store below
+      // and keeps every accumulator of the first tile live through the second
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(val[sub][i]));
+      __builtin_amdgcn_sched_barrier(0);                  // one tile's products live at a time
+    }
+    const int64_t tok = 32 * pair + 2 * r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = 4 * gq + i;
+      if (qi < a.n_q) {
+        float* o = out + (int64_t)qi * T + tok;
+        if (pairs_aligned && tok + 1 < T) {
+          *reinterpret_cast<float2*>(o) = make_float2(val[0][i], val[1][i]);
+        } else {
+          if (tok < T) o[0] = val[0][i];
+          if (tok + 1 < T) o[1] = val[1][i];
         }
       }
     }
@@ -3482,9 +3519,9 @@ hipError_t launch_query_prep(const QueryPrepArgs& a, hipStream_t s) {
 
 #if PQ_UNIT < 0 || PQ_UNIT == 3
 hipError_t launch_two_stage(int d, int bits, const TwoStageArgs& a, const LaunchCfg& c, hipStream_t s) {
-  const int64_t n_tiles = (a.n_tok + 15) >> 4;
+  const int64_t n_pairs = (a.n_tok + 31) >> 5;           // a wave takes 32 tokens at a time
   int64_t per_group = ((int64_t)c.cu_count * 2 + a.n_heads - 1) / a.n_heads;
-  const int64_t max_per_group = (n_tiles + kWaves - 1) / kWaves;
+  const int64_t max_per_group = (n_pairs + kWaves - 1) / kWaves;
   if (per_group > max_per_group) per_group = max_per_group;
   if (per_group < 1) per_group = 1;
   const int grid = (int)(per_group * a.n_heads);
