@@ -451,8 +451,11 @@ int pq_dequantize_bd(int d, int bits, const uint8_t* codes, const uint16_t* norm
  *   (2^bits - 1) for bits 1..8 and d >= 3, host arrays (either may be NULL).
  * pq_quantize_dense / pq_dequantize_dense:
  *   d          a multiple of 16 up to 512 (PQ_EINVAL / PQ_EUNSUPPORTED otherwise); d = 64 and
- *              128 run on the matrix cores, other d one block per wave with Pi in LDS while it
- *              fits (d <= 192) and read from global memory above
+ *              128 run on the matrix cores (bf16 blocks with x and codes 16-byte aligned on the
+ *              bf16 ones, Pi split exactly into bf16 parts; otherwise fp32 ones), other d one
+ *              block per wave with Pi in LDS while it fits (d <= 192) and read from global
+ *              memory above.  Every code is the fp64 decision: codes whose fast value lies
+ *              within the kernels' error bound of a boundary are decided again in fp64
  *   bits       1 .. 8
  *   rot        Pi, d x d fp32 row-major, device memory (the caller draws it; any orthogonal
  *              matrix is accepted and not checked)

@@ -898,6 +898,22 @@ int pq_quantize_dense(int d, int bits, int in_dtype, const void* x, int64_t n_bl
     a.beta[k] = (float)cb.beta[k];
     a.beta_lo[k] = (float)(cb.beta[k] - (double)a.beta[k]);
   }
+  // search grid of the matrix-core kernel: cells 0.9 of the smallest boundary gap wide over
+  // [-(max |beta| + w), max |beta| + w] (at most 4096 cells, else the kernel bisects)
+  {
+    const int nb = (1 << bits) - 1;
+    double gap = INFINITY, top = 0.0;
+    for (int k = 0; k + 1 < nb; ++k) gap = std::min(gap, (double)a.beta[k + 1] - (double)a.beta[k]);
+    for (int k = 0; k < nb; ++k) top = std::max(top, std::fabs((double)a.beta[k]));
+    const double w = nb == 1 ? 0.5 : 0.9 * gap;
+    const int half = (int)std::ceil((top + w) / w);
+    if (w > 0.0 && 2 * half + 1 <= 4096) {
+      a.half = half;
+      a.ncell = 2 * half + 1;
+      a.cell_w = (float)w;
+      a.cell_inv_w = (float)(1.0 / w);
+    }
+  }
   return hip_status(pqi::launch_quantize_dense(in_dtype == PQ_BF16, a, cfg, (hipStream_t)stream));
 }
 

@@ -3076,28 +3076,62 @@ __global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdA
 // the double boundaries, as the one-wave kernel.
 constexpr int kDenseQWaves = 8;                         // waves sharing one LDS copy of Pi^T
 
-template <bool IN_BF16, int D>
+template <bool IN_BF16, int D, bool VEC>
 __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kernel(const pqi::BdArgs a) {
   constexpr int PS = D + 16;                             // LDS row stride of Pi^T
+  constexpr int XS = D + 4;                              // LDS row stride of the blocks: rows 4 banks apart
   constexpr int NT = D / 16;
   constexpr float EPS = 2.0f * (float)D / 16777216.0f;   // twice the fp32 sum's error bound
-  extern __shared__ float dsm[];                         // [D][PS] Pi^T, then [waves][16][D] x
+  extern __shared__ __align__(16) float dsm[];           // [D][PS] Pi^T, [waves][16][XS] x, then the grid
   __shared__ float beta[(1 << pqi::kMaxBits) - 1];
   __shared__ double beta_d[(1 << pqi::kMaxBits) - 1];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nb = (1 << a.bits) - 1;
-  float* xs = dsm + D * PS + wv * 16 * D;
+  float* xs = dsm + D * PS + wv * 16 * XS;
+  uint4* gtab = reinterpret_cast<uint4*>(dsm + D * PS + kDenseQWaves * 16 * XS);
   for (int idx = threadIdx.x; idx < D * D; idx += blockDim.x) dsm[(idx % D) * PS + idx / D] = a.rot[idx];
   for (int j = threadIdx.x; j < nb; j += blockDim.x) {
     beta[j] = a.beta[j];
     beta_d[j] = (double)a.beta[j] + (double)a.beta_lo[j];
   }
+  // search grid over the codebook's boundaries (cells narrower than the smallest gap): cell k,
+  // centre (k - half) w, holds its nearest boundary, that boundary's index and the boundaries on
+  // either side of it (+-inf past the ends), so a code and its two enclosing boundaries come
+  // from one 16-byte read
+  const int ncell = a.ncell;
+  for (int i = threadIdx.x; i < ncell; i += blockDim.x) {
+    const float c = (float)(i - a.half) * a.cell_w;
+    int best = 0;
+    float bd = fabsf(a.beta[0] - c);
+    for (int j = 1; j < nb; ++j) {
+      const float dd = fabsf(a.beta[j] - c);
+      if (dd < bd) { bd = dd; best = j; }
+    }
+    gtab[i] = make_uint4(__float_as_uint(a.beta[best]), (uint32_t)best,
+                         __float_as_uint(best > 0 ? a.beta[best - 1] : -INFINITY),
+                         __float_as_uint(best + 1 < nb ? a.beta[best + 1] : INFINITY));
+  }
   __syncthreads();
-  auto decide = [&](float y) {
-    int code = 0;
-    for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
-      if (y > beta[code + step - 1]) code += step;
+  const float offM = (float)a.half + kMagic, topM = kMagic + (float)(ncell - 1), inv_w = a.cell_inv_w;
+  // code of y with its two enclosing boundaries (lo < y <= hi in exact arithmetic)
+  auto decide = [&](float y, float& lo, float& hi) {
+    int code;
+    if (ncell > 0) {
+      const float u = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
+      const uint4 e = gtab[__float_as_uint(u) - kMagicBits];
+      const float bb = __uint_as_float(e.x);
+      const bool gt = y > bb;
+      code = (int)e.y + (gt ? 1 : 0);
+      lo = gt ? bb : __uint_as_float(e.z);
+      hi = gt ? __uint_as_float(e.w) : bb;
+    } else {
+      code = 0;
+      for (int step = 1 << (a.bits - 1); step > 0; step >>= 1)
+        if (y > beta[code + step - 1]) code += step;
+      lo = code > 0 ? beta[code - 1] : -INFINITY;
+      hi = code < nb ? beta[code] : INFINITY;
+    }
     return code;
   };
   auto decide_d = [&](double y) {
@@ -3112,22 +3146,47 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
     // block r of the tile: lane group g stages a quarter of the row in LDS and sums its squares
     const int64_t blk = min(tile * 16 + r, a.n_blocks - 1);
     double ss = 0.0;
-    for (int e = g; e < D; e += 4) {
-      const float v = IN_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[blk * D + e])
-                              : static_cast<const float*>(a.x)[blk * D + e];
-      xs[r * D + e] = v;
-      ss += (double)v * (double)v;
+    if constexpr (VEC) {
+      // 16-byte loads: chunk c = g + 4 u of the row (8 bf16 or 4 fp32 values)
+      constexpr int CH = IN_BF16 ? 8 : 4;
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(a.x) +
+                                                        blk * D * (IN_BF16 ? 2 : 4));
+      uint4 w[D / CH / 4];
+#pragma unroll
+      for (int u = 0; u < D / CH / 4; ++u) w[u] = src[g + 4 * u];
+#pragma unroll
+      for (int u = 0; u < D / CH / 4; ++u) {
+        const int c = g + 4 * u;
+        float v[CH];
+        const uint32_t ww[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          v[j] = IN_BF16 ? ((j & 1) ? bf16_hi(ww[j >> 1]) : bf16_lo(ww[j >> 1])) : __uint_as_float(ww[j]);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) ss += (double)v[j] * (double)v[j];
+        float4* dst = reinterpret_cast<float4*>(xs + r * XS + c * CH);
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
+    } else {
+      for (int e = g; e < D; e += 4) {
+        const float v = IN_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[blk * D + e])
+                                : static_cast<const float*>(a.x)[blk * D + e];
+        xs[r * XS + e] = v;
+        ss += (double)v * (double)v;
+      }
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);                            // the block's sum in all four lanes
     // a block whose norm lies outside [2^-60, 2^60] is staged scaled by 2^-floor(log2 ||x||)
-    // (each lane its own elements); inside that range no fp32 product or sum leaves the
+    // (the four lanes of a block split its elements); inside that range no fp32 product or sum leaves the
     // normal range and the block is used as it is
     const int e0 = ss > 0.0 ? ilogb(sqrt(ss)) : 0;
     const int ex = e0 < -60 || e0 > 60 ? -e0 : 0;
     if (ex != 0) {
       const double scd = ldexp(1.0, ex);
-      for (int e = g; e < D; e += 4) xs[r * D + e] = (float)((double)xs[r * D + e] * scd);
+      __builtin_amdgcn_wave_barrier();
+      for (int e = g; e < D; e += 4) xs[r * XS + e] = (float)((double)xs[r * XS + e] * scd);
     }
     __builtin_amdgcn_wave_barrier();
     f32x4 acc[NT];
@@ -3135,7 +3194,7 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
     for (int s = 0; s < D / 4; ++s) {
-      const float av = xs[r * D + 4 * s + g];
+      const float av = xs[r * XS + 4 * s + g];
       const float* prow = dsm + (4 * s + g) * PS + r;
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, prow[16 * t], acc[t], 0, 0, 0);
@@ -3153,14 +3212,14 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int n = 16 * t + r;
-        float y = acc[t][i] * inv;
-        int code = decide(y);
-        const bool near = (code > 0 && fabsf(y - beta[code - 1]) < EPS) || (code < nb && fabsf(y - beta[code]) < EPS);
-        if (near) {
+        const float y = acc[t][i] * inv;
+        float lo, hi;
+        int code = decide(y, lo, hi);
+        if (fabsf(y - lo) < EPS || fabsf(y - hi) < EPS) {
           double s0 = 0.0, s1 = 0.0;
           for (int j = 0; j < D; j += 2) {
-            s0 += (double)dsm[j * PS + n] * (double)xs[bl * D + j];
-            s1 += (double)dsm[(j + 1) * PS + n] * (double)xs[bl * D + j + 1];
+            s0 += (double)dsm[j * PS + n] * (double)xs[bl * XS + j];
+            s1 += (double)dsm[(j + 1) * PS + n] * (double)xs[bl * XS + j + 1];
           }
           code = decide_d((s0 + s1) * invd);
         }
@@ -3169,6 +3228,260 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
       if (r == 0 && b < a.n_blocks) a.norms[b] = f32_to_f16((float)sqrt(sb));
     }
     __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Quantize bf16 blocks with the dense rotation on the bf16 matrix cores.  Pi is split exactly
+// into three bf16 parts, Pi = hi + mid + lo (each the round-to-nearest of what the parts before
+// it leave, so mid + lo and then hi + (mid + lo) give Pi back exactly in fp32).  A wave takes 16
+// blocks and forms Y^T (d x 16) = (hi + mid) X^T, two 16x16x32 products per K step: lane (r, g)
+// holds block r's values k = 32 u + 8 g .. + 7 straight from its 16-byte loads (the B operand as
+// loaded) and receives y[16 t + 4 g + i] of block r, so each lane decides four consecutive codes
+// of one block per column tile with that block's own 1 / ||x||.  Leaving lo out moves y by at most
+// 2^-16 ||x||; with the fp32 accumulation and normalisation this bounds |y - y_exact| by the
+// kernel's eps.  A code whose y lies within eps of its nearest boundary is queued and decided
+// again in fp64 from the block as loaded (kept in LDS) and Pi = hi + (mid + lo), eight lanes per
+// queued code; the queue is drained when full and at the end of every tile.
+constexpr int kDenseBWaves = 8;
+constexpr int kDenseBQueue = 64;                         // queued codes per wave
+
+template <int D>
+struct DenseBLayout {
+  static constexpr int KC = D / 8;                       // 16-byte k chunks of a row
+  static constexpr int NT = D / 16;                      // column tiles of 16 outputs
+  static constexpr int U = D / 32;                       // K steps of the 16x16x32 product
+  static constexpr int XR = 2 * D + 16;                  // bytes per staged block (rows 4 banks apart)
+  static constexpr int CR = D + 16;                      // bytes per code row
+  static constexpr int CPL = KC / 8;                     // k chunks per lane when 8 lanes share a code
+  static constexpr size_t PART = (size_t)KC * D * 16;    // one bf16 part of Pi as [kc][n] 16-byte chunks
+  static constexpr size_t WAVE = 16 * XR + 16 * CR + kDenseBQueue * 4;
+  static constexpr size_t bytes(int ncell) { return 3 * PART + kDenseBWaves * WAVE + (size_t)ncell * 8; }
+};
+
+// sum of a double over each aligned group of eight lanes (every lane of the group gets it)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double sum8_f64(double v) {
+  v += dpp_f64<0xB1>(v);                                 // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);                                 // quad_perm [2, 3, 0, 1]
+  return v + dpp_f64<0x141>(v);                          // row_half_mirror: the other quad
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kDenseBWaves) void pq_quantize_dense_bf16_kernel(const pqi::BdArgs a, float eps) {
+  using L = DenseBLayout<D>;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  constexpr int NT = L::NT, U = L::U, XR = L::XR, CR = L::CR, KC = L::KC;
+  extern __shared__ __align__(16) unsigned char dsb[];
+  __shared__ double beta_d[(1 << pqi::kMaxBits) - 1];
+  uint4* phi = reinterpret_cast<uint4*>(dsb);
+  uint4* pmid = phi + KC * D;
+  uint4* plo = pmid + KC * D;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  unsigned char* xs = dsb + 3 * L::PART + wv * L::WAVE;  // [16][XR] the wave's blocks as loaded
+  unsigned char* cb = xs + 16 * XR;                       // [16][CR] their codes
+  uint32_t* queue = reinterpret_cast<uint32_t*>(cb + 16 * CR);
+  uint2* gtab = reinterpret_cast<uint2*>(dsb + 3 * L::PART + kDenseBWaves * L::WAVE);
+  const int nb = (1 << a.bits) - 1;
+  // chunk (kc, n) of each part holds Pi[n][8 kc .. 8 kc + 7]
+  for (int idx = threadIdx.x; idx < KC * D; idx += blockDim.x) {
+    const int n = idx / KC, kc = idx % KC;
+    const float* src = a.rot + (size_t)n * D + 8 * kc;
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v0 = src[2 * j], v1 = src[2 * j + 1];
+      h[j] = pack_bf16x2(v0, v1);
+      const float r0 = v0 - bf16_lo(h[j]), r1 = v1 - bf16_hi(h[j]);
+      m[j] = pack_bf16x2(r0, r1);
+      l[j] = pack_bf16x2(r0 - bf16_lo(m[j]), r1 - bf16_hi(m[j]));
+    }
+    phi[kc * D + n] = make_uint4(h[0], h[1], h[2], h[3]);
+    pmid[kc * D + n] = make_uint4(m[0], m[1], m[2], m[3]);
+    plo[kc * D + n] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+  for (int j = threadIdx.x; j < nb; j += blockDim.x) beta_d[j] = (double)a.beta[j] + (double)a.beta_lo[j];
+  // search grid: cell k, centre (k - half) w, holds its nearest boundary and that boundary's
+  // index.  Cells are narrower than 0.9 of the smallest gap and eps is below a twentieth of it,
+  // so a y within eps of any boundary is within eps of its cell's one.
+  const int ncell = a.ncell;
+  for (int i = threadIdx.x; i < ncell; i += blockDim.x) {
+    const float c = (float)(i - a.half) * a.cell_w;
+    int best = 0;
+    float bd = fabsf(a.beta[0] - c);
+    for (int j = 1; j < nb; ++j) {
+      const float dd = fabsf(a.beta[j] - c);
+      if (dd < bd) { bd = dd; best = j; }
+    }
+    gtab[i] = make_uint2(__float_as_uint(a.beta[best]), (uint32_t)best);
+  }
+  __syncthreads();
+  const float offM = (float)a.half + kMagic, topM = kMagic + (float)(ncell - 1), inv_w = a.cell_inv_w;
+  const uint32_t last_cell = (uint32_t)(ncell - 1);
+
+  // decide the queued codes again in fp64: eight lanes per code, CPL chunks of k each
+  auto drain = [&](int cnt) {
+    asm volatile("" ::: "memory");
+    const int G = lane >> 3, j = lane & 7;
+    for (int q0 = 0; q0 < cnt; q0 += 8) {
+      const int qi = q0 + G;
+      const bool valid = qi < cnt;
+      const uint32_t e = queue[valid ? qi : q0];
+      const int b = e & 15, n = (e >> 4) & 127, best = (int)(e >> 11);
+      double dot = 0.0, sq = 0.0;
+#pragma unroll
+      for (int c = 0; c < L::CPL; ++c) {
+        const int kc = j * L::CPL + c;
+        const uint4 xv = *reinterpret_cast<const uint4*>(xs + b * XR + kc * 16);
+        const uint4 hv = phi[kc * D + n], mv = pmid[kc * D + n], lv = plo[kc * D + n];
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w};
+        const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w}, lw[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x0 = bf16_lo(xw[w]), x1 = bf16_hi(xw[w]);
+          const float p0 = bf16_lo(hw[w]) + (bf16_lo(mw[w]) + bf16_lo(lw[w]));   // Pi exactly
+          const float p1 = bf16_hi(hw[w]) + (bf16_hi(mw[w]) + bf16_hi(lw[w]));
+          dot = fma((double)x0, (double)p0, dot);
+          dot = fma((double)x1, (double)p1, dot);
+          sq = fma((double)x0, (double)x0, sq);
+          sq = fma((double)x1, (double)x1, sq);
+        }
+      }
+      dot = sum8_f64(dot);
+      sq = sum8_f64(sq);
+      const double y = sq > 0.0 ? dot / sqrt(sq) : 0.0;
+      const int code = best + (y > beta_d[best] ? 1 : 0);
+      if (valid && j == 0) cb[b * CR + n] = (uint8_t)code;
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t n_waves = (int64_t)gridDim.x * kDenseBWaves;
+  for (int64_t T = (int64_t)blockIdx.x * kDenseBWaves + wv; T < n_tiles; T += n_waves) {
+    const int64_t blk = min(T * 16 + r, a.n_blocks - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + blk * D);
+    uint4 xw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4 v = __builtin_nontemporal_load(src + 4 * u + g);
+      xw[u] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      *reinterpret_cast<uint4*>(xs + r * XR + (4 * u + g) * 16) = xw[u];
+      const uint32_t w4[4] = {xw[u].x, xw[u].y, xw[u].z, xw[u].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[w]), __builtin_bit_cast(bf16x2, w4[w]), ss, false);
+    }
+    ss = sum4(ss);                                       // the block's sum, equal in its four lanes
+    float inv;
+    uint16_t n16;
+    if (ss >= 0x1p-80f && ss <= 0x1p120f) {
+      // fp32 products and sums stay normal for such blocks
+      inv = __builtin_amdgcn_rsqf(ss);
+      n16 = f32_to_f16(sqrtf(ss));
+    } else {
+      // zero, tiny or huge block: its norm in fp64, and the block scaled by 2^-floor(log2 ||x||)
+      // (exact in bf16 but for values far below the norm, whose loss is below 2^-100 ||x||)
+      double sd = 0.0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t w4[4] = {xw[u].x, xw[u].y, xw[u].z, xw[u].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const double v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
+          sd = fma(v0, v0, fma(v1, v1, sd));
+        }
+      }
+      sd += __shfl_xor(sd, 16);
+      sd += __shfl_xor(sd, 32);
+      const double nrm = sqrt(sd);
+      n16 = f32_to_f16((float)nrm);
+      inv = 0.0f;
+      if (sd > 0.0) {
+        const double sc = ldexp(1.0, -ilogb(nrm));
+        inv = (float)(1.0 / (nrm * sc));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          uint32_t w4[4] = {xw[u].x, xw[u].y, xw[u].z, xw[u].w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            w4[w] = pack_bf16x2((float)((double)bf16_lo(w4[w]) * sc), (float)((double)bf16_hi(w4[w]) * sc));
+          xw[u] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+      }
+    }
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bf16x8 xf = __builtin_bit_cast(bf16x8, xw[u]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 h = __builtin_bit_cast(bf16x8, phi[(4 * u + g) * D + 16 * t + r]);
+        const bf16x8 m = __builtin_bit_cast(bf16x8, pmid[(4 * u + g) * D + 16 * t + r]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h, xf, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m, xf, acc[t], 0, 0, 0);
+      }
+    }
+    // codes: lane (r, g) holds y[16 t + 4 g + i] of block r
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t word = 0;
+      bool near[4];
+      uint32_t best[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = acc[t][i] * inv;
+        const float cu = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
+        const uint32_t ci = min(__float_as_uint(cu) - kMagicBits, last_cell);   // NaN stays in the table
+        const uint2 e = gtab[ci];
+        const float bb = __uint_as_float(e.x);
+        word |= (e.y + (y > bb ? 1u : 0u)) << (8 * i);
+        near[i] = fabsf(y - bb) < eps;
+        best[i] = e.y;
+      }
+      *reinterpret_cast<uint32_t*>(cb + r * CR + 16 * t + 4 * g) = word;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(near[i]);
+        if (m) {
+          const int c = __popcll(m);
+          if (cnt + c > kDenseBQueue) {
+            drain(cnt);
+            cnt = 0;
+          }
+          if (near[i]) {
+            const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            queue[pos] = (uint32_t)r | ((uint32_t)(16 * t + 4 * g + i) << 4) | (best[i] << 11);
+          }
+          cnt += c;
+        }
+      }
+    }
+    if (cnt) drain(cnt);
+    asm volatile("" ::: "memory");
+    // whole 16-byte pieces of the tile's code rows
+#pragma unroll
+    for (int c = 0; c < (16 * KC / 2) / 64; ++c) {
+      const int piece = lane + 64 * c, row = piece / (D / 16), col = piece % (D / 16);
+      const int64_t b = T * 16 + row;
+      const uint4 v = *reinterpret_cast<const uint4*>(cb + row * CR + col * 16);
+      if (b < a.n_blocks) *reinterpret_cast<uint4*>(a.codes + b * D + col * 16) = v;
+    }
+    if (g == 0 && T * 16 + r < a.n_blocks) a.norms[T * 16 + r] = n16;
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -3645,15 +3958,47 @@ hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg&
 }
 
 hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  if (in_bf16 && (a.d == 64 || a.d == 128) && ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.codes)) & 15) == 0 &&
+      a.ncell > 0) {
+    // bf16 matrix cores.  |y - y_exact| in units of 2^-24: 2^-16 for the part of Pi left out,
+    // one ulp for each of the 2 d fp32 additions of the accumulation (terms summing to at most
+    // 1.01 ||x||), and the fp32 norm (d / 8 dot2 roundings, the rsqrt, the final product); 10%
+    // on top.  The grid test needs eps under a twentieth of the smallest boundary gap.
+    const double units = 257.0 + 4.04 * a.d + 1.01 * (a.d / 8.0 + 4.0);
+    const float eps = (float)(1.1 * units * 0x1p-24);
+    const int nb = (1 << a.bits) - 1;
+    double gap = INFINITY;
+    for (int k = 0; k + 1 < nb; ++k) gap = std::min(gap, (double)a.beta[k + 1] - (double)a.beta[k]);
+    const size_t lds = a.d == 64 ? DenseBLayout<64>::bytes(a.ncell) : DenseBLayout<128>::bytes(a.ncell);
+    const size_t stat = ((size_t)1 << kMaxBits) * sizeof(double);   // the kernel's fp64 boundaries
+    if (lds + stat <= (size_t)c.max_lds && (nb == 1 || eps < 0.05 * gap)) {
+      const int per_cu = (int)std::max<size_t>(1, (size_t)c.max_lds / (lds + stat));
+      const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+      const int grid = (int)std::max<int64_t>(
+          1, std::min<int64_t>((n_tiles + kDenseBWaves - 1) / kDenseBWaves, (int64_t)c.cu_count * per_cu));
+      if (a.d == 64) hipLaunchKernelGGL((pq_quantize_dense_bf16_kernel<64>), grid, 64 * kDenseBWaves, lds, s, a, eps);
+      else hipLaunchKernelGGL((pq_quantize_dense_bf16_kernel<128>), grid, 64 * kDenseBWaves, lds, s, a, eps);
+      return hipGetLastError();
+    }
+  }
   if (a.d == 64 || a.d == 128) {
-    const size_t lds = ((size_t)a.d * (a.d + 16) + kDenseQWaves * 16 * (size_t)a.d) * sizeof(float);
+    // Pi^T, the waves' blocks and the search grid; without room for the grid the kernel bisects
+    BdArgs g = a;
+    const size_t base = ((size_t)a.d * (a.d + 16) + kDenseQWaves * 16 * (size_t)(a.d + 4)) * sizeof(float);
+    if (base + (size_t)a.ncell * 16 > (size_t)c.max_lds) g.ncell = 0;
+    const size_t lds = base + (size_t)g.ncell * 16;
     const int64_t n_tiles = (a.n_blocks + 15) >> 4;
     const int grid = (int)std::max<int64_t>(
         1, std::min<int64_t>((n_tiles + kDenseQWaves - 1) / kDenseQWaves, (int64_t)c.cu_count * 2));
-#define PQ_DENSE_MFMA(DD)                                                                                             \
-    if (in_bf16) hipLaunchKernelGGL((pq_quantize_dense_mfma_kernel<true, DD>), grid, 64 * kDenseQWaves, lds, s, a);  \
-    else hipLaunchKernelGGL((pq_quantize_dense_mfma_kernel<false, DD>), grid, 64 * kDenseQWaves, lds, s, a);
-    if (a.d == 64) { PQ_DENSE_MFMA(64) } else { PQ_DENSE_MFMA(128) }
+    const bool vec = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;   // 16-byte loads of the rows
+#define PQ_DENSE_MFMA(DD, V)                                                                                             \
+    if (in_bf16) hipLaunchKernelGGL((pq_quantize_dense_mfma_kernel<true, DD, V>), grid, 64 * kDenseQWaves, lds, s, g);  \
+    else hipLaunchKernelGGL((pq_quantize_dense_mfma_kernel<false, DD, V>), grid, 64 * kDenseQWaves, lds, s, g);
+    if (a.d == 64) {
+      if (vec) { PQ_DENSE_MFMA(64, true) } else { PQ_DENSE_MFMA(64, false) }
+    } else {
+      if (vec) { PQ_DENSE_MFMA(128, true) } else { PQ_DENSE_MFMA(128, false) }
+    }
 #undef PQ_DENSE_MFMA
     return hipGetLastError();
   }

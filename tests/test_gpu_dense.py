@@ -108,3 +108,82 @@ def test_dense_tiny_blocks(d):
         assert abs(ref["y"][b, i] - ref["beta"][lo]) < band / math.sqrt(d), "code differs away from a boundary at %s" % ((b, i),)
     assert len(diff) <= max(1, int(1e-6 * gc.size)) + int(np.sum(diff[:, 0] >= 64))
     assert np.all(parity.f16_values(norms) == 0.0)          # below fp16's range
+
+
+def _bf16_grid(e_lo, e_hi):
+    """Every positive bf16 value in [2^e_lo, 2^e_hi)."""
+    return np.array([(1.0 + m / 128.0) * 2.0 ** e for e in range(e_lo, e_hi) for m in range(128)])
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_dense_bf16_codes_near_boundaries(d):
+    """bf16 blocks built so that many rotated coordinates sit between 1e-7 and 1e-4 of a boundary
+    (Pi a signed permutation, a block holds c values +-p and d - c values +-q with p / ||x|| next
+    to a boundary): hundreds of codes per 16-block tile are decided again in fp64, the queue of
+    each wave fills and drains several times per tile, and every code equals the oracle's (its y
+    and the kernel's fp64 y are the same correctly rounded quotient here)."""
+    _case("dense rotation bf16 codes near boundaries d=%d" % d)
+    bits = 3
+    rng = np.random.default_rng(d + 901)
+    _, beta, _ = dense.beta_codebook(bits, d)
+    P = _bf16_grid(0, 1)
+    Q = _bf16_grid(-4, 2)
+    picks = []
+    for bk in beta[beta > 0]:
+        for c in (d // 2, d // 4, d // 8):                  # fewer p values reach larger ratios
+            ratio = P[:, None] / np.sqrt(c * P[:, None] ** 2 + (d - c) * Q[None, :] ** 2)
+            dist = np.abs(ratio - bk)
+            ii, jj = np.nonzero((dist > 1e-7) & (dist < 1e-4))
+            if ii.size >= 16:
+                break
+        assert ii.size >= 16, "no bf16 pair lands next to boundary %r" % bk
+        sel = rng.choice(ii.size, 16, replace=False)
+        picks += [(P[ii[s]], Q[jj[s]], c) for s in sel]
+    n = len(picks) * 2 + 5                                  # ragged last tile
+    x = np.zeros((n, d))
+    for b in range(n):
+        p, q, c = picks[b % len(picks)]
+        row = np.concatenate([np.full(c, p), np.full(d - c, q)]) * rng.choice([-1.0, 1.0], d)
+        x[b] = row[rng.permutation(d)]
+    xu = synth.bf16_from_f32(x.astype(np.float32))
+    assert np.array_equal(synth.bf16_to_f32(xu).astype(np.float64), x)
+    Pi = np.zeros((d, d), np.float32)
+    Pi[np.arange(d), rng.permutation(d)] = rng.choice([-1.0, 1.0], d)
+    codes, norms = pq.quantize_dense(parity.bf16_tensor(xu), d, bits, torch.from_numpy(Pi).cuda())
+    torch.cuda.synchronize()
+    ref = dense.quantize(x, bits, Pi.astype(np.float64))
+    near = np.min(np.abs(ref["y"][:, :, None] - beta[None, None, :]), axis=2) < 1e-4
+    assert near.sum() >= n * d // 8
+    gc = codes.cpu().numpy()
+    bad = np.argwhere(gc != ref["codes"])
+    assert bad.size == 0, "%d codes differ, first at %s" % (len(bad), bad[0])
+    parity.pick_candidate(parity.f16_values(norms), parity.fp16_candidates(ref["norm"]), "dense norms")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_dense_bf16_extreme_blocks(d):
+    """bf16 blocks scaled by 2^-100 (squares below fp32's range), 2^125 (sum of squares above
+    it, norm beyond fp16's), all-zero blocks and unit-scale ones: every code equals the oracle's
+    (the kernel takes such blocks' norms in fp64 and scales them by a power of two before the
+    bf16 products), norms are 0, inf or the oracle's fp16 rounding."""
+    _case("dense rotation bf16 extreme blocks d=%d" % d)
+    bits, n = 3, 16 * 10 + 3
+    rng = np.random.default_rng(d + 555)
+    xf = rng.standard_normal((n, d)).astype(np.float32)
+    xu = synth.bf16_from_f32(xf)
+    x = synth.bf16_to_f32(xu).astype(np.float64)
+    x[0:40] *= 2.0 ** -100
+    x[40:80] *= 2.0 ** 125
+    x[80:100] = 0.0
+    xu = synth.bf16_from_f32(x.astype(np.float32))
+    assert np.array_equal(synth.bf16_to_f32(xu).astype(np.float64), x)
+    Pi = _rotation(d + 17, d)
+    codes, norms = pq.quantize_dense(parity.bf16_tensor(xu), d, bits, torch.from_numpy(Pi).cuda())
+    torch.cuda.synchronize()
+    ref = dense.quantize(x, bits, Pi.astype(np.float64))
+    gc = codes.cpu().numpy()
+    bad = np.argwhere(gc != ref["codes"])
+    assert bad.size == 0, "%d codes differ, first at %s" % (len(bad), bad[0])
+    gn = parity.f16_values(norms)
+    assert np.all(gn[0:40] == 0.0) and np.all(np.isinf(gn[40:80])) and np.all(gn[80:100] == 0.0)
+    parity.pick_candidate(gn[100:], parity.fp16_candidates(ref["norm"][100:]), "dense norms")
