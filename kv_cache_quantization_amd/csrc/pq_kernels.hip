@@ -3485,6 +3485,111 @@ __global__ __launch_bounds__(64 * kDenseBWaves) void pq_quantize_dense_bf16_kern
   }
 }
 
+// Dequantize on the fp16 matrix cores.  2^6 Pi and 2^6 c are split into fp16 hi and lo parts
+// (the scale keeps the lo parts in fp16's normal range; each split leaves at most 2^-22 of the
+// value), and Xhat^T (d x 16) = 2^-12 n16 (Pi^T C^T) is formed from three 16x16x32 products per
+// K step (hi hi, hi lo, lo hi; the lo lo term is below 2^-22 of the sum's terms).  Lane (r, g)
+// builds block r's centroid fragment for rows n = 32 u + 8 g .. + 7 from eight code bytes and
+// receives xhat[16 t + 4 g + i] of block r; the tile goes out through LDS as whole 16-byte
+// pieces of its rows.
+constexpr int kDenseDWaves = 8;
+
+template <int D, bool OUT_BF16>
+struct DenseDLayout {
+  static constexpr int NC = D / 8;                       // 16-byte n chunks of a column
+  static constexpr int OR = D * (OUT_BF16 ? 2 : 4) + 16; // bytes per staged output row
+  static constexpr size_t PART = (size_t)NC * D * 16;    // one fp16 part of 2^6 Pi^T as [nc][k] chunks
+  static constexpr size_t bytes() { return 2 * PART + (size_t)kDenseDWaves * 16 * OR; }
+};
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * kDenseDWaves) void pq_dequantize_dense_f16_kernel(const pqi::BdArgs a) {
+  using L = DenseDLayout<D, OUT_BF16>;
+  constexpr int NC = L::NC, NT = D / 16, U = D / 32, OR = L::OR;
+  constexpr int PIECES = D * (OUT_BF16 ? 2 : 4) / 16;    // 16-byte pieces of an output row
+  extern __shared__ __align__(16) unsigned char dsd[];
+  __shared__ uint32_t chl[1 << pqi::kMaxBits];           // 2^6 c as fp16 hi | lo << 16
+  uint4* qhi = reinterpret_cast<uint4*>(dsd);
+  uint4* qlo = qhi + NC * D;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  unsigned char* stg = dsd + 2 * L::PART + wv * 16 * OR;
+  // chunk (nc, k) holds 2^6 Pi[8 nc .. 8 nc + 7][k]
+  for (int idx = threadIdx.x; idx < NC * D; idx += blockDim.x) {
+    const int nc = idx / D, k = idx % D;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v0 = 64.0f * a.rot[(size_t)(8 * nc + 2 * j) * D + k];
+      const float v1 = 64.0f * a.rot[(size_t)(8 * nc + 2 * j + 1) * D + k];
+      const uint16_t h0 = f32_to_f16(v0), h1 = f32_to_f16(v1);
+      h[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      l[j] = (uint32_t)f32_to_f16(v0 - f16_to_f32(h0)) | ((uint32_t)f32_to_f16(v1 - f16_to_f32(h1)) << 16);
+    }
+    qhi[idx] = make_uint4(h[0], h[1], h[2], h[3]);
+    qlo[idx] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+  for (int j = threadIdx.x; j < (1 << a.bits); j += blockDim.x) {
+    const float v = 64.0f * a.cent[j];
+    const uint16_t h = f32_to_f16(v);
+    chl[j] = (uint32_t)h | ((uint32_t)f32_to_f16(v - f16_to_f32(h)) << 16);
+  }
+  __syncthreads();
+  const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+  const int64_t n_waves = (int64_t)gridDim.x * kDenseDWaves;
+  for (int64_t T = (int64_t)blockIdx.x * kDenseDWaves + wv; T < n_tiles; T += n_waves) {
+    const int64_t blk = min(T * 16 + r, a.n_blocks - 1);
+    uint2 cw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cw[u] = *reinterpret_cast<const uint2*>(a.ccodes + blk * D + 32 * u + 8 * g);
+    const float scale = f16_to_f32(a.cnorms[blk]) * 0x1p-12f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = chl[((j < 4 ? cw[u].x : cw[u].y) >> (8 * (j & 3))) & 0xff];
+      uint32_t bh[4], bl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bh[j] = __builtin_amdgcn_perm(e[2 * j + 1], e[2 * j], 0x05040100u);   // the two hi halves
+        bl[j] = __builtin_amdgcn_perm(e[2 * j + 1], e[2 * j], 0x07060302u);   // the two lo halves
+      }
+      const f16x8 fh = __builtin_bit_cast(f16x8, make_uint4(bh[0], bh[1], bh[2], bh[3]));
+      const f16x8 fl = __builtin_bit_cast(f16x8, make_uint4(bl[0], bl[1], bl[2], bl[3]));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const f16x8 ah = __builtin_bit_cast(f16x8, qhi[(4 * u + g) * D + 16 * t + r]);
+        const f16x8 al = __builtin_bit_cast(f16x8, qlo[(4 * u + g) * D + 16 * t + r]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fh, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, fl, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, fh, acc[t], 0, 0, 0);
+      }
+    }
+    // lane (r, g) holds xhat[16 t + 4 g + i] of block r
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float v0 = acc[t][0] * scale, v1 = acc[t][1] * scale, v2 = acc[t][2] * scale, v3 = acc[t][3] * scale;
+      if constexpr (OUT_BF16)
+        *reinterpret_cast<uint2*>(stg + r * OR + (16 * t + 4 * g) * 2) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+      else
+        *reinterpret_cast<float4*>(stg + r * OR + (16 * t + 4 * g) * 4) = make_float4(v0, v1, v2, v3);
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < 16 * PIECES / 64; ++c) {
+      const int piece = lane + 64 * c, row = piece / PIECES, col = piece % PIECES;
+      const int64_t b = T * 16 + row;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + row * OR + col * 16);
+      if (b < a.n_blocks)
+        *reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.out) + (b * D) * (OUT_BF16 ? 2 : 4) + col * 16) = v;
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
 // Dequantize on the matrix cores: a wave takes 16 blocks, Xhat (16 x d) = C (16 x d) Pi with
 // v_mfma_f32_16x16x4f32 (fp32 products and sums; the centroids are fp32 exact).  K step s takes
 // k = 4 s + g in lane group g; Pi sits in LDS with a row stride of d + 16 words, so the four lane
@@ -4018,6 +4123,24 @@ hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg&
 }
 
 hipError_t launch_dequantize_dense(bool out_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
+  if ((a.d == 64 || a.d == 128) && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0) {
+    size_t lds;
+    if (a.d == 64) lds = out_bf16 ? DenseDLayout<64, true>::bytes() : DenseDLayout<64, false>::bytes();
+    else lds = out_bf16 ? DenseDLayout<128, true>::bytes() : DenseDLayout<128, false>::bytes();
+    const size_t stat = ((size_t)1 << kMaxBits) * sizeof(uint32_t);
+    if (lds + stat <= (size_t)c.max_lds) {
+      const int per_cu = (int)std::max<size_t>(1, (size_t)c.max_lds / (lds + stat));
+      const int64_t n_tiles = (a.n_blocks + 15) >> 4;
+      const int grid = (int)std::max<int64_t>(
+          1, std::min<int64_t>((n_tiles + kDenseDWaves - 1) / kDenseDWaves, (int64_t)c.cu_count * per_cu));
+#define PQ_DENSE_F16(DD)                                                                                               \
+      if (out_bf16) hipLaunchKernelGGL((pq_dequantize_dense_f16_kernel<DD, true>), grid, 64 * kDenseDWaves, lds, s, a); \
+      else hipLaunchKernelGGL((pq_dequantize_dense_f16_kernel<DD, false>), grid, 64 * kDenseDWaves, lds, s, a);
+      if (a.d == 64) { PQ_DENSE_F16(64) } else { PQ_DENSE_F16(128) }
+#undef PQ_DENSE_F16
+      return hipGetLastError();
+    }
+  }
   if (a.d == 64 || a.d == 128) {
     const size_t lds = (size_t)a.d * (a.d + 16) * sizeof(float);
     const int64_t n_tiles = (a.n_blocks + 15) >> 4;
