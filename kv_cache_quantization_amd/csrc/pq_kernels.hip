@@ -3240,8 +3240,9 @@ __global__ __launch_bounds__(64 * kDenseQWaves) void pq_quantize_dense_mfma_kern
 // of one block per column tile with that block's own 1 / ||x||.  Leaving lo out moves y by at most
 // 2^-16 ||x||; with the fp32 accumulation and normalisation this bounds |y - y_exact| by the
 // kernel's eps.  A code whose y lies within eps of its nearest boundary is queued and decided
-// again in fp64 from the block as loaded (kept in LDS) and Pi = hi + (mid + lo), eight lanes per
-// queued code; the queue is drained when full and at the end of every tile.
+// again in fp64 from the block as loaded (kept in LDS) and Pi = hi + (mid + lo), d / 8 lanes per
+// queued code; after a tile's decisions its near codes go to the queue, which is drained when the
+// next round of them may not fit and at the end.
 constexpr int kDenseBWaves = 8;
 constexpr int kDenseBQueue = 64;                         // queued codes per wave
 
@@ -3252,23 +3253,26 @@ struct DenseBLayout {
   static constexpr int U = D / 32;                       // K steps of the 16x16x32 product
   static constexpr int XR = 2 * D + 16;                  // bytes per staged block (rows 4 banks apart)
   static constexpr int CR = D + 16;                      // bytes per code row
-  static constexpr int CPL = KC / 8;                     // k chunks per lane when 8 lanes share a code
   static constexpr size_t PART = (size_t)KC * D * 16;    // one bf16 part of Pi as [kc][n] 16-byte chunks
   static constexpr size_t WAVE = 16 * XR + 16 * CR + kDenseBQueue * 4;
   static constexpr size_t bytes(int ncell) { return 3 * PART + kDenseBWaves * WAVE + (size_t)ncell * 8; }
 };
 
-// sum of a double over each aligned group of eight lanes (every lane of the group gets it)
+// sum of a double over each aligned group of N lanes (every lane of the group gets it)
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
   const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
   return __hiloint2double(hi, lo);
 }
-__device__ __forceinline__ double sum8_f64(double v) {
+template <int N>
+__device__ __forceinline__ double sum_lanes_f64(double v) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
   v += dpp_f64<0xB1>(v);                                 // quad_perm [1, 0, 3, 2]
   v += dpp_f64<0x4E>(v);                                 // quad_perm [2, 3, 0, 1]
-  return v + dpp_f64<0x141>(v);                          // row_half_mirror: the other quad
+  v += dpp_f64<0x141>(v);                                // row_half_mirror: the other quad
+  if constexpr (N == 16) v += dpp_f64<0x140>(v);         // row_mirror: the other half row
+  return v;
 }
 
 template <int D>
@@ -3324,54 +3328,67 @@ __global__ __launch_bounds__(64 * kDenseBWaves) void pq_quantize_dense_bf16_kern
   const float offM = (float)a.half + kMagic, topM = kMagic + (float)(ncell - 1), inv_w = a.cell_inv_w;
   const uint32_t last_cell = (uint32_t)(ncell - 1);
 
-  // decide the queued codes again in fp64: eight lanes per code, CPL chunks of k each
+  // decide the queued codes again in fp64: KC lanes per code, one 8-value chunk of k each.
+  // With best the index of the boundary b next to y, the code is best + (y > b), and y > b is
+  // taken from the sign of dot and of b and from dot^2 against b^2 ||x||^2 (no root or quotient)
   auto drain = [&](int cnt) {
     asm volatile("" ::: "memory");
-    const int G = lane >> 3, j = lane & 7;
-    for (int q0 = 0; q0 < cnt; q0 += 8) {
+    constexpr int PER = 64 / KC;                         // codes per pass
+    const int G = lane / KC, j = lane % KC;
+    for (int q0 = 0; q0 < cnt; q0 += PER) {
       const int qi = q0 + G;
       const bool valid = qi < cnt;
       const uint32_t e = queue[valid ? qi : q0];
-      const int b = e & 15, n = (e >> 4) & 127, best = (int)(e >> 11);
+      const int b = e & 15, n = (e >> 4) & 127;
+      const int best = (int)cb[b * CR + n] - (int)(e >> 11);   // the fast code less its side bit
+      const double bd = beta_d[best];
+      const uint4 xv = *reinterpret_cast<const uint4*>(xs + b * XR + j * 16);
+      const uint4 hv = phi[j * D + n], mv = pmid[j * D + n], lv = plo[j * D + n];
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w};
+      const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w}, lw[4] = {lv.x, lv.y, lv.z, lv.w};
       double dot = 0.0, sq = 0.0;
 #pragma unroll
-      for (int c = 0; c < L::CPL; ++c) {
-        const int kc = j * L::CPL + c;
-        const uint4 xv = *reinterpret_cast<const uint4*>(xs + b * XR + kc * 16);
-        const uint4 hv = phi[kc * D + n], mv = pmid[kc * D + n], lv = plo[kc * D + n];
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, hw[4] = {hv.x, hv.y, hv.z, hv.w};
-        const uint32_t mw[4] = {mv.x, mv.y, mv.z, mv.w}, lw[4] = {lv.x, lv.y, lv.z, lv.w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float x0 = bf16_lo(xw[w]), x1 = bf16_hi(xw[w]);
-          const float p0 = bf16_lo(hw[w]) + (bf16_lo(mw[w]) + bf16_lo(lw[w]));   // Pi exactly
-          const float p1 = bf16_hi(hw[w]) + (bf16_hi(mw[w]) + bf16_hi(lw[w]));
-          dot = fma((double)x0, (double)p0, dot);
-          dot = fma((double)x1, (double)p1, dot);
-          sq = fma((double)x0, (double)x0, sq);
-          sq = fma((double)x1, (double)x1, sq);
-        }
+      for (int w = 0; w < 4; ++w) {
+        const float x0 = bf16_lo(xw[w]), x1 = bf16_hi(xw[w]);
+        const float p0 = bf16_lo(hw[w]) + (bf16_lo(mw[w]) + bf16_lo(lw[w]));   // Pi exactly
+        const float p1 = bf16_hi(hw[w]) + (bf16_hi(mw[w]) + bf16_hi(lw[w]));
+        dot = fma((double)x0, (double)p0, dot);
+        dot = fma((double)x1, (double)p1, dot);
+        sq = fma((double)x0, (double)x0, sq);
+        sq = fma((double)x1, (double)x1, sq);
       }
-      dot = sum8_f64(dot);
-      sq = sum8_f64(sq);
-      const double y = sq > 0.0 ? dot / sqrt(sq) : 0.0;
-      const int code = best + (y > beta_d[best] ? 1 : 0);
-      if (valid && j == 0) cb[b * CR + n] = (uint8_t)code;
+      dot = sum_lanes_f64<KC>(dot);
+      sq = sum_lanes_f64<KC>(sq);
+      const double lhs = dot * dot, rhs = bd * bd * sq;
+      bool gt;
+      if (sq == 0.0) gt = 0.0 > bd;                      // y = 0
+      else if (dot >= 0.0) gt = bd < 0.0 || lhs > rhs;
+      else gt = bd < 0.0 && lhs < rhs;
+      if (valid && j == 0) cb[b * CR + n] = (uint8_t)(best + (gt ? 1 : 0));
     }
     asm volatile("" ::: "memory");
   };
 
   const int64_t n_tiles = (a.n_blocks + 15) >> 4;
   const int64_t n_waves = (int64_t)gridDim.x * kDenseBWaves;
-  for (int64_t T = (int64_t)blockIdx.x * kDenseBWaves + wv; T < n_tiles; T += n_waves) {
+  // block r of tile T, chunks k = 32 u + 8 g .. + 7 (the next tile's are loaded while this
+  // tile's codes are decided)
+  auto load_tile_x = [&](int64_t T, uint4 (&xw)[U]) {
     const int64_t blk = min(T * 16 + r, a.n_blocks - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + blk * D);
-    uint4 xw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const u32x4 v = __builtin_nontemporal_load(src + 4 * u + g);
       xw[u] = make_uint4(v[0], v[1], v[2], v[3]);
     }
+  };
+  uint4 xn[U];
+  int64_t T = (int64_t)blockIdx.x * kDenseBWaves + wv;
+  if (T < n_tiles) load_tile_x(T, xn);
+  for (; T < n_tiles; T += n_waves) {
+    uint4 xw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) xw[u] = xn[u];
     float ss = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -3419,9 +3436,11 @@ __global__ __launch_bounds__(64 * kDenseBWaves) void pq_quantize_dense_bf16_kern
         }
       }
     }
-    f32x4 acc[NT];
+    // hi and mid products in accumulators of their own: the rounding of the mid sum is 2^-8
+    // of the hi sum's
+    f32x4 acc[NT], accm[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NT; ++t) acc[t] = accm[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bf16x8 xf = __builtin_bit_cast(bf16x8, xw[u]);
@@ -3430,47 +3449,66 @@ __global__ __launch_bounds__(64 * kDenseBWaves) void pq_quantize_dense_bf16_kern
         const bf16x8 h = __builtin_bit_cast(bf16x8, phi[(4 * u + g) * D + 16 * t + r]);
         const bf16x8 m = __builtin_bit_cast(bf16x8, pmid[(4 * u + g) * D + 16 * t + r]);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h, xf, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m, xf, acc[t], 0, 0, 0);
+        accm[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m, xf, accm[t], 0, 0, 0);
       }
     }
-    // codes: lane (r, g) holds y[16 t + 4 g + i] of block r
-    int cnt = 0;
+    if (T + n_waves < n_tiles) load_tile_x(T + n_waves, xn);
+    // codes: lane (r, g) holds y[16 t + 4 g + i] of block r.  Element e = 4 t + i of the lane
+    // is bit 31 - e of near (within eps of its cell's boundary) and of side (above it).
+    // the grid lookups of two column tiles are issued together, then used
+    uint32_t near = 0, side = 0;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      uint32_t word = 0;
-      bool near[4];
-      uint32_t best[4];
+    for (int t0 = 0; t0 < NT; t0 += 2) {
+      float y[2][4];
+      uint2 e[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float y = acc[t][i] * inv;
-        const float cu = __builtin_amdgcn_fmed3f(fmaf(y, inv_w, offM), kMagic, topM);
-        const uint32_t ci = min(__float_as_uint(cu) - kMagicBits, last_cell);   // NaN stays in the table
-        const uint2 e = gtab[ci];
-        const float bb = __uint_as_float(e.x);
-        word |= (e.y + (y > bb ? 1u : 0u)) << (8 * i);
-        near[i] = fabsf(y - bb) < eps;
-        best[i] = e.y;
-      }
-      *reinterpret_cast<uint32_t*>(cb + r * CR + 16 * t + 4 * g) = word;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint64_t m = __builtin_amdgcn_ballot_w64(near[i]);
-        if (m) {
-          const int c = __popcll(m);
-          if (cnt + c > kDenseBQueue) {
-            drain(cnt);
-            cnt = 0;
-          }
-          if (near[i]) {
-            const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            queue[pos] = (uint32_t)r | ((uint32_t)(16 * t + 4 * g + i) << 4) | (best[i] << 11);
-          }
-          cnt += c;
+        for (int i = 0; i < 4; ++i) {
+          y[tt][i] = (acc[t0 + tt][i] + accm[t0 + tt][i]) * inv;
+          const float cu = __builtin_amdgcn_fmed3f(fmaf(y[tt][i], inv_w, offM), kMagic, topM);
+          const uint32_t ci = min(__float_as_uint(cu) - kMagicBits, last_cell);   // NaN stays in the table
+          e[tt][i] = gtab[ci];
         }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float bb = __uint_as_float(e[tt][i].x);
+          const uint32_t gt = y[tt][i] > bb ? 1u : 0u;
+          word |= (e[tt][i].y + gt) << (8 * i);
+          near = 2 * near + (fabsf(y[tt][i] - bb) < eps ? 1u : 0u);
+          side = 2 * side + gt;
+        }
+        *reinterpret_cast<uint32_t*>(cb + r * CR + 16 * (t0 + tt) + 4 * g) = word;
       }
     }
-    if (cnt) drain(cnt);
+    near <<= 32 - 4 * NT;
+    side <<= 32 - 4 * NT;
+    // queue the near codes, one per lane per round, draining whenever the next round may not fit
+    if (__builtin_amdgcn_ballot_w64(near != 0)) {
+      int cnt = 0;
+      for (;;) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(near != 0);
+        if (!m) break;
+        if (cnt + __popcll(m) > kDenseBQueue) {
+          drain(cnt);
+          cnt = 0;
+        }
+        if (near) {
+          const int e = __builtin_clz(near);
+          near &= ~(0x80000000u >> e);
+          const uint32_t gt = (side >> (31 - e)) & 1u;
+          const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          queue[pos] = (uint32_t)r | ((uint32_t)(16 * (e >> 2) + 4 * g + (e & 3)) << 4) | (gt << 11);
+        }
+        cnt += __popcll(m);
+      }
+      drain(cnt);
+    }
     asm volatile("" ::: "memory");
     // whole 16-byte pieces of the tile's code rows
 #pragma unroll
@@ -4065,11 +4103,12 @@ hipError_t launch_dequantize_bd(bool out_bf16, const BdArgs& a, const LaunchCfg&
 hipError_t launch_quantize_dense(bool in_bf16, const BdArgs& a, const LaunchCfg& c, hipStream_t s) {
   if (in_bf16 && (a.d == 64 || a.d == 128) && ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.codes)) & 15) == 0 &&
       a.ncell > 0) {
-    // bf16 matrix cores.  |y - y_exact| in units of 2^-24: 2^-16 for the part of Pi left out,
-    // one ulp for each of the 2 d fp32 additions of the accumulation (terms summing to at most
-    // 1.01 ||x||), and the fp32 norm (d / 8 dot2 roundings, the rsqrt, the final product); 10%
-    // on top.  The grid test needs eps under a twentieth of the smallest boundary gap.
-    const double units = 257.0 + 4.04 * a.d + 1.01 * (a.d / 8.0 + 4.0);
+    // bf16 matrix cores.  |y - y_exact| in units of 2^-24 ||x||: 2^-16 for the part of Pi left
+    // out; one ulp for each of the d additions of the hi accumulation (terms summing to at most
+    // 1.004 ||x||) and of the mid one (2^-8 of that), one for their sum; and the fp32 norm (d / 8
+    // dot2 roundings, the sum over four lanes, the rsqrt, the final product).  10% on top.  The
+    // grid test needs eps under a twentieth of the smallest boundary gap.
+    const double units = 257.0 + 2.016 * a.d + 2.0 + 1.01 * (a.d / 8.0 + 6.0);
     const float eps = (float)(1.1 * units * 0x1p-24);
     const int nb = (1 << a.bits) - 1;
     double gap = INFINITY;
