@@ -602,13 +602,18 @@ def dense_leg(pq, synth, torch, steps, warmup):
     tq, td = timed(torch, quant, steps), timed(torch, dequant, steps)
     qb = n * d * 2 + n * d + n * 2
     db = n * d + n * 2 + n * d * 2
+    # matrix-core work as issued: quantize two bf16 products per K step (the hi and mid parts
+    # of Pi), dequantize three fp16 products (hi hi, hi lo, lo hi); both against the 2.5 PFLOP/s
+    # dense bf16 / fp16 peak
     flops = 2.0 * n * d * d
     return {"dense_config": "[8][65536][128] bf16 (config-5 recipe at d=128), 3-bit sphere-coordinate codebook, "
                             "Haar rotation",
             "dense_quantize_us": round(tq * 1e6, 2), "dense_quantize_hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4),
-            "dense_quantize_fp32_mfma_tflops": round(flops / tq / 1e12, 2),
+            "dense_quantize_bf16_mfma_tflops": round(2 * flops / tq / 1e12, 2),
+            "dense_quantize_bf16_mfma_frac": round(2 * flops / tq / 1e12 / BF16_PEAK_TFLOPS, 4),
             "dense_dequantize_us": round(td * 1e6, 2), "dense_dequantize_hbm_frac": round(db / td / 1e9 / HBM_PEAK_GBS, 4),
-            "dense_dequantize_fp32_tflops": round(flops / td / 1e12, 2)}
+            "dense_dequantize_f16_mfma_tflops": round(3 * flops / td / 1e12, 2),
+            "dense_dequantize_f16_mfma_frac": round(3 * flops / td / 1e12 / FP16_PEAK_TFLOPS, 4)}
 
 
 def config3_weights(synth, torch, dev):
