@@ -3066,7 +3066,8 @@ __global__ __launch_bounds__(256) void pq_dequantize_dense_kernel(const pqi::BdA
   }
 }
 
-// Quantize on the matrix cores: a wave takes 16 blocks, Y (16 x d) = X (16 x d) Pi^T with
+// Quantize on the fp32 matrix cores (fp32 blocks, and bf16 ones whose input or codes are not
+// 16-byte aligned): a wave takes 16 blocks, Y (16 x d) = X (16 x d) Pi^T with
 // v_mfma_f32_16x16x4f32 (layout as the dequantize kernel below, Pi^T in LDS).  A block of
 // extreme norm is staged scaled by a power of two that brings its norm into [1, 2) (exact;
 // products of tiny blocks would otherwise fall into fp32's subnormal range).  An fp32 sum of d
@@ -3628,8 +3629,8 @@ __global__ __launch_bounds__(64 * kDenseDWaves) void pq_dequantize_dense_f16_ker
   }
 }
 
-// Dequantize on the matrix cores: a wave takes 16 blocks, Xhat (16 x d) = C (16 x d) Pi with
-// v_mfma_f32_16x16x4f32 (fp32 products and sums; the centroids are fp32 exact).  K step s takes
+// Dequantize on the fp32 matrix cores (output not 16-byte aligned): a wave takes 16 blocks,
+// Xhat (16 x d) = C (16 x d) Pi with v_mfma_f32_16x16x4f32 (fp32 products and sums; the centroids are fp32 exact).  K step s takes
 // k = 4 s + g in lane group g; Pi sits in LDS with a row stride of d + 16 words, so the four lane
 // groups of a B operand read four different bank quarters.
 template <bool OUT_BF16, int D>
