@@ -187,3 +187,41 @@ def test_dense_bf16_extreme_blocks(d):
     gn = parity.f16_values(norms)
     assert np.all(gn[0:40] == 0.0) and np.all(np.isinf(gn[40:80])) and np.all(gn[80:100] == 0.0)
     parity.pick_candidate(gn[100:], parity.fp16_candidates(ref["norm"][100:]), "dense norms")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_dense_unaligned_buffers(d):
+    """bf16 input and fp32 output 4 bytes off 16-byte alignment take the fp32 matrix-core kernels:
+    their codes are the oracle's fp64 decisions as the aligned run's are, norms are the oracle's
+    fp16 rounding, and both reconstructions meet the fp32 bound against the oracle."""
+    _case("dense rotation unaligned buffers d=%d" % d)
+    bits, n = 3, 16 * 9 + 7
+    rng = np.random.default_rng(d + 313)
+    xu = synth.bf16_from_f32(rng.standard_normal((n, d)).astype(np.float32))
+    x = synth.bf16_to_f32(xu).astype(np.float64)
+    whole = parity.bf16_tensor(np.concatenate([np.zeros(2, np.uint16), xu.reshape(-1)]))
+    x_off = whole[2:].view(n, d)                           # data 4 bytes past a 16-byte boundary
+    assert x_off.data_ptr() % 16 != 0
+    Pi = _rotation(d + 29, d)
+    rot = torch.from_numpy(Pi).cuda()
+    codes_a, norms_a = pq.quantize_dense(parity.bf16_tensor(xu), d, bits, rot)
+    codes_u, norms_u = pq.quantize_dense(x_off, d, bits, rot)
+    out_big = torch.empty(n * d + 1, dtype=torch.float32, device="cuda")
+    out_off = out_big[1:].view(n, d)
+    assert out_off.data_ptr() % 16 != 0
+    o_u = pq.dequantize_dense(codes_a, norms_a, d, bits, rot, out_dtype=torch.float32, out=out_off)
+    o_a = pq.dequantize_dense(codes_a, norms_a, d, bits, rot, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    P = Pi.astype(np.float64)
+    ref = dense.quantize(x, bits, P)
+    for codes, norms, what in ((codes_a, norms_a, "aligned"), (codes_u, norms_u, "unaligned")):
+        gc = codes.cpu().numpy()
+        bad = np.argwhere(gc != ref["codes"])
+        assert bad.size == 0, "%s: %d codes differ, first at %s" % (what, len(bad), bad[0])
+        parity.pick_candidate(parity.f16_values(norms), parity.fp16_candidates(ref["norm"]), "dense norms " + what)
+    gn = parity.f16_values(norms_a)
+    refd = dense.dequantize(codes_a.cpu().numpy(), gn, bits, P)
+    cmax = float(np.max(np.abs(dense.beta_codebook(bits, d)[0])))
+    for o, what in ((o_a, "aligned"), (o_u, "unaligned")):
+        err = np.abs(o.cpu().numpy().astype(np.float64) - refd)
+        assert np.all(err <= 2e-5 * gn[:, None] * cmax + 1e-30), what
