@@ -102,6 +102,14 @@ __device__ __forceinline__ void xch32(float (&v)[E]) {
   }
 }
 
+// Largest value over the four lanes of a block row (lanes r, r+16, r+32, r+48).
+__device__ __forceinline__ float max4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Sum of a value over the four lanes of a block row (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float sum4(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -51,6 +51,35 @@ __device__ void build_search_grid(const CodecTables& t, uint4* tab) {
   }
 }
 
+// Walsh-Hadamard operand fragments of the d = 128 rotation on the bf16 matrix cores.  H's entry
+// (k, n) is (-1)^popcount(k & n).  Output row tile t (coordinates 16 t + 0..15) and K step s
+// (elements 32 s + 0..31) take the block of H that is H's block (s = 0, t & 1) times
+// (-1)^popcount(s & (t >> 1)), since k = 32 s + kk and n = 16 t + nn share bits 5 and 6 only
+// through s and t >> 1.  So four fragments cover every (s, t): fragment f = (t & 1) + 2 neg, as
+// the A operand of v_mfma_f32_16x16x32_bf16 (lane l: row nn = l & 15, K = 8 (l >> 4) + 0..7),
+// entries +-1.0 in bf16, written to hf[f * 64 + lane].
+constexpr int kHfBytes = 4 * 64 * 16;
+
+__device__ void build_wht_frags(uint4* hf) {
+  for (int i = threadIdx.x; i < 4 * 64; i += blockDim.x) {
+    const int f = i >> 6, l = i & 63, t0 = f & 1, neg = f >> 1;
+    const int nn = l & 15, gk = l >> 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = 8 * gk + 2 * p + h;               // K index inside the step
+        const int par = (__popc(kk & nn) + (((kk >> 4) & 1) & t0) + neg) & 1;
+        word |= (par ? 0xBF80u : 0x3F80u) << (16 * h);
+      }
+      w[p] = word;
+    }
+    hf[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Adding 2^23 to a float in [0, 2^23) rounds it to an integer held in the low
 // mantissa bits: the search-grid cell of y is the bit pattern of
 // med3(fma(y, 1/w, half + 2^23), 2^23, 2^23 + ncell - 1) minus that of 2^23.
@@ -346,9 +375,14 @@ struct Quantizer {
   static constexpr int NR = IN_BF16 ? D / 32 : D / 16;      // 16-byte loads per lane per tile
   static constexpr uint32_t kRepShift = REP ? 8u : 4u;      // log2(bytes per cell)
 
+  // d = 128 bf16 blocks (without a projection, or with the rotated-basis one): the rotation on
+  // the bf16 matrix cores (the products x_k D_k H(k, n) are exact; only the fp32 sums round)
+  static constexpr bool MR = D == 128 && IN_BF16 && (!QJL || RB);
+
   const pqi::QuantArgs& a;
   const unsigned char* smem;
   const uint4* gl;
+  const uint4* hf = nullptr;          // the Walsh-Hadamard fragments in LDS (MR)
   // rotation signs of this lane's element pairs: per pair, the sign bits of its two elements
   // (bits 15 and 31: ORed with a bf16 scale in both halves they make the +-rscale pair of the
   // first butterfly; for fp32 input they flip the values directly); for d = 512 only the sign
@@ -433,6 +467,63 @@ struct Quantizer {
     }
   }
 
+  // v = H (D x) for the 16 blocks of a tile of bf16 input on the matrix cores (MR): the signs D
+  // flip the input's sign bits, the B operand of K step s is chunk s of the load layout (lane
+  // (r, g): elements 32 s + 8 g + 0..7 of block r), and output tile t leaves coordinate
+  // 16 t + 4 g + i of block r in register 4 t + i.
+  __device__ __forceinline__ void rotate_mfma(const uint4 (&w)[NR], float (&v)[E]) const {
+    bf16x8 b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      b[s] = __builtin_bit_cast(bf16x8, make_uint4(w[s].x ^ sgn(4 * s), w[s].y ^ sgn(4 * s + 1),
+                                                   w[s].z ^ sgn(4 * s + 2), w[s].w ^ sgn(4 * s + 3)));
+    f32x4 acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // one fragment live at a time: fragment f serves the (s, t) with t & 1 = f & 1 and
+    // popcount(s & (t >> 1)) odd exactly when f > 1
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, hf[f * 64 + lane]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = f & 1; t < 8; t += 2)
+          if ((__builtin_popcount(s & (t >> 1)) & 1) == (f >> 1))
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h, b[s], acc[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * t + i] = acc[t][i];
+  }
+
+  // The code words of the matrix-core layout (word t: codes of coordinates 16 t + 4 g + 0..3)
+  // to the contiguous layout (word w: codes 32 g + 4 w + 0..3): a 4 x 4 transpose of word pairs
+  // over the block's four lanes, lane bit 4 with word bit 1 and lane bit 5 with word bit 2,
+  // then a renaming of the words.
+  __device__ __forceinline__ void codes_to_runs(uint32_t (&cw)[8]) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & 2) continue;
+      auto x = __builtin_amdgcn_permlane16_swap(cw[j], cw[j | 2], false, false);
+      cw[j] = x[0];
+      cw[j | 2] = x[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & 4) continue;
+      auto x = __builtin_amdgcn_permlane32_swap(cw[j], cw[j | 4], false, false);
+      cw[j] = x[0];
+      cw[j | 4] = x[1];
+    }
+    uint32_t o[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) o[w] = cw[((w >> 2) & 1) | ((w & 1) << 1) | (((w >> 1) & 1) << 2)];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) cw[w] = o[w];
+  }
+
   __device__ __forceinline__ void decide(const uint4 (&raw)[NR], int64_t T, float (&v)[E]) {
     const int64_t blk = T * 16 + r;
     const bool valid = blk < n_blocks;
@@ -468,19 +559,65 @@ struct Quantizer {
       ss = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
     }
     ss = sum4(ss);
-    const float n = sqrtf(ss);
-    const uint16_t n16 = f32_to_f16(n);
+    float n = sqrtf(ss);
+    uint16_t n16 = f32_to_f16(n);
     // e in [-126, 126]: blocks with a norm below 2^-126 keep the largest scale that stays finite
     const int e = n > 0.0f ? min(max(-ilogbf(n), -126), 126) : 0;
     const float rscale = __uint_as_float((uint32_t)(127 + e) << 23);
-    const float nr = n * rscale;                                  // the norm on the scaled axis
-    const float nsc = f16_to_f32(n16) * rscale;                   // the stored norm, scaled
+    // On the matrix cores (MR) a block goes in as it is when its sum of squares lies in
+    // [2^-120, 2^122) (norm in [2^-60, 2^61)): no product or sum can then leave the fp32 range,
+    // and the QJL residual is then scaled by rscale.  Other blocks (a sum of squares that
+    // underflowed or overflowed included) go in scaled by 2^-k, k the exponent of their largest
+    // entry, with their norm taken again from the scaled entries; their residual keeps that
+    // scale.  es is the exponent of the scale the residual carries.
+    const bool pre = MR && !(ss >= 0x1p-120f && ss < 0x1p122f);
+    float nr = n * rscale;                                        // the norm on v's axis
+    float nsc = f16_to_f32(n16) * rscale;                         // the stored norm, on v's axis
+    [[maybe_unused]] float rres = 1.0f;                           // residual scale still to apply
+    [[maybe_unused]] int es = e;
+    [[maybe_unused]] uint4 w[MR ? NR : 1];
+    if constexpr (MR) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) w[i] = raw[i];
+      nr = n;
+      nsc = f16_to_f32(n16);
+      rres = rscale;
+      if (pre) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          const uint32_t q[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(q[u])), fabsf(bf16_hi(q[u]))));
+        }
+        mx = max4(mx);                     // the block's four lanes take this branch together
+        const int k = mx > 0.0f ? ilogbf(mx) : 0;
+        auto sc2 = [&](uint32_t x) { return pack_bf16x2(ldexpf(bf16_lo(x), -k), ldexpf(bf16_hi(x), -k)); };
+        float sq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          w[i] = make_uint4(sc2(w[i].x), sc2(w[i].y), sc2(w[i].z), sc2(w[i].w));
+          const uint32_t q[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sq = fmaf(bf16_lo(q[u]), bf16_lo(q[u]), fmaf(bf16_hi(q[u]), bf16_hi(q[u]), sq));
+        }
+        const float nq = sqrtf(sum4(sq));  // the norm of the scaled block
+        n = ldexpf(nq, k);
+        n16 = f32_to_f16(n);
+        nr = nq;
+        nsc = ldexpf(f16_to_f32(n16), -k);
+        rres = 1.0f;
+        es = -k;
+      }
+    }
     // scaled coordinate -> grid cells (a guess of the cell, the decision below is exact: a
     // one-ulp reciprocal moves only values within an ulp of a cell edge to the neighbouring
     // cell, whose entry decides them the same way unless a boundary sits on that edge)
     const float a_w = nr > 0.0f ? inv_w * __builtin_amdgcn_rcpf(nr) : 0.0f;
 
-    if constexpr (IN_BF16) {
+    if constexpr (MR) {
+      rotate_mfma(w, v);                   // v = H (D x), scaled by 2^-k when pre: matrix-core layout
+    } else if constexpr (IN_BF16) {
       // signs, bf16 -> fp32, the scale and the first butterfly (register bit 0 pairs the two
       // halves of a word) in two dot products per pair: (x0 D0 + x1 D1, x0 D0 - x1 D1) rscale
       const uint32_t scw = ((uint32_t)(127 + e) << 7) * 0x10001u;   // bf16 rscale in both halves
@@ -539,7 +676,8 @@ struct Quantizer {
           const bool gt = fmaf(-__uint_as_float(te[jj].x), nr, v[j]) > 0.0f;
           code = te[jj].y + (gt ? 1u : 0u);
           const float c = __uint_as_float(gt ? te[jj].w : te[jj].z);
-          v[j] = fmaf(-nsc, c, v[j]);
+          if constexpr (MR) v[j] = fmaf(-nsc, c, v[j]) * rres;     // the residual on the rscale axis
+          else v[j] = fmaf(-nsc, c, v[j]);
           asm volatile("" : "+v"(v[j]));   // keep the residual next to its lookup
         } else {
           code = te[jj].y + (fmaf(-__uint_as_float(te[jj].x), nr, v[j]) > 0.0f ? 1u : 0u);
@@ -553,6 +691,7 @@ struct Quantizer {
     // the store branch below and keeps every lookup result live until then
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) asm volatile("" : "+v"(cw[w]));
+    if constexpr (MR) codes_to_runs(cw);
     if constexpr (PK) {
       // bit-packed codes: the lane's run of E codes is E pbits / 8 contiguous bytes
       switch (a.pbits) {
@@ -593,7 +732,8 @@ struct Quantizer {
     if constexpr (QJL) {
       const float rss = sum4(tree_sumsq<E>(v));
       // ||r|| = ||H D r|| / sqrt(d); the product with 2^-e is the exact quotient by rscale
-      const float rn = sqrtf(rss) * __uint_as_float((uint32_t)(127 - e) << 23) * inv_sqrt_d;
+      const float rn = MR ? ldexpf(sqrtf(rss) * inv_sqrt_d, -es)
+                          : sqrtf(rss) * __uint_as_float((uint32_t)(127 - e) << 23) * inv_sqrt_d;
       if (valid && g == 0) a.rnorms[blk] = f32_to_f16(rn);
     }
   }
@@ -665,6 +805,17 @@ struct Quantizer {
       uint4 raw[D / 32];
       load_tile<D, true>(raw, a.proj, rt, m, m >> 4, r, g);
       float v[E];
+      if constexpr (MR) {
+        rotate_mfma(raw, v);
+        u32x4 hi[KS], lo[KS];
+        rotated_frags(v, hi, lo);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          gp[((size_t)rt * KS + k) * 64 + lane] = make_uint4(hi[k][0], hi[k][1], hi[k][2], hi[k][3]);
+          glo[((size_t)rt * KS + k) * 64 + lane] = make_uint4(lo[k][0], lo[k][1], lo[k][2], lo[k][3]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
         const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
@@ -799,6 +950,12 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
     if (T < n_tiles) load_tile<D, IN_BF16>(raw, a.x, T, a.n_blocks, full_tiles, threadIdx.x & 15, (threadIdx.x >> 4) & 3);
   build_search_grid(a.t, tab);
   Q q(a, smem, gl);
+  if constexpr (Q::MR) {
+    // the Walsh-Hadamard fragments after the grid and G D H
+    uint4* hfp = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16 + (QJL ? (size_t)q.m_pad * D * 4 : 0));
+    build_wht_frags(hfp);
+    q.hf = hfp;
+  }
   if constexpr (QJL && RB && Q::NR <= 4) {
     // the search grid first; the rows of G D H are then built (by the first waves) while
     // every wave takes the codes of its first tile, and only that tile's projection waits
@@ -1204,8 +1361,11 @@ void pq_quantize_many_kernel(const pqi::QuantArgs a, const pqi::TensorDesc* tab,
   using Q = Quantizer<D, IN_BF16, false, false, MODE>;
   extern __shared__ __align__(16) unsigned char smem[];
   build_search_grid(a.t, reinterpret_cast<uint4*>(smem));
+  uint4* hfp = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16);   // after the grid (MR)
+  if constexpr (Q::MR) build_wht_frags(hfp);
   __syncthreads();
   Q q(a, smem, nullptr);
+  if constexpr (Q::MR) q.hf = hfp;
   const int64_t total = many_total(tab, n_tensors);
   const int64_t n_waves = (int64_t)gridDim.x * kWaves;
   const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -3736,9 +3896,10 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   const size_t grb = (size_t)m_pad * D * 4;
   // (d <= 128: wider blocks hold too many registers at four waves per SIMD)
   if constexpr (D <= 128) {
-    if (qjl && base + grb <= (size_t)c.max_lds && base + grb <= 98304 &&
-        (mode < 2 || 3 * (base + grb) <= (size_t)c.max_lds)) {
-      const size_t lds = base + grb;
+    // bf16 blocks at d = 128 rotate on the matrix cores: their fragments follow G D H
+    const size_t rb = base + grb + (D == 128 && in_bf16 ? kHfBytes : 0);
+    if (qjl && rb <= (size_t)c.max_lds && base + grb <= 98304 && (mode < 2 || 3 * rb <= (size_t)c.max_lds)) {
+      const size_t lds = rb;
       if (mode == 2) {
         const int g4 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count * 3, (n_tiles + 3) / 4));
         if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, 2, 256, true>), g4, 256, lds, s, a);
@@ -3771,7 +3932,8 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
 #undef PQ_CHUNK_LAUNCH
     return hipGetLastError();
   }
-  const size_t lds = base + (g_lds ? glb : 0);
+  // (without the projection, bf16 blocks at d = 128 rotate on the matrix cores: fragments after the grid)
+  const size_t lds = base + (g_lds ? glb : 0) + (!qjl && D == 128 && in_bf16 ? kHfBytes : 0);
   const int grid = grid_for(n_tiles, c, lds > 65536 ? 1 : PQ_QUANT_WG_PER_CU);
   if (mode == 2) return launch_quantize_r<D, 2>(in_bf16, qjl, g_lds, grid, lds, a, s);
   if (mode == 1) return launch_quantize_r<D, 1>(in_bf16, qjl, g_lds, grid, lds, a, s);
@@ -4011,7 +4173,8 @@ namespace {
 template <int D>
 hipError_t launch_quantize_many_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::TensorDesc* tab, int n_tensors,
                                   const pqi::LaunchCfg& c, hipStream_t s) {
-  const size_t lds = (size_t)a.t.ncell * a.t.nrep * 16;
+  // bf16 blocks at d = 128 rotate on the matrix cores: their fragments after the grid
+  const size_t lds = (size_t)a.t.ncell * a.t.nrep * 16 + (D == 128 && in_bf16 ? kHfBytes : 0);
   const int grid = c.cu_count * PQ_MANY_WG_PER_CU;
   const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
 #define PQ_MANY_Q(MODE)                                                                                          \

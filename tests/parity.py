@@ -179,7 +179,7 @@ class Tally:
             label, t["code_flips"], t["codes"], t["code_flips"] / max(t["codes"], 1))
         assert t["bit_flips"] <= mismatch_cap(t["bits"]), "%s: %d band sign flips among %d bits (rate %.3g)" % (
             label, t["bit_flips"], t["bits"], t["bit_flips"] / max(t["bits"], 1))
-        stats = {k: v for k, v in t.items() if v or k in ("codes", "code_flips")}
+        stats = {k: v for k, v in t.items() if v or k in ("codes", "code_flips", "bits", "bit_flips")}
         if not t["bits"]:
             stats.pop("bits", None), stats.pop("bit_flips", None)
         return report(label, stats)

@@ -150,3 +150,40 @@ def test_empty_and_single_block():
     c, nn, _, _ = pq.quantize(xt, d, bits, st)
     torch.cuda.synchronize()
     parity.check_quantize(x, bits, D, c.cpu().numpy(), parity.f16_values(nn), label="single")
+
+
+@pytest.mark.parametrize("m", [0, 64])
+def test_extreme_norms_bf16_d128(m):
+    """bf16 blocks at d = 128 whose norms lie outside [2^-60, 2^61) (scaled to the unit range
+    before the rotation's products) mixed in the same tiles with ordinary ones, with and
+    without the QJL stage."""
+    _case("extreme norms d=128 bf16 m=%d" % m)
+    d, bits, n = 128, 5, 16 * 4 + 5
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((n, d)) * 0.02
+    x[1] *= 2.0 ** -75                    # norm near 2^-78
+    if m == 0:
+        # norms past the fp16 range: the QJL residual of such a block is not finite
+        x[6] = rng.standard_normal(d) * 2.0 ** 55   # norm near 2^58.5: as it is
+        x[9] = rng.standard_normal(d) * 2.0 ** 58   # norm near 2^61.5: scaled
+    else:
+        x[6] = rng.standard_normal(d) * 2.0 ** 12   # norm near 2^15.5 (finite in fp16)
+    x[17] = rng.standard_normal(d) * 1e-39      # bf16 subnormal entries (norm near 1e-38)
+    x[18, ::3] = 0.0
+    x[18] *= 2.0 ** -66
+    x[33] *= 2.0 ** 40                    # in range
+    x[64] *= 2.0 ** -90                   # ragged last tile
+    u = synth.bf16_from_f32(x.astype(np.float32))
+    xt, xs = parity.bf16_tensor(u), numerics.bf16_from_bits(u)
+    xs = xs.reshape(n, d)
+    st, D = _signs(d, 6)
+    if m:
+        Gt, G = _proj(m, d, 8)
+        codes, norms, qb, rn = pq.quantize(xt, d, bits, st, Gt)
+        torch.cuda.synchronize()
+        parity.check_quantize(xs, bits, D, codes.cpu().numpy(), parity.f16_values(norms), G, qb.cpu().numpy(),
+                              parity.f16_values(rn), label="extreme norms qjl")
+    else:
+        codes, norms, _, _ = pq.quantize(xt, d, bits, st)
+        torch.cuda.synchronize()
+        parity.check_quantize(xs, bits, D, codes.cpu().numpy(), parity.f16_values(norms), label="extreme norms")
