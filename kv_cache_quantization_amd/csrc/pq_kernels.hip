@@ -377,7 +377,10 @@ struct Quantizer {
 
   // d = 128 bf16 blocks (without a projection, or with the rotated-basis one): the rotation on
   // the bf16 matrix cores (the products x_k D_k H(k, n) are exact; only the fp32 sums round)
-  static constexpr bool MR = D == 128 && IN_BF16 && (!QJL || RB);
+  static constexpr bool MR = IN_BF16 && ((D == 128 && (!QJL || RB)) || D == 256);
+  // d = 256: the result is moved to the contiguous layout of the butterflies (MRT), so that
+  // the codes, the inverse transform of the residual and the projections stay as they are
+  static constexpr bool MRT = MR && D == 256;
 
   const pqi::QuantArgs& a;
   const unsigned char* smem;
@@ -470,39 +473,60 @@ struct Quantizer {
   // v = H (D x) for the 16 blocks of a tile of bf16 input on the matrix cores (MR): the signs D
   // flip the input's sign bits, the B operand of K step s is chunk s of the load layout (lane
   // (r, g): elements 32 s + 8 g + 0..7 of block r), and output tile t leaves coordinate
-  // 16 t + 4 g + i of block r in register 4 t + i.
+  // 16 t + 4 g + i of block r in register 4 t + i.  With MRT the two top bits of t are then
+  // exchanged with the lane bits 4 and 5 and the registers renamed: the contiguous layout.
   __device__ __forceinline__ void rotate_mfma(const uint4 (&w)[NR], float (&v)[E]) const {
-    bf16x8 b[4];
+    constexpr int KSM = D / 32, MT = D / 16;
+    bf16x8 b[KSM];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < KSM; ++s)
       b[s] = __builtin_bit_cast(bf16x8, make_uint4(w[s].x ^ sgn(4 * s), w[s].y ^ sgn(4 * s + 1),
                                                    w[s].z ^ sgn(4 * s + 2), w[s].w ^ sgn(4 * s + 3)));
-    f32x4 acc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[MT];
     // one fragment live at a time: fragment f serves the (s, t) with t & 1 = f & 1 and
-    // popcount(s & (t >> 1)) odd exactly when f > 1
+    // popcount(s & (t >> 1)) odd exactly when f > 1; s = 0 comes first for every t
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const bf16x8 h = __builtin_bit_cast(bf16x8, hf[f * 64 + lane]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < KSM; ++s)
 #pragma unroll
-        for (int t = f & 1; t < 8; t += 2)
+        for (int t = f & 1; t < MT; t += 2)
           if ((__builtin_popcount(s & (t >> 1)) & 1) == (f >> 1))
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h, b[s], acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h, b[s], s == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[t],
+                                                              0, 0, 0);
     }
+    if constexpr (MRT) {
+      constexpr int L = Log2<E>::v;
+      float u[E];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[4 * t + i] = acc[t][i];
+        for (int i = 0; i < 4; ++i) u[4 * t + i] = acc[t][i];
+      xch16<E, L - 2>(u);
+      xch32<E, L - 1>(u);
+      // register j now holds offset (j & 3) + 4 (bit L-2) + 8 (bit L-1) + 16 (bits 2..L-3) of
+      // the lane's run; the contiguous layout keeps offset o in register cperm_inv(o)
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int o = (j & 3) | (((j >> (L - 2)) & 1) << 2) | (((j >> (L - 1)) & 1) << 3) |
+                      (((j >> 2) & ((1 << (L - 4)) - 1)) << 4);
+        v[cperm_inv<D>(o)] = u[j];
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * t + i] = acc[t][i];
+    }
   }
 
   // The code words of the matrix-core layout (word t: codes of coordinates 16 t + 4 g + 0..3)
   // to the contiguous layout (word w: codes 32 g + 4 w + 0..3): a 4 x 4 transpose of word pairs
   // over the block's four lanes, lane bit 4 with word bit 1 and lane bit 5 with word bit 2,
   // then a renaming of the words.
-  __device__ __forceinline__ void codes_to_runs(uint32_t (&cw)[8]) const {
+  __device__ __forceinline__ void codes_to_runs(uint32_t (&cw)[E / 4]) const {
+    static_assert(E == 32, "d = 128 only");
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j & 2) continue;
@@ -691,7 +715,7 @@ struct Quantizer {
     // the store branch below and keeps every lookup result live until then
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) asm volatile("" : "+v"(cw[w]));
-    if constexpr (MR) codes_to_runs(cw);
+    if constexpr (MR && !MRT) codes_to_runs(cw);
     if constexpr (PK) {
       // bit-packed codes: the lane's run of E codes is E pbits / 8 contiguous bytes
       switch (a.pbits) {
@@ -952,7 +976,8 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
   Q q(a, smem, gl);
   if constexpr (Q::MR) {
     // the Walsh-Hadamard fragments after the grid and G D H
-    uint4* hfp = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16 + (QJL ? (size_t)q.m_pad * D * 4 : 0));
+    const size_t gbytes = QJL && RB ? (size_t)q.m_pad * D * 4 : QJL && G_LDS ? (size_t)q.m_pad * D * 2 : 0;
+    uint4* hfp = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16 + gbytes);
     build_wht_frags(hfp);
     q.hf = hfp;
   }
@@ -1037,6 +1062,12 @@ void pq_quantize_chunked_kernel(const pqi::QuantArgs a) {
   u32x4* rf = reinterpret_cast<u32x4*>(smem + a.t.ncell * a.t.nrep * 16);   // [WAVES][KS][2][64]
   build_search_grid(a.t, tab);
   Q q(a, smem, nullptr);
+  if constexpr (Q::MR) {
+    // the Walsh-Hadamard fragments after the residual fragments
+    uint4* hfp = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16 + chunk_frag_bytes<D>());
+    build_wht_frags(hfp);
+    q.hf = hfp;
+  }
   const int lane = q.lane, r = q.r, g = q.g, wv = threadIdx.x >> 6;
   // rotation signs of this lane's residual registers: chunk k holds columns 8 res_col8(g, k) + 0..7
   uint32_t rsg[(KS + 3) / 4];
@@ -3888,7 +3919,10 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   const bool qjl = a.m > 0;
   // G kept in LDS for the whole launch when it fits beside the search grid (several
   // workgroups per CU while it takes at most 64 KiB), else walked in chunks
-  const bool g_lds = qjl && base + glb <= (size_t)c.max_lds;
+  // bf16 blocks at d = 256 rotate on the matrix cores in every form: their fragments follow the
+  // grid and G (or the residual fragments)
+  const size_t hfx = D == 256 && in_bf16 ? kHfBytes : 0;
+  const bool g_lds = qjl && base + glb + hfx <= (size_t)c.max_lds;
   const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
   // rotated-basis projection when G D H (fp16 high + low) fits beside the grid: one
   // sixteen-wave workgroup per CU (four waves per SIMD at <= 128 VGPRs); packed codes hold
@@ -3918,7 +3952,7 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   }
   if (qjl && !g_lds) {
     // residual fragments of every tile of the workgroup beside the search grid
-    const size_t lds = base + chunk_frag_bytes<D>();
+    const size_t lds = base + chunk_frag_bytes<D>() + hfx;
     if (lds > (size_t)c.max_lds) return hipErrorInvalidConfiguration;
     const int64_t n_groups = (n_tiles + chunk_threads<D>() / 64 - 1) / (chunk_threads<D>() / 64);
     const int per_cu = std::max(1, (int)((size_t)c.max_lds / lds));
@@ -3932,8 +3966,9 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
 #undef PQ_CHUNK_LAUNCH
     return hipGetLastError();
   }
-  // (without the projection, bf16 blocks at d = 128 rotate on the matrix cores: fragments after the grid)
-  const size_t lds = base + (g_lds ? glb : 0) + (!qjl && D == 128 && in_bf16 ? kHfBytes : 0);
+  // (bf16 blocks at d = 256, and without the projection at d = 128, rotate on the matrix cores:
+  // fragments after the grid and G)
+  const size_t lds = base + (g_lds ? glb : 0) + hfx + (!qjl && D == 128 && in_bf16 ? kHfBytes : 0);
   const int grid = grid_for(n_tiles, c, lds > 65536 ? 1 : PQ_QUANT_WG_PER_CU);
   if (mode == 2) return launch_quantize_r<D, 2>(in_bf16, qjl, g_lds, grid, lds, a, s);
   if (mode == 1) return launch_quantize_r<D, 1>(in_bf16, qjl, g_lds, grid, lds, a, s);
@@ -4173,8 +4208,8 @@ namespace {
 template <int D>
 hipError_t launch_quantize_many_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::TensorDesc* tab, int n_tensors,
                                   const pqi::LaunchCfg& c, hipStream_t s) {
-  // bf16 blocks at d = 128 rotate on the matrix cores: their fragments after the grid
-  const size_t lds = (size_t)a.t.ncell * a.t.nrep * 16 + (D == 128 && in_bf16 ? kHfBytes : 0);
+  // bf16 blocks at d = 128 and 256 rotate on the matrix cores: their fragments after the grid
+  const size_t lds = (size_t)a.t.ncell * a.t.nrep * 16 + ((D == 128 || D == 256) && in_bf16 ? kHfBytes : 0);
   const int grid = c.cu_count * PQ_MANY_WG_PER_CU;
   const int mode = a.pbits ? 2 : (a.t.nrep == 16 ? 1 : 0);
 #define PQ_MANY_Q(MODE)                                                                                          \

@@ -63,6 +63,7 @@ CODEC_CASES = [
     # N-tile group (m = 600: 38 N tiles, 75-byte bit rows), and d = 256
     (128, 3, "f32", 16 * 3 + 7, 600),
     (256, 4, "f32", 16 * 5 + 3, 512),
+    (256, 3, "bf16", 16 * 6 + 5, 512),
 ]
 
 
@@ -152,13 +153,13 @@ def test_empty_and_single_block():
     parity.check_quantize(x, bits, D, c.cpu().numpy(), parity.f16_values(nn), label="single")
 
 
-@pytest.mark.parametrize("m", [0, 64])
-def test_extreme_norms_bf16_d128(m):
-    """bf16 blocks at d = 128 whose norms lie outside [2^-60, 2^61) (scaled to the unit range
-    before the rotation's products) mixed in the same tiles with ordinary ones, with and
-    without the QJL stage."""
-    _case("extreme norms d=128 bf16 m=%d" % m)
-    d, bits, n = 128, 5, 16 * 4 + 5
+@pytest.mark.parametrize("d,m", [(128, 0), (128, 64), (256, 0), (256, 256), (256, 512)])
+def test_extreme_norms_bf16(d, m):
+    """bf16 blocks whose norms lie outside [2^-60, 2^61) (scaled to the unit range before the
+    rotation's matrix-core products) mixed in the same tiles with ordinary ones, with and
+    without the QJL stage (d = 256: the projection from LDS and, at m = 512, the chunked form)."""
+    _case("extreme norms d=%d bf16 m=%d" % (d, m))
+    bits, n = 5, 16 * 4 + 5
     rng = np.random.default_rng(31)
     x = rng.standard_normal((n, d)) * 0.02
     x[1] *= 2.0 ** -75                    # norm near 2^-78
