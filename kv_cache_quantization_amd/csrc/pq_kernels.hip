@@ -471,17 +471,18 @@ struct Quantizer {
   }
 
   // v = H (D x) for the 16 blocks of a tile of bf16 input on the matrix cores (MR): the signs D
-  // flip the input's sign bits, the B operand of K step s is chunk s of the load layout (lane
+  // flip the input's sign bits (then addw raises the exponent fields of both bf16 halves), the
+  // B operand of K step s is chunk s of the load layout (lane
   // (r, g): elements 32 s + 8 g + 0..7 of block r), and output tile t leaves coordinate
   // 16 t + 4 g + i of block r in register 4 t + i.  With MRT the two top bits of t are then
   // exchanged with the lane bits 4 and 5 and the registers renamed: the contiguous layout.
-  __device__ __forceinline__ void rotate_mfma(const uint4 (&w)[NR], float (&v)[E]) const {
+  __device__ __forceinline__ void rotate_mfma(const uint4 (&w)[NR], float (&v)[E], uint32_t addw = 0) const {
     constexpr int KSM = D / 32, MT = D / 16;
     bf16x8 b[KSM];
 #pragma unroll
     for (int s = 0; s < KSM; ++s)
-      b[s] = __builtin_bit_cast(bf16x8, make_uint4(w[s].x ^ sgn(4 * s), w[s].y ^ sgn(4 * s + 1),
-                                                   w[s].z ^ sgn(4 * s + 2), w[s].w ^ sgn(4 * s + 3)));
+      b[s] = __builtin_bit_cast(bf16x8, make_uint4((w[s].x ^ sgn(4 * s)) + addw, (w[s].y ^ sgn(4 * s + 1)) + addw,
+                                                   (w[s].z ^ sgn(4 * s + 2)) + addw, (w[s].w ^ sgn(4 * s + 3)) + addw));
     f32x4 acc[MT];
     // one fragment live at a time: fragment f serves the (s, t) with t & 1 = f & 1 and
     // popcount(s & (t >> 1)) odd exactly when f > 1; s = 0 comes first for every t
@@ -588,24 +589,30 @@ struct Quantizer {
     // e in [-126, 126]: blocks with a norm below 2^-126 keep the largest scale that stays finite
     const int e = n > 0.0f ? min(max(-ilogbf(n), -126), 126) : 0;
     const float rscale = __uint_as_float((uint32_t)(127 + e) << 23);
-    // On the matrix cores (MR) a block goes in as it is when its sum of squares lies in
-    // [2^-120, 2^122) (norm in [2^-60, 2^61)): no product or sum can then leave the fp32 range,
-    // and the QJL residual is then scaled by rscale.  Other blocks (a sum of squares that
-    // underflowed or overflowed included) go in scaled by 2^-k, k the exponent of their largest
-    // entry, with their norm taken again from the scaled entries; their residual keeps that
-    // scale.  es is the exponent of the scale the residual carries.
-    const bool pre = MR && !(ss >= 0x1p-120f && ss < 0x1p122f);
+    // On the matrix cores (MR) a block whose norm lies in [2^-60, 2^12) (without the QJL stage
+    // [2^-60, 2^61)) goes in scaled by 2^es, es = max(e, 0): for e > 0 the exponent fields of its
+    // bf16 entries are raised by e (the same integer add that follows the sign flip; exact for
+    // normal entries, since no entry exceeds the norm, and a zero or subnormal entry becomes at
+    // most 2^-66 of the scaled norm).  No product or sum can then leave the fp32 range, and the
+    // QJL residual (at most 9 n per coordinate) stays inside the fp16 range for the split.
+    // Other blocks (a sum of squares that underflowed or overflowed included) go in scaled by
+    // 2^-k, k the exponent of their largest entry, rounded to bf16, with their norm taken again
+    // from the scaled entries.  es is the exponent of the scale v carries.
+    constexpr float kSsHi = QJL ? 0x1p24f : 0x1p122f;
+    const bool pre = MR && !(ss >= 0x1p-120f && ss < kSsHi);
     float nr = n * rscale;                                        // the norm on v's axis
     float nsc = f16_to_f32(n16) * rscale;                         // the stored norm, on v's axis
-    [[maybe_unused]] float rres = 1.0f;                           // residual scale still to apply
     [[maybe_unused]] int es = e;
+    [[maybe_unused]] uint32_t addw = 0;                           // exponent raise of both halves
     [[maybe_unused]] uint4 w[MR ? NR : 1];
     if constexpr (MR) {
 #pragma unroll
       for (int i = 0; i < NR; ++i) w[i] = raw[i];
-      nr = n;
-      nsc = f16_to_f32(n16);
-      rres = rscale;
+      es = max(e, 0);
+      const float sc = __uint_as_float((uint32_t)(127 + es) << 23);
+      nr = n * sc;
+      nsc = f16_to_f32(n16) * sc;
+      addw = (uint32_t)es * 0x00800080u;
       if (pre) {
         float mx = 0.0f;
 #pragma unroll
@@ -630,8 +637,8 @@ struct Quantizer {
         n16 = f32_to_f16(n);
         nr = nq;
         nsc = ldexpf(f16_to_f32(n16), -k);
-        rres = 1.0f;
         es = -k;
+        addw = 0;
       }
     }
     // scaled coordinate -> grid cells (a guess of the cell, the decision below is exact: a
@@ -640,7 +647,7 @@ struct Quantizer {
     const float a_w = nr > 0.0f ? inv_w * __builtin_amdgcn_rcpf(nr) : 0.0f;
 
     if constexpr (MR) {
-      rotate_mfma(w, v);                   // v = H (D x), scaled by 2^-k when pre: matrix-core layout
+      rotate_mfma(w, v, addw);             // v = 2^es H (D x)
     } else if constexpr (IN_BF16) {
       // signs, bf16 -> fp32, the scale and the first butterfly (register bit 0 pairs the two
       // halves of a word) in two dot products per pair: (x0 D0 + x1 D1, x0 D0 - x1 D1) rscale
@@ -700,8 +707,7 @@ struct Quantizer {
           const bool gt = fmaf(-__uint_as_float(te[jj].x), nr, v[j]) > 0.0f;
           code = te[jj].y + (gt ? 1u : 0u);
           const float c = __uint_as_float(gt ? te[jj].w : te[jj].z);
-          if constexpr (MR) v[j] = fmaf(-nsc, c, v[j]) * rres;     // the residual on the rscale axis
-          else v[j] = fmaf(-nsc, c, v[j]);
+          v[j] = fmaf(-nsc, c, v[j]);
           asm volatile("" : "+v"(v[j]));   // keep the residual next to its lookup
         } else {
           code = te[jj].y + (fmaf(-__uint_as_float(te[jj].x), nr, v[j]) > 0.0f ? 1u : 0u);
