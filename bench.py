@@ -149,11 +149,23 @@ def summarize(run_dir):
     lines = ["# Kernel durations of the benchmark (config 2 codec, config 4 QJL leg, config 5 two-stage and "
              "decode-attention legs, block-diagonal leg), one MI355X",
              "", "command: " + trace_cmd, "kernel source hash: " + kernel_source_hash(), "",
-             "%-58s %6s %12s %10s %10s" % ("kernel", "calls", "average_ns", "min_ns", "max_ns")]
+             "average_ns is rocprofv3's average over every call; median_ns and timed_avg_ns come from the "
+             "per-dispatch trace, timed_avg_ns over the calls within 25% of the median (the benchmark's set-up "
+             "launches the same kernels at other sizes, e.g. the attention leg quantizes its keys with the "
+             "config-2 instantiation)", "",
+             "%-58s %6s %12s %10s %12s %10s %10s" % ("kernel", "calls", "average_ns", "median_ns", "timed_avg_ns",
+                                                      "min_ns", "max_ns")]
+    durs = {}
+    for r in rows("prof_trace", "trace_kernel_trace.csv"):
+        durs.setdefault(short(r["Kernel_Name"]), []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     for r in rows("prof_trace", "trace_kernel_stats.csv"):
         n = short(r["Name"])
         if any(k in n for k in ("pq_", "qjl_")):
-            lines.append("%-58s %6s %12.1f %10s %10s" % (n, r["Calls"], float(r["AverageNs"]), r["MinNs"], r["MaxNs"]))
+            ds = sorted(durs.get(n, [0]))
+            med = ds[len(ds) // 2]
+            kept = [x for x in ds if abs(x - med) <= 0.25 * med] or ds
+            lines.append("%-58s %6s %12.1f %10d %12.1f %10s %10s" % (n, r["Calls"], float(r["AverageNs"]), med,
+                                                                     sum(kept) / len(kept), r["MinNs"], r["MaxNs"]))
     with open(os.path.join(out_dir, "bench_kernels_config2_config4_config5_trace.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -241,15 +253,27 @@ def summarize_sq(run_dir):
     import csv
     out_dir = os.path.join(ROOT, "profiles")
 
-    def load(sub):
-        vals = {}
+    def load(sub, key):
+        # per kernel, per dispatch, per counter; the benchmark also launches some of these kernels
+        # at other sizes while setting up its legs (the attention leg quantizes its keys with the
+        # config-2 instantiation), so only the dispatches whose `key` counter lies within 25% of
+        # that kernel's median are kept: the timed workload's launches
+        per = {}
         with open(os.path.join(run_dir, sub, "pmc_counter_collection.csv")) as fh:
             for r in csv.DictReader(fh):
                 name = r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "").split("(pqi::")[0]
-                vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                per.setdefault(name, {}).setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        vals = {}
+        for name, disp in per.items():
+            ks = sorted(d[key] for d in disp.values() if key in d)
+            med = ks[len(ks) // 2] if ks else 0.0
+            for d in disp.values():
+                if key in d and abs(d[key] - med) <= 0.25 * med:
+                    for c, v in d.items():
+                        vals.setdefault(name, {}).setdefault(c, []).append(v)
         return vals
 
-    a, b = load("pmc_sq_a"), load("pmc_sq_b")
+    a, b = load("pmc_sq_a", "SQ_INSTS_VALU"), load("pmc_sq_b", "SQ_ACTIVE_INST_VALU")
     rec = {"source_hash": kernel_source_hash(),
            "commands": ["rocprofv3 --pmc %s --output-format csv -d <dir>/pmc_sq_a -o pmc -- %s" % (SQ_SET_A, SQ_BENCH_ARGS),
                         "rocprofv3 --pmc %s --output-format csv -d <dir>/pmc_sq_b -o pmc -- %s" % (SQ_SET_B, SQ_BENCH_ARGS)],
@@ -257,7 +281,10 @@ def summarize_sq(run_dir):
                            "mfma_insts_per_tile": "SQ_INSTS_MFMA / tiles per launch",
                            "mfma_util": "sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs)",
                            "valu_busy": "sum SQ_ACTIVE_INST_VALU / 256 CUs / (GRBM_GUI_ACTIVE / 8)",
-                           "mfma_mops_per_launch": "(SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16 + _I8) x 512 flops (or int ops)"},
+                           "mfma_mops_per_launch": "(SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16 + _I8) x 512 flops (or int ops)",
+                           "dispatches": "launches of the timed workload: those whose SQ_INSTS_VALU (SQ_ACTIVE_INST_VALU in the "
+                                         "second run) lies within 25% of the kernel's median; set-up launches at other "
+                                         "sizes are left out"},
            "kernels": {}}
     lines = ["# SQ counters of the benchmark's hot kernels, one MI355X (per launch, means over dispatches)", "",
              "commands:"] + ["  " + c for c in rec["commands"]] + ["kernel source hash: " + rec["source_hash"], "",
