@@ -28,6 +28,13 @@ constexpr int kWaves = kThreads / 64;
 #ifndef PQ_QUANT_WAVES_PER_EU
 #define PQ_QUANT_WAVES_PER_EU 1
 #endif
+#ifndef PQ_RB_WPE
+#define PQ_RB_WPE 4              // rotated-basis quantize: waves per SIMD
+#endif
+#ifndef PQ_RB_WG
+#define PQ_RB_WG 1               // ... and workgroups per CU sharing them
+#endif
+constexpr int kRbThreads = 256 * PQ_RB_WPE / PQ_RB_WG;
 #ifndef PQ_LOOKUP_BATCH
 #define PQ_LOOKUP_BATCH 8        // grid lookups of the code decision in flight at once
 #endif
@@ -877,8 +884,9 @@ struct Quantizer {
     for (int nt0 = 0; nt0 < nt; nt0 += 4) {
       f32x4 acc[4];
 #pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if (nt0 + q < nt) {
 #pragma unroll
           for (int k = 0; k < KS; ++k) {
@@ -912,8 +920,30 @@ struct Quantizer {
     for (int nt0 = nt_begin; nt0 < nt_end; nt0 += 4) {
       f32x4 acc[4];
 #pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (nt0 + 4 <= nt_end) {
+        // four N tiles: their products interleaved, so that no product waits for the one before
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          f16x8 b[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = 16 * (nt0 + q) + r;
+            if constexpr (FROM_LDS) b[q] = __builtin_bit_cast(f16x8, gb[g_swizzle<D>(row - row0, res_col8<D>(g, k))]);
+            else b[q] = load_gfrag_f16<D, false>(gb, a.proj, a.signs, m, row, res_col8<D>(g, k));
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[q], __builtin_bit_cast(f16x8, ahi[k]), acc[q], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[q], __builtin_bit_cast(f16x8, alo[k]), acc[q], 0, 0, 0);
+        }
+        store_sign_bytes(sign_bytes4(acc), lane, T * 16, n_blocks, a.qbits, mb, nt0);
+        continue;
+      }
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if (nt0 + q < nt_end) {
           const int row = 16 * (nt0 + q) + r;
 #pragma unroll
@@ -962,7 +992,7 @@ __device__ void stage_projection_rows(const uint16_t* proj, const uint8_t* signs
 // per SIMD.  RB (rotated-basis projection, G D H in LDS): sixteen-wave workgroups, one per CU
 // (four waves per SIMD), so the grid and G D H are built once per CU.
 template <int D, bool IN_BF16, bool QJL, bool G_LDS, int MODE, int THREADS = kThreads, bool RB = false>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(RB ? (MODE == 2 ? 3 : 4) : (THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU))))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(RB ? (MODE == 2 ? 3 : PQ_RB_WPE) : (THREADS == 512 ? 2 : PQ_QUANT_WAVES_PER_EU))))
 void pq_quantize_kernel(const pqi::QuantArgs a) {
   using Q = Quantizer<D, IN_BF16, QJL, G_LDS, MODE, RB>;
   constexpr int WAVES = THREADS / 64;
@@ -3946,10 +3976,11 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
         else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, 2, 256, true>), g4, 256, lds, s, a);
         return hipGetLastError();
       }
-      const int g16 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count, (n_tiles + 15) / 16));
+      constexpr int rbw = kRbThreads / 64;
+      const int g16 = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)c.cu_count * PQ_RB_WG, (n_tiles + rbw - 1) / rbw));
 #define PQ_RB_LAUNCH(MODE)                                                                                       \
-  if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, MODE, 1024, true>), g16, 1024, lds, s, a); \
-  else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, MODE, 1024, true>), g16, 1024, lds, s, a);
+  if (in_bf16) hipLaunchKernelGGL((pq_quantize_kernel<D, true, true, false, MODE, kRbThreads, true>), g16, kRbThreads, lds, s, a); \
+  else hipLaunchKernelGGL((pq_quantize_kernel<D, false, true, false, MODE, kRbThreads, true>), g16, kRbThreads, lds, s, a);
       if (mode == 1) { PQ_RB_LAUNCH(1) }
       else { PQ_RB_LAUNCH(0) }
 #undef PQ_RB_LAUNCH
