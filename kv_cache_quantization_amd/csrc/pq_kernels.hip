@@ -594,7 +594,38 @@ struct Quantizer {
     float n = sqrtf(ss);
     uint16_t n16 = f32_to_f16(n);
     // e in [-126, 126]: blocks with a norm below 2^-126 keep the largest scale that stays finite
-    const int e = n > 0.0f ? min(max(-ilogbf(n), -126), 126) : 0;
+    int e = n > 0.0f ? min(max(-ilogbf(n), -126), 126) : 0;
+    [[maybe_unused]] float nr_far = -1.0f;
+    if constexpr (!MR) {
+      // a norm outside [2^-60, 2^61): the sum of squares may have left the fp32 range, so it is
+      // taken again from the entries scaled by 2^-k, k the exponent of the block's largest entry
+      // (the four lanes of a block take this branch together)
+      if (!(ss >= 0x1p-120f && ss < 0x1p122f)) {
+        auto ent = [&](int i) {          // entry i of this lane, i < 4 NR (fp32) or 8 NR (bf16)
+          const uint4& q = raw[IN_BF16 ? i >> 3 : i >> 2];
+          const int w = IN_BF16 ? (i >> 1) & 3 : i & 3;
+          const uint32_t x = w == 0 ? q.x : w == 1 ? q.y : w == 2 ? q.z : q.w;
+          return IN_BF16 ? ((i & 1) ? bf16_hi(x) : bf16_lo(x)) : __uint_as_float(x);
+        };
+        constexpr int NE = IN_BF16 ? 8 * NR : 4 * NR;
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) mx = fmaxf(mx, fabsf(ent(i)));
+        mx = max4(mx);
+        const int k = mx > 0.0f ? ilogbf(mx) : 0;
+        float sq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+          const float t = ldexpf(ent(i), -k);
+          sq = fmaf(t, t, sq);
+        }
+        const float nq = sqrtf(sum4(sq));
+        n = ldexpf(nq, k);
+        n16 = f32_to_f16(n);
+        e = nq > 0.0f ? min(max(-(ilogbf(nq) + k), -126), 126) : 0;
+        nr_far = ldexpf(nq, k + e);      // n 2^e without leaving the fp32 range
+      }
+    }
     const float rscale = __uint_as_float((uint32_t)(127 + e) << 23);
     // On the matrix cores (MR) a block whose norm lies in [2^-60, 2^12) (without the QJL stage
     // [2^-60, 2^61)) goes in scaled by 2^es, es = max(e, 0): for e > 0 the exponent fields of its
@@ -607,7 +638,7 @@ struct Quantizer {
     // from the scaled entries.  es is the exponent of the scale v carries.
     constexpr float kSsHi = QJL ? 0x1p24f : 0x1p122f;
     const bool pre = MR && !(ss >= 0x1p-120f && ss < kSsHi);
-    float nr = n * rscale;                                        // the norm on v's axis
+    float nr = nr_far >= 0.0f ? nr_far : n * rscale;             // the norm on v's axis
     float nsc = f16_to_f32(n16) * rscale;                         // the stored norm, on v's axis
     [[maybe_unused]] int es = e;
     [[maybe_unused]] uint32_t addw = 0;                           // exponent raise of both halves

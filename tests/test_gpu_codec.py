@@ -153,29 +153,41 @@ def test_empty_and_single_block():
     parity.check_quantize(x, bits, D, c.cpu().numpy(), parity.f16_values(nn), label="single")
 
 
-@pytest.mark.parametrize("d,m", [(128, 0), (128, 64), (256, 0), (256, 256), (256, 512)])
-def test_extreme_norms_bf16(d, m):
-    """bf16 blocks whose norms lie outside [2^-60, 2^61) (scaled to the unit range before the
-    rotation's matrix-core products) mixed in the same tiles with ordinary ones, with and
-    without the QJL stage (d = 256: the projection from LDS and, at m = 512, the chunked form)."""
-    _case("extreme norms d=%d bf16 m=%d" % (d, m))
+@pytest.mark.parametrize("d,dtype,m", [(128, "bf16", 0), (128, "bf16", 64), (256, "bf16", 0), (256, "bf16", 256),
+                                        (256, "bf16", 512), (128, "f32", 0), (128, "f32", 64), (512, "bf16", 0),
+                                        (512, "bf16", 512), (64, "bf16", 32), (256, "f32", 512)])
+def test_extreme_norms(d, dtype, m):
+    """Blocks whose norms lie outside [2^-60, 2^61), where a sum of squares in fp32 underflows or
+    overflows (the norm is then taken from entries scaled by a power of two; on the matrix cores
+    the entries themselves go in scaled), mixed in the same tiles with ordinary ones, with and
+    without the QJL stage: the matrix-core rotation (bf16, d = 128 and 256), the butterflies
+    (fp32 input, d = 64 and 512), the projection from LDS and the chunked form."""
+    _case("extreme norms d=%d %s m=%d" % (d, dtype, m))
     bits, n = 5, 16 * 4 + 5
-    rng = np.random.default_rng(31)
+    rng = np.random.default_rng(31 + d)
     x = rng.standard_normal((n, d)) * 0.02
     x[1] *= 2.0 ** -75                    # norm near 2^-78
     if m == 0:
         # norms past the fp16 range: the QJL residual of such a block is not finite
-        x[6] = rng.standard_normal(d) * 2.0 ** 55   # norm near 2^58.5: as it is
-        x[9] = rng.standard_normal(d) * 2.0 ** 58   # norm near 2^61.5: scaled
+        x[6] = rng.standard_normal(d) * 2.0 ** 55   # norm near 2^58.5
+        x[9] = rng.standard_normal(d) * 2.0 ** 58   # norm near 2^61.5
+        if dtype == "f32":
+            x[10] = rng.standard_normal(d) * 2.0 ** 66   # a sum of squares beyond fp32
     else:
         x[6] = rng.standard_normal(d) * 2.0 ** 12   # norm near 2^15.5 (finite in fp16)
-    x[17] = rng.standard_normal(d) * 1e-39      # bf16 subnormal entries (norm near 1e-38)
+    x[17] = rng.standard_normal(d) * 1e-39      # subnormal entries (norm near 1e-38)
     x[18, ::3] = 0.0
     x[18] *= 2.0 ** -66
     x[33] *= 2.0 ** 40                    # in range
     x[64] *= 2.0 ** -90                   # ragged last tile
-    u = synth.bf16_from_f32(x.astype(np.float32))
-    xt, xs = parity.bf16_tensor(u), numerics.bf16_from_bits(u)
+    if dtype == "f32":
+        x[20] = rng.standard_normal(d) * 1e-42    # fp32 subnormal entries
+        xs = x.astype(np.float32)
+        xt = torch.from_numpy(xs).cuda()
+        xs = xs.astype(np.float64)
+    else:
+        u = synth.bf16_from_f32(x.astype(np.float32))
+        xt, xs = parity.bf16_tensor(u), numerics.bf16_from_bits(u)
     xs = xs.reshape(n, d)
     st, D = _signs(d, 6)
     if m:
