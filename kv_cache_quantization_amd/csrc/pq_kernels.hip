@@ -2000,6 +2000,9 @@ __device__ __forceinline__ void load_key_bits(const uint8_t* kb, bool valid, uin
 }
 
 template <int KS, bool ADD>
+#ifndef PQ_SCORE_TILES
+#define PQ_SCORE_TILES 4         // key tiles of a QJL score iteration (the next ones load meanwhile)
+#endif
 __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArgs a, int chunks_per_group) {
   constexpr int m = 64 * KS, mb = m >> 3;
   const int group = a.q_heads / a.kv_heads;
@@ -2062,7 +2065,7 @@ __global__ __launch_bounds__(kThreads) void qjl_score_kernel(const pqi::ScoreArg
   // that lane (gq, r) ends with keys 2r and 2r + 1 and stores them together: 16 lanes write
   // a whole 128-byte line of a query head's scores.  U tiles (U/2 pairs) per iteration, the
   // next U tiles' bits and norms in flight meanwhile.
-  constexpr int U = 4;
+  constexpr int U = PQ_SCORE_TILES;
   const int64_t n_pairs = (T + 31) >> 5;
   const int64_t stride = (int64_t)chunks_per_group * kWaves;
   // loads of clamped keys (always in bounds, no branches, so several stay in flight); a
