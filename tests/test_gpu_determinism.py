@@ -15,7 +15,8 @@ from tests import parity, seeded
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("d,bits,m", [(128, 5, 64), (256, 3, 256), (512, 3, 512), (64, 4, 0)])
+@pytest.mark.parametrize("d,bits,m", [(128, 5, 64), (256, 3, 256), (512, 3, 512), (64, 4, 0), (128, 4, 0),
+                                      (256, 5, 0)])
 def test_split_and_grouped_calls_agree(d, bits, m):
     print("\n[case] determinism d=%d bits=%d m=%d" % (d, bits, m), flush=True)
     n, k = 16 * 97 + 11, 16 * 41 + 7                      # k: split inside a tile
@@ -45,3 +46,23 @@ def test_split_and_grouped_calls_agree(d, bits, m):
         assert torch.equal(torch.cat([g[0][0], g[1][0]]), full[0]) and torch.equal(g[2][0], full[0])
         assert torch.equal(torch.cat([g[0][1], g[1][1]]), full[1]) and torch.equal(g[2][1], full[1])
         assert torch.equal(torch.cat([go[0], go[1]]), out) and torch.equal(go[2], out)
+
+
+@pytest.mark.parametrize("d,dtype,m", [(128, "bf16", 64), (256, "bf16", 256), (512, "bf16", 512), (128, "f32", 64),
+                                       (64, "bf16", 32)])
+def test_residual_stage_leaves_codes_alone(d, dtype, m):
+    """The codes and norms of a call with the QJL residual stage equal those of the same call
+    without it (the stage only adds the residual's signs and norm; the kernels that carry it take
+    the codes by the same arithmetic)."""
+    print("\n[case] codes with and without QJL d=%d %s m=%d" % (d, dtype, m), flush=True)
+    n, bits = 16 * 53 + 9, 4
+    rng = np.random.default_rng(3 * d + m)
+    x = (rng.standard_normal((n, d)) * np.exp(rng.standard_normal((n, 1)))).astype(np.float32)
+    xt = torch.from_numpy(x).cuda() if dtype == "f32" else parity.bf16_tensor(synth.bf16_from_f32(x))
+    st = seeded.gpu_signs(11, d)
+    G = seeded.gpu_proj(13, m, d)
+    with_q = pq.quantize(xt, d, bits, st, G)
+    without = pq.quantize(xt, d, bits, st)
+    torch.cuda.synchronize()
+    assert torch.equal(with_q[0], without[0])
+    assert torch.equal(with_q[1], without[1])
