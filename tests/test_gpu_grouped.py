@@ -83,3 +83,39 @@ def test_grouped_config3_layer0():
         torch.cuda.synchronize()
         assert torch.equal(c, grouped[i][0]) and torch.equal(n, grouped[i][1]), "tensor %d" % i
         assert torch.equal(pq.dequantize(c, n, d, bits, st), outs[i]), "tensor %d dequantize" % i
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (256, "bf16"), (128, "f32")])
+def test_grouped_extreme_norms(d, dtype):
+    """Tensors of blocks whose norms leave [2^-60, 2^61) (tiny, subnormal entries, huge) in one
+    grouped launch beside an ordinary tensor: the oracle's codes, and the single calls' bytes."""
+    _case("grouped extreme norms d=%d %s" % (d, dtype))
+    bits = 4
+    rng = np.random.default_rng(7 + d)
+    xs, xs64, sts, Ds = [], [], [], []
+    for i, n in enumerate((16 * 3 + 5, 16 * 2)):
+        x = rng.standard_normal((n, d)) * 0.02
+        if i == 0:
+            x[0] *= 2.0 ** -80
+            x[3] = rng.standard_normal(d) * 1e-39
+            x[7] = rng.standard_normal(d) * 2.0 ** 58
+            x[20] *= 2.0 ** -66
+            x[n - 1] *= 2.0 ** -100
+        x = x.astype(np.float32)
+        if dtype == "bf16":
+            u = synth.bf16_from_f32(x)
+            xs.append(parity.bf16_tensor(u))
+            xs64.append(numerics.bf16_from_bits(u).reshape(n, d))
+        else:
+            xs.append(torch.from_numpy(x).cuda())
+            xs64.append(x.astype(np.float64))
+        sts.append(seeded.gpu_signs(20 + i, d))
+        Ds.append(seeded.oracle_D(20 + i, d))
+    grouped = pq.quantize_many(xs, d, bits, sts)
+    torch.cuda.synchronize()
+    for i in range(len(xs)):
+        c, nm, _, _ = pq.quantize(xs[i], d, bits, sts[i])
+        torch.cuda.synchronize()
+        assert torch.equal(c, grouped[i][0]) and torch.equal(nm, grouped[i][1]), "tensor %d" % i
+        parity.check_quantize(xs64[i], bits, Ds[i], grouped[i][0].cpu().numpy(), parity.f16_values(grouped[i][1]),
+                              label="grouped extreme t%d" % i)
