@@ -66,6 +66,7 @@ __device__ void build_search_grid(const CodecTables& t, uint4* tab) {
 // the A operand of v_mfma_f32_16x16x32_bf16 (lane l: row nn = l & 15, K = 8 (l >> 4) + 0..7),
 // entries +-1.0 in bf16, written to hf[f * 64 + lane].
 constexpr int kHfBytes = 4 * 64 * 16;
+constexpr int kSmBytes = 4 * 4 * 16;     // sign words of the rotated-basis kernel at d = 128
 
 __device__ void build_wht_frags(uint4* hf) {
   for (int i = threadIdx.x; i < 4 * 64; i += blockDim.x) {
@@ -399,7 +400,11 @@ struct Quantizer {
   // bytes (elements 32 s + 8 g .. +7) are held and the pairs are formed when used, which keeps
   // 48 registers free
   static constexpr bool kCompactSigns = D == 512;
-  uint32_t smask[kCompactSigns ? D / 32 : E / 2];
+  // the rotated-basis kernel on the matrix cores keeps the sign words in LDS instead (sml:
+  // [quarter g][K step s] as 16 bytes, the xor masks of chunk s of the load layout)
+  static constexpr bool SM_LDS = MR && QJL && RB;
+  uint32_t smask[SM_LDS ? 1 : (kCompactSigns ? D / 32 : E / 2)];
+  const uint4* sml = nullptr;
   int lane, r, g, m, m_pad, mb;
   float inv_w, offM, topM, inv_sqrt_d;
   uint32_t lane_off, rep_shift;
@@ -454,7 +459,7 @@ struct Quantizer {
     codes = a.codes;
     norms = a.norms;
     n_blocks = a.n_blocks;
-    if (a.signs) load_signs(a.signs);
+    if (a.signs && !SM_LDS) load_signs(a.signs);
     inv_w = a.t.cell_inv_w;
     offM = (float)a.t.half + kMagic;
     topM = kMagic + (float)(a.t.ncell - 1);
@@ -487,9 +492,13 @@ struct Quantizer {
     constexpr int KSM = D / 32, MT = D / 16;
     bf16x8 b[KSM];
 #pragma unroll
-    for (int s = 0; s < KSM; ++s)
-      b[s] = __builtin_bit_cast(bf16x8, make_uint4((w[s].x ^ sgn(4 * s)) + addw, (w[s].y ^ sgn(4 * s + 1)) + addw,
-                                                   (w[s].z ^ sgn(4 * s + 2)) + addw, (w[s].w ^ sgn(4 * s + 3)) + addw));
+    for (int s = 0; s < KSM; ++s) {
+      uint4 sm;
+      if constexpr (SM_LDS) sm = sml[g * KSM + s];
+      else sm = make_uint4(sgn(4 * s), sgn(4 * s + 1), sgn(4 * s + 2), sgn(4 * s + 3));
+      b[s] = __builtin_bit_cast(bf16x8, make_uint4((w[s].x ^ sm.x) + addw, (w[s].y ^ sm.y) + addw,
+                                                   (w[s].z ^ sm.z) + addw, (w[s].w ^ sm.w) + addw));
+    }
     f32x4 acc[MT];
     // one fragment live at a time: fragment f serves the (s, t) with t & 1 = f & 1 and
     // popcount(s & (t >> 1)) odd exactly when f > 1; s = 0 comes first for every t
@@ -1047,6 +1056,19 @@ void pq_quantize_kernel(const pqi::QuantArgs a) {
     uint4* hfp = reinterpret_cast<uint4*>(smem + a.t.ncell * a.t.nrep * 16 + gbytes);
     build_wht_frags(hfp);
     q.hf = hfp;
+    if constexpr (Q::SM_LDS) {
+      // the sign words after the fragments: entry g * (D / 32) + s, word t = pair 4 s + t of quarter g
+      uint4* sm = hfp + kHfBytes / 16;
+      for (int i = threadIdx.x; i < 4 * (D / 32); i += blockDim.x) {
+        const int gq = i / (D / 32), st = i % (D / 32);
+        const uint32_t b = a.signs[4 * st + gq];
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = (((b >> (2 * t)) & 1u) << 15) | (((b >> (2 * t + 1)) & 1u) << 31);
+        sm[i] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      q.sml = sm;
+    }
   }
   if constexpr (QJL && RB && Q::NR <= 4) {
     // the search grid first; the rows of G D H are then built (by the first waves) while
@@ -4001,7 +4023,7 @@ hipError_t launch_quantize_d(bool in_bf16, const pqi::QuantArgs& a, const pqi::L
   // (d <= 128: wider blocks hold too many registers at four waves per SIMD)
   if constexpr (D <= 128) {
     // bf16 blocks at d = 128 rotate on the matrix cores: their fragments follow G D H
-    const size_t rb = base + grb + (D == 128 && in_bf16 ? kHfBytes : 0);
+    const size_t rb = base + grb + (D == 128 && in_bf16 ? kHfBytes + kSmBytes : 0);
     if (qjl && rb <= (size_t)c.max_lds && base + grb <= 98304 && (mode < 2 || 3 * rb <= (size_t)c.max_lds)) {
       const size_t lds = rb;
       if (mode == 2) {
