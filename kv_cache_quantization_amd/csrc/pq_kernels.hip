@@ -99,6 +99,38 @@ __device__ void copy_centroids(const CodecTables& t, float* cent) {
   for (int k = threadIdx.x; k <= t.nbound; k += blockDim.x) cent[k] = t.cent[k];
 }
 
+// Dequantize at d = 512 on the fp16 matrix cores (the tables serve d = 256 as well).  Every centroid as an fp16 high part
+// and the fp16 rounding of the rest (22 significant bits), packed (high | low << 16); and the two
+// A fragments of the inverse transform: element bits 3, 4, 5 and the two top bits are summed by
+// v_mfma_f32_16x16x32_f16 (K index 8 gk + jj: jj holds element bits 3..5, gk the top two; output
+// row nn, tile t0: bits 3, 4 = nn >> 2, bit 5 = nn & 1, the top two = (nn >> 1) & 1 and t0), the
+// remaining element bits by butterflies over the K steps.  Entries +-1.0 in fp16.
+__device__ void build_dq_mr_tables(const CodecTables& t, uint32_t* cpair, uint4* hfd) {
+  for (int k = threadIdx.x; k <= t.nbound; k += blockDim.x) {
+    const float c = t.cent[k];
+    const _Float16 hi = (_Float16)c;
+    const _Float16 lo = (_Float16)(c - (float)hi);
+    cpair[k] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+  }
+  for (int i = threadIdx.x; i < 2 * 64; i += blockDim.x) {
+    const int t0 = i >> 6, l = i & 63, nn = l & 15, gk = l >> 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int jj = 2 * p + h;
+        const int par = ((jj & 1) & ((nn >> 2) & 1)) + (((jj >> 1) & 1) & ((nn >> 3) & 1)) + (((jj >> 2) & 1) & (nn & 1)) +
+                        ((gk & 1) & ((nn >> 1) & 1)) + (((gk >> 1) & 1) & t0);
+        word |= ((par & 1) ? 0xBC00u : 0x3C00u) << (16 * h);
+      }
+      w[p] = word;
+    }
+    hfd[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Projection matrix G (m x D bf16) staged in LDS, rows >= m zero.  16-byte chunk c
 // of row n is stored at chunk position c ^ (n & SW) so that the 16 rows read by
 // one 16-lane group hit 16 different bank groups.
@@ -1269,7 +1301,15 @@ struct Dequantizer {
   static constexpr int CB = PB ? PB : 8;                     // bits per stored code (PB = 0: a byte each)
   static constexpr int NB = E * CB / 8;                      // code bytes of the lane's run
   static constexpr int NQ = (NB + 3) / 4;                    // ... as dwords
+  // d = 512: the inverse transform on the fp16 matrix cores (MR), output chunk c of a lane
+  // (elements 32 c + 8 g + 0..7) in registers 8 c + 0..7, see inverse_mfma().  (At d = 256 the
+  // same form was faster with byte codes, 69 against 78 us at config 5, but slower with packed
+  // codes, 66 against 57 us; byte and packed codes must dequantize through one form, so d = 256
+  // keeps the butterflies.)
+  static constexpr bool MR = D == 512;
   const float* cent;
+  const uint32_t* cpair = nullptr;   // MR: centroid fp16 high | low << 16
+  const uint4* hfd = nullptr;        // MR: the two A fragments
   int r, g;
   uint32_t smask[E / 2];
   const uint8_t* codes;
@@ -1277,12 +1317,15 @@ struct Dequantizer {
   void* out;
   int64_t n_blocks;
 
+  // output elements 8 g + out_chunk(s) + 0..7 are register chunk s
+  static __host__ __device__ constexpr int out_chunk(int s) { return MR ? 32 * s : dq_out_chunk<D>(s); }
+
   __device__ __forceinline__ void retarget(const uint8_t* signs, const uint8_t* c, const uint16_t* nm, void* o,
                                            int64_t nb) {
     // byte loads (the mask may sit at any address): register chunk s is output elements
-    // 8 g + dq_out_chunk(s) + 0..7, sign byte g + dq_out_chunk(s) / 8
+    // 8 g + out_chunk(s) + 0..7, sign byte g + out_chunk(s) / 8
 #pragma unroll
-    for (int s = 0; s < E / 8; ++s) set_chunk(s, signs[g + dq_out_chunk<D>(s) / 8]);
+    for (int s = 0; s < E / 8; ++s) set_chunk(s, signs[g + out_chunk(s) / 8]);
     codes = c;
     norms = nm;
     out = o;
@@ -1297,9 +1340,9 @@ struct Dequantizer {
   }
   __device__ __forceinline__ void retarget(const SignWords<D>& sw, const uint8_t* c, const uint16_t* nm, void* o,
                                            int64_t nb) {
-    // register chunk s is output elements 8 g + dq_out_chunk(s) + 0..7: sign byte g + dq_out_chunk(s) / 8
+    // register chunk s is output elements 8 g + out_chunk(s) + 0..7: sign byte g + out_chunk(s) / 8
 #pragma unroll
-    for (int s = 0; s < E / 8; ++s) set_chunk(s, sw.byte(dq_out_chunk<D>(s) / 32, g));
+    for (int s = 0; s < E / 8; ++s) set_chunk(s, sw.byte(out_chunk(s) / 32, g));
     codes = c;
     norms = nm;
     out = o;
@@ -1314,13 +1357,60 @@ struct Dequantizer {
     nb = valid ? norms[blk] : (uint16_t)0;
   }
 
+  // MR: the lane's run (elements E g + j) as the B operand: K step s takes registers
+  // (s & 7) + 8 jj + 64 (s >> 3), jj = 0..7 (element bits 3..5), so the products sum element bits
+  // 3..5 and the lane bits; partial sums of K step s land in registers 8 s + 4 t0 + i, and
+  // butterflies over s (register bits 3 and up) finish the transform.  Afterwards register
+  // 8 (8 s_hi + b) + 4 t0 + i holds output element b + 8 g + 32 c, c = i0 + 2 i1 + 4 t0 (d = 256)
+  // or i0 + 2 s_hi + 4 i1 + 8 t0 (d = 512); the registers are then renamed to chunk order.
+  __device__ __forceinline__ void inverse_mfma(const uint32_t (&q)[NQ], float (&v)[E]) const {
+    constexpr int KSD = E / 8;
+    float u[E];
+    const f16x8 h0 = __builtin_bit_cast(f16x8, hfd[lane_id()]);
+    const f16x8 h1 = __builtin_bit_cast(f16x8, hfd[64 + lane_id()]);
+#pragma unroll
+    for (int s = 0; s < KSD; ++s) {
+      uint32_t cp[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) cp[jj] = cpair[stream_code<CB>(q, (s & 7) + 8 * jj + 64 * (s >> 3))];
+      u32x4 bh, bl;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        bh[p] = __builtin_amdgcn_perm(cp[2 * p + 1], cp[2 * p], 0x05040100u);   // high parts
+        bl[p] = __builtin_amdgcn_perm(cp[2 * p + 1], cp[2 * p], 0x07060302u);   // low parts
+      }
+      f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h0, __builtin_bit_cast(f16x8, bh), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h1, __builtin_bit_cast(f16x8, bh), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h0, __builtin_bit_cast(f16x8, bl), a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(h1, __builtin_bit_cast(f16x8, bl), a1, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[8 * s + i] = a0[i];
+        u[8 * s + 4 + i] = a1[i];
+      }
+    }
+    bfly<E, 3>(u); bfly<E, 4>(u); bfly<E, 5>(u);
+    if constexpr (D == 512) bfly<E, 6>(u);
+    // rename: chunk c, element b of the chunk -> register 8 c + b
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = j & 3, t0 = (j >> 2) & 1, b = (j >> 3) & 7, sh = j >> 6;
+      const int c = D == 256 ? (i & 1) + 2 * (i >> 1) + 4 * t0 : (i & 1) + 2 * sh + 4 * (i >> 1) + 8 * t0;
+      v[8 * c + b] = u[j];
+    }
+  }
+  static __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
   __device__ __forceinline__ void tile(const uint32_t (&q)[NQ], uint16_t nb, int64_t T) const {
     float v[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j) v[j] = cent[stream_code<CB>(q, j)];
     const float scale = f16_to_f32(nb) * (1.0f / (float)D);
-
-    wht_dequant<D>(v);
+    if constexpr (MR) {
+      inverse_mfma(q, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < E; ++j) v[j] = cent[stream_code<CB>(q, j)];
+      wht_dequant<D>(v);
+    }
 
     // Stores write whole 128-byte lines: a line of a block is two 16-byte pieces (a, b) in
     // each of its four lanes; the neighbouring blocks r & ~1 and r | 1 (lanes l, l ^ 1) trade
@@ -1350,10 +1440,11 @@ struct Dequantizer {
           w[t] = pack_bf16x2(v[8 * s + 2 * t] * scale, v[8 * s + 2 * t + 1] * scale) ^ smask[4 * s + t];
         return w;
       };
-      // chunk s and chunk dq_partner(s) hold the two halves of one output line
+      // chunk s and chunk partner(s) hold the two halves of one output line
 #pragma unroll
       for (int s = 0; s < E / 8; ++s)
-        if (dq_out_chunk<D>(s) % 64 == 0) put(row_e, pack(s), pack(dq_partner<D>(s)), dq_out_chunk<D>(s), dq_out_chunk<D>(s) + 32);
+        if (out_chunk(s) % 64 == 0)
+          put(row_e, pack(s), pack(MR ? s + 1 : dq_partner<D>(s)), out_chunk(s), out_chunk(s) + 32);
     } else {
       float* row_e = static_cast<float*>(out) + blk_e * D + 8 * g;
 #pragma unroll
@@ -1366,7 +1457,7 @@ struct Dequantizer {
         }
         const u32x4 pa = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
         const u32x4 pb = {__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7])};
-        put(row_e, pa, pb, dq_out_chunk<D>(s), dq_out_chunk<D>(s) + 4);
+        put(row_e, pa, pb, out_chunk(s), out_chunk(s) + 4);
       }
     }
   }
@@ -1376,11 +1467,16 @@ template <int D, bool OUT_BF16, int PB>
 __global__ __launch_bounds__(kThreads) void pq_dequantize_kernel(const pqi::DequantArgs a) {
   using DQ = Dequantizer<D, OUT_BF16, PB>;
   __shared__ float cent[1 << pqi::kMaxBits];
+  __shared__ uint32_t cpair[DQ::MR ? 1 << pqi::kMaxBits : 1];
+  __shared__ uint4 hfd[DQ::MR ? 128 : 1];
   copy_centroids(a.t, cent);
+  if constexpr (DQ::MR) build_dq_mr_tables(a.t, cpair, hfd);
   __syncthreads();
 
   DQ dq;
   dq.cent = cent;
+  dq.cpair = cpair;
+  dq.hfd = hfd;
   dq.r = threadIdx.x & 15;
   dq.g = (threadIdx.x & 63) >> 4;
   dq.retarget(a.signs, a.codes, a.norms, a.out, a.n_blocks);
@@ -1514,10 +1610,15 @@ __global__ __launch_bounds__(kThreads) void pq_dequantize_many_kernel(const pqi:
                                                                       int n_tensors) {
   using DQ = Dequantizer<D, OUT_BF16, PB>;
   __shared__ float cent[1 << pqi::kMaxBits];
+  __shared__ uint32_t cpair[DQ::MR ? 1 << pqi::kMaxBits : 1];
+  __shared__ uint4 hfd[DQ::MR ? 128 : 1];
   copy_centroids(a.t, cent);
+  if constexpr (DQ::MR) build_dq_mr_tables(a.t, cpair, hfd);
   __syncthreads();
   DQ dq;
   dq.cent = cent;
+  dq.cpair = cpair;
+  dq.hfd = hfd;
   dq.r = threadIdx.x & 15;
   dq.g = (threadIdx.x & 63) >> 4;
   const int64_t total = many_total(tab, n_tensors);
