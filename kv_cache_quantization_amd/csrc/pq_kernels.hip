@@ -99,7 +99,7 @@ __device__ void copy_centroids(const CodecTables& t, float* cent) {
   for (int k = threadIdx.x; k <= t.nbound; k += blockDim.x) cent[k] = t.cent[k];
 }
 
-// Dequantize at d = 256 and 512 on the fp16 matrix cores.  Every centroid as an fp16 high part
+// Dequantize at d = 512 on the fp16 matrix cores.  Every centroid as an fp16 high part
 // and the fp16 rounding of the rest (22 significant bits), packed (high | low << 16); and the two
 // A fragments of the inverse transform: element bits 3, 4, 5 and the two top bits are summed by
 // v_mfma_f32_16x16x32_f16 (K index 8 gk + jj: jj holds element bits 3..5, gk the top two; output
@@ -1301,9 +1301,12 @@ struct Dequantizer {
   static constexpr int CB = PB ? PB : 8;                     // bits per stored code (PB = 0: a byte each)
   static constexpr int NB = E * CB / 8;                      // code bytes of the lane's run
   static constexpr int NQ = (NB + 3) / 4;                    // ... as dwords
-  // d = 256 and 512: the inverse transform on the fp16 matrix cores (MR), output chunk c of a
-  // lane (elements 32 c + 8 g + 0..7) in registers 8 c + 0..7, see inverse_mfma()
-  static constexpr bool MR = D == 256 || D == 512;
+  // d = 512: the inverse transform on the fp16 matrix cores (MR), output chunk c of a lane
+  // (elements 32 c + 8 g + 0..7) in registers 8 c + 0..7, see inverse_mfma().  (At d = 256 the
+  // same form was faster with byte codes, 70 against 78 us at config 5, but slower with packed
+  // codes, 65-70 against 59 us; byte and packed codes dequantize through one form, so d = 256
+  // keeps the butterflies.)
+  static constexpr bool MR = D == 512;
   const float* cent;
   const uint32_t* cpair = nullptr;   // MR: centroid fp16 high | low << 16
   const uint4* hfd = nullptr;        // MR: the two A fragments
@@ -1360,27 +1363,16 @@ struct Dequantizer {
   // butterflies over s (register bits 3 and up) finish the transform.  Afterwards register
   // 8 (8 s_hi + b) + 4 t0 + i holds output element b + 8 g + 32 c, c = i0 + 2 i1 + 4 t0 (d = 256)
   // or i0 + 2 s_hi + 4 i1 + 8 t0 (d = 512); the registers are then renamed to chunk order.
-  __device__ __forceinline__ void inverse_mfma(const uint32_t (&qs)[NQ], float (&v)[E]) const {
+  __device__ __forceinline__ void inverse_mfma(const uint32_t (&q)[NQ], float (&v)[E]) const {
     constexpr int KSD = E / 8;
     float u[E];
-    // packed codes: unpacked to bytes in stream order first (the K steps take them out of order)
-    uint32_t q[E / 4];
-    if constexpr (PB) {
-#pragma unroll
-      for (int w = 0; w < E / 4; ++w) q[w] = 0;
-#pragma unroll
-      for (int j = 0; j < E; ++j) q[j >> 2] |= stream_code<CB>(qs, j) << (8 * (j & 3));
-    } else {
-#pragma unroll
-      for (int w = 0; w < E / 4; ++w) q[w] = qs[w];
-    }
     const f16x8 h0 = __builtin_bit_cast(f16x8, hfd[lane_id()]);
     const f16x8 h1 = __builtin_bit_cast(f16x8, hfd[64 + lane_id()]);
 #pragma unroll
     for (int s = 0; s < KSD; ++s) {
       uint32_t cp[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) cp[jj] = cpair[stream_code<8>(q, (s & 7) + 8 * jj + 64 * (s >> 3))];
+      for (int jj = 0; jj < 8; ++jj) cp[jj] = cpair[stream_code<CB>(q, (s & 7) + 8 * jj + 64 * (s >> 3))];
       u32x4 bh, bl;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
