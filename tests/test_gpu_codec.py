@@ -90,7 +90,7 @@ def test_quantize_dequantize_parity(d, bits, dtype, n, m):
         print("  max rel err", err, flush=True)
 
 
-@pytest.mark.parametrize("d,bits", [(64, 3), (128, 5), (256, 4), (512, 2)])
+@pytest.mark.parametrize("d,bits", [(64, 3), (128, 5), (256, 4), (512, 2), (512, 8), (512, 1)])
 def test_dequantize_random_codes(d, bits):
     """Dequantize arbitrary codes and norms (inputs the oracle side draws)."""
     _case("dequantize random codes d=%d bits=%d" % (d, bits))
